@@ -1,0 +1,141 @@
+"""KDA core for AMD MI355X (gfx950): thin Python binding over ``libkda.so``.
+
+Each function here has the name of a C entry point in ``include/kda.h`` and
+only marshals arguments (device pointers, sizes, row strides, the current
+torch stream); every step of the computation runs in the library's HIP
+kernels.  There is no CPU or PyTorch fallback: if ``libkda.so`` is missing or
+fails to load, importing this package raises.
+
+PyTorch supplies device memory and the stream.  Pointer tables (per-sequence
+state, snapshots, conv states) are device int64 tensors of addresses; build
+them with :func:`ptr_table`.
+"""
+import ctypes
+import os
+
+import torch  # loads the HIP runtime that libkda then shares
+
+from . import _lib
+from ._lib import KdaError, last_error  # noqa: F401
+
+__all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_decode", "kda_decode_k",
+           "gated_rmsnorm", "kda_prefill_workspace_bytes", "ptr_table", "KdaError",
+           "last_error", "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _rowstride(t, name):
+    if t.dim() < 2 or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be 2-D (or more) with unit innermost stride")
+    return int(t.stride(0)) if t.dim() == 2 else int(t.stride(-2))
+
+
+def _check(rc):
+    if rc != 0:
+        raise KdaError(rc, _lib.last_error())
+
+
+def ptr_table(tensors, device=None):
+    """Device int64 tensor of base addresses.
+
+    ``tensors`` is a list of CUDA tensors (one per entry), or one CUDA tensor
+    whose leading dimension indexes the entries (entry i = tensors[i])."""
+    if isinstance(tensors, torch.Tensor):
+        base = tensors.data_ptr()
+        step = tensors.stride(0) * tensors.element_size()
+        addrs = [base + i * step for i in range(tensors.shape[0])]
+        device = device or tensors.device
+    else:
+        addrs = [t.data_ptr() for t in tensors]
+        device = device or (tensors[0].device if tensors else torch.device("cuda"))
+    return torch.tensor(addrs, dtype=torch.int64, device=device)
+
+
+def conv_silu_l2(x, w, y, *, n_seq, rows, heads, head_dim, conv_state=None, conv_snap=None,
+                 eps_l2=1e-6, q32=None, k32=None, v32=None, kc=4):
+    """Causal depthwise conv + SiLU + q/k L2 (bf16 in/out).  ``conv_state`` and
+    ``conv_snap`` are pointer tables from :func:`ptr_table` (or None)."""
+    bf = torch.bfloat16
+    _check(_lib.lib.conv_silu_l2(
+        _ptr(x, bf, "x"), _rowstride(x, "x"), _ptr(w, bf, "w"),
+        _ptr(conv_state, torch.int64, "conv_state"), _ptr(conv_snap, torch.int64, "conv_snap"),
+        n_seq, rows, heads, head_dim, kc, float(eps_l2), _ptr(y, bf, "y"), _rowstride(y, "y"),
+        _ptr(q32, torch.float32, "q32"), _ptr(k32, torch.float32, "k32"),
+        _ptr(v32, torch.float32, "v32"), _stream()))
+
+
+def kda_gate(g_raw, a_log, dt_bias, gate, *, T, heads, head_dim, b_raw=None, beta=None):
+    """gate = -exp(a_log[h]) softplus(g_raw + dt_bias[c]); beta = sigmoid(b_raw)."""
+    bf = torch.bfloat16
+    ldb = _rowstride(b_raw, "b_raw") if b_raw is not None else 0
+    _check(_lib.lib.kda_gate(
+        _ptr(g_raw, bf, "g_raw"), _rowstride(g_raw, "g_raw"), _ptr(b_raw, bf, "b_raw"), ldb,
+        _ptr(a_log, torch.float32, "a_log"), _ptr(dt_bias, torch.float32, "dt_bias"),
+        T, heads, head_dim, _ptr(gate, torch.float32, "gate"),
+        _ptr(beta, torch.float32, "beta"), _stream()))
+
+
+def kda_prefill_workspace_bytes(T_pad, heads, head_dim, chunk):
+    return int(_lib.lib.kda_prefill_workspace_bytes(T_pad, heads, head_dim, chunk))
+
+
+def kda_prefill(q, k, v, gate, beta, state, core, workspace, *, T, T_pad, heads, head_dim,
+                chunk, scale):
+    """Chunked prefill from the carried ``state`` (updated in place)."""
+    f = torch.float32
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("beta", beta),
+                    ("state", state), ("core", core)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _check(_lib.lib.kda_prefill(
+        _ptr(q, f, "q"), _ptr(k, f, "k"), _ptr(v, f, "v"), _ptr(gate, f, "gate"),
+        _ptr(beta, f, "beta"), _ptr(state, f, "state"), _ptr(core, f, "core"),
+        T, T_pad, heads, head_dim, chunk, float(scale), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream()))
+
+
+def kda_decode(qkv, gate, beta, state, core, *, B, heads, head_dim, scale):
+    """One token per sequence; ``state`` is a pointer table (see ptr_table)."""
+    f = torch.float32
+    _check(_lib.lib.kda_decode(
+        _ptr(qkv, torch.bfloat16, "qkv"), _rowstride(qkv, "qkv"), _ptr(gate, f, "gate"),
+        _ptr(beta, f, "beta"), _ptr(state, torch.int64, "state"), _ptr(core, f, "core"),
+        B, heads, head_dim, float(scale), _stream()))
+
+
+def kda_decode_k(qkv, gate, beta, state, core, *, B, K, heads, head_dim, scale, snap=None):
+    """K tokens per sequence, bit-identical to K kda_decode calls; ``snap`` is
+    a pointer table of B*(K-1) snapshot buffers or None."""
+    f = torch.float32
+    _check(_lib.lib.kda_decode_k(
+        _ptr(qkv, torch.bfloat16, "qkv"), _rowstride(qkv, "qkv"), _ptr(gate, f, "gate"),
+        _ptr(beta, f, "beta"), _ptr(state, torch.int64, "state"),
+        _ptr(snap, torch.int64, "snap"), _ptr(core, f, "core"), B, K, heads, head_dim,
+        float(scale), _stream()))
+
+
+def gated_rmsnorm(core, out_gate, w, out, *, T, heads, head_dim, eps=1e-5):
+    """out = bf16(x / sqrt(mean x^2 + eps) * w * sigmoid(out_gate)) per head."""
+    bf = torch.bfloat16
+    c2 = core.reshape(core.shape[0], -1) if core.dim() == 3 else core
+    _check(_lib.lib.gated_rmsnorm(
+        _ptr(c2, torch.float32, "core"), _rowstride(c2, "core"), _ptr(out_gate, bf, "out_gate"),
+        _rowstride(out_gate, "out_gate"), _ptr(w, bf, "w"), T, heads, head_dim, float(eps),
+        _ptr(out, bf, "out"), _rowstride(out, "out"), _stream()))

@@ -1,0 +1,54 @@
+"""ctypes declarations of the libkda C ABI (include/kda.h).
+
+The library is built in-tree by ``build.py``; loading it never compiles and
+never falls back to anything else: a missing or unloadable library raises.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+# exported C symbols, as declared in include/kda.h
+SYMBOLS = ("kda_last_error", "conv_silu_l2", "kda_gate", "kda_prefill_workspace_bytes",
+           "kda_prefill", "kda_decode", "kda_decode_k", "gated_rmsnorm")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libkda error {code}: {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libkda.so not built at {LIB_PATH}; run "
+                          "`python gated_delta_rule_bounded_amd/build.py` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.conv_silu_l2.restype = ctypes.c_int
+    lib.conv_silu_l2.argtypes = [P, i64, P, P, P, i32, i32, i32, i32, i32, f32, P, i64, P, P, P, P]
+    lib.kda_gate.restype = ctypes.c_int
+    lib.kda_gate.argtypes = [P, i64, P, i64, P, P, i32, i32, i32, P, P, P]
+    lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, f32, P,
+                                ctypes.c_size_t, P]
+    lib.kda_decode.restype = ctypes.c_int
+    lib.kda_decode.argtypes = [P, i64, P, P, P, P, i32, i32, i32, f32, P]
+    lib.kda_decode_k.restype = ctypes.c_int
+    lib.kda_decode_k.argtypes = [P, i64, P, P, P, P, P, i32, i32, i32, i32, f32, P]
+    lib.gated_rmsnorm.restype = ctypes.c_int
+    lib.gated_rmsnorm.argtypes = [P, i64, P, i64, P, i32, i32, i32, f32, P, i64, P]
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.kda_last_error().decode()

@@ -1,0 +1,227 @@
+// C entry points of libkda: argument validation, error reporting, dispatch to
+// the kernel launchers.  The library allocates nothing and never synchronises.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return KDA_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_dim_ok(int d) { return d == 16 || d == 128; }
+
+// [lo, hi) byte ranges overlap
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_last_error(void) { return g_err; }
+
+int conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w,
+                 uint16_t *const *conv_state, uint16_t *const *conv_snap, int32_t n_seq,
+                 int32_t rows, int32_t heads, int32_t head_dim, int32_t kc, float eps_l2,
+                 uint16_t *y, int64_t ldy, float *q32, float *k32, float *v32,
+                 hipStream_t stream)
+{
+    if (n_seq < 0 || rows < 0 || heads <= 0)
+        return fail(KDA_ERR_SHAPE, "conv_silu_l2: n_seq=%d rows=%d heads=%d", n_seq, rows, heads);
+    if (!head_dim_ok(head_dim) || kc != 4)
+        return fail(KDA_ERR_UNSUPPORTED, "conv_silu_l2: head_dim=%d kc=%d (need 16|128, 4)",
+                    head_dim, kc);
+    if (n_seq == 0 || rows == 0) return ok();
+    if (!x || !w || !y) return fail(KDA_ERR_NULL, "conv_silu_l2: x, w and y are required");
+    const int64_t conv_dim = 3LL * heads * head_dim;
+    if (ldx < conv_dim || ldy < conv_dim || ldx % 8 || ldy % 8)
+        return fail(KDA_ERR_SHAPE, "conv_silu_l2: ldx=%lld ldy=%lld conv_dim=%lld",
+                    (long long)ldx, (long long)ldy, (long long)conv_dim);
+    const bool any32 = q32 || k32 || v32;
+    if (any32 && !(q32 && k32 && v32))
+        return fail(KDA_ERR_NULL, "conv_silu_l2: q32, k32, v32 must all be given or all NULL");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y) ||
+        (any32 && (!aligned16(q32) || !aligned16(k32) || !aligned16(v32))))
+        return fail(KDA_ERR_SHAPE, "conv_silu_l2: pointers must be 16-byte aligned");
+    const int64_t nrows = (int64_t)n_seq * rows;
+    if (overlap(x, (size_t)((nrows - 1) * ldx + conv_dim) * 2, y,
+                (size_t)((nrows - 1) * ldy + conv_dim) * 2))
+        return fail(KDA_ERR_ALIAS, "conv_silu_l2: y overlaps x");
+    return hip_status(kda::launch_conv_silu_l2(x, ldx, w, conv_state, conv_snap, n_seq, rows,
+                                               heads, head_dim, eps_l2, y, ldy, q32, k32, v32,
+                                               stream),
+                      "conv_silu_l2 launch");
+}
+
+int kda_gate(const uint16_t *g_raw, int64_t ldg, const uint16_t *b_raw, int64_t ldb,
+             const float *a_log, const float *dt_bias, int32_t T, int32_t heads,
+             int32_t head_dim, float *gate, float *beta, hipStream_t stream)
+{
+    if (T < 0 || heads <= 0)
+        return fail(KDA_ERR_SHAPE, "kda_gate: T=%d heads=%d", T, heads);
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_gate: head_dim=%d", head_dim);
+    if (T == 0) return ok();
+    if (!g_raw || !a_log || !dt_bias || !gate || (b_raw && !beta))
+        return fail(KDA_ERR_NULL, "kda_gate: g_raw, a_log, dt_bias, gate (and beta with b_raw) required");
+    const int64_t qkv = (int64_t)heads * head_dim;
+    if (ldg < qkv || ldg % 8 || (b_raw && ldb < heads))
+        return fail(KDA_ERR_SHAPE, "kda_gate: ldg=%lld ldb=%lld", (long long)ldg, (long long)ldb);
+    if (!aligned16(g_raw) || !aligned16(dt_bias) || !aligned16(gate))
+        return fail(KDA_ERR_SHAPE, "kda_gate: g_raw, dt_bias, gate must be 16-byte aligned");
+    if (overlap(gate, (size_t)T * qkv * 4, g_raw, (size_t)((T - 1) * ldg + qkv) * 2) ||
+        (b_raw && overlap(beta, (size_t)T * heads * 4, b_raw, (size_t)((T - 1) * ldb + heads) * 2)))
+        return fail(KDA_ERR_ALIAS, "kda_gate: an output overlaps an input");
+    return hip_status(kda::launch_kda_gate(g_raw, ldg, b_raw, ldb, a_log, dt_bias, T, heads,
+                                           head_dim, gate, beta, stream),
+                      "kda_gate launch");
+}
+
+size_t kda_prefill_workspace_bytes(int32_t T_pad, int32_t heads, int32_t head_dim, int32_t chunk)
+{
+    if (T_pad < 0 || heads <= 0 || !(chunk == 16 || chunk == 64) || T_pad % chunk) return 0;
+    return kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
+}
+
+int kda_prefill(const float *q, const float *k, const float *v, const float *gate,
+                const float *beta, float *state, float *core, int32_t T, int32_t T_pad,
+                int32_t heads, int32_t head_dim, int32_t chunk, float scale, void *workspace,
+                size_t workspace_bytes, hipStream_t stream)
+{
+    if (!head_dim_ok(head_dim) || !(chunk == 16 || chunk == 64))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: head_dim=%d chunk=%d (need 16|128, 16|64)",
+                    head_dim, chunk);
+    if (T < 0 || heads <= 0 || T_pad < T || T_pad % chunk)
+        return fail(KDA_ERR_SHAPE, "kda_prefill: T=%d T_pad=%d heads=%d chunk=%d", T, T_pad,
+                    heads, chunk);
+    if (T == 0) return ok();
+    if (!q || !k || !v || !gate || !beta || !state || !core || !workspace)
+        return fail(KDA_ERR_NULL, "kda_prefill: null pointer argument");
+    const size_t need = kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "kda_prefill: workspace %zu bytes < %zu needed",
+                    workspace_bytes, need);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) ||
+        !aligned16(state) || !aligned16(core) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(KDA_ERR_SHAPE, "kda_prefill: misaligned pointer");
+    const size_t rows_b = (size_t)T_pad * heads * head_dim * 4;
+    const size_t st_b = (size_t)heads * head_dim * head_dim * 4;
+    const void *ins[] = {q, k, v, gate};
+    for (const void *p : ins)
+        if (overlap(core, rows_b, p, rows_b) || overlap(state, st_b, p, rows_b))
+            return fail(KDA_ERR_ALIAS, "kda_prefill: core or state overlaps an input");
+    if (overlap(core, rows_b, beta, (size_t)T_pad * heads * 4) || overlap(core, rows_b, state, st_b) ||
+        overlap(workspace, need, core, rows_b) || overlap(workspace, need, state, st_b))
+        return fail(KDA_ERR_ALIAS, "kda_prefill: core, state, beta or workspace overlap");
+    return hip_status(kda::launch_kda_prefill(q, k, v, gate, beta, state, core, T, T_pad, heads,
+                                              head_dim, chunk, scale, workspace, stream),
+                      "kda_prefill launch");
+}
+
+static int check_decode(const char *who, const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                        const float *beta, float *const *state, float *core, int32_t rows,
+                        int32_t heads, int32_t head_dim)
+{
+    if (!qkv || !gate || !beta || !state || !core)
+        return fail(KDA_ERR_NULL, "%s: null pointer argument", who);
+    const int64_t qkvw = (int64_t)heads * head_dim;
+    if (ldqkv < 3 * qkvw)
+        return fail(KDA_ERR_SHAPE, "%s: ldqkv=%lld < 3*heads*head_dim", who, (long long)ldqkv);
+    if (!aligned16(core))
+        return fail(KDA_ERR_SHAPE, "%s: core must be 16-byte aligned", who);
+    if (overlap(core, (size_t)rows * qkvw * 4, gate, (size_t)rows * qkvw * 4) ||
+        overlap(core, (size_t)rows * qkvw * 4, qkv, (size_t)((rows - 1) * ldqkv + 3 * qkvw) * 2) ||
+        overlap(core, (size_t)rows * qkvw * 4, beta, (size_t)rows * heads * 4))
+        return fail(KDA_ERR_ALIAS, "%s: core overlaps an input", who);
+    return KDA_OK;
+}
+
+int kda_decode(const uint16_t *qkv, int64_t ldqkv, const float *gate, const float *beta,
+               float *const *state, float *core, int32_t B, int32_t heads, int32_t head_dim,
+               float scale, hipStream_t stream)
+{
+    if (B < 0 || heads <= 0) return fail(KDA_ERR_SHAPE, "kda_decode: B=%d heads=%d", B, heads);
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_decode: head_dim=%d", head_dim);
+    if (B == 0) return ok();
+    if (int rc = check_decode("kda_decode", qkv, ldqkv, gate, beta, state, core, B, heads, head_dim))
+        return rc;
+    return hip_status(kda::launch_kda_recurrent(qkv, ldqkv, gate, beta, state, nullptr, core, B,
+                                                1, heads, head_dim, scale, stream),
+                      "kda_decode launch");
+}
+
+int kda_decode_k(const uint16_t *qkv, int64_t ldqkv, const float *gate, const float *beta,
+                 float *const *state, float *const *snap, float *core, int32_t B, int32_t K,
+                 int32_t heads, int32_t head_dim, float scale, hipStream_t stream)
+{
+    if (B < 0 || K < 0 || heads <= 0)
+        return fail(KDA_ERR_SHAPE, "kda_decode_k: B=%d K=%d heads=%d", B, K, heads);
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_k: head_dim=%d", head_dim);
+    if (B == 0 || K == 0) return ok();
+    if ((int64_t)B * K > (int64_t)1 << 30)
+        return fail(KDA_ERR_SHAPE, "kda_decode_k: B*K too large");
+    if (int rc = check_decode("kda_decode_k", qkv, ldqkv, gate, beta, state, core, B * K, heads,
+                              head_dim))
+        return rc;
+    if (snap && (const void *)snap == (const void *)state)
+        return fail(KDA_ERR_ALIAS, "kda_decode_k: snapshot table is the state table");
+    return hip_status(kda::launch_kda_recurrent(qkv, ldqkv, gate, beta, state,
+                                                K > 1 ? snap : nullptr, core, B, K, heads,
+                                                head_dim, scale, stream),
+                      "kda_decode_k launch");
+}
+
+int gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate, int64_t ldo,
+                  const uint16_t *w, int32_t T, int32_t heads, int32_t head_dim, float eps,
+                  uint16_t *out, int64_t ldy, hipStream_t stream)
+{
+    if (T < 0 || heads <= 0) return fail(KDA_ERR_SHAPE, "gated_rmsnorm: T=%d heads=%d", T, heads);
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "gated_rmsnorm: head_dim=%d", head_dim);
+    if (T == 0) return ok();
+    if (!core || !out_gate || !w || !out)
+        return fail(KDA_ERR_NULL, "gated_rmsnorm: null pointer argument");
+    const int64_t qkv = (int64_t)heads * head_dim;
+    if (ldc < qkv || ldo < qkv || ldy < qkv || ldc % 4 || ldo % 8 || ldy % 8)
+        return fail(KDA_ERR_SHAPE, "gated_rmsnorm: bad row stride");
+    if (!aligned16(core) || !aligned16(out_gate) || !aligned16(w) || !aligned16(out))
+        return fail(KDA_ERR_SHAPE, "gated_rmsnorm: pointers must be 16-byte aligned");
+    const size_t ob = (size_t)((T - 1) * ldy + qkv) * 2;
+    if (overlap(out, ob, out_gate, (size_t)((T - 1) * ldo + qkv) * 2) ||
+        overlap(out, ob, core, (size_t)((T - 1) * ldc + qkv) * 4))
+        return fail(KDA_ERR_ALIAS, "gated_rmsnorm: out overlaps an input");
+    return hip_status(kda::launch_gated_rmsnorm(core, ldc, out_gate, ldo, w, T, heads, head_dim,
+                                                eps, out, ldy, stream),
+                      "gated_rmsnorm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+// conv_silu_l2: short causal depthwise conv + SiLU + per-head L2 of q and k
+// ("Glm5NextKdaWorkspace" page, fields qkv_proj, conv_out and q_f32;
+// "Glm5NextKdaWeights" page, field conv; "Glm5NextKdaLayer" page, decode and
+// decode_k for the carried conv state and its per-row snapshots).
+//
+// For each row t and channel c (window = the last KC pre-conv rows, newest
+// last; it starts from the carried conv state):
+//   pre = sum_j w[c][j] * window[j][c]       (tap KC-1 meets row t)
+//   s   = pre * sigmoid(pre)
+//   q and k sections: s /= sqrt(sum over the head's D channels of s^2 + eps)
+//   y   = bf16(s)  (one rounding), optional exact fp32 copies of q, k, v.
+//
+// Mapping: a thread owns 8 consecutive channels (one 16-byte bf16 load per
+// row) and walks a tile of consecutive rows with the window in registers, so
+// each input row is read once.  The D/8 threads of one head are adjacent
+// lanes; the L2 sum reduces among them by xor-shuffles in a fixed order.  The
+// per-row arithmetic does not depend on the tiling, so the K-row snapshot
+// mode is bit-identical to K single-row calls.  Only row tile 0 of a sequence
+// reads the old conv state, and the same threads write the new state after
+// reading it, so no other workgroup can observe a half-updated state.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+constexpr int kConvThreads = 256;
+constexpr int kConvKC = 4;
+constexpr int kConvRowsPerTile = 16;
+
+template <int D>
+__global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
+    const uint16_t *__restrict__ x, int64_t ldx, const uint16_t *__restrict__ w,
+    uint16_t *const *__restrict__ conv_state, uint16_t *const *__restrict__ conv_snap,
+    int rows, int H, int ntiles, float eps_l2, uint16_t *__restrict__ y, int64_t ldy,
+    float *__restrict__ q32, float *__restrict__ k32, float *__restrict__ v32)
+{
+    constexpr int KC = kConvKC;
+    constexpr int LANES_PER_HEAD = D / 8;
+    const int qkv = H * D;
+    const int conv_dim = 3 * qkv;
+    const int grp = blockIdx.x * kConvThreads + threadIdx.x;
+    const bool active = grp < conv_dim / 8;
+    const int c0 = active ? grp * 8 : 0;
+    const int tile = blockIdx.y;
+    const int seq = blockIdx.z;
+    const int t0 = tile * kConvRowsPerTile;
+    const int t1 = min(rows, t0 + kConvRowsPerTile);
+    const int64_t row0 = (int64_t)seq * rows;   // first row of this sequence
+    const uint16_t *__restrict__ st = conv_state ? conv_state[seq] : nullptr;
+
+    // taps for the 8 channels: w[c][0..KC-1]
+    float wt[8][KC];
+    {
+        const uint4 *wp = reinterpret_cast<const uint4 *>(w + (int64_t)c0 * KC);
+        float f[8];
+#pragma unroll
+        for (int p = 0; p < KC * 8 / 8; ++p) {
+            unpack8(wp[p], f);   // channels 2p, 2p+1, each KC taps
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wt[(p * 8 + e) / KC][(p * 8 + e) % KC] = f[e];
+        }
+    }
+
+    // window: win[j] holds input row (t - KC + 1 + j) once row t is loaded
+    uint4 win[KC];
+#pragma unroll
+    for (int j = 1; j < KC; ++j) {
+        const int r = t0 - KC + j;   // sequence-local row index, may be < 0
+        if (r >= 0)
+            win[j] = *reinterpret_cast<const uint4 *>(x + (row0 + r) * ldx + c0);
+        else if (st != nullptr)
+            win[j] = *reinterpret_cast<const uint4 *>(st + (int64_t)(KC + r) * conv_dim + c0);
+        else
+            win[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    win[0] = make_uint4(0u, 0u, 0u, 0u);
+
+    const int section = c0 / qkv;           // 0 = q, 1 = k, 2 = v
+    const int cs = c0 - section * qkv;      // channel within the section
+
+    for (int t = t0; t < t1; ++t) {
+#pragma unroll
+        for (int j = 0; j + 1 < KC; ++j) win[j] = win[j + 1];
+        win[KC - 1] = *reinterpret_cast<const uint4 *>(x + (row0 + t) * ldx + c0);
+
+        float xv[KC][8];
+#pragma unroll
+        for (int j = 0; j < KC; ++j) unpack8(win[j], xv[j]);
+        float s[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float pre = wt[e][0] * xv[0][e];
+#pragma unroll
+            for (int j = 1; j < KC; ++j) pre = __builtin_fmaf(wt[e][j], xv[j][e], pre);
+            s[e] = pre / (1.0f + expf(-pre));
+            ss = __builtin_fmaf(s[e], s[e], ss);
+        }
+#pragma unroll
+        for (int off = 1; off < LANES_PER_HEAD; off <<= 1) ss += __shfl_xor(ss, off);
+        if (section < 2) {
+            const float inv = 1.0f / sqrtf(ss + eps_l2);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] *= inv;
+        }
+        const uint4 packed = pack8(s);
+        if (active) {
+            *reinterpret_cast<uint4 *>(y + (row0 + t) * ldy + c0) = packed;
+            if (q32 != nullptr) {
+                float *dst = (section == 0 ? q32 : section == 1 ? k32 : v32) +
+                             (row0 + t) * qkv + cs;
+                float f[8];
+                unpack8(packed, f);
+                reinterpret_cast<float4 *>(dst)[0] = make_float4(f[0], f[1], f[2], f[3]);
+                reinterpret_cast<float4 *>(dst)[1] = make_float4(f[4], f[5], f[6], f[7]);
+            }
+            if (conv_snap != nullptr && t + 1 < rows) {
+                uint16_t *dst = conv_snap[row0 - seq + t];   // seq*(rows-1) + t
+#pragma unroll
+                for (int j = 0; j < KC; ++j)
+                    *reinterpret_cast<uint4 *>(dst + (int64_t)j * conv_dim + c0) = win[j];
+            }
+        }
+    }
+
+    // new conv state = the window after the sequence's last row
+    if (tile == 0 && st != nullptr && active) {
+        uint16_t *dst = conv_state[seq];
+        if (ntiles == 1) {
+#pragma unroll
+            for (int j = 0; j < KC; ++j)
+                *reinterpret_cast<uint4 *>(dst + (int64_t)j * conv_dim + c0) = win[j];
+        } else {
+            // rows >= kConvRowsPerTile >= KC: the window is the last KC rows of x
+#pragma unroll
+            for (int j = 0; j < KC; ++j)
+                *reinterpret_cast<uint4 *>(dst + (int64_t)j * conv_dim + c0) =
+                    *reinterpret_cast<const uint4 *>(x + (row0 + rows - KC + j) * ldx + c0);
+        }
+    }
+}
+
+hipError_t launch_conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w,
+                               uint16_t *const *conv_state, uint16_t *const *conv_snap,
+                               int n_seq, int rows, int heads, int head_dim, float eps_l2,
+                               uint16_t *y, int64_t ldy, float *q32, float *k32, float *v32,
+                               hipStream_t stream)
+{
+    const int conv_dim = 3 * heads * head_dim;
+    const int ntiles = (rows + kConvRowsPerTile - 1) / kConvRowsPerTile;
+    const dim3 grid((conv_dim / 8 + kConvThreads - 1) / kConvThreads, ntiles, n_seq);
+    if (head_dim == 128) {
+        hipLaunchKernelGGL(conv_silu_l2_kernel<128>, grid, dim3(kConvThreads), 0, stream, x, ldx,
+                           w, conv_state, conv_snap, rows, heads, ntiles, eps_l2, y, ldy, q32,
+                           k32, v32);
+    } else {
+        hipLaunchKernelGGL(conv_silu_l2_kernel<16>, grid, dim3(kConvThreads), 0, stream, x, ldx,
+                           w, conv_state, conv_snap, rows, heads, ntiles, eps_l2, y, ldy, q32,
+                           k32, v32);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kda

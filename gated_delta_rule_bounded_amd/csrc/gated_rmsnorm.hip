@@ -1,0 +1,63 @@
+// gated_rmsnorm: sigmoid-gated RMSNorm of the core output per (token, head)
+// ("Glm5NextKdaWorkspace" page, fields core, out_gate and o_norm_out;
+// "Glm5NextKdaWeights" page, field o_norm).
+//   out[t, h*D+d] = bf16( x_d * rsqrt(mean_d x^2 + eps) * w[d] * sigmoid(gate[t, h*D+d]) )
+// HBM-bound: each thread owns 8 consecutive channels (two 16-byte fp32 loads,
+// one 16-byte bf16 gate load, one 16-byte store); the D/8 threads of a head are
+// adjacent lanes and reduce the sum of squares by xor-shuffles.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+constexpr int kNormThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
+    const float *__restrict__ core, int64_t ldc, const uint16_t *__restrict__ out_gate,
+    int64_t ldo, const uint16_t *__restrict__ w, int T, int H, float eps,
+    uint16_t *__restrict__ out, int64_t ldy)
+{
+    constexpr int LANES_PER_HEAD = D / 8;
+    const int groups_per_row = H * D / 8;
+    const int64_t gidx = (int64_t)blockIdx.x * kNormThreads + threadIdx.x;
+    const bool active = gidx < (int64_t)T * groups_per_row;
+    const int t = active ? (int)(gidx / groups_per_row) : 0;
+    const int c0 = active ? (int)(gidx % groups_per_row) * 8 : 0;
+    const int d0 = c0 % D;
+
+    const float4 a = *reinterpret_cast<const float4 *>(core + (int64_t)t * ldc + c0);
+    const float4 b = *reinterpret_cast<const float4 *>(core + (int64_t)t * ldc + c0 + 4);
+    const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(xv[e], xv[e], ss);
+#pragma unroll
+    for (int off = 1; off < LANES_PER_HEAD; off <<= 1) ss += __shfl_xor(ss, off);
+    const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+
+    float g[8], wv[8], o[8];
+    unpack8(*reinterpret_cast<const uint4 *>(out_gate + (int64_t)t * ldo + c0), g);
+    unpack8(*reinterpret_cast<const uint4 *>(w + d0), wv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = xv[e] * r * wv[e] * (1.0f / (1.0f + expf(-g[e])));
+    if (active) *reinterpret_cast<uint4 *>(out + (int64_t)t * ldy + c0) = pack8(o);
+}
+
+hipError_t launch_gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate,
+                                int64_t ldo, const uint16_t *w, int T, int heads,
+                                int head_dim, float eps, uint16_t *out, int64_t ldy,
+                                hipStream_t stream)
+{
+    const int64_t groups = (int64_t)T * heads * head_dim / 8;
+    const dim3 grid((unsigned)((groups + kNormThreads - 1) / kNormThreads));
+    if (head_dim == 128)
+        hipLaunchKernelGGL(gated_rmsnorm_kernel<128>, grid, dim3(kNormThreads), 0, stream, core,
+                           ldc, out_gate, ldo, w, T, heads, eps, out, ldy);
+    else
+        hipLaunchKernelGGL(gated_rmsnorm_kernel<16>, grid, dim3(kNormThreads), 0, stream, core,
+                           ldc, out_gate, ldo, w, T, heads, eps, out, ldy);
+    return hipGetLastError();
+}
+
+}  // namespace kda

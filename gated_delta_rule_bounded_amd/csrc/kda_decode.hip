@@ -1,0 +1,166 @@
+// Recurrent KDA decode: one or K tokens per sequence, state read once from HBM,
+// walked in registers, written once (plus optional per-row snapshots).
+//
+// Operation ("Glm5NextKdaLayer" page, decode and decode_k): per head, with
+// S[i][j] (i = key channel, j = value channel), each token:
+//   S' = diag(exp(g)) S;  u = beta (v - S'^T k);  S = S' + k u^T;
+//   o  = scale S^T q = scale (S'^T q + u (k . q)).
+// The second form of o needs one reduction pass over S instead of two; it is
+// the same quantity.
+//
+// Layout: one workgroup per (head, sequence).  The head's D x D fp32 state is
+// contiguous (64 KiB at D = 128); thread t owns the float4 column group
+// cg = t % (D/4) of rows rg + RG*r, so every load/store instruction of the
+// workgroup covers whole contiguous rows (128-bit accesses, fully coalesced).
+// Column sums over the key axis reduce within a wave by xor-shuffles, then
+// across waves through LDS, always in the same order.  The same kernel serves
+// single-token decode (K = 1) and K-token decode, which makes the K-token
+// result bit-identical to K single-token calls: each step runs the same
+// instructions on the same values, and fp32 registers hold exactly what an
+// fp32 store and reload would.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+template <int D>
+struct RecCfg {
+    static constexpr int kThreads = (D >= 128) ? 256 : 64;
+    static constexpr int kCG = D / 4;              // float4 column groups per row
+    static constexpr int kRG = kThreads / kCG;     // row groups
+    static constexpr int kRPT = D / kRG;           // rows per thread
+    static constexpr int kWaves = kThreads / kWave;
+    static_assert(kCG <= kWave, "a row's column groups must fit in one wave");
+    static_assert(kRG * kCG == kThreads && kRPT * kRG == D, "bad tiling");
+};
+
+__device__ __forceinline__ float4 fma4(float a, const float4 &b, const float4 &c) {
+    return make_float4(__builtin_fmaf(a, b.x, c.x), __builtin_fmaf(a, b.y, c.y),
+                       __builtin_fmaf(a, b.z, c.z), __builtin_fmaf(a, b.w, c.w));
+}
+
+template <int D>
+__global__ __launch_bounds__(RecCfg<D>::kThreads) void kda_recurrent_kernel(
+    const uint16_t *__restrict__ qkv, int64_t ldqkv, const float *__restrict__ gate,
+    const float *__restrict__ beta, float *const *__restrict__ state,
+    float *const *__restrict__ snap, float *__restrict__ core, int K, int H, float scale)
+{
+    using Cfg = RecCfg<D>;
+    constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT, NWAVE = Cfg::kWaves;
+
+    const int h = blockIdx.x;
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int cg = tid % CG;
+    const int rg = tid / CG;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int qkvw = H * D;
+
+    __shared__ __align__(16) float s_q[D], s_k[D], s_v[D], s_e[D];
+    __shared__ float4 s_red[NWAVE > 1 ? NWAVE : 1][2][CG];
+    __shared__ float s_kq[NWAVE > 1 ? NWAVE : 1];
+
+    float *__restrict__ Sg = state[b] + (size_t)h * D * D;
+    float4 S[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+        S[r] = reinterpret_cast<const float4 *>(Sg + (size_t)(rg + RG * r) * D)[cg];
+
+    for (int t = 0; t < K; ++t) {
+        const size_t row = (size_t)b * K + t;
+        const uint16_t *__restrict__ qrow = qkv + row * ldqkv + (size_t)h * D;
+        for (int i = tid; i < D; i += Cfg::kThreads) {
+            s_q[i] = bf16_to_f32(qrow[i]);
+            s_k[i] = bf16_to_f32(qrow[qkvw + i]);
+            s_v[i] = bf16_to_f32(qrow[2 * qkvw + i]);
+            s_e[i] = exp2_fast(gate[(row * H + h) * D + i] * kLog2e);
+        }
+        const float bt = beta[row * H + h];
+        __syncthreads();
+
+        // decay, then partial column sums of S'^T k and S'^T q over this
+        // thread's rows, and the matching partial of k . q
+        float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
+        float kq = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int i = rg + RG * r;
+            const float e = s_e[i], ki = s_k[i], qi = s_q[i];
+            S[r] = make_float4(S[r].x * e, S[r].y * e, S[r].z * e, S[r].w * e);
+            pk = fma4(ki, S[r], pk);
+            pq = fma4(qi, S[r], pq);
+            kq = __builtin_fmaf(ki, qi, kq);
+        }
+        // reduce over the row groups held by this wave
+#pragma unroll
+        for (int off = CG; off < kWave; off <<= 1) {
+            pk.x += __shfl_xor(pk.x, off); pk.y += __shfl_xor(pk.y, off);
+            pk.z += __shfl_xor(pk.z, off); pk.w += __shfl_xor(pk.w, off);
+            pq.x += __shfl_xor(pq.x, off); pq.y += __shfl_xor(pq.y, off);
+            pq.z += __shfl_xor(pq.z, off); pq.w += __shfl_xor(pq.w, off);
+            kq += __shfl_xor(kq, off);
+        }
+        if constexpr (NWAVE > 1) {
+            if (lane < CG) {
+                s_red[wave][0][lane] = pk;
+                s_red[wave][1][lane] = pq;
+                if (lane == 0) s_kq[wave] = kq;
+            }
+            __syncthreads();
+            pk = s_red[0][0][cg];
+            pq = s_red[0][1][cg];
+            kq = s_kq[0];
+#pragma unroll
+            for (int w = 1; w < NWAVE; ++w) {
+                const float4 a = s_red[w][0][cg], c = s_red[w][1][cg];
+                pk = make_float4(pk.x + a.x, pk.y + a.y, pk.z + a.z, pk.w + a.w);
+                pq = make_float4(pq.x + c.x, pq.y + c.y, pq.z + c.z, pq.w + c.w);
+                kq += s_kq[w];
+            }
+        }
+        const float4 v4 = reinterpret_cast<const float4 *>(s_v)[cg];
+        const float4 u = make_float4(bt * (v4.x - pk.x), bt * (v4.y - pk.y),
+                                     bt * (v4.z - pk.z), bt * (v4.w - pk.w));
+        if (rg == 0) {
+            const float4 o = make_float4(scale * __builtin_fmaf(u.x, kq, pq.x),
+                                         scale * __builtin_fmaf(u.y, kq, pq.y),
+                                         scale * __builtin_fmaf(u.z, kq, pq.z),
+                                         scale * __builtin_fmaf(u.w, kq, pq.w));
+            reinterpret_cast<float4 *>(core + (row * H + h) * D)[cg] = o;
+        }
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+            S[r] = fma4(s_k[rg + RG * r], u, S[r]);
+
+        if (snap != nullptr && t + 1 < K) {
+            float *__restrict__ Sn = snap[(size_t)b * (K - 1) + t] + (size_t)h * D * D;
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                reinterpret_cast<float4 *>(Sn + (size_t)(rg + RG * r) * D)[cg] = S[r];
+        }
+        __syncthreads();  // LDS is rewritten by the next row
+    }
+
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+        reinterpret_cast<float4 *>(Sg + (size_t)(rg + RG * r) * D)[cg] = S[r];
+}
+
+hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                                const float *beta, float *const *state, float *const *snap,
+                                float *core, int B, int K, int heads, int head_dim,
+                                float scale, hipStream_t stream)
+{
+    const dim3 grid(heads, B);
+    if (head_dim == 128) {
+        hipLaunchKernelGGL(kda_recurrent_kernel<128>, grid, dim3(RecCfg<128>::kThreads), 0,
+                           stream, qkv, ldqkv, gate, beta, state, snap, core, K, heads, scale);
+    } else {
+        hipLaunchKernelGGL(kda_recurrent_kernel<16>, grid, dim3(RecCfg<16>::kThreads), 0,
+                           stream, qkv, ldqkv, gate, beta, state, snap, core, K, heads, scale);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kda

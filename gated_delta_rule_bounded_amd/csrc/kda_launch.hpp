@@ -1,0 +1,43 @@
+// Host-side launchers, one per kernel family.  Arguments are validated by the
+// C entry points (api.cpp) before any launcher runs; launchers only pick the
+// template instance and grid, enqueue on `stream`, and return the launch
+// status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+hipError_t launch_conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w,
+                               uint16_t *const *conv_state, uint16_t *const *conv_snap,
+                               int n_seq, int rows, int heads, int head_dim, float eps_l2,
+                               uint16_t *y, int64_t ldy, float *q32, float *k32, float *v32,
+                               hipStream_t stream);
+
+hipError_t launch_kda_gate(const uint16_t *g_raw, int64_t ldg, const uint16_t *b_raw,
+                           int64_t ldb, const float *a_log, const float *dt_bias, int T,
+                           int heads, int head_dim, float *gate, float *beta,
+                           hipStream_t stream);
+
+hipError_t launch_gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate,
+                                int64_t ldo, const uint16_t *w, int T, int heads,
+                                int head_dim, float eps, uint16_t *out, int64_t ldy,
+                                hipStream_t stream);
+
+// K = 1 is single-token decode; the same kernel serves both entry points so
+// that K-row decode is bit-identical to K single-row calls.
+hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                                const float *beta, float *const *state, float *const *snap,
+                                float *core, int B, int K, int heads, int head_dim,
+                                float scale, hipStream_t stream);
+
+size_t prefill_workspace_bytes(int T_pad, int heads, int head_dim, int chunk);
+
+hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
+                              const float *gate, const float *beta, float *state,
+                              float *core, int T, int T_pad, int heads, int head_dim,
+                              int chunk, float scale, void *workspace, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,188 @@
+/*
+ * libkda — Kimi-Delta-Attention (KDA) core for AMD MI355X (gfx950).
+ *
+ * C ABI.  Every entry point:
+ *   - takes DEVICE pointers owned by the caller (the library allocates
+ *     nothing and keeps no pointer after returning);
+ *   - enqueues its kernels on `stream` and returns without synchronising
+ *     (stream-ordered, like any HIP launch);
+ *   - returns KDA_OK (0) or a negative kda_status; on error nothing has been
+ *     enqueued and kda_last_error() gives a message (thread-local);
+ *   - never writes outside the rows and buffers it documents.
+ *
+ * Types: bf16 values travel as uint16_t bit patterns; fp32 as float.  Row
+ * strides (`ld*`) are in ELEMENTS and must be multiples of 8 for bf16 rows and
+ * of 4 for fp32 rows; base pointers must be 16-byte aligned.  Channel
+ * c = h*head_dim + d everywhere.  Supported: head_dim in {16, 128}, prefill
+ * chunk in {16, 64}, conv kernel width 4.
+ *
+ * Cited passages are from the four API pages of the documented engine:
+ * "Glm5NextKdaWorkspace" (the buffer contract), "Glm5NextKdaLayer" (decode,
+ * decode_k, prefill, prefill_with_pad_fill), "Glm5NextLayer" (engine traits)
+ * and "Glm5NextKdaWeights" (the weights).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = -1,        /* a required pointer is NULL                      */
+    KDA_ERR_SHAPE = -2,       /* negative size, T_pad < T, T_pad % chunk != 0,
+                                 bad stride or misaligned pointer                */
+    KDA_ERR_UNSUPPORTED = -3, /* head_dim, chunk or conv width not built         */
+    KDA_ERR_ALIAS = -4,       /* an output aliases an input it must not          */
+    KDA_ERR_WORKSPACE = -5,   /* workspace smaller than kda_prefill_workspace_bytes */
+    KDA_ERR_HIP = -6          /* the HIP runtime rejected a launch               */
+} kda_status;
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char *kda_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * conv_silu_l2 — short causal depthwise conv + SiLU + per-head L2 of q and k.
+ * "Glm5NextKdaWorkspace" page, fields qkv_proj and conv_out (conv + SiLU with
+ * q|k L2-normalised, fused on decode); "Glm5NextKdaWeights" page, field conv
+ * ([conv_dim, conv_kernel] depthwise weight); "Glm5NextKdaLayer" page, decode
+ * and decode_k (the conv state is carried, snapshots after each row).
+ *
+ * n_seq sequences of `rows` rows each, sequence-major:
+ *   x          bf16 [n_seq*rows, conv_dim] (row stride ldx), conv_dim =
+ *              3*heads*head_dim, channels q|k|v.
+ *   w          bf16 [conv_dim, kc]; tap kc-1 multiplies the current row.
+ *   conv_state device array [n_seq] of pointers to bf16 [kc, conv_dim]: the
+ *              last kc pre-conv rows, newest last.  In/out: on return it holds
+ *              the window after the sequence's last row.
+ *   conv_snap  NULL, or a device array [n_seq*(rows-1)] of pointers to bf16
+ *              [kc, conv_dim]; entry s*(rows-1)+t receives the window after
+ *              row t of sequence s (t < rows-1).
+ *   y          bf16 [n_seq*rows, conv_dim] (row stride ldy): SiLU(conv), with
+ *              each head of the q and k sections divided by
+ *              sqrt(sum of squares + eps_l2), rounded once to bf16.
+ *   q32,k32,v32 NULL (all three) or fp32 [n_seq*rows, heads*head_dim] each:
+ *              the q, k, v sections of y widened exactly ("Glm5NextKdaWorkspace"
+ *              page, field q_f32).  Rows past n_seq*rows are not touched.
+ * y must not alias x (KDA_ERR_ALIAS).  rows == 0 or n_seq == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+int conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w,
+                 uint16_t *const *conv_state, uint16_t *const *conv_snap,
+                 int32_t n_seq, int32_t rows, int32_t heads, int32_t head_dim,
+                 int32_t kc, float eps_l2, uint16_t *y, int64_t ldy,
+                 float *q32, float *k32, float *v32, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_gate — bounded per-channel log-decay and beta.
+ * "Glm5NextKdaWorkspace" page, fields g_raw, gate and beta; "Glm5NextKdaWeights"
+ * page, fields a_log ([heads], per head) and dt_bias ([heads*head_dim], per
+ * channel).
+ *   g_raw   bf16 [T, heads*head_dim] (row stride ldg)
+ *   b_raw   bf16 [T, heads] (row stride ldb, b_proj output) or NULL
+ *   gate    fp32 [T_pad, heads, head_dim]: for t < T,
+ *           gate[t,h,d] = -exp(a_log[h]) * softplus(g_raw[t,h*D+d] + dt_bias[h*D+d]),
+ *           softplus(z) = log(1+e^z), z for z > 20.  exp(gate) is in (0, 1].
+ *   beta    fp32 [T_pad, heads]: beta[t,h] = 1/(1+exp(-b_raw[t,h])); not touched
+ *           when b_raw is NULL (then beta may be NULL).
+ * Rows t >= T of gate/beta are not touched.  T == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+int kda_gate(const uint16_t *g_raw, int64_t ldg, const uint16_t *b_raw,
+             int64_t ldb, const float *a_log, const float *dt_bias, int32_t T,
+             int32_t heads, int32_t head_dim, float *gate, float *beta,
+             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_prefill — chunked prefill of the KDA recurrence from a carried state.
+ * "Glm5NextKdaLayer" page, prefill (chunked prefill over t tokens from the
+ * carried state) and prefill_with_pad_fill (the chunk kernels guard past T:
+ * the padded tail may hold anything); "Glm5NextKdaWorkspace" page, fields
+ * q_f32/k_f32/v_f32, gate, beta, core (shapes; buffers padded to whole chunks).
+ *
+ * Per head, with S[i][j] (i = key channel, j = value channel), each token t:
+ *   S <- diag(exp(gate_t)) S;  u = beta_t (v_t - S^T k_t);  S <- S + k_t u^T;
+ *   core_t = scale * S^T q_t.
+ * q and k are used as given (pre-normalised contract, no re-normalisation).
+ *   q,k,v,gate fp32 [T_pad, heads, head_dim]; beta fp32 [T_pad, heads].
+ *   state      fp32 [heads, head_dim, head_dim], in/out (updated in place).
+ *   core       fp32 [T_pad, heads, head_dim]; rows t < T written, rows >= T
+ *              not touched.
+ *   Rows t >= T of every input are never used: any bits (0, 1e30, NaN) give
+ *   bitwise the same core rows < T and state.  T_pad % chunk == 0, T_pad >= T.
+ *   workspace  device scratch of at least kda_prefill_workspace_bytes(...)
+ *              bytes, 256-byte aligned; contents on return are unspecified.
+ * core must not alias an input or state (KDA_ERR_ALIAS).  T == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+size_t kda_prefill_workspace_bytes(int32_t T_pad, int32_t heads,
+                                   int32_t head_dim, int32_t chunk);
+
+int kda_prefill(const float *q, const float *k, const float *v,
+                const float *gate, const float *beta, float *state, float *core,
+                int32_t T, int32_t T_pad, int32_t heads, int32_t head_dim,
+                int32_t chunk, float scale, void *workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_decode — one token for each of B independent sequences.
+ * "Glm5NextKdaLayer" page, decode (single-token decode; q/k arrive already
+ * normalised from the fused conv and must not be re-normalised; the state is
+ * updated in place).  Same step as kda_prefill, one row.
+ *   qkv    bf16 [B, 3*heads*head_dim] (row stride ldqkv): the conv_out rows,
+ *          q | k | v sections.
+ *   gate   fp32 [B, heads, head_dim]; beta fp32 [B, heads].
+ *   state  device array [B] of pointers to fp32 [heads, head_dim, head_dim],
+ *          in/out.  Entries must be distinct.
+ *   core   fp32 [B, heads, head_dim].
+ * B == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+int kda_decode(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+               const float *beta, float *const *state, float *core, int32_t B,
+               int32_t heads, int32_t head_dim, float scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_decode_k — K consecutive tokens of each of B sequences (speculative
+ * verify), with the state after every row but the last copied out.
+ * "Glm5NextKdaLayer" page, decode_k: the recurrence walks one token at a
+ * time exactly as decode does and the result is bit-identical to K serial
+ * kda_decode calls; snapshots[t] receives the state AFTER row t, K-1 of them
+ * or none.
+ *   qkv    bf16 [B*K, 3*heads*head_dim], sequence-major (row b*K + t).
+ *   gate   fp32 [B*K, heads, head_dim]; beta fp32 [B*K, heads].
+ *   state  device array [B] of pointers to fp32 [heads, head_dim, head_dim],
+ *          in/out: on return the state after row K-1.
+ *   snap   NULL or device array [B*(K-1)] of pointers to fp32
+ *          [heads, head_dim, head_dim]; entry b*(K-1)+t = state after row t.
+ *          Snapshot buffers must not overlap any state.
+ *   core   fp32 [B*K, heads, head_dim].
+ * B == 0 or K == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+int kda_decode_k(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                 const float *beta, float *const *state, float *const *snap,
+                 float *core, int32_t B, int32_t K, int32_t heads,
+                 int32_t head_dim, float scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * gated_rmsnorm — sigmoid-gated RMSNorm of the core output, per (token, head).
+ * "Glm5NextKdaWorkspace" page, fields core, out_gate and o_norm_out;
+ * "Glm5NextKdaWeights" page, field o_norm ([head_dim] bf16).
+ *   core     fp32 [T, heads*head_dim] (row stride ldc)
+ *   out_gate bf16 [T, heads*head_dim] (row stride ldo)
+ *   w        bf16 [head_dim]
+ *   out      bf16 [T, heads*head_dim] (row stride ldy):
+ *            out = bf16(x / sqrt(mean_d x^2 + eps) * w[d] * sigmoid(out_gate)).
+ * out must not alias out_gate or core (KDA_ERR_ALIAS).  T == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+int gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate,
+                  int64_t ldo, const uint16_t *w, int32_t T, int32_t heads,
+                  int32_t head_dim, float eps, uint16_t *out, int64_t ldy,
+                  hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every symbol include/kda.h declares, and
+rejects bad arguments with the documented status codes.  Every call here
+returns before any HIP call (validation only), so it runs without a GPU; the
+pointer values are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIAS, E_WS = 0, -1, -2, -3, -4, -5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gated_delta_rule_bounded_amd as kda
+    return kda._lib.lib
+
+
+def _declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", txt)) - {"defined"})
+
+
+def test_header_declares_the_six_calls():
+    names = _declared_functions()
+    for n in ("conv_silu_l2", "kda_gate", "kda_prefill", "kda_decode", "kda_decode_k",
+              "gated_rmsnorm", "kda_last_error", "kda_prefill_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import gated_delta_rule_bounded_amd as kda
+    so = ctypes.CDLL(kda.library_path())
+    for n in _declared_functions():
+        assert hasattr(so, n), f"libkda.so does not export {n}"
+    assert set(_declared_functions()) == set(kda._lib.SYMBOLS)
+
+
+A = 1 << 20          # fake, 256-byte aligned device addresses: never dereferenced
+B = 1 << 32
+C = 1 << 36
+Dp = 1 << 40
+E = 1 << 44
+F = 1 << 48
+
+
+def test_prefill_validation(lib):
+    ws = lib.kda_prefill_workspace_bytes(4096, 32, 128, 64)
+    assert ws == 2 * (4096 // 64) * 32 * 64 * 64 * 4
+    assert lib.kda_prefill_workspace_bytes(100, 32, 128, 64) == 0     # T_pad % chunk
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("q", A), ("k", B), ("v", C), ("gate", Dp), ("beta", E), ("state", F), ("core", 1 << 52),
+        ("T", 57), ("T_pad", 64), ("H", 2), ("D", 16), ("C", 16), ("scale", 1.0),
+        ("ws", 1 << 56), ("wsb", 1 << 30), ("stream", None))]
+    assert lib.kda_prefill(*args(D=64)) == E_UNSUP
+    assert lib.kda_prefill(*args(C=32)) == E_UNSUP
+    assert lib.kda_prefill(*args(T_pad=48)) == E_SHAPE
+    assert lib.kda_prefill(*args(T_pad=72)) == E_SHAPE
+    assert lib.kda_prefill(*args(T=-1)) == E_SHAPE
+    assert lib.kda_prefill(*args(T=0, q=None)) == OK                   # no-op before pointer checks
+    assert lib.kda_prefill(*args(q=None)) == E_NULL
+    assert lib.kda_prefill(*args(wsb=100)) == E_WS
+    assert lib.kda_prefill(*args(core=A)) == E_ALIAS                    # core == q
+    assert lib.kda_prefill(*args(state=C + 64)) == E_ALIAS              # state inside v
+    assert lib.kda_prefill(*args(q=A + 4)) == E_SHAPE                   # misaligned
+    err = lib.kda_last_error().decode()
+    assert "misaligned" in err
+
+
+def test_decode_validation(lib):
+    base = dict(qkv=A, ld=3 * 2 * 128, gate=B, beta=C, state=Dp, core=E, Bn=4, H=2, D=128,
+                scale=1.0, stream=None)
+    order = ("qkv", "ld", "gate", "beta", "state", "core", "Bn", "H", "D", "scale", "stream")
+    call = lambda **kw: lib.kda_decode(*[{**base, **kw}[n] for n in order])
+    assert call(D=64) == E_UNSUP
+    assert call(Bn=-1) == E_SHAPE
+    assert call(Bn=0, qkv=None) == OK
+    assert call(state=None) == E_NULL
+    assert call(ld=100) == E_SHAPE
+    assert call(core=B) == E_ALIAS
+
+
+def test_decode_k_validation(lib):
+    base = dict(qkv=A, ld=3 * 2 * 16, gate=B, beta=C, state=Dp, snap=F, core=E, Bn=4, K=4,
+                H=2, D=16, scale=1.0, stream=None)
+    order = ("qkv", "ld", "gate", "beta", "state", "snap", "core", "Bn", "K", "H", "D", "scale",
+             "stream")
+    call = lambda **kw: lib.kda_decode_k(*[{**base, **kw}[n] for n in order])
+    assert call(K=-1) == E_SHAPE
+    assert call(K=0, qkv=None) == OK
+    assert call(snap=Dp) == E_ALIAS
+    assert call(gate=None) == E_NULL
+
+
+def test_stage_validation(lib):
+    # conv: kc must be 4; y must not alias x; q32/k32/v32 all or none
+    conv = lambda **kw: lib.conv_silu_l2(*[{**dict(
+        x=A, ldx=96, w=B, st=None, snap=None, n=1, rows=8, H=2, D=16, kc=4, eps=1e-6, y=C,
+        ldy=96, q32=None, k32=None, v32=None, stream=None), **kw}[n] for n in (
+        "x", "ldx", "w", "st", "snap", "n", "rows", "H", "D", "kc", "eps", "y", "ldy", "q32",
+        "k32", "v32", "stream")])
+    assert conv(kc=3) == E_UNSUP
+    assert conv(y=A) == E_ALIAS
+    assert conv(q32=Dp) == E_NULL
+    assert conv(ldx=95) == E_SHAPE
+    assert conv(rows=0, x=None) == OK
+    # gate
+    gate = lambda **kw: lib.kda_gate(*[{**dict(
+        g=A, ldg=32, b=None, ldb=0, a=B, dt=C, T=5, H=2, D=16, gate=Dp, beta=None,
+        stream=None), **kw}[n] for n in ("g", "ldg", "b", "ldb", "a", "dt", "T", "H", "D",
+                                          "gate", "beta", "stream")])
+    assert gate(D=32) == E_UNSUP
+    assert gate(b=E) == E_NULL          # b_raw without beta
+    assert gate(gate=A) == E_ALIAS
+    assert gate(T=0, g=None) == OK
+    # rmsnorm
+    norm = lambda **kw: lib.gated_rmsnorm(*[{**dict(
+        core=A, ldc=32, og=B, ldo=32, w=C, T=5, H=2, D=16, eps=1e-5, out=Dp, ldy=32,
+        stream=None), **kw}[n] for n in ("core", "ldc", "og", "ldo", "w", "T", "H", "D", "eps",
+                                          "out", "ldy", "stream")])
+    assert norm(out=B) == E_ALIAS
+    assert norm(w=None) == E_NULL
+    assert norm(ldo=30) == E_SHAPE
+    assert norm(T=0, core=None) == OK

@@ -1,0 +1,161 @@
+"""kda_decode / kda_decode_k on the GPU.
+
+Against the oracle: max relative error < 2e-3 on core and states (fp32 work).
+decode_k against K serial decode calls: bit-identical core, final state and
+every snapshot ("Glm5NextKdaLayer" page, decode_k).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from conftest import relerr
+from kda_cases import THREADS, cuda, say
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _steps(B, H, D, n_steps, seed):
+    """Per step: qkv bf16 [B, 3HD] (q/k unit-normalised), gate fp32 [B,H,D],
+    beta fp32 [B,H] (gate/beta from the oracle's gate on the seeded draws)."""
+    a_log, dt = workloads.gate_params(H, D, seed)
+    out = []
+    for s in range(n_steps):
+        r = workloads.decode_step_raw(B, H, D, seed + 1 + s)
+        g, b = oracle.kda_gate(r["g_raw"], a_log, dt, H, D, b_raw=r["b_raw"])
+        out.append(dict(qkv=r["qkv"], gate=g.astype(np.float32), beta=b.astype(np.float32)))
+    return out
+
+
+def _oracle_seq(steps, S0_b, b, H, D, scale):
+    """Oracle over the steps of sequence b: returns core [n, H, D], S, snaps."""
+    qkv = np.stack([s["qkv"][b].double().numpy() for s in steps])        # [n, 3HD]
+    n = qkv.shape[0]
+    q = qkv[:, : H * D].reshape(n, H, D)
+    k = qkv[:, H * D: 2 * H * D].reshape(n, H, D)
+    v = qkv[:, 2 * H * D:].reshape(n, H, D)
+    g = np.stack([s["gate"][b] for s in steps])
+    bt = np.stack([s["beta"][b] for s in steps])
+    return oracle.kda_recurrence(q, k, v, g, bt, S0_b, scale, snapshots=True, threads=THREADS)
+
+
+@pytest.mark.parametrize("B,H,D,n_steps", [(3, 2, 16, 8), (4, 4, 128, 5)])
+def test_decode_matches_oracle(B, H, D, n_steps):
+    import gated_delta_rule_bounded_amd as kda
+    scale = D ** -0.5
+    S0 = workloads.state(H, D, 0.05, 2002, B=B)
+    steps = _steps(B, H, D, n_steps, 3000)
+    st = cuda(S0)
+    table = kda.ptr_table(st)
+    cores = []
+    say("decode", B, H, D, n_steps)
+    for s in steps:
+        core = torch.empty(B, H, D, device="cuda")
+        kda.kda_decode(cuda(s["qkv"], torch.bfloat16), cuda(s["gate"]), cuda(s["beta"]), table,
+                       core, B=B, heads=H, head_dim=D, scale=scale)
+        cores.append(core)
+    torch.cuda.synchronize()
+    got_core = torch.stack(cores, 1).cpu().numpy()      # [B, n, H, D]
+    got_S = st.cpu().numpy()
+    for b in range(B):
+        ref_core, ref_S, _ = _oracle_seq(steps, S0[b], b, H, D, scale)
+        assert relerr(got_core[b], ref_core) < TOL
+        assert relerr(got_S[b], ref_S) < TOL
+
+
+def _decode_k_vs_serial(B, K, H, D, seed, snapshots=True):
+    import gated_delta_rule_bounded_amd as kda
+    scale = D ** -0.5
+    S0 = workloads.state(H, D, 0.05, seed, B=B)
+    rows = _steps(B, H, D, K, seed)                        # K steps of B sequences
+    # sequence-major [B*K] layout for decode_k
+    qkv = torch.stack([r["qkv"] for r in rows], 1).reshape(B * K, -1)
+    gate = np.stack([r["gate"] for r in rows], 1).reshape(B * K, H, D)
+    beta = np.stack([r["beta"] for r in rows], 1).reshape(B * K, H)
+
+    st_k = cuda(S0)
+    snaps = torch.full((B * max(K - 1, 1), H, D, D), float("nan"), device="cuda")
+    core_k = torch.empty(B * K, H, D, device="cuda")
+    say("decode_k", B, K, H, D)
+    kda.kda_decode_k(cuda(qkv, torch.bfloat16), cuda(gate), cuda(beta), kda.ptr_table(st_k),
+                     core_k, B=B, K=K, heads=H, head_dim=D, scale=scale,
+                     snap=kda.ptr_table(snaps) if snapshots and K > 1 else None)
+
+    st_s = cuda(S0)
+    tab_s = kda.ptr_table(st_s)
+    serial_core, serial_states = [], []
+    for t, r in enumerate(rows):
+        c = torch.empty(B, H, D, device="cuda")
+        kda.kda_decode(cuda(r["qkv"], torch.bfloat16), cuda(r["gate"]), cuda(r["beta"]), tab_s, c,
+                       B=B, heads=H, head_dim=D, scale=scale)
+        serial_core.append(c)
+        serial_states.append(st_s.clone())
+    torch.cuda.synchronize()
+    ck = core_k.view(B, K, H, D)
+    for t in range(K):
+        assert torch.equal(ck[:, t].view(torch.int32), serial_core[t].view(torch.int32))
+    assert torch.equal(st_k.view(torch.int32), st_s.view(torch.int32))
+    if snapshots and K > 1:
+        sn = snaps.view(B, K - 1, H, D, D)
+        for t in range(K - 1):
+            assert torch.equal(sn[:, t].view(torch.int32), serial_states[t].view(torch.int32))
+    return rows, S0, ck.cpu().numpy(), st_k.cpu().numpy(), snaps
+
+
+@pytest.mark.parametrize("B,K,H,D", [(3, 4, 2, 16), (5, 4, 4, 128), (2, 1, 4, 128), (2, 7, 2, 128)])
+def test_decode_k_bitwise_equals_serial_decode(B, K, H, D):
+    rows, S0, ck, sk, _ = _decode_k_vs_serial(B, K, H, D, 4000 + K)
+    for b in range(B):
+        ref_core, ref_S, _ = _oracle_seq(rows, S0[b], b, H, D, D ** -0.5)
+        assert relerr(ck[b], ref_core) < TOL
+        assert relerr(sk[b], ref_S) < TOL
+
+
+def test_decode_k_full_size_b64_k4():
+    """Speculative-verify workload: 64 sequences, K=4, H=32, D=128, three
+    snapshots per sequence; bitwise vs 4 serial decodes, oracle on a sample."""
+    B, K, H, D = 64, 4, 32, 128
+    rows, S0, ck, sk, snaps = _decode_k_vs_serial(B, K, H, D, 2003)
+    sn = snaps.view(B, K - 1, H, D, D)
+    for b in (0, 37, 63):
+        ref_core, ref_S, ref_snaps = _oracle_seq(rows, S0[b], b, H, D, D ** -0.5)
+        assert relerr(ck[b], ref_core) < TOL
+        assert relerr(sk[b], ref_S) < TOL
+        for t in range(K - 1):
+            assert relerr(sn[b, t].cpu().numpy(), ref_snaps[t]) < TOL
+
+
+def test_decode_full_size_b256():
+    """Batched decode workload: 256 sequences, H=32, D=128, state ~ N(0, 0.05),
+    64 steps on the GPU; the oracle follows 3 sampled sequences through all 64
+    steps and all 256 sequences through the first step."""
+    import gated_delta_rule_bounded_amd as kda
+    B, H, D, n_steps = 256, 32, 128, 64
+    scale = D ** -0.5
+    S0 = workloads.state(H, D, 0.05, 2002, B=B)
+    steps = _steps(B, H, D, n_steps, 3002)
+    st = cuda(S0)
+    table = kda.ptr_table(st)
+    say("decode full", B, n_steps)
+    first_S = None
+    cores = torch.empty(n_steps, B, H, D, device="cuda")
+    for i, s in enumerate(steps):
+        kda.kda_decode(cuda(s["qkv"], torch.bfloat16), cuda(s["gate"]), cuda(s["beta"]), table,
+                       cores[i], B=B, heads=H, head_dim=D, scale=scale)
+        if i == 0:
+            first_S = st.cpu().numpy()
+    torch.cuda.synchronize()
+    got = cores.cpu().numpy()
+    # step 1, every sequence
+    for b in range(B):
+        ref_core, ref_S, _ = _oracle_seq(steps[:1], S0[b], b, H, D, scale)
+        assert relerr(got[0, b], ref_core[0]) < TOL
+        assert relerr(first_S[b], ref_S) < TOL
+    # 64 steps, sampled sequences
+    final = st.cpu().numpy()
+    for b in (0, 101, 255):
+        ref_core, ref_S, _ = _oracle_seq(steps, S0[b], b, H, D, scale)
+        assert relerr(got[:, b], ref_core) < TOL
+        assert relerr(final[b], ref_S) < TOL

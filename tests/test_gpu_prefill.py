@@ -1,0 +1,143 @@
+"""kda_prefill on the GPU against the token-serial oracle.
+
+Tolerance: max relative error (max |gpu - oracle| / max |oracle|, per tensor)
+below 2e-3 on core rows < T and on the carried state (fp32 work).  Poison in
+the pad tail must change nothing, bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from conftest import relerr
+from kda_cases import core_case, gpu_prefill, oracle_core, say
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+@pytest.mark.parametrize("T,T_pad,C,state_std", [
+    (64, 64, 16, 0.0), (64, 64, 16, 0.1),        # the tiny workload, both initial states
+    (57, 64, 16, 0.1), (64, 80, 16, 0.1),         # ragged tail; a wholly padded chunk
+    (64, 64, 64, 0.1), (50, 128, 64, 0.1),
+])
+def test_prefill_tiny_d16(T, T_pad, C, state_std):
+    H, D = 2, 16
+    case = core_case(T, H, D, 1000, state_std)
+    scale = D ** -0.5
+    say("prefill tiny", T, T_pad, C, state_std)
+    core, S = gpu_prefill(case, T, T_pad, C, scale)
+    ref_core, ref_S = oracle_core(case, scale)
+    assert relerr(core[:T], ref_core) < TOL
+    assert relerr(S, ref_S) < TOL
+    assert np.all(core[T:] == 7.0), "core rows >= T must not be written"
+
+
+@pytest.mark.parametrize("T,T_pad,C", [(300, 320, 64), (300, 304, 16), (128, 128, 64), (1, 64, 64)])
+def test_prefill_d128_ragged(T, T_pad, C):
+    H, D = 4, 128
+    case = core_case(T, H, D, 1101, 0.05, qkv_bf16=True)
+    scale = D ** -0.5
+    say("prefill d128", T, T_pad, C)
+    core, S = gpu_prefill(case, T, T_pad, C, scale)
+    ref_core, ref_S = oracle_core(case, scale)
+    assert relerr(core[:T], ref_core) < TOL
+    assert relerr(S, ref_S) < TOL
+    for h in range(H):
+        assert relerr(core[:T, h], ref_core[:, h]) < TOL
+        assert relerr(S[h], ref_S[h]) < TOL
+    assert np.all(core[T:] == 7.0)
+
+
+@pytest.mark.parametrize("fill", [1e30, float("nan"), -3.0])
+@pytest.mark.parametrize("T,T_pad,C", [(57, 64, 16), (200, 256, 64), (64, 128, 64)])
+def test_prefill_poisoned_tail_is_bitwise_inert(T, T_pad, C, fill):
+    H, D = (2, 16) if C == 16 else (4, 128)
+    case = core_case(T, H, D, 1202, 0.1)
+    say("poison", T, T_pad, C, fill)
+    core0, S0 = gpu_prefill(case, T, T_pad, C, D ** -0.5, fill=0.0)
+    core1, S1 = gpu_prefill(case, T, T_pad, C, D ** -0.5, fill=fill)
+    assert np.array_equal(core0[:T].view(np.int32), core1[:T].view(np.int32))
+    assert np.array_equal(S0.view(np.int32), S1.view(np.int32))
+    assert np.all(core1[T:] == 7.0)
+
+
+@pytest.mark.parametrize("a", [1, 63, 64, 100])
+def test_prefill_split_invariance(a):
+    """[0,T) in one call equals [0,a) then [a,T) from the carried state."""
+    T, H, D, C = 200, 4, 128, 64
+    case = core_case(T, H, D, 1303, 0.05)
+    scale = D ** -0.5
+    say("split", a)
+    core_all, S_all = gpu_prefill(case, T, 256, C, scale)
+    first = {n: case[n][:a] for n in ("q", "k", "v", "gate", "beta")}
+    first["S0"] = case["S0"]
+    c1, S1 = gpu_prefill(first, a, ((a + C - 1) // C) * C, C, scale)
+    second = {n: case[n][a:] for n in ("q", "k", "v", "gate", "beta")}
+    second["S0"] = S1
+    c2, S2 = gpu_prefill(second, T - a, ((T - a + C - 1) // C) * C, C, scale)
+    ref_core, ref_S = oracle_core(case, scale)
+    assert relerr(np.concatenate([c1[:a], c2[:T - a]]), ref_core) < TOL
+    assert relerr(S2, ref_S) < TOL
+    assert relerr(S2, S_all) < TOL
+
+
+def test_prefill_unnormalised_qk_used_as_given():
+    """q, k scaled by 1.01 (not unit): the kernel must not re-normalise."""
+    T, H, D, C = 130, 2, 128, 64
+    case = core_case(T, H, D, 1404, 0.05, qk_scale=1.01)
+    say("prenorm contract")
+    core, S = gpu_prefill(case, T, 192, C, 1.0)
+    ref_core, ref_S = oracle_core(case, 1.0)
+    assert relerr(core[:T], ref_core) < TOL
+    assert relerr(S, ref_S) < TOL
+
+
+@pytest.mark.parametrize("C", [16, 64])
+def test_prefill_steep_decay_takes_exact_diagonal_path(C):
+    """Gates scaled so some 16-row blocks decay by more than 2^86 inside the
+    block: the factored diagonal would overflow fp32; the exact pairwise path
+    must still match the oracle."""
+    T, H, D = 128, 2, 128
+    case = core_case(T, H, D, 1505, 0.05, gate_scale=1.6)
+    g2 = case["gate"] / np.log(2)           # log2 units, as the kernel measures spans
+    spans = np.array([[(-g2[16 * b + 1:16 * b + 16, h].sum(0)).max() for h in range(H)]
+                      for b in range(T // 16)])
+    assert (spans > 86.0).any() and (spans <= 86.0).any(), "need both diagonal paths"
+    say("steep decay", C)
+    core, S = gpu_prefill(case, T, T, C, D ** -0.5)
+    ref_core, ref_S = oracle_core(case, D ** -0.5)
+    assert np.all(np.isfinite(core[:T])) and np.all(np.isfinite(S))
+    assert relerr(core[:T], ref_core) < TOL
+    assert relerr(S, ref_S) < TOL
+
+
+def test_prefill_empty_is_noop():
+    import gated_delta_rule_bounded_amd as kda
+    H, D = 2, 16
+    st = torch.randn(H, D, D, device="cuda")
+    before = st.clone()
+    z = torch.zeros(64, H, D, device="cuda")
+    core = torch.full((64, H, D), 7.0, device="cuda")
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(64, H, D, 16), dtype=torch.uint8, device="cuda")
+    kda.kda_prefill(z, z, z, z, torch.zeros(64, H, device="cuda"), st, core, ws, T=0, T_pad=64,
+                    heads=H, head_dim=D, chunk=16, scale=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(st, before) and bool((core == 7.0).all())
+
+
+@pytest.mark.parametrize("T,T_pad,fill", [(4096, 4096, 0.0), (4059, 4096, 1e30), (4096, 4160, float("nan"))])
+def test_prefill_full_size_h32_d128(T, T_pad, fill):
+    """The chunked-prefill workload at full size: T=4096, H=32, D=128, chunk 64,
+    q/k/v generated in bf16 and widened, state ~ N(0, 0.05); every output
+    element against the oracle."""
+    H, D, C = 32, 128, 64
+    case = core_case(4096, H, D, 1001, 0.05, qkv_bf16=True)
+    scale = D ** -0.5
+    say("prefill full", T, T_pad, fill)
+    core, S = gpu_prefill(case, T, T_pad, C, scale, fill=fill)
+    ref_core, ref_S = oracle_core(case, scale, T=T)
+    e_core, e_S = relerr(core[:T], ref_core), relerr(S, ref_S)
+    print(f"relerr core {e_core:.3e} state {e_S:.3e}")
+    assert e_core < TOL and e_S < TOL
+    if T_pad > T:
+        assert np.all(core[T:] == 7.0)

@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA core on one MI355X.
+
+Step (the timed unit): one chunked prefill of the KDA core over the workload
+T=4096 tokens, 32 heads, head_dim 128, chunk 64, from an fp32 carried state
+~ N(0, 0.05): kda_prefill_prepare then kda_prefill_forward (together exactly
+kda_prefill) on inputs already resident in HBM.  value = T / step time.
+
+Also reported on the same JSON line (measured after the timed steps):
+  decode    B=256 sequences x 64 steps, state [256,32,128,128] fp32: state
+            read+write bytes / median step time (the metric's second half);
+  decode_k  B=64, K=4 with 3 snapshots per sequence (conv decode-K + kda_decode_k);
+  stages    conv_silu_l2 / kda_gate / gated_rmsnorm at T=8192 (block shapes);
+  roofline  for the dominant prefill kernel, from HIP events on the stream
+            the kernels run on;
+  cpu_baseline  the fp64 oracle on the same prefill workload, on host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "KDA prefill tokens/s (H=32,D=128) + decode state HBM GB/s, 1 MI355X"
+PEAK_FP32_MFMA = 157.3e12     # MI355X dense fp32 matrix peak, FLOP/s
+PEAK_HBM = 8.0e12             # MI355X HBM3E peak, B/s
+
+T, H, D, C = 4096, 32, 128, 64
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def cpu_threads():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+# algorithmic work per token and head (see the prefill kernel header)
+def fwd_flops_per_token_head(D, C):
+    # (K e^G) S, (Q e^G) S, (K e^{G_C-G})^T U: 2*D*D each; Tb X and P U over
+    # the lower triangle: (C+1)*D each
+    return 6 * D * D + 2 * (C + 1) * D
+
+
+def prep_flops_per_token_head(D, C):
+    # A strictly lower (C-1)*D, P with diagonal (C+1)*D, triangular inverse C^2/3
+    return 2 * C * D + C * C / 3.0
+
+
+def fwd_bytes(T, H, D, C):
+    # read q, k, v, gate, Tb, P; write core; state read + write
+    return T * H * (4 * D * 4 + 2 * C * 4 + D * 4) + 2 * H * D * D * 4
+
+
+def prep_bytes(T, H, D, C):
+    # read q, k, gate, beta; write Tb, P
+    return T * H * (3 * D * 4 + 4 + 2 * C * 4)
+
+
+def ev():
+    return torch.cuda.Event(enable_timing=True)
+
+
+def setup_prefill(kda, dev):
+    raw = workloads.core_raw(T, H, D, workloads.SEED_INPUT + 1, qkv_bf16=True)
+    q, k, v = (torch.from_numpy(raw[n]).to(dev) for n in ("q", "k", "v"))
+    gate = torch.empty(T, H, D, device=dev)
+    beta = torch.empty(T, H, device=dev)
+    kda.kda_gate(workloads.to_bf16(raw["g_raw"]).to(dev), torch.from_numpy(raw["a_log"]).to(dev),
+                 torch.from_numpy(raw["dt_bias"]).to(dev), gate, T=T, heads=H, head_dim=D,
+                 b_raw=workloads.to_bf16(raw["b_raw"]).to(dev), beta=beta)
+    state = torch.from_numpy(workloads.state(H, D, 0.05, workloads.SEED_STATE + 1)).to(dev)
+    core = torch.empty(T, H, D, device=dev)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(T, H, D, C), dtype=torch.uint8, device=dev)
+    return dict(q=q, k=k, v=v, gate=gate, beta=beta, state=state, core=core, ws=ws, raw=raw)
+
+
+def prefill_step(kda, P, e0=None, e1=None, e2=None):
+    kw = dict(T=T, T_pad=T, heads=H, head_dim=D, chunk=C)
+    if e0 is not None:
+        e0.record()
+    kda.kda_prefill_prepare(P["q"], P["k"], P["gate"], P["beta"], P["ws"], **kw)
+    if e1 is not None:
+        e1.record()
+    kda.kda_prefill_forward(P["q"], P["k"], P["v"], P["gate"], P["state"], P["core"], P["ws"],
+                            scale=D ** -0.5, **kw)
+    if e2 is not None:
+        e2.record()
+
+
+def bench_decode(kda, dev, n_steps=64, n_inputs=8):
+    B = 256
+    a_log, dt = workloads.gate_params(H, D, workloads.SEED_INPUT + 2)
+    a_log, dt = torch.from_numpy(a_log).to(dev), torch.from_numpy(dt).to(dev)
+    steps = []
+    for s in range(n_inputs):
+        r = workloads.decode_step_raw(B, H, D, workloads.SEED_INPUT + 20 + s)
+        g = torch.empty(B, H, D, device=dev)
+        b = torch.empty(B, H, device=dev)
+        kda.kda_gate(workloads.to_bf16(r["g_raw"]).to(dev), a_log, dt, g, T=B, heads=H,
+                     head_dim=D, b_raw=workloads.to_bf16(r["b_raw"]).to(dev), beta=b)
+        steps.append((r["qkv"].to(dev), g, b))
+    state = torch.from_numpy(workloads.state(H, D, 0.05, workloads.SEED_STATE + 2, B=B)).to(dev)
+    table = kda.ptr_table(state)
+    core = torch.empty(B, H, D, device=dev)
+
+    def one(i):
+        qkv, g, b = steps[i % n_inputs]
+        kda.kda_decode(qkv, g, b, table, core, B=B, heads=H, head_dim=D, scale=D ** -0.5)
+
+    for i in range(4):
+        one(i)
+    evs = [(ev(), ev()) for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    for i in range(n_steps):
+        evs[i][0].record()
+        one(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    t = float(np.median(ms)) * 1e-3
+    state_bytes = 2 * B * H * D * D * 4
+    io_bytes = B * (3 * H * D * 2 + H * D * 4 + H * 4 + H * D * 4)
+    return dict(config="decode B=256 H=32 D=128, 64 steps, fp32 state 537 MB",
+                state_GBps=state_bytes / t / 1e9, total_GBps=(state_bytes + io_bytes) / t / 1e9,
+                ms_per_step_median=t * 1e3, tokens_per_s=B / t,
+                hbm_frac=(state_bytes + io_bytes) / t / PEAK_HBM,
+                state_bytes_per_step=state_bytes)
+
+
+def bench_decode_k(kda, dev, n_calls=32, n_sets=4):
+    B, K = 64, 4
+    cd = 3 * H * D
+    a_log, dt = workloads.gate_params(H, D, workloads.SEED_INPUT + 3)
+    a_log, dt = torch.from_numpy(a_log).to(dev), torch.from_numpy(dt).to(dev)
+    conv = workloads.conv_raw(B * K, H, D, 4, workloads.SEED_INPUT + 3, n_seq=B)
+    x = conv["x"].to(dev)
+    w = conv["w"].to(dev)
+    g_raw = workloads.to_bf16(np.random.default_rng(31).standard_normal((B * K, H * D))).to(dev)
+    b_raw = workloads.to_bf16(np.random.default_rng(32).standard_normal((B * K, H))).to(dev)
+    gate = torch.empty(B * K, H, D, device=dev)
+    beta = torch.empty(B * K, H, device=dev)
+    kda.kda_gate(g_raw, a_log, dt, gate, T=B * K, heads=H, head_dim=D, b_raw=b_raw, beta=beta)
+    # rotate state sets so the 134 MB working set does not sit in the 256 MB cache
+    sets = []
+    for s in range(n_sets):
+        st = torch.from_numpy(workloads.state(H, D, 0.05, workloads.SEED_STATE + 30 + s, B=B)).to(dev)
+        cs = conv["state"].to(dev).clone()
+        sets.append((st, kda.ptr_table(st), cs, kda.ptr_table(cs)))
+    snaps = torch.empty(B * (K - 1), H, D, D, device=dev)
+    snap_tab = kda.ptr_table(snaps)
+    csnaps = torch.empty(B * (K - 1), 4, cd, dtype=torch.bfloat16, device=dev)
+    csnap_tab = kda.ptr_table(csnaps)
+    y = torch.empty(B * K, cd, dtype=torch.bfloat16, device=dev)
+    core = torch.empty(B * K, H, D, device=dev)
+
+    def one(i, e=None):
+        st, tab, cs, ctab = sets[i % n_sets]
+        if e:
+            e[0].record()
+        kda.conv_silu_l2(x, w, y, n_seq=B, rows=K, heads=H, head_dim=D, conv_state=ctab,
+                         conv_snap=csnap_tab)
+        if e:
+            e[1].record()
+        kda.kda_decode_k(y, gate, beta, tab, core, B=B, K=K, heads=H, head_dim=D,
+                         scale=D ** -0.5, snap=snap_tab)
+        if e:
+            e[2].record()
+
+    for i in range(n_sets):
+        one(i)
+    evs = [(ev(), ev(), ev()) for _ in range(n_calls)]
+    torch.cuda.synchronize()
+    for i in range(n_calls):
+        one(i, evs[i])
+    torch.cuda.synchronize()
+    t_conv = float(np.median([a.elapsed_time(b) for a, b, _ in evs])) * 1e-3
+    t_dk = float(np.median([b.elapsed_time(c) for _, b, c in evs])) * 1e-3
+    state_b = B * H * D * D * 4 * (2 + (K - 1))                 # read, final write, K-1 snapshots
+    io_b = B * K * (cd * 2 + H * D * 4 + H * 4 + H * D * 4)     # qkv, gate, beta, core
+    conv_b = B * (4 * cd * 2) * (2 + (K - 1)) + B * K * cd * 2 * 2 + cd * 4 * 2
+    return dict(config="decode_k B=64 K=4 H=32 D=128, 3 snapshots/seq, conv decode-K with snapshots",
+                decode_k_ms=t_dk * 1e3, decode_k_GBps=(state_b + io_b) / t_dk / 1e9,
+                decode_k_hbm_frac=(state_b + io_b) / t_dk / PEAK_HBM,
+                conv_ms=t_conv * 1e3, conv_GBps=conv_b / t_conv / 1e9,
+                verify_tokens_per_s=B * K / (t_dk + t_conv))
+
+
+def bench_stages(kda, dev, reps=10):
+    Tb = 8192
+    cd = 3 * H * D
+    conv = workloads.conv_raw(Tb, H, D, 4, workloads.SEED_INPUT + 4, n_seq=1)
+    x, w = conv["x"].to(dev), conv["w"].to(dev)
+    cs = torch.zeros(1, 4, cd, dtype=torch.bfloat16, device=dev)
+    ctab = kda.ptr_table(cs)
+    y = torch.empty(Tb, cd, dtype=torch.bfloat16, device=dev)
+    q32, k32, v32 = (torch.empty(Tb, H * D, device=dev) for _ in range(3))
+    r = np.random.default_rng(41)
+    g_raw = workloads.to_bf16(r.standard_normal((Tb, H * D))).to(dev)
+    b_raw = workloads.to_bf16(r.standard_normal((Tb, H))).to(dev)
+    a_log, dt = workloads.gate_params(H, D, 42)
+    a_log, dt = torch.from_numpy(a_log).to(dev), torch.from_numpy(dt).to(dev)
+    gate = torch.empty(Tb, H, D, device=dev)
+    beta = torch.empty(Tb, H, device=dev)
+    nr = workloads.norm_raw(Tb, H, D, 43)
+    core = torch.from_numpy(nr["core"]).to(dev).view(Tb, H * D)
+    og, ow = nr["out_gate"].to(dev), nr["w"].to(dev)
+    out = torch.empty(Tb, H * D, dtype=torch.bfloat16, device=dev)
+    calls = {
+        "conv_silu_l2": (lambda: kda.conv_silu_l2(x, w, y, n_seq=1, rows=Tb, heads=H, head_dim=D,
+                                                  conv_state=ctab, q32=q32, k32=k32, v32=v32),
+                         Tb * cd * 2 * 2 + Tb * H * D * 4 * 3),
+        "kda_gate": (lambda: kda.kda_gate(g_raw, a_log, dt, gate, T=Tb, heads=H, head_dim=D,
+                                          b_raw=b_raw, beta=beta),
+                     Tb * H * D * (2 + 4) + Tb * H * (2 + 4)),
+        "gated_rmsnorm": (lambda: kda.gated_rmsnorm(core, og, ow, out, T=Tb, heads=H, head_dim=D),
+                          Tb * H * D * (4 + 2 + 2)),
+    }
+    res = {}
+    for name, (fn, nbytes) in calls.items():
+        fn()
+        es = [(ev(), ev()) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in es:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        t = float(np.median([a.elapsed_time(b) for a, b in es])) * 1e-3
+        res[name] = dict(ms=t * 1e3, GBps=nbytes / t / 1e9, hbm_frac=nbytes / t / PEAK_HBM,
+                         bytes=nbytes)
+    res["config"] = "T=8192 rows, H=32, D=128 (conv_dim 12288), conv with fp32 q/k/v copies"
+    return res
+
+
+def cpu_baseline(raw, threads):
+    """The fp64 oracle, as it stands, on the full prefill workload."""
+    import oracle
+    g, b = oracle.kda_gate(raw["g_raw"], raw["a_log"], raw["dt_bias"], H, D, b_raw=raw["b_raw"])
+    S0 = workloads.state(H, D, 0.05, workloads.SEED_STATE + 1)
+    t0 = time.perf_counter()
+    oracle.kda_recurrence(raw["q"], raw["k"], raw["v"], g, b, S0, D ** -0.5, threads=threads)
+    dt = time.perf_counter() - t0
+    return dict(value=T / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"the whole prefill workload (T={T}, H={H}, D={D}), token-serial fp64, "
+                       f"heads split over {threads} threads; {dt:.2f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time the prefill steps only (profiler runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (scales HBM counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the KDA core is measured per GPU and sharding is by "
+              "sequence or head with no exchange inside the core.", file=sys.stderr)
+        sys.exit(2)
+
+    import gated_delta_rule_bounded_amd as kda
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, device=dev)           # 1 GiB fp32
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB write done")
+        del src, dst
+
+    P = setup_prefill(kda, dev)
+    log("prefill inputs ready")
+    for _ in range(args.warmup):
+        prefill_step(kda, P)
+    evs = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        prefill_step(kda, P, *evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    t_prep = float(np.mean([a.elapsed_time(b) for a, b, _ in evs])) * 1e-3
+    t_fwd = float(np.mean([b.elapsed_time(c) for _, b, c in evs])) * 1e-3
+    log(f"prefill: {ms_step:.4f} ms/step, prepare {t_prep*1e6:.1f} us, forward {t_fwd*1e6:.1f} us")
+
+    f_fwd = fwd_flops_per_token_head(D, C) * T * H
+    f_prep = prep_flops_per_token_head(D, C) * T * H
+    kernels = {
+        "kda_chunk_fwd": dict(avg_us=t_fwd * 1e6, flops=f_fwd, TFLOPs=f_fwd / t_fwd / 1e12,
+                              bytes=fwd_bytes(T, H, D, C),
+                              GBps=fwd_bytes(T, H, D, C) / t_fwd / 1e9),
+        "kda_chunk_prep": dict(avg_us=t_prep * 1e6, flops=f_prep, TFLOPs=f_prep / t_prep / 1e12,
+                               bytes=prep_bytes(T, H, D, C),
+                               GBps=prep_bytes(T, H, D, C) / t_prep / 1e9),
+    }
+    dom, t_dom, f_dom = (("kda_chunk_fwd", t_fwd, f_fwd) if t_fwd >= t_prep
+                         else ("kda_chunk_prep", t_prep, f_prep))
+    achieved = f_dom / t_dom / 1e12
+    roofline = dict(kernel=dom, bound="mfma", achieved=achieved, peak=PEAK_FP32_MFMA / 1e12,
+                    unit="TFLOP/s", frac=achieved / (PEAK_FP32_MFMA / 1e12), traffic=None,
+                    dtype="fp32 MFMA (v_mfma_f32_16x16x4_f32)")
+
+    out = {
+        "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "chunked prefill core, 1 sequence, T=4096, heads=32, head_dim=128, "
+                               "chunk=64, fp32 carried state ~N(0,0.05), q/k/v bf16-widened",
+                   "T": T, "heads": H, "head_dim": D, "chunk": C},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.prefill_only:
+        log("decode ...")
+        out["decode"] = bench_decode(kda, dev)
+        log(f"decode: {out['decode']['state_GBps']:.1f} GB/s state")
+        log("decode_k ...")
+        out["decode_k"] = bench_decode_k(kda, dev)
+        log("stages ...")
+        out["stages"] = bench_stages(kda, dev)
+    if not args.no_cpu_baseline and not args.prefill_only:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(P["raw"], cpu_threads())
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

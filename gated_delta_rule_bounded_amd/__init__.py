@@ -18,7 +18,8 @@ import torch  # loads the HIP runtime that libkda then shares
 from . import _lib
 from ._lib import KdaError, last_error  # noqa: F401
 
-__all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_decode", "kda_decode_k",
+__all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_prepare",
+           "kda_prefill_forward", "kda_decode", "kda_decode_k",
            "gated_rmsnorm", "kda_prefill_workspace_bytes", "ptr_table", "KdaError",
            "last_error", "library_path"]
 
@@ -108,6 +109,27 @@ def kda_prefill(q, k, v, gate, beta, state, core, workspace, *, T, T_pad, heads,
         _ptr(q, f, "q"), _ptr(k, f, "k"), _ptr(v, f, "v"), _ptr(gate, f, "gate"),
         _ptr(beta, f, "beta"), _ptr(state, f, "state"), _ptr(core, f, "core"),
         T, T_pad, heads, head_dim, chunk, float(scale), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream()))
+
+
+def kda_prefill_prepare(q, k, gate, beta, workspace, *, T, T_pad, heads, head_dim, chunk):
+    """Phase 1 of kda_prefill: per-chunk UT transform and scores into the
+    workspace (reads no state)."""
+    f = torch.float32
+    _check(_lib.lib.kda_prefill_prepare(
+        _ptr(q, f, "q"), _ptr(k, f, "k"), _ptr(gate, f, "gate"), _ptr(beta, f, "beta"),
+        T, T_pad, heads, head_dim, chunk, _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream()))
+
+
+def kda_prefill_forward(q, k, v, gate, state, core, workspace, *, T, T_pad, heads, head_dim,
+                        chunk, scale):
+    """Phase 2 of kda_prefill: walk the chunks from the carried state."""
+    f = torch.float32
+    _check(_lib.lib.kda_prefill_forward(
+        _ptr(q, f, "q"), _ptr(k, f, "k"), _ptr(v, f, "v"), _ptr(gate, f, "gate"),
+        _ptr(state, f, "state"), _ptr(core, f, "core"), T, T_pad, heads, head_dim, chunk,
+        float(scale), _ptr(workspace, None, "workspace"),
         workspace.numel() * workspace.element_size(), _stream()))
 
 

@@ -109,40 +109,95 @@ size_t kda_prefill_workspace_bytes(int32_t T_pad, int32_t heads, int32_t head_di
     return kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
 }
 
+// Shared validation of the prefill family; v may be NULL for prepare, beta
+// NULL for forward, state/core NULL for prepare.
+static int check_prefill(const char *who, const float *q, const float *k, const float *v,
+                         const float *gate, const float *beta, const float *state,
+                         const float *core, int32_t T, int32_t T_pad, int32_t heads,
+                         int32_t head_dim, int32_t chunk, const void *workspace,
+                         size_t workspace_bytes, bool need_v, bool need_beta, bool need_out)
+{
+    if (!head_dim_ok(head_dim) || !(chunk == 16 || chunk == 64))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: head_dim=%d chunk=%d (need 16|128, 16|64)", who,
+                    head_dim, chunk);
+    if (T < 0 || heads <= 0 || T_pad < T || T_pad % chunk)
+        return fail(KDA_ERR_SHAPE, "%s: T=%d T_pad=%d heads=%d chunk=%d", who, T, T_pad, heads,
+                    chunk);
+    if (T == 0) return 1;   // no-op
+    if (!q || !k || !gate || !workspace || (need_v && !v) || (need_beta && !beta) ||
+        (need_out && (!state || !core)))
+        return fail(KDA_ERR_NULL, "%s: null pointer argument", who);
+    const size_t need = kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", who,
+                    workspace_bytes, need);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(gate) || (need_v && !aligned16(v)) ||
+        (need_out && (!aligned16(state) || !aligned16(core))) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(KDA_ERR_SHAPE, "%s: misaligned pointer", who);
+    const size_t rows_b = (size_t)T_pad * heads * head_dim * 4;
+    const size_t st_b = (size_t)heads * head_dim * head_dim * 4;
+    const void *ins[] = {q, k, v, gate};
+    if (need_out) {
+        for (const void *p : ins)
+            if (overlap(core, rows_b, p, rows_b) || overlap(state, st_b, p, rows_b))
+                return fail(KDA_ERR_ALIAS, "%s: core or state overlaps an input", who);
+        if (overlap(core, rows_b, beta, (size_t)T_pad * heads * 4) ||
+            overlap(core, rows_b, state, st_b) || overlap(workspace, need, core, rows_b) ||
+            overlap(workspace, need, state, st_b))
+            return fail(KDA_ERR_ALIAS, "%s: core, state, beta or workspace overlap", who);
+    }
+    for (const void *p : ins)
+        if (overlap(workspace, need, p, rows_b))
+            return fail(KDA_ERR_ALIAS, "%s: workspace overlaps an input", who);
+    if (overlap(workspace, need, beta, (size_t)T_pad * heads * 4))
+        return fail(KDA_ERR_ALIAS, "%s: workspace overlaps beta", who);
+    return KDA_OK;
+}
+
 int kda_prefill(const float *q, const float *k, const float *v, const float *gate,
                 const float *beta, float *state, float *core, int32_t T, int32_t T_pad,
                 int32_t heads, int32_t head_dim, int32_t chunk, float scale, void *workspace,
                 size_t workspace_bytes, hipStream_t stream)
 {
-    if (!head_dim_ok(head_dim) || !(chunk == 16 || chunk == 64))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: head_dim=%d chunk=%d (need 16|128, 16|64)",
-                    head_dim, chunk);
-    if (T < 0 || heads <= 0 || T_pad < T || T_pad % chunk)
-        return fail(KDA_ERR_SHAPE, "kda_prefill: T=%d T_pad=%d heads=%d chunk=%d", T, T_pad,
-                    heads, chunk);
-    if (T == 0) return ok();
-    if (!q || !k || !v || !gate || !beta || !state || !core || !workspace)
-        return fail(KDA_ERR_NULL, "kda_prefill: null pointer argument");
-    const size_t need = kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
-    if (workspace_bytes < need)
-        return fail(KDA_ERR_WORKSPACE, "kda_prefill: workspace %zu bytes < %zu needed",
-                    workspace_bytes, need);
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) ||
-        !aligned16(state) || !aligned16(core) ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u))
-        return fail(KDA_ERR_SHAPE, "kda_prefill: misaligned pointer");
-    const size_t rows_b = (size_t)T_pad * heads * head_dim * 4;
-    const size_t st_b = (size_t)heads * head_dim * head_dim * 4;
-    const void *ins[] = {q, k, v, gate};
-    for (const void *p : ins)
-        if (overlap(core, rows_b, p, rows_b) || overlap(state, st_b, p, rows_b))
-            return fail(KDA_ERR_ALIAS, "kda_prefill: core or state overlaps an input");
-    if (overlap(core, rows_b, beta, (size_t)T_pad * heads * 4) || overlap(core, rows_b, state, st_b) ||
-        overlap(workspace, need, core, rows_b) || overlap(workspace, need, state, st_b))
-        return fail(KDA_ERR_ALIAS, "kda_prefill: core, state, beta or workspace overlap");
+    const int rc = check_prefill("kda_prefill", q, k, v, gate, beta, state, core, T, T_pad,
+                                 heads, head_dim, chunk, workspace, workspace_bytes, true, true,
+                                 true);
+    if (rc == 1) return ok();
+    if (rc) return rc;
     return hip_status(kda::launch_kda_prefill(q, k, v, gate, beta, state, core, T, T_pad, heads,
                                               head_dim, chunk, scale, workspace, stream),
                       "kda_prefill launch");
+}
+
+int kda_prefill_prepare(const float *q, const float *k, const float *gate, const float *beta,
+                        int32_t T, int32_t T_pad, int32_t heads, int32_t head_dim,
+                        int32_t chunk, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream)
+{
+    const int rc = check_prefill("kda_prefill_prepare", q, k, nullptr, gate, beta, nullptr,
+                                 nullptr, T, T_pad, heads, head_dim, chunk, workspace,
+                                 workspace_bytes, false, true, false);
+    if (rc == 1) return ok();
+    if (rc) return rc;
+    return hip_status(kda::launch_kda_prefill_prepare(q, k, gate, beta, T, T_pad, heads, head_dim,
+                                                      chunk, workspace, stream),
+                      "kda_prefill_prepare launch");
+}
+
+int kda_prefill_forward(const float *q, const float *k, const float *v, const float *gate,
+                        float *state, float *core, int32_t T, int32_t T_pad, int32_t heads,
+                        int32_t head_dim, int32_t chunk, float scale, const void *workspace,
+                        size_t workspace_bytes, hipStream_t stream)
+{
+    const int rc = check_prefill("kda_prefill_forward", q, k, v, gate, nullptr, state, core, T,
+                                 T_pad, heads, head_dim, chunk, workspace, workspace_bytes, true,
+                                 false, true);
+    if (rc == 1) return ok();
+    if (rc) return rc;
+    return hip_status(kda::launch_kda_prefill_forward(q, k, v, gate, state, core, T, T_pad, heads,
+                                                      head_dim, chunk, scale, workspace, stream),
+                      "kda_prefill_forward launch");
 }
 
 static int check_decode(const char *who, const uint16_t *qkv, int64_t ldqkv, const float *gate,

@@ -469,22 +469,53 @@ size_t prefill_workspace_bytes(int T_pad, int heads, int head_dim, int chunk)
 }
 
 template <int D, int C>
-static hipError_t launch_prefill_t(const float *q, const float *k, const float *v,
-                                   const float *gate, const float *beta, float *state,
-                                   float *core, int T, int T_pad, int H, float scale,
-                                   void *workspace, hipStream_t stream)
+static hipError_t prepare_t(const float *q, const float *k, const float *gate,
+                            const float *beta, int T, int T_pad, int H, void *workspace,
+                            hipStream_t stream)
 {
     const int NC = (T + C - 1) / C;
     float *Tb = static_cast<float *>(workspace);
     float *Pm = Tb + (size_t)(T_pad / C) * H * C * C;
     hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C>), dim3(NC, H), dim3(PrefCfg<D, C>::kThreads),
                        0, stream, q, k, gate, beta, T, H, Tb, Pm);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+template <int D, int C>
+static hipError_t forward_t(const float *q, const float *k, const float *v, const float *gate,
+                            float *state, float *core, int T, int T_pad, int H, float scale,
+                            const void *workspace, hipStream_t stream)
+{
+    const int NC = (T + C - 1) / C;
+    const float *Tb = static_cast<const float *>(workspace);
+    const float *Pm = Tb + (size_t)(T_pad / C) * H * C * C;
     hipLaunchKernelGGL((kda_chunk_fwd_kernel<D, C>), dim3(H * PrefCfg<D, C>::kDT),
                        dim3(PrefCfg<D, C>::kThreads), 0, stream, q, k, v, gate, state, core, Tb,
                        Pm, T, NC, H, scale);
     return hipGetLastError();
+}
+
+#define KDA_PREFILL_DISPATCH(FN, ...)                                        \
+    (head_dim == 128 && chunk == 64)   ? FN<128, 64>(__VA_ARGS__)            \
+    : (head_dim == 128 && chunk == 16) ? FN<128, 16>(__VA_ARGS__)            \
+    : (head_dim == 16 && chunk == 64)  ? FN<16, 64>(__VA_ARGS__)             \
+                                       : FN<16, 16>(__VA_ARGS__)
+
+hipError_t launch_kda_prefill_prepare(const float *q, const float *k, const float *gate,
+                                      const float *beta, int T, int T_pad, int heads,
+                                      int head_dim, int chunk, void *workspace,
+                                      hipStream_t stream)
+{
+    return KDA_PREFILL_DISPATCH(prepare_t, q, k, gate, beta, T, T_pad, heads, workspace, stream);
+}
+
+hipError_t launch_kda_prefill_forward(const float *q, const float *k, const float *v,
+                                      const float *gate, float *state, float *core, int T,
+                                      int T_pad, int heads, int head_dim, int chunk, float scale,
+                                      const void *workspace, hipStream_t stream)
+{
+    return KDA_PREFILL_DISPATCH(forward_t, q, k, v, gate, state, core, T, T_pad, heads, scale,
+                                workspace, stream);
 }
 
 hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
@@ -492,17 +523,11 @@ hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
                               float *core, int T, int T_pad, int heads, int head_dim,
                               int chunk, float scale, void *workspace, hipStream_t stream)
 {
-    if (head_dim == 128 && chunk == 64)
-        return launch_prefill_t<128, 64>(q, k, v, gate, beta, state, core, T, T_pad, heads,
-                                         scale, workspace, stream);
-    if (head_dim == 128 && chunk == 16)
-        return launch_prefill_t<128, 16>(q, k, v, gate, beta, state, core, T, T_pad, heads,
-                                         scale, workspace, stream);
-    if (head_dim == 16 && chunk == 64)
-        return launch_prefill_t<16, 64>(q, k, v, gate, beta, state, core, T, T_pad, heads,
-                                        scale, workspace, stream);
-    return launch_prefill_t<16, 16>(q, k, v, gate, beta, state, core, T, T_pad, heads, scale,
-                                    workspace, stream);
+    hipError_t e = launch_kda_prefill_prepare(q, k, gate, beta, T, T_pad, heads, head_dim, chunk,
+                                              workspace, stream);
+    if (e != hipSuccess) return e;
+    return launch_kda_prefill_forward(q, k, v, gate, state, core, T, T_pad, heads, head_dim,
+                                      chunk, scale, workspace, stream);
 }
 
 }  // namespace kda

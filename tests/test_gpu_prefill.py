@@ -141,3 +141,23 @@ def test_prefill_full_size_h32_d128(T, T_pad, fill):
     assert e_core < TOL and e_S < TOL
     if T_pad > T:
         assert np.all(core[T:] == 7.0)
+
+
+def test_prefill_phases_equal_one_call_bitwise():
+    """kda_prefill_prepare then kda_prefill_forward == kda_prefill, bit for bit."""
+    import gated_delta_rule_bounded_amd as kda
+    from kda_cases import cuda, pad_rows
+    T, T_pad, H, D, C = 300, 320, 4, 128, 64
+    case = core_case(T, H, D, 1606, 0.05)
+    core_a, S_a = gpu_prefill(case, T, T_pad, C, D ** -0.5)
+    q, k, v, g, b = (cuda(pad_rows(case[n], T_pad, 0.0)) for n in ("q", "k", "v", "gate", "beta"))
+    st = cuda(case["S0"]).contiguous()
+    core = torch.full((T_pad, H, D), 7.0, device="cuda")
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(T_pad, H, D, C), dtype=torch.uint8, device="cuda")
+    kw = dict(T=T, T_pad=T_pad, heads=H, head_dim=D, chunk=C)
+    say("phases")
+    kda.kda_prefill_prepare(q, k, g, b, ws, **kw)
+    kda.kda_prefill_forward(q, k, v, g, st, core, ws, scale=D ** -0.5, **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(core.cpu().numpy().view(np.int32), core_a.view(np.int32))
+    assert np.array_equal(st.cpu().numpy().view(np.int32), S_a.view(np.int32))

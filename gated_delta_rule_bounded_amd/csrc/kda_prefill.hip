@@ -72,64 +72,94 @@ __device__ __forceinline__ float4 exp2_4(const float4 &a) {
 }
 __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 
-// Load this lane's A-layout slice of chunk row `t` (channels 16*t8 + 4*lg ..
-// +3 for every tile t8) of k, q and the gate; the gate is scaled to log2
-// units.  Rows past T read as zero.
+// Load this lane's A-layout slice of chunk row (channels 16*t8 + 4*lg .. +3
+// for every tile t8) of k, q and the gate.  The loads are unconditional: a
+// chunk never extends past T_pad rows, so every row it touches is in bounds;
+// rows past T are replaced afterwards by select_rows.  Keeping the loads free
+// of branches and arithmetic lets them stay in flight across other work.
 template <int D>
 __device__ __forceinline__ void load_rows(const float *__restrict__ q, const float *__restrict__ k,
-                                          const float *__restrict__ gate, int64_t roff,
-                                          bool valid, int lg, float4 (&K)[D / 16],
-                                          float4 (&Q)[D / 16], float4 (&G)[D / 16])
+                                          const float *__restrict__ gate, int64_t roff, int lg,
+                                          float4 (&K)[D / 16], float4 (&Q)[D / 16],
+                                          float4 (&G)[D / 16])
 {
 #pragma unroll
     for (int t8 = 0; t8 < D / 16; ++t8) {
         const int d0 = 16 * t8 + 4 * lg;
-        float4 kk = zero4(), qq = zero4(), gg = zero4();
-        if (valid) {
-            kk = *reinterpret_cast<const float4 *>(k + roff + d0);
-            qq = *reinterpret_cast<const float4 *>(q + roff + d0);
-            gg = *reinterpret_cast<const float4 *>(gate + roff + d0);
-        }
-        K[t8] = kk;
-        Q[t8] = qq;
-        G[t8] = make_float4(gg.x * kLog2e, gg.y * kLog2e, gg.z * kLog2e, gg.w * kLog2e);
+        K[t8] = *reinterpret_cast<const float4 *>(k + roff + d0);
+        Q[t8] = *reinterpret_cast<const float4 *>(q + roff + d0);
+        G[t8] = *reinterpret_cast<const float4 *>(gate + roff + d0);
     }
 }
 
-// In-chunk inclusive prefix over rows of the log2 gate, in place.  Wave w owns
-// chunk rows 16w + lr (lr = lane % 16).  The scan runs over the 16 lanes of
-// each row group, then adds the totals of the preceding waves in wave order.
-// Gend receives the chunk total (the last row's value) for the lane's
-// channels.  Both prefill kernels use this one routine with the same layout,
-// so they see bitwise the same cumulative decay.
+// Rows past T become k = q = 0 and zero log-decay (a select, so the bits they
+// held never reach the arithmetic); the gate is scaled to log2 units.
+template <int D>
+__device__ __forceinline__ void select_rows(bool valid, float4 (&K)[D / 16], float4 (&Q)[D / 16],
+                                            float4 (&G)[D / 16])
+{
+#pragma unroll
+    for (int t8 = 0; t8 < D / 16; ++t8) {
+        const float4 g = G[t8];
+        K[t8] = valid ? K[t8] : zero4();
+        Q[t8] = valid ? Q[t8] : zero4();
+        G[t8] = valid ? make_float4(g.x * kLog2e, g.y * kLog2e, g.z * kLog2e, g.w * kLog2e)
+                      : zero4();
+    }
+}
+
+// Row shift within each 16-lane DPP row; lanes shifted in from outside the
+// row read 0.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf,
+                                                      true));
+}
+
+// In-chunk inclusive prefix over rows of the log2 gate, in two phases so the
+// cross-wave exchange can share a barrier with other work.  Wave w owns chunk
+// rows 16w + lr (lr = lane % 16, one DPP row of the wave); for channel tile
+// t8 the lane holds channels 16*t8 + 4*lg .. +3.
+//   scan_local: Hillis-Steele over the 16 lanes of each row (DPP row shifts),
+//               then (NW > 1) the wave's row totals to s_tot.
+//   scan_carry: after a barrier, add the totals of the preceding waves in wave
+//               order; Gend = the chunk's last row (the chunk total).
+// Both prefill kernels use these with the same layout, so they see bitwise the
+// same cumulative decay.
 template <int D, int NW>
-__device__ __forceinline__ void chunk_cumsum(float4 (&G)[D / 16], float4 (&Gend)[D / 16],
-                                             float *s_tot, int w, int lane)
+__device__ __forceinline__ void scan_local(float4 (&G)[D / 16], float *s_tot, int w, int lane)
 {
     const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-#pragma unroll
-        for (int t8 = 0; t8 < D / 16; ++t8) {
-            const float ox = __shfl_up(G[t8].x, off, 16), oy = __shfl_up(G[t8].y, off, 16);
-            const float oz = __shfl_up(G[t8].z, off, 16), ow = __shfl_up(G[t8].w, off, 16);
-            if (lr >= off) G[t8] = add4(G[t8], make_float4(ox, oy, oz, ow));
-        }
+    for (int t8 = 0; t8 < D / 16; ++t8) {
+        float4 g = G[t8];
+        g = add4(g, make_float4(row_shr<1>(g.x), row_shr<1>(g.y), row_shr<1>(g.z), row_shr<1>(g.w)));
+        g = add4(g, make_float4(row_shr<2>(g.x), row_shr<2>(g.y), row_shr<2>(g.z), row_shr<2>(g.w)));
+        g = add4(g, make_float4(row_shr<4>(g.x), row_shr<4>(g.y), row_shr<4>(g.z), row_shr<4>(g.w)));
+        g = add4(g, make_float4(row_shr<8>(g.x), row_shr<8>(g.y), row_shr<8>(g.z), row_shr<8>(g.w)));
+        G[t8] = g;
+        if (NW > 1 && lr == 15)
+            *reinterpret_cast<float4 *>(s_tot + w * D + 16 * t8 + 4 * lg) = g;
     }
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void scan_carry(float4 (&G)[D / 16], float4 (&Gend)[D / 16],
+                                           const float *s_tot, int w, int lane)
+{
+    const int lg = lane >> 4;
     if constexpr (NW > 1) {
-        if (lr == 15) {
-#pragma unroll
-            for (int t8 = 0; t8 < D / 16; ++t8)
-                *reinterpret_cast<float4 *>(s_tot + w * D + 16 * t8 + 4 * lg) = G[t8];
-        }
-        __syncthreads();
 #pragma unroll
         for (int t8 = 0; t8 < D / 16; ++t8) {
+            float4 tot[NW];
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww)
+                tot[ww] = *reinterpret_cast<const float4 *>(s_tot + ww * D + 16 * t8 + 4 * lg);
             float4 run = zero4(), carry = zero4();
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) {
-                if (ww == w) carry = run;
-                run = add4(run, *reinterpret_cast<const float4 *>(s_tot + ww * D + 16 * t8 + 4 * lg));
+                if (ww == w) carry = run;   // w is wave-uniform: a scalar branch
+                run = add4(run, tot[ww]);
             }
             G[t8] = add4(G[t8], carry);
             Gend[t8] = run;
@@ -138,6 +168,15 @@ __device__ __forceinline__ void chunk_cumsum(float4 (&G)[D / 16], float4 (&Gend)
 #pragma unroll
         for (int t8 = 0; t8 < D / 16; ++t8) Gend[t8] = shfl4(G[t8], (lane & 48) | 15);
     }
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void chunk_cumsum(float4 (&G)[D / 16], float4 (&Gend)[D / 16],
+                                             float *s_tot, int w, int lane)
+{
+    scan_local<D, NW>(G, s_tot, w, lane);
+    if (NW > 1) __syncthreads();
+    scan_carry<D, NW>(G, Gend, s_tot, w, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -152,7 +191,9 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
     const int n = blockIdx.x, h = blockIdx.y;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+    // wave index, uniform across the wave (scalar register)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
     const int rl = 16 * w + lr;
     const int64_t tg = (int64_t)n * C + rl;
     const bool valid = tg < T;
@@ -165,8 +206,10 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     __shared__ float s_beta[C];
 
     float4 K[DT], Q[DT], G[DT], Gend[DT];
-    load_rows<D>(q, k, gate, roff, valid, lg, K, Q, G);
-    if (lg == 0) s_beta[rl] = valid ? beta[tg * H + h] : 0.f;
+    load_rows<D>(q, k, gate, roff, lg, K, Q, G);
+    const float braw = beta[tg * H + h];
+    select_rows<D>(valid, K, Q, G);
+    if (lg == 0) s_beta[rl] = valid ? braw : 0.f;
     chunk_cumsum<D, NW>(G, Gend, s_tot, w, lane);
 
     // Column operand Kc = K e^{G_last - G}, relative to the last row of this
@@ -333,7 +376,59 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
 
 // ---------------------------------------------------------------------------
 // kda_chunk_fwd: per (head h, value slice j0..j0+15), serial over chunks.
+//
+// Software pipeline: the global loads of chunk n+1 (this wave's 16 rows of
+// k, q, gate, the v slice, and its rows of Tb and P) are issued at the top of
+// iteration n and consumed after its last barrier, so their latency overlaps
+// the MFMA work of chunk n.  The in-chunk scan of chunk n+1 shares that last
+// barrier with the state broadcast, leaving three barriers per chunk:
+//   B1  X rows and Kd rows visible      (U needs X of waves <= w)
+//   B2  U rows visible                  (P U and the state update need U)
+//   B3  new state slice and scan totals visible
 // ---------------------------------------------------------------------------
+template <int D, int C>
+struct FwdRows {
+    float4 K[D / 16], Q[D / 16], G[D / 16];   // A-layout row slices of k, q, gate
+    float V[4];                               // v[16w + 4lg + i][j0 + lr]
+    float4 Tb[C / 16], P[C / 16];             // Tb, P row 16w + lr, columns 16w2 + 4lg ..
+};
+
+template <int D, int C>
+__device__ __forceinline__ void fwd_load(FwdRows<D, C> &R, const float *__restrict__ q,
+                                         const float *__restrict__ k, const float *__restrict__ v,
+                                         const float *__restrict__ gate,
+                                         const float *__restrict__ Tb,
+                                         const float *__restrict__ Pm, int n, int T, int H, int h,
+                                         int j0, int w, int lr, int lg)
+{
+    constexpr int NW = C / 16;
+    const int64_t tg = (int64_t)n * C + 16 * w + lr;
+    load_rows<D>(q, k, gate, (tg * H + h) * D, lg, R.K, R.Q, R.G);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + i;
+        R.V[i] = v[(tr * H + h) * D + j0 + lr];
+    }
+    // the blocks above the diagonal are loaded (in bounds) but never used
+    const int64_t toff = (((int64_t)n * H + h) * C + 16 * w + lr) * C + 4 * lg;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+        R.Tb[w2] = *reinterpret_cast<const float4 *>(Tb + toff + 16 * w2);
+        R.P[w2] = *reinterpret_cast<const float4 *>(Pm + toff + 16 * w2);
+    }
+}
+
+// Pad-row selects of a loaded chunk (see select_rows), applied when the
+// chunk's values are first used.
+template <int D, int C>
+__device__ __forceinline__ void fwd_select(FwdRows<D, C> &R, int n, int T, int w, int lr, int lg)
+{
+    select_rows<D>((int64_t)n * C + 16 * w + lr < T, R.K, R.Q, R.G);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        R.V[i] = ((int64_t)n * C + 16 * w + 4 * lg + i < T) ? R.V[i] : 0.f;
+}
+
 template <int D, int C>
 __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
@@ -345,7 +440,9 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
     // all value slices of one head share an XCD (workgroups are dealt to the
     // 8 XCDs round-robin), so they share that XCD's L2 copy of q/k/gate/Tb/P
     const int h = blockIdx.x % H, jt = blockIdx.x / H, j0 = 16 * jt;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+    // wave index, uniform across the wave (scalar register)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
     const int rl = 16 * w + lr;
 
     __shared__ __align__(16) float s_tot[NW * D];
@@ -362,73 +459,83 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) Sr[t8][i] = Sg[(int64_t)(16 * t8 + 4 * lg + i) * D + j0 + lr];
 
-    for (int n = 0; n < NC; ++n) {
-        const int64_t tg = (int64_t)n * C + rl;
-        const bool valid = tg < T;
-        const int64_t roff = (tg * H + h) * D;
-        float4 K[DT], Q[DT], G[DT], Gend[DT];
-        load_rows<D>(q, k, gate, roff, valid, lg, K, Q, G);
-        chunk_cumsum<D, NW>(G, Gend, s_tot, w, lane);
+    FwdRows<D, C> R;
+    float4 Kg[DT], Qg[DT], Gend[DT];
+    float V[4];
+    float4 TbR[NW], PR[NW];
 
-        // Kd = K e^{G_C - G} rows to LDS; K e^{G}, Q e^{G} stay in registers
+    // chunk 0: load, scan, operands
+    fwd_load<D, C>(R, q, k, v, gate, Tb, Pm, 0, T, H, h, j0, w, lr, lg);
+    fwd_select<D, C>(R, 0, T, w, lr, lg);
+    scan_local<D, NW>(R.G, s_tot, w, lane);
+    if (NW > 1) __syncthreads();
+
+    for (int n = 0; n < NC; ++n) {
+        // ---- operands of chunk n from R (its scan totals are in s_tot) ----
+        scan_carry<D, NW>(R.G, Gend, s_tot, w, lane);
 #pragma unroll
         for (int t8 = 0; t8 < DT; ++t8) {
-            const float4 ed = exp2_4(sub4(Gend[t8], G[t8]));
-            *reinterpret_cast<float4 *>(&s_kd[rl][16 * t8 + 4 * lg]) = mul4(K[t8], ed);
-            const float4 eg = exp2_4(G[t8]);
-            K[t8] = mul4(K[t8], eg);
-            Q[t8] = mul4(Q[t8], eg);
+            const float4 ed = exp2_4(sub4(Gend[t8], R.G[t8]));
+            *reinterpret_cast<float4 *>(&s_kd[rl][16 * t8 + 4 * lg]) = mul4(R.K[t8], ed);
+            const float4 eg = exp2_4(R.G[t8]);
+            Kg[t8] = mul4(R.K[t8], eg);
+            Qg[t8] = mul4(R.Q[t8], eg);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) V[i] = R.V[i];
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            TbR[w2] = R.Tb[w2];
+            PR[w2] = R.P[w2];
+        }
+        // ---- prefetch chunk n+1 ----
+        if (n + 1 < NC) fwd_load<D, C>(R, q, k, v, gate, Tb, Pm, n + 1, T, H, h, j0, w, lr, lg);
 
         // X = V - (K e^G) S ;  QS = (Q e^G) S   (rows 16w.., D-deep products)
-        floatx4 X, QS = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-            const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + vv;
-            X[vv] = tr < T ? v[(tr * H + h) * D + j0 + lr] : 0.f;
-        }
+        floatx4 X = {V[0], V[1], V[2], V[3]}, QS = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t8 = 0; t8 < DT; ++t8) {
-            X = mfma4(-K[t8].x, Sr[t8][0], X);
-            QS = mfma4(Q[t8].x, Sr[t8][0], QS);
-            X = mfma4(-K[t8].y, Sr[t8][1], X);
-            QS = mfma4(Q[t8].y, Sr[t8][1], QS);
-            X = mfma4(-K[t8].z, Sr[t8][2], X);
-            QS = mfma4(Q[t8].z, Sr[t8][2], QS);
-            X = mfma4(-K[t8].w, Sr[t8][3], X);
-            QS = mfma4(Q[t8].w, Sr[t8][3], QS);
+            X = mfma4(-Kg[t8].x, Sr[t8][0], X);
+            QS = mfma4(Qg[t8].x, Sr[t8][0], QS);
+            X = mfma4(-Kg[t8].y, Sr[t8][1], X);
+            QS = mfma4(Qg[t8].y, Sr[t8][1], QS);
+            X = mfma4(-Kg[t8].z, Sr[t8][2], X);
+            QS = mfma4(Qg[t8].z, Sr[t8][2], QS);
+            X = mfma4(-Kg[t8].w, Sr[t8][3], X);
+            QS = mfma4(Qg[t8].w, Sr[t8][3], QS);
         }
 #pragma unroll
-        for (int vv = 0; vv < 4; ++vv) s_x[16 * w + 4 * lg + vv][lr] = X[vv];
-        __syncthreads();
+        for (int i = 0; i < 4; ++i) s_x[16 * w + 4 * lg + i][lr] = X[i];
+        __syncthreads();   // B1
 
         // U = Tb X  (block row w, lower triangle)
-        const int64_t toff = (((int64_t)n * H + h) * C + rl) * C;
         floatx4 U = {0.f, 0.f, 0.f, 0.f};
-        for (int w2 = 0; w2 <= w; ++w2) {
-            const float4 ta = *reinterpret_cast<const float4 *>(Tb + toff + 16 * w2 + 4 * lg);
-            U = mfma4(ta.x, s_x[16 * w2 + 4 * lg + 0][lr], U);
-            U = mfma4(ta.y, s_x[16 * w2 + 4 * lg + 1][lr], U);
-            U = mfma4(ta.z, s_x[16 * w2 + 4 * lg + 2][lr], U);
-            U = mfma4(ta.w, s_x[16 * w2 + 4 * lg + 3][lr], U);
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            if (w2 > w) continue;
+            U = mfma4(TbR[w2].x, s_x[16 * w2 + 4 * lg + 0][lr], U);
+            U = mfma4(TbR[w2].y, s_x[16 * w2 + 4 * lg + 1][lr], U);
+            U = mfma4(TbR[w2].z, s_x[16 * w2 + 4 * lg + 2][lr], U);
+            U = mfma4(TbR[w2].w, s_x[16 * w2 + 4 * lg + 3][lr], U);
         }
 #pragma unroll
-        for (int vv = 0; vv < 4; ++vv) s_u[16 * w + 4 * lg + vv][lr] = U[vv];
-        __syncthreads();
+        for (int i = 0; i < 4; ++i) s_u[16 * w + 4 * lg + i][lr] = U[i];
+        __syncthreads();   // B2
 
         // O = scale (QS + P U)
         floatx4 O = QS;
-        for (int w2 = 0; w2 <= w; ++w2) {
-            const float4 pa = *reinterpret_cast<const float4 *>(Pm + toff + 16 * w2 + 4 * lg);
-            O = mfma4(pa.x, s_u[16 * w2 + 4 * lg + 0][lr], O);
-            O = mfma4(pa.y, s_u[16 * w2 + 4 * lg + 1][lr], O);
-            O = mfma4(pa.z, s_u[16 * w2 + 4 * lg + 2][lr], O);
-            O = mfma4(pa.w, s_u[16 * w2 + 4 * lg + 3][lr], O);
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            if (w2 > w) continue;
+            O = mfma4(PR[w2].x, s_u[16 * w2 + 4 * lg + 0][lr], O);
+            O = mfma4(PR[w2].y, s_u[16 * w2 + 4 * lg + 1][lr], O);
+            O = mfma4(PR[w2].z, s_u[16 * w2 + 4 * lg + 2][lr], O);
+            O = mfma4(PR[w2].w, s_u[16 * w2 + 4 * lg + 3][lr], O);
         }
 #pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-            const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + vv;
-            if (tr < T) core[(tr * H + h) * D + j0 + lr] = scale * O[vv];
+        for (int i = 0; i < 4; ++i) {
+            const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + i;
+            if (tr < T) core[(tr * H + h) * D + j0 + lr] = scale * O[i];
         }
 
         // S' = diag(e^{G_C}) S + Kd^T U for the channel tiles this wave owns
@@ -446,7 +553,12 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) s_S[16 * t8 + 4 * lg + i][lr] = acc[i];
         }
-        __syncthreads();
+        // in-row scan of chunk n+1 (its loads were issued above)
+        if (n + 1 < NC) {
+            fwd_select<D, C>(R, n + 1, T, w, lr, lg);
+            scan_local<D, NW>(R.G, s_tot, w, lane);
+        }
+        __syncthreads();   // B3
 #pragma unroll
         for (int t8 = 0; t8 < DT; ++t8)
 #pragma unroll

@@ -47,26 +47,33 @@ def cpu_threads():
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-# algorithmic work per token and head (see the prefill kernel header)
+# Algorithmic work per token and head of the two prefill kernels (chunk C,
+# head_dim D).  Matrix products count 2 flops per multiply-add; products over
+# a lower triangle count its (C+1)/2 average row length.
 def fwd_flops_per_token_head(D, C):
-    # (K e^G) S, (Q e^G) S, (K e^{G_C-G})^T U: 2*D*D each; Tb X and P U over
-    # the lower triangle: (C+1)*D each
-    return 6 * D * D + 2 * (C + 1) * D
+    # W S, Qg S, KdT U: 2*D*D each;  P U over the lower triangle: (C+1)*D
+    return 6 * D * D + (C + 1) * D
 
 
 def prep_flops_per_token_head(D, C):
-    # A strictly lower (C-1)*D, P with diagonal (C+1)*D, triangular inverse C^2/3
-    return 2 * C * D + C * C / 3.0
+    # A strictly lower (C-1)*D and P with diagonal (C+1)*D; the unit-lower
+    # triangular inverse C^2/3; W = Tb Kg and U' = Tb V: (C+1)*D each
+    return 2 * C * D + C * C / 3.0 + 2 * (C + 1) * D
+
+
+def block_floats(D, C):
+    # per (chunk, head) operand block: W, U', Qg, KdT, P, Ec
+    return 4 * C * D + C * C + D
 
 
 def fwd_bytes(T, H, D, C):
-    # read q, k, v, gate, Tb, P; write core; state read + write
-    return T * H * (4 * D * 4 + 2 * C * 4 + D * 4) + 2 * H * D * D * 4
+    # read every operand block once, write core, read + write the state
+    return (T // C) * H * block_floats(D, C) * 4 + T * H * D * 4 + 2 * H * D * D * 4
 
 
 def prep_bytes(T, H, D, C):
-    # read q, k, gate, beta; write Tb, P
-    return T * H * (3 * D * 4 + 4 + 2 * C * 4)
+    # read q, k, v, gate, beta; write the operand blocks
+    return T * H * (4 * D * 4 + 4) + (T // C) * H * block_floats(D, C) * 4
 
 
 def ev():
@@ -91,11 +98,10 @@ def prefill_step(kda, P, e0=None, e1=None, e2=None):
     kw = dict(T=T, T_pad=T, heads=H, head_dim=D, chunk=C)
     if e0 is not None:
         e0.record()
-    kda.kda_prefill_prepare(P["q"], P["k"], P["gate"], P["beta"], P["ws"], **kw)
+    kda.kda_prefill_prepare(P["q"], P["k"], P["v"], P["gate"], P["beta"], P["ws"], **kw)
     if e1 is not None:
         e1.record()
-    kda.kda_prefill_forward(P["q"], P["k"], P["v"], P["gate"], P["state"], P["core"], P["ws"],
-                            scale=D ** -0.5, **kw)
+    kda.kda_prefill_forward(P["state"], P["core"], P["ws"], scale=D ** -0.5, **kw)
     if e2 is not None:
         e2.record()
 

@@ -112,22 +112,21 @@ def kda_prefill(q, k, v, gate, beta, state, core, workspace, *, T, T_pad, heads,
         workspace.numel() * workspace.element_size(), _stream()))
 
 
-def kda_prefill_prepare(q, k, gate, beta, workspace, *, T, T_pad, heads, head_dim, chunk):
-    """Phase 1 of kda_prefill: per-chunk UT transform and scores into the
-    workspace (reads no state)."""
+def kda_prefill_prepare(q, k, v, gate, beta, workspace, *, T, T_pad, heads, head_dim, chunk):
+    """Phase 1 of kda_prefill: every per-chunk operand of the state walk into
+    the workspace (reads no state)."""
     f = torch.float32
     _check(_lib.lib.kda_prefill_prepare(
-        _ptr(q, f, "q"), _ptr(k, f, "k"), _ptr(gate, f, "gate"), _ptr(beta, f, "beta"),
-        T, T_pad, heads, head_dim, chunk, _ptr(workspace, None, "workspace"),
-        workspace.numel() * workspace.element_size(), _stream()))
+        _ptr(q, f, "q"), _ptr(k, f, "k"), _ptr(v, f, "v"), _ptr(gate, f, "gate"),
+        _ptr(beta, f, "beta"), T, T_pad, heads, head_dim, chunk,
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream()))
 
 
-def kda_prefill_forward(q, k, v, gate, state, core, workspace, *, T, T_pad, heads, head_dim,
-                        chunk, scale):
+def kda_prefill_forward(state, core, workspace, *, T, T_pad, heads, head_dim, chunk, scale):
     """Phase 2 of kda_prefill: walk the chunks from the carried state."""
     f = torch.float32
     _check(_lib.lib.kda_prefill_forward(
-        _ptr(q, f, "q"), _ptr(k, f, "k"), _ptr(v, f, "v"), _ptr(gate, f, "gate"),
         _ptr(state, f, "state"), _ptr(core, f, "core"), T, T_pad, heads, head_dim, chunk,
         float(scale), _ptr(workspace, None, "workspace"),
         workspace.numel() * workspace.element_size(), _stream()))

@@ -11,7 +11,8 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 
 # exported C symbols, as declared in include/kda.h
 SYMBOLS = ("kda_last_error", "conv_silu_l2", "kda_gate", "kda_prefill_workspace_bytes",
-           "kda_prefill", "kda_prefill_prepare", "kda_prefill_forward", "kda_decode", "kda_decode_k", "gated_rmsnorm")
+           "kda_prefill", "kda_prefill_prepare", "kda_prefill_forward", "kda_decode",
+           "kda_decode_k", "gated_rmsnorm")
 
 
 class KdaError(RuntimeError):
@@ -39,10 +40,10 @@ def _load():
     lib.kda_prefill.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, f32, P,
                                 ctypes.c_size_t, P]
     lib.kda_prefill_prepare.restype = ctypes.c_int
-    lib.kda_prefill_prepare.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P, ctypes.c_size_t, P]
-    lib.kda_prefill_forward.restype = ctypes.c_int
-    lib.kda_prefill_forward.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, f32, P,
+    lib.kda_prefill_prepare.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, P,
                                         ctypes.c_size_t, P]
+    lib.kda_prefill_forward.restype = ctypes.c_int
+    lib.kda_prefill_forward.argtypes = [P, P, i32, i32, i32, i32, i32, f32, P, ctypes.c_size_t, P]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [P, i64, P, P, P, P, i32, i32, i32, f32, P]
     lib.kda_decode_k.restype = ctypes.c_int

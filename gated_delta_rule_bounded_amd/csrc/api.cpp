@@ -165,38 +165,52 @@ int kda_prefill(const float *q, const float *k, const float *v, const float *gat
                                  true);
     if (rc == 1) return ok();
     if (rc) return rc;
-    return hip_status(kda::launch_kda_prefill(q, k, v, gate, beta, state, core, T, T_pad, heads,
+    return hip_status(kda::launch_kda_prefill(q, k, v, gate, beta, state, core, T, heads,
                                               head_dim, chunk, scale, workspace, stream),
                       "kda_prefill launch");
 }
 
-int kda_prefill_prepare(const float *q, const float *k, const float *gate, const float *beta,
-                        int32_t T, int32_t T_pad, int32_t heads, int32_t head_dim,
-                        int32_t chunk, void *workspace, size_t workspace_bytes,
-                        hipStream_t stream)
+int kda_prefill_prepare(const float *q, const float *k, const float *v, const float *gate,
+                        const float *beta, int32_t T, int32_t T_pad, int32_t heads,
+                        int32_t head_dim, int32_t chunk, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream)
 {
-    const int rc = check_prefill("kda_prefill_prepare", q, k, nullptr, gate, beta, nullptr,
-                                 nullptr, T, T_pad, heads, head_dim, chunk, workspace,
-                                 workspace_bytes, false, true, false);
+    const int rc = check_prefill("kda_prefill_prepare", q, k, v, gate, beta, nullptr, nullptr, T,
+                                 T_pad, heads, head_dim, chunk, workspace, workspace_bytes, true,
+                                 true, false);
     if (rc == 1) return ok();
     if (rc) return rc;
-    return hip_status(kda::launch_kda_prefill_prepare(q, k, gate, beta, T, T_pad, heads, head_dim,
+    return hip_status(kda::launch_kda_prefill_prepare(q, k, v, gate, beta, T, heads, head_dim,
                                                       chunk, workspace, stream),
                       "kda_prefill_prepare launch");
 }
 
-int kda_prefill_forward(const float *q, const float *k, const float *v, const float *gate,
-                        float *state, float *core, int32_t T, int32_t T_pad, int32_t heads,
+int kda_prefill_forward(float *state, float *core, int32_t T, int32_t T_pad, int32_t heads,
                         int32_t head_dim, int32_t chunk, float scale, const void *workspace,
                         size_t workspace_bytes, hipStream_t stream)
 {
-    const int rc = check_prefill("kda_prefill_forward", q, k, v, gate, nullptr, state, core, T,
-                                 T_pad, heads, head_dim, chunk, workspace, workspace_bytes, true,
-                                 false, true);
-    if (rc == 1) return ok();
-    if (rc) return rc;
-    return hip_status(kda::launch_kda_prefill_forward(q, k, v, gate, state, core, T, T_pad, heads,
-                                                      head_dim, chunk, scale, workspace, stream),
+    if (!head_dim_ok(head_dim) || !(chunk == 16 || chunk == 64))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill_forward: head_dim=%d chunk=%d", head_dim,
+                    chunk);
+    if (T < 0 || heads <= 0 || T_pad < T || T_pad % chunk)
+        return fail(KDA_ERR_SHAPE, "kda_prefill_forward: T=%d T_pad=%d heads=%d chunk=%d", T,
+                    T_pad, heads, chunk);
+    if (T == 0) return ok();
+    if (!state || !core || !workspace)
+        return fail(KDA_ERR_NULL, "kda_prefill_forward: null pointer argument");
+    const size_t need = kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "kda_prefill_forward: workspace %zu bytes < %zu needed",
+                    workspace_bytes, need);
+    if (!aligned16(state) || !aligned16(core) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(KDA_ERR_SHAPE, "kda_prefill_forward: misaligned pointer");
+    const size_t rows_b = (size_t)T_pad * heads * head_dim * 4;
+    const size_t st_b = (size_t)heads * head_dim * head_dim * 4;
+    if (overlap(core, rows_b, state, st_b) || overlap(workspace, need, core, rows_b) ||
+        overlap(workspace, need, state, st_b))
+        return fail(KDA_ERR_ALIAS, "kda_prefill_forward: core, state or workspace overlap");
+    return hip_status(kda::launch_kda_prefill_forward(state, core, T, heads, head_dim, chunk,
+                                                      scale, workspace, stream),
                       "kda_prefill_forward launch");
 }
 

@@ -36,18 +36,17 @@ hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float 
 size_t prefill_workspace_bytes(int T_pad, int heads, int head_dim, int chunk);
 
 // phase 1 (per chunk, state-free) and phase 2 (serial over chunks)
-hipError_t launch_kda_prefill_prepare(const float *q, const float *k, const float *gate,
-                                      const float *beta, int T, int T_pad, int heads,
+hipError_t launch_kda_prefill_prepare(const float *q, const float *k, const float *v,
+                                      const float *gate, const float *beta, int T, int heads,
                                       int head_dim, int chunk, void *workspace,
                                       hipStream_t stream);
-hipError_t launch_kda_prefill_forward(const float *q, const float *k, const float *v,
-                                      const float *gate, float *state, float *core, int T,
-                                      int T_pad, int heads, int head_dim, int chunk, float scale,
-                                      const void *workspace, hipStream_t stream);
+hipError_t launch_kda_prefill_forward(float *state, float *core, int T, int heads, int head_dim,
+                                      int chunk, float scale, const void *workspace,
+                                      hipStream_t stream);
 
 hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
                               const float *gate, const float *beta, float *state,
-                              float *core, int T, int T_pad, int heads, int head_dim,
-                              int chunk, float scale, void *workspace, hipStream_t stream);
+                              float *core, int T, int heads, int head_dim, int chunk,
+                              float scale, void *workspace, hipStream_t stream);
 
 }  // namespace kda

@@ -38,6 +38,8 @@
 // log-decay by a select at load time, never by arithmetic with their bits, so
 // poison in the tail cannot change a single bit of the result.  Chunks wholly
 // past T are not visited; core rows >= T are not written.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -180,16 +182,48 @@ __device__ __forceinline__ void chunk_cumsum(float4 (&G)[D / 16], float4 (&Gend)
 }
 
 // ---------------------------------------------------------------------------
-// kda_chunk_prep: per (chunk n, head h) -> Tb = (I + diag(b) A)^{-1} diag(b)
-// and P (masked lower triangle), both [C][C] fp32 in the workspace.
+// Per-chunk operand block in the workspace, for chunk n and head h at
+// float offset ((n*H + h) * kSize).  All parts are fp32:
+//   W   [C x D]  Tb (K e^{G})          U'  [C x D]  Tb V
+//   Qg  [C x D]  Q e^{G}               Kd  [C x D]  K e^{G_C - G}
+//   P   [C x C]  decayed scores (lower triangle incl. diagonal)
+//   Ec  [D]      e^{G_C}
+// with Tb = (I + diag(b) A)^{-1} diag(b).  Rows past T are exactly zero in
+// W, U', Qg, Kd and P (their k, q, v and beta were replaced by zero).
+//
+// The matrices are stored in fragment order: a fragment is what one wave
+// holds after one 16-byte-per-lane load (64 lanes x 4 floats), and it is
+// stored as 1 KiB of consecutive memory, so every load of the forward pass
+// is a fully contiguous 1 KiB read (row-strided 64-byte pieces read from L2
+// at well under a third of that rate).  With lane = 16*lg + lr:
+//   W, Qg  fragment (w, t8):  X[16w + lr][16t8 + 4lg + i]
+//   U'     fragment (jt, w):  U'[16w + 4lg + i][16jt + lr]
+//   P      fragment (w, w2):  P[16w + lr][16w2 + 4lg + i]
+//   Kd     fragment (t8, w2): Kd[16w2 + 4lg + i][16t8 + lr]
+// for i = 0..3, i.e. exactly the register layout of the MFMA operand or
+// accumulator that consumes it.
+// ---------------------------------------------------------------------------
+template <int D, int C>
+struct Blk {
+    static constexpr int NW = C / 16, DT = D / 16;
+    static constexpr int kW = 0, kU = C * D, kQ = 2 * C * D, kKd = 3 * C * D;
+    static constexpr int kP = 4 * C * D, kEc = 4 * C * D + C * C;
+    static constexpr int kSize = 4 * C * D + C * C + D;
+    // float offset of fragment (a, b) of a part with nb fragments per a
+    static __device__ __forceinline__ int frag(int a, int b, int nb) { return (a * nb + b) * 256; }
+};
+
+// ---------------------------------------------------------------------------
+// kda_chunk_prep: one workgroup per (chunk n, head h), all chunks in parallel.
 // ---------------------------------------------------------------------------
 template <int D, int C>
 __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
-    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ gate,
-    const float *__restrict__ beta, int T, int H, float *__restrict__ Tb_out,
-    float *__restrict__ P_out)
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
+    float *__restrict__ ws)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
+    using B = Blk<D, C>;
     const int n = blockIdx.x, h = blockIdx.y;
     // wave index, uniform across the wave (scalar register)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -198,17 +232,23 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     const int64_t tg = (int64_t)n * C + rl;
     const bool valid = tg < T;
     const int64_t roff = (tg * H + h) * D;
+    float *__restrict__ blk = ws + ((int64_t)n * H + h) * B::kSize;
 
     __shared__ __align__(16) float s_tot[NW * D];
-    __shared__ __align__(16) float s_kc[C][D + kPadK];
+    __shared__ __align__(16) float s_kc[C][D + kPadK];   // Kc, then Kg, then V
     __shared__ __align__(16) float s_M[C][C + kPadC];
     __shared__ __align__(16) float s_T[C][C + kPadC];
-    __shared__ float s_beta[C];
+    __shared__ __align__(16) float s_beta[C];
 
-    float4 K[DT], Q[DT], G[DT], Gend[DT];
+    float4 K[DT], Q[DT], G[DT], Gend[DT], V[DT];
     load_rows<D>(q, k, gate, roff, lg, K, Q, G);
+#pragma unroll
+    for (int t8 = 0; t8 < DT; ++t8)
+        V[t8] = *reinterpret_cast<const float4 *>(v + roff + 16 * t8 + 4 * lg);
     const float braw = beta[tg * H + h];
     select_rows<D>(valid, K, Q, G);
+#pragma unroll
+    for (int t8 = 0; t8 < DT; ++t8) V[t8] = valid ? V[t8] : zero4();
     if (lg == 0) s_beta[rl] = valid ? braw : 0.f;
     chunk_cumsum<D, NW>(G, Gend, s_tot, w, lane);
 
@@ -251,14 +291,16 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
             const float4 e = exp2_4(sub4(G[t8], ref));
             const float4 kr = mul4(K[t8], e), qr = mul4(Q[t8], e);
             const float4 kc = *reinterpret_cast<const float4 *>(&s_kc[16 * bj + lr][16 * t8 + 4 * lg]);
+            // A tile (rows r) and P tile transposed (rows s): the swapped
+            // operand order leaves P^T in the fragment order of P
             Aacc[bj] = mfma4(kr.x, kc.x, Aacc[bj]);
-            Pacc[bj] = mfma4(qr.x, kc.x, Pacc[bj]);
+            Pacc[bj] = mfma4(kc.x, qr.x, Pacc[bj]);
             Aacc[bj] = mfma4(kr.y, kc.y, Aacc[bj]);
-            Pacc[bj] = mfma4(qr.y, kc.y, Pacc[bj]);
+            Pacc[bj] = mfma4(kc.y, qr.y, Pacc[bj]);
             Aacc[bj] = mfma4(kr.z, kc.z, Aacc[bj]);
-            Pacc[bj] = mfma4(qr.z, kc.z, Pacc[bj]);
+            Pacc[bj] = mfma4(kc.z, qr.z, Pacc[bj]);
             Aacc[bj] = mfma4(kr.w, kc.w, Aacc[bj]);
-            Pacc[bj] = mfma4(qr.w, kc.w, Pacc[bj]);
+            Pacc[bj] = mfma4(kc.w, qr.w, Pacc[bj]);
         }
     }
 
@@ -271,27 +313,23 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
         }
         __syncthreads();
         if (!diag_ok) {
+            // sum_d x_r[d] k_s[d] e^{G_r[d] - G_s[d]} for one (r, s) of this
+            // block, with x = k (A) or q (P); rows past T contribute zero
+            auto pair = [&](int r, int sc, const float *__restrict__ x) {
+                float acc = 0.f;
+                const int64_t tr = (int64_t)n * C + r, ts = (int64_t)n * C + sc;
+                if (sc <= r && tr < T && ts < T) {
+                    const float *xr = x + (tr * H + h) * D, *ks = k + (ts * H + h) * D;
+                    for (int d = 0; d < D; ++d)
+                        acc = __builtin_fmaf(xr[d], ks[d] * exp2_fast(s_kc[r][d] - s_kc[sc][d]), acc);
+                }
+                return acc;
+            };
             float da[4], dp[4];
 #pragma unroll
             for (int vv = 0; vv < 4; ++vv) {
-                const int r = 16 * w + 4 * lg + vv, s = 16 * w + lr;
-                float a = 0.f, p = 0.f;
-                const int64_t tr = (int64_t)n * C + r, ts = (int64_t)n * C + s;
-                if (s <= r && ts < T) {
-                    const float *kr = k + (tr * H + h) * D, *qr = q + (tr * H + h) * D;
-                    const float *ks = k + (ts * H + h) * D;
-                    const bool rv = tr < T;
-                    for (int d = 0; d < D; ++d) {
-                        const float e = exp2_fast(s_kc[r][d] - s_kc[s][d]);
-                        const float kse = ks[d] * e;
-                        if (rv) {
-                            a = __builtin_fmaf(kr[d], kse, a);
-                            p = __builtin_fmaf(qr[d], kse, p);
-                        }
-                    }
-                }
-                da[vv] = a;
-                dp[vv] = p;
+                da[vv] = pair(16 * w + 4 * lg + vv, 16 * w + lr, k);   // A tile layout
+                dp[vv] = pair(16 * w + lr, 16 * w + 4 * lg + vv, q);   // P^T tile layout
             }
 #pragma unroll
             for (int bj = 0; bj < NW; ++bj)
@@ -300,22 +338,27 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
         }
     }
 
-    // Masked tiles: M = diag(b) A (strictly lower) to LDS, P to the workspace.
-    float *Pn = P_out + ((int64_t)n * H + h) * C * C;
+    // Masked tiles: M = diag(b) A (strictly lower) to LDS; P to the workspace
+    // as fragments (w, bj), the blocks above the diagonal as zeros so the
+    // forward pass can run the whole block row without branching.
+    float *Pf = blk + B::kP;
 #pragma unroll
     for (int bj = 0; bj < NW; ++bj) {
-        if (bj > w) continue;
+        float4 pv = zero4();
+        if (bj <= w) {
+            float pe[4];
 #pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-            const int r = 16 * w + 4 * lg + vv, s = 16 * bj + lr;
-            float a = Aacc[bj][vv], p = Pacc[bj][vv];
-            if (bj == w) {
-                if (s >= r) a = 0.f;
-                if (s > r) p = 0.f;
+            for (int vv = 0; vv < 4; ++vv) {
+                const int r = 16 * w + 4 * lg + vv, sc = 16 * bj + lr;
+                float a = Aacc[bj][vv];
+                if (bj == w && sc >= r) a = 0.f;
+                s_M[r][sc] = s_beta[r] * a;
+                // P^T element: s = 16bj + 4lg + vv, r = 16w + lr
+                pe[vv] = (bj == w && 4 * lg + vv > lr) ? 0.f : Pacc[bj][vv];
             }
-            s_M[r][s] = s_beta[r] * a;
-            Pn[(int64_t)r * C + s] = p;
+            pv = make_float4(pe[0], pe[1], pe[2], pe[3]);
         }
+        *reinterpret_cast<float4 *>(Pf + B::frag(w, bj, NW) + 4 * lane) = pv;
     }
     __syncthreads();
 
@@ -359,95 +402,100 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
         __syncthreads();
     }
 
-    // Tb = T diag(b), lower block triangle of block row w.
-    float *Tn = Tb_out + ((int64_t)n * H + h) * C * C;
+    // Row operands that need no product: Qg (already in fragment layout),
+    // Ec; Kg into LDS as the left operand of W^T = Kg^T Tb^T.  (s_kc is free:
+    // the fallback used it before the barriers of the inversion.)
+    float4 Kd[DT];
 #pragma unroll
-    for (int bj = 0; bj < NW; ++bj) {
-        if (bj > w) continue;
-        const int s = 16 * bj + lr;
-        const float bs = s_beta[s];
+    for (int t8 = 0; t8 < DT; ++t8) {
+        const float4 eg = exp2_4(G[t8]);
+        *reinterpret_cast<float4 *>(blk + B::kQ + B::frag(w, t8, DT) + 4 * lane) = mul4(Q[t8], eg);
+        *reinterpret_cast<float4 *>(&s_kc[rl][16 * t8 + 4 * lg]) = mul4(K[t8], eg);
+        Kd[t8] = mul4(K[t8], exp2_4(sub4(Gend[t8], G[t8])));
+        if (w == 0 && lr == 0)
+            *reinterpret_cast<float4 *>(blk + B::kEc + 16 * t8 + 4 * lg) = exp2_4(Gend[t8]);
+    }
+    __syncthreads();
+
+    // W = Tb Kg, then U' = Tb V, then the Kd fragments: wave w owns channel
+    // tiles t8 = w (mod NW), all row blocks (balanced across waves).
+    // Tb = T diag(b) is formed on the fly from s_T and s_beta.  W is computed
+    // transposed (operands swapped), which leaves each output tile in W's
+    // fragment order; U' in its natural orientation is already in U''s.
 #pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-            const int r = 16 * w + 4 * lg + vv;
-            Tn[(int64_t)r * C + s] = s_T[r][s] * bs;
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int t8 = 0; t8 < DT; ++t8) {
+            if (t8 % NW != w) continue;
+#pragma unroll
+            for (int bi = 0; bi < NW; ++bi) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w2 = 0; w2 <= bi; ++w2) {
+                    const float4 ta = mul4(
+                        *reinterpret_cast<const float4 *>(&s_T[16 * bi + lr][16 * w2 + 4 * lg]),
+                        *reinterpret_cast<const float4 *>(&s_beta[16 * w2 + 4 * lg]));
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const float x = s_kc[16 * w2 + 4 * lg + kk][16 * t8 + lr];
+                        acc = pass == 0 ? mfma4(x, get4(ta, kk), acc) : mfma4(get4(ta, kk), x, acc);
+                    }
+                }
+                float *dst = pass == 0 ? blk + B::kW + B::frag(bi, t8, DT)
+                                       : blk + B::kU + B::frag(t8, bi, NW);
+                *reinterpret_cast<float4 *>(dst + 4 * lane) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t8 = 0; t8 < DT; ++t8)   // next right operand: V, then Kd
+            *reinterpret_cast<float4 *>(&s_kc[rl][16 * t8 + 4 * lg]) = pass == 0 ? V[t8] : Kd[t8];
+        __syncthreads();
+    }
+    // Kd fragments (t8, w2): a transpose of the 16 x 16 tiles through LDS
+#pragma unroll
+    for (int t8 = 0; t8 < DT; ++t8) {
+        if (t8 % NW != w) continue;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            const float4 kv = make_float4(s_kc[16 * w2 + 4 * lg + 0][16 * t8 + lr],
+                                          s_kc[16 * w2 + 4 * lg + 1][16 * t8 + lr],
+                                          s_kc[16 * w2 + 4 * lg + 2][16 * t8 + lr],
+                                          s_kc[16 * w2 + 4 * lg + 3][16 * t8 + lr]);
+            *reinterpret_cast<float4 *>(blk + B::kKd + B::frag(t8, w2, NW) + 4 * lane) = kv;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // kda_chunk_fwd: per (head h, value slice j0..j0+15), serial over chunks.
-//
-// Software pipeline: the global loads of chunk n+1 (this wave's 16 rows of
-// k, q, gate, the v slice, and its rows of Tb and P) are issued at the top of
-// iteration n and consumed after its last barrier, so their latency overlaps
-// the MFMA work of chunk n.  The in-chunk scan of chunk n+1 shares that last
-// barrier with the state broadcast, leaving three barriers per chunk:
-//   B1  X rows and Kd rows visible      (U needs X of waves <= w)
-//   B2  U rows visible                  (P U and the state update need U)
-//   B3  new state slice and scan totals visible
+// Wave w owns chunk rows 16w..16w+15; the state slice S[:, j0..j0+15] lives
+// in registers of every wave in MFMA output layout.  Per chunk:
+//   U  = U' - W S            (D-deep, this wave's rows)
+//   QS = Qg S                (D-deep)
+//   -- B1: U rows visible --
+//   O  = scale (QS + P U)    (lower block triangle)
+//   S' = Ec * S + KdT U      (C-deep, channel tiles t8 = w mod NW)
+//   -- B2: new state slice visible --
+// Every operand arrives pre-laid-out from kda_chunk_prep.  Loads of chunk
+// n+1's operands are issued as soon as chunk n's copy of that operand has
+// been consumed (rolling prefetch), so they overlap the rest of the chunk.
 // ---------------------------------------------------------------------------
 template <int D, int C>
-struct FwdRows {
-    float4 K[D / 16], Q[D / 16], G[D / 16];   // A-layout row slices of k, q, gate
-    float V[4];                               // v[16w + 4lg + i][j0 + lr]
-    float4 Tb[C / 16], P[C / 16];             // Tb, P row 16w + lr, columns 16w2 + 4lg ..
-};
-
-template <int D, int C>
-__device__ __forceinline__ void fwd_load(FwdRows<D, C> &R, const float *__restrict__ q,
-                                         const float *__restrict__ k, const float *__restrict__ v,
-                                         const float *__restrict__ gate,
-                                         const float *__restrict__ Tb,
-                                         const float *__restrict__ Pm, int n, int T, int H, int h,
-                                         int j0, int w, int lr, int lg)
-{
-    constexpr int NW = C / 16;
-    const int64_t tg = (int64_t)n * C + 16 * w + lr;
-    load_rows<D>(q, k, gate, (tg * H + h) * D, lg, R.K, R.Q, R.G);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + i;
-        R.V[i] = v[(tr * H + h) * D + j0 + lr];
-    }
-    // the blocks above the diagonal are loaded (in bounds) but never used
-    const int64_t toff = (((int64_t)n * H + h) * C + 16 * w + lr) * C + 4 * lg;
-#pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) {
-        R.Tb[w2] = *reinterpret_cast<const float4 *>(Tb + toff + 16 * w2);
-        R.P[w2] = *reinterpret_cast<const float4 *>(Pm + toff + 16 * w2);
-    }
-}
-
-// Pad-row selects of a loaded chunk (see select_rows), applied when the
-// chunk's values are first used.
-template <int D, int C>
-__device__ __forceinline__ void fwd_select(FwdRows<D, C> &R, int n, int T, int w, int lr, int lg)
-{
-    select_rows<D>((int64_t)n * C + 16 * w + lr < T, R.K, R.Q, R.G);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        R.V[i] = ((int64_t)n * C + 16 * w + 4 * lg + i < T) ? R.V[i] : 0.f;
-}
-
-template <int D, int C>
 __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
-    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    const float *__restrict__ gate, float *__restrict__ state, float *__restrict__ core,
-    const float *__restrict__ Tb, const float *__restrict__ Pm, int T, int NC, int H,
-    float scale)
+    const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
+    int NC, int H, float scale)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
+    constexpr int OWN = (DT + NW - 1) / NW;   // channel tiles per wave in the state update
+    using B = Blk<D, C>;
     // all value slices of one head share an XCD (workgroups are dealt to the
-    // 8 XCDs round-robin), so they share that XCD's L2 copy of q/k/gate/Tb/P
+    // 8 XCDs round-robin), so they share that XCD's L2 copy of the operands
     const int h = blockIdx.x % H, jt = blockIdx.x / H, j0 = 16 * jt;
-    // wave index, uniform across the wave (scalar register)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
     const int rl = 16 * w + lr;
 
-    __shared__ __align__(16) float s_tot[NW * D];
-    __shared__ __align__(16) float s_kd[C][D + kPadK];
-    __shared__ float s_x[C][16 + kPad16];
     __shared__ float s_u[C][16 + kPad16];
     __shared__ float s_S[D][16 + kPad16];
 
@@ -459,151 +507,203 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) Sr[t8][i] = Sg[(int64_t)(16 * t8 + 4 * lg + i) * D + j0 + lr];
 
-    FwdRows<D, C> R;
-    float4 Kg[DT], Qg[DT], Gend[DT];
-    float V[4];
-    float4 TbR[NW], PR[NW];
+    // the state tiles this wave updates (t8 = w + NW*o; a wave with no tile
+    // of its own, possible only when D/16 < C/16, repeats the last tile and
+    // writes the same values as its owner)
+    auto own_tile = [&](int o) { return min(w + NW * o, DT - 1); };
+    floatx4 Sown[OWN];
+#pragma unroll
+    for (int o = 0; o < OWN; ++o)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            Sown[o][i] = Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + j0 + lr];
 
-    // chunk 0: load, scan, operands
-    fwd_load<D, C>(R, q, k, v, gate, Tb, Pm, 0, T, H, h, j0, w, lr, lg);
-    fwd_select<D, C>(R, 0, T, w, lr, lg);
-    scan_local<D, NW>(R.G, s_tot, w, lane);
-    if (NW > 1) __syncthreads();
-
-    for (int n = 0; n < NC; ++n) {
-        // ---- operands of chunk n from R (its scan totals are in s_tot) ----
-        scan_carry<D, NW>(R.G, Gend, s_tot, w, lane);
+    auto block = [&](int n) { return ws + ((int64_t)n * H + h) * B::kSize; };
+    // One chunk's operands in registers (A layout unless noted).
+    struct Ops {
+        float4 Wr[DT], Qr[DT], Pr[NW], Kd[OWN][NW], Ec[OWN];
+        float4 Up;     // U'[16w + 4lg + i][j0 + lr], i = 0..3
+    };
+    auto load_ops = [&](Ops &R, const float *b) {
+        R.Up = *reinterpret_cast<const float4 *>(b + B::kU + B::frag(jt, w, NW) + 4 * lane);
 #pragma unroll
         for (int t8 = 0; t8 < DT; ++t8) {
-            const float4 ed = exp2_4(sub4(Gend[t8], R.G[t8]));
-            *reinterpret_cast<float4 *>(&s_kd[rl][16 * t8 + 4 * lg]) = mul4(R.K[t8], ed);
-            const float4 eg = exp2_4(R.G[t8]);
-            Kg[t8] = mul4(R.K[t8], eg);
-            Qg[t8] = mul4(R.Q[t8], eg);
+            R.Wr[t8] = *reinterpret_cast<const float4 *>(b + B::kW + B::frag(w, t8, DT) + 4 * lane);
+            R.Qr[t8] = *reinterpret_cast<const float4 *>(b + B::kQ + B::frag(w, t8, DT) + 4 * lane);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) V[i] = R.V[i];
+        for (int w2 = 0; w2 < NW; ++w2)
+            R.Pr[w2] = *reinterpret_cast<const float4 *>(b + B::kP + B::frag(w, w2, NW) + 4 * lane);
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-            TbR[w2] = R.Tb[w2];
-            PR[w2] = R.P[w2];
+        for (int o = 0; o < OWN; ++o) {
+            const int t8 = own_tile(o);
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2)
+                R.Kd[o][w2] = *reinterpret_cast<const float4 *>(b + B::kKd + B::frag(t8, w2, NW) + 4 * lane);
+            R.Ec[o] = *reinterpret_cast<const float4 *>(b + B::kEc + 16 * t8 + 4 * lg);
         }
-        // ---- prefetch chunk n+1 ----
-        if (n + 1 < NC) fwd_load<D, C>(R, q, k, v, gate, Tb, Pm, n + 1, T, H, h, j0, w, lr, lg);
+    };
 
-        // X = V - (K e^G) S ;  QS = (Q e^G) S   (rows 16w.., D-deep products)
-        floatx4 X = {V[0], V[1], V[2], V[3]}, QS = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t8 = 0; t8 < DT; ++t8) {
-            X = mfma4(-Kg[t8].x, Sr[t8][0], X);
-            QS = mfma4(Qg[t8].x, Sr[t8][0], QS);
-            X = mfma4(-Kg[t8].y, Sr[t8][1], X);
-            QS = mfma4(Qg[t8].y, Sr[t8][1], QS);
-            X = mfma4(-Kg[t8].z, Sr[t8][2], X);
-            QS = mfma4(Qg[t8].z, Sr[t8][2], QS);
-            X = mfma4(-Kg[t8].w, Sr[t8][3], X);
-            QS = mfma4(Qg[t8].w, Sr[t8][3], QS);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_x[16 * w + 4 * lg + i][lr] = X[i];
-        __syncthreads();   // B1
+    Ops X, Y;
+    load_ops(X, block(0));
+    // Drain the prologue's loads once; inside the loop the only loads in
+    // flight are the next chunk's, issued a whole chunk before their use.
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
 
-        // U = Tb X  (block row w, lower triangle)
-        floatx4 U = {0.f, 0.f, 0.f, 0.f};
+    // One chunk: consume `cur`, prefetch chunk n+1 into `nxt`.  The two
+    // operand sets alternate (the loop is unrolled by two), so no register
+    // copies tie the prefetch to a wait.  The body has no branches (a branch
+    // splits it into blocks across which the compiler's wait counting turns
+    // conservative).  LAST adds the row guard on the output store: only the
+    // last chunk can hold rows >= T.
+    auto chunk = [&](int n, Ops &cur, Ops &nxt, auto last) {
+        constexpr bool LAST = decltype(last)::value;
+        // U = U' - W S = -(W S - U') ;  QS = Qg S.  U' is consumed before
+        // its register is reloaded.  Each product runs as two independent
+        // accumulators (even / odd channel tiles), four chains interleaved.
+        // The next chunk's operands are loaded in small groups between the
+        // MFMA groups (same order as load_ops), so the memory pipeline is fed
+        // steadily instead of stalling the wave on one burst of loads.
+        const float *bn = block(min(n + 1, NC - 1));   // the last chunk reloads itself
+        floatx4 WS0 = {-cur.Up.x, -cur.Up.y, -cur.Up.z, -cur.Up.w};
+        floatx4 WS1 = {0.f, 0.f, 0.f, 0.f}, QS0 = WS1, QS1 = WS1;
+        __builtin_amdgcn_sched_barrier(0);
+        nxt.Up = *reinterpret_cast<const float4 *>(bn + B::kU + B::frag(jt, w, NW) + 4 * lane);
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-            if (w2 > w) continue;
-            U = mfma4(TbR[w2].x, s_x[16 * w2 + 4 * lg + 0][lr], U);
-            U = mfma4(TbR[w2].y, s_x[16 * w2 + 4 * lg + 1][lr], U);
-            U = mfma4(TbR[w2].z, s_x[16 * w2 + 4 * lg + 2][lr], U);
-            U = mfma4(TbR[w2].w, s_x[16 * w2 + 4 * lg + 3][lr], U);
+        for (int t8 = 0; t8 < DT; t8 += 2) {
+#pragma unroll
+            for (int u = 0; u < 2 && t8 + u < DT; ++u) {
+                nxt.Wr[t8 + u] = *reinterpret_cast<const float4 *>(bn + B::kW + B::frag(w, t8 + u, DT) + 4 * lane);
+                nxt.Qr[t8 + u] = *reinterpret_cast<const float4 *>(bn + B::kQ + B::frag(w, t8 + u, DT) + 4 * lane);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                WS0 = mfma4(get4(cur.Wr[t8], i), Sr[t8][i], WS0);
+                QS0 = mfma4(get4(cur.Qr[t8], i), Sr[t8][i], QS0);
+                if (t8 + 1 < DT) {
+                    WS1 = mfma4(get4(cur.Wr[t8 + 1], i), Sr[t8 + 1][i], WS1);
+                    QS1 = mfma4(get4(cur.Qr[t8 + 1], i), Sr[t8 + 1][i], QS1);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_u[16 * w + 4 * lg + i][lr] = U[i];
-        __syncthreads();   // B2
+        for (int i = 0; i < 4; ++i) s_u[16 * w + 4 * lg + i][lr] = -(WS0[i] + WS1[i]);
+        __syncthreads();   // B1: U rows visible
 
-        // O = scale (QS + P U)
-        floatx4 O = QS;
+        // O = scale (QS + P U) and S' = Ec * S + KdT U for the owned tiles,
+        // interleaved: P U and each owned tile's product run as two chains
+        // (even / odd 16-row blocks of U).  P's blocks above the diagonal are
+        // zero.
+        float uk[NW][4];
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-            if (w2 > w) continue;
-            O = mfma4(PR[w2].x, s_u[16 * w2 + 4 * lg + 0][lr], O);
-            O = mfma4(PR[w2].y, s_u[16 * w2 + 4 * lg + 1][lr], O);
-            O = mfma4(PR[w2].z, s_u[16 * w2 + 4 * lg + 2][lr], O);
-            O = mfma4(PR[w2].w, s_u[16 * w2 + 4 * lg + 3][lr], O);
+        for (int w2 = 0; w2 < NW; ++w2)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) uk[w2][kk] = s_u[16 * w2 + 4 * lg + kk][lr];
+        floatx4 O0 = {QS0[0] + QS1[0], QS0[1] + QS1[1], QS0[2] + QS1[2], QS0[3] + QS1[3]};
+        floatx4 O1 = {0.f, 0.f, 0.f, 0.f};
+        floatx4 A0[OWN], A1[OWN];
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) {
+            A0[o] = floatx4{Sown[o][0] * cur.Ec[o].x, Sown[o][1] * cur.Ec[o].y,
+                            Sown[o][2] * cur.Ec[o].z, Sown[o][3] * cur.Ec[o].w};
+            A1[o] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int w2 = 0; w2 < NW; w2 += 2) {
+#pragma unroll
+            for (int u = 0; u < 2 && w2 + u < NW; ++u)
+                nxt.Pr[w2 + u] = *reinterpret_cast<const float4 *>(bn + B::kP + B::frag(w, w2 + u, NW) + 4 * lane);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                O0 = mfma4(get4(cur.Pr[w2], kk), uk[w2][kk], O0);
+#pragma unroll
+                for (int o = 0; o < OWN; ++o)
+                    A0[o] = mfma4(get4(cur.Kd[o][w2], kk), uk[w2][kk], A0[o]);
+                if (w2 + 1 < NW) {
+                    O1 = mfma4(get4(cur.Pr[w2 + 1], kk), uk[w2 + 1][kk], O1);
+#pragma unroll
+                    for (int o = 0; o < OWN; ++o)
+                        A1[o] = mfma4(get4(cur.Kd[o][w2 + 1], kk), uk[w2 + 1][kk], A1[o]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) {
+            const int t8 = own_tile(o);
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2)
+                nxt.Kd[o][w2] = *reinterpret_cast<const float4 *>(bn + B::kKd + B::frag(t8, w2, NW) + 4 * lane);
+            nxt.Ec[o] = *reinterpret_cast<const float4 *>(bn + B::kEc + 16 * t8 + 4 * lg);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + i;
-            if (tr < T) core[(tr * H + h) * D + j0 + lr] = scale * O[i];
+            if (!LAST || tr < T) core[(tr * H + h) * D + j0 + lr] = scale * (O0[i] + O1[i]);
         }
-
-        // S' = diag(e^{G_C}) S + Kd^T U for the channel tiles this wave owns
 #pragma unroll
-        for (int t8 = 0; t8 < DT; ++t8) {
-            if (t8 % NW != w) continue;
-            const float4 ec = exp2_4(Gend[t8]);
-            floatx4 acc = {Sr[t8][0] * ec.x, Sr[t8][1] * ec.y, Sr[t8][2] * ec.z, Sr[t8][3] * ec.w};
+        for (int o = 0; o < OWN; ++o) {
 #pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    acc = mfma4(s_kd[16 * w2 + 4 * lg + kk][16 * t8 + lr],
-                                s_u[16 * w2 + 4 * lg + kk][lr], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s_S[16 * t8 + 4 * lg + i][lr] = acc[i];
+            for (int i = 0; i < 4; ++i) {
+                Sown[o][i] = A0[o][i] + A1[o][i];
+                s_S[16 * own_tile(o) + 4 * lg + i][lr] = Sown[o][i];
+            }
         }
-        // in-row scan of chunk n+1 (its loads were issued above)
-        if (n + 1 < NC) {
-            fwd_select<D, C>(R, n + 1, T, w, lr, lg);
-            scan_local<D, NW>(R.G, s_tot, w, lane);
-        }
-        __syncthreads();   // B3
+        __syncthreads();   // B2: new state slice visible
 #pragma unroll
         for (int t8 = 0; t8 < DT; ++t8)
 #pragma unroll
             for (int i = 0; i < 4; ++i) Sr[t8][i] = s_S[16 * t8 + 4 * lg + i][lr];
+    };
+
+    int n = 0;
+    for (; n + 2 < NC; n += 2) {
+        chunk(n, X, Y, std::false_type{});
+        chunk(n + 1, Y, X, std::false_type{});
+    }
+    if (n + 1 < NC) {       // two chunks left
+        chunk(n, X, Y, std::false_type{});
+        chunk(n + 1, Y, X, std::true_type{});
+    } else {                // one chunk left
+        chunk(n, X, Y, std::true_type{});
     }
 
 #pragma unroll
-    for (int t8 = 0; t8 < DT; ++t8) {
-        if (t8 % NW != w) continue;
+    for (int o = 0; o < OWN; ++o)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Sg[(int64_t)(16 * t8 + 4 * lg + i) * D + j0 + lr] = Sr[t8][i];
-    }
+        for (int i = 0; i < 4; ++i)
+            Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + j0 + lr] = Sown[o][i];
 }
 
 size_t prefill_workspace_bytes(int T_pad, int heads, int head_dim, int chunk)
 {
-    (void)head_dim;
-    // Tb and P: [T_pad/chunk, heads, chunk, chunk] fp32 each
-    return 2 * (size_t)(T_pad / chunk) * heads * chunk * chunk * sizeof(float);
+    // one operand block per (chunk, head): 4*C*D + C*C + D fp32
+    const size_t blk = 4 * (size_t)chunk * head_dim + (size_t)chunk * chunk + head_dim;
+    return (size_t)(T_pad / chunk) * heads * blk * sizeof(float);
 }
 
 template <int D, int C>
-static hipError_t prepare_t(const float *q, const float *k, const float *gate,
-                            const float *beta, int T, int T_pad, int H, void *workspace,
-                            hipStream_t stream)
+static hipError_t prepare_t(const float *q, const float *k, const float *v, const float *gate,
+                            const float *beta, int T, int H, void *workspace, hipStream_t stream)
 {
     const int NC = (T + C - 1) / C;
-    float *Tb = static_cast<float *>(workspace);
-    float *Pm = Tb + (size_t)(T_pad / C) * H * C * C;
     hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C>), dim3(NC, H), dim3(PrefCfg<D, C>::kThreads),
-                       0, stream, q, k, gate, beta, T, H, Tb, Pm);
+                       0, stream, q, k, v, gate, beta, T, H, static_cast<float *>(workspace));
     return hipGetLastError();
 }
 
 template <int D, int C>
-static hipError_t forward_t(const float *q, const float *k, const float *v, const float *gate,
-                            float *state, float *core, int T, int T_pad, int H, float scale,
+static hipError_t forward_t(float *state, float *core, int T, int H, float scale,
                             const void *workspace, hipStream_t stream)
 {
     const int NC = (T + C - 1) / C;
-    const float *Tb = static_cast<const float *>(workspace);
-    const float *Pm = Tb + (size_t)(T_pad / C) * H * C * C;
     hipLaunchKernelGGL((kda_chunk_fwd_kernel<D, C>), dim3(H * PrefCfg<D, C>::kDT),
-                       dim3(PrefCfg<D, C>::kThreads), 0, stream, q, k, v, gate, state, core, Tb,
-                       Pm, T, NC, H, scale);
+                       dim3(PrefCfg<D, C>::kThreads), 0, stream,
+                       static_cast<const float *>(workspace), state, core, T, NC, H, scale);
     return hipGetLastError();
 }
 
@@ -613,33 +713,31 @@ static hipError_t forward_t(const float *q, const float *k, const float *v, cons
     : (head_dim == 16 && chunk == 64)  ? FN<16, 64>(__VA_ARGS__)             \
                                        : FN<16, 16>(__VA_ARGS__)
 
-hipError_t launch_kda_prefill_prepare(const float *q, const float *k, const float *gate,
-                                      const float *beta, int T, int T_pad, int heads,
+hipError_t launch_kda_prefill_prepare(const float *q, const float *k, const float *v,
+                                      const float *gate, const float *beta, int T, int heads,
                                       int head_dim, int chunk, void *workspace,
                                       hipStream_t stream)
 {
-    return KDA_PREFILL_DISPATCH(prepare_t, q, k, gate, beta, T, T_pad, heads, workspace, stream);
+    return KDA_PREFILL_DISPATCH(prepare_t, q, k, v, gate, beta, T, heads, workspace, stream);
 }
 
-hipError_t launch_kda_prefill_forward(const float *q, const float *k, const float *v,
-                                      const float *gate, float *state, float *core, int T,
-                                      int T_pad, int heads, int head_dim, int chunk, float scale,
-                                      const void *workspace, hipStream_t stream)
+hipError_t launch_kda_prefill_forward(float *state, float *core, int T, int heads, int head_dim,
+                                      int chunk, float scale, const void *workspace,
+                                      hipStream_t stream)
 {
-    return KDA_PREFILL_DISPATCH(forward_t, q, k, v, gate, state, core, T, T_pad, heads, scale,
-                                workspace, stream);
+    return KDA_PREFILL_DISPATCH(forward_t, state, core, T, heads, scale, workspace, stream);
 }
 
 hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
                               const float *gate, const float *beta, float *state,
-                              float *core, int T, int T_pad, int heads, int head_dim,
-                              int chunk, float scale, void *workspace, hipStream_t stream)
+                              float *core, int T, int heads, int head_dim, int chunk,
+                              float scale, void *workspace, hipStream_t stream)
 {
-    hipError_t e = launch_kda_prefill_prepare(q, k, gate, beta, T, T_pad, heads, head_dim, chunk,
+    hipError_t e = launch_kda_prefill_prepare(q, k, v, gate, beta, T, heads, head_dim, chunk,
                                               workspace, stream);
     if (e != hipSuccess) return e;
-    return launch_kda_prefill_forward(q, k, v, gate, state, core, T, T_pad, heads, head_dim,
-                                      chunk, scale, workspace, stream);
+    return launch_kda_prefill_forward(state, core, T, heads, head_dim, chunk, scale, workspace,
+                                      stream);
 }
 
 }  // namespace kda

@@ -131,30 +131,27 @@ int kda_prefill(const float *q, const float *k, const float *v,
  * kda_prefill_prepare / kda_prefill_forward — the two phases of kda_prefill,
  * callable separately ("Glm5NextLayer" page, split-prefill section: a batched
  * linear-attention prefill runs its phases as separate steps).  Calling
- * prepare then forward on one stream, with the same arguments and workspace,
- * gives bitwise the same result as kda_prefill.
- *   prepare: reads q, k, gate, beta (rows < T); writes, per chunk and head,
- *            the UT transform of the chunk (lower-triangular chunk x chunk)
- *            and the decayed query-key scores into the workspace.  It does
- *            not read or write the state, so it may run ahead of the forward
- *            pass of an earlier segment.
- *   forward: reads q, k, v, gate and the prepared workspace; walks the
- *            chunks in order from the carried state; writes core rows < T and
- *            the final state.
+ * prepare then forward on one stream with the same T, T_pad, heads,
+ * head_dim, chunk and workspace gives bitwise the same result as kda_prefill.
+ *   prepare: reads q, k, v, gate, beta (rows < T) and writes, per chunk and
+ *            head, every operand of the chunk-state walk into the workspace
+ *            (the UT-transformed keys and values, decayed queries and keys,
+ *            the decayed query-key scores, the chunk decay).  It reads no
+ *            state: it may run before the carried state is known.
+ *   forward: reads only the workspace and the carried state; walks the
+ *            chunks in order; writes core rows < T and the final state.
  * Arguments, layouts and errors are those of kda_prefill.
  * ------------------------------------------------------------------------ */
-int kda_prefill_prepare(const float *q, const float *k, const float *gate,
-                        const float *beta, int32_t T, int32_t T_pad,
-                        int32_t heads, int32_t head_dim, int32_t chunk,
-                        void *workspace, size_t workspace_bytes,
+int kda_prefill_prepare(const float *q, const float *k, const float *v,
+                        const float *gate, const float *beta, int32_t T,
+                        int32_t T_pad, int32_t heads, int32_t head_dim,
+                        int32_t chunk, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
-int kda_prefill_forward(const float *q, const float *k, const float *v,
-                        const float *gate, float *state, float *core,
-                        int32_t T, int32_t T_pad, int32_t heads,
-                        int32_t head_dim, int32_t chunk, float scale,
-                        const void *workspace, size_t workspace_bytes,
-                        hipStream_t stream);
+int kda_prefill_forward(float *state, float *core, int32_t T, int32_t T_pad,
+                        int32_t heads, int32_t head_dim, int32_t chunk,
+                        float scale, const void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * kda_decode — one token for each of B independent sequences.

@@ -156,8 +156,8 @@ def test_prefill_phases_equal_one_call_bitwise():
     ws = torch.empty(kda.kda_prefill_workspace_bytes(T_pad, H, D, C), dtype=torch.uint8, device="cuda")
     kw = dict(T=T, T_pad=T_pad, heads=H, head_dim=D, chunk=C)
     say("phases")
-    kda.kda_prefill_prepare(q, k, g, b, ws, **kw)
-    kda.kda_prefill_forward(q, k, v, g, st, core, ws, scale=D ** -0.5, **kw)
+    kda.kda_prefill_prepare(q, k, v, g, b, ws, **kw)
+    kda.kda_prefill_forward(st, core, ws, scale=D ** -0.5, **kw)
     torch.cuda.synchronize()
     assert np.array_equal(core.cpu().numpy().view(np.int32), core_a.view(np.int32))
     assert np.array_equal(st.cpu().numpy().view(np.int32), S_a.view(np.int32))

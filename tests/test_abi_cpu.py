@@ -51,7 +51,8 @@ F = 1 << 48
 
 def test_prefill_validation(lib):
     ws = lib.kda_prefill_workspace_bytes(4096, 32, 128, 64)
-    assert ws == 2 * (4096 // 64) * 32 * 64 * 64 * 4
+    # one operand block per (chunk, head): 4*C*D + C*C + D floats
+    assert ws == (4096 // 64) * 32 * (4 * 64 * 128 + 64 * 64 + 128) * 4
     assert lib.kda_prefill_workspace_bytes(100, 32, 128, 64) == 0     # T_pad % chunk
     args = lambda **kw: [kw.get(n, d) for n, d in (
         ("q", A), ("k", B), ("v", C), ("gate", Dp), ("beta", E), ("state", F), ("core", 1 << 52),

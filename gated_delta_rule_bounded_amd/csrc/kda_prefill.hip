@@ -240,30 +240,37 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     __shared__ __align__(16) float s_T[C][C + kPadC];
     __shared__ __align__(16) float s_beta[C];
 
-    float4 K[DT], Q[DT], G[DT], Gend[DT], V[DT];
+    // Register lifetimes are kept short so two workgroups fit on a CU: Q e^G,
+    // e^{G_C} and Kd = K e^{G_C - G} are formed right after the scan, K e^G
+    // goes to LDS right after the A/P products, v is loaded only for U'.
+    float4 K[DT], Q[DT], G[DT], Kd[DT];
     load_rows<D>(q, k, gate, roff, lg, K, Q, G);
-#pragma unroll
-    for (int t8 = 0; t8 < DT; ++t8)
-        V[t8] = *reinterpret_cast<const float4 *>(v + roff + 16 * t8 + 4 * lg);
     const float braw = beta[tg * H + h];
     select_rows<D>(valid, K, Q, G);
-#pragma unroll
-    for (int t8 = 0; t8 < DT; ++t8) V[t8] = valid ? V[t8] : zero4();
     if (lg == 0) s_beta[rl] = valid ? braw : 0.f;
-    chunk_cumsum<D, NW>(G, Gend, s_tot, w, lane);
+    {
+        float4 Gend[DT];
+        chunk_cumsum<D, NW>(G, Gend, s_tot, w, lane);
+#pragma unroll
+        for (int t8 = 0; t8 < DT; ++t8) {
+            *reinterpret_cast<float4 *>(blk + B::kQ + B::frag(w, t8, DT) + 4 * lane) =
+                mul4(Q[t8], exp2_4(G[t8]));
+            Kd[t8] = mul4(K[t8], exp2_4(sub4(Gend[t8], G[t8])));
+            if (w == 0 && lr == 0)
+                *reinterpret_cast<float4 *>(blk + B::kEc + 16 * t8 + 4 * lg) = exp2_4(Gend[t8]);
+        }
+    }
 
     // Column operand Kc = K e^{G_last - G}, relative to the last row of this
     // wave's 16-row block (all factors <= 1); also the block's decay span.
     float span = 0.f;
-    float4 Gl[DT];
 #pragma unroll
     for (int t8 = 0; t8 < DT; ++t8) {
-        Gl[t8] = shfl4(G[t8], (lane & 48) | 15);
+        const float4 Gl = shfl4(G[t8], (lane & 48) | 15);
         const float4 Gf = shfl4(G[t8], lane & 48);
-        const float4 e = exp2_4(sub4(Gl[t8], G[t8]));
+        const float4 e = exp2_4(sub4(Gl, G[t8]));
         *reinterpret_cast<float4 *>(&s_kc[rl][16 * t8 + 4 * lg]) = mul4(K[t8], e);
-        span = fmaxf(span, fmaxf(fmaxf(Gf.x - Gl[t8].x, Gf.y - Gl[t8].y),
-                                 fmaxf(Gf.z - Gl[t8].z, Gf.w - Gl[t8].w)));
+        span = fmaxf(span, fmaxf(fmaxf(Gf.x - Gl.x, Gf.y - Gl.y), fmaxf(Gf.z - Gl.z, Gf.w - Gl.w)));
     }
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) span = fmaxf(span, __shfl_xor(span, off));
@@ -281,8 +288,10 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
         if (bj > w || (bj == w && !diag_ok)) continue;
 #pragma unroll
         for (int t8 = 0; t8 < DT; ++t8) {
-            float4 ref = Gl[t8];
-            if (bj < w) {
+            float4 ref = zero4();
+            if (bj == w) {
+                ref = shfl4(G[t8], (lane & 48) | 15);
+            } else {
                 ref = zero4();
 #pragma unroll
                 for (int ww = 0; ww <= bj; ++ww)
@@ -361,6 +370,11 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
         *reinterpret_cast<float4 *>(Pf + B::frag(w, bj, NW) + 4 * lane) = pv;
     }
     __syncthreads();
+    // Kg = K e^G into LDS as the left operand of W^T = Kg^T Tb^T (the fallback
+    // is done with s_kc; the inversion's barriers order this before its use)
+#pragma unroll
+    for (int t8 = 0; t8 < DT; ++t8)
+        *reinterpret_cast<float4 *>(&s_kc[rl][16 * t8 + 4 * lg]) = mul4(K[t8], exp2_4(G[t8]));
 
     // T = (I + M)^{-1}, M strictly lower.  Diagonal 16x16 blocks by forward
     // substitution (lane lr solves column lr), then block levels
@@ -402,21 +416,6 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
         __syncthreads();
     }
 
-    // Row operands that need no product: Qg (already in fragment layout),
-    // Ec; Kg into LDS as the left operand of W^T = Kg^T Tb^T.  (s_kc is free:
-    // the fallback used it before the barriers of the inversion.)
-    float4 Kd[DT];
-#pragma unroll
-    for (int t8 = 0; t8 < DT; ++t8) {
-        const float4 eg = exp2_4(G[t8]);
-        *reinterpret_cast<float4 *>(blk + B::kQ + B::frag(w, t8, DT) + 4 * lane) = mul4(Q[t8], eg);
-        *reinterpret_cast<float4 *>(&s_kc[rl][16 * t8 + 4 * lg]) = mul4(K[t8], eg);
-        Kd[t8] = mul4(K[t8], exp2_4(sub4(Gend[t8], G[t8])));
-        if (w == 0 && lr == 0)
-            *reinterpret_cast<float4 *>(blk + B::kEc + 16 * t8 + 4 * lg) = exp2_4(Gend[t8]);
-    }
-    __syncthreads();
-
     // W = Tb Kg, then U' = Tb V, then the Kd fragments: wave w owns channel
     // tiles t8 = w (mod NW), all row blocks (balanced across waves).
     // Tb = T diag(b) is formed on the fly from s_T and s_beta.  W is computed
@@ -447,9 +446,17 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
             }
         }
         __syncthreads();
+        if (pass == 0) {   // next right operand: V
 #pragma unroll
-        for (int t8 = 0; t8 < DT; ++t8)   // next right operand: V, then Kd
-            *reinterpret_cast<float4 *>(&s_kc[rl][16 * t8 + 4 * lg]) = pass == 0 ? V[t8] : Kd[t8];
+            for (int t8 = 0; t8 < DT; ++t8) {
+                const float4 vv = *reinterpret_cast<const float4 *>(v + roff + 16 * t8 + 4 * lg);
+                *reinterpret_cast<float4 *>(&s_kc[rl][16 * t8 + 4 * lg]) = valid ? vv : zero4();
+            }
+        } else {           // then Kd, to be transposed into its fragments
+#pragma unroll
+            for (int t8 = 0; t8 < DT; ++t8)
+                *reinterpret_cast<float4 *>(&s_kc[rl][16 * t8 + 4 * lg]) = Kd[t8];
+        }
         __syncthreads();
     }
     // Kd fragments (t8, w2): a transpose of the 16 x 16 tiles through LDS

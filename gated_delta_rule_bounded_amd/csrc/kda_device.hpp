@@ -55,6 +55,40 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 bf16 MFMA with fp32 accumulation: lane l supplies A[l%16][8*(l/16)+j]
+// and B[8*(l/16)+j][l%16] for j = 0..7; the result layout is that of mfma4.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ floatx4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Split fp32 values into bf16 hi = rne(x) and lo = rne(x - hi): hi + lo
+// carries x to about 2^-16 relative, so hi*hi + hi*lo + lo*hi gives an
+// fp32-grade product on the bf16 matrix units.  Pairs are packed as the
+// matrix units read them (element 2i in the low half of 32-bit word i).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, bf16x2));
+}
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = pk_bf16(a, b);
+    lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+// four values -> 8 bytes hi, 8 bytes lo
+__device__ __forceinline__ void split4(const float4 &x, uint2 &hi, uint2 &lo) {
+    split2(x.x, x.y, hi.x, lo.x);
+    split2(x.z, x.w, hi.y, lo.y);
+}
+// eight values (a then b) -> one 16x16x32 operand each for hi and lo
+__device__ __forceinline__ void split8(const float4 &a, const float4 &b, bf16x8 &hi, bf16x8 &lo) {
+    uint2 ha, la, hb, lb;
+    split4(a, ha, la);
+    split4(b, hb, lb);
+    hi = __builtin_bit_cast(bf16x8, make_uint4(ha.x, ha.y, hb.x, hb.y));
+    lo = __builtin_bit_cast(bf16x8, make_uint4(la.x, la.y, lb.x, lb.y));
+}
+
 __device__ __forceinline__ float get4(const float4 &v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

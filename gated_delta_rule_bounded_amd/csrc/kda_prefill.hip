@@ -202,6 +202,19 @@ __device__ __forceinline__ void chunk_cumsum(float4 (&G)[D / 16], float4 (&Gend)
 //   Kd     fragment (t8, w2): Kd[16w2 + 4lg + i][16t8 + lr]
 // for i = 0..3, i.e. exactly the register layout of the MFMA operand or
 // accumulator that consumes it.
+//
+// Split form (kSplit: D and C multiples of 32).  W, Qg, P and Kd are the
+// left operands of the forward pass's products; there they are stored as
+// bf16 pairs hi = rne(x), lo = rne(x - hi), so each product runs on the bf16
+// matrix units as hi*hi + hi*lo + lo*hi with fp32 accumulation (the dropped
+// lo*lo term and lo's rounding are both near 2^-16 relative).  A pair
+// fragment (a, kb) covers the two fp32 fragments (a, 2kb) and (a, 2kb+1): lane
+// l holds their eight values in that order, as bf16x8 hi at float offset
+// 4l and lo at 256 + 4l of the 2 KiB pair fragment.  For the 16x16x32 bf16
+// MFMA this is a fixed permutation of the 32-deep contraction index, and the
+// right operand (the state S, the corrected writes U) is split the same way
+// from the same two fp32 fragments, so the products are unchanged.  The block
+// layout and size are those of the fp32 form; U' and Ec stay fp32.
 // ---------------------------------------------------------------------------
 template <int D, int C>
 struct Blk {
@@ -209,15 +222,29 @@ struct Blk {
     static constexpr int kW = 0, kU = C * D, kQ = 2 * C * D, kKd = 3 * C * D;
     static constexpr int kP = 4 * C * D, kEc = 4 * C * D + C * C;
     static constexpr int kSize = 4 * C * D + C * C + D;
+    static constexpr bool kSplit = (D % 32 == 0) && (C % 32 == 0);
     // float offset of fragment (a, b) of a part with nb fragments per a
     static __device__ __forceinline__ int frag(int a, int b, int nb) { return (a * nb + b) * 256; }
+    // float offset of pair fragment (a, kb) of a part with nkb pairs per a
+    static __device__ __forceinline__ int pfrag(int a, int kb, int nkb) { return (a * nkb + kb) * 512; }
 };
+
+// Store this lane's share of a pair fragment: fp32 fragments x0, x1 split
+// into bf16 hi / lo halves (see Blk).
+__device__ __forceinline__ void store_pair(float *dst, int lane, const float4 &x0, const float4 &x1)
+{
+    bf16x8 hi, lo;
+    split8(x0, x1, hi, lo);
+    *reinterpret_cast<bf16x8 *>(dst + 4 * lane) = hi;
+    *reinterpret_cast<bf16x8 *>(dst + 256 + 4 * lane) = lo;
+}
+__device__ __forceinline__ float4 f4(const floatx4 &a) { return make_float4(a[0], a[1], a[2], a[3]); }
 
 // ---------------------------------------------------------------------------
 // kda_chunk_prep: one workgroup per (chunk n, head h), all chunks in parallel.
 // ---------------------------------------------------------------------------
 template <int D, int C>
-__global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
+__global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
     float *__restrict__ ws)
@@ -253,8 +280,14 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
         chunk_cumsum<D, NW>(G, Gend, s_tot, w, lane);
 #pragma unroll
         for (int t8 = 0; t8 < DT; ++t8) {
-            *reinterpret_cast<float4 *>(blk + B::kQ + B::frag(w, t8, DT) + 4 * lane) =
-                mul4(Q[t8], exp2_4(G[t8]));
+            if constexpr (B::kSplit) {
+                if (t8 % 2 == 1)
+                    store_pair(blk + B::kQ + B::pfrag(w, t8 / 2, DT / 2), lane,
+                               mul4(Q[t8 - 1], exp2_4(G[t8 - 1])), mul4(Q[t8], exp2_4(G[t8])));
+            } else {
+                *reinterpret_cast<float4 *>(blk + B::kQ + B::frag(w, t8, DT) + 4 * lane) =
+                    mul4(Q[t8], exp2_4(G[t8]));
+            }
             Kd[t8] = mul4(K[t8], exp2_4(sub4(Gend[t8], G[t8])));
             if (w == 0 && lr == 0)
                 *reinterpret_cast<float4 *>(blk + B::kEc + 16 * t8 + 4 * lg) = exp2_4(Gend[t8]);
@@ -351,9 +384,10 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     // as fragments (w, bj), the blocks above the diagonal as zeros so the
     // forward pass can run the whole block row without branching.
     float *Pf = blk + B::kP;
+    float4 pv[NW];
 #pragma unroll
     for (int bj = 0; bj < NW; ++bj) {
-        float4 pv = zero4();
+        pv[bj] = zero4();
         if (bj <= w) {
             float pe[4];
 #pragma unroll
@@ -365,9 +399,13 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
                 // P^T element: s = 16bj + 4lg + vv, r = 16w + lr
                 pe[vv] = (bj == w && 4 * lg + vv > lr) ? 0.f : Pacc[bj][vv];
             }
-            pv = make_float4(pe[0], pe[1], pe[2], pe[3]);
+            pv[bj] = make_float4(pe[0], pe[1], pe[2], pe[3]);
         }
-        *reinterpret_cast<float4 *>(Pf + B::frag(w, bj, NW) + 4 * lane) = pv;
+        if constexpr (B::kSplit) {
+            if (bj % 2 == 1) store_pair(Pf + B::pfrag(w, bj / 2, NW / 2), lane, pv[bj - 1], pv[bj]);
+        } else {
+            *reinterpret_cast<float4 *>(Pf + B::frag(w, bj, NW) + 4 * lane) = pv[bj];
+        }
     }
     __syncthreads();
     // Kg = K e^G into LDS as the left operand of W^T = Kg^T Tb^T (the fallback
@@ -416,19 +454,24 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
         __syncthreads();
     }
 
-    // W = Tb Kg, then U' = Tb V, then the Kd fragments: wave w owns channel
-    // tiles t8 = w (mod NW), all row blocks (balanced across waves).
-    // Tb = T diag(b) is formed on the fly from s_T and s_beta.  W is computed
-    // transposed (operands swapped), which leaves each output tile in W's
-    // fragment order; U' in its natural orientation is already in U''s.
+    // W = Tb Kg, then U' = Tb V, then the Kd fragments: wave w owns the
+    // groups of TG channel tiles g = w (mod NW), all row blocks (balanced
+    // across waves; a group is the tile pair of one W pair fragment in the
+    // split form).  Tb = T diag(b) is formed on the fly from s_T and s_beta.
+    // W is computed transposed (operands swapped), which leaves each output
+    // tile in W's fragment order; U' in its natural orientation is already in
+    // U''s.
+    constexpr int TG = B::kSplit ? 2 : 1;
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int t8 = 0; t8 < DT; ++t8) {
-            if (t8 % NW != w) continue;
+        for (int g = 0; g < DT / TG; ++g) {
+            if (g % NW != w) continue;
 #pragma unroll
             for (int bi = 0; bi < NW; ++bi) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                floatx4 acc[TG];
+#pragma unroll
+                for (int u = 0; u < TG; ++u) acc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int w2 = 0; w2 <= bi; ++w2) {
                     const float4 ta = mul4(
@@ -436,13 +479,24 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
                         *reinterpret_cast<const float4 *>(&s_beta[16 * w2 + 4 * lg]));
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
-                        const float x = s_kc[16 * w2 + 4 * lg + kk][16 * t8 + lr];
-                        acc = pass == 0 ? mfma4(x, get4(ta, kk), acc) : mfma4(get4(ta, kk), x, acc);
+#pragma unroll
+                        for (int u = 0; u < TG; ++u) {
+                            const float x = s_kc[16 * w2 + 4 * lg + kk][16 * (TG * g + u) + lr];
+                            acc[u] = pass == 0 ? mfma4(x, get4(ta, kk), acc[u])
+                                               : mfma4(get4(ta, kk), x, acc[u]);
+                        }
                     }
                 }
-                float *dst = pass == 0 ? blk + B::kW + B::frag(bi, t8, DT)
-                                       : blk + B::kU + B::frag(t8, bi, NW);
-                *reinterpret_cast<float4 *>(dst + 4 * lane) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                if (pass == 0 && B::kSplit) {
+                    store_pair(blk + B::kW + B::pfrag(bi, g, DT / 2), lane, f4(acc[0]), f4(acc[TG - 1]));
+                } else {
+#pragma unroll
+                    for (int u = 0; u < TG; ++u) {
+                        float *dst = pass == 0 ? blk + B::kW + B::frag(bi, TG * g + u, DT)
+                                               : blk + B::kU + B::frag(TG * g + u, bi, NW);
+                        *reinterpret_cast<float4 *>(dst + 4 * lane) = f4(acc[u]);
+                    }
+                }
             }
         }
         __syncthreads();
@@ -462,14 +516,20 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     // Kd fragments (t8, w2): a transpose of the 16 x 16 tiles through LDS
 #pragma unroll
     for (int t8 = 0; t8 < DT; ++t8) {
-        if (t8 % NW != w) continue;
+        if ((t8 / TG) % NW != w) continue;
+        float4 kv[NW];
 #pragma unroll
         for (int w2 = 0; w2 < NW; ++w2) {
-            const float4 kv = make_float4(s_kc[16 * w2 + 4 * lg + 0][16 * t8 + lr],
-                                          s_kc[16 * w2 + 4 * lg + 1][16 * t8 + lr],
-                                          s_kc[16 * w2 + 4 * lg + 2][16 * t8 + lr],
-                                          s_kc[16 * w2 + 4 * lg + 3][16 * t8 + lr]);
-            *reinterpret_cast<float4 *>(blk + B::kKd + B::frag(t8, w2, NW) + 4 * lane) = kv;
+            kv[w2] = make_float4(s_kc[16 * w2 + 4 * lg + 0][16 * t8 + lr],
+                                 s_kc[16 * w2 + 4 * lg + 1][16 * t8 + lr],
+                                 s_kc[16 * w2 + 4 * lg + 2][16 * t8 + lr],
+                                 s_kc[16 * w2 + 4 * lg + 3][16 * t8 + lr]);
+            if constexpr (B::kSplit) {
+                if (w2 % 2 == 1)
+                    store_pair(blk + B::kKd + B::pfrag(t8, w2 / 2, NW / 2), lane, kv[w2 - 1], kv[w2]);
+            } else {
+                *reinterpret_cast<float4 *>(blk + B::kKd + B::frag(t8, w2, NW) + 4 * lane) = kv[w2];
+            }
         }
     }
 }
@@ -686,6 +746,237 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
             Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + j0 + lr] = Sown[o][i];
 }
 
+// ---------------------------------------------------------------------------
+// kda_chunk_fwd_split: the same pass over the split operand blocks (D and C
+// multiples of 32).  Every product runs on the 16x16x32 bf16 MFMA as
+// hi*hi + (hi*lo + lo*hi), the two parts in separate fp32 accumulators.
+// The right operands (the state slice S and the corrected writes U) are
+// split once, by the wave that produced them, and exchanged through LDS as
+// ready-made bf16 operands in the pair order of the left operands (see Blk):
+// for contraction block kb, lane l's eight values are its elements of fp32
+// tiles 2kb and 2kb+1, so the producer of tile t writes its lane's four
+// values to half t%2 of block t/2 of the same lane.  The state itself stays
+// fp32 in the registers of the wave that updates it.
+//
+// Per chunk the critical path is S -> W S -> U -> Kd^T U -> S'; the products
+// off that path (Qg S, P U) are issued after the critical ones of their phase
+// so that they fill the waits on LDS and barriers.  Besides the next chunk's
+// operands, each wave touches its share of the cache lines of the block
+// three chunks ahead (one 4-byte load per lane, one line per lane, issued
+// after the chunk's operand loads; the value is only waited for two chunks
+// later), so that block is in L2 by the time its operand loads are issued.
+// ---------------------------------------------------------------------------
+template <int D, int C>
+__global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_split_kernel(
+    const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
+    int NC, int H, float scale)
+{
+    constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
+    constexpr int KD = DT / 2, KC = NW / 2;   // 32-deep blocks over D and over C
+    constexpr int OWN = (DT + NW - 1) / NW;
+    using B = Blk<D, C>;
+    static_assert(B::kSplit, "split operand blocks need D, C multiples of 32");
+    // L2 prefetch: the DT * NW waves of a head's workgroups each touch 64 of
+    // the block's 128-byte lines
+    static_assert(B::kSize <= DT * NW * kWave * 32, "prefetch must cover the block");
+    const int h = blockIdx.x % H, jt = blockIdx.x / H, j0 = 16 * jt;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+
+    __shared__ __align__(16) uint4 s_Sb[KD][2][kWave];   // S slice, right operand (hi, lo)
+    __shared__ __align__(16) uint4 s_Ub[KC][2][kWave];   // U, right operand (hi, lo)
+
+    float *__restrict__ Sg = state + (int64_t)h * D * D;
+    auto own_tile = [&](int o) { return min(w + NW * o, DT - 1); };
+    // Sown[o][i] = S[16*t + 4*lg + i][j0 + lr], t = own_tile(o)
+    float4 Sown[OWN];
+#pragma unroll
+    for (int o = 0; o < OWN; ++o) {
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + j0 + lr];
+        Sown[o] = make_float4(e[0], e[1], e[2], e[3]);
+    }
+    // publish an owned tile (or a U tile) as a right operand: 8 bytes of hi
+    // and of lo in half `half` of this lane's 16-byte slots
+    auto put = [&](uint4 (&dst)[2][kWave], int half, const float4 &x) {
+        uint2 hi, lo;
+        split4(x, hi, lo);
+        reinterpret_cast<uint2 *>(&dst[0][lane])[half] = hi;
+        reinterpret_cast<uint2 *>(&dst[1][lane])[half] = lo;
+    };
+    auto get = [&](const uint4 (&src)[2][kWave], bf16x8 &hi, bf16x8 &lo) {
+        hi = __builtin_bit_cast(bf16x8, src[0][lane]);
+        lo = __builtin_bit_cast(bf16x8, src[1][lane]);
+    };
+
+    auto block = [&](int n) { return ws + ((int64_t)n * H + h) * B::kSize; };
+    struct Ops {
+        bf16x8 Wh[KD], Wl[KD], Qh[KD], Ql[KD], Ph[KC], Pl[KC], Kh[OWN][KC], Kl[OWN][KC];
+        float4 Ec[OWN];
+        float4 Up;     // U'[16w + 4lg + i][j0 + lr], i = 0..3
+        float pf;      // L2 prefetch in flight
+    };
+    auto ldp = [&](const float *p, bf16x8 &hi, bf16x8 &lo) {
+        hi = *reinterpret_cast<const bf16x8 *>(p + 4 * lane);
+        lo = *reinterpret_cast<const bf16x8 *>(p + 256 + 4 * lane);
+    };
+    auto load_Kd = [&](Ops &R, const float *b) {
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) {
+            const int t8 = own_tile(o);
+#pragma unroll
+            for (int kb = 0; kb < KC; ++kb) ldp(b + B::kKd + B::pfrag(t8, kb, KC), R.Kh[o][kb], R.Kl[o][kb]);
+            R.Ec[o] = *reinterpret_cast<const float4 *>(b + B::kEc + 16 * t8 + 4 * lg);
+        }
+    };
+    auto load_ops = [&](Ops &R, const float *b) {
+        R.Up = *reinterpret_cast<const float4 *>(b + B::kU + B::frag(jt, w, NW) + 4 * lane);
+#pragma unroll
+        for (int kb = 0; kb < KD; ++kb) {
+            ldp(b + B::kW + B::pfrag(w, kb, KD), R.Wh[kb], R.Wl[kb]);
+            ldp(b + B::kQ + B::pfrag(w, kb, KD), R.Qh[kb], R.Ql[kb]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < KC; ++kb) ldp(b + B::kP + B::pfrag(w, kb, KC), R.Ph[kb], R.Pl[kb]);
+        load_Kd(R, b);
+    };
+    auto prefetch = [&](int n) {
+        const int line = (jt * NW + w) * kWave + lane;
+        return block(min(n, NC - 1))[min(line * 32, B::kSize - 1)];   // stays inside the block
+    };
+
+    Ops X, Y;
+    load_ops(X, block(0));
+    X.pf = prefetch(1);
+    Y.pf = prefetch(2);
+#pragma unroll
+    for (int o = 0; o < OWN; ++o) {
+        const int t8 = own_tile(o);
+        if (DT % NW == 0 || w + NW * o < DT) put(s_Sb[t8 / 2], t8 % 2, Sown[o]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    auto chunk = [&](int n, Ops &cur, Ops &nxt, auto last) {
+        constexpr bool LAST = decltype(last)::value;
+        const float *bn = block(min(n + 1, NC - 1));   // the last chunk reloads itself
+        // ---- phase 1: U = -(W S - U') (critical), then QS = Qg S
+        bf16x8 sh[KD], sl[KD];
+#pragma unroll
+        for (int kb = 0; kb < KD; ++kb) get(s_Sb[kb], sh[kb], sl[kb]);
+        floatx4 Wa[2], Wb[2];
+        Wa[0] = floatx4{-cur.Up.x, -cur.Up.y, -cur.Up.z, -cur.Up.w};
+        Wa[1] = Wb[0] = Wb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_sched_barrier(0);
+        nxt.Up = *reinterpret_cast<const float4 *>(bn + B::kU + B::frag(jt, w, NW) + 4 * lane);
+#pragma unroll
+        for (int kb = 0; kb < KD; ++kb) {
+            ldp(bn + B::kW + B::pfrag(w, kb, KD), nxt.Wh[kb], nxt.Wl[kb]);
+            Wa[kb & 1] = mfma_bf16(cur.Wh[kb], sh[kb], Wa[kb & 1]);
+            Wb[kb & 1] = mfma_bf16(cur.Wh[kb], sl[kb], Wb[kb & 1]);
+            Wb[kb & 1] = mfma_bf16(cur.Wl[kb], sh[kb], Wb[kb & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float4 u;
+        u.x = -((Wa[0][0] + Wa[1][0]) + (Wb[0][0] + Wb[1][0]));
+        u.y = -((Wa[0][1] + Wa[1][1]) + (Wb[0][1] + Wb[1][1]));
+        u.z = -((Wa[0][2] + Wa[1][2]) + (Wb[0][2] + Wb[1][2]));
+        u.w = -((Wa[0][3] + Wa[1][3]) + (Wb[0][3] + Wb[1][3]));
+        put(s_Ub[w / 2], w % 2, u);
+        __builtin_amdgcn_sched_barrier(0);
+        floatx4 Qa[2], Qb[2];
+        Qa[0] = Qa[1] = Qb[0] = Qb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KD; ++kb) {
+            ldp(bn + B::kQ + B::pfrag(w, kb, KD), nxt.Qh[kb], nxt.Ql[kb]);
+            Qa[kb & 1] = mfma_bf16(cur.Qh[kb], sh[kb], Qa[kb & 1]);
+            Qb[kb & 1] = mfma_bf16(cur.Qh[kb], sl[kb], Qb[kb & 1]);
+            Qb[kb & 1] = mfma_bf16(cur.Ql[kb], sh[kb], Qb[kb & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();   // B1: U operand visible; every read of the S operand done
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- phase 2: S' = Ec * S + Kd^T U (critical), then O = scale (QS + P U)
+        bf16x8 uh[KC], ul[KC];
+#pragma unroll
+        for (int kb = 0; kb < KC; ++kb) get(s_Ub[kb], uh[kb], ul[kb]);
+        floatx4 Aa[OWN], Ab[OWN];
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) {
+            Aa[o] = floatx4{Sown[o].x * cur.Ec[o].x, Sown[o].y * cur.Ec[o].y,
+                            Sown[o].z * cur.Ec[o].z, Sown[o].w * cur.Ec[o].w};
+            Ab[o] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < KC; ++kb) {
+#pragma unroll
+            for (int o = 0; o < OWN; ++o) {
+                Aa[o] = mfma_bf16(cur.Kh[o][kb], uh[kb], Aa[o]);
+                Ab[o] = mfma_bf16(cur.Kh[o][kb], ul[kb], Ab[o]);
+                Ab[o] = mfma_bf16(cur.Kl[o][kb], uh[kb], Ab[o]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        load_Kd(nxt, bn);
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) {
+            Sown[o] = make_float4(Aa[o][0] + Ab[o][0], Aa[o][1] + Ab[o][1], Aa[o][2] + Ab[o][2],
+                                  Aa[o][3] + Ab[o][3]);
+            const int t8 = own_tile(o);
+            if (DT % NW == 0 || w + NW * o < DT) put(s_Sb[t8 / 2], t8 % 2, Sown[o]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        floatx4 Oa = {(Qa[0][0] + Qa[1][0]) + (Qb[0][0] + Qb[1][0]),
+                      (Qa[0][1] + Qa[1][1]) + (Qb[0][1] + Qb[1][1]),
+                      (Qa[0][2] + Qa[1][2]) + (Qb[0][2] + Qb[1][2]),
+                      (Qa[0][3] + Qa[1][3]) + (Qb[0][3] + Qb[1][3])};
+        floatx4 Ob = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KC; ++kb) {
+            ldp(bn + B::kP + B::pfrag(w, kb, KC), nxt.Ph[kb], nxt.Pl[kb]);
+            Oa = mfma_bf16(cur.Ph[kb], uh[kb], Oa);
+            Ob = mfma_bf16(cur.Ph[kb], ul[kb], Ob);
+            Ob = mfma_bf16(cur.Pl[kb], uh[kb], Ob);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + i;
+            if (!LAST || tr < T) core[(tr * H + h) * D + j0 + lr] = scale * (Oa[i] + Ob[i]);
+        }
+        // The prefetch goes after every operand load of this chunk: loads
+        // complete in issue order for the wait counter, so an earlier slow
+        // prefetch would hold up the waits for the operands issued after it.
+        asm volatile("" ::"v"(cur.pf));   // the prefetch of two chunks ago has landed
+        cur.pf = prefetch(n + 3);
+        __syncthreads();   // B2: S operand visible; every read of the U operand done
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    int n = 0;
+    for (; n + 2 < NC; n += 2) {
+        chunk(n, X, Y, std::false_type{});
+        chunk(n + 1, Y, X, std::false_type{});
+    }
+    if (n + 1 < NC) {
+        chunk(n, X, Y, std::false_type{});
+        chunk(n + 1, Y, X, std::true_type{});
+    } else {
+        chunk(n, X, Y, std::true_type{});
+    }
+
+#pragma unroll
+    for (int o = 0; o < OWN; ++o) {
+        const float e[4] = {Sown[o].x, Sown[o].y, Sown[o].z, Sown[o].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + j0 + lr] = e[i];
+    }
+}
+
 size_t prefill_workspace_bytes(int T_pad, int heads, int head_dim, int chunk)
 {
     // one operand block per (chunk, head): 4*C*D + C*C + D fp32
@@ -708,9 +999,14 @@ static hipError_t forward_t(float *state, float *core, int T, int H, float scale
                             const void *workspace, hipStream_t stream)
 {
     const int NC = (T + C - 1) / C;
-    hipLaunchKernelGGL((kda_chunk_fwd_kernel<D, C>), dim3(H * PrefCfg<D, C>::kDT),
-                       dim3(PrefCfg<D, C>::kThreads), 0, stream,
-                       static_cast<const float *>(workspace), state, core, T, NC, H, scale);
+    if constexpr (Blk<D, C>::kSplit)
+        hipLaunchKernelGGL((kda_chunk_fwd_split_kernel<D, C>), dim3(H * PrefCfg<D, C>::kDT),
+                           dim3(PrefCfg<D, C>::kThreads), 0, stream,
+                           static_cast<const float *>(workspace), state, core, T, NC, H, scale);
+    else
+        hipLaunchKernelGGL((kda_chunk_fwd_kernel<D, C>), dim3(H * PrefCfg<D, C>::kDT),
+                           dim3(PrefCfg<D, C>::kThreads), 0, stream,
+                           static_cast<const float *>(workspace), state, core, T, NC, H, scale);
     return hipGetLastError();
 }
 

@@ -240,11 +240,67 @@ __device__ __forceinline__ void store_pair(float *dst, int lane, const float4 &x
 }
 __device__ __forceinline__ float4 f4(const floatx4 &a) { return make_float4(a[0], a[1], a[2], a[3]); }
 
+// T = (I + M)^{-1} for the strictly lower C x C matrix M in s_M, into the
+// lower block triangle of s_T (blocks above the diagonal are not written).
+// Diagonal 16x16 blocks by forward substitution (wave w solves block w, lane
+// lr column lr), then block levels T_ij = -T_ii sum_{m=j}^{i-1} M_im T_mj on
+// fp32 MFMA, one level per barrier.  Ends with a barrier.
+template <int C>
+__device__ __forceinline__ void invert_unit_lower(const float (*__restrict__ s_M)[C + kPadC],
+                                                  float (*__restrict__ s_T)[C + kPadC], int w,
+                                                  int lane)
+{
+    constexpr int NW = C / 16;
+    const int lr = lane & 15, lg = lane >> 4;
+    {
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == lr) ? 1.f : 0.f;
+#pragma unroll
+            for (int s4 = 0; s4 < r; s4 += 4) {
+                const float4 m = *reinterpret_cast<const float4 *>(&s_M[16 * w + r][16 * w + s4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (s4 + i < r) acc = __builtin_fmaf(-get4(m, i), x[s4 + i], acc);
+            }
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if ((r >> 2) == lg) s_T[16 * w + r][16 * w + lr] = x[r];
+    }
+    __syncthreads();
+    for (int lev = 1; lev < NW; ++lev) {
+        if (w >= lev) {
+            const int i = w, j = w - lev;
+            floatx4 X = {0.f, 0.f, 0.f, 0.f};
+            for (int m = j; m < i; ++m) {
+                const float4 ma = *reinterpret_cast<const float4 *>(&s_M[16 * i + lr][16 * m + 4 * lg]);
+                X = mfma4(ma.x, s_T[16 * m + 4 * lg + 0][16 * j + lr], X);
+                X = mfma4(ma.y, s_T[16 * m + 4 * lg + 1][16 * j + lr], X);
+                X = mfma4(ma.z, s_T[16 * m + 4 * lg + 2][16 * j + lr], X);
+                X = mfma4(ma.w, s_T[16 * m + 4 * lg + 3][16 * j + lr], X);
+            }
+            const float4 ta = *reinterpret_cast<const float4 *>(&s_T[16 * i + lr][16 * i + 4 * lg]);
+            floatx4 Y = {0.f, 0.f, 0.f, 0.f};
+            Y = mfma4(ta.x, X[0], Y);
+            Y = mfma4(ta.y, X[1], Y);
+            Y = mfma4(ta.z, X[2], Y);
+            Y = mfma4(ta.w, X[3], Y);
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) s_T[16 * i + 4 * lg + vv][16 * j + lr] = -Y[vv];
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
-// kda_chunk_prep: one workgroup per (chunk n, head h), all chunks in parallel.
+// kda_chunk_prep: one workgroup per (chunk n, head h), all chunks in parallel;
+// fp32 fragments and fp32 MFMA, for the shapes without a split form.
 // ---------------------------------------------------------------------------
 template <int D, int C>
-__global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep_kernel(
+__global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
     float *__restrict__ ws)
@@ -280,14 +336,8 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
         chunk_cumsum<D, NW>(G, Gend, s_tot, w, lane);
 #pragma unroll
         for (int t8 = 0; t8 < DT; ++t8) {
-            if constexpr (B::kSplit) {
-                if (t8 % 2 == 1)
-                    store_pair(blk + B::kQ + B::pfrag(w, t8 / 2, DT / 2), lane,
-                               mul4(Q[t8 - 1], exp2_4(G[t8 - 1])), mul4(Q[t8], exp2_4(G[t8])));
-            } else {
-                *reinterpret_cast<float4 *>(blk + B::kQ + B::frag(w, t8, DT) + 4 * lane) =
-                    mul4(Q[t8], exp2_4(G[t8]));
-            }
+            *reinterpret_cast<float4 *>(blk + B::kQ + B::frag(w, t8, DT) + 4 * lane) =
+                mul4(Q[t8], exp2_4(G[t8]));
             Kd[t8] = mul4(K[t8], exp2_4(sub4(Gend[t8], G[t8])));
             if (w == 0 && lr == 0)
                 *reinterpret_cast<float4 *>(blk + B::kEc + 16 * t8 + 4 * lg) = exp2_4(Gend[t8]);
@@ -401,11 +451,7 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
             }
             pv[bj] = make_float4(pe[0], pe[1], pe[2], pe[3]);
         }
-        if constexpr (B::kSplit) {
-            if (bj % 2 == 1) store_pair(Pf + B::pfrag(w, bj / 2, NW / 2), lane, pv[bj - 1], pv[bj]);
-        } else {
-            *reinterpret_cast<float4 *>(Pf + B::frag(w, bj, NW) + 4 * lane) = pv[bj];
-        }
+        *reinterpret_cast<float4 *>(Pf + B::frag(w, bj, NW) + 4 * lane) = pv[bj];
     }
     __syncthreads();
     // Kg = K e^G into LDS as the left operand of W^T = Kg^T Tb^T (the fallback
@@ -414,54 +460,14 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     for (int t8 = 0; t8 < DT; ++t8)
         *reinterpret_cast<float4 *>(&s_kc[rl][16 * t8 + 4 * lg]) = mul4(K[t8], exp2_4(G[t8]));
 
-    // T = (I + M)^{-1}, M strictly lower.  Diagonal 16x16 blocks by forward
-    // substitution (lane lr solves column lr), then block levels
-    // T_ij = -T_ii sum_{m=j}^{i-1} M_im T_mj on MFMA.
-    {
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == lr) ? 1.f : 0.f;
-#pragma unroll
-            for (int s = 0; s < r; ++s) acc = __builtin_fmaf(-s_M[16 * w + r][16 * w + s], x[s], acc);
-            x[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if ((r >> 2) == lg) s_T[16 * w + r][16 * w + lr] = x[r];
-    }
-    __syncthreads();
-    for (int lev = 1; lev < NW; ++lev) {
-        if (w >= lev) {
-            const int i = w, j = w - lev;
-            floatx4 X = {0.f, 0.f, 0.f, 0.f};
-            for (int m = j; m < i; ++m) {
-                const float4 ma = *reinterpret_cast<const float4 *>(&s_M[16 * i + lr][16 * m + 4 * lg]);
-                X = mfma4(ma.x, s_T[16 * m + 4 * lg + 0][16 * j + lr], X);
-                X = mfma4(ma.y, s_T[16 * m + 4 * lg + 1][16 * j + lr], X);
-                X = mfma4(ma.z, s_T[16 * m + 4 * lg + 2][16 * j + lr], X);
-                X = mfma4(ma.w, s_T[16 * m + 4 * lg + 3][16 * j + lr], X);
-            }
-            const float4 ta = *reinterpret_cast<const float4 *>(&s_T[16 * i + lr][16 * i + 4 * lg]);
-            floatx4 Y = {0.f, 0.f, 0.f, 0.f};
-            Y = mfma4(ta.x, X[0], Y);
-            Y = mfma4(ta.y, X[1], Y);
-            Y = mfma4(ta.z, X[2], Y);
-            Y = mfma4(ta.w, X[3], Y);
-#pragma unroll
-            for (int vv = 0; vv < 4; ++vv) s_T[16 * i + 4 * lg + vv][16 * j + lr] = -Y[vv];
-        }
-        __syncthreads();
-    }
+    invert_unit_lower<C>(s_M, s_T, w, lane);
 
-    // W = Tb Kg, then U' = Tb V, then the Kd fragments: wave w owns the
-    // groups of TG channel tiles g = w (mod NW), all row blocks (balanced
-    // across waves; a group is the tile pair of one W pair fragment in the
-    // split form).  Tb = T diag(b) is formed on the fly from s_T and s_beta.
-    // W is computed transposed (operands swapped), which leaves each output
-    // tile in W's fragment order; U' in its natural orientation is already in
-    // U''s.
-    constexpr int TG = B::kSplit ? 2 : 1;
+    // W = Tb Kg, then U' = Tb V, then the Kd fragments: wave w owns channel
+    // tiles t8 = w (mod NW), all row blocks (balanced across waves).
+    // Tb = T diag(b) is formed on the fly from s_T and s_beta.  W is computed
+    // transposed (operands swapped), which leaves each output tile in W's
+    // fragment order; U' in its natural orientation is already in U''s.
+    constexpr int TG = 1;
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -487,15 +493,11 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
                         }
                     }
                 }
-                if (pass == 0 && B::kSplit) {
-                    store_pair(blk + B::kW + B::pfrag(bi, g, DT / 2), lane, f4(acc[0]), f4(acc[TG - 1]));
-                } else {
 #pragma unroll
-                    for (int u = 0; u < TG; ++u) {
-                        float *dst = pass == 0 ? blk + B::kW + B::frag(bi, TG * g + u, DT)
-                                               : blk + B::kU + B::frag(TG * g + u, bi, NW);
-                        *reinterpret_cast<float4 *>(dst + 4 * lane) = f4(acc[u]);
-                    }
+                for (int u = 0; u < TG; ++u) {
+                    float *dst = pass == 0 ? blk + B::kW + B::frag(bi, TG * g + u, DT)
+                                           : blk + B::kU + B::frag(TG * g + u, bi, NW);
+                    *reinterpret_cast<float4 *>(dst + 4 * lane) = f4(acc[u]);
                 }
             }
         }
@@ -524,12 +526,360 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
                                  s_kc[16 * w2 + 4 * lg + 1][16 * t8 + lr],
                                  s_kc[16 * w2 + 4 * lg + 2][16 * t8 + lr],
                                  s_kc[16 * w2 + 4 * lg + 3][16 * t8 + lr]);
-            if constexpr (B::kSplit) {
-                if (w2 % 2 == 1)
-                    store_pair(blk + B::kKd + B::pfrag(t8, w2 / 2, NW / 2), lane, kv[w2 - 1], kv[w2]);
-            } else {
-                *reinterpret_cast<float4 *>(blk + B::kKd + B::frag(t8, w2, NW) + 4 * lane) = kv[w2];
+            *reinterpret_cast<float4 *>(blk + B::kKd + B::frag(t8, w2, NW) + 4 * lane) = kv[w2];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// kda_chunk_prep_split: the split form of kda_chunk_prep (D, C multiples of
+// 32), one workgroup per (chunk n, head h).  Every product runs on the
+// 16x16x32 bf16 MFMA as hi*hi + hi*lo + lo*hi (fp32 accumulation); operands
+// are in the pair order of Blk, so a lane's eight values of a 32-deep block
+// are its elements of fp32 tiles 2kb and 2kb+1.
+//
+// Decay references.  With R_b the cumulative log-decay at the end of 16-row
+// block b (R_{-1} = 0) and G_r the cumulative log-decay of row r (both per
+// channel), a row r of block w and a row s of block bj <= w give
+//   e^{G_r - G_s} = e^{G_r - R_{w-1}} * e^{R_{w-1} - R_{bj-1}} * e^{R_{bj-1} - G_s}
+// with the first two factors <= 1 and the third >= 1 but bounded by block
+// bj's own decay span (for a decay gate, G <= 0 per token).  So the row operands are K e^{G - R_{w-1}} and
+// Q e^{G - R_{w-1}} (one exponential per element, formed once), the column
+// operand of block bj is K e^{R_{bj-1} - G} (once per row), and the middle
+// factor is a per-channel table entry applied to the column operand of an
+// off-diagonal tile.  Q e^G, K e^G and Kd follow from the same two
+// exponentials and per-channel tables.  A block whose span exceeds
+// kBlockSpanLog2 (a decay beyond e^{-66} within 16 tokens), or any growing
+// (positive) log-gate, would push a factor out of range: such a chunk takes
+// the exact pairwise sum for every entry of A and P instead (slow, correct
+// for any gate).
+// ---------------------------------------------------------------------------
+constexpr float kBlockSpanLog2 = 96.0f;
+
+template <int D, int C>
+__global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep_split_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
+    float *__restrict__ ws)
+{
+    constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
+    constexpr int KD = DT / 2, KC = NW / 2;   // 32-deep blocks over D and over C
+    using B = Blk<D, C>;
+    static_assert(B::kSplit, "split operand blocks need D, C multiples of 32");
+    const int n = blockIdx.x, h = blockIdx.y;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+    const int rl = 16 * w + lr;
+    const int64_t tg = (int64_t)n * C + rl;
+    const bool valid = tg < T;
+    const int64_t roff = (tg * H + h) * D;
+    float *__restrict__ blk = ws + ((int64_t)n * H + h) * B::kSize;
+
+    __shared__ __align__(16) float s_tot[NW * D];
+    __shared__ __align__(16) float s_beta[C];
+    // s_xbuf, fp32: first Kd^T, then the column operand K e^{R_{w-1} - G} as
+    // rows (or, on the pairwise path, the cumulative log-decay rows), then
+    // the right operands of the W and U' passes transposed: (K e^G)^T, V^T.
+    // A transposed operand is read as two 16-byte pieces per lane.
+    constexpr int kXRow = C * (D + kPadK), kXCol = D * (C + kPadC);
+    __shared__ __align__(16) float s_xbuf[kXRow > kXCol ? kXRow : kXCol];
+    auto s_x = reinterpret_cast<float (*)[D + kPadK]>(s_xbuf);    // rows [C][D]
+    auto s_xT = reinterpret_cast<float (*)[C + kPadC]>(s_xbuf);   // transposed [D][C]
+    __shared__ __align__(16) float s_M[C][C + kPadC];
+    __shared__ __align__(16) float s_T[C][C + kPadC];
+    __shared__ __align__(16) float s_tab[2 * NW + NW * (NW - 1) / 2 + 1][D];
+
+    float4 K[DT], Q[DT], G[DT];
+    load_rows<D>(q, k, gate, roff, lg, K, Q, G);
+    const float braw = beta[tg * H + h];
+    select_rows<D>(valid, K, Q, G);
+    if (lg == 0) s_beta[rl] = valid ? braw : 0.f;
+    // G: inclusive cumulative log-decay within this wave's block (relative
+    // to R_{w-1}); the block totals go to s_tot
+    scan_local<D, NW>(G, s_tot, w, lane);
+    __syncthreads();
+    // Per-channel tables from the block totals, and the span check.  Rows:
+    //   w            e^{R_{w-1}}                (Q e^G, K e^G from the row operands)
+    //   NW + w       e^{R_{NW-1} - R_{w-1}}     (Kd from the column operand)
+    //   2NW + w(w-1)/2 + bj   e^{R_{w-1} - R_{bj-1}}, bj < w   (off-diagonal tiles)
+    //   kRowEc       e^{R_{NW-1}} = e^{G_C}     (also stored as Ec)
+    constexpr int kRowF = 2 * NW, kRowEc = 2 * NW + NW * (NW - 1) / 2, kRows = kRowEc + 1;
+    {
+        // a thread takes one channel d and every kParts-th row (kParts threads
+        // share a channel when the workgroup has more threads than channels)
+        constexpr int NT = NW * kWave, kParts = NT >= D ? NT / D : 1;
+        const int part = NT >= D ? (int)threadIdx.x / D : 0;
+        for (int d = NT >= D ? (int)threadIdx.x % D : (int)threadIdx.x; d < D; d += NT >= D ? D : NT) {
+            float R[NW + 1];   // R[b + 1] = R_b
+            R[0] = 0.f;
+#pragma unroll
+            for (int b = 0; b < NW; ++b) R[b + 1] = R[b] + s_tot[b * D + d];
+#pragma unroll
+            for (int row = 0; row < kRows; ++row) {
+                if (row % kParts != part) continue;
+                float x;
+                if (row < NW) {
+                    x = R[row];
+                } else if (row < kRowF) {
+                    x = R[NW] - R[row - NW];
+                } else if (row < kRowEc) {
+                    int ww = 1, r0 = row - kRowF;   // row = kRowF + ww(ww-1)/2 + r0, r0 < ww
+                    while (r0 >= ww) r0 -= ww++;
+                    x = R[ww] - R[r0];
+                } else {
+                    x = R[NW];
+                }
+                const float ex = exp2_fast(x);
+                s_tab[row][d] = ex;
+                if (row == kRowEc) blk[B::kEc + d] = ex;
             }
+        }
+    }
+    bool bad = false;
+    // every factor stays in range when each in-block cumulative log-decay lies
+    // in [-kBlockSpanLog2, 0] (always true of a decay gate whose blocks span
+    // less than the limit)
+#pragma unroll
+    for (int t8 = 0; t8 < DT; ++t8) {
+        const float4 g = G[t8];
+        bad |= fminf(fminf(g.x, g.y), fminf(g.z, g.w)) < -kBlockSpanLog2 ||
+               fmaxf(fmaxf(g.x, g.y), fmaxf(g.z, g.w)) > 0.f;
+    }
+    const bool wide = __syncthreads_or(bad);
+    auto tab4 = [&](int row, int c) { return *reinterpret_cast<const float4 *>(&s_tab[row][c]); };
+
+    // Row operands B = K e^{G - R_{w-1}}, Qb = Q e^{G - R_{w-1}} (split), the
+    // column operand Kc = K e^{R_{w-1} - G} (fp32 rows, later), and from them
+    // Q e^G (stored), K e^G (split kept for W) and Kd = K e^{G_C - G} (rows,
+    // transposed into its pair fragments through s_x first)
+    auto x_operand = [&](int t8, int kb2, bf16x8 &xh, bf16x8 &xl) {
+        // this lane's X[s(kb2, lg, j)][16t8 + lr] from X^T in s_xT
+        const int s0 = 32 * kb2 + 4 * lg, c = 16 * t8 + lr;
+        split8(*reinterpret_cast<const float4 *>(&s_xT[c][s0]),
+               *reinterpret_cast<const float4 *>(&s_xT[c][s0 + 16]), xh, xl);
+    };
+    auto put_T = [&](int t8, const float4 &x) {   // this lane's row piece into X^T
+        const int c = 16 * t8 + 4 * lg;
+        s_xT[c + 0][rl] = x.x;
+        s_xT[c + 1][rl] = x.y;
+        s_xT[c + 2][rl] = x.z;
+        s_xT[c + 3][rl] = x.w;
+    };
+    bf16x8 Bh[KD], Bl[KD], Qh[KD], Ql[KD], Kh[KD], Kl[KD];
+    float4 Kc[DT];
+#pragma unroll
+    for (int kb = 0; kb < KD; ++kb) {
+        float4 b2[2], qb2[2], qg[2], kg[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t8 = 2 * kb + u, c = 16 * t8 + 4 * lg;
+            const float4 e = exp2_4(G[t8]);
+            const float4 ei = exp2_4(make_float4(-G[t8].x, -G[t8].y, -G[t8].z, -G[t8].w));
+            b2[u] = mul4(K[t8], e);
+            qb2[u] = mul4(Q[t8], e);
+            Kc[t8] = mul4(K[t8], ei);
+            const float4 pw = tab4(w, c);
+            qg[u] = mul4(qb2[u], pw);
+            kg[u] = mul4(b2[u], pw);
+            put_T(t8, mul4(Kc[t8], tab4(NW + w, c)));   // Kd
+        }
+        split8(b2[0], b2[1], Bh[kb], Bl[kb]);
+        split8(qb2[0], qb2[1], Qh[kb], Ql[kb]);
+        split8(kg[0], kg[1], Kh[kb], Kl[kb]);
+        store_pair(blk + B::kQ + B::pfrag(w, kb, KD), lane, qg[0], qg[1]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < KD; ++g) {
+        if (g % NW != w) continue;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int kb2 = 0; kb2 < KC; ++kb2) {
+                bf16x8 xh, xl;
+                x_operand(2 * g + u, kb2, xh, xl);
+                float *dst = blk + B::kKd + B::pfrag(2 * g + u, kb2, KC);
+                *reinterpret_cast<bf16x8 *>(dst + 4 * lane) = xh;
+                *reinterpret_cast<bf16x8 *>(dst + 256 + 4 * lane) = xl;
+            }
+    }
+    __syncthreads();
+    if (!wide) {
+#pragma unroll
+        for (int t8 = 0; t8 < DT; ++t8) *reinterpret_cast<float4 *>(&s_x[rl][16 * t8 + 4 * lg]) = Kc[t8];
+    } else {   // the chunk-relative cumulative log-decay rows, for the pairwise sums
+#pragma unroll
+        for (int t8 = 0; t8 < DT; ++t8) {
+            float4 g = G[t8];
+#pragma unroll
+            for (int b = 0; b < NW; ++b)
+                if (b < w) g = add4(g, *reinterpret_cast<const float4 *>(&s_tot[b * D + 16 * t8 + 4 * lg]));
+            *reinterpret_cast<float4 *>(&s_x[rl][16 * t8 + 4 * lg]) = g;
+        }
+    }
+    __syncthreads();
+
+    // Block row w of A (tile layout: element i is A[16w + 4lg + i][16bj + lr])
+    // and of P (fragment layout: element i is P[16w + lr][16bj + 4lg + i]).
+    floatx4 Aacc[NW], Pacc[NW];
+#pragma unroll
+    for (int bj = 0; bj < NW; ++bj) Aacc[bj] = Pacc[bj] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (!wide) {
+#pragma unroll
+        for (int bj = 0; bj < NW; ++bj) {
+            if (bj > w) continue;
+            const int frow = kRowF + w * (w - 1) / 2 + bj;   // used only when bj < w
+#pragma unroll
+            for (int kb = 0; kb < KD; ++kb) {
+                // column operand: block bj's K e^{R_{bj-1} - G}, times e^{R_{w-1} - R_{bj-1}}
+                const int c0 = 32 * kb + 4 * lg;
+                float4 x0 = *reinterpret_cast<const float4 *>(&s_x[16 * bj + lr][c0]);
+                float4 x1 = *reinterpret_cast<const float4 *>(&s_x[16 * bj + lr][c0 + 16]);
+                if (bj < w) {
+                    x0 = mul4(x0, tab4(frow, c0));
+                    x1 = mul4(x1, tab4(frow, c0 + 16));
+                }
+                bf16x8 ch, cl;
+                split8(x0, x1, ch, cl);
+                Aacc[bj] = mfma_bf16(Bh[kb], ch, Aacc[bj]);
+                Pacc[bj] = mfma_bf16(ch, Qh[kb], Pacc[bj]);
+                Aacc[bj] = mfma_bf16(Bh[kb], cl, Aacc[bj]);
+                Pacc[bj] = mfma_bf16(ch, Ql[kb], Pacc[bj]);
+                Aacc[bj] = mfma_bf16(Bl[kb], ch, Aacc[bj]);
+                Pacc[bj] = mfma_bf16(cl, Qh[kb], Pacc[bj]);
+            }
+        }
+    } else {
+        // sum_d x_r[d] k_s[d] e^{G_r[d] - G_s[d]} for one (r, s) of the chunk,
+        // x = k (A) or q (P); rows past T contribute zero
+        auto pair = [&](int r, int sc, const float *__restrict__ x) {
+            float acc = 0.f;
+            const int64_t tr = (int64_t)n * C + r, ts = (int64_t)n * C + sc;
+            if (sc <= r && tr < T && ts < T) {
+                const float *xr = x + (tr * H + h) * D, *ks = k + (ts * H + h) * D;
+                for (int d = 0; d < D; ++d)
+                    acc = __builtin_fmaf(xr[d], ks[d] * exp2_fast(s_x[r][d] - s_x[sc][d]), acc);
+            }
+            return acc;
+        };
+#pragma unroll
+        for (int bj = 0; bj < NW; ++bj) {
+            if (bj > w) continue;
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+                Aacc[bj][vv] = pair(16 * w + 4 * lg + vv, 16 * bj + lr, k);
+                Pacc[bj][vv] = pair(16 * w + lr, 16 * bj + 4 * lg + vv, q);
+            }
+        }
+    }
+
+    // M = diag(b) A, strictly lower, to LDS; P as pair fragments (blocks above
+    // the diagonal as zeros)
+    float4 pv[NW];
+#pragma unroll
+    for (int bj = 0; bj < NW; ++bj) {
+        pv[bj] = zero4();
+        if (bj <= w) {
+            float pe[4];
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+                const int r = 16 * w + 4 * lg + vv, sc = 16 * bj + lr;
+                float a = Aacc[bj][vv];
+                if (bj == w && sc >= r) a = 0.f;
+                s_M[r][sc] = s_beta[r] * a;
+                pe[vv] = (bj == w && 4 * lg + vv > lr) ? 0.f : Pacc[bj][vv];
+            }
+            pv[bj] = make_float4(pe[0], pe[1], pe[2], pe[3]);
+        }
+        if (bj % 2 == 1) store_pair(blk + B::kP + B::pfrag(w, bj / 2, KC), lane, pv[bj - 1], pv[bj]);
+    }
+    __syncthreads();   // s_M complete; s_x free
+    // V now, for the U' pass (its latency hidden behind the inversion and W)
+    float4 Vr[DT];
+#pragma unroll
+    for (int t8 = 0; t8 < DT; ++t8) Vr[t8] = *reinterpret_cast<const float4 *>(v + roff + 16 * t8 + 4 * lg);
+#pragma unroll
+    for (int kb = 0; kb < KD; ++kb) {
+        // K e^G = hi + lo (exact in fp32), back to rows
+        const uint4 h4 = __builtin_bit_cast(uint4, Kh[kb]), l4 = __builtin_bit_cast(uint4, Kl[kb]);
+        const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w}, lw[4] = {l4.x, l4.y, l4.z, l4.w};
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(hw[i] << 16) + __uint_as_float(lw[i] << 16);
+            x[2 * i + 1] = __uint_as_float(hw[i] & 0xffff0000u) + __uint_as_float(lw[i] & 0xffff0000u);
+        }
+        put_T(2 * kb, make_float4(x[0], x[1], x[2], x[3]));
+        put_T(2 * kb + 1, make_float4(x[4], x[5], x[6], x[7]));
+    }
+
+    invert_unit_lower<C>(s_M, s_T, w, lane);   // ends with a barrier: s_T and s_x visible
+
+    // W = Tb Kg, then U' = Tb V (Tb = T diag(b)).  Wave
+    // w owns the channel-tile pairs g = w (mod NW).  The Tb operand of row
+    // block bi over rows 32kb2.. is read from s_T rows (zero where the 16-row
+    // block lies above the diagonal, which s_T does not hold); the right
+    // operand X (K e^G, then V) is gathered from the s_x rows, transposed.
+    auto tb_operand = [&](int bi, int kb2, bf16x8 &th, bf16x8 &tl) {
+        const int s0 = 32 * kb2 + 4 * lg;
+        const float4 t0 = mul4(*reinterpret_cast<const float4 *>(&s_T[16 * bi + lr][s0]),
+                               *reinterpret_cast<const float4 *>(&s_beta[s0]));
+        const float4 t1 = (2 * kb2 + 1 <= bi)
+                              ? mul4(*reinterpret_cast<const float4 *>(&s_T[16 * bi + lr][s0 + 16]),
+                                     *reinterpret_cast<const float4 *>(&s_beta[s0 + 16]))
+                              : zero4();
+        split8(t0, t1, th, tl);
+    };
+    // the Tb operands, shared by both passes
+    bf16x8 tbh[NW][KC], tbl[NW][KC];
+#pragma unroll
+    for (int bi = 0; bi < NW; ++bi)
+#pragma unroll
+        for (int kb2 = 0; kb2 <= bi / 2; ++kb2) tb_operand(bi, kb2, tbh[bi][kb2], tbl[bi][kb2]);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int g = 0; g < KD; ++g) {
+            if (g % NW != w) continue;
+            bf16x8 xh[2][KC], xl[2][KC];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int kb2 = 0; kb2 < KC; ++kb2) x_operand(2 * g + u, kb2, xh[u][kb2], xl[u][kb2]);
+#pragma unroll
+            for (int bi = 0; bi < NW; ++bi) {
+                floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int kb2 = 0; kb2 <= bi / 2; ++kb2) {
+                    const bf16x8 th = tbh[bi][kb2], tl = tbl[bi][kb2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        if (pass == 0) {   // W^T tile (t8, bi) = X^T Tb^T: W's fragment order
+                            acc[u] = mfma_bf16(xh[u][kb2], th, acc[u]);
+                            acc[u] = mfma_bf16(xh[u][kb2], tl, acc[u]);
+                            acc[u] = mfma_bf16(xl[u][kb2], th, acc[u]);
+                        } else {           // U' tile = Tb X: U''s fragment order
+                            acc[u] = mfma_bf16(th, xh[u][kb2], acc[u]);
+                            acc[u] = mfma_bf16(th, xl[u][kb2], acc[u]);
+                            acc[u] = mfma_bf16(tl, xh[u][kb2], acc[u]);
+                        }
+                    }
+                }
+                if (pass == 0) {
+                    store_pair(blk + B::kW + B::pfrag(bi, g, KD), lane, f4(acc[0]), f4(acc[1]));
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        *reinterpret_cast<float4 *>(blk + B::kU + B::frag(2 * g + u, bi, NW) + 4 * lane) = f4(acc[u]);
+                }
+            }
+        }
+        if (pass == 0) {
+            __syncthreads();
+#pragma unroll
+            for (int t8 = 0; t8 < DT; ++t8)
+                put_T(t8, valid ? Vr[t8] : zero4());
+            __syncthreads();
         }
     }
 }
@@ -989,8 +1339,14 @@ static hipError_t prepare_t(const float *q, const float *k, const float *v, cons
                             const float *beta, int T, int H, void *workspace, hipStream_t stream)
 {
     const int NC = (T + C - 1) / C;
-    hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C>), dim3(NC, H), dim3(PrefCfg<D, C>::kThreads),
-                       0, stream, q, k, v, gate, beta, T, H, static_cast<float *>(workspace));
+    if constexpr (Blk<D, C>::kSplit)
+        hipLaunchKernelGGL((kda_chunk_prep_split_kernel<D, C>), dim3(NC, H),
+                           dim3(PrefCfg<D, C>::kThreads), 0, stream, q, k, v, gate, beta, T, H,
+                           static_cast<float *>(workspace));
+    else
+        hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C>), dim3(NC, H),
+                           dim3(PrefCfg<D, C>::kThreads), 0, stream, q, k, v, gate, beta, T, H,
+                           static_cast<float *>(workspace));
     return hipGetLastError();
 }
 

@@ -33,18 +33,17 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 METRIC = "KDA prefill tokens/s (H=32,D=128) + decode state HBM GB/s, 1 MI355X"
-PEAK_FP32_MFMA = 157.3e12     # MI355X dense fp32 matrix peak, FLOP/s
 PEAK_BF16_MFMA = 2.5e15       # MI355X dense bf16 matrix peak, FLOP/s
 PEAK_HBM = 8.0e12             # MI355X HBM3E peak, B/s
-# The forward kernel runs each fp32 product as three bf16 products (hi*hi,
-# hi*lo, lo*hi), so its matrix-unit ceiling in fp32-equivalent flops is a
-# third of the bf16 peak; the prepare kernel's products are fp32 MFMA.
 # HBM bytes per launch (FETCH_SIZE and WRITE_SIZE scaled by the copy
 # calibration) from rocprofv3 counter runs of the kernels as they are built
 # now; a kernel is left out once it changes after its counters were taken.
-TRAFFIC_BYTES = {}
+TRAFFIC_BYTES = {"kda_chunk_fwd": (150041 * 2.0 + 67756 * 1.0) * 1024}
+# Both prefill kernels run each fp32 product as three bf16 products (hi*hi,
+# hi*lo, lo*hi, fp32 accumulation), so their matrix-unit ceiling in
+# fp32-equivalent flops is a third of the bf16 peak.
 MATRIX_PEAK = {"kda_chunk_fwd": (PEAK_BF16_MFMA / 3, "bf16x3 MFMA (v_mfma_f32_16x16x32_bf16)"),
-               "kda_chunk_prep": (PEAK_FP32_MFMA, "fp32 MFMA (v_mfma_f32_16x16x4_f32)")}
+               "kda_chunk_prep": (PEAK_BF16_MFMA / 3, "bf16x3 MFMA (v_mfma_f32_16x16x32_bf16)")}
 
 T, H, D, C = 4096, 32, 128, 64
 
@@ -355,7 +354,8 @@ def main():
     out = {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 (products as 3 x bf16 MFMA, f32 accumulate)",
         "data": "synthetic",
         "config": {"workload": "chunked prefill core, 1 sequence, T=4096, heads=32, head_dim=128, "
                                "chunk=64, fp32 carried state ~N(0,0.05), q/k/v bf16-widened",

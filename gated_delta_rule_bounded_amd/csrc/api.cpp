@@ -83,7 +83,7 @@ int kda_gate(const uint16_t *g_raw, int64_t ldg, const uint16_t *b_raw, int64_t 
              const float *a_log, const float *dt_bias, int32_t T, int32_t heads,
              int32_t head_dim, float *gate, float *beta, hipStream_t stream)
 {
-    if (T < 0 || heads <= 0)
+    if (T < 0 || T > (1 << 24) || heads <= 0)
         return fail(KDA_ERR_SHAPE, "kda_gate: T=%d heads=%d", T, heads);
     if (!head_dim_ok(head_dim))
         return fail(KDA_ERR_UNSUPPORTED, "kda_gate: head_dim=%d", head_dim);

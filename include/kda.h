@@ -90,7 +90,8 @@ int conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w,
  *           softplus(z) = log(1+e^z), z for z > 20.  exp(gate) is in (0, 1].
  *   beta    fp32 [T_pad, heads]: beta[t,h] = 1/(1+exp(-b_raw[t,h])); not touched
  *           when b_raw is NULL (then beta may be NULL).
- * Rows t >= T of gate/beta are not touched.  T == 0 is a no-op.
+ * Rows t >= T of gate/beta are not touched.  T == 0 is a no-op; T above 2^24
+ * returns KDA_ERR_SHAPE.
  * ------------------------------------------------------------------------ */
 int kda_gate(const uint16_t *g_raw, int64_t ldg, const uint16_t *b_raw,
              int64_t ldb, const float *a_log, const float *dt_bias, int32_t T,

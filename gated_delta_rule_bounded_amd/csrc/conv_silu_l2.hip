@@ -6,7 +6,8 @@
 // For each row t and channel c (window = the last KC pre-conv rows, newest
 // last; it starts from the carried conv state):
 //   pre = sum_j w[c][j] * window[j][c]       (tap KC-1 meets row t)
-//   s   = pre * sigmoid(pre)
+//   s   = pre * sigmoid(pre)   (exp, reciprocal and rsqrt on the
+//                               transcendental unit, ~1 ulp each)
 //   q and k sections: s /= sqrt(sum over the head's D channels of s^2 + eps)
 //   y   = bf16(s)  (one rounding), optional exact fp32 copies of q, k, v.
 //
@@ -78,10 +79,19 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
     const int section = c0 / qkv;           // 0 = q, 1 = k, 2 = v
     const int cs = c0 - section * qkv;      // channel within the section
 
-    for (int t = t0; t < t1; ++t) {
+    // the tile's rows are all loaded up front (many 16-byte loads in flight
+    // per wave), then computed in order
+    uint4 rowv[kConvRowsPerTile];
+#pragma unroll
+    for (int i = 0; i < kConvRowsPerTile; ++i)
+        if (t0 + i < t1) rowv[i] = *reinterpret_cast<const uint4 *>(x + (row0 + t0 + i) * ldx + c0);
+#pragma unroll
+    for (int i = 0; i < kConvRowsPerTile; ++i) {
+        const int t = t0 + i;
+        if (t >= t1) break;
 #pragma unroll
         for (int j = 0; j + 1 < KC; ++j) win[j] = win[j + 1];
-        win[KC - 1] = *reinterpret_cast<const uint4 *>(x + (row0 + t) * ldx + c0);
+        win[KC - 1] = rowv[i];
 
         float xv[KC][8];
 #pragma unroll
@@ -93,13 +103,13 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
             float pre = wt[e][0] * xv[0][e];
 #pragma unroll
             for (int j = 1; j < KC; ++j) pre = __builtin_fmaf(wt[e][j], xv[j][e], pre);
-            s[e] = pre / (1.0f + expf(-pre));
+            s[e] = pre * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-pre * kLog2e));
             ss = __builtin_fmaf(s[e], s[e], ss);
         }
 #pragma unroll
         for (int off = 1; off < LANES_PER_HEAD; off <<= 1) ss += __shfl_xor(ss, off);
         if (section < 2) {
-            const float inv = 1.0f / sqrtf(ss + eps_l2);
+            const float inv = __builtin_amdgcn_rsqf(ss + eps_l2);
 #pragma unroll
             for (int e = 0; e < 8; ++e) s[e] *= inv;
         }

@@ -25,7 +25,7 @@ namespace kda {
 
 template <int D>
 struct RecCfg {
-    static constexpr int kThreads = (D >= 128) ? 256 : 64;
+    static constexpr int kThreads = (D >= 128) ? 512 : 64;
     static constexpr int kCG = D / 4;              // float4 column groups per row
     static constexpr int kRG = kThreads / kCG;     // row groups
     static constexpr int kRPT = D / kRG;           // rows per thread
@@ -33,6 +33,16 @@ struct RecCfg {
     static_assert(kCG <= kWave, "a row's column groups must fit in one wave");
     static_assert(kRG * kCG == kThreads && kRPT * kRG == D, "bad tiling");
 };
+
+// State traffic is touched once per call: non-temporal 16-byte accesses
+// (streaming through the caches) measured ~11 % faster than plain ones.
+__device__ __forceinline__ float4 load_stream(const float *p) {
+    const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store_stream(float *p, const float4 &v) {
+    __builtin_nontemporal_store(floatx4{v.x, v.y, v.z, v.w}, reinterpret_cast<floatx4 *>(p));
+}
 
 __device__ __forceinline__ float4 fma4(float a, const float4 &b, const float4 &c) {
     return make_float4(__builtin_fmaf(a, b.x, c.x), __builtin_fmaf(a, b.y, c.y),
@@ -65,7 +75,7 @@ __global__ __launch_bounds__(RecCfg<D>::kThreads) void kda_recurrent_kernel(
     float4 S[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-        S[r] = reinterpret_cast<const float4 *>(Sg + (size_t)(rg + RG * r) * D)[cg];
+        S[r] = load_stream(Sg + (size_t)(rg + RG * r) * D + 4 * cg);
 
     for (int t = 0; t < K; ++t) {
         const size_t row = (size_t)b * K + t;
@@ -137,14 +147,14 @@ __global__ __launch_bounds__(RecCfg<D>::kThreads) void kda_recurrent_kernel(
             float *__restrict__ Sn = snap[(size_t)b * (K - 1) + t] + (size_t)h * D * D;
 #pragma unroll
             for (int r = 0; r < RPT; ++r)
-                reinterpret_cast<float4 *>(Sn + (size_t)(rg + RG * r) * D)[cg] = S[r];
+                store_stream(Sn + (size_t)(rg + RG * r) * D + 4 * cg, S[r]);
         }
         __syncthreads();  // LDS is rewritten by the next row
     }
 
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-        reinterpret_cast<float4 *>(Sg + (size_t)(rg + RG * r) * D)[cg] = S[r];
+        store_stream(Sg + (size_t)(rg + RG * r) * D + 4 * cg, S[r]);
 }
 
 hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float *gate,

@@ -273,7 +273,8 @@ int gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate, int6
                   const uint16_t *w, int32_t T, int32_t heads, int32_t head_dim, float eps,
                   uint16_t *out, int64_t ldy, hipStream_t stream)
 {
-    if (T < 0 || heads <= 0) return fail(KDA_ERR_SHAPE, "gated_rmsnorm: T=%d heads=%d", T, heads);
+    if (T < 0 || T > (1 << 24) || heads <= 0)
+        return fail(KDA_ERR_SHAPE, "gated_rmsnorm: T=%d heads=%d", T, heads);
     if (!head_dim_ok(head_dim))
         return fail(KDA_ERR_UNSUPPORTED, "gated_rmsnorm: head_dim=%d", head_dim);
     if (T == 0) return ok();

@@ -12,6 +12,9 @@ namespace kda {
 
 constexpr int kNormThreads = 256;
 
+// Grid (rows, channel groups of 8 / kNormThreads): no integer division on
+// the way to the element.  rsqrt, exp and the reciprocal run on the
+// transcendental unit (~1 ulp each, far inside the bf16 output rounding).
 template <int D>
 __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
     const float *__restrict__ core, int64_t ldc, const uint16_t *__restrict__ out_gate,
@@ -19,13 +22,11 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
     uint16_t *__restrict__ out, int64_t ldy)
 {
     constexpr int LANES_PER_HEAD = D / 8;
-    const int groups_per_row = H * D / 8;
-    const int64_t gidx = (int64_t)blockIdx.x * kNormThreads + threadIdx.x;
-    const bool active = gidx < (int64_t)T * groups_per_row;
-    const int t = active ? (int)(gidx / groups_per_row) : 0;
-    const int c0 = active ? (int)(gidx % groups_per_row) * 8 : 0;
+    const int t = blockIdx.x;
+    const int cg = blockIdx.y * kNormThreads + threadIdx.x;
+    const bool active = cg < H * D / 8;
+    const int c0 = active ? cg * 8 : 0;
     const int d0 = c0 % D;
-
     const float4 a = *reinterpret_cast<const float4 *>(core + (int64_t)t * ldc + c0);
     const float4 b = *reinterpret_cast<const float4 *>(core + (int64_t)t * ldc + c0 + 4);
     const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -34,13 +35,13 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
     for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(xv[e], xv[e], ss);
 #pragma unroll
     for (int off = 1; off < LANES_PER_HEAD; off <<= 1) ss += __shfl_xor(ss, off);
-    const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-
+    const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
     float g[8], wv[8], o[8];
     unpack8(*reinterpret_cast<const uint4 *>(out_gate + (int64_t)t * ldo + c0), g);
     unpack8(*reinterpret_cast<const uint4 *>(w + d0), wv);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = xv[e] * r * wv[e] * (1.0f / (1.0f + expf(-g[e])));
+    for (int e = 0; e < 8; ++e)
+        o[e] = xv[e] * r * wv[e] * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-g[e] * kLog2e));
     if (active) *reinterpret_cast<uint4 *>(out + (int64_t)t * ldy + c0) = pack8(o);
 }
 
@@ -49,8 +50,8 @@ hipError_t launch_gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *
                                 int head_dim, float eps, uint16_t *out, int64_t ldy,
                                 hipStream_t stream)
 {
-    const int64_t groups = (int64_t)T * heads * head_dim / 8;
-    const dim3 grid((unsigned)((groups + kNormThreads - 1) / kNormThreads));
+    const int groups_per_row = heads * head_dim / 8;
+    const dim3 grid(T, (groups_per_row + kNormThreads - 1) / kNormThreads);
     if (head_dim == 128)
         hipLaunchKernelGGL(gated_rmsnorm_kernel<128>, grid, dim3(kNormThreads), 0, stream, core,
                            ldc, out_gate, ldo, w, T, heads, eps, out, ldy);

@@ -202,7 +202,8 @@ int kda_decode_k(const uint16_t *qkv, int64_t ldqkv, const float *gate,
  *   w        bf16 [head_dim]
  *   out      bf16 [T, heads*head_dim] (row stride ldy):
  *            out = bf16(x / sqrt(mean_d x^2 + eps) * w[d] * sigmoid(out_gate)).
- * out must not alias out_gate or core (KDA_ERR_ALIAS).  T == 0 is a no-op.
+ * out must not alias out_gate or core (KDA_ERR_ALIAS).  T == 0 is a no-op;
+ * T above 2^24 returns KDA_ERR_SHAPE.
  * ------------------------------------------------------------------------ */
 int gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate,
                   int64_t ldo, const uint16_t *w, int32_t T, int32_t heads,

@@ -681,7 +681,16 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
             const float4 pw = tab4(w, c);
             qg[u] = mul4(qb2[u], pw);
             kg[u] = mul4(b2[u], pw);
-            put_T(t8, mul4(Kc[t8], tab4(NW + w, c)));   // Kd
+            if (!wide) {
+                put_T(t8, mul4(Kc[t8], tab4(NW + w, c)));   // Kd = K e^{R_{w-1} - G} e^{G_C - R_{w-1}}
+            } else {
+                // e^{-G} may overflow here: Kd = K e^{(G_C - R_{w-1}) - G}, exponent <= 0
+                float4 x = zero4();
+#pragma unroll
+                for (int b = 0; b < NW; ++b)
+                    if (b >= w) x = add4(x, *reinterpret_cast<const float4 *>(&s_tot[b * D + c]));
+                put_T(t8, mul4(K[t8], exp2_4(sub4(x, G[t8]))));
+            }
         }
         split8(b2[0], b2[1], Bh[kb], Bl[kb]);
         split8(qb2[0], qb2[1], Qh[kb], Ql[kb]);

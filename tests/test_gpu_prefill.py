@@ -111,6 +111,46 @@ def test_prefill_steep_decay_takes_exact_diagonal_path(C):
     assert relerr(S, ref_S) < TOL
 
 
+def test_prefill_wide_chunks_take_exact_pairwise_path():
+    """Split form (D = 128, chunk 64): chunks 1 and 3 get gates steep enough
+    that a 16-row block decays by more than 2^96 (their A and P come from
+    the exact pairwise sums), chunks 0 and 2 keep the factored path; both
+    must match the oracle."""
+    T, H, D, C = 256, 2, 128, 64
+    case = core_case(T, H, D, 1507, 0.05)
+    g = case["gate"].copy()
+    g[64:128] *= 6.0
+    g[192:256] *= 6.0
+    case["gate"] = g.astype(np.float32)
+    g2 = case["gate"] / np.log(2)
+    blk = np.array([[(-g2[16 * b:16 * b + 16, h].sum(0)).max() for h in range(H)]
+                    for b in range(T // 16)])
+    assert (blk[4:8] > 96.0).any() and (blk[0:4] <= 96.0).all(), "need both paths"
+    say("wide chunks", C)
+    core, S = gpu_prefill(case, T, T, C, D ** -0.5)
+    ref_core, ref_S = oracle_core(case, D ** -0.5)
+    assert np.all(np.isfinite(core)) and np.all(np.isfinite(S))
+    assert relerr(core, ref_core) < TOL
+    assert relerr(S, ref_S) < TOL
+
+
+def test_prefill_growing_gate_rows():
+    """A few positive log-gates (growth instead of decay) in one chunk: the
+    factored decay references do not apply there and that chunk takes the
+    exact pairwise path; results still match the oracle."""
+    T, H, D, C = 192, 2, 128, 64
+    case = core_case(T, H, D, 1508, 0.05)
+    g = case["gate"].copy()
+    g[66:80] = 0.3
+    case["gate"] = g.astype(np.float32)
+    assert g[64:80].sum(0).max() > 0.0, "need a positive in-block cumulative log-gate"
+    say("growing gate", C)
+    core, S = gpu_prefill(case, T, T, C, D ** -0.5)
+    ref_core, ref_S = oracle_core(case, D ** -0.5)
+    assert relerr(core, ref_core) < TOL
+    assert relerr(S, ref_S) < TOL
+
+
 def test_prefill_empty_is_noop():
     import gated_delta_rule_bounded_amd as kda
     H, D = 2, 16

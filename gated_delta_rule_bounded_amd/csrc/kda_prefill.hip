@@ -1125,8 +1125,11 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
 // after the chunk's operand loads; the value is only waited for two chunks
 // later), so that block is in L2 by the time its operand loads are issued.
 // ---------------------------------------------------------------------------
+// (Capped at 256 registers: within that budget the compiler keeps every
+// operand and accumulator in VGPRs, which measured faster than the larger
+// VGPR + AGPR allocation it picks uncapped.)
 template <int D, int C>
-__global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_split_kernel(
+__global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_fwd_split_kernel(
     const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
     int NC, int H, float scale)
 {

@@ -3,8 +3,11 @@
 
 Step (the timed unit): one chunked prefill of the KDA core over the workload
 T=4096 tokens, 32 heads, head_dim 128, chunk 64, from an fp32 carried state
-~ N(0, 0.05): kda_prefill_prepare then kda_prefill_forward (together exactly
-kda_prefill) on inputs already resident in HBM.  value = T / step time.
+~ N(0, 0.05), on inputs already resident in HBM: one kda_prefill call (per
+segment of kda_prefill_segment_chunks chunks, prepare then forward).
+value = T / step time.  Kernel durations for the roofline come from the same
+number of steps right after, in the same schedule spelled out phase by phase
+with HIP events between the kernels.
 
 Also reported on the same JSON line (measured after the timed steps):
   decode    B=256 sequences x 64 steps, state [256,32,128,128] fp32: state
@@ -99,20 +102,41 @@ def setup_prefill(kda, dev):
                  b_raw=workloads.to_bf16(raw["b_raw"]).to(dev), beta=beta)
     state = torch.from_numpy(workloads.state(H, D, 0.05, workloads.SEED_STATE + 1)).to(dev)
     core = torch.empty(T, H, D, device=dev)
+    # kda_prefill's schedule: segments of `seg` chunks, each prepared into the
+    # start of the workspace and walked at once
+    seg = kda.kda_prefill_segment_chunks(T, H, D, C)
     ws = torch.empty(kda.kda_prefill_workspace_bytes(T, H, D, C), dtype=torch.uint8, device=dev)
-    return dict(q=q, k=k, v=v, gate=gate, beta=beta, state=state, core=core, ws=ws, raw=raw)
+    # the segments' row views, built once so the phase pass launches back to back
+    rows = seg * C
+    segs = []
+    for r0 in range(0, T, rows):
+        sl = slice(r0, min(T, r0 + rows))
+        segs.append((q[sl], k[sl], v[sl], gate[sl], beta[sl], core[sl], sl.stop - sl.start))
+    return dict(q=q, k=k, v=v, gate=gate, beta=beta, state=state, core=core, ws=ws, raw=raw,
+                seg=seg, segs=segs)
 
 
-def prefill_step(kda, P, e0=None, e1=None, e2=None):
-    kw = dict(T=T, T_pad=T, heads=H, head_dim=D, chunk=C)
-    if e0 is not None:
-        e0.record()
-    kda.kda_prefill_prepare(P["q"], P["k"], P["v"], P["gate"], P["beta"], P["ws"], **kw)
-    if e1 is not None:
-        e1.record()
-    kda.kda_prefill_forward(P["state"], P["core"], P["ws"], scale=D ** -0.5, **kw)
-    if e2 is not None:
-        e2.record()
+def prefill_step(kda, P):
+    """One whole prefill of T tokens: one kda_prefill call."""
+    kda.kda_prefill(P["q"], P["k"], P["v"], P["gate"], P["beta"], P["state"], P["core"], P["ws"],
+                    T=T, T_pad=T, heads=H, head_dim=D, chunk=C, scale=D ** -0.5)
+
+
+def prefill_step_phases(kda, P, evs=None):
+    """The same prefill as kda_prefill's own schedule spelled out (per segment
+    of P["seg"] chunks: prepare into the start of the workspace, then
+    forward; bitwise kda_prefill), with events (e0, e1, e2) per segment
+    around the two kernels when evs is given."""
+    for i, (q, k, v, g, b, core, Ts) in enumerate(P["segs"]):
+        kw = dict(T=Ts, T_pad=Ts, heads=H, head_dim=D, chunk=C)
+        if evs is not None:
+            evs[i][0].record()
+        kda.kda_prefill_prepare(q, k, v, g, b, P["ws"], **kw)
+        if evs is not None:
+            evs[i][1].record()
+        kda.kda_prefill_forward(P["state"], core, P["ws"], scale=D ** -0.5, **kw)
+        if evs is not None:
+            evs[i][2].record()
 
 
 def bench_decode(kda, dev, n_steps=64, n_inputs=8):
@@ -307,30 +331,44 @@ def main():
         del src, dst
 
     P = setup_prefill(kda, dev)
-    log("prefill inputs ready")
+    nseg = -(-T // (P["seg"] * C))
+    log(f"prefill inputs ready ({nseg} segments of {P['seg']} chunks)")
     for _ in range(args.warmup):
         prefill_step(kda, P)
-    evs = [(ev(), ev(), ev()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        prefill_step(kda, P, *evs[i])
+        prefill_step(kda, P)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
-    t_prep = float(np.mean([a.elapsed_time(b) for a, b, _ in evs])) * 1e-3
-    t_fwd = float(np.mean([b.elapsed_time(c) for _, b, c in evs])) * 1e-3
-    log(f"prefill: {ms_step:.4f} ms/step, prepare {t_prep*1e6:.1f} us, forward {t_fwd*1e6:.1f} us")
+    # kernel durations: the same steps again in the spelled-out schedule, with
+    # HIP events on the stream between the kernels
+    evs = [[(ev(), ev(), ev()) for _ in range(nseg)] for _ in range(args.steps)]
+    for _ in range(2):
+        prefill_step_phases(kda, P)
+    for i in range(args.steps):
+        prefill_step_phases(kda, P, evs[i])
+    torch.cuda.synchronize()
+    # per kernel: the whole prefill's time in that kernel (sum over segments)
+    t_prep = float(np.mean([sum(a.elapsed_time(b) for a, b, _ in e) for e in evs])) * 1e-3
+    t_fwd = float(np.mean([sum(b.elapsed_time(c) for _, b, c in e) for e in evs])) * 1e-3
+    log(f"prefill: {ms_step:.4f} ms/step, prepare {t_prep*1e6:.1f} us, forward {t_fwd*1e6:.1f} us "
+        f"(per step, over {nseg} segments)")
 
-    f_fwd = fwd_flops_per_token_head(D, C) * T * H
-    f_prep = prep_flops_per_token_head(D, C) * T * H
+    # per launch (each kernel runs once per segment; the segments here are
+    # equal): algorithmic work of its rows and its average event duration
+    f_fwd = fwd_flops_per_token_head(D, C) * T * H / nseg
+    f_prep = prep_flops_per_token_head(D, C) * T * H / nseg
+    b_fwd = fwd_bytes(T, H, D, C) / nseg
+    b_prep = prep_bytes(T, H, D, C) / nseg
+    t_fwd, t_prep = t_fwd / nseg, t_prep / nseg
     kernels = {
-        "kda_chunk_fwd": dict(avg_us=t_fwd * 1e6, flops=f_fwd, TFLOPs=f_fwd / t_fwd / 1e12,
-                              bytes=fwd_bytes(T, H, D, C),
-                              GBps=fwd_bytes(T, H, D, C) / t_fwd / 1e9),
-        "kda_chunk_prep": dict(avg_us=t_prep * 1e6, flops=f_prep, TFLOPs=f_prep / t_prep / 1e12,
-                               bytes=prep_bytes(T, H, D, C),
-                               GBps=prep_bytes(T, H, D, C) / t_prep / 1e9),
+        "kda_chunk_fwd": dict(avg_us=t_fwd * 1e6, launches_per_step=nseg, flops=f_fwd,
+                              TFLOPs=f_fwd / t_fwd / 1e12, bytes=b_fwd, GBps=b_fwd / t_fwd / 1e9),
+        "kda_chunk_prep": dict(avg_us=t_prep * 1e6, launches_per_step=nseg, flops=f_prep,
+                               TFLOPs=f_prep / t_prep / 1e12, bytes=b_prep,
+                               GBps=b_prep / t_prep / 1e9),
     }
     # The dominant kernel is the slower one; its bound is the ceiling it would
     # hit first: HBM bytes at 8 TB/s or its products at the matrix peak.

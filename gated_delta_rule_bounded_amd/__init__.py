@@ -20,7 +20,8 @@ from ._lib import KdaError, last_error  # noqa: F401
 
 __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_prepare",
            "kda_prefill_forward", "kda_decode", "kda_decode_k",
-           "gated_rmsnorm", "kda_prefill_workspace_bytes", "ptr_table", "KdaError",
+           "gated_rmsnorm", "kda_prefill_workspace_bytes", "kda_prefill_segment_chunks",
+           "ptr_table", "KdaError",
            "last_error", "library_path"]
 
 
@@ -95,6 +96,11 @@ def kda_gate(g_raw, a_log, dt_bias, gate, *, T, heads, head_dim, b_raw=None, bet
 
 def kda_prefill_workspace_bytes(T_pad, heads, head_dim, chunk):
     return int(_lib.lib.kda_prefill_workspace_bytes(T_pad, heads, head_dim, chunk))
+
+
+def kda_prefill_segment_chunks(T, heads, head_dim, chunk):
+    """Chunks per segment that kda_prefill walks at a time."""
+    return int(_lib.lib.kda_prefill_segment_chunks(T, heads, head_dim, chunk))
 
 
 def kda_prefill(q, k, v, gate, beta, state, core, workspace, *, T, T_pad, heads, head_dim,

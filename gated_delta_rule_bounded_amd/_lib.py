@@ -11,8 +11,8 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 
 # exported C symbols, as declared in include/kda.h
 SYMBOLS = ("kda_last_error", "conv_silu_l2", "kda_gate", "kda_prefill_workspace_bytes",
-           "kda_prefill", "kda_prefill_prepare", "kda_prefill_forward", "kda_decode",
-           "kda_decode_k", "gated_rmsnorm")
+           "kda_prefill_segment_chunks", "kda_prefill", "kda_prefill_prepare",
+           "kda_prefill_forward", "kda_decode", "kda_decode_k", "gated_rmsnorm")
 
 
 class KdaError(RuntimeError):
@@ -36,6 +36,8 @@ def _load():
     lib.kda_gate.argtypes = [P, i64, P, i64, P, P, i32, i32, i32, P, P, P]
     lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.kda_prefill_segment_chunks.restype = ctypes.c_int32
+    lib.kda_prefill_segment_chunks.argtypes = [i32, i32, i32, i32]
     lib.kda_prefill.restype = ctypes.c_int
     lib.kda_prefill.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, f32, P,
                                 ctypes.c_size_t, P]

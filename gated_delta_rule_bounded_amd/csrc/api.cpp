@@ -109,6 +109,12 @@ size_t kda_prefill_workspace_bytes(int32_t T_pad, int32_t heads, int32_t head_di
     return kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
 }
 
+int32_t kda_prefill_segment_chunks(int32_t T, int32_t heads, int32_t head_dim, int32_t chunk)
+{
+    if (T < 0 || heads <= 0 || !head_dim_ok(head_dim) || !(chunk == 16 || chunk == 64)) return 0;
+    return kda::prefill_segment_chunks(T, heads, head_dim, chunk);
+}
+
 // Shared validation of the prefill family; v may be NULL for prepare, beta
 // NULL for forward, state/core NULL for prepare.
 static int check_prefill(const char *who, const float *q, const float *k, const float *v,

@@ -34,6 +34,7 @@ hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float 
                                 float scale, hipStream_t stream);
 
 size_t prefill_workspace_bytes(int T_pad, int heads, int head_dim, int chunk);
+int prefill_segment_chunks(int T, int heads, int head_dim, int chunk);
 
 // phase 1 (per chunk, state-free) and phase 2 (serial over chunks)
 hipError_t launch_kda_prefill_prepare(const float *q, const float *k, const float *v,

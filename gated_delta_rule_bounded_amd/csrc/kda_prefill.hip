@@ -38,6 +38,7 @@
 // log-decay by a select at load time, never by arithmetic with their bits, so
 // poison in the tail cannot change a single bit of the result.  Chunks wholly
 // past T are not visited; core rows >= T are not written.
+#include <algorithm>
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -1346,6 +1347,15 @@ size_t prefill_workspace_bytes(int T_pad, int heads, int head_dim, int chunk)
     return (size_t)(T_pad / chunk) * heads * blk * sizeof(float);
 }
 
+int prefill_segment_chunks(int T, int heads, int head_dim, int chunk)
+{
+    constexpr size_t kCacheBudget = size_t(160) << 20;   // of MI355X's 256 MiB last-level cache
+    const int NC = std::max(1, (T + chunk - 1) / chunk);
+    const size_t per_chunk = prefill_workspace_bytes(chunk, heads, head_dim, chunk);
+    const int nseg = (int)std::max<size_t>(1, (NC * per_chunk + kCacheBudget - 1) / kCacheBudget);
+    return (NC + nseg - 1) / nseg;
+}
+
 template <int D, int C>
 static hipError_t prepare_t(const float *q, const float *k, const float *v, const float *gate,
                             const float *beta, int T, int H, void *workspace, hipStream_t stream)
@@ -1404,11 +1414,26 @@ hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
                               float *core, int T, int heads, int head_dim, int chunk,
                               float scale, void *workspace, hipStream_t stream)
 {
-    hipError_t e = launch_kda_prefill_prepare(q, k, v, gate, beta, T, heads, head_dim, chunk,
-                                              workspace, stream);
-    if (e != hipSuccess) return e;
-    return launch_kda_prefill_forward(state, core, T, heads, head_dim, chunk, scale, workspace,
-                                      stream);
+    // Segments of `seg` chunks, each prepared into the start of the workspace
+    // and walked at once: a segment's operand blocks (at most the cache
+    // budget) are still in the last-level cache when the walk reads them.
+    // Chunk boundaries and the carried state are those of one long pass, so
+    // the result is bitwise the same.
+    const int NC = (T + chunk - 1) / chunk;
+    const int seg = prefill_segment_chunks(T, heads, head_dim, chunk);
+    const int64_t HD = (int64_t)heads * head_dim;
+    for (int c0 = 0; c0 < NC; c0 += seg) {
+        const int64_t r0 = (int64_t)c0 * chunk;
+        const int Ts = (int)std::min<int64_t>((int64_t)T - r0, (int64_t)seg * chunk);
+        hipError_t e = launch_kda_prefill_prepare(q + r0 * HD, k + r0 * HD, v + r0 * HD,
+                                                  gate + r0 * HD, beta + r0 * heads, Ts, heads,
+                                                  head_dim, chunk, workspace, stream);
+        if (e != hipSuccess) return e;
+        e = launch_kda_prefill_forward(state, core + r0 * HD, Ts, heads, head_dim, chunk, scale,
+                                       workspace, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kda

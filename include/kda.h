@@ -118,9 +118,22 @@ int kda_gate(const uint16_t *g_raw, int64_t ldg, const uint16_t *b_raw,
  *   workspace  device scratch of at least kda_prefill_workspace_bytes(...)
  *              bytes, 256-byte aligned; contents on return are unspecified.
  * core must not alias an input or state (KDA_ERR_ALIAS).  T == 0 is a no-op.
+ *
+ * kda_prefill runs the two phases below over consecutive segments of
+ * kda_prefill_segment_chunks(...) chunks (prepare, then forward, per segment,
+ * each segment reusing the start of the workspace), so the operand blocks of
+ * a segment are still in the last-level cache when the forward phase reads
+ * them.  The result is bitwise that of one prepare + forward over all rows.
  * ------------------------------------------------------------------------ */
 size_t kda_prefill_workspace_bytes(int32_t T_pad, int32_t heads,
                                    int32_t head_dim, int32_t chunk);
+
+/* Chunks per segment of kda_prefill for T tokens (at least 1; 0 on invalid
+ * heads/head_dim/chunk): the number of segments is the workspace of all
+ * ceil(T/chunk) chunks divided by a 160 MiB cache budget, rounded up, and
+ * the chunks are spread evenly over them. */
+int32_t kda_prefill_segment_chunks(int32_t T, int32_t heads, int32_t head_dim,
+                                   int32_t chunk);
 
 int kda_prefill(const float *q, const float *k, const float *v,
                 const float *gate, const float *beta, float *state, float *core,

@@ -29,7 +29,8 @@ def _declared_functions():
 def test_header_declares_the_six_calls():
     names = _declared_functions()
     for n in ("conv_silu_l2", "kda_gate", "kda_prefill", "kda_decode", "kda_decode_k",
-              "gated_rmsnorm", "kda_last_error", "kda_prefill_workspace_bytes"):
+              "gated_rmsnorm", "kda_last_error", "kda_prefill_workspace_bytes",
+              "kda_prefill_segment_chunks"):
         assert n in names
 
 
@@ -54,6 +55,15 @@ def test_prefill_validation(lib):
     # one operand block per (chunk, head): 4*C*D + C*C + D floats
     assert ws == (4096 // 64) * 32 * (4 * 64 * 128 + 64 * 64 + 128) * 4
     assert lib.kda_prefill_workspace_bytes(100, 32, 128, 64) == 0     # T_pad % chunk
+    # segments of kda_prefill: ceil(workspace of all chunks / 160 MiB) of them,
+    # chunks spread evenly; 2 x 32 chunks at T = 4096, one segment when it fits
+    per_chunk = 32 * (4 * 64 * 128 + 64 * 64 + 128) * 4
+    for T, segs in ((4096, 2), (8192, 4), (2048, 1), (4059, 2), (64, 1), (0, 1)):
+        nc = max(1, -(-T // 64))
+        assert -(-nc * per_chunk // (160 << 20)) == segs or T == 0
+        assert lib.kda_prefill_segment_chunks(T, 32, 128, 64) == -(-nc // segs)
+    assert lib.kda_prefill_segment_chunks(4096, 32, 128, 32) == 0     # chunk not built
+    assert lib.kda_prefill_segment_chunks(4096, 0, 128, 64) == 0
     args = lambda **kw: [kw.get(n, d) for n, d in (
         ("q", A), ("k", B), ("v", C), ("gate", Dp), ("beta", E), ("state", F), ("core", 1 << 52),
         ("T", 57), ("T_pad", 64), ("H", 2), ("D", 16), ("C", 16), ("scale", 1.0),

@@ -95,8 +95,9 @@ def test_prefill_unnormalised_qk_used_as_given():
 @pytest.mark.parametrize("C", [16, 64])
 def test_prefill_steep_decay_takes_exact_diagonal_path(C):
     """Gates scaled so some 16-row blocks decay by more than 2^86 inside the
-    block: the factored diagonal would overflow fp32; the exact pairwise path
-    must still match the oracle."""
+    block (the fp32 chunk-16 form's limit for factoring its diagonal block)
+    and others less; at chunk 64 the same gates run the split form.  Both
+    must match the oracle."""
     T, H, D = 128, 2, 128
     case = core_case(T, H, D, 1505, 0.05, gate_scale=1.6)
     g2 = case["gate"] / np.log(2)           # log2 units, as the kernel measures spans
@@ -201,3 +202,34 @@ def test_prefill_phases_equal_one_call_bitwise():
     torch.cuda.synchronize()
     assert np.array_equal(core.cpu().numpy().view(np.int32), core_a.view(np.int32))
     assert np.array_equal(st.cpu().numpy().view(np.int32), S_a.view(np.int32))
+
+
+def test_prefill_segments_equal_one_pass_bitwise():
+    """kda_prefill walks segments of kda_prefill_segment_chunks chunks, each
+    prepared into the start of the workspace; at H = 64 a 2200-token prefill
+    takes three segments (the last one ragged).  Core and state must equal one
+    prepare + forward over all rows, bit for bit."""
+    import gated_delta_rule_bounded_amd as kda
+    T, T_pad, H, D, C = 2200, 2240, 64, 128, 64
+    seg = kda.kda_prefill_segment_chunks(T, H, D, C)
+    assert 1 < seg < -(-T // C), "need more than one segment"
+    g = torch.Generator(device="cuda").manual_seed(1707)
+    rnd = lambda *shape: torch.randn(*shape, device="cuda", generator=g)
+    q = torch.nn.functional.normalize(rnd(T_pad, H, D), dim=-1)
+    k = torch.nn.functional.normalize(rnd(T_pad, H, D), dim=-1)
+    v = rnd(T_pad, H, D) * 0.5
+    gate = -torch.rand(T_pad, H, D, device="cuda", generator=g) * 0.3
+    beta = torch.rand(T_pad, H, device="cuda", generator=g)
+    S0 = rnd(H, D, D) * 0.05
+    kw = dict(T=T, T_pad=T_pad, heads=H, head_dim=D, chunk=C)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(T_pad, H, D, C), dtype=torch.uint8, device="cuda")
+    say("segments", T, H, seg)
+    st_a, core_a = S0.clone(), torch.full((T_pad, H, D), 7.0, device="cuda")
+    kda.kda_prefill(q, k, v, gate, beta, st_a, core_a, ws, scale=D ** -0.5, **kw)
+    st_b, core_b = S0.clone(), torch.full((T_pad, H, D), 7.0, device="cuda")
+    kda.kda_prefill_prepare(q, k, v, gate, beta, ws, **kw)
+    kda.kda_prefill_forward(st_b, core_b, ws, scale=D ** -0.5, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(core_a.view(torch.int32), core_b.view(torch.int32))
+    assert torch.equal(st_a.view(torch.int32), st_b.view(torch.int32))
+    assert bool((core_a[T:] == 7.0).all())

@@ -593,7 +593,13 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     float4 K[DT], Q[DT], G[DT];
     load_rows<D>(q, k, gate, roff, lg, K, Q, G);
     const float braw = beta[tg * H + h];
-    select_rows<D>(valid, K, Q, G);
+    if ((int64_t)(n + 1) * C <= T) {   // a whole chunk (uniform): no row to replace
+#pragma unroll
+        for (int t8 = 0; t8 < DT; ++t8)
+            G[t8] = make_float4(G[t8].x * kLog2e, G[t8].y * kLog2e, G[t8].z * kLog2e, G[t8].w * kLog2e);
+    } else {
+        select_rows<D>(valid, K, Q, G);
+    }
     if (lg == 0) s_beta[rl] = valid ? braw : 0.f;
     // G: inclusive cumulative log-decay within this wave's block (relative
     // to R_{w-1}); the block totals go to s_tot
@@ -651,8 +657,9 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
 
     // Row operands B = K e^{G - R_{w-1}}, Qb = Q e^{G - R_{w-1}} (split), the
     // column operand Kc = K e^{R_{w-1} - G} (fp32 rows, later), and from them
-    // Q e^G (stored), K e^G (split kept for W) and Kd = K e^{G_C - G} (rows,
-    // transposed into its pair fragments through s_x first)
+    // Q e^G (stored), K e^G (fp32, the right operand of W) and
+    // Kd = K e^{G_C - G} (rows, transposed into its pair fragments through
+    // s_x first)
     auto x_operand = [&](int t8, int kb2, bf16x8 &xh, bf16x8 &xl) {
         // this lane's X[s(kb2, lg, j)][16t8 + lr] from X^T in s_xT
         const int s0 = 32 * kb2 + 4 * lg, c = 16 * t8 + lr;
@@ -666,11 +673,11 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
         s_xT[c + 2][rl] = x.z;
         s_xT[c + 3][rl] = x.w;
     };
-    bf16x8 Bh[KD], Bl[KD], Qh[KD], Ql[KD], Kh[KD], Kl[KD];
-    float4 Kc[DT];
+    bf16x8 Bh[KD], Bl[KD], Qh[KD], Ql[KD];
+    float4 Kc[DT], Kg[DT];
 #pragma unroll
     for (int kb = 0; kb < KD; ++kb) {
-        float4 b2[2], qb2[2], qg[2], kg[2];
+        float4 b2[2], qb2[2], qg[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int t8 = 2 * kb + u, c = 16 * t8 + 4 * lg;
@@ -681,7 +688,7 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
             Kc[t8] = mul4(K[t8], ei);
             const float4 pw = tab4(w, c);
             qg[u] = mul4(qb2[u], pw);
-            kg[u] = mul4(b2[u], pw);
+            Kg[t8] = mul4(b2[u], pw);
             if (!wide) {
                 put_T(t8, mul4(Kc[t8], tab4(NW + w, c)));   // Kd = K e^{R_{w-1} - G} e^{G_C - R_{w-1}}
             } else {
@@ -695,7 +702,6 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
         }
         split8(b2[0], b2[1], Bh[kb], Bl[kb]);
         split8(qb2[0], qb2[1], Qh[kb], Ql[kb]);
-        split8(kg[0], kg[1], Kh[kb], Kl[kb]);
         store_pair(blk + B::kQ + B::pfrag(w, kb, KD), lane, qg[0], qg[1]);
     }
     __syncthreads();
@@ -809,19 +815,7 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
     for (int t8 = 0; t8 < DT; ++t8) Vr[t8] = *reinterpret_cast<const float4 *>(v + roff + 16 * t8 + 4 * lg);
 #pragma unroll
-    for (int kb = 0; kb < KD; ++kb) {
-        // K e^G = hi + lo (exact in fp32), back to rows
-        const uint4 h4 = __builtin_bit_cast(uint4, Kh[kb]), l4 = __builtin_bit_cast(uint4, Kl[kb]);
-        const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w}, lw[4] = {l4.x, l4.y, l4.z, l4.w};
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __uint_as_float(hw[i] << 16) + __uint_as_float(lw[i] << 16);
-            x[2 * i + 1] = __uint_as_float(hw[i] & 0xffff0000u) + __uint_as_float(lw[i] & 0xffff0000u);
-        }
-        put_T(2 * kb, make_float4(x[0], x[1], x[2], x[3]));
-        put_T(2 * kb + 1, make_float4(x[4], x[5], x[6], x[7]));
-    }
+    for (int t8 = 0; t8 < DT; ++t8) put_T(t8, Kg[t8]);   // (K e^G)^T, right operand of W
 
     invert_unit_lower<C>(s_M, s_T, w, lane);   // ends with a barrier: s_T and s_x visible
 

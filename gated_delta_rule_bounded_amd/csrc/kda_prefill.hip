@@ -1112,19 +1112,18 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
 // values to half t%2 of block t/2 of the same lane.  The state itself stays
 // fp32 in the registers of the wave that updates it.
 //
-// Per chunk the critical path is S -> W S -> U -> Kd^T U -> S'; the products
-// off that path (Qg S, P U) are issued after the critical ones of their phase
-// so that they fill the waits on LDS and barriers.  Besides the next chunk's
-// operands, each wave touches its share of the cache lines of the block
-// three chunks ahead (one 4-byte load per lane, one line per lane, issued
-// after the chunk's operand loads; the value is only waited for two chunks
-// later), so that block is in L2 by the time its operand loads are issued.
+// Two waves per 16-row block of the chunk, one per role, so that each SIMD
+// runs one wave of each: the chain waves carry the critical path
+// S -> W S -> U -> Kd^T U -> S' and own the state tiles; the output waves
+// compute O = scale (Qg S + P U) from the same LDS operands, off that path.
+// Both roles pass the same two barriers per chunk (U published; S' published)
+// and load their own operands of the next chunk while computing the current
+// one.  The operand blocks of a segment are read from the last-level cache;
+// what bounds a chunk is the CU's vector-memory data path (each workgroup
+// reads the head's whole block per chunk, about 116 KiB).
 // ---------------------------------------------------------------------------
-// (Capped at 256 registers: within that budget the compiler keeps every
-// operand and accumulator in VGPRs, which measured faster than the larger
-// VGPR + AGPR allocation it picks uncapped.)
 template <int D, int C>
-__global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_fwd_split_kernel(
+__global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_fwd_split_kernel(
     const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
     int NC, int H, float scale)
 {
@@ -1133,27 +1132,15 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     constexpr int OWN = (DT + NW - 1) / NW;
     using B = Blk<D, C>;
     static_assert(B::kSplit, "split operand blocks need D, C multiples of 32");
-    // L2 prefetch: the DT * NW waves of a head's workgroups each touch 64 of
-    // the block's 128-byte lines
-    static_assert(B::kSize <= DT * NW * kWave * 32, "prefetch must cover the block");
     const int h = blockIdx.x % H, jt = blockIdx.x / H, j0 = 16 * jt;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool chain = r < NW;            // waves 0..NW-1 carry the state
+    const int w = chain ? r : r - NW;     // 16-row block of the chunk (and state tiles w + NW o)
     const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
 
     __shared__ __align__(16) uint4 s_Sb[KD][2][kWave];   // S slice, right operand (hi, lo)
     __shared__ __align__(16) uint4 s_Ub[KC][2][kWave];   // U, right operand (hi, lo)
 
-    float *__restrict__ Sg = state + (int64_t)h * D * D;
-    auto own_tile = [&](int o) { return min(w + NW * o, DT - 1); };
-    // Sown[o][i] = S[16*t + 4*lg + i][j0 + lr], t = own_tile(o)
-    float4 Sown[OWN];
-#pragma unroll
-    for (int o = 0; o < OWN; ++o) {
-        float e[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + j0 + lr];
-        Sown[o] = make_float4(e[0], e[1], e[2], e[3]);
-    }
     // publish an owned tile (or a U tile) as a right operand: 8 bytes of hi
     // and of lo in half `half` of this lane's 16-byte slots
     auto put = [&](uint4 (&dst)[2][kWave], int half, const float4 &x) {
@@ -1166,171 +1153,192 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
         hi = __builtin_bit_cast(bf16x8, src[0][lane]);
         lo = __builtin_bit_cast(bf16x8, src[1][lane]);
     };
-
     auto block = [&](int n) { return ws + ((int64_t)n * H + h) * B::kSize; };
-    struct Ops {
-        bf16x8 Wh[KD], Wl[KD], Qh[KD], Ql[KD], Ph[KC], Pl[KC], Kh[OWN][KC], Kl[OWN][KC];
-        float4 Ec[OWN];
-        float4 Up;     // U'[16w + 4lg + i][j0 + lr], i = 0..3
-        float pf;      // L2 prefetch in flight
-    };
     auto ldp = [&](const float *p, bf16x8 &hi, bf16x8 &lo) {
         hi = *reinterpret_cast<const bf16x8 *>(p + 4 * lane);
         lo = *reinterpret_cast<const bf16x8 *>(p + 256 + 4 * lane);
     };
-    auto load_Kd = [&](Ops &R, const float *b) {
+
+    if (chain) {
+        // ---- state chain: U = U' - W S, S' = Ec * S + Kd^T U
+        float *__restrict__ Sg = state + (int64_t)h * D * D;
+        auto own_tile = [&](int o) { return min(w + NW * o, DT - 1); };
+        // Sown[o][i] = S[16*t + 4*lg + i][j0 + lr], t = own_tile(o)
+        float4 Sown[OWN];
 #pragma unroll
         for (int o = 0; o < OWN; ++o) {
-            const int t8 = own_tile(o);
+            float e[4];
 #pragma unroll
-            for (int kb = 0; kb < KC; ++kb) ldp(b + B::kKd + B::pfrag(t8, kb, KC), R.Kh[o][kb], R.Kl[o][kb]);
-            R.Ec[o] = *reinterpret_cast<const float4 *>(b + B::kEc + 16 * t8 + 4 * lg);
+            for (int i = 0; i < 4; ++i) e[i] = Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + j0 + lr];
+            Sown[o] = make_float4(e[0], e[1], e[2], e[3]);
         }
-    };
-    auto load_ops = [&](Ops &R, const float *b) {
-        R.Up = *reinterpret_cast<const float4 *>(b + B::kU + B::frag(jt, w, NW) + 4 * lane);
-#pragma unroll
-        for (int kb = 0; kb < KD; ++kb) {
-            ldp(b + B::kW + B::pfrag(w, kb, KD), R.Wh[kb], R.Wl[kb]);
-            ldp(b + B::kQ + B::pfrag(w, kb, KD), R.Qh[kb], R.Ql[kb]);
-        }
-#pragma unroll
-        for (int kb = 0; kb < KC; ++kb) ldp(b + B::kP + B::pfrag(w, kb, KC), R.Ph[kb], R.Pl[kb]);
-        load_Kd(R, b);
-    };
-    auto prefetch = [&](int n) {
-        const int line = (jt * NW + w) * kWave + lane;
-        return block(min(n, NC - 1))[min(line * 32, B::kSize - 1)];   // stays inside the block
-    };
-
-    Ops X, Y;
-    load_ops(X, block(0));
-    X.pf = prefetch(1);
-    Y.pf = prefetch(2);
-#pragma unroll
-    for (int o = 0; o < OWN; ++o) {
-        const int t8 = own_tile(o);
-        if (DT % NW == 0 || w + NW * o < DT) put(s_Sb[t8 / 2], t8 % 2, Sown[o]);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-
-    auto chunk = [&](int n, Ops &cur, Ops &nxt, auto last) {
-        constexpr bool LAST = decltype(last)::value;
-        const float *bn = block(min(n + 1, NC - 1));   // the last chunk reloads itself
-        // ---- phase 1: U = -(W S - U') (critical), then QS = Qg S
-        bf16x8 sh[KD], sl[KD];
-#pragma unroll
-        for (int kb = 0; kb < KD; ++kb) get(s_Sb[kb], sh[kb], sl[kb]);
-        floatx4 Wa[2], Wb[2];
-        Wa[0] = floatx4{-cur.Up.x, -cur.Up.y, -cur.Up.z, -cur.Up.w};
-        Wa[1] = Wb[0] = Wb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
-        __builtin_amdgcn_sched_barrier(0);
-        nxt.Up = *reinterpret_cast<const float4 *>(bn + B::kU + B::frag(jt, w, NW) + 4 * lane);
-#pragma unroll
-        for (int kb = 0; kb < KD; ++kb) {
-            ldp(bn + B::kW + B::pfrag(w, kb, KD), nxt.Wh[kb], nxt.Wl[kb]);
-            Wa[kb & 1] = mfma_bf16(cur.Wh[kb], sh[kb], Wa[kb & 1]);
-            Wb[kb & 1] = mfma_bf16(cur.Wh[kb], sl[kb], Wb[kb & 1]);
-            Wb[kb & 1] = mfma_bf16(cur.Wl[kb], sh[kb], Wb[kb & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        float4 u;
-        u.x = -((Wa[0][0] + Wa[1][0]) + (Wb[0][0] + Wb[1][0]));
-        u.y = -((Wa[0][1] + Wa[1][1]) + (Wb[0][1] + Wb[1][1]));
-        u.z = -((Wa[0][2] + Wa[1][2]) + (Wb[0][2] + Wb[1][2]));
-        u.w = -((Wa[0][3] + Wa[1][3]) + (Wb[0][3] + Wb[1][3]));
-        put(s_Ub[w / 2], w % 2, u);
-        __builtin_amdgcn_sched_barrier(0);
-        floatx4 Qa[2], Qb[2];
-        Qa[0] = Qa[1] = Qb[0] = Qb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KD; ++kb) {
-            ldp(bn + B::kQ + B::pfrag(w, kb, KD), nxt.Qh[kb], nxt.Ql[kb]);
-            Qa[kb & 1] = mfma_bf16(cur.Qh[kb], sh[kb], Qa[kb & 1]);
-            Qb[kb & 1] = mfma_bf16(cur.Qh[kb], sl[kb], Qb[kb & 1]);
-            Qb[kb & 1] = mfma_bf16(cur.Ql[kb], sh[kb], Qb[kb & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        __syncthreads();   // B1: U operand visible; every read of the S operand done
-        __builtin_amdgcn_sched_barrier(0);
-
-        // ---- phase 2: S' = Ec * S + Kd^T U (critical), then O = scale (QS + P U)
-        bf16x8 uh[KC], ul[KC];
-#pragma unroll
-        for (int kb = 0; kb < KC; ++kb) get(s_Ub[kb], uh[kb], ul[kb]);
-        floatx4 Aa[OWN], Ab[OWN];
-#pragma unroll
-        for (int o = 0; o < OWN; ++o) {
-            Aa[o] = floatx4{Sown[o].x * cur.Ec[o].x, Sown[o].y * cur.Ec[o].y,
-                            Sown[o].z * cur.Ec[o].z, Sown[o].w * cur.Ec[o].w};
-            Ab[o] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kb = 0; kb < KC; ++kb) {
+        struct Ops {
+            bf16x8 Wh[KD], Wl[KD], Kh[OWN][KC], Kl[OWN][KC];
+            float4 Ec[OWN];
+            float4 Up;     // U'[16w + 4lg + i][j0 + lr], i = 0..3
+        };
+        auto load_Kd = [&](Ops &R, const float *b) {
 #pragma unroll
             for (int o = 0; o < OWN; ++o) {
-                Aa[o] = mfma_bf16(cur.Kh[o][kb], uh[kb], Aa[o]);
-                Ab[o] = mfma_bf16(cur.Kh[o][kb], ul[kb], Ab[o]);
-                Ab[o] = mfma_bf16(cur.Kl[o][kb], uh[kb], Ab[o]);
+                const int t8 = own_tile(o);
+#pragma unroll
+                for (int kb = 0; kb < KC; ++kb) ldp(b + B::kKd + B::pfrag(t8, kb, KC), R.Kh[o][kb], R.Kl[o][kb]);
+                R.Ec[o] = *reinterpret_cast<const float4 *>(b + B::kEc + 16 * t8 + 4 * lg);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        load_Kd(nxt, bn);
+        };
+        Ops X, Y;
+        X.Up = *reinterpret_cast<const float4 *>(block(0) + B::kU + B::frag(jt, w, NW) + 4 * lane);
+#pragma unroll
+        for (int kb = 0; kb < KD; ++kb) ldp(block(0) + B::kW + B::pfrag(w, kb, KD), X.Wh[kb], X.Wl[kb]);
+        load_Kd(X, block(0));
 #pragma unroll
         for (int o = 0; o < OWN; ++o) {
-            Sown[o] = make_float4(Aa[o][0] + Ab[o][0], Aa[o][1] + Ab[o][1], Aa[o][2] + Ab[o][2],
-                                  Aa[o][3] + Ab[o][3]);
             const int t8 = own_tile(o);
             if (DT % NW == 0 || w + NW * o < DT) put(s_Sb[t8 / 2], t8 % 2, Sown[o]);
         }
+        __syncthreads();   // B0: S operand visible
         __builtin_amdgcn_sched_barrier(0);
-        floatx4 Oa = {(Qa[0][0] + Qa[1][0]) + (Qb[0][0] + Qb[1][0]),
-                      (Qa[0][1] + Qa[1][1]) + (Qb[0][1] + Qb[1][1]),
-                      (Qa[0][2] + Qa[1][2]) + (Qb[0][2] + Qb[1][2]),
-                      (Qa[0][3] + Qa[1][3]) + (Qb[0][3] + Qb[1][3])};
-        floatx4 Ob = {0.f, 0.f, 0.f, 0.f};
+
+        auto chunk = [&](int n, Ops &cur, Ops &nxt) {
+            const float *bn = block(min(n + 1, NC - 1));   // the last chunk reloads itself
+            bf16x8 sh[KD], sl[KD];
 #pragma unroll
-        for (int kb = 0; kb < KC; ++kb) {
-            ldp(bn + B::kP + B::pfrag(w, kb, KC), nxt.Ph[kb], nxt.Pl[kb]);
-            Oa = mfma_bf16(cur.Ph[kb], uh[kb], Oa);
-            Ob = mfma_bf16(cur.Ph[kb], ul[kb], Ob);
-            Ob = mfma_bf16(cur.Pl[kb], uh[kb], Ob);
+            for (int kb = 0; kb < KD; ++kb) get(s_Sb[kb], sh[kb], sl[kb]);
+            floatx4 Wa[2], Wb[2];
+            Wa[0] = floatx4{-cur.Up.x, -cur.Up.y, -cur.Up.z, -cur.Up.w};
+            Wa[1] = Wb[0] = Wb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
             __builtin_amdgcn_sched_barrier(0);
-        }
+            nxt.Up = *reinterpret_cast<const float4 *>(bn + B::kU + B::frag(jt, w, NW) + 4 * lane);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + i;
-            if (!LAST || tr < T) core[(tr * H + h) * D + j0 + lr] = scale * (Oa[i] + Ob[i]);
-        }
-        // The prefetch goes after every operand load of this chunk: loads
-        // complete in issue order for the wait counter, so an earlier slow
-        // prefetch would hold up the waits for the operands issued after it.
-        asm volatile("" ::"v"(cur.pf));   // the prefetch of two chunks ago has landed
-        cur.pf = prefetch(n + 3);
-        __syncthreads();   // B2: S operand visible; every read of the U operand done
-        __builtin_amdgcn_sched_barrier(0);
-    };
+            for (int kb = 0; kb < KD; ++kb) {
+                ldp(bn + B::kW + B::pfrag(w, kb, KD), nxt.Wh[kb], nxt.Wl[kb]);
+                Wa[kb & 1] = mfma_bf16(cur.Wh[kb], sh[kb], Wa[kb & 1]);
+                Wb[kb & 1] = mfma_bf16(cur.Wh[kb], sl[kb], Wb[kb & 1]);
+                Wb[kb & 1] = mfma_bf16(cur.Wl[kb], sh[kb], Wb[kb & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float4 u;
+            u.x = -((Wa[0][0] + Wa[1][0]) + (Wb[0][0] + Wb[1][0]));
+            u.y = -((Wa[0][1] + Wa[1][1]) + (Wb[0][1] + Wb[1][1]));
+            u.z = -((Wa[0][2] + Wa[1][2]) + (Wb[0][2] + Wb[1][2]));
+            u.w = -((Wa[0][3] + Wa[1][3]) + (Wb[0][3] + Wb[1][3]));
+            put(s_Ub[w / 2], w % 2, u);
+            __syncthreads();   // B1: U operand visible; every read of the S operand done
+            __builtin_amdgcn_sched_barrier(0);
 
-    int n = 0;
-    for (; n + 2 < NC; n += 2) {
-        chunk(n, X, Y, std::false_type{});
-        chunk(n + 1, Y, X, std::false_type{});
-    }
-    if (n + 1 < NC) {
-        chunk(n, X, Y, std::false_type{});
-        chunk(n + 1, Y, X, std::true_type{});
+            bf16x8 uh[KC], ul[KC];
+#pragma unroll
+            for (int kb = 0; kb < KC; ++kb) get(s_Ub[kb], uh[kb], ul[kb]);
+            floatx4 Aa[OWN], Ab[OWN];
+#pragma unroll
+            for (int o = 0; o < OWN; ++o) {
+                Aa[o] = floatx4{Sown[o].x * cur.Ec[o].x, Sown[o].y * cur.Ec[o].y,
+                                Sown[o].z * cur.Ec[o].z, Sown[o].w * cur.Ec[o].w};
+                Ab[o] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < KC; ++kb) {
+#pragma unroll
+                for (int o = 0; o < OWN; ++o) {
+                    Aa[o] = mfma_bf16(cur.Kh[o][kb], uh[kb], Aa[o]);
+                    Ab[o] = mfma_bf16(cur.Kh[o][kb], ul[kb], Ab[o]);
+                    Ab[o] = mfma_bf16(cur.Kl[o][kb], uh[kb], Ab[o]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            load_Kd(nxt, bn);
+#pragma unroll
+            for (int o = 0; o < OWN; ++o) {
+                Sown[o] = make_float4(Aa[o][0] + Ab[o][0], Aa[o][1] + Ab[o][1], Aa[o][2] + Ab[o][2],
+                                      Aa[o][3] + Ab[o][3]);
+                const int t8 = own_tile(o);
+                if (DT % NW == 0 || w + NW * o < DT) put(s_Sb[t8 / 2], t8 % 2, Sown[o]);
+            }
+            __syncthreads();   // B2: S operand visible; every read of the U operand done
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int n = 0;
+        for (; n + 1 < NC; n += 2) {
+            chunk(n, X, Y);
+            chunk(n + 1, Y, X);
+        }
+        if (n < NC) chunk(n, X, Y);
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) {
+            const float e[4] = {Sown[o].x, Sown[o].y, Sown[o].z, Sown[o].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + j0 + lr] = e[i];
+        }
     } else {
-        chunk(n, X, Y, std::true_type{});
-    }
+        // ---- outputs: O = scale (Qg S + P U)
+        struct Ops {
+            bf16x8 Qh[KD], Ql[KD], Ph[KC], Pl[KC];
+        };
+        Ops X, Y;
+#pragma unroll
+        for (int kb = 0; kb < KD; ++kb) ldp(block(0) + B::kQ + B::pfrag(w, kb, KD), X.Qh[kb], X.Ql[kb]);
+#pragma unroll
+        for (int kb = 0; kb < KC; ++kb) ldp(block(0) + B::kP + B::pfrag(w, kb, KC), X.Ph[kb], X.Pl[kb]);
+        __syncthreads();   // B0
+        __builtin_amdgcn_sched_barrier(0);
 
+        auto chunk = [&](int n, Ops &cur, Ops &nxt, auto last) {
+            constexpr bool LAST = decltype(last)::value;
+            const float *bn = block(min(n + 1, NC - 1));
+            bf16x8 sh[KD], sl[KD];
 #pragma unroll
-    for (int o = 0; o < OWN; ++o) {
-        const float e[4] = {Sown[o].x, Sown[o].y, Sown[o].z, Sown[o].w};
+            for (int kb = 0; kb < KD; ++kb) get(s_Sb[kb], sh[kb], sl[kb]);
+            floatx4 Qa[2], Qb[2];
+            Qa[0] = Qa[1] = Qb[0] = Qb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + j0 + lr] = e[i];
+            for (int kb = 0; kb < KD; ++kb) {
+                ldp(bn + B::kQ + B::pfrag(w, kb, KD), nxt.Qh[kb], nxt.Ql[kb]);
+                Qa[kb & 1] = mfma_bf16(cur.Qh[kb], sh[kb], Qa[kb & 1]);
+                Qb[kb & 1] = mfma_bf16(cur.Qh[kb], sl[kb], Qb[kb & 1]);
+                Qb[kb & 1] = mfma_bf16(cur.Ql[kb], sh[kb], Qb[kb & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            floatx4 Oa = {(Qa[0][0] + Qa[1][0]) + (Qb[0][0] + Qb[1][0]),
+                          (Qa[0][1] + Qa[1][1]) + (Qb[0][1] + Qb[1][1]),
+                          (Qa[0][2] + Qa[1][2]) + (Qb[0][2] + Qb[1][2]),
+                          (Qa[0][3] + Qa[1][3]) + (Qb[0][3] + Qb[1][3])};
+            __syncthreads();   // B1
+            __builtin_amdgcn_sched_barrier(0);
+
+            bf16x8 uh[KC], ul[KC];
+#pragma unroll
+            for (int kb = 0; kb < KC; ++kb) get(s_Ub[kb], uh[kb], ul[kb]);
+            floatx4 Ob = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KC; ++kb) {
+                ldp(bn + B::kP + B::pfrag(w, kb, KC), nxt.Ph[kb], nxt.Pl[kb]);
+                Oa = mfma_bf16(cur.Ph[kb], uh[kb], Oa);
+                Ob = mfma_bf16(cur.Ph[kb], ul[kb], Ob);
+                Ob = mfma_bf16(cur.Pl[kb], uh[kb], Ob);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + i;
+                if (!LAST || tr < T) core[(tr * H + h) * D + j0 + lr] = scale * (Oa[i] + Ob[i]);
+            }
+
+            __syncthreads();   // B2
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int n = 0;
+        for (; n + 2 < NC; n += 2) {
+            chunk(n, X, Y, std::false_type{});
+            chunk(n + 1, Y, X, std::false_type{});
+        }
+        if (n + 1 < NC) {
+            chunk(n, X, Y, std::false_type{});
+            chunk(n + 1, Y, X, std::true_type{});
+        } else {
+            chunk(n, X, Y, std::true_type{});
+        }
     }
 }
 
@@ -1373,7 +1381,7 @@ static hipError_t forward_t(float *state, float *core, int T, int H, float scale
     const int NC = (T + C - 1) / C;
     if constexpr (Blk<D, C>::kSplit)
         hipLaunchKernelGGL((kda_chunk_fwd_split_kernel<D, C>), dim3(H * PrefCfg<D, C>::kDT),
-                           dim3(PrefCfg<D, C>::kThreads), 0, stream,
+                           dim3(2 * PrefCfg<D, C>::kThreads), 0, stream,
                            static_cast<const float *>(workspace), state, core, T, NC, H, scale);
     else
         hipLaunchKernelGGL((kda_chunk_fwd_kernel<D, C>), dim3(H * PrefCfg<D, C>::kDT),

@@ -301,8 +301,10 @@ def cpu_baseline(raw, threads):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # defaults: ~20 ms of warm-up steps bring the GPU to its sustained clocks
+    # (with 5 warm-up steps, 20 timed steps read ~20 % slower than steady state)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--prefill-only", action="store_true",
                     help="time the prefill steps only (profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -47,6 +47,10 @@ def _load():
     lib.orc_kda_recurrence.restype = None
     lib.orc_kda_recurrence.argtypes = ([ctypes.c_int] * 5 + [_D] * 5
                                        + [ctypes.c_double] + [_D] * 3)
+    lib.orc_bf16_array.restype = None
+    lib.orc_bf16_array.argtypes = [ctypes.c_int64, _D, _D]
+    lib.orc_linear.restype = None
+    lib.orc_linear.argtypes = [ctypes.c_int] * 3 + [_D] * 3
     lib.orc_gated_rmsnorm.restype = None
     lib.orc_gated_rmsnorm.argtypes = [ctypes.c_int] * 3 + [ctypes.c_double] + [_D] * 4
     _lib = lib
@@ -68,10 +72,74 @@ def bf16(x):
     lib = _load()
     x = _f64(x)
     out = np.empty_like(x)
-    flat_in, flat_out = x.reshape(-1), out.reshape(-1)
-    for i in range(flat_in.size):
-        flat_out[i] = lib.orc_bf16(float(flat_in[i]))
+    lib.orc_bf16_array(x.size, _p(x), _p(out))
     return out
+
+
+def linear_plain(x, w):
+    """One projection written out as loops in C: bf16(x w^T), w in torch
+    Linear layout [out, in] (small shapes: the definition the matmul form is
+    checked against)."""
+    lib = _load()
+    x, w = _f64(x), _f64(w)
+    T, n_in = x.shape
+    n_out = w.shape[0]
+    assert w.shape == (n_out, n_in)
+    y = np.empty((T, n_out))
+    lib.orc_linear(T, n_in, n_out, _p(x), _p(w), _p(y))
+    return y
+
+
+def linear(x, w):
+    """The same projection with the product taken by numpy's fp64 matmul."""
+    x, w = _f64(x), _f64(w)
+    assert x.shape[1] == w.shape[1]
+    return bf16(x @ w.T)
+
+
+def kda_block_prefill(hidden, wts, S0, conv_state, heads, head_dim, scale,
+                      eps_l2=1e-6, eps_rms=1e-5, threads=1):
+    """One KDA block over one sequence ("Glm5NextKdaLayer" page, prefill;
+    buffers of the "Glm5NextKdaWorkspace" page; weights of the
+    "Glm5NextKdaWeights" page):
+
+      qkv_proj  = [x q_proj^T | x k_proj^T | x v_proj^T]        (bf16 each)
+      conv_out  = conv_silu_l2(qkv_proj) from conv_state
+      g_raw     = f_b(f_a(x)),  b_raw = b_proj(x)                (bf16 each)
+      gate, beta = kda_gate(g_raw, b_raw)
+      core, S   = token-serial recurrence over conv_out's q|k|v from S0
+      out_gate  = g_b(g_a(x))                                    (bf16 each)
+      o_norm_out = gated_rmsnorm(core, out_gate, o_norm)
+      final_out = o_norm_out o_proj^T                            (bf16)
+
+    Readings: the rank-128 intermediates f_a(x) and g_a(x) are rounded to
+    bf16 like every projection output; the recurrence reads the conv output's
+    bf16 values (their fp32 widening is exact).  ``wts`` maps the weight
+    names of the weights page to arrays in [out, in] layout (conv [conv_dim,
+    kc], a_log [H], dt_bias [H*D], o_norm [D]).  Returns a dict of every
+    stage buffer plus the final state and conv state."""
+    H, D = heads, head_dim
+    qkv = H * D
+    x = _f64(hidden)
+    T = x.shape[0]
+    qkv_proj = np.concatenate([linear(x, wts["q_proj"]), linear(x, wts["k_proj"]),
+                               linear(x, wts["v_proj"])], axis=1)
+    conv_out, conv_st, _ = conv_silu_l2(qkv_proj, wts["conv"], conv_state, H, D, eps_l2)
+    fa = linear(x, wts["f_a"])
+    g_raw = linear(fa, wts["f_b"])
+    b_raw = linear(x, wts["b_proj"])
+    gate, beta = kda_gate(g_raw, wts["a_log"], wts["dt_bias"], H, D, b_raw=b_raw)
+    qf = conv_out[:, :qkv].reshape(T, H, D)
+    kf = conv_out[:, qkv:2 * qkv].reshape(T, H, D)
+    vf = conv_out[:, 2 * qkv:].reshape(T, H, D)
+    core, S, _ = kda_recurrence(qf, kf, vf, gate, beta, S0, scale, threads=threads)
+    ga = linear(x, wts["g_a"])
+    out_gate = linear(ga, wts["g_b"])
+    o_norm_out = gated_rmsnorm(core, out_gate, wts["o_norm"], eps_rms)
+    final_out = linear(o_norm_out, wts["o_proj"])
+    return dict(qkv_proj=qkv_proj, conv_out=conv_out, fa=fa, g_raw=g_raw, b_raw=b_raw,
+                gate=gate, beta=beta, core=core, ga=ga, out_gate=out_gate,
+                o_norm_out=o_norm_out, final_out=final_out, state=S, conv_state=conv_st)
 
 
 def conv_silu_l2(x, w, state, heads, head_dim, eps_l2=1e-6, snapshots=False):

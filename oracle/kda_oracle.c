@@ -37,6 +37,30 @@ double orc_bf16(double x)
     return copysign(r, x);
 }
 
+void orc_bf16_array(int64_t n, const double *x, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_bf16(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* One projection ("Glm5NextKdaWeights" page: weights in torch Linear        */
+/* layout [out, in], BF16): y = x W^T, i.e. y[t][o] = sum_i x[t][i] w[o][i],  */
+/* summed in fp64 in index order, then rounded to bf16, since every          */
+/* projection output is a BF16 buffer ("Glm5NextKdaWorkspace" page: fields   */
+/* qkv_parts, g_raw, out_gate, final_out).                                   */
+/* ------------------------------------------------------------------------ */
+void orc_linear(int T, int in, int out, const double *x, const double *w, double *y)
+{
+    for (int t = 0; t < T; ++t)
+        for (int o = 0; o < out; ++o) {
+            double acc = 0.0;
+            for (int i = 0; i < in; ++i)
+                acc += x[(size_t)t * in + i] * w[(size_t)o * in + i];
+            y[(size_t)t * out + o] = orc_bf16(acc);
+        }
+}
+
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 /* softplus(x) = log(1 + e^x); above 20 the correction log1p(e^-x) < 2.1e-9

@@ -34,6 +34,13 @@ extern "C" {
  * value as a double.  NaN stays NaN. */
 double orc_bf16(double x);
 
+/* orc_bf16 applied to each of n values. */
+void orc_bf16_array(int64_t n, const double *x, double *out);
+
+/* One projection with torch Linear weights ("Glm5NextKdaWeights" page):
+ *   x [T][in], w [out][in]  ->  y [T][out] = bf16(x w^T), fp64 sums. */
+void orc_linear(int T, int in, int out, const double *x, const double *w, double *y);
+
 /* Short causal depthwise conv + SiLU + per-head L2 on the q and k sections,
  * for ONE sequence ("Glm5NextKdaWorkspace" page, field conv_out;
  * "Glm5NextKdaWeights" page, field conv).

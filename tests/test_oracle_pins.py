@@ -390,3 +390,92 @@ def test_rmsnorm_unit_rms_and_scale_free(orc):
     o1 = orc.gated_rmsnorm(x, gate, w, eps=0.0)
     o2 = orc.gated_rmsnorm(x * 3.7, gate, w, eps=0.0)
     assert relerr(o2, o1) < 2.0 ** -7
+
+
+# --------------------------------------------------------------------------
+# Block: projections around the stages
+# --------------------------------------------------------------------------
+def test_linear_layout_hand_example_and_plain_loops(orc):
+    # torch Linear layout [out, in]: y = x W^T.  A transposed weight would not
+    # even have the right shape here, and a swapped operand order gives 3 rows.
+    y = orc.linear(np.array([[1.0, 2.0]]), np.array([[1.0, 0.0], [0.0, 2.0], [1.0, 1.0]]))
+    np.testing.assert_array_equal(y, [[1.0, 4.0, 3.0]])
+    # the output is a bf16 buffer: 1 + 2^-8 is a tie and rounds to even (1.0)
+    y = orc.linear(np.array([[1.0, 2.0 ** -8]]), np.array([[1.0, 1.0]]))
+    np.testing.assert_array_equal(y, [[1.0]])
+    # the matmul form equals the definition written as loops
+    r = np.random.default_rng(5)
+    x, w = r.standard_normal((6, 37)), r.standard_normal((11, 37))
+    np.testing.assert_array_equal(orc.linear(x, w), orc.linear_plain(x, w))
+
+
+def _tiny_block(T=24, H=2, D=16, rank=8, seed=131):
+    hidden = H * D
+    x, w = workloads.block_raw(T, hidden, H, D, rank, 4, seed, w_std=0.1)
+    wd = {n: t.double().numpy() for n, t in w.items()}
+    return x.double().numpy(), wd, H, D
+
+
+def _run_block(orc, x, wd, H, D, S0=None, conv_state=None):
+    qkv = H * D
+    S0 = np.zeros((H, D, D)) if S0 is None else S0
+    cs = np.zeros((4, 3 * qkv)) if conv_state is None else conv_state
+    return orc.kda_block_prefill(x, wd, S0, cs, H, D, D ** -0.5)
+
+
+def test_block_is_causal_prefix(orc):
+    # every stage is row-local or causal, so the block over the first T'
+    # rows equals the first T' rows of the block over T rows
+    x, wd, H, D = _tiny_block()
+    full = _run_block(orc, x, wd, H, D)
+    part = _run_block(orc, x[:10], wd, H, D)
+    for name in ("qkv_proj", "conv_out", "g_raw", "gate", "beta", "core", "out_gate",
+                 "o_norm_out", "final_out"):
+        np.testing.assert_array_equal(part[name], full[name][:10], err_msg=name)
+
+
+def test_block_zero_gate_projections_give_closed_forms(orc):
+    # f_b = 0: g_raw = 0, so the decay is -exp(a_log[h]) softplus(dt_bias[c]);
+    # b_proj = 0: beta = sigmoid(0) = 1/2 exactly
+    x, wd, H, D = _tiny_block()
+    wd = dict(wd, f_b=np.zeros_like(wd["f_b"]), b_proj=np.zeros_like(wd["b_proj"]))
+    out = _run_block(orc, x, wd, H, D)
+    T = x.shape[0]
+    sp = np.logaddexp(0.0, wd["dt_bias"]).reshape(H, D)
+    want = -np.exp(wd["a_log"])[:, None] * sp
+    assert relerr(out["gate"], np.broadcast_to(want, (T, H, D))) < 1e-14
+    np.testing.assert_array_equal(out["beta"], np.full((T, H), 0.5))
+
+
+def test_block_wires_sections_norm_and_output(orc):
+    # hidden = H*D.  q/k/v projections 1, 2, 3 times the identity make the
+    # pre-conv rows [x, 2x, 3x] (bf16); an identity conv tap; g_b = 0 makes
+    # the output gate sigmoid(0) = 1/2; o_proj = I passes o_norm_out through.
+    # Each stage then has an independently pinned reference, so a swapped
+    # q/k/v section, a wrong gate input or a skipped norm fails here.
+    x, wd, H, D = _tiny_block()
+    qkv = H * D
+    eye = np.eye(qkv)
+    conv = np.zeros((3 * qkv, 4))
+    conv[:, 3] = 1.0
+    wd = dict(wd, q_proj=eye, k_proj=2 * eye, v_proj=3 * eye, conv=conv,
+              g_b=np.zeros_like(wd["g_b"]), o_proj=eye)
+    r = np.random.default_rng(17)
+    S0 = r.normal(0.0, 0.1, size=(H, D, D))
+    out = _run_block(orc, x, wd, H, D, S0=S0)
+    T = x.shape[0]
+    pre = np.concatenate([orc.bf16(x), orc.bf16(2 * x), orc.bf16(3 * x)], axis=1)
+    np.testing.assert_array_equal(out["qkv_proj"], pre)
+    y, _, _ = orc.conv_silu_l2(pre, conv, np.zeros((4, 3 * qkv)), H, D)
+    np.testing.assert_array_equal(out["conv_out"], y)
+    gate, beta = orc.kda_gate(out["g_raw"], wd["a_log"], wd["dt_bias"], H, D,
+                              b_raw=out["b_raw"])
+    core, S, _ = orc.kda_recurrence(y[:, :qkv].reshape(T, H, D),
+                                    y[:, qkv:2 * qkv].reshape(T, H, D),
+                                    y[:, 2 * qkv:].reshape(T, H, D), gate, beta, S0, D ** -0.5)
+    np.testing.assert_array_equal(out["core"], core)
+    np.testing.assert_array_equal(out["state"], S)
+    np.testing.assert_array_equal(out["out_gate"], np.zeros((T, qkv)))
+    norm = orc.gated_rmsnorm(core, np.zeros((T, qkv)), wd["o_norm"])
+    np.testing.assert_array_equal(out["o_norm_out"], norm)
+    np.testing.assert_array_equal(out["final_out"], norm)

@@ -104,3 +104,23 @@ def norm_raw(T, H, D, seed):
         out_gate=to_bf16(r.standard_normal((T, H * D))),
         w=to_bf16(r.normal(1.0, 0.1, size=D)),
     )
+
+
+def block_raw(T, hidden, H, D, rank, kc, seed, w_std=0.02):
+    """Inputs of one KDA block: hidden ~ N(0,1) bf16 [T, hidden]; every bf16
+    weight ~ N(0, w_std) in torch Linear layout [out, in]: q/k/v_proj
+    [H*D, hidden], conv [3*H*D, kc], f_a/g_a [rank, hidden], f_b/g_b
+    [H*D, rank], b_proj [H, hidden], o_norm [D], o_proj [hidden, H*D]; the
+    two fp32 gate parameters a_log ~ U(-1, 0.5) [H], dt_bias ~ N(0, 0.5)
+    [H*D].  Returns (hidden, weights) as torch CPU tensors (bf16 / fp32)."""
+    r = np.random.default_rng(seed)
+    qkv = H * D
+    x = to_bf16(r.standard_normal((T, hidden)))
+    shapes = dict(q_proj=(qkv, hidden), k_proj=(qkv, hidden), v_proj=(qkv, hidden),
+                  conv=(3 * qkv, kc), f_a=(rank, hidden), f_b=(qkv, rank),
+                  b_proj=(H, hidden), g_a=(rank, hidden), g_b=(qkv, rank), o_norm=(D,),
+                  o_proj=(hidden, qkv))
+    w = {n: to_bf16(r.normal(0.0, w_std, size=s)) for n, s in shapes.items()}
+    w["a_log"] = torch.from_numpy(r.uniform(-1.0, 0.5, size=H).astype(np.float32))
+    w["dt_bias"] = torch.from_numpy(r.normal(0.0, 0.5, size=qkv).astype(np.float32))
+    return x, w

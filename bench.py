@@ -14,6 +14,8 @@ Also reported on the same JSON line (measured after the timed steps):
             read+write bytes / median step time (the metric's second half);
   decode_k  B=64, K=4 with 3 snapshots per sequence (conv decode-K + kda_decode_k);
   stages    conv_silu_l2 / kda_gate / gated_rmsnorm at T=8192 (block shapes);
+  block     the full KDA block (kda_block_prefill) at T=8192, hidden 4096:
+            tokens/s, each stage kernel alone, and the projections' share;
   roofline  for the dominant prefill kernel, from HIP events on the stream
             the kernels run on;
   cpu_baseline  the fp64 oracle on the same prefill workload, on host cores.
@@ -285,6 +287,69 @@ def bench_stages(kda, dev, reps=10):
     return res
 
 
+def bench_block(kda, dev, reps=10):
+    """The full KDA block at T = 8192 (hidden 4096, 32 heads x 128, rank-128
+    gates, weights ~ N(0, 0.02)): one kda_block_prefill call per repetition,
+    from a zero state.  The projections' share is the block time less the
+    stage kernels timed alone on the same buffers."""
+    Tb, hidden, rank = 8192, 4096, 128
+    qkv = H * D
+    x, w = workloads.block_raw(Tb, hidden, H, D, rank, 4, workloads.SEED_INPUT + 4)
+    x = x.to(dev)
+    wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+    st = torch.zeros(H, D, D, device=dev)
+    cs = torch.zeros(1, 4, 3 * qkv, dtype=torch.bfloat16, device=dev)
+    ctab = kda.ptr_table(cs)
+    buf = kda.block_buffers(Tb, heads=H, head_dim=D, rank=rank, chunk=C, device=dev)
+    out = torch.empty(Tb, hidden, dtype=torch.bfloat16, device=dev)
+
+    def block():
+        kda.kda_block_prefill(x, wd, st, ctab, buf, out, T=Tb, T_pad=Tb, hidden_size=hidden,
+                              heads=H, head_dim=D, rank=rank, chunk=C, scale=D ** -0.5)
+
+    stages = {
+        "conv_silu_l2": lambda: kda.conv_silu_l2(buf["qkv_proj"], wd["conv"], buf["conv_out"],
+                                                 n_seq=1, rows=Tb, heads=H, head_dim=D,
+                                                 conv_state=ctab, q32=buf["q32"], k32=buf["k32"],
+                                                 v32=buf["v32"]),
+        "kda_gate": lambda: kda.kda_gate(buf["g_raw"], wd["a_log"], wd["dt_bias"], buf["gate"],
+                                         T=Tb, heads=H, head_dim=D, b_raw=buf["b_raw"],
+                                         beta=buf["beta"]),
+        "kda_prefill": lambda: kda.kda_prefill(buf["q32"], buf["k32"], buf["v32"], buf["gate"],
+                                               buf["beta"], st, buf["core"], buf["prefill_ws"],
+                                               T=Tb, T_pad=Tb, heads=H, head_dim=D, chunk=C,
+                                               scale=D ** -0.5),
+        "gated_rmsnorm": lambda: kda.gated_rmsnorm(buf["core"].view(Tb, qkv), buf["out_gate"],
+                                                   wd["o_norm"], buf["o_norm_out"], T=Tb, heads=H,
+                                                   head_dim=D),
+    }
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        es = [(ev(), ev()) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in es:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in es])) * 1e-3
+
+    t_block = timed(block)
+    t_st = {n: timed(f) for n, f in stages.items()}
+    gemm_flops = 2.0 * Tb * (3 * qkv * hidden + 2 * rank * hidden + 2 * qkv * rank
+                             + H * hidden + hidden * qkv)
+    t_gemm = t_block - sum(t_st.values())
+    return dict(config=f"block prefill T={Tb}, hidden={hidden}, heads={H}, head_dim={D}, "
+                       f"rank={rank}, bf16 weights ~N(0,0.02), zero initial state",
+                tokens_per_s=Tb / t_block, ms=t_block * 1e3,
+                stage_ms={n: t * 1e3 for n, t in t_st.items()},
+                projections_ms=t_gemm * 1e3, projection_gflop=gemm_flops / 1e9,
+                projection_TFLOPs=gemm_flops / t_gemm / 1e12,
+                projection_mfma_frac=gemm_flops / t_gemm / PEAK_BF16_MFMA)
+
+
 def cpu_baseline(raw, threads):
     """The fp64 oracle, as it stands, on the full prefill workload."""
     import oracle
@@ -412,6 +477,9 @@ def main():
         out["decode_k"] = bench_decode_k(kda, dev)
         log("stages ...")
         out["stages"] = bench_stages(kda, dev)
+        log("block ...")
+        out["block"] = bench_block(kda, dev)
+        log(f"block: {out['block']['tokens_per_s'] / 1e6:.2f} M tokens/s")
     if not args.no_cpu_baseline and not args.prefill_only:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(P["raw"], cpu_threads())

@@ -21,6 +21,7 @@ from ._lib import KdaError, last_error  # noqa: F401
 __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_prepare",
            "kda_prefill_forward", "kda_decode", "kda_decode_k",
            "gated_rmsnorm", "kda_prefill_workspace_bytes", "kda_prefill_segment_chunks",
+           "kda_block_prefill", "block_buffers", "BLOCK_WEIGHT_NAMES",
            "ptr_table", "KdaError",
            "last_error", "library_path"]
 
@@ -166,3 +167,60 @@ def gated_rmsnorm(core, out_gate, w, out, *, T, heads, head_dim, eps=1e-5):
         _ptr(c2, torch.float32, "core"), _rowstride(c2, "core"), _ptr(out_gate, bf, "out_gate"),
         _rowstride(out_gate, "out_gate"), _ptr(w, bf, "w"), T, heads, head_dim, float(eps),
         _ptr(out, bf, "out"), _rowstride(out, "out"), _stream()))
+
+
+# weight names of struct kda_block_weights, in order
+BLOCK_WEIGHT_NAMES = ("q_proj", "k_proj", "v_proj", "conv", "f_a", "f_b", "dt_bias", "a_log",
+                      "b_proj", "g_a", "g_b", "o_norm", "o_proj")
+
+
+def block_buffers(T_pad, *, heads, head_dim, rank, chunk, device, gemm_ws_bytes=32 << 20):
+    """Allocate the stage buffers of kda_block_prefill as torch tensors (a
+    dict keyed by the fields of struct kda_block_buffers)."""
+    qkv = heads * head_dim
+    bf, f = torch.bfloat16, torch.float32
+    e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
+    return dict(
+        qkv_proj=e((T_pad, 3 * qkv), bf), conv_out=e((T_pad, 3 * qkv), bf),
+        q32=e((T_pad, heads, head_dim), f), k32=e((T_pad, heads, head_dim), f),
+        v32=e((T_pad, heads, head_dim), f), fa=e((T_pad, rank), bf), g_raw=e((T_pad, qkv), bf),
+        b_raw=e((T_pad, heads), bf), gate=e((T_pad, heads, head_dim), f),
+        beta=e((T_pad, heads), f), core=e((T_pad, heads, head_dim), f), ga=e((T_pad, rank), bf),
+        out_gate=e((T_pad, qkv), bf), o_norm_out=e((T_pad, qkv), bf),
+        prefill_ws=e((kda_prefill_workspace_bytes(T_pad, heads, head_dim, chunk),), torch.uint8),
+        gemm_ws=e((gemm_ws_bytes,), torch.uint8) if gemm_ws_bytes else None)
+
+
+def kda_block_prefill(hidden, weights, state, conv_state, buffers, out, *, T, T_pad, hidden_size,
+                      heads, head_dim, rank, chunk, scale, eps_l2=1e-6, eps_rms=1e-5):
+    """One KDA block over T tokens (see include/kda.h).  ``weights`` maps
+    BLOCK_WEIGHT_NAMES to device tensors (bf16, a_log and dt_bias fp32);
+    ``buffers`` is a dict from :func:`block_buffers`; ``conv_state`` is a
+    pointer table (:func:`ptr_table`) of one conv state."""
+    bf = torch.bfloat16
+    wts = _lib.BlockWeights()
+    for n in BLOCK_WEIGHT_NAMES:
+        dt = torch.float32 if n in ("a_log", "dt_bias") else bf
+        t = weights[n]
+        if not t.is_contiguous():
+            raise ValueError(f"weight {n} must be contiguous")
+        setattr(wts, n, _ptr(t, dt, n).value)
+    bufs = _lib.BlockBuffers()
+    for n, _ in _lib.BlockBuffers._fields_:
+        if n.endswith("_bytes"):
+            continue
+        t = buffers.get(n)
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"buffer {n} must be contiguous")
+        setattr(bufs, n, _ptr(t, None, n).value if t is not None else None)
+    bufs.prefill_ws_bytes = buffers["prefill_ws"].numel()
+    g = buffers.get("gemm_ws")
+    bufs.gemm_ws_bytes = g.numel() * g.element_size() if g is not None else 0
+    for name, t in (("hidden", hidden), ("out", out), ("state", state)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _check(_lib.lib.kda_block_prefill(
+        _ptr(hidden, bf, "hidden"), ctypes.byref(wts), _ptr(state, torch.float32, "state"),
+        _ptr(conv_state, torch.int64, "conv_state"), ctypes.byref(bufs), _ptr(out, bf, "out"),
+        T, T_pad, hidden_size, heads, head_dim, rank, chunk, float(scale), float(eps_l2),
+        float(eps_rms), _stream()))

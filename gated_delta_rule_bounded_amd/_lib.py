@@ -12,7 +12,24 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 # exported C symbols, as declared in include/kda.h
 SYMBOLS = ("kda_last_error", "conv_silu_l2", "kda_gate", "kda_prefill_workspace_bytes",
            "kda_prefill_segment_chunks", "kda_prefill", "kda_prefill_prepare",
-           "kda_prefill_forward", "kda_decode", "kda_decode_k", "gated_rmsnorm")
+           "kda_prefill_forward", "kda_decode", "kda_decode_k", "gated_rmsnorm",
+           "kda_block_prefill")
+
+
+class BlockWeights(ctypes.Structure):
+    """struct kda_block_weights (include/kda.h)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "q_proj", "k_proj", "v_proj", "conv", "f_a", "f_b", "dt_bias", "a_log", "b_proj",
+        "g_a", "g_b", "o_norm", "o_proj")]
+
+
+class BlockBuffers(ctypes.Structure):
+    """struct kda_block_buffers (include/kda.h)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "qkv_proj", "conv_out", "q32", "k32", "v32", "fa", "g_raw", "b_raw", "gate", "beta",
+        "core", "ga", "out_gate", "o_norm_out", "prefill_ws")] + [
+        ("prefill_ws_bytes", ctypes.c_size_t), ("gemm_ws", ctypes.c_void_p),
+        ("gemm_ws_bytes", ctypes.c_size_t)]
 
 
 class KdaError(RuntimeError):
@@ -52,6 +69,9 @@ def _load():
     lib.kda_decode_k.argtypes = [P, i64, P, P, P, P, P, i32, i32, i32, i32, f32, P]
     lib.gated_rmsnorm.restype = ctypes.c_int
     lib.gated_rmsnorm.argtypes = [P, i64, P, i64, P, i32, i32, i32, f32, P, i64, P]
+    lib.kda_block_prefill.restype = ctypes.c_int
+    lib.kda_block_prefill.argtypes = [P, ctypes.POINTER(BlockWeights), P, P,
+                                      ctypes.POINTER(BlockBuffers), P] + [i32] * 7 + [f32] * 3 + [P]
     return lib
 
 

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "conv_silu_l2.hip", "kda_gate.hip", "gated_rmsnorm.hip",
+SOURCES = ["api.cpp", "kda_gemm.cpp", "conv_silu_l2.hip", "kda_gate.hip", "gated_rmsnorm.hip",
            "kda_decode.hip", "kda_prefill.hip"]
 
 FLAGS = [
@@ -48,7 +48,8 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
+           "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

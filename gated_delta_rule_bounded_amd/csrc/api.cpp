@@ -300,4 +300,131 @@ int gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate, int6
                       "gated_rmsnorm launch");
 }
 
+int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float *state,
+                      uint16_t *const *conv_state, const kda_block_buffers *b, uint16_t *out,
+                      int32_t T, int32_t T_pad, int32_t hidden_size, int32_t heads,
+                      int32_t head_dim, int32_t rank, int32_t chunk, float scale, float eps_l2,
+                      float eps_rms, hipStream_t stream)
+{
+    if (!head_dim_ok(head_dim) || !(chunk == 16 || chunk == 64))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_block_prefill: head_dim=%d chunk=%d", head_dim, chunk);
+    const int64_t qkv = (int64_t)heads * head_dim, cd = 3 * qkv;
+    if (T < 0 || T_pad < T || T_pad % chunk || heads <= 0 || hidden_size <= 0 || rank <= 0 ||
+        hidden_size % 8 || rank % 8 || qkv % 8 || T_pad > (1 << 24))
+        return fail(KDA_ERR_SHAPE, "kda_block_prefill: T=%d T_pad=%d hidden=%d heads=%d rank=%d",
+                    T, T_pad, hidden_size, heads, rank);
+    if (T == 0) return ok();
+    if (!hidden || !w || !state || !conv_state || !b || !out)
+        return fail(KDA_ERR_NULL, "kda_block_prefill: null pointer argument");
+    const void *wp[] = {w->q_proj, w->k_proj, w->v_proj, w->conv, w->f_a, w->f_b, w->dt_bias,
+                        w->a_log, w->b_proj, w->g_a, w->g_b, w->o_norm, w->o_proj};
+    const void *bp[] = {b->qkv_proj, b->conv_out, b->q32, b->k32, b->v32, b->fa, b->g_raw,
+                        b->b_raw, b->gate, b->beta, b->core, b->ga, b->out_gate,
+                        b->o_norm_out, b->prefill_ws};
+    for (const void *p : wp)
+        if (!p) return fail(KDA_ERR_NULL, "kda_block_prefill: a weight pointer is NULL");
+    for (const void *p : bp)
+        if (!p) return fail(KDA_ERR_NULL, "kda_block_prefill: a buffer pointer is NULL");
+    if (!b->gemm_ws && b->gemm_ws_bytes)
+        return fail(KDA_ERR_NULL, "kda_block_prefill: gemm_ws is NULL with gemm_ws_bytes > 0");
+    const size_t need = kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
+    if (b->prefill_ws_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "kda_block_prefill: prefill workspace %zu bytes < %zu needed",
+                    b->prefill_ws_bytes, need);
+    for (const void *p : wp)
+        if (!aligned16(p)) return fail(KDA_ERR_SHAPE, "kda_block_prefill: misaligned weight");
+    for (const void *p : bp)
+        if (!aligned16(p)) return fail(KDA_ERR_SHAPE, "kda_block_prefill: misaligned buffer");
+    if (!aligned16(hidden) || !aligned16(out) || !aligned16(state) ||
+        (reinterpret_cast<uintptr_t>(b->prefill_ws) & 255u))
+        return fail(KDA_ERR_SHAPE, "kda_block_prefill: misaligned pointer");
+
+    // every region the call reads or writes; outputs must not touch any other
+    const size_t Tp = (size_t)T_pad, H2 = 2, F4 = 4;
+    struct Region { const void *p; size_t n; bool written; };
+    const Region rg[] = {
+        {hidden, (size_t)T * hidden_size * H2, false},
+        {w->q_proj, (size_t)qkv * hidden_size * H2, false},
+        {w->k_proj, (size_t)qkv * hidden_size * H2, false},
+        {w->v_proj, (size_t)qkv * hidden_size * H2, false},
+        {w->conv, (size_t)cd * 4 * H2, false},
+        {w->f_a, (size_t)rank * hidden_size * H2, false},
+        {w->f_b, (size_t)qkv * rank * H2, false},
+        {w->dt_bias, (size_t)qkv * F4, false},
+        {w->a_log, (size_t)heads * F4, false},
+        {w->b_proj, (size_t)heads * hidden_size * H2, false},
+        {w->g_a, (size_t)rank * hidden_size * H2, false},
+        {w->g_b, (size_t)qkv * rank * H2, false},
+        {w->o_norm, (size_t)head_dim * H2, false},
+        {w->o_proj, (size_t)hidden_size * qkv * H2, false},
+        {b->qkv_proj, Tp * cd * H2, true},
+        {b->conv_out, Tp * cd * H2, true},
+        {b->q32, Tp * qkv * F4, true},
+        {b->k32, Tp * qkv * F4, true},
+        {b->v32, Tp * qkv * F4, true},
+        {b->fa, Tp * rank * H2, true},
+        {b->g_raw, Tp * qkv * H2, true},
+        {b->b_raw, Tp * heads * H2, true},
+        {b->gate, Tp * qkv * F4, true},
+        {b->beta, Tp * heads * F4, true},
+        {b->core, Tp * qkv * F4, true},
+        {b->ga, Tp * rank * H2, true},
+        {b->out_gate, Tp * qkv * H2, true},
+        {b->o_norm_out, Tp * qkv * H2, true},
+        {b->prefill_ws, need, true},
+        {b->gemm_ws, b->gemm_ws_bytes, true},
+        {state, (size_t)heads * head_dim * head_dim * F4, true},
+        {out, (size_t)T * hidden_size * H2, true},
+    };
+    const int nr = sizeof(rg) / sizeof(rg[0]);
+    for (int i = 0; i < nr; ++i)
+        for (int j = i + 1; j < nr; ++j)
+            if ((rg[i].written || rg[j].written) && overlap(rg[i].p, rg[i].n, rg[j].p, rg[j].n))
+                return fail(KDA_ERR_ALIAS, "kda_block_prefill: regions %d and %d overlap", i, j);
+
+    const char *what = "";
+    auto gemm = [&](const char *name, const uint16_t *x, int64_t ldx, const uint16_t *wt,
+                    uint16_t *y, int64_t ldy, int n_out, int n_in) {
+        if (kda::gemm_bf16_xwT(x, ldx, wt, n_in, y, ldy, T, n_out, n_in, b->gemm_ws,
+                               b->gemm_ws_bytes, stream, &what))
+            return fail(KDA_ERR_HIP, "kda_block_prefill: %s projection: hipBLASLt %s", name, what);
+        return (int)KDA_OK;
+    };
+    int rc;
+    // q|k|v projections straight into the packed pre-conv rows
+    if ((rc = gemm("q", hidden, hidden_size, w->q_proj, b->qkv_proj, cd, (int)qkv, hidden_size)) ||
+        (rc = gemm("k", hidden, hidden_size, w->k_proj, b->qkv_proj + qkv, cd, (int)qkv, hidden_size)) ||
+        (rc = gemm("v", hidden, hidden_size, w->v_proj, b->qkv_proj + 2 * qkv, cd, (int)qkv, hidden_size)))
+        return rc;
+    if ((rc = hip_status(kda::launch_conv_silu_l2(b->qkv_proj, cd, w->conv, conv_state, nullptr, 1,
+                                                  T, heads, head_dim, eps_l2, b->conv_out, cd,
+                                                  b->q32, b->k32, b->v32, stream),
+                         "kda_block_prefill: conv_silu_l2 launch")))
+        return rc;
+    if ((rc = gemm("f_a", hidden, hidden_size, w->f_a, b->fa, rank, rank, hidden_size)) ||
+        (rc = gemm("f_b", b->fa, rank, w->f_b, b->g_raw, qkv, (int)qkv, rank)) ||
+        (rc = gemm("b_proj", hidden, hidden_size, w->b_proj, b->b_raw, heads, heads, hidden_size)))
+        return rc;
+    if ((rc = hip_status(kda::launch_kda_gate(b->g_raw, qkv, b->b_raw, heads, w->a_log, w->dt_bias,
+                                              T, heads, head_dim, b->gate, b->beta, stream),
+                         "kda_block_prefill: kda_gate launch")))
+        return rc;
+    if ((rc = hip_status(kda::launch_kda_prefill(b->q32, b->k32, b->v32, b->gate, b->beta, state,
+                                                 b->core, T, heads, head_dim, chunk, scale,
+                                                 b->prefill_ws, stream),
+                         "kda_block_prefill: kda_prefill launch")))
+        return rc;
+    if ((rc = gemm("g_a", hidden, hidden_size, w->g_a, b->ga, rank, rank, hidden_size)) ||
+        (rc = gemm("g_b", b->ga, rank, w->g_b, b->out_gate, qkv, (int)qkv, rank)))
+        return rc;
+    if ((rc = hip_status(kda::launch_gated_rmsnorm(b->core, qkv, b->out_gate, qkv, w->o_norm, T,
+                                                   heads, head_dim, eps_rms, b->o_norm_out, qkv,
+                                                   stream),
+                         "kda_block_prefill: gated_rmsnorm launch")))
+        return rc;
+    if ((rc = gemm("o", b->o_norm_out, qkv, w->o_proj, out, hidden_size, hidden_size, (int)qkv)))
+        return rc;
+    return ok();
+}
+
 }  // extern "C"

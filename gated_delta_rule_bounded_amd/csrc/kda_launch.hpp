@@ -50,4 +50,11 @@ hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
                               float *core, int T, int heads, int head_dim, int chunk,
                               float scale, void *workspace, hipStream_t stream);
 
+// y[rows][n_out] (row stride ldy) = bf16(x[rows][n_in] (stride ldx) w^T), w in
+// torch Linear layout [n_out][n_in] (stride ldw), fp32 accumulation, on the
+// vendor GEMM (kda_gemm.cpp).  Returns 0, or 1 with *what naming the failure.
+int gemm_bf16_xwT(const uint16_t *x, int64_t ldx, const uint16_t *w, int64_t ldw, uint16_t *y,
+                  int64_t ldy, int rows, int n_out, int n_in, void *ws, size_t ws_bytes,
+                  hipStream_t stream, const char **what);
+
 }  // namespace kda

@@ -915,7 +915,6 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
     const int h = blockIdx.x % H, jt = blockIdx.x / H, j0 = 16 * jt;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-    const int rl = 16 * w + lr;
 
     __shared__ float s_u[C][16 + kPad16];
     __shared__ float s_S[D][16 + kPad16];

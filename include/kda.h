@@ -223,6 +223,73 @@ int gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate,
                   int32_t head_dim, float eps, uint16_t *out, int64_t ldy,
                   hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * kda_block_prefill — one whole KDA block over one sequence of T tokens from
+ * the carried state ("Glm5NextKdaLayer" page, prefill; stage buffers of the
+ * "Glm5NextKdaWorkspace" page; weights of the "Glm5NextKdaWeights" page):
+ *
+ *   qkv_proj   = [h q_proj^T | h k_proj^T | h v_proj^T]     bf16 projections
+ *   conv_out   = conv_silu_l2(qkv_proj) from *conv_state[0] (updated), plus
+ *                its fp32 widening q32/k32/v32
+ *   fa = h f_a^T, g_raw = fa f_b^T, b_raw = h b_proj^T      bf16 projections
+ *   gate, beta = kda_gate(g_raw, b_raw, a_log, dt_bias)
+ *   core       = kda_prefill(q32, k32, v32, gate, beta) from state (updated)
+ *   ga = h g_a^T, out_gate = ga g_b^T                       bf16 projections
+ *   o_norm_out = gated_rmsnorm(core, out_gate, o_norm)
+ *   out        = o_norm_out o_proj^T                        bf16 [T, hidden]
+ *
+ * The projections are plain GEMMs (bf16 operands, fp32 accumulation, bf16
+ * result) run by the vendor library (hipBLASLt); everything between them is
+ * this library's own kernels.  The library keeps one hipBLASLt handle and
+ * one algorithm choice per GEMM shape for each device, made on first use;
+ * it allocates no device memory of its own per call (the GEMM workspace is
+ * gemm_ws, which may be NULL with gemm_ws_bytes 0).
+ *
+ * Weights (device, caller-owned) are bf16 in torch Linear layout [out, in]:
+ *   q_proj, k_proj, v_proj [heads*head_dim, hidden]; conv [3*heads*head_dim, 4];
+ *   f_a, g_a [rank, hidden]; f_b, g_b [heads*head_dim, rank];
+ *   b_proj [heads, hidden]; o_norm [head_dim]; o_proj [hidden, heads*head_dim];
+ *   a_log fp32 [heads]; dt_bias fp32 [heads*head_dim].
+ * Buffers (device, caller-owned, rows beyond T left as they are):
+ *   qkv_proj, conv_out bf16 [T_pad, 3*heads*head_dim]; q32, k32, v32, core,
+ *   gate fp32 [T_pad, heads*head_dim]; beta fp32 [T_pad, heads];
+ *   fa, ga bf16 [T_pad, rank]; g_raw, out_gate, o_norm_out bf16
+ *   [T_pad, heads*head_dim]; b_raw bf16 [T_pad, heads];
+ *   prefill_ws of at least kda_prefill_workspace_bytes(T_pad, ...) bytes.
+ * hidden bf16 [T, hidden]; out bf16 [T, hidden]; state fp32 [heads, head_dim,
+ * head_dim] in/out; conv_state a device table of one pointer to bf16
+ * [4, 3*heads*head_dim] in/out.
+ * Every buffer, out, state and the conv state must be pairwise disjoint and
+ * disjoint from hidden and the weights (KDA_ERR_ALIAS).  hidden, rank and
+ * heads*head_dim must be multiples of 8; chunk 16 or 64 with T_pad % chunk
+ * == 0 (KDA_ERR_SHAPE / KDA_ERR_UNSUPPORTED).  A vendor GEMM failure returns
+ * KDA_ERR_HIP with its reason in kda_last_error().  T == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+typedef struct kda_block_weights {
+    const uint16_t *q_proj, *k_proj, *v_proj, *conv;
+    const uint16_t *f_a, *f_b;
+    const float *dt_bias, *a_log;
+    const uint16_t *b_proj, *g_a, *g_b, *o_norm, *o_proj;
+} kda_block_weights;
+
+typedef struct kda_block_buffers {
+    uint16_t *qkv_proj, *conv_out;
+    float *q32, *k32, *v32;
+    uint16_t *fa, *g_raw, *b_raw;
+    float *gate, *beta, *core;
+    uint16_t *ga, *out_gate, *o_norm_out;
+    void *prefill_ws;
+    size_t prefill_ws_bytes;
+    void *gemm_ws;
+    size_t gemm_ws_bytes;
+} kda_block_buffers;
+
+int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float *state,
+                      uint16_t *const *conv_state, const kda_block_buffers *buf,
+                      uint16_t *out, int32_t T, int32_t T_pad, int32_t hidden_size,
+                      int32_t heads, int32_t head_dim, int32_t rank, int32_t chunk,
+                      float scale, float eps_l2, float eps_rms, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -138,3 +138,54 @@ def test_stage_validation(lib):
     assert norm(w=None) == E_NULL
     assert norm(ldo=30) == E_SHAPE
     assert norm(T=0, core=None) == OK
+
+
+def _block_args(lib):
+    import gated_delta_rule_bounded_amd as kda
+    L = kda._lib
+    w = L.BlockWeights()
+    for i, (n, _) in enumerate(L.BlockWeights._fields_):
+        setattr(w, n, (i + 1) << 36)                 # distinct, far apart, 256-aligned
+    b = L.BlockBuffers()
+    for i, (n, _) in enumerate(L.BlockBuffers._fields_):
+        if not n.endswith("_bytes"):
+            setattr(b, n, (i + 20) << 36)
+    b.prefill_ws_bytes = lib.kda_prefill_workspace_bytes(128, 2, 16, 16)
+    b.gemm_ws_bytes = 1 << 20
+    return w, b
+
+
+def test_block_validation(lib):
+    w, b = _block_args(lib)
+    ref = ctypes.byref
+    H, Dh, hid, rank = 2, 16, 64, 16
+
+    def call(w_=w, b_=b, T=100, T_pad=128, head_dim=Dh, chunk=16, hidden=hid, rk=rank,
+             state=60 << 36, out=61 << 36, conv=62 << 36, x=63 << 36):
+        return lib.kda_block_prefill(x, ref(w_) if w_ is not None else None, state, conv,
+                                     ref(b_) if b_ is not None else None, out, T, T_pad,
+                                     hidden, H, head_dim, rk, chunk, 0.25, 1e-6, 1e-5, None)
+
+    assert call(T=0) == OK                                   # no-op before any pointer is used
+    assert call(head_dim=64) == E_UNSUP
+    assert call(chunk=32) == E_UNSUP
+    assert call(T_pad=120) == E_SHAPE                        # T_pad % chunk
+    assert call(T=129) == E_SHAPE                            # T_pad < T
+    assert call(hidden=60) == E_SHAPE                        # hidden % 8
+    assert call(rk=12) == E_SHAPE                            # rank % 8
+    assert call(w_=None) == E_NULL
+    assert call(b_=None) == E_NULL
+    assert call(out=0) == E_NULL
+    w2, b2 = _block_args(lib)
+    w2.o_proj = None
+    assert call(w_=w2) == E_NULL
+    w2, b2 = _block_args(lib)
+    b2.prefill_ws_bytes -= 1
+    assert call(b_=b2) == E_WS
+    w2, b2 = _block_args(lib)
+    b2.out_gate = b2.g_raw                                   # the pages forbid this alias
+    assert call(b_=b2) == E_ALIAS
+    w2, b2 = _block_args(lib)
+    assert call(out=w2.q_proj) == E_ALIAS                    # writing over a weight
+    assert call(state=b2.core + 64) == E_ALIAS
+    assert call(x=b2.qkv_proj) == E_ALIAS                    # a buffer over the input

@@ -1,0 +1,92 @@
+"""kda_block_prefill on the GPU (projections on the vendor GEMM around this
+library's stage kernels) against the oracle's block.
+
+Tolerance 2e-2 (max relative error per tensor) on every stage buffer, the
+block output and the carried state: every stage after the projections reads
+bf16 projection outputs, and a projection's fp32-accumulated sum may round
+to the bf16 neighbour of the oracle's fp64 sum, so everything downstream
+carries bf16-level differences (the bf16-stage bound).  At the full block
+size (T = 8192, hidden 4096, 32 heads) the oracle runs the causal prefix of
+the first rows: every stage is row-local or causal, so those rows of the
+GPU's full-length run must match it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_bounded_amd as kda
+import workloads
+from conftest import relerr
+from kda_cases import say
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+STAGES = ("qkv_proj", "conv_out", "fa", "g_raw", "b_raw", "gate", "beta", "core", "ga",
+          "out_gate", "o_norm_out")
+
+
+def run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale):
+    dev = torch.device("cuda")
+    wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+    xg = x[:T].to(dev).contiguous()
+    st = torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).to(dev)
+    cs = conv0.to(dev).contiguous()
+    buf = kda.block_buffers(T_pad, heads=H, head_dim=D, rank=rank, chunk=C, device=dev)
+    out = torch.empty(T, hidden, dtype=torch.bfloat16, device=dev)
+    say("block", T, T_pad, hidden, H, D, rank, C)
+    kda.kda_block_prefill(xg, wd, st, kda.ptr_table([cs]), buf, out, T=T, T_pad=T_pad,
+                          hidden_size=hidden, heads=H, head_dim=D, rank=rank, chunk=C,
+                          scale=scale)
+    torch.cuda.synchronize()
+    res = {n: buf[n][:T].float().cpu().numpy() for n in STAGES}
+    res["final_out"] = out.float().cpu().numpy()
+    res["state"] = st.cpu().numpy()
+    res["conv_state"] = cs.float().cpu().numpy()
+    return res
+
+
+def run_oracle(orc, x, w, T, H, D, S0, conv0, scale):
+    wd = {n: t.double().numpy() for n, t in w.items()}
+    return orc.kda_block_prefill(x[:T].double().numpy(), wd, np.asarray(S0, dtype=np.float64),
+                                 conv0.double().numpy(), H, D, scale, threads=8)
+
+
+def compare(got, ref, T, H, D, names):
+    for n in names:
+        g = got[n][:T].reshape(ref[n].shape)
+        e = relerr(g, ref[n])
+        assert e < TOL, f"{n}: relerr {e:.3e}"
+
+
+@pytest.mark.parametrize("T,T_pad,H,D,hidden,rank,C", [
+    (50, 64, 2, 16, 64, 16, 16),
+    (200, 256, 2, 128, 256, 32, 64),
+])
+def test_block_small_against_oracle(orc, T, T_pad, H, D, hidden, rank, C):
+    x, w = workloads.block_raw(T, hidden, H, D, rank, 4, 1004, w_std=0.05)
+    S0 = workloads.state(H, D, 0.05, 2004)
+    conv0 = workloads.conv_raw(1, H, D, 4, 3004)["state"][0]
+    scale = D ** -0.5
+    got = run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale)
+    ref = run_oracle(orc, x, w, T, H, D, S0, conv0, scale)
+    compare(got, ref, T, H, D, STAGES + ("final_out",))
+    assert relerr(got["state"], ref["state"]) < TOL
+    assert relerr(got["conv_state"], ref["conv_state"]) < TOL
+
+
+def test_block_full_size_causal_prefix(orc):
+    # the full KDA block workload: T = 8192, hidden 4096, 32 heads x 128,
+    # rank-128 gates, weights ~ N(0, 0.02), zero initial state and conv state
+    T, T_pad, H, D, hidden, rank, C = 8192, 8192, 32, 128, 4096, 128, 64
+    Tp = 256
+    x, w = workloads.block_raw(T, hidden, H, D, rank, 4, 1004)
+    S0 = np.zeros((H, D, D), dtype=np.float32)
+    conv0 = torch.zeros(4, 3 * H * D, dtype=torch.bfloat16)
+    scale = D ** -0.5
+    got = run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale)
+    ref = run_oracle(orc, x, w, Tp, H, D, S0, conv0, scale)
+    compare(got, ref, Tp, H, D, STAGES + ("final_out",))
+    for n in STAGES + ("final_out",):
+        assert np.all(np.isfinite(got[n])), n
+    assert np.all(np.isfinite(got["state"]))

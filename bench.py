@@ -372,6 +372,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--prefill-only", action="store_true",
                     help="time the prefill steps only (profiler runs)")
+    ap.add_argument("--block-only", action="store_true",
+                    help="time the full-block call only and print its JSON object (profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (scales HBM counters)")
@@ -387,6 +389,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.block_only:
+        print(json.dumps({"block": bench_block(kda, dev)}), flush=True)
+        return
 
     if args.calibrate_copy:
         # one elementwise kernel that reads 1 GiB and writes 1 GiB: the scale

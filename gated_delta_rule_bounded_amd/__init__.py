@@ -22,6 +22,8 @@ __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_prepare",
            "kda_prefill_forward", "kda_decode", "kda_decode_k",
            "gated_rmsnorm", "kda_prefill_workspace_bytes", "kda_prefill_segment_chunks",
            "kda_block_prefill", "block_buffers", "BLOCK_WEIGHT_NAMES",
+           "dense_gemv_bf16_batchm", "kda_block_decode", "kda_block_decode_k",
+           "block_decode_buffers",
            "ptr_table", "KdaError",
            "last_error", "library_path"]
 
@@ -191,6 +193,17 @@ def block_buffers(T_pad, *, heads, head_dim, rank, chunk, device, gemm_ws_bytes=
         gemm_ws=e((gemm_ws_bytes,), torch.uint8) if gemm_ws_bytes else None)
 
 
+def _block_weights(weights):
+    wts = _lib.BlockWeights()
+    for n in BLOCK_WEIGHT_NAMES:
+        dt = torch.float32 if n in ("a_log", "dt_bias") else torch.bfloat16
+        t = weights[n]
+        if not t.is_contiguous():
+            raise ValueError(f"weight {n} must be contiguous")
+        setattr(wts, n, _ptr(t, dt, n).value)
+    return wts
+
+
 def kda_block_prefill(hidden, weights, state, conv_state, buffers, out, *, T, T_pad, hidden_size,
                       heads, head_dim, rank, chunk, scale, eps_l2=1e-6, eps_rms=1e-5):
     """One KDA block over T tokens (see include/kda.h).  ``weights`` maps
@@ -198,13 +211,7 @@ def kda_block_prefill(hidden, weights, state, conv_state, buffers, out, *, T, T_
     ``buffers`` is a dict from :func:`block_buffers`; ``conv_state`` is a
     pointer table (:func:`ptr_table`) of one conv state."""
     bf = torch.bfloat16
-    wts = _lib.BlockWeights()
-    for n in BLOCK_WEIGHT_NAMES:
-        dt = torch.float32 if n in ("a_log", "dt_bias") else bf
-        t = weights[n]
-        if not t.is_contiguous():
-            raise ValueError(f"weight {n} must be contiguous")
-        setattr(wts, n, _ptr(t, dt, n).value)
+    wts = _block_weights(weights)
     bufs = _lib.BlockBuffers()
     for n, _ in _lib.BlockBuffers._fields_:
         if n.endswith("_bytes"):
@@ -224,3 +231,65 @@ def kda_block_prefill(hidden, weights, state, conv_state, buffers, out, *, T, T_
         _ptr(conv_state, torch.int64, "conv_state"), ctypes.byref(bufs), _ptr(out, bf, "out"),
         T, T_pad, hidden_size, heads, head_dim, rank, chunk, float(scale), float(eps_l2),
         float(eps_rms), _stream()))
+
+
+def dense_gemv_bf16_batchm(x, w, y, *, M, N, Kd):
+    """y[:M] = bf16(x[:M] w^T), each row exactly as it would come out alone."""
+    bf = torch.bfloat16
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    _check(_lib.lib.dense_gemv_bf16_batchm(
+        _ptr(x, bf, "x"), _rowstride(x, "x"), _ptr(w, bf, "w"), M, N, Kd, _ptr(y, bf, "y"),
+        _rowstride(y, "y"), _stream()))
+
+
+def block_decode_buffers(rows, *, heads, head_dim, rank, device):
+    """Allocate the stage buffers of kda_block_decode(_k) for ``rows`` = B*K
+    rows (a dict keyed by the fields of struct kda_block_decode_buffers)."""
+    qkv = heads * head_dim
+    bf, f = torch.bfloat16, torch.float32
+    e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
+    return dict(
+        qkv_proj=e((rows, 3 * qkv), bf), conv_out=e((rows, 3 * qkv), bf),
+        fa=e((rows, rank), bf), g_raw=e((rows, qkv), bf), b_raw=e((rows, heads), bf),
+        gate=e((rows, heads, head_dim), f), beta=e((rows, heads), f),
+        core=e((rows, heads, head_dim), f), ga=e((rows, rank), bf),
+        out_gate=e((rows, qkv), bf), o_norm_out=e((rows, qkv), bf))
+
+
+def _decode_buffers(buffers):
+    bufs = _lib.BlockDecodeBuffers()
+    for n, _ in _lib.BlockDecodeBuffers._fields_:
+        t = buffers[n]
+        if not t.is_contiguous():
+            raise ValueError(f"buffer {n} must be contiguous")
+        setattr(bufs, n, _ptr(t, None, n).value)
+    return bufs
+
+
+def kda_block_decode_k(hidden, weights, state, conv_state, buffers, out, *, B, K, hidden_size,
+                       heads, head_dim, rank, scale, snap=None, conv_snap=None, eps_l2=1e-6,
+                       eps_rms=1e-5):
+    """K tokens of each of B sequences through the whole block, bit-identical
+    to K kda_block_decode calls.  ``state`` / ``conv_state`` are pointer
+    tables of B entries; ``snap`` / ``conv_snap`` tables of B*(K-1) or None."""
+    bf = torch.bfloat16
+    wts, bufs = _block_weights(weights), _decode_buffers(buffers)
+    _check(_lib.lib.kda_block_decode_k(
+        _ptr(hidden, bf, "hidden"), ctypes.byref(wts), _ptr(state, torch.int64, "state"),
+        _ptr(conv_state, torch.int64, "conv_state"), _ptr(snap, torch.int64, "snap"),
+        _ptr(conv_snap, torch.int64, "conv_snap"), ctypes.byref(bufs), _ptr(out, bf, "out"),
+        B, K, hidden_size, heads, head_dim, rank, float(scale), float(eps_l2), float(eps_rms),
+        _stream()))
+
+
+def kda_block_decode(hidden, weights, state, conv_state, buffers, out, *, B, hidden_size, heads,
+                     head_dim, rank, scale, eps_l2=1e-6, eps_rms=1e-5):
+    """One token of each of B sequences through the whole block."""
+    bf = torch.bfloat16
+    wts, bufs = _block_weights(weights), _decode_buffers(buffers)
+    _check(_lib.lib.kda_block_decode(
+        _ptr(hidden, bf, "hidden"), ctypes.byref(wts), _ptr(state, torch.int64, "state"),
+        _ptr(conv_state, torch.int64, "conv_state"), ctypes.byref(bufs), _ptr(out, bf, "out"),
+        B, hidden_size, heads, head_dim, rank, float(scale), float(eps_l2), float(eps_rms),
+        _stream()))

@@ -13,7 +13,8 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 SYMBOLS = ("kda_last_error", "conv_silu_l2", "kda_gate", "kda_prefill_workspace_bytes",
            "kda_prefill_segment_chunks", "kda_prefill", "kda_prefill_prepare",
            "kda_prefill_forward", "kda_decode", "kda_decode_k", "gated_rmsnorm",
-           "kda_block_prefill")
+           "kda_block_prefill", "dense_gemv_bf16_batchm", "kda_block_decode_k",
+           "kda_block_decode")
 
 
 class BlockWeights(ctypes.Structure):
@@ -30,6 +31,13 @@ class BlockBuffers(ctypes.Structure):
         "core", "ga", "out_gate", "o_norm_out", "prefill_ws")] + [
         ("prefill_ws_bytes", ctypes.c_size_t), ("gemm_ws", ctypes.c_void_p),
         ("gemm_ws_bytes", ctypes.c_size_t)]
+
+
+class BlockDecodeBuffers(ctypes.Structure):
+    """struct kda_block_decode_buffers (include/kda.h)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "qkv_proj", "conv_out", "fa", "g_raw", "b_raw", "gate", "beta", "core", "ga",
+        "out_gate", "o_norm_out")]
 
 
 class KdaError(RuntimeError):
@@ -72,6 +80,16 @@ def _load():
     lib.kda_block_prefill.restype = ctypes.c_int
     lib.kda_block_prefill.argtypes = [P, ctypes.POINTER(BlockWeights), P, P,
                                       ctypes.POINTER(BlockBuffers), P] + [i32] * 7 + [f32] * 3 + [P]
+    lib.dense_gemv_bf16_batchm.restype = ctypes.c_int
+    lib.dense_gemv_bf16_batchm.argtypes = [P, i64, P, i32, i32, i32, P, i64, P]
+    lib.kda_block_decode_k.restype = ctypes.c_int
+    lib.kda_block_decode_k.argtypes = [P, ctypes.POINTER(BlockWeights), P, P, P, P,
+                                       ctypes.POINTER(BlockDecodeBuffers), P] + [i32] * 6 + \
+        [f32] * 3 + [P]
+    lib.kda_block_decode.restype = ctypes.c_int
+    lib.kda_block_decode.argtypes = [P, ctypes.POINTER(BlockWeights), P, P,
+                                     ctypes.POINTER(BlockDecodeBuffers), P] + [i32] * 5 + \
+        [f32] * 3 + [P]
     return lib
 
 

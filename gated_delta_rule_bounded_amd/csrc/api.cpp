@@ -427,4 +427,151 @@ int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float 
     return ok();
 }
 
+int dense_gemv_bf16_batchm(const uint16_t *x, int64_t ldx, const uint16_t *w, int32_t M,
+                           int32_t N, int32_t Kd, uint16_t *y, int64_t ldy, hipStream_t stream)
+{
+    if (M < 0 || N <= 0 || Kd <= 0 || Kd % 32 || M > (1 << 24))
+        return fail(KDA_ERR_SHAPE, "dense_gemv_bf16_batchm: M=%d N=%d Kd=%d (Kd %% 32 == 0)", M,
+                    N, Kd);
+    if (M == 0) return ok();
+    if (!x || !w || !y) return fail(KDA_ERR_NULL, "dense_gemv_bf16_batchm: null pointer argument");
+    if (ldx < Kd || ldy < N || ldx % 8)
+        return fail(KDA_ERR_SHAPE, "dense_gemv_bf16_batchm: ldx=%lld ldy=%lld", (long long)ldx,
+                    (long long)ldy);
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y))
+        return fail(KDA_ERR_SHAPE, "dense_gemv_bf16_batchm: pointers must be 16-byte aligned");
+    const size_t yb = (size_t)((M - 1) * ldy + N) * 2;
+    if (overlap(y, yb, x, (size_t)((M - 1) * ldx + Kd) * 2) ||
+        overlap(y, yb, w, (size_t)N * Kd * 2))
+        return fail(KDA_ERR_ALIAS, "dense_gemv_bf16_batchm: y overlaps x or w");
+    const kda::GemvSeg seg{x, w, y, ldx, ldy, N, Kd};
+    return hip_status(kda::launch_gemv_bf16_batchm(&seg, 1, M, stream),
+                      "dense_gemv_bf16_batchm launch");
+}
+
+int kda_block_decode_k(const uint16_t *hidden, const kda_block_weights *w, float *const *state,
+                       uint16_t *const *conv_state, float *const *snap,
+                       uint16_t *const *conv_snap, const kda_block_decode_buffers *b,
+                       uint16_t *out, int32_t B, int32_t K, int32_t hidden_size, int32_t heads,
+                       int32_t head_dim, int32_t rank, float scale, float eps_l2, float eps_rms,
+                       hipStream_t stream)
+{
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_block_decode_k: head_dim=%d", head_dim);
+    const int64_t qkv = (int64_t)heads * head_dim, cd = 3 * qkv;
+    if (B < 0 || K < 0 || heads <= 0 || hidden_size <= 0 || rank <= 0 || hidden_size % 32 ||
+        rank % 32 || qkv % 32 || (int64_t)B * K > (1 << 24))
+        return fail(KDA_ERR_SHAPE, "kda_block_decode_k: B=%d K=%d hidden=%d heads=%d rank=%d", B,
+                    K, hidden_size, heads, rank);
+    if (B == 0 || K == 0) return ok();
+    if (!hidden || !w || !state || !conv_state || !b || !out)
+        return fail(KDA_ERR_NULL, "kda_block_decode_k: null pointer argument");
+    const void *wp[] = {w->q_proj, w->k_proj, w->v_proj, w->conv, w->f_a, w->f_b, w->dt_bias,
+                        w->a_log, w->b_proj, w->g_a, w->g_b, w->o_norm, w->o_proj};
+    const void *bp[] = {b->qkv_proj, b->conv_out, b->fa, b->g_raw, b->b_raw, b->gate,
+                        b->beta, b->core, b->ga, b->out_gate, b->o_norm_out};
+    for (const void *p : wp)
+        if (!p) return fail(KDA_ERR_NULL, "kda_block_decode_k: a weight pointer is NULL");
+    for (const void *p : bp)
+        if (!p) return fail(KDA_ERR_NULL, "kda_block_decode_k: a buffer pointer is NULL");
+    for (const void *p : wp)
+        if (!aligned16(p)) return fail(KDA_ERR_SHAPE, "kda_block_decode_k: misaligned weight");
+    for (const void *p : bp)
+        if (!aligned16(p)) return fail(KDA_ERR_SHAPE, "kda_block_decode_k: misaligned buffer");
+    if (!aligned16(hidden) || !aligned16(out))
+        return fail(KDA_ERR_SHAPE, "kda_block_decode_k: misaligned pointer");
+    if (snap && (const void *)snap == (const void *)state)
+        return fail(KDA_ERR_ALIAS, "kda_block_decode_k: snapshot table is the state table");
+    if (conv_snap && (const void *)conv_snap == (const void *)conv_state)
+        return fail(KDA_ERR_ALIAS, "kda_block_decode_k: conv snapshot table is the conv state table");
+
+    const size_t M = (size_t)B * K, H2 = 2, F4 = 4;
+    struct Region { const void *p; size_t n; bool written; };
+    const Region rg[] = {
+        {hidden, M * hidden_size * H2, false},
+        {w->q_proj, (size_t)qkv * hidden_size * H2, false},
+        {w->k_proj, (size_t)qkv * hidden_size * H2, false},
+        {w->v_proj, (size_t)qkv * hidden_size * H2, false},
+        {w->conv, (size_t)cd * 4 * H2, false},
+        {w->f_a, (size_t)rank * hidden_size * H2, false},
+        {w->f_b, (size_t)qkv * rank * H2, false},
+        {w->dt_bias, (size_t)qkv * F4, false},
+        {w->a_log, (size_t)heads * F4, false},
+        {w->b_proj, (size_t)heads * hidden_size * H2, false},
+        {w->g_a, (size_t)rank * hidden_size * H2, false},
+        {w->g_b, (size_t)qkv * rank * H2, false},
+        {w->o_norm, (size_t)head_dim * H2, false},
+        {w->o_proj, (size_t)hidden_size * qkv * H2, false},
+        {b->qkv_proj, M * cd * H2, true},
+        {b->conv_out, M * cd * H2, true},
+        {b->fa, M * rank * H2, true},
+        {b->g_raw, M * qkv * H2, true},
+        {b->b_raw, M * heads * H2, true},
+        {b->gate, M * qkv * F4, true},
+        {b->beta, M * heads * F4, true},
+        {b->core, M * qkv * F4, true},
+        {b->ga, M * rank * H2, true},
+        {b->out_gate, M * qkv * H2, true},
+        {b->o_norm_out, M * qkv * H2, true},
+        {out, M * hidden_size * H2, true},
+    };
+    const int nr = sizeof(rg) / sizeof(rg[0]);
+    for (int i = 0; i < nr; ++i)
+        for (int j = i + 1; j < nr; ++j)
+            if ((rg[i].written || rg[j].written) && overlap(rg[i].p, rg[i].n, rg[j].p, rg[j].n))
+                return fail(KDA_ERR_ALIAS, "kda_block_decode_k: regions %d and %d overlap", i, j);
+
+    const int Mi = (int)M, hs = hidden_size, rk = rank, qk = (int)qkv;
+    // front: every projection of the hidden rows, one launch
+    const kda::GemvSeg front[] = {
+        {hidden, w->q_proj, b->qkv_proj, hs, cd, qk, hs},
+        {hidden, w->k_proj, b->qkv_proj + qkv, hs, cd, qk, hs},
+        {hidden, w->v_proj, b->qkv_proj + 2 * qkv, hs, cd, qk, hs},
+        {hidden, w->f_a, b->fa, hs, rk, rk, hs},
+        {hidden, w->g_a, b->ga, hs, rk, rk, hs},
+        {hidden, w->b_proj, b->b_raw, hs, heads, heads, hs},
+    };
+    const kda::GemvSeg mid[] = {
+        {b->fa, w->f_b, b->g_raw, rk, qkv, qk, rk},
+        {b->ga, w->g_b, b->out_gate, rk, qkv, qk, rk},
+    };
+    const kda::GemvSeg back[] = {{b->o_norm_out, w->o_proj, out, qkv, hs, hs, qk}};
+    int rc;
+    if ((rc = hip_status(kda::launch_gemv_bf16_batchm(front, 6, Mi, stream),
+                         "kda_block_decode_k: front projections launch")) ||
+        (rc = hip_status(kda::launch_gemv_bf16_batchm(mid, 2, Mi, stream),
+                         "kda_block_decode_k: low-rank projections launch")) ||
+        (rc = hip_status(kda::launch_conv_silu_l2(b->qkv_proj, cd, w->conv, conv_state,
+                                                  K > 1 ? conv_snap : nullptr, B, K, heads,
+                                                  head_dim, eps_l2, b->conv_out, cd, nullptr,
+                                                  nullptr, nullptr, stream),
+                         "kda_block_decode_k: conv_silu_l2 launch")) ||
+        (rc = hip_status(kda::launch_kda_gate(b->g_raw, qkv, b->b_raw, heads, w->a_log,
+                                              w->dt_bias, Mi, heads, head_dim, b->gate, b->beta,
+                                              stream),
+                         "kda_block_decode_k: kda_gate launch")) ||
+        (rc = hip_status(kda::launch_kda_recurrent(b->conv_out, cd, b->gate, b->beta, state,
+                                                   K > 1 ? snap : nullptr, b->core, B, K, heads,
+                                                   head_dim, scale, stream),
+                         "kda_block_decode_k: recurrent launch")) ||
+        (rc = hip_status(kda::launch_gated_rmsnorm(b->core, qkv, b->out_gate, qkv, w->o_norm, Mi,
+                                                   heads, head_dim, eps_rms, b->o_norm_out, qkv,
+                                                   stream),
+                         "kda_block_decode_k: gated_rmsnorm launch")) ||
+        (rc = hip_status(kda::launch_gemv_bf16_batchm(back, 1, Mi, stream),
+                         "kda_block_decode_k: o_proj launch")))
+        return rc;
+    return ok();
+}
+
+int kda_block_decode(const uint16_t *hidden, const kda_block_weights *w, float *const *state,
+                     uint16_t *const *conv_state, const kda_block_decode_buffers *b,
+                     uint16_t *out, int32_t B, int32_t hidden_size, int32_t heads,
+                     int32_t head_dim, int32_t rank, float scale, float eps_l2, float eps_rms,
+                     hipStream_t stream)
+{
+    return kda_block_decode_k(hidden, w, state, conv_state, nullptr, nullptr, b, out, B, 1,
+                              hidden_size, heads, head_dim, rank, scale, eps_l2, eps_rms, stream);
+}
+
 }  // extern "C"

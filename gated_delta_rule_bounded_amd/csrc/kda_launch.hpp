@@ -50,6 +50,21 @@ hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
                               float *core, int T, int heads, int head_dim, int chunk,
                               float scale, void *workspace, hipStream_t stream);
 
+// Row-order-exact bf16 products y = bf16(x w^T) for a few rows (kda_gemv.hip).
+// Each segment has its own x [M][Kd] (stride ldx), w [N][Kd] (contiguous
+// rows) and y [M][N] (stride ldy); all segments share M.  Kd % 32 == 0, rows
+// 16-byte aligned.  Each output element's accumulation order depends on
+// neither M nor the row's position.
+constexpr int kGemvMaxSegs = 6;
+struct GemvSeg {
+    const uint16_t *x;
+    const uint16_t *w;
+    uint16_t *y;
+    int64_t ldx, ldy;
+    int32_t N, Kd;
+};
+hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStream_t stream);
+
 // y[rows][n_out] (row stride ldy) = bf16(x[rows][n_in] (stride ldx) w^T), w in
 // torch Linear layout [n_out][n_in] (stride ldw), fp32 accumulation, on the
 // vendor GEMM (kda_gemm.cpp).  Returns 0, or 1 with *what naming the failure.

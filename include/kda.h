@@ -290,6 +290,85 @@ int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float 
                       int32_t heads, int32_t head_dim, int32_t rank, int32_t chunk,
                       float scale, float eps_l2, float eps_rms, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * dense_gemv_bf16_batchm — y = bf16(x w^T) for a few rows, row-order exact.
+ * "Glm5NextKdaLayer" page, decode_k: the weight-heavy projections of K rows
+ * run once over all rows (weights read once), and each row's result must be
+ * bit-identical to the same row's product computed alone, because an
+ * accepted draft token must equal what single-token decode would emit.
+ *   x  bf16 [M, Kd] (row stride ldx)
+ *   w  bf16 [N, Kd] in torch Linear layout [out, in], contiguous rows
+ *   y  bf16 [M, N] (row stride ldy): y[m][n] = bf16(sum_k x[m][k] w[n][k]),
+ *      fp32 accumulation in an order fixed by (n, k) alone — not by M, not by
+ *      the row's position among the M rows.  Rounding to nearest, ties to even.
+ * Kd % 32 == 0, ldx % 8 == 0, N >= 1; x, w, y 16-byte aligned
+ * (KDA_ERR_SHAPE).  y must not overlap x or w (KDA_ERR_ALIAS).  M == 0 is a
+ * no-op.  Meant for small M (up to a few hundred rows); each 64 rows re-read
+ * the weights.
+ * ------------------------------------------------------------------------ */
+int dense_gemv_bf16_batchm(const uint16_t *x, int64_t ldx, const uint16_t *w,
+                           int32_t M, int32_t N, int32_t Kd, uint16_t *y,
+                           int64_t ldy, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_block_decode_k — K consecutive tokens of each of B sequences through a
+ * whole KDA block ("Glm5NextKdaLayer" page, decode_k: the projections run
+ * once over all B*K rows, the recurrence walks one token at a time; result
+ * bit-identical to K serial kda_block_decode calls, snapshots[t] = the
+ * recurrent state and the conv state AFTER row t, K-1 of them or none).
+ * Per row, the stages of kda_block_prefill:
+ *
+ *   qkv_proj   = [h q_proj^T | h k_proj^T | h v_proj^T]   dense_gemv_bf16_batchm
+ *   fa = h f_a^T, ga = h g_a^T, b_raw = h b_proj^T        (same launch)
+ *   g_raw = fa f_b^T, out_gate = ga g_b^T                  dense_gemv_bf16_batchm
+ *   conv_out   = conv_silu_l2 row by row from *conv_state[b] (updated)
+ *   gate, beta = kda_gate(g_raw, b_raw, a_log, dt_bias)
+ *   core       = kda_decode_k(conv_out, gate, beta) from *state[b] (updated)
+ *   o_norm_out = gated_rmsnorm(core, out_gate, o_norm)
+ *   out        = o_norm_out o_proj^T                       dense_gemv_bf16_batchm
+ *
+ * hidden bf16 [B*K, hidden], sequence-major (row b*K + t); out bf16
+ * [B*K, hidden].  Weights as kda_block_prefill.  state: device array [B] of
+ * pointers to fp32 [heads, head_dim, head_dim]; conv_state: device array [B]
+ * of pointers to bf16 [4, 3*heads*head_dim]; snap / conv_snap: NULL or device
+ * arrays [B*(K-1)] (entry b*(K-1)+t = after row t).  Buffers (caller-owned,
+ * B*K rows each): qkv_proj, conv_out bf16 [., 3*heads*head_dim]; fa, ga bf16
+ * [., rank]; g_raw, out_gate, o_norm_out bf16 [., heads*head_dim]; b_raw bf16
+ * [., heads]; gate, core fp32 [., heads*head_dim]; beta fp32 [., heads].
+ * hidden, rank and heads*head_dim must be multiples of 32 (KDA_ERR_SHAPE);
+ * head_dim 16 or 128 (KDA_ERR_UNSUPPORTED).  Buffers, out, hidden and the
+ * weights must be pairwise disjoint where one of them is written
+ * (KDA_ERR_ALIAS); the per-sequence states are reached through the tables
+ * and must be distinct, with snapshots disjoint from them.  B == 0 or K == 0
+ * is a no-op.  Allocates nothing; seven launches on `stream`.
+ * ------------------------------------------------------------------------ */
+typedef struct kda_block_decode_buffers {
+    uint16_t *qkv_proj, *conv_out;
+    uint16_t *fa, *g_raw, *b_raw;
+    float *gate, *beta, *core;
+    uint16_t *ga, *out_gate, *o_norm_out;
+} kda_block_decode_buffers;
+
+int kda_block_decode_k(const uint16_t *hidden, const kda_block_weights *w,
+                       float *const *state, uint16_t *const *conv_state,
+                       float *const *snap, uint16_t *const *conv_snap,
+                       const kda_block_decode_buffers *buf, uint16_t *out, int32_t B,
+                       int32_t K, int32_t hidden_size, int32_t heads, int32_t head_dim,
+                       int32_t rank, float scale, float eps_l2, float eps_rms,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_block_decode — one token for each of B sequences through the whole
+ * block ("Glm5NextKdaLayer" page, decode: single-token decode carrying both
+ * states, result in out, states updated in place).  Exactly
+ * kda_block_decode_k with K = 1 (same kernels, no snapshots).
+ * ------------------------------------------------------------------------ */
+int kda_block_decode(const uint16_t *hidden, const kda_block_weights *w,
+                     float *const *state, uint16_t *const *conv_state,
+                     const kda_block_decode_buffers *buf, uint16_t *out, int32_t B,
+                     int32_t hidden_size, int32_t heads, int32_t head_dim, int32_t rank,
+                     float scale, float eps_l2, float eps_rms, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

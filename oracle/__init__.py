@@ -98,7 +98,7 @@ def linear(x, w):
 
 
 def kda_block_prefill(hidden, wts, S0, conv_state, heads, head_dim, scale,
-                      eps_l2=1e-6, eps_rms=1e-5, threads=1):
+                      eps_l2=1e-6, eps_rms=1e-5, threads=1, snapshots=False):
     """One KDA block over one sequence ("Glm5NextKdaLayer" page, prefill;
     buffers of the "Glm5NextKdaWorkspace" page; weights of the
     "Glm5NextKdaWeights" page):
@@ -117,14 +117,17 @@ def kda_block_prefill(hidden, wts, S0, conv_state, heads, head_dim, scale,
     bf16 values (their fp32 widening is exact).  ``wts`` maps the weight
     names of the weights page to arrays in [out, in] layout (conv [conv_dim,
     kc], a_log [H], dt_bias [H*D], o_norm [D]).  Returns a dict of every
-    stage buffer plus the final state and conv state."""
+    stage buffer plus the final state and conv state; with ``snapshots`` also
+    the recurrent and conv states after each row but the last ("state_snaps"
+    [T-1, H, D, D], "conv_snaps" [T-1, kc, 3*H*D])."""
     H, D = heads, head_dim
     qkv = H * D
     x = _f64(hidden)
     T = x.shape[0]
     qkv_proj = np.concatenate([linear(x, wts["q_proj"]), linear(x, wts["k_proj"]),
                                linear(x, wts["v_proj"])], axis=1)
-    conv_out, conv_st, _ = conv_silu_l2(qkv_proj, wts["conv"], conv_state, H, D, eps_l2)
+    conv_out, conv_st, conv_snaps = conv_silu_l2(qkv_proj, wts["conv"], conv_state, H, D,
+                                                 eps_l2, snapshots=snapshots)
     fa = linear(x, wts["f_a"])
     g_raw = linear(fa, wts["f_b"])
     b_raw = linear(x, wts["b_proj"])
@@ -132,14 +135,30 @@ def kda_block_prefill(hidden, wts, S0, conv_state, heads, head_dim, scale,
     qf = conv_out[:, :qkv].reshape(T, H, D)
     kf = conv_out[:, qkv:2 * qkv].reshape(T, H, D)
     vf = conv_out[:, 2 * qkv:].reshape(T, H, D)
-    core, S, _ = kda_recurrence(qf, kf, vf, gate, beta, S0, scale, threads=threads)
+    core, S, state_snaps = kda_recurrence(qf, kf, vf, gate, beta, S0, scale,
+                                          snapshots=snapshots, threads=threads)
     ga = linear(x, wts["g_a"])
     out_gate = linear(ga, wts["g_b"])
     o_norm_out = gated_rmsnorm(core, out_gate, wts["o_norm"], eps_rms)
     final_out = linear(o_norm_out, wts["o_proj"])
     return dict(qkv_proj=qkv_proj, conv_out=conv_out, fa=fa, g_raw=g_raw, b_raw=b_raw,
                 gate=gate, beta=beta, core=core, ga=ga, out_gate=out_gate,
-                o_norm_out=o_norm_out, final_out=final_out, state=S, conv_state=conv_st)
+                o_norm_out=o_norm_out, final_out=final_out, state=S, conv_state=conv_st,
+                state_snaps=state_snaps, conv_snaps=conv_snaps)
+
+
+def kda_block_decode_k(hidden, wts, S0, conv_state, heads, head_dim, scale,
+                       eps_l2=1e-6, eps_rms=1e-5):
+    """K tokens of each of B sequences through one KDA block ("Glm5NextKdaLayer"
+    page, decode_k; decode is K = 1).  The block is causal and token-serial,
+    so each sequence's K rows are exactly kda_block_prefill over those rows
+    from that sequence's carried states, with the snapshots after rows
+    0..K-2.  hidden [B, K, hidden]; S0 [B, H, D, D]; conv_state [B, kc,
+    3*H*D].  Returns a list of B result dicts of kda_block_prefill."""
+    hidden = _f64(hidden)
+    return [kda_block_prefill(hidden[b], wts, S0[b], conv_state[b], heads, head_dim, scale,
+                              eps_l2, eps_rms, snapshots=True)
+            for b in range(hidden.shape[0])]
 
 
 def conv_silu_l2(x, w, state, heads, head_dim, eps_l2=1e-6, snapshots=False):

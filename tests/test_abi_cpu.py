@@ -189,3 +189,64 @@ def test_block_validation(lib):
     assert call(out=w2.q_proj) == E_ALIAS                    # writing over a weight
     assert call(state=b2.core + 64) == E_ALIAS
     assert call(x=b2.qkv_proj) == E_ALIAS                    # a buffer over the input
+
+
+def test_gemv_validation(lib):
+    def call(x=A, ldx=256, w=B, M=4, N=48, Kd=256, y=C, ldy=48):
+        return lib.dense_gemv_bf16_batchm(x, ldx, w, M, N, Kd, y, ldy, None)
+
+    assert call(M=0) == OK                                   # no-op
+    assert call(Kd=100) == E_SHAPE                           # Kd % 32
+    assert call(N=0) == E_SHAPE
+    assert call(M=-1) == E_SHAPE
+    assert call(ldx=128) == E_SHAPE                          # ldx < Kd
+    assert call(ldy=40) == E_SHAPE                           # ldy < N
+    assert call(x=0) == E_NULL
+    assert call(y=A + 64) == E_ALIAS                         # y over x
+    assert call(y=B) == E_ALIAS                              # y over the weights
+    assert call(x=A + 2) == E_SHAPE                          # misaligned
+
+
+def _decode_bufs():
+    import gated_delta_rule_bounded_amd as kda
+    b = kda._lib.BlockDecodeBuffers()
+    for i, (n, _) in enumerate(kda._lib.BlockDecodeBuffers._fields_):
+        setattr(b, n, (i + 20) << 36)
+    return b
+
+
+def test_block_decode_validation(lib):
+    w, _ = _block_args(lib)
+    b = _decode_bufs()
+    ref = ctypes.byref
+    H, Dh, hid, rank = 2, 16, 64, 32
+
+    def call(w_=w, b_=b, Bn=3, K=4, head_dim=Dh, hidden=hid, rk=rank, state=60 << 36,
+             conv=61 << 36, snap=None, csnap=None, out=62 << 36, x=63 << 36):
+        return lib.kda_block_decode_k(x, ref(w_) if w_ is not None else None, state, conv, snap,
+                                      csnap, ref(b_) if b_ is not None else None, out, Bn, K,
+                                      hidden, H, head_dim, rk, 0.25, 1e-6, 1e-5, None)
+
+    assert call(K=0) == OK and call(Bn=0) == OK
+    assert call(head_dim=64) == E_UNSUP
+    assert call(hidden=48) == E_SHAPE                        # hidden % 32
+    assert call(rk=16) == E_SHAPE                            # rank % 32
+    assert call(K=-1) == E_SHAPE
+    assert call(w_=None) == E_NULL
+    assert call(b_=None) == E_NULL
+    assert call(state=0) == E_NULL
+    b2 = _decode_bufs()
+    b2.core = None
+    assert call(b_=b2) == E_NULL
+    b2 = _decode_bufs()
+    b2.out_gate = b2.g_raw
+    assert call(b_=b2) == E_ALIAS
+    assert call(out=w.o_proj) == E_ALIAS                     # writing over a weight
+    assert call(x=b.qkv_proj) == E_ALIAS
+    assert call(snap=60 << 36) == E_ALIAS                    # snapshot table = state table
+    assert call(csnap=61 << 36) == E_ALIAS
+    # the one-token form is the K = 1 case of the same checks
+    assert lib.kda_block_decode(63 << 36, ref(w), 60 << 36, 61 << 36, ref(b), 62 << 36, 3,
+                                hid, H, 64, rank, 0.25, 1e-6, 1e-5, None) == E_UNSUP
+    assert lib.kda_block_decode(63 << 36, ref(w), 60 << 36, 61 << 36, ref(b), 62 << 36, 0,
+                                hid, H, Dh, rank, 0.25, 1e-6, 1e-5, None) == OK

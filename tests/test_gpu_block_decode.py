@@ -1,0 +1,205 @@
+"""Block-level decode on the GPU: the row-order-exact batched-M projection
+(dense_gemv_bf16_batchm) and kda_block_decode / kda_block_decode_k against
+the oracle's block, and K-row verify against K serial single-token calls.
+
+Tolerances.  A projection's fp32-accumulated sum may round to the bf16
+neighbour of the oracle's fp64 sum, so the projection outputs and
+everything downstream of them are held to the bf16-stage bound 2e-2 (max
+relative error per tensor), as for the block prefill.  K-row verify against
+K single-token calls is bitwise: every stage buffer, the block output, the
+final recurrent and conv states and every snapshot ("Glm5NextKdaLayer" page,
+decode_k: an accepted draft token must be exactly what plain decode emits).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_bounded_amd as kda
+import workloads
+from conftest import relerr
+from kda_cases import say
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+STAGES = ("qkv_proj", "conv_out", "fa", "g_raw", "b_raw", "gate", "beta", "core", "ga",
+          "out_gate", "o_norm_out")
+
+
+# --------------------------------------------------------------------------
+# dense_gemv_bf16_batchm
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,Kd", [(1, 48, 96), (4, 4096, 4096), (7, 40, 4096), (70, 136, 256),
+                                    (16, 32, 4096)])
+def test_gemv_matches_oracle(orc, M, N, Kd):
+    r = np.random.default_rng(M * 7 + N + Kd)
+    x = workloads.to_bf16(r.standard_normal((M, Kd)))
+    w = workloads.to_bf16(r.normal(0.0, 0.02, size=(N, Kd)))
+    y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    say("gemv", M, N, Kd)
+    kda.dense_gemv_bf16_batchm(x.cuda(), w.cuda(), y, M=M, N=N, Kd=Kd)
+    torch.cuda.synchronize()
+    ref = orc.linear(x.double().numpy(), w.double().numpy())
+    got = y.float().cpu().numpy()
+    assert relerr(got, ref) < TOL
+    # fp32 accumulation of bf16 products: at most one bf16 step off per element
+    step = np.abs(ref) * 2.0 ** -7 + 1e-30
+    assert np.all(np.abs(got - ref) <= step + 1e-5 * np.max(np.abs(ref)))
+
+
+def test_gemv_rows_are_order_exact():
+    # each row's result is the same bits whether computed alone, among M rows,
+    # at another position among them, or past the first 64-row group
+    M, N, Kd = 70, 96, 4096
+    r = np.random.default_rng(99)
+    x = workloads.to_bf16(r.standard_normal((M, Kd))).cuda()
+    w = workloads.to_bf16(r.normal(0.0, 0.02, size=(N, Kd))).cuda()
+    say("gemv rows", M, N, Kd)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    kda.dense_gemv_bf16_batchm(x, w, y, M=M, N=N, Kd=Kd)
+    perm = torch.from_numpy(r.permutation(M)).cuda()
+    yp = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    kda.dense_gemv_bf16_batchm(x[perm].contiguous(), w, yp, M=M, N=N, Kd=Kd)
+    singles = []
+    for m in (0, 3, 17, 63, 64, 69):
+        y1 = torch.empty(1, N, dtype=torch.bfloat16, device="cuda")
+        kda.dense_gemv_bf16_batchm(x[m:m + 1], w, y1, M=1, N=N, Kd=Kd)
+        singles.append((m, y1))
+    y4 = torch.empty(4, N, dtype=torch.bfloat16, device="cuda")
+    kda.dense_gemv_bf16_batchm(x[30:34], w, y4, M=4, N=N, Kd=Kd)
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y[perm])
+    for m, y1 in singles:
+        assert torch.equal(y1[0], y[m]), m
+    assert torch.equal(y4, y[30:34])
+
+
+# --------------------------------------------------------------------------
+# kda_block_decode / kda_block_decode_k
+# --------------------------------------------------------------------------
+
+def _case(B, K, H, D, hidden, rank, seed, w_std=0.05):
+    x, w = workloads.block_raw(B * K, hidden, H, D, rank, 4, seed, w_std=w_std)
+    S0 = workloads.state(H, D, 0.05, seed + 1000, B=B)
+    conv0 = workloads.conv_raw(1, H, D, 4, seed + 2000, n_seq=B)["state"]
+    return x, w, S0, conv0
+
+
+def _gpu_decode_k(x, w, S0, conv0, B, K, H, D, hidden, rank, scale, snapshots=True):
+    dev = torch.device("cuda")
+    wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+    states = [torch.from_numpy(np.ascontiguousarray(S0[b])).to(dev) for b in range(B)]
+    convs = [conv0[b].to(dev).contiguous() for b in range(B)]
+    snaps = [torch.full((H, D, D), 5.0, device=dev) for _ in range(B * (K - 1))]
+    csnaps = [torch.zeros(4, 3 * H * D, dtype=torch.bfloat16, device=dev)
+              for _ in range(B * (K - 1))]
+    buf = kda.block_decode_buffers(B * K, heads=H, head_dim=D, rank=rank, device=dev)
+    out = torch.empty(B * K, hidden, dtype=torch.bfloat16, device=dev)
+    say("block decode_k", B, K, hidden, H, D, rank)
+    kda.kda_block_decode_k(x.to(dev).contiguous(), wd, kda.ptr_table(states),
+                           kda.ptr_table(convs), buf, out, B=B, K=K, hidden_size=hidden,
+                           heads=H, head_dim=D, rank=rank, scale=scale,
+                           snap=kda.ptr_table(snaps) if snapshots and K > 1 else None,
+                           conv_snap=kda.ptr_table(csnaps) if snapshots and K > 1 else None)
+    torch.cuda.synchronize()
+    res = {n: buf[n].float().cpu().numpy() for n in STAGES}
+    res["final_out"] = out.float().cpu().numpy()
+    res["state"] = np.stack([s.cpu().numpy() for s in states])
+    res["conv_state"] = np.stack([c.float().cpu().numpy() for c in convs])
+    if K > 1:
+        res["state_snaps"] = np.stack([s.cpu().numpy() for s in snaps]).reshape(B, K - 1, H, D, D)
+        res["conv_snaps"] = np.stack([c.float().cpu().numpy() for c in csnaps]).reshape(
+            B, K - 1, 4, 3 * H * D)
+    return res
+
+
+def _gpu_serial(x, w, S0, conv0, B, K, H, D, hidden, rank, scale):
+    """K kda_block_decode calls, one token of each sequence per call."""
+    dev = torch.device("cuda")
+    wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+    states = [torch.from_numpy(np.ascontiguousarray(S0[b])).to(dev) for b in range(B)]
+    convs = [conv0[b].to(dev).contiguous() for b in range(B)]
+    xs = x.view(B, K, hidden)
+    per_row, snaps, csnaps = [], [], []
+    for t in range(K):
+        buf = kda.block_decode_buffers(B, heads=H, head_dim=D, rank=rank, device=dev)
+        out = torch.empty(B, hidden, dtype=torch.bfloat16, device=dev)
+        say("block decode", B, t, hidden, H, D, rank)
+        kda.kda_block_decode(xs[:, t].contiguous().to(dev), wd, kda.ptr_table(states),
+                             kda.ptr_table(convs), buf, out, B=B, hidden_size=hidden, heads=H,
+                             head_dim=D, rank=rank, scale=scale)
+        torch.cuda.synchronize()
+        row = {n: buf[n].float().cpu().numpy() for n in STAGES}
+        row["final_out"] = out.float().cpu().numpy()
+        per_row.append(row)
+        if t < K - 1:
+            snaps.append(np.stack([s.cpu().numpy() for s in states]))
+            csnaps.append(np.stack([c.float().cpu().numpy() for c in convs]))
+    res = {n: np.stack([r[n] for r in per_row], 1).reshape((B * K,) + per_row[0][n].shape[1:])
+           for n in per_row[0]}
+    res["state"] = np.stack([s.cpu().numpy() for s in states])
+    res["conv_state"] = np.stack([c.float().cpu().numpy() for c in convs])
+    if K > 1:
+        res["state_snaps"] = np.stack(snaps, 1)
+        res["conv_snaps"] = np.stack(csnaps, 1)
+    return res
+
+
+def _check_oracle(orc, got, x, w, S0, conv0, B, K, H, D, hidden, scale):
+    wd = {n: t.double().numpy() for n, t in w.items()}
+    ref = orc.kda_block_decode_k(x.double().numpy().reshape(B, K, hidden), wd,
+                                 np.asarray(S0, np.float64), conv0.double().numpy(), H, D, scale)
+    for n in STAGES + ("final_out",):
+        g = got[n].reshape((B, K) + ref[0][n].shape[1:])
+        for b in range(B):
+            e = relerr(g[b], ref[b][n])
+            assert e < TOL, f"{n} seq {b}: relerr {e:.3e}"
+    for b in range(B):
+        assert relerr(got["state"][b], ref[b]["state"]) < TOL
+        assert relerr(got["conv_state"][b], ref[b]["conv_state"]) < TOL
+        if K > 1:
+            for t in range(K - 1):
+                assert relerr(got["state_snaps"][b, t], ref[b]["state_snaps"][t]) < TOL
+                assert relerr(got["conv_snaps"][b, t], ref[b]["conv_snaps"][t]) < TOL
+
+
+@pytest.mark.parametrize("B,K,H,D,hidden,rank", [
+    (3, 4, 2, 16, 128, 32),
+    (2, 5, 2, 128, 256, 32),
+    (4, 1, 2, 16, 64, 32),
+])
+def test_block_decode_k_small_against_oracle(orc, B, K, H, D, hidden, rank):
+    x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1101 + K)
+    scale = D ** -0.5
+    got = _gpu_decode_k(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)
+    _check_oracle(orc, got, x, w, S0, conv0, B, K, H, D, hidden, scale)
+
+
+@pytest.mark.parametrize("B,K,H,D,hidden,rank", [
+    (3, 4, 2, 16, 128, 32),
+    (2, 5, 2, 128, 256, 32),
+])
+def test_block_decode_k_bitwise_equals_serial_decodes(B, K, H, D, hidden, rank):
+    x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1201 + K)
+    scale = D ** -0.5
+    got = _gpu_decode_k(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)
+    ser = _gpu_serial(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)
+    for n in STAGES + ("final_out", "state", "conv_state", "state_snaps", "conv_snaps"):
+        np.testing.assert_array_equal(got[n], ser[n], err_msg=n)
+
+
+def test_block_decode_k_full_size(orc):
+    # the layer at full size (hidden 4096, 32 heads x 128, rank 128, weights
+    # ~ N(0, 0.02)): one sequence verifying K = 4 draft tokens, against the
+    # oracle and bitwise against four single-token decodes
+    B, K, H, D, hidden, rank = 1, 4, 32, 128, 4096, 128
+    x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1301, w_std=0.02)
+    scale = D ** -0.5
+    got = _gpu_decode_k(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)
+    _check_oracle(orc, got, x, w, S0, conv0, B, K, H, D, hidden, scale)
+    ser = _gpu_serial(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)
+    for n in STAGES + ("final_out", "state", "conv_state", "state_snaps", "conv_snaps"):
+        np.testing.assert_array_equal(got[n], ser[n], err_msg=n)
+    for n in STAGES + ("final_out",):
+        assert np.all(np.isfinite(got[n])), n

@@ -479,3 +479,36 @@ def test_block_wires_sections_norm_and_output(orc):
     norm = orc.gated_rmsnorm(core, np.zeros((T, qkv)), wd["o_norm"])
     np.testing.assert_array_equal(out["o_norm_out"], norm)
     np.testing.assert_array_equal(out["final_out"], norm)
+
+
+def test_block_decode_k_snapshots_are_prefix_states(orc):
+    # decode_k over K rows from carried states: the recurrent snapshot after
+    # row t is the final state of the block over rows 0..t alone, and the conv
+    # snapshot after row t is the window of the last 4 pre-conv rows (a copy
+    # of the carried window followed by the projected rows); K single-row
+    # decodes chained through their states give the same rows and states
+    x, wd, H, D = _tiny_block(T=5)
+    qkv = H * D
+    r = np.random.default_rng(23)
+    S0 = r.normal(0.0, 0.1, size=(2, H, D, D))
+    cs = orc.bf16(r.standard_normal((2, 4, 3 * qkv)))
+    xb = np.stack([x, x[::-1]])                        # two sequences, K = 5
+    res = orc.kda_block_decode_k(xb, wd, S0, cs, H, D, D ** -0.5)
+    for b in range(2):
+        out = res[b]
+        assert out["state_snaps"].shape == (4, H, D, D)
+        for t in range(4):
+            pre = orc.kda_block_prefill(xb[b, :t + 1], wd, S0[b], cs[b], H, D, D ** -0.5)
+            np.testing.assert_array_equal(out["state_snaps"][t], pre["state"])
+            window = np.concatenate([cs[b], out["qkv_proj"][:t + 1]])[-4:]
+            np.testing.assert_array_equal(out["conv_snaps"][t], window)
+        np.testing.assert_array_equal(out["conv_state"],
+                                      np.concatenate([cs[b], out["qkv_proj"]])[-4:])
+        S, c = S0[b], cs[b]
+        for t in range(5):
+            one = orc.kda_block_decode_k(xb[b, t][None, None], wd, S[None], c[None], H, D,
+                                         D ** -0.5)[0]
+            np.testing.assert_array_equal(one["final_out"][0], out["final_out"][t])
+            S, c = one["state"], one["conv_state"]
+        np.testing.assert_array_equal(S, out["state"])
+        np.testing.assert_array_equal(c, out["conv_state"])

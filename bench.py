@@ -350,6 +350,78 @@ def bench_block(kda, dev, reps=10):
                 projection_mfma_frac=gemm_flops / t_gemm / PEAK_BF16_MFMA)
 
 
+def bench_block_decode(kda, dev, reps=40, n_sets=4):
+    """Block-level decode at the layer's full size (hidden 4096, 32 heads x
+    128, rank-128 gates, weights ~ N(0, 0.02)): one sequence verifying K = 4
+    draft tokens in one kda_block_decode_k call (3 state and conv snapshots)
+    against one single-token kda_block_decode.  Calls rotate over n_sets
+    independent layers (weights, state, conv state) whose weights together
+    exceed the 256 MB last-level cache, as consecutive layers of a model
+    would, so the weights stream from HBM.  The projection kernel alone
+    (dense_gemv_bf16_batchm, q|k|v as one [12288, 4096] weight, 4 rows) gives
+    the weight-read roofline."""
+    hidden, rank, K = 4096, 128, 4
+    qkv = H * D
+    sets = []
+    for s in range(n_sets):
+        x, w = workloads.block_raw(K, hidden, H, D, rank, 4, workloads.SEED_INPUT + 5 + s)
+        wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+        st = torch.from_numpy(workloads.state(H, D, 0.05, workloads.SEED_STATE + 5 + s)).to(dev)
+        cs = workloads.conv_raw(1, H, D, 4, workloads.SEED_INPUT + 5 + s)["state"].to(dev)
+        wqkv = torch.cat([wd["q_proj"], wd["k_proj"], wd["v_proj"]]).contiguous()
+        sets.append(dict(x=x.to(dev).contiguous(), w=wd, st=st, tab=kda.ptr_table(st),
+                         cs=cs, ctab=kda.ptr_table(cs), wqkv=wqkv))
+    snaps = torch.empty(K - 1, H, D, D, device=dev)
+    csnaps = torch.empty(K - 1, 4, 3 * qkv, dtype=torch.bfloat16, device=dev)
+    snap_tab, csnap_tab = kda.ptr_table(snaps), kda.ptr_table(csnaps)
+    buf_k = kda.block_decode_buffers(K, heads=H, head_dim=D, rank=rank, device=dev)
+    buf_1 = kda.block_decode_buffers(1, heads=H, head_dim=D, rank=rank, device=dev)
+    out = torch.empty(K, hidden, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(K, 3 * qkv, dtype=torch.bfloat16, device=dev)
+
+    def verify(i):
+        S = sets[i % n_sets]
+        kda.kda_block_decode_k(S["x"], S["w"], S["tab"], S["ctab"], buf_k, out, B=1, K=K,
+                               hidden_size=hidden, heads=H, head_dim=D, rank=rank,
+                               scale=D ** -0.5, snap=snap_tab, conv_snap=csnap_tab)
+
+    def decode(i):
+        S = sets[i % n_sets]
+        kda.kda_block_decode(S["x"][:1], S["w"], S["tab"], S["ctab"], buf_1, out[:1], B=1,
+                             hidden_size=hidden, heads=H, head_dim=D, rank=rank,
+                             scale=D ** -0.5)
+
+    def gemv(i):
+        S = sets[i % n_sets]
+        kda.dense_gemv_bf16_batchm(S["x"], S["wqkv"], y, M=K, N=3 * qkv, Kd=hidden)
+
+    def timed(fn):
+        for i in range(2 * n_sets):
+            fn(i)
+        es = [(ev(), ev()) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(es):
+            a.record()
+            fn(i)
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in es])) * 1e-3
+
+    t_v, t_d, t_g = timed(verify), timed(decode), timed(gemv)
+    w_bytes = 2 * (3 * qkv * hidden + 2 * rank * hidden + H * hidden + 2 * qkv * rank
+                   + hidden * qkv)
+    g_bytes = 2 * (3 * qkv * hidden + K * hidden + K * 3 * qkv)
+    return dict(config=f"block decode, 1 sequence, K={K} verify rows, hidden={hidden}, "
+                       f"heads={H}, head_dim={D}, rank={rank}, bf16 weights ~N(0,0.02), "
+                       f"{n_sets} layers rotated (weights from HBM)",
+                verify_ms=t_v * 1e3, decode_ms=t_d * 1e3,
+                verify_tokens_per_s=K / t_v, decode_tokens_per_s=1.0 / t_d,
+                speedup_vs_serial=K * t_d / t_v, weight_bytes=w_bytes,
+                verify_weight_GBps=w_bytes / t_v / 1e9,
+                gemv=dict(shape=f"M={K} N={3 * qkv} Kd={hidden}", us=t_g * 1e6, bytes=g_bytes,
+                          GBps=g_bytes / t_g / 1e9, hbm_frac=g_bytes / t_g / PEAK_HBM))
+
+
 def cpu_baseline(raw, threads):
     """The fp64 oracle, as it stands, on the full prefill workload."""
     import oracle
@@ -374,6 +446,8 @@ def main():
                     help="time the prefill steps only (profiler runs)")
     ap.add_argument("--block-only", action="store_true",
                     help="time the full-block call only and print its JSON object (profiler runs)")
+    ap.add_argument("--block-decode-only", action="store_true",
+                    help="time the block decode / K-row verify only (profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (scales HBM counters)")
@@ -392,6 +466,9 @@ def main():
 
     if args.block_only:
         print(json.dumps({"block": bench_block(kda, dev)}), flush=True)
+        return
+    if args.block_decode_only:
+        print(json.dumps({"block_decode": bench_block_decode(kda, dev)}), flush=True)
         return
 
     if args.calibrate_copy:
@@ -486,6 +563,10 @@ def main():
         log("block ...")
         out["block"] = bench_block(kda, dev)
         log(f"block: {out['block']['tokens_per_s'] / 1e6:.2f} M tokens/s")
+        log("block decode ...")
+        out["block_decode"] = bench_block_decode(kda, dev)
+        log(f"block decode: verify {out['block_decode']['verify_ms'] * 1e3:.1f} us, "
+            f"decode {out['block_decode']['decode_ms'] * 1e3:.1f} us")
     if not args.no_cpu_baseline and not args.prefill_only:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(P["raw"], cpu_threads())

@@ -435,7 +435,7 @@ int dense_gemv_bf16_batchm(const uint16_t *x, int64_t ldx, const uint16_t *w, in
                     N, Kd);
     if (M == 0) return ok();
     if (!x || !w || !y) return fail(KDA_ERR_NULL, "dense_gemv_bf16_batchm: null pointer argument");
-    if (ldx < Kd || ldy < N || ldx % 8)
+    if (ldx < Kd || ldy < N || ldx % 8 || ldx > (1 << 22))
         return fail(KDA_ERR_SHAPE, "dense_gemv_bf16_batchm: ldx=%lld ldy=%lld", (long long)ldx,
                     (long long)ldy);
     if (!aligned16(x) || !aligned16(w) || !aligned16(y))
@@ -460,7 +460,8 @@ int kda_block_decode_k(const uint16_t *hidden, const kda_block_weights *w, float
         return fail(KDA_ERR_UNSUPPORTED, "kda_block_decode_k: head_dim=%d", head_dim);
     const int64_t qkv = (int64_t)heads * head_dim, cd = 3 * qkv;
     if (B < 0 || K < 0 || heads <= 0 || hidden_size <= 0 || rank <= 0 || hidden_size % 32 ||
-        rank % 32 || qkv % 32 || (int64_t)B * K > (1 << 24))
+        rank % 32 || qkv % 32 || (int64_t)B * K > (1 << 24) || hidden_size > (1 << 22) ||
+        rank > (1 << 22) || qkv > (1 << 22))
         return fail(KDA_ERR_SHAPE, "kda_block_decode_k: B=%d K=%d hidden=%d heads=%d rank=%d", B,
                     K, hidden_size, heads, rank);
     if (B == 0 || K == 0) return ok();

@@ -5,8 +5,8 @@
 // Row-order exactness.  Every output element is accumulated in the same
 // order whatever M is and wherever its row sits:
 //   * the contraction is cut into 32-deep steps; wave w of the workgroup takes
-//     steps w, w+4, w+8, ... and chains them through one bf16 16x16x32 MFMA
-//     accumulator in increasing order;
+//     the w-th quarter of them and chains them through one bf16 16x16x32 MFMA
+//     accumulator in an order set by the output column's tile alone;
 //   * the four waves' partial sums meet in LDS and are added as
 //     ((p0 + p1) + p2) + p3, then rounded to bf16 (nearest, ties to even).
 // A row enters an MFMA only as its own A-operand row, and the matrix unit
@@ -26,10 +26,8 @@
 namespace kda {
 namespace {
 
-constexpr int kColTile = 16;       // output columns per workgroup
-constexpr int kRowTiles = 4;       // 16-row tiles per workgroup (64 rows)
+constexpr int kColTile = 16;  // output columns per workgroup
 constexpr int kWaves = 4;
-constexpr int kStepsInFlight = 4;  // contraction steps loaded ahead per wave
 
 struct Seg {
     const uint16_t *x;
@@ -46,9 +44,61 @@ struct Args {
     int32_t M;
 };
 
+// Operands of SIF contraction steps (st0, st0 + 1, ...) for RT row tiles.
+// Every load is issued unconditionally, so the compiler can count the loads
+// in flight exactly and wait for one stage while the next is still coming:
+// steps past the end re-read the last step (their products are skipped).  x
+// is read through a buffer resource bounded by the rows that exist: lanes of
+// rows past M carry an offset beyond the bound, which the hardware answers
+// with zeros and no memory traffic.
+template <int RT, int SIF>
+struct Stage {
+    uint4 w[SIF];
+    uint4 x[SIF][RT];
+};
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ uint4 load_x(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <int RT, int SIF>
+__device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *wrow,
+                                           __amdgpu_buffer_rsrc_t xr,
+                                           const uint32_t (&xoff)[RT], int st0, int last)
+{
+#pragma unroll
+    for (int j = 0; j < SIF; ++j) {
+        const int st = min(st0 + j, last);
+        S.w[j] = *reinterpret_cast<const uint4 *>(wrow + 32 * st);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) S.x[j][t] = load_x(xr, xoff[t] + 64u * st);
+    }
+}
+
+template <int RT, int SIF>
+__device__ __forceinline__ void mma_stage(const Stage<RT, SIF> &S, floatx4 (&acc)[RT], int st0,
+                                          int end)
+{
+#pragma unroll
+    for (int j = 0; j < SIF; ++j) {
+        if (st0 + j >= end) break;
+        const bf16x8 b = __builtin_bit_cast(bf16x8, S.w[j]);
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+            acc[t] = mfma_bf16(__builtin_bit_cast(bf16x8, S.x[j][t]), b, acc[t]);
+    }
+}
+
+// RT 16-row tiles per workgroup (grid.y covers the rest of M); SIF steps per
+// load stage, two stages in flight.  Neither changes any element's order of
+// accumulation, only how many rows a workgroup carries and how far its loads
+// run ahead.
+template <int RT, int SIF>
 __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
 {
-    __shared__ float part[kWaves][kRowTiles][16][17];
+    __shared__ float part[kWaves][RT][16][17];
 
     // segment of this column tile (uniform scalar search over a handful)
     int s = 0;
@@ -57,60 +107,62 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
         if ((int)blockIdx.x >= a.seg[i].tile0) s = i;
     const Seg g = a.seg[s];
     const int n0 = ((int)blockIdx.x - g.tile0) * kColTile;
-    const int m0 = (int)blockIdx.y * (kRowTiles * 16);
+    const int m0 = (int)blockIdx.y * (RT * 16);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, kg = lane >> 4;
     const int nsteps = g.Kd >> 5;
-    const int ntiles = min(kRowTiles, (a.M - m0 + 15) >> 4);
 
     // this lane's weight row (columns past N read row 0 and are never stored)
     const int n = n0 + r;
     const uint16_t *wrow = g.w + (int64_t)(n < g.N ? n : 0) * g.Kd + 8 * kg;
-    // this lane's x rows, one per 16-row tile (rows past M give zero operands)
-    const uint16_t *xrow[kRowTiles];
-    bool xok[kRowTiles];
+    // this lane's x rows, one per 16-row tile: byte offsets from the first
+    // row of the workgroup, or out of range for rows past M
+    const int rows = min(a.M - m0, RT * 16);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(g.x + (int64_t)m0 * g.ldx), (short)0,
+        (int)((int64_t)rows * g.ldx * 2), 0x00020000);
+    uint32_t xoff[RT];
 #pragma unroll
-    for (int t = 0; t < kRowTiles; ++t) {
-        const int m = m0 + 16 * t + r;
-        xok[t] = m < a.M;
-        xrow[t] = g.x + (int64_t)(xok[t] ? m : 0) * g.ldx + 8 * kg;
+    for (int t = 0; t < RT; ++t) {
+        const int m = 16 * t + r;
+        xoff[t] = m < rows ? (uint32_t)(((int64_t)m * g.ldx + 8 * kg) * 2) : kOutOfRange;
     }
 
-    floatx4 acc[kRowTiles];
+    floatx4 acc[RT];
 #pragma unroll
-    for (int t = 0; t < kRowTiles; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < RT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // steps wave, wave+4, ...: operands of kStepsInFlight steps loaded at once
+    // Wave w owns the contiguous steps [beg, end) and walks them in stages of
+    // SIF steps, starting at a stage rotated by the column tile and wrapping
+    // around, so that at any moment the workgroups in flight read different
+    // parts of their weight rows rather than all the same offset.  The order
+    // depends only on the column tile and the wave, never on M.
+    const int per = (nsteps + kWaves - 1) / kWaves;
+    const int beg = min(wave * per, nsteps), end = min(beg + per, nsteps);
+    if (beg < end) {
+        const int nst = (end - beg + SIF - 1) / SIF;
+        const int rot = (n0 / kColTile) % nst;
+        auto stage = [&](int i) {  // first step of the i-th stage visited (i may run past nst)
+            int q = i + rot;
+            q -= q >= nst ? nst : 0;
+            q -= q >= nst ? nst : 0;
+            return beg + q * SIF;
+        };
+        Stage<RT, SIF> A, B;
+        load_stage(A, wrow, xr, xoff, stage(0), end - 1);
 #pragma unroll 1
-    for (int s0 = wave; s0 < nsteps; s0 += kWaves * kStepsInFlight) {
-        uint4 wb[kStepsInFlight], xb[kStepsInFlight][kRowTiles];
-#pragma unroll
-        for (int j = 0; j < kStepsInFlight; ++j) {
-            const int st = s0 + kWaves * j;
-            const bool ok = st < nsteps;
-            wb[j] = ok ? *reinterpret_cast<const uint4 *>(wrow + 32 * st) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int t = 0; t < kRowTiles; ++t)
-                xb[j][t] = (ok && t < ntiles && xok[t])
-                               ? *reinterpret_cast<const uint4 *>(xrow[t] + 32 * st)
-                               : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < kStepsInFlight; ++j) {
-            if (s0 + kWaves * j >= nsteps) break;
-            const bf16x8 b = __builtin_bit_cast(bf16x8, wb[j]);
-#pragma unroll
-            for (int t = 0; t < kRowTiles; ++t) {
-                if (t >= ntiles) break;
-                acc[t] = mfma_bf16(__builtin_bit_cast(bf16x8, xb[j][t]), b, acc[t]);
-            }
+        for (int i = 0; i < nst; i += 2) {
+            load_stage(B, wrow, xr, xoff, stage(i + 1), end - 1);
+            mma_stage(A, acc, stage(i), end);
+            load_stage(A, wrow, xr, xoff, stage(i + 2), end - 1);
+            if (i + 1 < nst) mma_stage(B, acc, stage(i + 1), end);
         }
     }
 
     // lane holds rows 4*kg + i of each tile at column r
 #pragma unroll
-    for (int t = 0; t < kRowTiles; ++t)
+    for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) part[wave][t][4 * kg + i][r] = acc[t][i];
     __syncthreads();
@@ -119,9 +171,9 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
     const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
     if (n0 + tc < g.N) {
 #pragma unroll
-        for (int t = 0; t < kRowTiles; ++t) {
+        for (int t = 0; t < RT; ++t) {
             const int m = m0 + 16 * t + tr;
-            if (t < ntiles && m < a.M) {
+            if (m < a.M) {
                 const float v = ((part[0][t][tr][tc] + part[1][t][tr][tc]) + part[2][t][tr][tc]) +
                                 part[3][t][tr][tc];
                 g.y[(int64_t)m * g.ldy + n0 + tc] = (uint16_t)f32_to_bf16(v);
@@ -144,8 +196,13 @@ hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStre
     }
     a.nseg = nseg;
     a.M = M;
-    const dim3 grid(tiles, (M + kRowTiles * 16 - 1) / (kRowTiles * 16));
-    hipLaunchKernelGGL(gemv_bf16_batchm, grid, dim3(256), 0, stream, a);
+    // up to 16 rows: one row tile, deeper loads; more rows: four row tiles
+    if (M <= 16) {
+        hipLaunchKernelGGL((gemv_bf16_batchm<1, 6>), dim3(tiles, 1), dim3(256), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((gemv_bf16_batchm<4, 2>), dim3(tiles, (M + 63) / 64), dim3(256), 0,
+                           stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -301,7 +301,7 @@ int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float 
  *   y  bf16 [M, N] (row stride ldy): y[m][n] = bf16(sum_k x[m][k] w[n][k]),
  *      fp32 accumulation in an order fixed by (n, k) alone — not by M, not by
  *      the row's position among the M rows.  Rounding to nearest, ties to even.
- * Kd % 32 == 0, ldx % 8 == 0, N >= 1; x, w, y 16-byte aligned
+ * Kd % 32 == 0, ldx % 8 == 0, ldx <= 2^22, N >= 1; x, w, y 16-byte aligned
  * (KDA_ERR_SHAPE).  y must not overlap x or w (KDA_ERR_ALIAS).  M == 0 is a
  * no-op.  Meant for small M (up to a few hundred rows); each 64 rows re-read
  * the weights.
@@ -335,7 +335,8 @@ int dense_gemv_bf16_batchm(const uint16_t *x, int64_t ldx, const uint16_t *w,
  * B*K rows each): qkv_proj, conv_out bf16 [., 3*heads*head_dim]; fa, ga bf16
  * [., rank]; g_raw, out_gate, o_norm_out bf16 [., heads*head_dim]; b_raw bf16
  * [., heads]; gate, core fp32 [., heads*head_dim]; beta fp32 [., heads].
- * hidden, rank and heads*head_dim must be multiples of 32 (KDA_ERR_SHAPE);
+ * hidden, rank and heads*head_dim must be multiples of 32 and at most 2^22
+ * (KDA_ERR_SHAPE);
  * head_dim 16 or 128 (KDA_ERR_UNSUPPORTED).  Buffers, out, hidden and the
  * weights must be pairwise disjoint where one of them is written
  * (KDA_ERR_ALIAS); the per-sequence states are reached through the tables

@@ -205,6 +205,7 @@ def test_gemv_validation(lib):
     assert call(y=A + 64) == E_ALIAS                         # y over x
     assert call(y=B) == E_ALIAS                              # y over the weights
     assert call(x=A + 2) == E_SHAPE                          # misaligned
+    assert call(ldx=(1 << 22) + 8) == E_SHAPE                # beyond the 32-bit x offsets
 
 
 def _decode_bufs():

@@ -22,7 +22,7 @@ __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_prepare",
            "kda_prefill_forward", "kda_decode", "kda_decode_k",
            "gated_rmsnorm", "kda_prefill_workspace_bytes", "kda_prefill_segment_chunks",
            "kda_block_prefill", "block_buffers", "BLOCK_WEIGHT_NAMES",
-           "dense_gemv_bf16_batchm", "kda_block_decode", "kda_block_decode_k",
+           "dense_gemv_bf16_batchm", "kda_prefill_varlen", "varlen_chunks", "kda_block_decode", "kda_block_decode_k",
            "block_decode_buffers",
            "ptr_table", "KdaError",
            "last_error", "library_path"]
@@ -292,4 +292,24 @@ def kda_block_decode(hidden, weights, state, conv_state, buffers, out, *, B, hid
         _ptr(hidden, bf, "hidden"), ctypes.byref(wts), _ptr(state, torch.int64, "state"),
         _ptr(conv_state, torch.int64, "conv_state"), ctypes.byref(bufs), _ptr(out, bf, "out"),
         B, hidden_size, heads, head_dim, rank, float(scale), float(eps_l2), float(eps_rms),
+        _stream()))
+
+
+def varlen_chunks(lengths, chunk):
+    """(max_chunks, total_chunks) of kda_prefill_varlen for host-known lengths."""
+    n = [-(-int(t) // chunk) for t in lengths]
+    return (max(n) if n else 0), sum(n)
+
+
+def kda_prefill_varlen(q, k, v, gate, beta, state, core, cu_seqlens, workspace, *, B, rows,
+                       max_chunks, total_chunks, heads, head_dim, chunk, scale):
+    """B sequences back to back (rows [cu_seqlens[s], cu_seqlens[s+1])), one
+    state pointer each (``state``: a :func:`ptr_table`); ``cu_seqlens`` a
+    device int32 tensor of B+1 row offsets."""
+    f = torch.float32
+    _check(_lib.lib.kda_prefill_varlen(
+        _ptr(q, f, "q"), _ptr(k, f, "k"), _ptr(v, f, "v"), _ptr(gate, f, "gate"),
+        _ptr(beta, f, "beta"), _ptr(state, torch.int64, "state"), _ptr(core, f, "core"),
+        _ptr(cu_seqlens, torch.int32, "cu_seqlens"), B, rows, max_chunks, total_chunks, heads,
+        head_dim, chunk, float(scale), _ptr(workspace, None, "workspace"), workspace.numel(),
         _stream()))

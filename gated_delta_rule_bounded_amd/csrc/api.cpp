@@ -220,6 +220,41 @@ int kda_prefill_forward(float *state, float *core, int32_t T, int32_t T_pad, int
                       "kda_prefill_forward launch");
 }
 
+int kda_prefill_varlen(const float *q, const float *k, const float *v, const float *gate,
+                       const float *beta, float *const *state, float *core,
+                       const int32_t *cu_seqlens, int32_t B, int32_t rows, int32_t max_chunks,
+                       int32_t total_chunks, int32_t heads, int32_t head_dim, int32_t chunk,
+                       float scale, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!head_dim_ok(head_dim) || !(chunk == 16 || chunk == 64))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill_varlen: head_dim=%d chunk=%d", head_dim,
+                    chunk);
+    if (B < 0 || rows < 0 || max_chunks < 0 || total_chunks < 0 || heads <= 0 ||
+        max_chunks > 65535 || B > 65535)
+        return fail(KDA_ERR_SHAPE, "kda_prefill_varlen: B=%d rows=%d max_chunks=%d total_chunks=%d",
+                    B, rows, max_chunks, total_chunks);
+    if (B == 0 || rows == 0 || total_chunks == 0 || max_chunks == 0) return ok();
+    if (!q || !k || !v || !gate || !beta || !state || !core || !cu_seqlens || !workspace)
+        return fail(KDA_ERR_NULL, "kda_prefill_varlen: null pointer argument");
+    const size_t need = kda::prefill_workspace_bytes(total_chunks * chunk, heads, head_dim, chunk);
+    if ((int64_t)total_chunks * chunk > (int64_t)1 << 30 || workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "kda_prefill_varlen: workspace %zu bytes < %zu needed",
+                    workspace_bytes, need);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(core) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(KDA_ERR_SHAPE, "kda_prefill_varlen: misaligned pointer");
+    const size_t rows_b = (size_t)rows * heads * head_dim * 4;
+    if (overlap(core, rows_b, q, rows_b) || overlap(core, rows_b, k, rows_b) ||
+        overlap(core, rows_b, v, rows_b) || overlap(core, rows_b, gate, rows_b) ||
+        overlap(core, rows_b, beta, (size_t)rows * heads * 4) ||
+        overlap(workspace, need, core, rows_b))
+        return fail(KDA_ERR_ALIAS, "kda_prefill_varlen: core or workspace overlaps an input");
+    return hip_status(kda::launch_kda_prefill_varlen(q, k, v, gate, beta, state, core, cu_seqlens,
+                                                     B, rows, max_chunks, total_chunks, heads,
+                                                     head_dim, chunk, scale, workspace, stream),
+                      "kda_prefill_varlen launch");
+}
+
 static int check_decode(const char *who, const uint16_t *qkv, int64_t ldqkv, const float *gate,
                         const float *beta, float *const *state, float *core, int32_t rows,
                         int32_t heads, int32_t head_dim)

@@ -50,6 +50,17 @@ hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
                               float *core, int T, int heads, int head_dim, int chunk,
                               float scale, void *workspace, hipStream_t stream);
 
+// Several sequences back to back (rows [cu[s], cu[s+1]) of sequence s), one
+// state pointer each; one prepare and one walk for all of them.  total_chunks
+// = sum over sequences of ceil(len / chunk) operand blocks in the workspace;
+// max_chunks = the longest sequence's chunk count.  Sequences that would not
+// fit either are left untouched.
+hipError_t launch_kda_prefill_varlen(const float *q, const float *k, const float *v,
+                                     const float *gate, const float *beta, float *const *state,
+                                     float *core, const int32_t *cu_seqlens, int B, int64_t rows,
+                                     int max_chunks, int total_chunks, int heads, int head_dim,
+                                     int chunk, float scale, void *workspace, hipStream_t stream);
+
 // Row-order-exact bf16 products y = bf16(x w^T) for a few rows (kda_gemv.hip).
 // Each segment has its own x [M][Kd] (stride ldx), w [N][Kd] (contiguous
 // rows) and y [M][N] (stride ldy); all segments share M.  Kd % 32 == 0, rows

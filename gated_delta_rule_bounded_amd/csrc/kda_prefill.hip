@@ -51,6 +51,62 @@ constexpr int kPadC = 4;            // ... of [C][C] tiles
 constexpr int kPad16 = 4;           // ... of [rows][16] tiles
 constexpr float kSpanLimit = 86.0f; // log2 units: largest diagonal-block decay span factored
 
+// ---------------------------------------------------------------------------
+// Several sequences in one launch ("Glm5NextLayer" page, batched and varlen
+// linear-attention prefill: one state pointer per sequence, the sequences'
+// tokens back to back, row offsets cu_seqlens).  Sequence s owns rows
+// [cu[s], cu[s+1]) of the row arrays and the dense run of operand blocks that
+// follows the blocks of sequences 0..s-1.  A workgroup maps itself onto its
+// sequence and then runs exactly the single-sequence code: the rows of the
+// next sequence past the end of its last chunk are pad rows to it, replaced
+// at load time like any pad tail.  cu == nullptr: one sequence, the plain
+// arguments apply.
+// ---------------------------------------------------------------------------
+struct Varlen {
+    const int32_t *cu;      // [B + 1] row offsets, or nullptr
+    float *const *states;   // [B] state pointers (forward)
+    int64_t rows;           // rows held by the row arrays
+    int32_t max_chunks;     // chunks of the longest sequence (prepare grid)
+    int32_t total_chunks;   // operand blocks in the workspace
+};
+
+struct SeqSpan {
+    int64_t row0, chunk0;
+    int T, nch;
+    bool ok;   // inside the workspace and the prepare grid
+};
+
+// Rows of sequence i, clamped to [0, rows): the same clamp for every i, so
+// chunk offsets and chunk counts agree between all workgroups.
+__device__ __forceinline__ void seq_rows(const Varlen &vl, int i, int64_t &lo, int64_t &hi)
+{
+    lo = min(max((int64_t)vl.cu[i], (int64_t)0), vl.rows);
+    hi = min(max((int64_t)vl.cu[i + 1], lo), vl.rows);
+}
+
+template <int C>
+__device__ __forceinline__ SeqSpan seq_span(const Varlen &vl, int s)
+{
+    SeqSpan r;
+    int64_t hi;
+    seq_rows(vl, s, r.row0, hi);
+    r.T = (int)(hi - r.row0);
+    r.nch = (r.T + C - 1) / C;
+    // chunk offset: chunks of sequences 0..s-1, summed across the wave
+    const int lane = threadIdx.x & 63;
+    int64_t acc = 0;
+    for (int i = lane; i < s; i += kWave) {
+        int64_t lo_i, hi_i;
+        seq_rows(vl, i, lo_i, hi_i);
+        acc += (hi_i - lo_i + C - 1) / C;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    r.chunk0 = acc;
+    r.ok = r.nch <= vl.max_chunks && r.chunk0 + r.nch <= vl.total_chunks;
+    return r;
+}
+
 template <int D, int C>
 struct PrefCfg {
     static constexpr int kNW = C / 16;   // waves per workgroup: wave w owns chunk rows 16w..16w+15
@@ -304,19 +360,29 @@ template <int D, int C>
 __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
-    float *__restrict__ ws)
+    float *__restrict__ ws, const Varlen vl)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
     using B = Blk<D, C>;
     const int n = blockIdx.x, h = blockIdx.y;
+    int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
+    if (vl.cu) {
+        const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
+        if (!sp.ok || n >= sp.nch) return;   // uniform over the workgroup
+        const int64_t r0 = sp.row0 * H;
+        q += r0 * D, k += r0 * D, v += r0 * D, gate += r0 * D, beta += r0;
+        T = sp.T;
+        nblk = sp.chunk0 + n;
+        tmax = vl.rows - 1 - sp.row0;
+    }
     // wave index, uniform across the wave (scalar register)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
     const int rl = 16 * w + lr;
-    const int64_t tg = (int64_t)n * C + rl;
-    const bool valid = tg < T;
+    const int64_t tg = min((int64_t)n * C + rl, tmax);   // rows past T are replaced
+    const bool valid = (int64_t)n * C + rl < T;
     const int64_t roff = (tg * H + h) * D;
-    float *__restrict__ blk = ws + ((int64_t)n * H + h) * B::kSize;
+    float *__restrict__ blk = ws + (nblk * H + h) * B::kSize;
 
     __shared__ __align__(16) float s_tot[NW * D];
     __shared__ __align__(16) float s_kc[C][D + kPadK];   // Kc, then Kg, then V
@@ -561,20 +627,30 @@ template <int D, int C>
 __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep_split_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
-    float *__restrict__ ws)
+    float *__restrict__ ws, const Varlen vl)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
     constexpr int KD = DT / 2, KC = NW / 2;   // 32-deep blocks over D and over C
     using B = Blk<D, C>;
     static_assert(B::kSplit, "split operand blocks need D, C multiples of 32");
     const int n = blockIdx.x, h = blockIdx.y;
+    int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
+    if (vl.cu) {
+        const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
+        if (!sp.ok || n >= sp.nch) return;   // uniform over the workgroup
+        const int64_t r0 = sp.row0 * H;
+        q += r0 * D, k += r0 * D, v += r0 * D, gate += r0 * D, beta += r0;
+        T = sp.T;
+        nblk = sp.chunk0 + n;
+        tmax = vl.rows - 1 - sp.row0;
+    }
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
     const int rl = 16 * w + lr;
-    const int64_t tg = (int64_t)n * C + rl;
-    const bool valid = tg < T;
+    const int64_t tg = min((int64_t)n * C + rl, tmax);   // rows past T are replaced
+    const bool valid = (int64_t)n * C + rl < T;
     const int64_t roff = (tg * H + h) * D;
-    float *__restrict__ blk = ws + ((int64_t)n * H + h) * B::kSize;
+    float *__restrict__ blk = ws + (nblk * H + h) * B::kSize;
 
     __shared__ __align__(16) float s_tot[NW * D];
     __shared__ __align__(16) float s_beta[C];
@@ -905,7 +981,7 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
 template <int D, int C>
 __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
     const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
-    int NC, int H, float scale)
+    int NC, int H, float scale, const Varlen vl)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
     constexpr int OWN = (DT + NW - 1) / NW;   // channel tiles per wave in the state update
@@ -913,6 +989,15 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
     // all value slices of one head share an XCD (workgroups are dealt to the
     // 8 XCDs round-robin), so they share that XCD's L2 copy of the operands
     const int h = blockIdx.x % H, jt = blockIdx.x / H, j0 = 16 * jt;
+    if (vl.cu) {   // sequence blockIdx.y: its state, rows and operand blocks
+        const SeqSpan sp = seq_span<C>(vl, blockIdx.y);
+        if (!sp.ok || sp.nch == 0) return;   // uniform over the workgroup
+        state = vl.states[blockIdx.y];
+        core += sp.row0 * H * D;
+        ws += sp.chunk0 * H * B::kSize;
+        T = sp.T;
+        NC = sp.nch;
+    }
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
 
@@ -1124,7 +1209,7 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
 template <int D, int C>
 __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_fwd_split_kernel(
     const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
-    int NC, int H, float scale)
+    int NC, int H, float scale, const Varlen vl)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
     constexpr int KD = DT / 2, KC = NW / 2;   // 32-deep blocks over D and over C
@@ -1132,6 +1217,15 @@ __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu
     using B = Blk<D, C>;
     static_assert(B::kSplit, "split operand blocks need D, C multiples of 32");
     const int h = blockIdx.x % H, jt = blockIdx.x / H, j0 = 16 * jt;
+    if (vl.cu) {   // sequence blockIdx.y: its state, rows and operand blocks
+        const SeqSpan sp = seq_span<C>(vl, blockIdx.y);
+        if (!sp.ok || sp.nch == 0) return;   // uniform over the workgroup
+        state = vl.states[blockIdx.y];
+        core += sp.row0 * H * D;
+        ws += sp.chunk0 * H * B::kSize;
+        T = sp.T;
+        NC = sp.nch;
+    }
     const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool chain = r < NW;            // waves 0..NW-1 carry the state
     const int w = chain ? r : r - NW;     // 16-row block of the chunk (and state tiles w + NW o)
@@ -1359,33 +1453,35 @@ int prefill_segment_chunks(int T, int heads, int head_dim, int chunk)
 
 template <int D, int C>
 static hipError_t prepare_t(const float *q, const float *k, const float *v, const float *gate,
-                            const float *beta, int T, int H, void *workspace, hipStream_t stream)
+                            const float *beta, int T, int H, void *workspace, const Varlen &vl,
+                            int B, hipStream_t stream)
 {
-    const int NC = (T + C - 1) / C;
+    const dim3 grid = vl.cu ? dim3(vl.max_chunks, H, B) : dim3((T + C - 1) / C, H);
     if constexpr (Blk<D, C>::kSplit)
-        hipLaunchKernelGGL((kda_chunk_prep_split_kernel<D, C>), dim3(NC, H),
+        hipLaunchKernelGGL((kda_chunk_prep_split_kernel<D, C>), grid,
                            dim3(PrefCfg<D, C>::kThreads), 0, stream, q, k, v, gate, beta, T, H,
-                           static_cast<float *>(workspace));
+                           static_cast<float *>(workspace), vl);
     else
-        hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C>), dim3(NC, H),
+        hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C>), grid,
                            dim3(PrefCfg<D, C>::kThreads), 0, stream, q, k, v, gate, beta, T, H,
-                           static_cast<float *>(workspace));
+                           static_cast<float *>(workspace), vl);
     return hipGetLastError();
 }
 
 template <int D, int C>
 static hipError_t forward_t(float *state, float *core, int T, int H, float scale,
-                            const void *workspace, hipStream_t stream)
+                            const void *workspace, const Varlen &vl, int B, hipStream_t stream)
 {
     const int NC = (T + C - 1) / C;
+    const dim3 grid(H * PrefCfg<D, C>::kDT, vl.cu ? B : 1);
     if constexpr (Blk<D, C>::kSplit)
-        hipLaunchKernelGGL((kda_chunk_fwd_split_kernel<D, C>), dim3(H * PrefCfg<D, C>::kDT),
+        hipLaunchKernelGGL((kda_chunk_fwd_split_kernel<D, C>), grid,
                            dim3(2 * PrefCfg<D, C>::kThreads), 0, stream,
-                           static_cast<const float *>(workspace), state, core, T, NC, H, scale);
+                           static_cast<const float *>(workspace), state, core, T, NC, H, scale, vl);
     else
-        hipLaunchKernelGGL((kda_chunk_fwd_kernel<D, C>), dim3(H * PrefCfg<D, C>::kDT),
+        hipLaunchKernelGGL((kda_chunk_fwd_kernel<D, C>), grid,
                            dim3(PrefCfg<D, C>::kThreads), 0, stream,
-                           static_cast<const float *>(workspace), state, core, T, NC, H, scale);
+                           static_cast<const float *>(workspace), state, core, T, NC, H, scale, vl);
     return hipGetLastError();
 }
 
@@ -1400,14 +1496,16 @@ hipError_t launch_kda_prefill_prepare(const float *q, const float *k, const floa
                                       int head_dim, int chunk, void *workspace,
                                       hipStream_t stream)
 {
-    return KDA_PREFILL_DISPATCH(prepare_t, q, k, v, gate, beta, T, heads, workspace, stream);
+    return KDA_PREFILL_DISPATCH(prepare_t, q, k, v, gate, beta, T, heads, workspace, Varlen{},
+                                1, stream);
 }
 
 hipError_t launch_kda_prefill_forward(float *state, float *core, int T, int heads, int head_dim,
                                       int chunk, float scale, const void *workspace,
                                       hipStream_t stream)
 {
-    return KDA_PREFILL_DISPATCH(forward_t, state, core, T, heads, scale, workspace, stream);
+    return KDA_PREFILL_DISPATCH(forward_t, state, core, T, heads, scale, workspace, Varlen{}, 1,
+                                stream);
 }
 
 hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
@@ -1435,6 +1533,22 @@ hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_kda_prefill_varlen(const float *q, const float *k, const float *v,
+                                     const float *gate, const float *beta, float *const *state,
+                                     float *core, const int32_t *cu_seqlens, int B, int64_t rows,
+                                     int max_chunks, int total_chunks, int heads, int head_dim,
+                                     int chunk, float scale, void *workspace, hipStream_t stream)
+{
+    // one prepare over every chunk of every sequence, then one walk per
+    // (sequence, head, value slice)
+    const Varlen vl{cu_seqlens, state, rows, max_chunks, total_chunks};
+    hipError_t e = KDA_PREFILL_DISPATCH(prepare_t, q, k, v, gate, beta, 0, heads, workspace, vl,
+                                        B, stream);
+    if (e != hipSuccess) return e;
+    return KDA_PREFILL_DISPATCH(forward_t, nullptr, core, 0, heads, scale, workspace, vl, B,
+                                stream);
 }
 
 }  // namespace kda

@@ -168,6 +168,42 @@ int kda_prefill_forward(float *state, float *core, int32_t T, int32_t T_pad,
                         size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kda_prefill_varlen — chunked prefill of B sequences in one call, each from
+ * its own carried state.  "Glm5NextLayer" page, batched linear-attention
+ * prefill (prefill_gdn_full_batched / ..._varlen): one state pointer per
+ * sequence in a device table, the sequences' tokens back to back in the
+ * stage buffers, row offsets in a device cu_seqlens array, the longest
+ * sequence's chunk count and the total chunk count passed alongside.
+ *   q, k, v, gate fp32 [rows, heads, head_dim]; beta fp32 [rows, heads]:
+ *          sequence s owns rows [cu_seqlens[s], cu_seqlens[s+1]); rows past
+ *          the last sequence may hold anything.
+ *   state  device array [B] of pointers to fp32 [heads, head_dim, head_dim],
+ *          in/out; entries must be distinct.
+ *   core   fp32 [rows, heads, head_dim]: rows of each sequence written,
+ *          other rows untouched.
+ *   cu_seqlens  device int32 [B+1], non-decreasing, cu_seqlens[B] <= rows.
+ *   max_chunks  max over s of ceil(len_s / chunk);
+ *   total_chunks sum over s of ceil(len_s / chunk);
+ *   workspace   at least kda_prefill_workspace_bytes(total_chunks * chunk,
+ *               heads, head_dim, chunk) bytes, 256-byte aligned.
+ * Each sequence's core rows and final state are bitwise those of a
+ * kda_prefill call on that sequence alone (the chunk arithmetic is the same;
+ * a chunk's rows past its sequence's end are pad rows to it).  The lengths
+ * live in device memory, so the host checks only the sizes it is given; a
+ * sequence whose chunks would fall outside max_chunks or total_chunks is
+ * skipped (its state and core rows are left as they are), never written
+ * past the workspace.  Rows are clamped to [0, rows).  B == 0 or
+ * total_chunks == 0 is a no-op.  Errors as kda_prefill; B and max_chunks at
+ * most 65535.
+ * ------------------------------------------------------------------------ */
+int kda_prefill_varlen(const float *q, const float *k, const float *v,
+                       const float *gate, const float *beta, float *const *state,
+                       float *core, const int32_t *cu_seqlens, int32_t B,
+                       int32_t rows, int32_t max_chunks, int32_t total_chunks,
+                       int32_t heads, int32_t head_dim, int32_t chunk, float scale,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * kda_decode — one token for each of B independent sequences.
  * "Glm5NextKdaLayer" page, decode (single-token decode; q/k arrive already
  * normalised from the fused conv and must not be re-normalised; the state is

@@ -251,3 +251,26 @@ def test_block_decode_validation(lib):
                                 hid, H, 64, rank, 0.25, 1e-6, 1e-5, None) == E_UNSUP
     assert lib.kda_block_decode(63 << 36, ref(w), 60 << 36, 61 << 36, ref(b), 62 << 36, 0,
                                 hid, H, Dh, rank, 0.25, 1e-6, 1e-5, None) == OK
+
+
+def test_varlen_validation(lib):
+    H, Dh, C = 2, 16, 16
+    ws = lib.kda_prefill_workspace_bytes(10 * C, H, Dh, C)
+
+    def call(q=A, core=B, cu=C, state=Dp, wsp=E, ws_bytes=ws, Bn=3, rows=100, mx=4, tot=10,
+             head_dim=Dh, chunk=C):
+        return lib.kda_prefill_varlen(q, q + (1 << 30), q + (2 << 30), q + (3 << 30),
+                                      q + (4 << 30), state, core, cu, Bn, rows, mx, tot, H,
+                                      head_dim, chunk, 0.25, wsp, ws_bytes, None)
+
+    assert call(Bn=0) == OK and call(tot=0) == OK and call(rows=0) == OK
+    assert call(head_dim=64) == E_UNSUP
+    assert call(chunk=32) == E_UNSUP
+    assert call(Bn=-1) == E_SHAPE
+    assert call(mx=70000) == E_SHAPE
+    assert call(cu=0) == E_NULL
+    assert call(state=0) == E_NULL
+    assert call(ws_bytes=ws - 1) == E_WS
+    assert call(core=A + 64) == E_ALIAS                        # core over q
+    assert call(wsp=B + 256) == E_ALIAS                        # workspace over core
+    assert call(q=A + 4) == E_SHAPE                            # misaligned

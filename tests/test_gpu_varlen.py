@@ -1,0 +1,113 @@
+"""kda_prefill_varlen: several sequences back to back in one call, each from
+its own carried state ("Glm5NextLayer" page, batched / varlen linear-attention
+prefill), against the oracle per sequence (2e-3, max relative error) and
+bitwise against kda_prefill on each sequence alone."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_bounded_amd as kda
+from conftest import relerr
+from kda_cases import THREADS, core_case, cuda, gpu_prefill, say
+import oracle
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+SENTINEL = 7.0
+
+
+def run_varlen(cases, H, D, C, scale, tail=3, tail_fill=np.nan, total_chunks=None):
+    lengths = [c["q"].shape[0] for c in cases]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    rows = int(cu[-1]) + tail      # rows past the last sequence hold poison
+
+    def stack(name, shape):
+        out = np.full((rows,) + shape, tail_fill, np.float32)
+        for s, c in enumerate(cases):
+            out[cu[s]:cu[s + 1]] = c[name]
+        return cuda(out)
+
+    q, k, v, g = (stack(n, (H, D)) for n in ("q", "k", "v", "gate"))
+    b = stack("beta", (H,))
+    states = [cuda(c["S0"]).contiguous() for c in cases]
+    core = torch.full((rows, H, D), SENTINEL, dtype=torch.float32, device="cuda")
+    mx, tot = kda.varlen_chunks(lengths, C)
+    tot = tot if total_chunks is None else total_chunks
+    ws = torch.empty(max(1, kda.kda_prefill_workspace_bytes(max(tot, 1) * C, H, D, C)),
+                     dtype=torch.uint8, device="cuda")
+    say("varlen", lengths, H, D, C, tot)
+    kda.kda_prefill_varlen(q, k, v, g, b, kda.ptr_table(states), core,
+                           torch.from_numpy(cu).cuda(), ws, B=len(cases), rows=rows,
+                           max_chunks=mx, total_chunks=tot, heads=H, head_dim=D, chunk=C,
+                           scale=scale)
+    torch.cuda.synchronize()
+    return cu, core.cpu().numpy(), [s.cpu().numpy() for s in states]
+
+
+@pytest.mark.parametrize("lengths,H,D,C", [
+    ([57, 0, 64, 130, 1], 2, 16, 16),
+    ([57, 16, 33], 2, 16, 64),
+    ([200, 64, 0, 31, 129], 2, 128, 64),
+    ([40, 17], 2, 128, 16),
+])
+def test_varlen_matches_oracle_and_single_calls(lengths, H, D, C):
+    scale = D ** -0.5
+    cases = [core_case(T, H, D, 1400 + 7 * s + T, 0.05) for s, T in enumerate(lengths)]
+    cu, core, states = run_varlen(cases, H, D, C, scale)
+    covered = np.zeros(core.shape[0], bool)
+    for s, (c, T) in enumerate(zip(cases, lengths)):
+        rows = core[cu[s]:cu[s + 1]]
+        covered[cu[s]:cu[s + 1]] = True
+        if T == 0:
+            np.testing.assert_array_equal(states[s], c["S0"])
+            continue
+        ref_core, ref_S, _ = oracle.kda_recurrence(c["q"], c["k"], c["v"], c["gate"], c["beta"],
+                                                   c["S0"], scale)
+        assert relerr(rows, ref_core) < TOL, f"seq {s} core"
+        assert relerr(states[s], ref_S) < TOL, f"seq {s} state"
+        T_pad = -(-T // C) * C
+        one_core, one_S = gpu_prefill(c, T, T_pad, C, scale, fill=0.0)
+        np.testing.assert_array_equal(rows, one_core[:T], err_msg=f"seq {s} core bitwise")
+        np.testing.assert_array_equal(states[s], one_S, err_msg=f"seq {s} state bitwise")
+    assert np.all(core[~covered] == SENTINEL)
+
+
+def test_varlen_full_size_many_prompts():
+    # the prefill workload's 4096 tokens as 8 prompts of mixed length at the
+    # full head shape (32 heads x 128, chunk 64), each from its own state
+    H, D, C = 32, 128, 64
+    lengths = [512, 1000, 64, 7, 777, 1024, 300, 412]
+    assert sum(lengths) == 4096
+    scale = D ** -0.5
+    cases = [core_case(T, H, D, 1500 + s, 0.05, qkv_bf16=True) for s, T in enumerate(lengths)]
+    cu, core, states = run_varlen(cases, H, D, C, scale)
+    for s, (c, T) in enumerate(zip(cases, lengths)):
+        rows = core[cu[s]:cu[s + 1]]
+        T_pad = -(-T // C) * C
+        one_core, one_S = gpu_prefill(c, T, T_pad, C, scale, fill=0.0)
+        np.testing.assert_array_equal(rows, one_core[:T], err_msg=f"seq {s} core bitwise")
+        np.testing.assert_array_equal(states[s], one_S, err_msg=f"seq {s} state bitwise")
+        if s in (1, 3, 6):
+            ref_core, ref_S, _ = oracle.kda_recurrence(c["q"], c["k"], c["v"], c["gate"],
+                                                       c["beta"], c["S0"], scale, threads=THREADS)
+            assert relerr(rows, ref_core) < TOL, f"seq {s} core"
+            assert relerr(states[s], ref_S) < TOL, f"seq {s} state"
+    assert np.all(core[cu[-1]:] == SENTINEL)
+
+
+def test_varlen_sequence_outside_the_workspace_is_left_alone():
+    # total_chunks one short: the last sequence's blocks would not fit, so it
+    # is skipped whole (state and core rows untouched); the others are exact
+    H, D, C = 2, 128, 64
+    lengths = [100, 64, 70]
+    scale = D ** -0.5
+    cases = [core_case(T, H, D, 1600 + s, 0.05) for s, T in enumerate(lengths)]
+    _, tot = kda.varlen_chunks(lengths, C)
+    cu, core, states = run_varlen(cases, H, D, C, scale, total_chunks=tot - 1)
+    np.testing.assert_array_equal(states[2], cases[2]["S0"])
+    assert np.all(core[cu[2]:cu[3]] == SENTINEL)
+    for s in (0, 1):
+        T = lengths[s]
+        one_core, one_S = gpu_prefill(cases[s], T, -(-T // C) * C, C, scale)
+        np.testing.assert_array_equal(core[cu[s]:cu[s + 1]], one_core[:T])
+        np.testing.assert_array_equal(states[s], one_S)

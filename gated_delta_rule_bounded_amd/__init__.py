@@ -22,7 +22,8 @@ __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_prepare",
            "kda_prefill_forward", "kda_decode", "kda_decode_k",
            "gated_rmsnorm", "kda_prefill_workspace_bytes", "kda_prefill_segment_chunks",
            "kda_block_prefill", "block_buffers", "BLOCK_WEIGHT_NAMES",
-           "dense_gemv_bf16_batchm", "kda_prefill_varlen", "varlen_chunks", "kda_block_decode", "kda_block_decode_k",
+           "dense_gemv_bf16_batchm", "kda_prefill_varlen", "varlen_chunks",
+           "kda_verify_k", "kda_fold_accepted", "kda_block_decode", "kda_block_decode_k",
            "block_decode_buffers",
            "ptr_table", "KdaError",
            "last_error", "library_path"]
@@ -313,3 +314,23 @@ def kda_prefill_varlen(q, k, v, gate, beta, state, core, cu_seqlens, workspace, 
         _ptr(cu_seqlens, torch.int32, "cu_seqlens"), B, rows, max_chunks, total_chunks, heads,
         head_dim, chunk, float(scale), _ptr(workspace, None, "workspace"), workspace.numel(),
         _stream()))
+
+
+def kda_verify_k(qkv, gate, beta, state, core, *, B, K, heads, head_dim, scale):
+    """Outputs of K rows per sequence (bitwise those of kda_decode_k); the
+    states are left as they are."""
+    f = torch.float32
+    _check(_lib.lib.kda_verify_k(
+        _ptr(qkv, torch.bfloat16, "qkv"), _rowstride(qkv, "qkv"), _ptr(gate, f, "gate"),
+        _ptr(beta, f, "beta"), _ptr(state, torch.int64, "state"), _ptr(core, f, "core"), B, K,
+        heads, head_dim, float(scale), _stream()))
+
+
+def kda_fold_accepted(qkv, gate, beta, state, n_accept, *, B, K, heads, head_dim):
+    """Fold the first n_accept[b] verified rows into each state (``n_accept``
+    a device int32 tensor of B counts)."""
+    f = torch.float32
+    _check(_lib.lib.kda_fold_accepted(
+        _ptr(qkv, torch.bfloat16, "qkv"), _rowstride(qkv, "qkv"), _ptr(gate, f, "gate"),
+        _ptr(beta, f, "beta"), _ptr(state, torch.int64, "state"),
+        _ptr(n_accept, torch.int32, "n_accept"), B, K, heads, head_dim, _stream()))

@@ -310,6 +310,46 @@ int kda_decode_k(const uint16_t *qkv, int64_t ldqkv, const float *gate, const fl
                       "kda_decode_k launch");
 }
 
+int kda_verify_k(const uint16_t *qkv, int64_t ldqkv, const float *gate, const float *beta,
+                 float *const *state, float *core, int32_t B, int32_t K, int32_t heads,
+                 int32_t head_dim, float scale, hipStream_t stream)
+{
+    if (B < 0 || K < 0 || heads <= 0)
+        return fail(KDA_ERR_SHAPE, "kda_verify_k: B=%d K=%d heads=%d", B, K, heads);
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_verify_k: head_dim=%d", head_dim);
+    if (B == 0 || K == 0) return ok();
+    if ((int64_t)B * K > (int64_t)1 << 30)
+        return fail(KDA_ERR_SHAPE, "kda_verify_k: B*K too large");
+    if (int rc = check_decode("kda_verify_k", qkv, ldqkv, gate, beta, state, core, B * K, heads,
+                              head_dim))
+        return rc;
+    return hip_status(kda::launch_kda_verify(qkv, ldqkv, gate, beta, state, core, B, K, heads,
+                                             head_dim, scale, stream),
+                      "kda_verify_k launch");
+}
+
+int kda_fold_accepted(const uint16_t *qkv, int64_t ldqkv, const float *gate, const float *beta,
+                      float *const *state, const int32_t *n_accept, int32_t B, int32_t K,
+                      int32_t heads, int32_t head_dim, hipStream_t stream)
+{
+    if (B < 0 || K < 0 || heads <= 0)
+        return fail(KDA_ERR_SHAPE, "kda_fold_accepted: B=%d K=%d heads=%d", B, K, heads);
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_fold_accepted: head_dim=%d", head_dim);
+    if (B == 0 || K == 0) return ok();
+    if ((int64_t)B * K > (int64_t)1 << 30)
+        return fail(KDA_ERR_SHAPE, "kda_fold_accepted: B*K too large");
+    if (!qkv || !gate || !beta || !state || !n_accept)
+        return fail(KDA_ERR_NULL, "kda_fold_accepted: null pointer argument");
+    if (ldqkv < 3LL * heads * head_dim)
+        return fail(KDA_ERR_SHAPE, "kda_fold_accepted: ldqkv=%lld < 3*heads*head_dim",
+                    (long long)ldqkv);
+    return hip_status(kda::launch_kda_fold(qkv, ldqkv, gate, beta, state, n_accept, B, K, heads,
+                                           head_dim, stream),
+                      "kda_fold_accepted launch");
+}
+
 int gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate, int64_t ldo,
                   const uint16_t *w, int32_t T, int32_t heads, int32_t head_dim, float eps,
                   uint16_t *out, int64_t ldy, hipStream_t stream)

@@ -18,6 +18,13 @@
 // result bit-identical to K single-token calls: each step runs the same
 // instructions on the same values, and fp32 registers hold exactly what an
 // fp32 store and reload would.
+//
+// Write-on-accept ("Glm5NextLayer" page, LayerWriteOnAccept: verify, then
+// fold the accepted rows into the state) is two more runs of the same code:
+// a verify run writes the K rows' outputs and leaves the state untouched
+// (write_state false), and a fold run applies the first n_accept[b] rows to
+// the state and writes no output.  The state a fold leaves is therefore
+// bitwise the snapshot a K-row decode would have written after that row.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -53,7 +60,8 @@ template <int D>
 __global__ __launch_bounds__(RecCfg<D>::kThreads) void kda_recurrent_kernel(
     const uint16_t *__restrict__ qkv, int64_t ldqkv, const float *__restrict__ gate,
     const float *__restrict__ beta, float *const *__restrict__ state,
-    float *const *__restrict__ snap, float *__restrict__ core, int K, int H, float scale)
+    float *const *__restrict__ snap, float *__restrict__ core, int K, int H, float scale,
+    bool write_state, const int32_t *__restrict__ n_accept)
 {
     using Cfg = RecCfg<D>;
     constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT, NWAVE = Cfg::kWaves;
@@ -71,13 +79,17 @@ __global__ __launch_bounds__(RecCfg<D>::kThreads) void kda_recurrent_kernel(
     __shared__ float4 s_red[NWAVE > 1 ? NWAVE : 1][2][CG];
     __shared__ float s_kq[NWAVE > 1 ? NWAVE : 1];
 
+    // rows walked: all K, or the accepted ones when folding (none: nothing to do)
+    const int rows = n_accept ? min(max(n_accept[b], 0), K) : K;
+    if (rows == 0) return;   // uniform over the workgroup
+
     float *__restrict__ Sg = state[b] + (size_t)h * D * D;
     float4 S[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
         S[r] = load_stream(Sg + (size_t)(rg + RG * r) * D + 4 * cg);
 
-    for (int t = 0; t < K; ++t) {
+    for (int t = 0; t < rows; ++t) {
         const size_t row = (size_t)b * K + t;
         const uint16_t *__restrict__ qrow = qkv + row * ldqkv + (size_t)h * D;
         for (int i = tid; i < D; i += Cfg::kThreads) {
@@ -132,7 +144,7 @@ __global__ __launch_bounds__(RecCfg<D>::kThreads) void kda_recurrent_kernel(
         const float4 v4 = reinterpret_cast<const float4 *>(s_v)[cg];
         const float4 u = make_float4(bt * (v4.x - pk.x), bt * (v4.y - pk.y),
                                      bt * (v4.z - pk.z), bt * (v4.w - pk.w));
-        if (rg == 0) {
+        if (core != nullptr && rg == 0) {
             const float4 o = make_float4(scale * __builtin_fmaf(u.x, kq, pq.x),
                                          scale * __builtin_fmaf(u.y, kq, pq.y),
                                          scale * __builtin_fmaf(u.z, kq, pq.z),
@@ -152,9 +164,23 @@ __global__ __launch_bounds__(RecCfg<D>::kThreads) void kda_recurrent_kernel(
         __syncthreads();  // LDS is rewritten by the next row
     }
 
+    if (write_state) {
 #pragma unroll
-    for (int r = 0; r < RPT; ++r)
-        store_stream(Sg + (size_t)(rg + RG * r) * D + 4 * cg, S[r]);
+        for (int r = 0; r < RPT; ++r)
+            store_stream(Sg + (size_t)(rg + RG * r) * D + 4 * cg, S[r]);
+    }
+}
+
+template <int D>
+static hipError_t recurrent_t(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                              const float *beta, float *const *state, float *const *snap,
+                              float *core, int B, int K, int heads, float scale, bool write_state,
+                              const int32_t *n_accept, hipStream_t stream)
+{
+    hipLaunchKernelGGL(kda_recurrent_kernel<D>, dim3(heads, B), dim3(RecCfg<D>::kThreads), 0,
+                       stream, qkv, ldqkv, gate, beta, state, snap, core, K, heads, scale,
+                       write_state, n_accept);
+    return hipGetLastError();
 }
 
 hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float *gate,
@@ -162,15 +188,33 @@ hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float 
                                 float *core, int B, int K, int heads, int head_dim,
                                 float scale, hipStream_t stream)
 {
-    const dim3 grid(heads, B);
-    if (head_dim == 128) {
-        hipLaunchKernelGGL(kda_recurrent_kernel<128>, grid, dim3(RecCfg<128>::kThreads), 0,
-                           stream, qkv, ldqkv, gate, beta, state, snap, core, K, heads, scale);
-    } else {
-        hipLaunchKernelGGL(kda_recurrent_kernel<16>, grid, dim3(RecCfg<16>::kThreads), 0,
-                           stream, qkv, ldqkv, gate, beta, state, snap, core, K, heads, scale);
-    }
-    return hipGetLastError();
+    return head_dim == 128
+               ? recurrent_t<128>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
+                                  true, nullptr, stream)
+               : recurrent_t<16>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
+                                 true, nullptr, stream);
+}
+
+hipError_t launch_kda_verify(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                             const float *beta, float *const *state, float *core, int B, int K,
+                             int heads, int head_dim, float scale, hipStream_t stream)
+{
+    return head_dim == 128
+               ? recurrent_t<128>(qkv, ldqkv, gate, beta, state, nullptr, core, B, K, heads,
+                                  scale, false, nullptr, stream)
+               : recurrent_t<16>(qkv, ldqkv, gate, beta, state, nullptr, core, B, K, heads,
+                                 scale, false, nullptr, stream);
+}
+
+hipError_t launch_kda_fold(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                           const float *beta, float *const *state, const int32_t *n_accept,
+                           int B, int K, int heads, int head_dim, hipStream_t stream)
+{
+    return head_dim == 128
+               ? recurrent_t<128>(qkv, ldqkv, gate, beta, state, nullptr, nullptr, B, K, heads,
+                                  1.f, true, n_accept, stream)
+               : recurrent_t<16>(qkv, ldqkv, gate, beta, state, nullptr, nullptr, B, K, heads,
+                                 1.f, true, n_accept, stream);
 }
 
 }  // namespace kda

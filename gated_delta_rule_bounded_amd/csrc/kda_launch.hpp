@@ -33,6 +33,15 @@ hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float 
                                 float *core, int B, int K, int heads, int head_dim,
                                 float scale, hipStream_t stream);
 
+// Write-on-accept: outputs of K rows with the state left as it is, then the
+// first n_accept[b] rows folded into the state (same per-row code as above).
+hipError_t launch_kda_verify(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                             const float *beta, float *const *state, float *core, int B, int K,
+                             int heads, int head_dim, float scale, hipStream_t stream);
+hipError_t launch_kda_fold(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                           const float *beta, float *const *state, const int32_t *n_accept,
+                           int B, int K, int heads, int head_dim, hipStream_t stream);
+
 size_t prefill_workspace_bytes(int T_pad, int heads, int head_dim, int chunk);
 int prefill_segment_chunks(int T, int heads, int head_dim, int chunk);
 

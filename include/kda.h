@@ -243,6 +243,34 @@ int kda_decode_k(const uint16_t *qkv, int64_t ldqkv, const float *gate,
                  int32_t head_dim, float scale, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kda_verify_k / kda_fold_accepted — write-on-accept form of decode_k.
+ * "Glm5NextLayer" page, LayerWriteOnAccept: the verify produces the K rows'
+ * outputs without writing the state, and once the number of accepted rows of
+ * each sequence is known, gdn_fold_accepted folds those rows into the state
+ * (na_tab: a device array of accepted row counts in batch order).  Against
+ * kda_decode_k with K-1 snapshots this moves each sequence's state 3 times
+ * (read, then read and write) instead of K+1 times.
+ *
+ * kda_verify_k: arguments as kda_decode_k without snapshots; core rows are
+ *   bitwise those of kda_decode_k; every state is left unchanged.
+ * kda_fold_accepted: qkv, gate, beta must hold the same rows the verify read
+ *   ([B*K, ...], sequence-major); n_accept device int32 [B], each clamped to
+ *   [0, K].  Afterwards *state[b] is bitwise the state kda_decode_k would
+ *   have left after row n_accept[b]-1 (its snapshot, or its final state for
+ *   n_accept[b] == K); n_accept[b] == 0 leaves it untouched.  Writes no output.
+ * Errors as kda_decode_k (n_accept required).  B == 0 or K == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+int kda_verify_k(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                 const float *beta, float *const *state, float *core, int32_t B,
+                 int32_t K, int32_t heads, int32_t head_dim, float scale,
+                 hipStream_t stream);
+
+int kda_fold_accepted(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                      const float *beta, float *const *state, const int32_t *n_accept,
+                      int32_t B, int32_t K, int32_t heads, int32_t head_dim,
+                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * gated_rmsnorm — sigmoid-gated RMSNorm of the core output, per (token, head).
  * "Glm5NextKdaWorkspace" page, fields core, out_gate and o_norm_out;
  * "Glm5NextKdaWeights" page, field o_norm ([head_dim] bf16).

@@ -274,3 +274,18 @@ def test_varlen_validation(lib):
     assert call(core=A + 64) == E_ALIAS                        # core over q
     assert call(wsp=B + 256) == E_ALIAS                        # workspace over core
     assert call(q=A + 4) == E_SHAPE                            # misaligned
+
+
+def test_write_on_accept_validation(lib):
+    def verify(qkv=A, ld=3 * 32, core=B, Bn=2, K=4, head_dim=16, state=C):
+        return lib.kda_verify_k(qkv, ld, Dp, E, state, core, Bn, K, 2, head_dim, 0.25, None)
+
+    def fold(qkv=A, ld=3 * 32, na=F, Bn=2, K=4, head_dim=16, state=C):
+        return lib.kda_fold_accepted(qkv, ld, Dp, E, state, na, Bn, K, 2, head_dim, None)
+
+    assert verify(K=0) == OK and fold(Bn=0) == OK
+    assert verify(head_dim=64) == E_UNSUP and fold(head_dim=64) == E_UNSUP
+    assert verify(K=-1) == E_SHAPE and fold(K=-1) == E_SHAPE
+    assert verify(ld=90) == E_SHAPE and fold(ld=90) == E_SHAPE
+    assert verify(state=0) == E_NULL and fold(na=0) == E_NULL
+    assert verify(core=A + 64) == E_ALIAS                     # core over the qkv rows

@@ -159,3 +159,38 @@ def test_decode_full_size_b256():
         ref_core, ref_S, _ = _oracle_seq(steps, S0[b], b, H, D, scale)
         assert relerr(got[:, b], ref_core) < TOL
         assert relerr(final[b], ref_S) < TOL
+
+
+@pytest.mark.parametrize("B,K,H,D", [(6, 4, 2, 16), (6, 4, 4, 128), (64, 4, 32, 128), (3, 1, 2, 128)])
+def test_write_on_accept_equals_snapshots(B, K, H, D):
+    """Verify then fold ("Glm5NextLayer" page, write-on-accept): the verify's
+    rows are bitwise those of decode_k and leave the states alone; folding
+    n_accept rows leaves exactly decode_k's snapshot after that row (the
+    starting state for 0, decode_k's final state for K).  n_accept runs over
+    every value 0..K and two out-of-range values, which clamp."""
+    import gated_delta_rule_bounded_amd as kda
+    scale = D ** -0.5
+    seed = 4100 + B + K
+    rows, S0, ck, sk, snaps = _decode_k_vs_serial(B, K, H, D, seed)
+    qkv = cuda(torch.stack([r["qkv"] for r in rows], 1).reshape(B * K, -1), torch.bfloat16)
+    gate = cuda(np.stack([r["gate"] for r in rows], 1).reshape(B * K, H, D))
+    beta = cuda(np.stack([r["beta"] for r in rows], 1).reshape(B * K, H))
+    st = cuda(S0)
+    tab = kda.ptr_table(st)
+    core = torch.empty(B * K, H, D, device="cuda")
+    say("verify_k", B, K, H, D)
+    kda.kda_verify_k(qkv, gate, beta, tab, core, B=B, K=K, heads=H, head_dim=D, scale=scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(core.view(B, K, H, D).cpu().numpy(), ck)
+    np.testing.assert_array_equal(st.cpu().numpy(), S0)
+    na = np.array([(b % (K + 3)) - 1 for b in range(B)], np.int32)   # -1, 0, .., K, K+1, ...
+    say("fold_accepted", B, K, H, D)
+    kda.kda_fold_accepted(qkv, gate, beta, tab, torch.from_numpy(na).cuda(), B=B, K=K, heads=H,
+                          head_dim=D)
+    torch.cuda.synchronize()
+    got = st.cpu().numpy()
+    sn = snaps.view(B, K - 1, H, D, D).cpu().numpy() if K > 1 else None
+    for b in range(B):
+        n = min(max(int(na[b]), 0), K)
+        want = S0[b] if n == 0 else (sk[b] if n == K else sn[b, n - 1])
+        np.testing.assert_array_equal(got[b], want, err_msg=f"seq {b} n_accept {na[b]}")

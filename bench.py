@@ -230,6 +230,35 @@ def bench_decode_k(kda, dev, n_calls=32, n_sets=4):
     torch.cuda.synchronize()
     t_conv = float(np.median([a.elapsed_time(b) for a, b, _ in evs])) * 1e-3
     t_dk = float(np.median([b.elapsed_time(c) for _, b, c in evs])) * 1e-3
+
+    # write-on-accept on the same rows: verify (state read only), then fold
+    # K-1 accepted rows of every sequence (state read and written once)
+    na = torch.full((B,), K - 1, dtype=torch.int32, device=dev)
+
+    def woa(i, e=None):
+        st, tab, _, _ = sets[i % n_sets]
+        if e:
+            e[0].record()
+        kda.kda_verify_k(y, gate, beta, tab, core, B=B, K=K, heads=H, head_dim=D,
+                         scale=D ** -0.5)
+        if e:
+            e[1].record()
+        kda.kda_fold_accepted(y, gate, beta, tab, na, B=B, K=K, heads=H, head_dim=D)
+        if e:
+            e[2].record()
+
+    for i in range(n_sets):
+        woa(i)
+    evw = [(ev(), ev(), ev()) for _ in range(n_calls)]
+    torch.cuda.synchronize()
+    for i in range(n_calls):
+        woa(i, evw[i])
+    torch.cuda.synchronize()
+    t_ver = float(np.median([a.elapsed_time(b) for a, b, _ in evw])) * 1e-3
+    t_fold = float(np.median([b.elapsed_time(c) for _, b, c in evw])) * 1e-3
+    st1 = B * H * D * D * 4
+    ver_b = st1 + B * K * (cd * 2 + H * D * 4 + H * 4 + H * D * 4)
+    fold_b = 2 * st1 + B * (K - 1) * (2 * H * D * 2 + H * D * 4 + H * 4)
     state_b = B * H * D * D * 4 * (2 + (K - 1))                 # read, final write, K-1 snapshots
     io_b = B * K * (cd * 2 + H * D * 4 + H * 4 + H * D * 4)     # qkv, gate, beta, core
     conv_b = B * (4 * cd * 2) * (2 + (K - 1)) + B * K * cd * 2 * 2 + cd * 4 * 2
@@ -237,7 +266,13 @@ def bench_decode_k(kda, dev, n_calls=32, n_sets=4):
                 decode_k_ms=t_dk * 1e3, decode_k_GBps=(state_b + io_b) / t_dk / 1e9,
                 decode_k_hbm_frac=(state_b + io_b) / t_dk / PEAK_HBM,
                 conv_ms=t_conv * 1e3, conv_GBps=conv_b / t_conv / 1e9,
-                verify_tokens_per_s=B * K / (t_dk + t_conv))
+                verify_tokens_per_s=B * K / (t_dk + t_conv),
+                write_on_accept=dict(verify_ms=t_ver * 1e3, fold_ms=t_fold * 1e3,
+                                     verify_GBps=ver_b / t_ver / 1e9,
+                                     fold_GBps=fold_b / t_fold / 1e9,
+                                     state_bytes=3 * st1, decode_k_state_bytes=state_b,
+                                     speedup_vs_snapshots=t_dk / (t_ver + t_fold),
+                                     n_accept=K - 1))
 
 
 def bench_stages(kda, dev, reps=10):
@@ -350,6 +385,49 @@ def bench_block(kda, dev, reps=10):
                 projection_mfma_frac=gemm_flops / t_gemm / PEAK_BF16_MFMA)
 
 
+def bench_prefill_varlen(kda, dev, reps=50):
+    """The prefill workload's 4096 tokens (32 heads x 128, chunk 64, fp32
+    states ~ N(0, 0.05)) as many prompts in one kda_prefill_varlen call:
+    8 x 512 and 64 x 64 tokens, each prompt from its own state."""
+    out = {}
+    for n_seq in (8, 64):
+        L = T // n_seq
+        raw = workloads.core_raw(T, H, D, workloads.SEED_INPUT + 6, qkv_bf16=True)
+        a_log, dt = torch.from_numpy(raw["a_log"]).to(dev), torch.from_numpy(raw["dt_bias"]).to(dev)
+        gate = torch.empty(T, H, D, device=dev)
+        beta = torch.empty(T, H, device=dev)
+        kda.kda_gate(workloads.to_bf16(raw["g_raw"]).to(dev), a_log, dt, gate, T=T, heads=H,
+                     head_dim=D, b_raw=workloads.to_bf16(raw["b_raw"]).to(dev), beta=beta)
+        q, k, v = (torch.from_numpy(raw[n]).to(dev) for n in ("q", "k", "v"))
+        st = torch.from_numpy(workloads.state(H, D, 0.05, workloads.SEED_STATE + 6, B=n_seq)).to(dev)
+        tab = kda.ptr_table(st)
+        cu = torch.arange(0, T + 1, L, dtype=torch.int32, device=dev)
+        mx, tot = kda.varlen_chunks([L] * n_seq, C)
+        ws = torch.empty(kda.kda_prefill_workspace_bytes(tot * C, H, D, C), dtype=torch.uint8,
+                         device=dev)
+        core = torch.empty(T, H, D, device=dev)
+
+        def call():
+            kda.kda_prefill_varlen(q, k, v, gate, beta, tab, core, cu, ws, B=n_seq, rows=T,
+                                   max_chunks=mx, total_chunks=tot, heads=H, head_dim=D,
+                                   chunk=C, scale=D ** -0.5)
+
+        for _ in range(5):
+            call()
+        es = [(ev(), ev()) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in es:
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        t = float(np.median([a.elapsed_time(b) for a, b in es])) * 1e-3
+        out[f"{n_seq}x{L}"] = dict(ms=t * 1e3, tokens_per_s=T / t)
+    out["config"] = (f"{T} tokens as equal prompts, heads={H}, head_dim={D}, chunk={C}, "
+                     "one kda_prefill_varlen call, per-prompt fp32 states")
+    return out
+
+
 def bench_block_decode(kda, dev, reps=40, n_sets=4):
     """Block-level decode at the layer's full size (hidden 4096, 32 heads x
     128, rank-128 gates, weights ~ N(0, 0.02)): one sequence verifying K = 4
@@ -422,17 +500,22 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
                           GBps=g_bytes / t_g / 1e9, hbm_frac=g_bytes / t_g / PEAK_HBM))
 
 
-def cpu_baseline(raw, threads):
-    """The fp64 oracle, as it stands, on the full prefill workload."""
+def cpu_baseline(raw, threads, min_seconds=10.0):
+    """The fp64 oracle, as it stands, on the full prefill workload, repeated
+    until about min_seconds of CPU time have passed."""
     import oracle
     g, b = oracle.kda_gate(raw["g_raw"], raw["a_log"], raw["dt_bias"], H, D, b_raw=raw["b_raw"])
     S0 = workloads.state(H, D, 0.05, workloads.SEED_STATE + 1)
-    t0 = time.perf_counter()
-    oracle.kda_recurrence(raw["q"], raw["k"], raw["v"], g, b, S0, D ** -0.5, threads=threads)
-    dt = time.perf_counter() - t0
-    return dict(value=T / dt, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"the whole prefill workload (T={T}, H={H}, D={D}), token-serial fp64, "
-                       f"heads split over {threads} threads; {dt:.2f} s")
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.kda_recurrence(raw["q"], raw["k"], raw["v"], g, b, S0, D ** -0.5, threads=threads)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return dict(value=n * T / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"the whole prefill workload (T={T}, H={H}, D={D}) {n} times, "
+                       f"token-serial fp64, heads split over {threads} threads; {dt:.1f} s")
 
 
 def main():
@@ -563,6 +646,8 @@ def main():
         log("block ...")
         out["block"] = bench_block(kda, dev)
         log(f"block: {out['block']['tokens_per_s'] / 1e6:.2f} M tokens/s")
+        log("prefill varlen ...")
+        out["prefill_varlen"] = bench_prefill_varlen(kda, dev)
         log("block decode ...")
         out["block_decode"] = bench_block_decode(kda, dev)
         log(f"block decode: verify {out['block_decode']['verify_ms'] * 1e3:.1f} us, "

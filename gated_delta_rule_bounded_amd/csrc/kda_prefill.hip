@@ -59,15 +59,19 @@ constexpr float kSpanLimit = 86.0f; // log2 units: largest diagonal-block decay 
 // follows the blocks of sequences 0..s-1.  A workgroup maps itself onto its
 // sequence and then runs exactly the single-sequence code: the rows of the
 // next sequence past the end of its last chunk are pad rows to it, replaced
-// at load time like any pad tail.  cu == nullptr: one sequence, the plain
-// arguments apply.
+// at load time like any pad tail.  A launch covers the global chunks
+// [seg_lo, seg_hi) only (a cache-sized segment); a sequence that straddles a
+// segment boundary continues in the next launch from the state the previous
+// one stored, on the same chunk grid, so the result does not depend on the
+// segmentation.  cu == nullptr: one sequence, the plain arguments apply.
 // ---------------------------------------------------------------------------
 struct Varlen {
     const int32_t *cu;      // [B + 1] row offsets, or nullptr
     float *const *states;   // [B] state pointers (forward)
     int64_t rows;           // rows held by the row arrays
     int32_t max_chunks;     // chunks of the longest sequence (prepare grid)
-    int32_t total_chunks;   // operand blocks in the workspace
+    int32_t total_chunks;   // chunks of all sequences
+    int32_t seg_lo, seg_hi; // global chunks of this launch; block 0 of the workspace = seg_lo
 };
 
 struct SeqSpan {
@@ -368,11 +372,12 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
     if (vl.cu) {
         const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
-        if (!sp.ok || n >= sp.nch) return;   // uniform over the workgroup
+        nblk = sp.chunk0 + n;
+        if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
+        nblk -= vl.seg_lo;
         const int64_t r0 = sp.row0 * H;
         q += r0 * D, k += r0 * D, v += r0 * D, gate += r0 * D, beta += r0;
         T = sp.T;
-        nblk = sp.chunk0 + n;
         tmax = vl.rows - 1 - sp.row0;
     }
     // wave index, uniform across the wave (scalar register)
@@ -637,11 +642,12 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
     if (vl.cu) {
         const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
-        if (!sp.ok || n >= sp.nch) return;   // uniform over the workgroup
+        nblk = sp.chunk0 + n;
+        if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
+        nblk -= vl.seg_lo;
         const int64_t r0 = sp.row0 * H;
         q += r0 * D, k += r0 * D, v += r0 * D, gate += r0 * D, beta += r0;
         T = sp.T;
-        nblk = sp.chunk0 + n;
         tmax = vl.rows - 1 - sp.row0;
     }
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -989,14 +995,17 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
     // all value slices of one head share an XCD (workgroups are dealt to the
     // 8 XCDs round-robin), so they share that XCD's L2 copy of the operands
     const int h = blockIdx.x % H, jt = blockIdx.x / H, j0 = 16 * jt;
-    if (vl.cu) {   // sequence blockIdx.y: its state, rows and operand blocks
+    if (vl.cu) {   // sequence blockIdx.y: its state, and its chunks inside this segment
         const SeqSpan sp = seq_span<C>(vl, blockIdx.y);
-        if (!sp.ok || sp.nch == 0) return;   // uniform over the workgroup
+        const int64_t g0 = max(sp.chunk0, (int64_t)vl.seg_lo);
+        const int64_t g1 = min(sp.chunk0 + sp.nch, (int64_t)vl.seg_hi);
+        if (!sp.ok || g0 >= g1) return;   // uniform over the workgroup
+        const int c0 = (int)(g0 - sp.chunk0);   // first chunk of the sequence walked here
         state = vl.states[blockIdx.y];
-        core += sp.row0 * H * D;
-        ws += sp.chunk0 * H * B::kSize;
-        T = sp.T;
-        NC = sp.nch;
+        core += (sp.row0 + (int64_t)c0 * C) * H * D;
+        ws += (g0 - vl.seg_lo) * H * B::kSize;
+        NC = (int)(g1 - g0);
+        T = min(sp.T - c0 * C, NC * C);
     }
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
@@ -1217,14 +1226,17 @@ __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu
     using B = Blk<D, C>;
     static_assert(B::kSplit, "split operand blocks need D, C multiples of 32");
     const int h = blockIdx.x % H, jt = blockIdx.x / H, j0 = 16 * jt;
-    if (vl.cu) {   // sequence blockIdx.y: its state, rows and operand blocks
+    if (vl.cu) {   // sequence blockIdx.y: its state, and its chunks inside this segment
         const SeqSpan sp = seq_span<C>(vl, blockIdx.y);
-        if (!sp.ok || sp.nch == 0) return;   // uniform over the workgroup
+        const int64_t g0 = max(sp.chunk0, (int64_t)vl.seg_lo);
+        const int64_t g1 = min(sp.chunk0 + sp.nch, (int64_t)vl.seg_hi);
+        if (!sp.ok || g0 >= g1) return;   // uniform over the workgroup
+        const int c0 = (int)(g0 - sp.chunk0);   // first chunk of the sequence walked here
         state = vl.states[blockIdx.y];
-        core += sp.row0 * H * D;
-        ws += sp.chunk0 * H * B::kSize;
-        T = sp.T;
-        NC = sp.nch;
+        core += (sp.row0 + (int64_t)c0 * C) * H * D;
+        ws += (g0 - vl.seg_lo) * H * B::kSize;
+        NC = (int)(g1 - g0);
+        T = min(sp.T - c0 * C, NC * C);
     }
     const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool chain = r < NW;            // waves 0..NW-1 carry the state
@@ -1541,14 +1553,22 @@ hipError_t launch_kda_prefill_varlen(const float *q, const float *k, const float
                                      int max_chunks, int total_chunks, int heads, int head_dim,
                                      int chunk, float scale, void *workspace, hipStream_t stream)
 {
-    // one prepare over every chunk of every sequence, then one walk per
-    // (sequence, head, value slice)
-    const Varlen vl{cu_seqlens, state, rows, max_chunks, total_chunks};
-    hipError_t e = KDA_PREFILL_DISPATCH(prepare_t, q, k, v, gate, beta, 0, heads, workspace, vl,
-                                        B, stream);
-    if (e != hipSuccess) return e;
-    return KDA_PREFILL_DISPATCH(forward_t, nullptr, core, 0, heads, scale, workspace, vl, B,
-                                stream);
+    // Segments of global chunks sized as kda_prefill's: each is prepared into
+    // the start of the workspace and walked at once (one walk per sequence,
+    // head and value slice that has chunks in it), so the forward pass reads
+    // operand blocks the prepare pass has just left in the last-level cache.
+    const int seg = prefill_segment_chunks(total_chunks * chunk, heads, head_dim, chunk);
+    for (int lo = 0; lo < total_chunks; lo += seg) {
+        const Varlen vl{cu_seqlens, state, rows, max_chunks, total_chunks, lo,
+                        std::min(lo + seg, total_chunks)};
+        hipError_t e = KDA_PREFILL_DISPATCH(prepare_t, q, k, v, gate, beta, 0, heads, workspace,
+                                            vl, B, stream);
+        if (e != hipSuccess) return e;
+        e = KDA_PREFILL_DISPATCH(forward_t, nullptr, core, 0, heads, scale, workspace, vl, B,
+                                 stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kda

@@ -43,8 +43,8 @@ PEAK_HBM = 8.0e12             # MI355X HBM3E peak, B/s
 # HBM bytes per launch (FETCH_SIZE and WRITE_SIZE scaled by the copy
 # calibration) from rocprofv3 counter runs of the kernels as they are built
 # now; a kernel is left out once it changes after its counters were taken.
-TRAFFIC_BYTES = {"kda_chunk_prep": (66160.11 * 2.0 + 147968.05 * 1.0) * 1024,
-                 "kda_chunk_fwd": (75090.61 * 2.0 + 34816.0 * 1.0) * 1024}
+TRAFFIC_BYTES = {"kda_chunk_prep": (66676.55 * 2.0 + 147968.04 * 1.0) * 1024,
+                 "kda_chunk_fwd": (75098.71 * 2.0 + 34816.0 * 1.0) * 1024}
 # Both prefill kernels run each fp32 product as three bf16 products (hi*hi,
 # hi*lo, lo*hi, fp32 accumulation), so their matrix-unit ceiling in
 # fp32-equivalent flops is a third of the bf16 peak.

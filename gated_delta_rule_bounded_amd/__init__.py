@@ -23,7 +23,7 @@ __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_prepare",
            "gated_rmsnorm", "kda_prefill_workspace_bytes", "kda_prefill_segment_chunks",
            "kda_block_prefill", "block_buffers", "BLOCK_WEIGHT_NAMES",
            "dense_gemv_bf16_batchm", "kda_prefill_varlen", "varlen_chunks",
-           "kda_verify_k", "kda_fold_accepted", "kda_block_decode", "kda_block_decode_k",
+           "kda_verify_k", "kda_fold_accepted", "kda_prefill_split", "kda_block_decode", "kda_block_decode_k",
            "block_decode_buffers",
            "ptr_table", "KdaError",
            "last_error", "library_path"]
@@ -334,3 +334,15 @@ def kda_fold_accepted(qkv, gate, beta, state, n_accept, *, B, K, heads, head_dim
         _ptr(qkv, torch.bfloat16, "qkv"), _rowstride(qkv, "qkv"), _ptr(gate, f, "gate"),
         _ptr(beta, f, "beta"), _ptr(state, torch.int64, "state"),
         _ptr(n_accept, torch.int32, "n_accept"), B, K, heads, head_dim, _stream()))
+
+
+def kda_prefill_split(q, k, v, gate, beta, state, core, cap_state, workspace, *, T, cap, T_pad,
+                      heads, head_dim, chunk, scale):
+    """Prefill rows [0, cap), copy the state to ``cap_state``, then rows
+    [cap, T) on chunks starting at cap (bitwise two kda_prefill calls)."""
+    f = torch.float32
+    _check(_lib.lib.kda_prefill_split(
+        _ptr(q, f, "q"), _ptr(k, f, "k"), _ptr(v, f, "v"), _ptr(gate, f, "gate"),
+        _ptr(beta, f, "beta"), _ptr(state, f, "state"), _ptr(core, f, "core"),
+        _ptr(cap_state, f, "cap_state"), T, cap, T_pad, heads, head_dim, chunk, float(scale),
+        _ptr(workspace, None, "workspace"), workspace.numel(), _stream()))

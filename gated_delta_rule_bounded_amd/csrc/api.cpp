@@ -176,6 +176,48 @@ int kda_prefill(const float *q, const float *k, const float *v, const float *gat
                       "kda_prefill launch");
 }
 
+int kda_prefill_split(const float *q, const float *k, const float *v, const float *gate,
+                      const float *beta, float *state, float *core, float *cap_state,
+                      int32_t T, int32_t cap, int32_t T_pad, int32_t heads, int32_t head_dim,
+                      int32_t chunk, float scale, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream)
+{
+    if (!(chunk == 16 || chunk == 64) || cap < 0 || T < 0 || cap > T)
+        return fail(chunk == 16 || chunk == 64 ? KDA_ERR_SHAPE : KDA_ERR_UNSUPPORTED,
+                    "kda_prefill_split: T=%d cap=%d chunk=%d", T, cap, chunk);
+    // the tail's chunks start at cap, so its last chunk ends at
+    // cap + round_up(T - cap, chunk): those rows must exist
+    const int64_t need_rows = (int64_t)cap + ((int64_t)(T - cap) + chunk - 1) / chunk * chunk;
+    if (T_pad < need_rows)
+        return fail(KDA_ERR_SHAPE, "kda_prefill_split: T_pad=%d < cap + round_up(T - cap) = %lld",
+                    T_pad, (long long)need_rows);
+    const int rc = check_prefill("kda_prefill_split", q, k, v, gate, beta, state, core, T, T_pad,
+                                 heads, head_dim, chunk, workspace, workspace_bytes, true, true,
+                                 true);
+    if (rc == 1) return ok();
+    if (rc) return rc;
+    if (!cap_state) return fail(KDA_ERR_NULL, "kda_prefill_split: cap_state is NULL");
+    const size_t st_b = (size_t)heads * head_dim * head_dim * 4;
+    const size_t rows_b = (size_t)T_pad * heads * head_dim * 4;
+    if (!aligned16(cap_state))
+        return fail(KDA_ERR_SHAPE, "kda_prefill_split: cap_state must be 16-byte aligned");
+    if (overlap(cap_state, st_b, state, st_b) || overlap(cap_state, st_b, core, rows_b) ||
+        overlap(cap_state, st_b, workspace, workspace_bytes))
+        return fail(KDA_ERR_ALIAS, "kda_prefill_split: cap_state overlaps state, core or workspace");
+    const int64_t HD = (int64_t)heads * head_dim;
+    hipError_t e = hipSuccess;
+    if (cap > 0)
+        e = kda::launch_kda_prefill(q, k, v, gate, beta, state, core, cap, heads, head_dim, chunk,
+                                    scale, workspace, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(cap_state, state, st_b, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess && T > cap)
+        e = kda::launch_kda_prefill(q + cap * HD, k + cap * HD, v + cap * HD, gate + cap * HD,
+                                    beta + (int64_t)cap * heads, state, core + cap * HD, T - cap,
+                                    heads, head_dim, chunk, scale, workspace, stream);
+    return hip_status(e, "kda_prefill_split launch");
+}
+
 int kda_prefill_prepare(const float *q, const float *k, const float *v, const float *gate,
                         const float *beta, int32_t T, int32_t T_pad, int32_t heads,
                         int32_t head_dim, int32_t chunk, void *workspace,

@@ -168,6 +168,28 @@ int kda_prefill_forward(float *state, float *core, int32_t T, int32_t T_pad,
                         size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kda_prefill_split — one prefill pass split at row cap, with the state at
+ * the split captured.  "Glm5NextLayer" page, supports_replay_tail_split: the
+ * rows from cap on get exactly the bits a prefill starting at cap gives them
+ * (the linear-attention layer splits its recurrence there and copies its
+ * state into the plan's slot).
+ *   Rows [0, cap) are prefilled from *state on chunks starting at row 0; the
+ *   state after row cap-1 is copied to cap_state (fp32 [heads, head_dim,
+ *   head_dim], caller-owned); rows [cap, T) are prefilled from that state on
+ *   chunks starting at row cap.  Bitwise the same as kda_prefill over
+ *   [0, cap) followed by kda_prefill over [cap, T).
+ * Arguments and errors as kda_prefill, plus: 0 <= cap <= T; T_pad at least
+ * cap + round_up(T - cap, chunk) (the tail's last chunk must exist; rows
+ * past T may hold anything); cap_state 16-byte aligned and disjoint from
+ * state, core and workspace (KDA_ERR_ALIAS).  T == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+int kda_prefill_split(const float *q, const float *k, const float *v,
+                      const float *gate, const float *beta, float *state, float *core,
+                      float *cap_state, int32_t T, int32_t cap, int32_t T_pad,
+                      int32_t heads, int32_t head_dim, int32_t chunk, float scale,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * kda_prefill_varlen — chunked prefill of B sequences in one call, each from
  * its own carried state.  "Glm5NextLayer" page, batched linear-attention
  * prefill (prefill_gdn_full_batched / ..._varlen): one state pointer per

@@ -289,3 +289,22 @@ def test_write_on_accept_validation(lib):
     assert verify(ld=90) == E_SHAPE and fold(ld=90) == E_SHAPE
     assert verify(state=0) == E_NULL and fold(na=0) == E_NULL
     assert verify(core=A + 64) == E_ALIAS                     # core over the qkv rows
+
+
+def test_prefill_split_validation(lib):
+    H, Dh, C = 2, 16, 16
+    ws = lib.kda_prefill_workspace_bytes(128, H, Dh, C)
+
+    def call(T=100, cap=37, T_pad=128, cap_state=E + (1 << 30), state=Dp, chunk=C):
+        return lib.kda_prefill_split(A, A + (1 << 30), A + (2 << 30), A + (3 << 30),
+                                     A + (4 << 30), state, B, cap_state, T, cap, T_pad, H, Dh,
+                                     chunk, 0.25, E, ws, None)
+
+    assert call(T=0, cap=0) == OK
+    assert call(cap=101) == E_SHAPE                            # cap > T
+    assert call(cap=-1) == E_SHAPE
+    assert call(T=120, cap=1) == E_SHAPE                       # tail chunks end past T_pad
+    assert call(chunk=32) == E_UNSUP
+    assert call(cap_state=0) == E_NULL
+    assert call(cap_state=Dp + 64) == E_ALIAS                  # over the state
+    assert call(cap_state=E + 256) == E_ALIAS                  # over the workspace

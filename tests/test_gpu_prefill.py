@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from conftest import relerr
-from kda_cases import core_case, gpu_prefill, oracle_core, say
+from kda_cases import core_case, cuda, gpu_prefill, oracle_core, pad_rows, say
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -233,3 +233,51 @@ def test_prefill_segments_equal_one_pass_bitwise():
     assert torch.equal(core_a.view(torch.int32), core_b.view(torch.int32))
     assert torch.equal(st_a.view(torch.int32), st_b.view(torch.int32))
     assert bool((core_a[T:] == 7.0).all())
+
+
+@pytest.mark.parametrize("T,cap,T_pad,C,D", [(200, 37, 256, 64, 128), (200, 1, 320, 64, 128),
+                                             (200, 0, 256, 64, 128), (200, 200, 256, 64, 128),
+                                             (57, 20, 80, 16, 16), (4059, 2101, 4160, 64, 128)])
+def test_prefill_split_captures_state_at_cap(T, cap, T_pad, C, D):
+    """Replay-tail split ("Glm5NextLayer" page): rows from cap get the bits of
+    a prefill starting at cap, and the state at cap is captured.  Bitwise
+    against two kda_prefill calls; against the oracle's state after cap rows
+    and its whole run (the token-serial recurrence does not see the split)."""
+    import gated_delta_rule_bounded_amd as kda
+    H = 4 if D == 128 else 2
+    if T > 1000:
+        H = 32
+    scale = D ** -0.5
+    case = core_case(T, H, D, 7100 + cap, 0.05)
+    ins = [cuda(pad_rows(case[n], T_pad, np.nan)) for n in ("q", "k", "v", "gate", "beta")]
+    st = cuda(case["S0"]).contiguous()
+    cap_st = torch.full_like(st, 3.0)
+    core = torch.full((T_pad, H, D), 7.0, device="cuda")
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(T_pad, H, D, C), dtype=torch.uint8,
+                     device="cuda")
+    say("prefill_split", T, cap, T_pad, C, D)
+    kda.kda_prefill_split(*ins, st, core, cap_st, ws, T=T, cap=cap, T_pad=T_pad, heads=H,
+                          head_dim=D, chunk=C, scale=scale)
+    torch.cuda.synchronize()
+    got_core, got_S, got_cap = core.cpu().numpy(), st.cpu().numpy(), cap_st.cpu().numpy()
+    # two plain calls: [0, cap), then [cap, T) from the carried state
+    if cap > 0:
+        a_core, a_S = gpu_prefill(case, cap, -(-cap // C) * C, C, scale)
+    else:
+        a_core, a_S = np.zeros((0, H, D), np.float32), case["S0"]
+    np.testing.assert_array_equal(got_cap, a_S)
+    np.testing.assert_array_equal(got_core[:cap], a_core[:cap])
+    if T > cap:
+        tail = {n: case[n][cap:] for n in ("q", "k", "v", "gate", "beta")}
+        tail["S0"] = a_S
+        Tb = T - cap
+        b_core, b_S = gpu_prefill(tail, Tb, -(-Tb // C) * C, C, scale)
+        np.testing.assert_array_equal(got_core[cap:T], b_core[:Tb])
+        np.testing.assert_array_equal(got_S, b_S)
+    assert np.all(got_core[T:] == 7.0)
+    ref_core, ref_S = oracle_core(case, scale)
+    assert relerr(got_core[:T], ref_core) < TOL
+    assert relerr(got_S, ref_S) < TOL
+    if cap > 0:
+        _, ref_cap = oracle_core(case, scale, T=cap)
+        assert relerr(got_cap, ref_cap) < TOL

@@ -45,6 +45,9 @@ PEAK_HBM = 8.0e12             # MI355X HBM3E peak, B/s
 # now; a kernel is left out once it changes after its counters were taken.
 TRAFFIC_BYTES = {"kda_chunk_prep": (66676.55 * 2.0 + 147968.04 * 1.0) * 1024,
                  "kda_chunk_fwd": (75098.71 * 2.0 + 34816.0 * 1.0) * 1024}
+# Counted HBM traffic of one decode step at 256 sequences (FETCH_SIZE x 2 +
+# WRITE_SIZE, KiB per dispatch) for the recurrent kernel as built now.
+DECODE_TRAFFIC_BYTES = (267441.1 * 2.0 + 528922.7 * 1.0) * 1024
 # Both prefill kernels run each fp32 product as three bf16 products (hi*hi,
 # hi*lo, lo*hi, fp32 accumulation), so their matrix-unit ceiling in
 # fp32-equivalent flops is a third of the bf16 peak.
@@ -179,7 +182,7 @@ def bench_decode(kda, dev, n_steps=64, n_inputs=8):
                 state_GBps=state_bytes / t / 1e9, total_GBps=(state_bytes + io_bytes) / t / 1e9,
                 ms_per_step_median=t * 1e3, tokens_per_s=B / t,
                 hbm_frac=(state_bytes + io_bytes) / t / PEAK_HBM,
-                state_bytes_per_step=state_bytes)
+                state_bytes_per_step=state_bytes, traffic=DECODE_TRAFFIC_BYTES)
 
 
 def bench_decode_k(kda, dev, n_calls=32, n_sets=4):
@@ -529,6 +532,8 @@ def main():
                     help="time the prefill steps only (profiler runs)")
     ap.add_argument("--block-only", action="store_true",
                     help="time the full-block call only and print its JSON object (profiler runs)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time decode and decode_k only and print their JSON objects (profiler runs)")
     ap.add_argument("--block-decode-only", action="store_true",
                     help="time the block decode / K-row verify only (profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -549,6 +554,16 @@ def main():
 
     if args.block_only:
         print(json.dumps({"block": bench_block(kda, dev)}), flush=True)
+        return
+    if args.decode_only:
+        if args.calibrate_copy:
+            src = torch.ones(1 << 28, device=dev)
+            dst = torch.empty_like(src)
+            torch.neg(src, out=dst)
+            torch.cuda.synchronize()
+            del src, dst
+        print(json.dumps({"decode": bench_decode(kda, dev), "decode_k": bench_decode_k(kda, dev)}),
+              flush=True)
         return
     if args.block_decode_only:
         print(json.dumps({"block_decode": bench_block_decode(kda, dev)}), flush=True)

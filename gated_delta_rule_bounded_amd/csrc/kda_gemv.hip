@@ -6,7 +6,8 @@
 // order whatever M is and wherever its row sits:
 //   * the contraction is cut into 32-deep steps; wave w of the workgroup takes
 //     the w-th quarter of them and chains them through one bf16 16x16x32 MFMA
-//     accumulator in an order set by the output column's tile alone;
+//     accumulator in an order set by the output column's tile alone (the
+//     same for every kernel instance below, whatever its load depth);
 //   * the four waves' partial sums meet in LDS and are added as
 //     ((p0 + p1) + p2) + p3, then rounded to bf16 (nearest, ties to even).
 // A row enters an MFMA only as its own A-operand row, and the matrix unit
@@ -44,10 +45,36 @@ struct Args {
     int32_t M;
 };
 
+// Visit order of a wave's contraction steps.  Wave w owns the contiguous
+// steps [beg, beg + cnt) and visits them starting at beg + rho, wrapping
+// around, rho = 12 x (column tile) mod cnt: the workgroups in flight read
+// different parts of their weight rows rather than all the same offset.  The
+// order depends on the column tile and the wave alone (not on M, and not on
+// how many steps a kernel instance loads at once), so every instance
+// accumulates an element in the same order.
+struct Visit {
+    int beg, cnt, rho;
+    __device__ __forceinline__ int step(int v) const {   // v-th visited step, v < 2 cnt
+        const int q = rho + v;
+        return beg + (q >= cnt ? q - cnt : q);
+    }
+};
+
+__device__ __forceinline__ Visit visit_of(int wave, int nsteps, int tile)
+{
+    const int per = (nsteps + kWaves - 1) / kWaves;
+    Visit vs;
+    vs.beg = min(wave * per, nsteps);
+    vs.cnt = min(vs.beg + per, nsteps) - vs.beg;
+    vs.rho = vs.cnt > 0 ? (12 * tile) % vs.cnt : 0;
+    return vs;
+}
+
 // Operands of SIF contraction steps (st0, st0 + 1, ...) for RT row tiles.
 // Every load is issued unconditionally, so the compiler can count the loads
 // in flight exactly and wait for one stage while the next is still coming:
-// steps past the end re-read the last step (their products are skipped).  x
+// slots past the wave's last step re-read its first one (their products are
+// skipped).  x
 // is read through a buffer resource bounded by the rows that exist: lanes of
 // rows past M carry an offset beyond the bound, which the hardware answers
 // with zeros and no memory traffic.
@@ -66,11 +93,11 @@ __device__ __forceinline__ uint4 load_x(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 template <int RT, int SIF>
 __device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *wrow,
                                            __amdgpu_buffer_rsrc_t xr,
-                                           const uint32_t (&xoff)[RT], int st0, int last)
+                                           const uint32_t (&xoff)[RT], const Visit &vs, int v0)
 {
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
-        const int st = min(st0 + j, last);
+        const int st = v0 + j < vs.cnt ? vs.step(v0 + j) : vs.beg;   // past the end: a valid dummy
         S.w[j] = *reinterpret_cast<const uint4 *>(wrow + 32 * st);
 #pragma unroll
         for (int t = 0; t < RT; ++t) S.x[j][t] = load_x(xr, xoff[t] + 64u * st);
@@ -78,12 +105,12 @@ __device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *wr
 }
 
 template <int RT, int SIF>
-__device__ __forceinline__ void mma_stage(const Stage<RT, SIF> &S, floatx4 (&acc)[RT], int st0,
-                                          int end)
+__device__ __forceinline__ void mma_stage(const Stage<RT, SIF> &S, floatx4 (&acc)[RT],
+                                          const Visit &vs, int v0)
 {
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
-        if (st0 + j >= end) break;
+        if (v0 + j >= vs.cnt) break;
         const bf16x8 b = __builtin_bit_cast(bf16x8, S.w[j]);
 #pragma unroll
         for (int t = 0; t < RT; ++t)
@@ -133,30 +160,16 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // Wave w owns the contiguous steps [beg, end) and walks them in stages of
-    // SIF steps, starting at a stage rotated by the column tile and wrapping
-    // around, so that at any moment the workgroups in flight read different
-    // parts of their weight rows rather than all the same offset.  The order
-    // depends only on the column tile and the wave, never on M.
-    const int per = (nsteps + kWaves - 1) / kWaves;
-    const int beg = min(wave * per, nsteps), end = min(beg + per, nsteps);
-    if (beg < end) {
-        const int nst = (end - beg + SIF - 1) / SIF;
-        const int rot = (n0 / kColTile) % nst;
-        auto stage = [&](int i) {  // first step of the i-th stage visited (i may run past nst)
-            int q = i + rot;
-            q -= q >= nst ? nst : 0;
-            q -= q >= nst ? nst : 0;
-            return beg + q * SIF;
-        };
+    const Visit vs = visit_of(wave, nsteps, n0 / kColTile);
+    if (vs.cnt > 0) {
         Stage<RT, SIF> A, B;
-        load_stage(A, wrow, xr, xoff, stage(0), end - 1);
+        load_stage(A, wrow, xr, xoff, vs, 0);
 #pragma unroll 1
-        for (int i = 0; i < nst; i += 2) {
-            load_stage(B, wrow, xr, xoff, stage(i + 1), end - 1);
-            mma_stage(A, acc, stage(i), end);
-            load_stage(A, wrow, xr, xoff, stage(i + 2), end - 1);
-            if (i + 1 < nst) mma_stage(B, acc, stage(i + 1), end);
+        for (int v = 0; v < vs.cnt; v += 2 * SIF) {
+            load_stage(B, wrow, xr, xoff, vs, v + SIF);
+            mma_stage(A, acc, vs, v);
+            load_stage(A, wrow, xr, xoff, vs, v + 2 * SIF);
+            mma_stage(B, acc, vs, v + SIF);
         }
     }
 

@@ -187,6 +187,7 @@ def test_block_decode_k_small_against_oracle(orc, B, K, H, D, hidden, rank):
 @pytest.mark.parametrize("B,K,H,D,hidden,rank", [
     (3, 4, 2, 16, 128, 32),
     (2, 5, 2, 128, 256, 32),
+    (5, 4, 2, 128, 256, 32),     # 20 verify rows against 5-row steps: two kernel instances
 ])
 def test_block_decode_k_bitwise_equals_serial_decodes(B, K, H, D, hidden, rank):
     x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1201 + K)

@@ -23,7 +23,8 @@ __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_prepare",
            "gated_rmsnorm", "kda_prefill_workspace_bytes", "kda_prefill_segment_chunks",
            "kda_block_prefill", "block_buffers", "BLOCK_WEIGHT_NAMES",
            "dense_gemv_bf16_batchm", "kda_prefill_varlen", "varlen_chunks",
-           "kda_verify_k", "kda_fold_accepted", "kda_prefill_split", "kda_block_decode", "kda_block_decode_k",
+           "kda_verify_k", "kda_fold_accepted", "kda_prefill_split",
+           "kda_block_verify_k", "kda_block_fold_accepted", "kda_block_decode", "kda_block_decode_k",
            "block_decode_buffers",
            "ptr_table", "KdaError",
            "last_error", "library_path"]
@@ -346,3 +347,26 @@ def kda_prefill_split(q, k, v, gate, beta, state, core, cap_state, workspace, *,
         _ptr(beta, f, "beta"), _ptr(state, f, "state"), _ptr(core, f, "core"),
         _ptr(cap_state, f, "cap_state"), T, cap, T_pad, heads, head_dim, chunk, float(scale),
         _ptr(workspace, None, "workspace"), workspace.numel(), _stream()))
+
+
+def kda_block_verify_k(hidden, weights, state, conv_state, buffers, out, *, B, K, hidden_size,
+                       heads, head_dim, rank, scale, eps_l2=1e-6, eps_rms=1e-5):
+    """The block over K rows of B sequences, bitwise as kda_block_decode_k,
+    with the recurrent and conv states left unwritten."""
+    bf = torch.bfloat16
+    wts, bufs = _block_weights(weights), _decode_buffers(buffers)
+    _check(_lib.lib.kda_block_verify_k(
+        _ptr(hidden, bf, "hidden"), ctypes.byref(wts), _ptr(state, torch.int64, "state"),
+        _ptr(conv_state, torch.int64, "conv_state"), ctypes.byref(bufs), _ptr(out, bf, "out"),
+        B, K, hidden_size, heads, head_dim, rank, float(scale), float(eps_l2), float(eps_rms),
+        _stream()))
+
+
+def kda_block_fold_accepted(buffers, state, conv_state, n_accept, *, B, K, heads, head_dim):
+    """Fold the first n_accept[b] verified rows into each recurrent and conv
+    state (``buffers`` those of the verify)."""
+    bufs = _decode_buffers(buffers)
+    _check(_lib.lib.kda_block_fold_accepted(
+        ctypes.byref(bufs), _ptr(state, torch.int64, "state"),
+        _ptr(conv_state, torch.int64, "conv_state"), _ptr(n_accept, torch.int32, "n_accept"), B,
+        K, heads, head_dim, _stream()))

@@ -15,7 +15,7 @@ SYMBOLS = ("kda_last_error", "conv_silu_l2", "kda_gate", "kda_prefill_workspace_
            "kda_prefill_forward", "kda_decode", "kda_decode_k", "gated_rmsnorm",
            "kda_block_prefill", "dense_gemv_bf16_batchm", "kda_block_decode_k",
            "kda_block_decode", "kda_prefill_varlen", "kda_verify_k", "kda_fold_accepted",
-           "kda_prefill_split")
+           "kda_prefill_split", "kda_block_verify_k", "kda_block_fold_accepted")
 
 
 class BlockWeights(ctypes.Structure):
@@ -97,6 +97,13 @@ def _load():
     lib.kda_block_decode_k.argtypes = [P, ctypes.POINTER(BlockWeights), P, P, P, P,
                                        ctypes.POINTER(BlockDecodeBuffers), P] + [i32] * 6 + \
         [f32] * 3 + [P]
+    lib.kda_block_verify_k.restype = ctypes.c_int
+    lib.kda_block_verify_k.argtypes = [P, ctypes.POINTER(BlockWeights), P, P,
+                                       ctypes.POINTER(BlockDecodeBuffers), P] + [i32] * 6 + \
+        [f32] * 3 + [P]
+    lib.kda_block_fold_accepted.restype = ctypes.c_int
+    lib.kda_block_fold_accepted.argtypes = [ctypes.POINTER(BlockDecodeBuffers), P, P, P, i32, i32,
+                                            i32, i32, P]
     lib.kda_block_decode.restype = ctypes.c_int
     lib.kda_block_decode.argtypes = [P, ctypes.POINTER(BlockWeights), P, P,
                                      ctypes.POINTER(BlockDecodeBuffers), P] + [i32] * 5 + \

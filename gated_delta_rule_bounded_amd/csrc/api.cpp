@@ -566,12 +566,15 @@ int dense_gemv_bf16_batchm(const uint16_t *x, int64_t ldx, const uint16_t *w, in
                       "dense_gemv_bf16_batchm launch");
 }
 
-int kda_block_decode_k(const uint16_t *hidden, const kda_block_weights *w, float *const *state,
-                       uint16_t *const *conv_state, float *const *snap,
-                       uint16_t *const *conv_snap, const kda_block_decode_buffers *b,
-                       uint16_t *out, int32_t B, int32_t K, int32_t hidden_size, int32_t heads,
-                       int32_t head_dim, int32_t rank, float scale, float eps_l2, float eps_rms,
-                       hipStream_t stream)
+// K rows of B sequences through the block: decode_k (states written, optional
+// snapshots) or, with `verify`, the write-on-accept verify (no state, conv
+// state or snapshot written).
+static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
+                            float *const *state, uint16_t *const *conv_state, float *const *snap,
+                            uint16_t *const *conv_snap, const kda_block_decode_buffers *b,
+                            uint16_t *out, int32_t B, int32_t K, int32_t hidden_size,
+                            int32_t heads, int32_t head_dim, int32_t rank, float scale,
+                            float eps_l2, float eps_rms, bool verify, hipStream_t stream)
 {
     if (!head_dim_ok(head_dim))
         return fail(KDA_ERR_UNSUPPORTED, "kda_block_decode_k: head_dim=%d", head_dim);
@@ -660,17 +663,21 @@ int kda_block_decode_k(const uint16_t *hidden, const kda_block_weights *w, float
         (rc = hip_status(kda::launch_gemv_bf16_batchm(mid, 2, Mi, stream),
                          "kda_block_decode_k: low-rank projections launch")) ||
         (rc = hip_status(kda::launch_conv_silu_l2(b->qkv_proj, cd, w->conv, conv_state,
-                                                  K > 1 ? conv_snap : nullptr, B, K, heads,
-                                                  head_dim, eps_l2, b->conv_out, cd, nullptr,
-                                                  nullptr, nullptr, stream),
+                                                  K > 1 && !verify ? conv_snap : nullptr, B, K,
+                                                  heads, head_dim, eps_l2, b->conv_out, cd,
+                                                  nullptr, nullptr, nullptr, stream, !verify),
                          "kda_block_decode_k: conv_silu_l2 launch")) ||
         (rc = hip_status(kda::launch_kda_gate(b->g_raw, qkv, b->b_raw, heads, w->a_log,
                                               w->dt_bias, Mi, heads, head_dim, b->gate, b->beta,
                                               stream),
                          "kda_block_decode_k: kda_gate launch")) ||
-        (rc = hip_status(kda::launch_kda_recurrent(b->conv_out, cd, b->gate, b->beta, state,
-                                                   K > 1 ? snap : nullptr, b->core, B, K, heads,
-                                                   head_dim, scale, stream),
+        (rc = hip_status(verify ? kda::launch_kda_verify(b->conv_out, cd, b->gate, b->beta,
+                                                         state, b->core, B, K, heads, head_dim,
+                                                         scale, stream)
+                                : kda::launch_kda_recurrent(b->conv_out, cd, b->gate, b->beta,
+                                                            state, K > 1 ? snap : nullptr,
+                                                            b->core, B, K, heads, head_dim,
+                                                            scale, stream),
                          "kda_block_decode_k: recurrent launch")) ||
         (rc = hip_status(kda::launch_gated_rmsnorm(b->core, qkv, b->out_gate, qkv, w->o_norm, Mi,
                                                    heads, head_dim, eps_rms, b->o_norm_out, qkv,
@@ -678,6 +685,53 @@ int kda_block_decode_k(const uint16_t *hidden, const kda_block_weights *w, float
                          "kda_block_decode_k: gated_rmsnorm launch")) ||
         (rc = hip_status(kda::launch_gemv_bf16_batchm(back, 1, Mi, stream),
                          "kda_block_decode_k: o_proj launch")))
+        return rc;
+    return ok();
+}
+
+int kda_block_decode_k(const uint16_t *hidden, const kda_block_weights *w, float *const *state,
+                       uint16_t *const *conv_state, float *const *snap,
+                       uint16_t *const *conv_snap, const kda_block_decode_buffers *b,
+                       uint16_t *out, int32_t B, int32_t K, int32_t hidden_size, int32_t heads,
+                       int32_t head_dim, int32_t rank, float scale, float eps_l2, float eps_rms,
+                       hipStream_t stream)
+{
+    return block_decode_run(hidden, w, state, conv_state, snap, conv_snap, b, out, B, K,
+                            hidden_size, heads, head_dim, rank, scale, eps_l2, eps_rms, false,
+                            stream);
+}
+
+int kda_block_verify_k(const uint16_t *hidden, const kda_block_weights *w, float *const *state,
+                       uint16_t *const *conv_state, const kda_block_decode_buffers *b,
+                       uint16_t *out, int32_t B, int32_t K, int32_t hidden_size, int32_t heads,
+                       int32_t head_dim, int32_t rank, float scale, float eps_l2, float eps_rms,
+                       hipStream_t stream)
+{
+    return block_decode_run(hidden, w, state, conv_state, nullptr, nullptr, b, out, B, K,
+                            hidden_size, heads, head_dim, rank, scale, eps_l2, eps_rms, true,
+                            stream);
+}
+
+int kda_block_fold_accepted(const kda_block_decode_buffers *b, float *const *state,
+                            uint16_t *const *conv_state, const int32_t *n_accept, int32_t B,
+                            int32_t K, int32_t heads, int32_t head_dim, hipStream_t stream)
+{
+    if (B < 0 || K < 0 || heads <= 0 || (int64_t)B * K > (1 << 24))
+        return fail(KDA_ERR_SHAPE, "kda_block_fold_accepted: B=%d K=%d heads=%d", B, K, heads);
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_block_fold_accepted: head_dim=%d", head_dim);
+    if (B == 0 || K == 0) return ok();
+    if (!b || !state || !conv_state || !n_accept || !b->qkv_proj || !b->conv_out || !b->gate ||
+        !b->beta)
+        return fail(KDA_ERR_NULL, "kda_block_fold_accepted: null pointer argument");
+    const int64_t cd = 3LL * heads * head_dim;
+    int rc;
+    if ((rc = hip_status(kda::launch_kda_fold(b->conv_out, cd, b->gate, b->beta, state, n_accept,
+                                              B, K, heads, head_dim, stream),
+                         "kda_block_fold_accepted: state fold launch")) ||
+        (rc = hip_status(kda::launch_conv_fold(b->qkv_proj, cd, conv_state, n_accept, B, K, heads,
+                                               head_dim, stream),
+                         "kda_block_fold_accepted: conv fold launch")))
         return rc;
     return ok();
 }

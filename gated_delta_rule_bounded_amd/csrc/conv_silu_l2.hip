@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, const uint16_t *__restrict__ w,
     uint16_t *const *__restrict__ conv_state, uint16_t *const *__restrict__ conv_snap,
     int rows, int H, int ntiles, float eps_l2, uint16_t *__restrict__ y, int64_t ldy,
-    float *__restrict__ q32, float *__restrict__ k32, float *__restrict__ v32)
+    float *__restrict__ q32, float *__restrict__ k32, float *__restrict__ v32, bool write_state)
 {
     constexpr int KC = kConvKC;
     constexpr int LANES_PER_HEAD = D / 8;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
     }
 
     // new conv state = the window after the sequence's last row
-    if (tile == 0 && st != nullptr && active) {
+    if (write_state && tile == 0 && st != nullptr && active) {
         uint16_t *dst = conv_state[seq];
         if (ntiles == 1) {
 #pragma unroll
@@ -150,11 +150,53 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
     }
 }
 
+// Write-on-accept for the conv window ("Glm5NextLayer" page,
+// LayerWriteOnAccept): after a verify that left the conv states untouched,
+// sequence b's window moves past its first n = n_accept[b] pre-conv rows
+// (clamped to [0, K]): the new window is the last KC rows of [old window;
+// rows b*K .. b*K + n - 1 of x], exactly the snapshot a K-row conv call writes
+// after row n - 1.  A thread owns 8 channels and reads its whole old window
+// before writing any of it.
+__global__ __launch_bounds__(kConvThreads) void conv_fold_kernel(
+    const uint16_t *__restrict__ x, int64_t ldx, uint16_t *const *__restrict__ conv_state,
+    const int32_t *__restrict__ n_accept, int K, int conv_dim)
+{
+    constexpr int KC = kConvKC;
+    const int grp = blockIdx.x * kConvThreads + threadIdx.x;
+    const int b = blockIdx.y;
+    const int n = min(max(n_accept[b], 0), K);
+    if (grp >= conv_dim / 8 || n == 0) return;
+    const int c0 = grp * 8;
+    uint16_t *__restrict__ st = conv_state[b];
+    uint4 old[KC];
+#pragma unroll
+    for (int j = 0; j < KC; ++j) old[j] = *reinterpret_cast<const uint4 *>(st + (int64_t)j * conv_dim + c0);
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+        const int idx = n + j;   // position in [old window; accepted rows]
+        const uint4 v = idx < KC ? old[idx]
+                                 : *reinterpret_cast<const uint4 *>(
+                                       x + ((int64_t)b * K + idx - KC) * ldx + c0);
+        *reinterpret_cast<uint4 *>(st + (int64_t)j * conv_dim + c0) = v;
+    }
+}
+
+hipError_t launch_conv_fold(const uint16_t *x, int64_t ldx, uint16_t *const *conv_state,
+                            const int32_t *n_accept, int B, int K, int heads, int head_dim,
+                            hipStream_t stream)
+{
+    const int conv_dim = 3 * heads * head_dim;
+    const dim3 grid((conv_dim / 8 + kConvThreads - 1) / kConvThreads, B);
+    hipLaunchKernelGGL(conv_fold_kernel, grid, dim3(kConvThreads), 0, stream, x, ldx, conv_state,
+                       n_accept, K, conv_dim);
+    return hipGetLastError();
+}
+
 hipError_t launch_conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w,
                                uint16_t *const *conv_state, uint16_t *const *conv_snap,
                                int n_seq, int rows, int heads, int head_dim, float eps_l2,
                                uint16_t *y, int64_t ldy, float *q32, float *k32, float *v32,
-                               hipStream_t stream)
+                               hipStream_t stream, bool write_state)
 {
     const int conv_dim = 3 * heads * head_dim;
     const int ntiles = (rows + kConvRowsPerTile - 1) / kConvRowsPerTile;
@@ -162,11 +204,11 @@ hipError_t launch_conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w
     if (head_dim == 128) {
         hipLaunchKernelGGL(conv_silu_l2_kernel<128>, grid, dim3(kConvThreads), 0, stream, x, ldx,
                            w, conv_state, conv_snap, rows, heads, ntiles, eps_l2, y, ldy, q32,
-                           k32, v32);
+                           k32, v32, write_state);
     } else {
         hipLaunchKernelGGL(conv_silu_l2_kernel<16>, grid, dim3(kConvThreads), 0, stream, x, ldx,
                            w, conv_state, conv_snap, rows, heads, ntiles, eps_l2, y, ldy, q32,
-                           k32, v32);
+                           k32, v32, write_state);
     }
     return hipGetLastError();
 }

@@ -14,7 +14,13 @@ hipError_t launch_conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w
                                uint16_t *const *conv_state, uint16_t *const *conv_snap,
                                int n_seq, int rows, int heads, int head_dim, float eps_l2,
                                uint16_t *y, int64_t ldy, float *q32, float *k32, float *v32,
-                               hipStream_t stream);
+                               hipStream_t stream, bool write_state = true);
+
+// Move each conv window past the first n_accept[b] of its K pre-conv rows x
+// (sequence-major [B*K] rows): the write-on-accept fold of the conv state.
+hipError_t launch_conv_fold(const uint16_t *x, int64_t ldx, uint16_t *const *conv_state,
+                            const int32_t *n_accept, int B, int K, int heads, int head_dim,
+                            hipStream_t stream);
 
 hipError_t launch_kda_gate(const uint16_t *g_raw, int64_t ldg, const uint16_t *b_raw,
                            int64_t ldb, const float *a_log, const float *dt_bias, int T,

@@ -445,6 +445,33 @@ int kda_block_decode_k(const uint16_t *hidden, const kda_block_weights *w,
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kda_block_verify_k / kda_block_fold_accepted — write-on-accept form of
+ * kda_block_decode_k ("Glm5NextLayer" page, LayerWriteOnAccept: verify
+ * without writing the layer's states, then gdn_fold_accepted folds the
+ * accepted rows of each sequence into them).
+ * kda_block_verify_k: arguments as kda_block_decode_k without snapshots;
+ *   every stage buffer and out are bitwise those of kda_block_decode_k; the
+ *   recurrent states and conv states are read, never written.
+ * kda_block_fold_accepted: buf must hold the verify's stage buffers (its
+ *   qkv_proj, conv_out, gate and beta rows are what the fold reads);
+ *   n_accept device int32 [B], each clamped to [0, K].  Afterwards *state[b]
+ *   and *conv_state[b] are bitwise the recurrent and conv snapshots
+ *   kda_block_decode_k would have written after row n_accept[b]-1 (its final
+ *   states for n_accept[b] == K); n_accept[b] == 0 leaves both untouched.
+ *   Two launches; no output.  Errors as kda_block_decode_k.
+ * ------------------------------------------------------------------------ */
+int kda_block_verify_k(const uint16_t *hidden, const kda_block_weights *w,
+                       float *const *state, uint16_t *const *conv_state,
+                       const kda_block_decode_buffers *buf, uint16_t *out, int32_t B,
+                       int32_t K, int32_t hidden_size, int32_t heads, int32_t head_dim,
+                       int32_t rank, float scale, float eps_l2, float eps_rms,
+                       hipStream_t stream);
+
+int kda_block_fold_accepted(const kda_block_decode_buffers *buf, float *const *state,
+                            uint16_t *const *conv_state, const int32_t *n_accept, int32_t B,
+                            int32_t K, int32_t heads, int32_t head_dim, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * kda_block_decode — one token for each of B sequences through the whole
  * block ("Glm5NextKdaLayer" page, decode: single-token decode carrying both
  * states, result in out, states updated in place).  Exactly

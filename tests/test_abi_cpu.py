@@ -308,3 +308,24 @@ def test_prefill_split_validation(lib):
     assert call(cap_state=0) == E_NULL
     assert call(cap_state=Dp + 64) == E_ALIAS                  # over the state
     assert call(cap_state=E + 256) == E_ALIAS                  # over the workspace
+
+
+def test_block_write_on_accept_validation(lib):
+    w, _ = _block_args(lib)
+    b = _decode_bufs()
+    ref = ctypes.byref
+    assert lib.kda_block_verify_k(63 << 36, ref(w), 60 << 36, 61 << 36, ref(b), 62 << 36, 3, 0,
+                                  64, 2, 16, 32, 0.25, 1e-6, 1e-5, None) == OK
+    assert lib.kda_block_verify_k(63 << 36, ref(w), 60 << 36, 61 << 36, ref(b), 62 << 36, 3, 4,
+                                  64, 2, 64, 32, 0.25, 1e-6, 1e-5, None) == E_UNSUP
+    assert lib.kda_block_verify_k(63 << 36, ref(w), 60 << 36, 61 << 36, ref(b), w.q_proj, 3, 4,
+                                  64, 2, 16, 32, 0.25, 1e-6, 1e-5, None) == E_ALIAS
+    assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 64 << 36, 0, 4, 2, 16,
+                                       None) == OK
+    assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 64 << 36, 3, 4, 2, 64,
+                                       None) == E_UNSUP
+    assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 0, 3, 4, 2, 16, None) == E_NULL
+    assert lib.kda_block_fold_accepted(None, 60 << 36, 61 << 36, 64 << 36, 3, 4, 2, 16,
+                                       None) == E_NULL
+    assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 64 << 36, 3, -1, 2, 16,
+                                       None) == E_SHAPE

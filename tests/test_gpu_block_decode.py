@@ -212,3 +212,53 @@ def test_block_decode_k_full_size(orc):
         np.testing.assert_array_equal(got[n], ser[n], err_msg=n)
     for n in STAGES + ("final_out",):
         assert np.all(np.isfinite(got[n])), n
+
+
+@pytest.mark.parametrize("B,K,H,D,hidden,rank", [
+    (7, 4, 2, 16, 128, 32),
+    (6, 4, 2, 128, 256, 32),
+    (1, 4, 32, 128, 4096, 128),
+])
+def test_block_write_on_accept_equals_snapshots(B, K, H, D, hidden, rank):
+    """Block verify then fold ("Glm5NextLayer" page, write-on-accept): the
+    verify's stage buffers and output are bitwise those of kda_block_decode_k
+    and no state is written; folding n_accept rows leaves the recurrent and
+    conv states bitwise equal to decode_k's snapshots after that row (the
+    carried states for 0, decode_k's final states for K; out-of-range counts
+    clamp)."""
+    x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1701 + B, w_std=0.05 if hidden < 4096 else 0.02)
+    scale = D ** -0.5
+    ref = _gpu_decode_k(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)
+    dev = torch.device("cuda")
+    wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+    states = [torch.from_numpy(np.ascontiguousarray(S0[b])).to(dev) for b in range(B)]
+    convs = [conv0[b].to(dev).contiguous() for b in range(B)]
+    st_tab, cv_tab = kda.ptr_table(states), kda.ptr_table(convs)
+    buf = kda.block_decode_buffers(B * K, heads=H, head_dim=D, rank=rank, device=dev)
+    out = torch.empty(B * K, hidden, dtype=torch.bfloat16, device=dev)
+    say("block verify_k", B, K, hidden, H, D, rank)
+    kda.kda_block_verify_k(x.to(dev).contiguous(), wd, st_tab, cv_tab, buf, out, B=B, K=K,
+                           hidden_size=hidden, heads=H, head_dim=D, rank=rank, scale=scale)
+    torch.cuda.synchronize()
+    for n in STAGES:
+        np.testing.assert_array_equal(buf[n].float().cpu().numpy(), ref[n], err_msg=n)
+    np.testing.assert_array_equal(out.float().cpu().numpy(), ref["final_out"])
+    for b in range(B):
+        np.testing.assert_array_equal(states[b].cpu().numpy(), S0[b])
+        np.testing.assert_array_equal(convs[b].float().cpu().numpy(), conv0[b].float().numpy())
+    na = np.array([(b % (K + 3)) - 1 for b in range(B)], np.int32) if B > 1 else np.array([2], np.int32)
+    say("block fold_accepted", B, K, list(na))
+    kda.kda_block_fold_accepted(buf, st_tab, cv_tab, torch.from_numpy(na).cuda(), B=B, K=K,
+                                heads=H, head_dim=D)
+    torch.cuda.synchronize()
+    for b in range(B):
+        n = min(max(int(na[b]), 0), K)
+        if n == 0:
+            want_s, want_c = S0[b], conv0[b].float().numpy()
+        elif n == K:
+            want_s, want_c = ref["state"][b], ref["conv_state"][b]
+        else:
+            want_s, want_c = ref["state_snaps"][b, n - 1], ref["conv_snaps"][b, n - 1]
+        np.testing.assert_array_equal(states[b].cpu().numpy(), want_s, err_msg=f"seq {b} state")
+        np.testing.assert_array_equal(convs[b].float().cpu().numpy(), want_c,
+                                      err_msg=f"seq {b} conv state")

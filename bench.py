@@ -476,6 +476,15 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
         S = sets[i % n_sets]
         kda.dense_gemv_bf16_batchm(S["x"], S["wqkv"], y, M=K, N=3 * qkv, Kd=hidden)
 
+    na = torch.full((1,), K - 1, dtype=torch.int32, device=dev)
+
+    def woa(i):   # write-on-accept: verify (no state writes), then fold K-1 rows
+        S = sets[i % n_sets]
+        kda.kda_block_verify_k(S["x"], S["w"], S["tab"], S["ctab"], buf_k, out, B=1, K=K,
+                               hidden_size=hidden, heads=H, head_dim=D, rank=rank,
+                               scale=D ** -0.5)
+        kda.kda_block_fold_accepted(buf_k, S["tab"], S["ctab"], na, B=1, K=K, heads=H, head_dim=D)
+
     def timed(fn):
         for i in range(2 * n_sets):
             fn(i)
@@ -488,14 +497,14 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in es])) * 1e-3
 
-    t_v, t_d, t_g = timed(verify), timed(decode), timed(gemv)
+    t_v, t_d, t_g, t_w = timed(verify), timed(decode), timed(gemv), timed(woa)
     w_bytes = 2 * (3 * qkv * hidden + 2 * rank * hidden + H * hidden + 2 * qkv * rank
                    + hidden * qkv)
     g_bytes = 2 * (3 * qkv * hidden + K * hidden + K * 3 * qkv)
     return dict(config=f"block decode, 1 sequence, K={K} verify rows, hidden={hidden}, "
                        f"heads={H}, head_dim={D}, rank={rank}, bf16 weights ~N(0,0.02), "
                        f"{n_sets} layers rotated (weights from HBM)",
-                verify_ms=t_v * 1e3, decode_ms=t_d * 1e3,
+                verify_ms=t_v * 1e3, decode_ms=t_d * 1e3, write_on_accept_ms=t_w * 1e3,
                 verify_tokens_per_s=K / t_v, decode_tokens_per_s=1.0 / t_d,
                 speedup_vs_serial=K * t_d / t_v, weight_bytes=w_bytes,
                 verify_weight_GBps=w_bytes / t_v / 1e9,

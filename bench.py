@@ -498,6 +498,28 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
         return float(np.median([a.elapsed_time(b) for a, b in es])) * 1e-3
 
     t_v, t_d, t_g, t_w = timed(verify), timed(decode), timed(gemv), timed(woa)
+
+    # the same calls captured once per layer in a HIP graph and replayed (the
+    # seven launches of a call are enqueued back to back without host gaps)
+    def graphs_of(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(n_sets):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gs = []
+        for i in range(n_sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn(i)
+            gs.append(g)
+        return gs
+
+    gv, gd = graphs_of(verify), graphs_of(decode)
+    t_gv = timed(lambda i: gv[i % n_sets].replay())
+    t_gd = timed(lambda i: gd[i % n_sets].replay())
     w_bytes = 2 * (3 * qkv * hidden + 2 * rank * hidden + H * hidden + 2 * qkv * rank
                    + hidden * qkv)
     g_bytes = 2 * (3 * qkv * hidden + K * hidden + K * 3 * qkv)
@@ -505,6 +527,8 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
                        f"heads={H}, head_dim={D}, rank={rank}, bf16 weights ~N(0,0.02), "
                        f"{n_sets} layers rotated (weights from HBM)",
                 verify_ms=t_v * 1e3, decode_ms=t_d * 1e3, write_on_accept_ms=t_w * 1e3,
+                graph_verify_ms=t_gv * 1e3, graph_decode_ms=t_gd * 1e3,
+                graph_speedup_vs_serial=K * t_gd / t_gv,
                 verify_tokens_per_s=K / t_v, decode_tokens_per_s=1.0 / t_d,
                 speedup_vs_serial=K * t_d / t_v, weight_bytes=w_bytes,
                 verify_weight_GBps=w_bytes / t_v / 1e9,

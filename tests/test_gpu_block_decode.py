@@ -262,3 +262,61 @@ def test_block_write_on_accept_equals_snapshots(B, K, H, D, hidden, rank):
         np.testing.assert_array_equal(states[b].cpu().numpy(), want_s, err_msg=f"seq {b} state")
         np.testing.assert_array_equal(convs[b].float().cpu().numpy(), want_c,
                                       err_msg=f"seq {b} conv state")
+
+
+def test_block_decode_k_graph_replay_matches_eager():
+    """The block verify (seven stream-ordered launches, no allocation, no
+    memset, no synchronisation) captured once in a HIP graph and replayed
+    several times, with eager work and synchronisation between replays: every
+    replay equals the eager call bit for bit (output, states, snapshots)."""
+    B, K, H, D, hidden, rank = 2, 4, 2, 128, 256, 32
+    x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1801)
+    scale = D ** -0.5
+    ref = _gpu_decode_k(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)
+    dev = torch.device("cuda")
+    wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+    xg = x.to(dev).contiguous()
+    S0g = torch.from_numpy(np.ascontiguousarray(S0)).to(dev)
+    C0g = conv0.to(dev).contiguous()
+    states = [torch.empty(H, D, D, device=dev) for _ in range(B)]
+    convs = [torch.empty(4, 3 * H * D, dtype=torch.bfloat16, device=dev) for _ in range(B)]
+    snaps = [torch.empty(H, D, D, device=dev) for _ in range(B * (K - 1))]
+    csnaps = [torch.empty(4, 3 * H * D, dtype=torch.bfloat16, device=dev) for _ in range(B * (K - 1))]
+    tabs = [kda.ptr_table(t) for t in (states, convs, snaps, csnaps)]
+    buf = kda.block_decode_buffers(B * K, heads=H, head_dim=D, rank=rank, device=dev)
+    out = torch.empty(B * K, hidden, dtype=torch.bfloat16, device=dev)
+
+    def reset():
+        for b in range(B):
+            states[b].copy_(S0g[b])
+            convs[b].copy_(C0g[b])
+
+    def call():
+        kda.kda_block_decode_k(xg, wd, tabs[0], tabs[1], buf, out, B=B, K=K, hidden_size=hidden,
+                               heads=H, head_dim=D, rank=rank, scale=scale, snap=tabs[2],
+                               conv_snap=tabs[3])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        reset()
+        call()                      # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say("graph capture block decode_k", B, K)
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(4):
+        reset()                     # eager work between replays
+        out.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.float().cpu().numpy(), ref["final_out"], err_msg=f"replay {rep}")
+        got_s = np.stack([s.cpu().numpy() for s in states])
+        np.testing.assert_array_equal(got_s, ref["state"], err_msg=f"replay {rep} state")
+        got_sn = np.stack([s.cpu().numpy() for s in snaps]).reshape(B, K - 1, H, D, D)
+        np.testing.assert_array_equal(got_sn, ref["state_snaps"], err_msg=f"replay {rep} snaps")
+        got_c = np.stack([c.float().cpu().numpy() for c in convs])
+        np.testing.assert_array_equal(got_c, ref["conv_state"], err_msg=f"replay {rep} conv")

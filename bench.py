@@ -335,6 +335,10 @@ def bench_block(kda, dev, reps=10):
     x, w = workloads.block_raw(Tb, hidden, H, D, rank, 4, workloads.SEED_INPUT + 4)
     x = x.to(dev)
     wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+    # q, k, v projection weights packed back to back, as a serving engine
+    # stores them (the block then runs them as one GEMM)
+    wqkv = torch.cat([wd["q_proj"], wd["k_proj"], wd["v_proj"]]).contiguous()
+    wd["q_proj"], wd["k_proj"], wd["v_proj"] = wqkv[:qkv], wqkv[qkv:2 * qkv], wqkv[2 * qkv:]
     st = torch.zeros(H, D, D, device=dev)
     cs = torch.zeros(1, 4, 3 * qkv, dtype=torch.bfloat16, device=dev)
     ctab = kda.ptr_table(cs)

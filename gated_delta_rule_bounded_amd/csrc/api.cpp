@@ -508,11 +508,22 @@ int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float 
         return (int)KDA_OK;
     };
     int rc;
-    // q|k|v projections straight into the packed pre-conv rows
-    if ((rc = gemm("q", hidden, hidden_size, w->q_proj, b->qkv_proj, cd, (int)qkv, hidden_size)) ||
-        (rc = gemm("k", hidden, hidden_size, w->k_proj, b->qkv_proj + qkv, cd, (int)qkv, hidden_size)) ||
-        (rc = gemm("v", hidden, hidden_size, w->v_proj, b->qkv_proj + 2 * qkv, cd, (int)qkv, hidden_size)))
+    // q|k|v projections straight into the packed pre-conv rows; weights that
+    // lie back to back ([q_proj; k_proj; v_proj] as one [3*qkv, hidden]
+    // matrix, as a serving engine packs them) run as one wider GEMM
+    const size_t wsz = (size_t)qkv * hidden_size;
+    if (w->k_proj == w->q_proj + wsz && w->v_proj == w->k_proj + wsz) {
+        if ((rc = gemm("qkv", hidden, hidden_size, w->q_proj, b->qkv_proj, cd, (int)cd,
+                       hidden_size)))
+            return rc;
+    } else if ((rc = gemm("q", hidden, hidden_size, w->q_proj, b->qkv_proj, cd, (int)qkv,
+                          hidden_size)) ||
+               (rc = gemm("k", hidden, hidden_size, w->k_proj, b->qkv_proj + qkv, cd, (int)qkv,
+                          hidden_size)) ||
+               (rc = gemm("v", hidden, hidden_size, w->v_proj, b->qkv_proj + 2 * qkv, cd,
+                          (int)qkv, hidden_size))) {
         return rc;
+    }
     if ((rc = hip_status(kda::launch_conv_silu_l2(b->qkv_proj, cd, w->conv, conv_state, nullptr, 1,
                                                   T, heads, head_dim, eps_l2, b->conv_out, cd,
                                                   b->q32, b->k32, b->v32, stream),

@@ -26,9 +26,13 @@ STAGES = ("qkv_proj", "conv_out", "fa", "g_raw", "b_raw", "gate", "beta", "core"
           "out_gate", "o_norm_out")
 
 
-def run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale):
+def run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=False):
     dev = torch.device("cuda")
     wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+    if packed:   # q, k, v weights back to back: the block runs them as one GEMM
+        qkv = H * D
+        wqkv = torch.cat([wd["q_proj"], wd["k_proj"], wd["v_proj"]]).contiguous()
+        wd["q_proj"], wd["k_proj"], wd["v_proj"] = wqkv[:qkv], wqkv[qkv:2 * qkv], wqkv[2 * qkv:]
     xg = x[:T].to(dev).contiguous()
     st = torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).to(dev)
     cs = conv0.to(dev).contiguous()
@@ -59,16 +63,17 @@ def compare(got, ref, T, H, D, names):
         assert e < TOL, f"{n}: relerr {e:.3e}"
 
 
-@pytest.mark.parametrize("T,T_pad,H,D,hidden,rank,C", [
-    (50, 64, 2, 16, 64, 16, 16),
-    (200, 256, 2, 128, 256, 32, 64),
+@pytest.mark.parametrize("T,T_pad,H,D,hidden,rank,C,packed", [
+    (50, 64, 2, 16, 64, 16, 16, False),
+    (200, 256, 2, 128, 256, 32, 64, False),
+    (200, 256, 2, 128, 256, 32, 64, True),
 ])
-def test_block_small_against_oracle(orc, T, T_pad, H, D, hidden, rank, C):
+def test_block_small_against_oracle(orc, T, T_pad, H, D, hidden, rank, C, packed):
     x, w = workloads.block_raw(T, hidden, H, D, rank, 4, 1004, w_std=0.05)
     S0 = workloads.state(H, D, 0.05, 2004)
     conv0 = workloads.conv_raw(1, H, D, 4, 3004)["state"][0]
     scale = D ** -0.5
-    got = run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale)
+    got = run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=packed)
     ref = run_oracle(orc, x, w, T, H, D, S0, conv0, scale)
     compare(got, ref, T, H, D, STAGES + ("final_out",))
     assert relerr(got["state"], ref["state"]) < TOL
@@ -84,7 +89,7 @@ def test_block_full_size_causal_prefix(orc):
     S0 = np.zeros((H, D, D), dtype=np.float32)
     conv0 = torch.zeros(4, 3 * H * D, dtype=torch.bfloat16)
     scale = D ** -0.5
-    got = run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale)
+    got = run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=True)
     ref = run_oracle(orc, x, w, Tp, H, D, S0, conv0, scale)
     compare(got, ref, Tp, H, D, STAGES + ("final_out",))
     for n in STAGES + ("final_out",):

@@ -540,6 +540,26 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
                           GBps=g_bytes / t_g / 1e9, hbm_frac=g_bytes / t_g / PEAK_HBM))
 
 
+def measured_copy_bw(dev, nbytes=1 << 30, reps=20):
+    """HBM bandwidth torch's device copy reaches on this GPU (read + write
+    bytes per second, median of reps)."""
+    src = torch.empty(nbytes // 4, device=dev)
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    es = [(ev(), ev()) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in es:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    t = float(np.median([a.elapsed_time(b) for a, b in es])) * 1e-3
+    del src, dst
+    return 2 * nbytes / t
+
+
 def cpu_baseline(raw, threads, min_seconds=10.0):
     """The fp64 oracle, as it stands, on the full prefill workload, repeated
     until about min_seconds of CPU time have passed."""
@@ -674,6 +694,9 @@ def main():
     traffic = TRAFFIC_BYTES.get(dom)
     if traffic is not None:
         roofline["traffic"] = traffic
+    # context beside the datasheet peak: what a plain torch device copy
+    # reaches here (not a ceiling: the decode kernel streams faster)
+    roofline["torch_copy_GBps"] = measured_copy_bw(dev) / 1e9
 
     out = {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,

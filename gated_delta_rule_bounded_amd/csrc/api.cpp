@@ -33,6 +33,9 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool head_dim_ok(int d) { return d == 16 || d == 128; }
 
+// largest grid extent along y and z of a launch
+constexpr int64_t kMaxGridYZ = 65535;
+
 // [lo, hi) byte ranges overlap
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
     if (!a || !b || na == 0 || nb == 0) return false;
@@ -52,7 +55,7 @@ int conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w,
                  uint16_t *y, int64_t ldy, float *q32, float *k32, float *v32,
                  hipStream_t stream)
 {
-    if (n_seq < 0 || rows < 0 || heads <= 0)
+    if (n_seq < 0 || rows < 0 || heads <= 0 || n_seq > kMaxGridYZ || (rows + 15) / 16 > kMaxGridYZ)
         return fail(KDA_ERR_SHAPE, "conv_silu_l2: n_seq=%d rows=%d heads=%d", n_seq, rows, heads);
     if (!head_dim_ok(head_dim) || kc != 4)
         return fail(KDA_ERR_UNSUPPORTED, "conv_silu_l2: head_dim=%d kc=%d (need 16|128, 4)",
@@ -319,7 +322,8 @@ int kda_decode(const uint16_t *qkv, int64_t ldqkv, const float *gate, const floa
                float *const *state, float *core, int32_t B, int32_t heads, int32_t head_dim,
                float scale, hipStream_t stream)
 {
-    if (B < 0 || heads <= 0) return fail(KDA_ERR_SHAPE, "kda_decode: B=%d heads=%d", B, heads);
+    if (B < 0 || heads <= 0 || B > kMaxGridYZ)
+        return fail(KDA_ERR_SHAPE, "kda_decode: B=%d heads=%d", B, heads);
     if (!head_dim_ok(head_dim))
         return fail(KDA_ERR_UNSUPPORTED, "kda_decode: head_dim=%d", head_dim);
     if (B == 0) return ok();
@@ -334,7 +338,7 @@ int kda_decode_k(const uint16_t *qkv, int64_t ldqkv, const float *gate, const fl
                  float *const *state, float *const *snap, float *core, int32_t B, int32_t K,
                  int32_t heads, int32_t head_dim, float scale, hipStream_t stream)
 {
-    if (B < 0 || K < 0 || heads <= 0)
+    if (B < 0 || K < 0 || heads <= 0 || B > kMaxGridYZ)
         return fail(KDA_ERR_SHAPE, "kda_decode_k: B=%d K=%d heads=%d", B, K, heads);
     if (!head_dim_ok(head_dim))
         return fail(KDA_ERR_UNSUPPORTED, "kda_decode_k: head_dim=%d", head_dim);
@@ -356,7 +360,7 @@ int kda_verify_k(const uint16_t *qkv, int64_t ldqkv, const float *gate, const fl
                  float *const *state, float *core, int32_t B, int32_t K, int32_t heads,
                  int32_t head_dim, float scale, hipStream_t stream)
 {
-    if (B < 0 || K < 0 || heads <= 0)
+    if (B < 0 || K < 0 || heads <= 0 || B > kMaxGridYZ)
         return fail(KDA_ERR_SHAPE, "kda_verify_k: B=%d K=%d heads=%d", B, K, heads);
     if (!head_dim_ok(head_dim))
         return fail(KDA_ERR_UNSUPPORTED, "kda_verify_k: head_dim=%d", head_dim);
@@ -375,7 +379,7 @@ int kda_fold_accepted(const uint16_t *qkv, int64_t ldqkv, const float *gate, con
                       float *const *state, const int32_t *n_accept, int32_t B, int32_t K,
                       int32_t heads, int32_t head_dim, hipStream_t stream)
 {
-    if (B < 0 || K < 0 || heads <= 0)
+    if (B < 0 || K < 0 || heads <= 0 || B > kMaxGridYZ)
         return fail(KDA_ERR_SHAPE, "kda_fold_accepted: B=%d K=%d heads=%d", B, K, heads);
     if (!head_dim_ok(head_dim))
         return fail(KDA_ERR_UNSUPPORTED, "kda_fold_accepted: head_dim=%d", head_dim);
@@ -558,7 +562,7 @@ int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float 
 int dense_gemv_bf16_batchm(const uint16_t *x, int64_t ldx, const uint16_t *w, int32_t M,
                            int32_t N, int32_t Kd, uint16_t *y, int64_t ldy, hipStream_t stream)
 {
-    if (M < 0 || N <= 0 || Kd <= 0 || Kd % 32 || M > (1 << 24))
+    if (M < 0 || N <= 0 || Kd <= 0 || Kd % 32 || M > kMaxGridYZ * 64)
         return fail(KDA_ERR_SHAPE, "dense_gemv_bf16_batchm: M=%d N=%d Kd=%d (Kd %% 32 == 0)", M,
                     N, Kd);
     if (M == 0) return ok();
@@ -591,7 +595,8 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
         return fail(KDA_ERR_UNSUPPORTED, "kda_block_decode_k: head_dim=%d", head_dim);
     const int64_t qkv = (int64_t)heads * head_dim, cd = 3 * qkv;
     if (B < 0 || K < 0 || heads <= 0 || hidden_size <= 0 || rank <= 0 || hidden_size % 32 ||
-        rank % 32 || qkv % 32 || (int64_t)B * K > (1 << 24) || hidden_size > (1 << 22) ||
+        rank % 32 || qkv % 32 || (int64_t)B * K > kMaxGridYZ * 64 || B > kMaxGridYZ ||
+        hidden_size > (1 << 22) ||
         rank > (1 << 22) || qkv > (1 << 22))
         return fail(KDA_ERR_SHAPE, "kda_block_decode_k: B=%d K=%d hidden=%d heads=%d rank=%d", B,
                     K, hidden_size, heads, rank);
@@ -727,7 +732,7 @@ int kda_block_fold_accepted(const kda_block_decode_buffers *b, float *const *sta
                             uint16_t *const *conv_state, const int32_t *n_accept, int32_t B,
                             int32_t K, int32_t heads, int32_t head_dim, hipStream_t stream)
 {
-    if (B < 0 || K < 0 || heads <= 0 || (int64_t)B * K > (1 << 24))
+    if (B < 0 || K < 0 || heads <= 0 || (int64_t)B * K > (1 << 24) || B > kMaxGridYZ)
         return fail(KDA_ERR_SHAPE, "kda_block_fold_accepted: B=%d K=%d heads=%d", B, K, heads);
     if (!head_dim_ok(head_dim))
         return fail(KDA_ERR_UNSUPPORTED, "kda_block_fold_accepted: head_dim=%d", head_dim);

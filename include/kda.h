@@ -23,6 +23,9 @@
  */
 #ifndef KDA_H
 #define KDA_H
+/* Launch-grid limits, reported as KDA_ERR_SHAPE: a batch B of sequences
+ * (decode paths, conv n_seq, block decode) at most 65535, and at most
+ * 65535 x 16 rows per sequence in conv_silu_l2. */
 
 #include <stddef.h>
 #include <stdint.h>
@@ -387,8 +390,8 @@ int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float 
  *   y  bf16 [M, N] (row stride ldy): y[m][n] = bf16(sum_k x[m][k] w[n][k]),
  *      fp32 accumulation in an order fixed by (n, k) alone — not by M, not by
  *      the row's position among the M rows.  Rounding to nearest, ties to even.
- * Kd % 32 == 0, ldx % 8 == 0, ldx <= 2^22, N >= 1; x, w, y 16-byte aligned
- * (KDA_ERR_SHAPE).  y must not overlap x or w (KDA_ERR_ALIAS).  M == 0 is a
+ * Kd % 32 == 0, ldx % 8 == 0, ldx <= 2^22, N >= 1, M <= 65535 * 64; x, w, y
+ * 16-byte aligned (KDA_ERR_SHAPE).  y must not overlap x or w (KDA_ERR_ALIAS).  M == 0 is a
  * no-op.  Meant for small M (up to a few hundred rows); each 64 rows re-read
  * the weights.
  * ------------------------------------------------------------------------ */

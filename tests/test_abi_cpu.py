@@ -329,3 +329,14 @@ def test_block_write_on_accept_validation(lib):
                                        None) == E_NULL
     assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 64 << 36, 3, -1, 2, 16,
                                        None) == E_SHAPE
+
+
+def test_grid_limits_are_shape_errors(lib):
+    # batches past the launch grid's y extent are refused before any launch
+    assert lib.kda_decode(A, 96, B, C, Dp, E, 70000, 2, 16, 0.25, None) == E_SHAPE
+    assert lib.kda_decode_k(A, 96, B, C, Dp, 0, E, 70000, 2, 2, 16, 0.25, None) == E_SHAPE
+    assert lib.kda_verify_k(A, 96, B, C, Dp, E, 70000, 2, 2, 16, 0.25, None) == E_SHAPE
+    assert lib.kda_fold_accepted(A, 96, B, C, Dp, E, 70000, 2, 2, 16, None) == E_SHAPE
+    assert lib.conv_silu_l2(A, 96, B, None, None, 70000, 1, 2, 16, 4, 1e-6, C, 96,
+                            None, None, None, None) == E_SHAPE
+    assert lib.dense_gemv_bf16_batchm(A, 256, B, 65535 * 64 + 1, 48, 256, C, 48, None) == E_SHAPE

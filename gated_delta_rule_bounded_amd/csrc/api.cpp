@@ -666,10 +666,13 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
         {hidden, w->v_proj, b->qkv_proj + 2 * qkv, hs, cd, qk, hs},
         {hidden, w->f_a, b->fa, hs, rk, rk, hs},
         {hidden, w->g_a, b->ga, hs, rk, rk, hs},
-        {hidden, w->b_proj, b->b_raw, hs, heads, heads, hs},
+        // b_proj with beta = sigmoid(b_raw) fused into its epilogue
+        {hidden, w->b_proj, b->b_raw, hs, heads, heads, hs, kda::kEpiBeta, b->beta},
     };
     const kda::GemvSeg mid[] = {
-        {b->fa, w->f_b, b->g_raw, rk, qkv, qk, rk},
+        // f_b with the log-decay gate fused into its epilogue
+        {b->fa, w->f_b, b->g_raw, rk, qkv, qk, rk, kda::kEpiGate, b->gate, w->a_log, w->dt_bias,
+         head_dim},
         {b->ga, w->g_b, b->out_gate, rk, qkv, qk, rk},
     };
     const kda::GemvSeg back[] = {{b->o_norm_out, w->o_proj, out, qkv, hs, hs, qk}};
@@ -683,10 +686,6 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
                                                   heads, head_dim, eps_l2, b->conv_out, cd,
                                                   nullptr, nullptr, nullptr, stream, !verify),
                          "kda_block_decode_k: conv_silu_l2 launch")) ||
-        (rc = hip_status(kda::launch_kda_gate(b->g_raw, qkv, b->b_raw, heads, w->a_log,
-                                              w->dt_bias, Mi, heads, head_dim, b->gate, b->beta,
-                                              stream),
-                         "kda_block_decode_k: kda_gate launch")) ||
         (rc = hip_status(verify ? kda::launch_kda_verify(b->conv_out, cd, b->gate, b->beta,
                                                          state, b->core, B, K, heads, head_dim,
                                                          scale, stream)

@@ -48,6 +48,26 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
     return 1.0f / (1.0f + exp2_fast(-x * kLog2e));
 }
 
+// softplus(z) = log(1 + e^z), with e^z and log on the transcendental unit:
+// log1p(y) is taken as log(u) * y / (u - 1), u = 1 + y (exact for the
+// rounding of u, so small y keeps its relative accuracy; u == 1 means
+// log1p(y) = y to within rounding); z > 20 returns z as the pages' threshold.
+__device__ __forceinline__ float softplus_fast(float z) {
+    const float y = exp2_fast(z * kLog2e);
+    const float u = 1.0f + y;
+    const float l1p = u == 1.0f ? y : __builtin_amdgcn_logf(u) * 0.69314718055994531f * (y / (u - 1.0f));
+    return z > 20.0f ? z : l1p;
+}
+
+// The bounded log-decay of one channel ("Glm5NextKdaWeights" page, a_log per
+// head and dt_bias per channel): g = -exp(a_log) * softplus(x + dt_bias),
+// with rate = exp(a_log) from decay_rate.  kda_gate and the projection
+// epilogue of the block decode both form it here.
+__device__ __forceinline__ float decay_rate(float a_log) { return exp2_fast(a_log * kLog2e); }
+__device__ __forceinline__ float log_decay(float x, float dt_bias, float rate) {
+    return -rate * softplus_fast(x + dt_bias);
+}
+
 // 16x16x4 fp32 MFMA: D[m][n] = sum_k A[m][k] B[k][n] + C[m][n].
 // Lane l supplies A[l%16][l/16] and B[l/16][l%16]; on return lane l holds
 // D[4*(l/16) + i][l%16] in element i.

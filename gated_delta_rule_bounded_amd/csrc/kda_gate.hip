@@ -14,17 +14,6 @@ namespace kda {
 
 constexpr int kGateThreads = 256;
 
-// softplus(z) = log(1 + e^z), with e^z and log on the transcendental unit:
-// log1p(y) is taken as log(u) * y / (u - 1), u = 1 + y (exact for the
-// rounding of u, so small y keeps its relative accuracy; u == 1 means
-// log1p(y) = y to within rounding); z > 20 returns z as the pages' threshold.
-__device__ __forceinline__ float softplus_fast(float z) {
-    const float y = exp2_fast(z * kLog2e);
-    const float u = 1.0f + y;
-    const float l1p = u == 1.0f ? y : __builtin_amdgcn_logf(u) * 0.69314718055994531f * (y / (u - 1.0f));
-    return z > 20.0f ? z : l1p;
-}
-
 // Grid (rows, channel groups of 8 per row / kGateThreads): no integer
 // division on the way to the element; blocks with blockIdx.x >= T compute
 // beta, kGateThreads * gridDim.y elements of the [T, H] array each.
@@ -44,10 +33,10 @@ __global__ __launch_bounds__(kGateThreads) void kda_gate_kernel(
         const float4 b0 = *reinterpret_cast<const float4 *>(dt_bias + c0);
         const float4 b1 = *reinterpret_cast<const float4 *>(dt_bias + c0 + 4);
         const float bias[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        const float A = exp2_fast(a_log[h] * kLog2e);
+        const float A = decay_rate(a_log[h]);
         float g[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) g[e] = -A * softplus_fast(x[e] + bias[e]);
+        for (int e = 0; e < 8; ++e) g[e] = log_decay(x[e], bias[e], A);
         float4 *dst = reinterpret_cast<float4 *>(gate + (int64_t)row * qkv + c0);
         dst[0] = make_float4(g[0], g[1], g[2], g[3]);
         dst[1] = make_float4(g[4], g[5], g[6], g[7]);

@@ -37,7 +37,22 @@ struct Seg {
     int64_t ldx, ldy;
     int32_t N, Kd;
     int32_t tile0;  // first column tile of this segment in the grid
+    int32_t epi, head_dim;
+    float *act;
+    const float *a_log, *dt_bias;
 };
+
+// Store one result: its bf16 rounding, and the segment's activation of it.
+__device__ __forceinline__ void store_out(const Seg &g, int m, int n, float v)
+{
+    const uint32_t u = f32_to_bf16(v);
+    g.y[(int64_t)m * g.ldy + n] = (uint16_t)u;
+    if (g.epi == kEpiGate)
+        g.act[(int64_t)m * g.N + n] =
+            log_decay(bf16_to_f32(u), g.dt_bias[n], decay_rate(g.a_log[n / g.head_dim]));
+    else if (g.epi == kEpiBeta)
+        g.act[(int64_t)m * g.N + n] = sigmoid_fast(bf16_to_f32(u));
+}
 
 struct Args {
     Seg seg[kGemvMaxSegs];
@@ -189,7 +204,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
             if (m < a.M) {
                 const float v = ((part[0][t][tr][tc] + part[1][t][tr][tc]) + part[2][t][tr][tc]) +
                                 part[3][t][tr][tc];
-                g.y[(int64_t)m * g.ldy + n0 + tc] = (uint16_t)f32_to_bf16(v);
+                store_out(g, m, n0 + tc, v);
             }
         }
     }
@@ -203,8 +218,10 @@ hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStre
     Args a = {};
     int tiles = 0;
     for (int i = 0; i < nseg; ++i) {
-        a.seg[i] = Seg{segs[i].x, segs[i].w, segs[i].y, segs[i].ldx, segs[i].ldy,
-                       segs[i].N, segs[i].Kd, tiles};
+        a.seg[i] = Seg{segs[i].x,     segs[i].w,        segs[i].y,   segs[i].ldx,
+                       segs[i].ldy,   segs[i].N,        segs[i].Kd,  tiles,
+                       segs[i].epi,   segs[i].head_dim, segs[i].act, segs[i].a_log,
+                       segs[i].dt_bias};
         tiles += (segs[i].N + kColTile - 1) / kColTile;
     }
     a.nseg = nseg;

@@ -82,12 +82,22 @@ hipError_t launch_kda_prefill_varlen(const float *q, const float *k, const float
 // 16-byte aligned.  Each output element's accumulation order depends on
 // neither M nor the row's position.
 constexpr int kGemvMaxSegs = 6;
+// Epilogue of a segment: the bf16 result only, or also the fp32 activation
+// the KDA stages take from it — the log-decay gate (from g_raw, with a_log
+// per head of head_dim channels and dt_bias per channel) or beta =
+// sigmoid(b_raw) — written to act[m * N + n], exactly as kda_gate forms
+// them from the same bf16 values.
+enum GemvEpi : int32_t { kEpiNone = 0, kEpiGate = 1, kEpiBeta = 2 };
 struct GemvSeg {
     const uint16_t *x;
     const uint16_t *w;
     uint16_t *y;
     int64_t ldx, ldy;
     int32_t N, Kd;
+    int32_t epi = kEpiNone;
+    float *act = nullptr;
+    const float *a_log = nullptr, *dt_bias = nullptr;
+    int32_t head_dim = 0;
 };
 hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStream_t stream);
 

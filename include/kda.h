@@ -408,10 +408,11 @@ int dense_gemv_bf16_batchm(const uint16_t *x, int64_t ldx, const uint16_t *w,
  * Per row, the stages of kda_block_prefill:
  *
  *   qkv_proj   = [h q_proj^T | h k_proj^T | h v_proj^T]   dense_gemv_bf16_batchm
- *   fa = h f_a^T, ga = h g_a^T, b_raw = h b_proj^T        (same launch)
+ *   fa = h f_a^T, ga = h g_a^T, b_raw = h b_proj^T        (same launch;
+ *                beta = sigmoid(b_raw) formed as b_raw is stored)
  *   g_raw = fa f_b^T, out_gate = ga g_b^T                  dense_gemv_bf16_batchm
+ *                (gate = kda_gate's log-decay of g_raw formed as it is stored)
  *   conv_out   = conv_silu_l2 row by row from *conv_state[b] (updated)
- *   gate, beta = kda_gate(g_raw, b_raw, a_log, dt_bias)
  *   core       = kda_decode_k(conv_out, gate, beta) from *state[b] (updated)
  *   o_norm_out = gated_rmsnorm(core, out_gate, o_norm)
  *   out        = o_norm_out o_proj^T                       dense_gemv_bf16_batchm
@@ -430,7 +431,7 @@ int dense_gemv_bf16_batchm(const uint16_t *x, int64_t ldx, const uint16_t *w,
  * weights must be pairwise disjoint where one of them is written
  * (KDA_ERR_ALIAS); the per-sequence states are reached through the tables
  * and must be distinct, with snapshots disjoint from them.  B == 0 or K == 0
- * is a no-op.  Allocates nothing; seven launches on `stream`.
+ * is a no-op.  Allocates nothing; six launches on `stream`.
  * ------------------------------------------------------------------------ */
 typedef struct kda_block_decode_buffers {
     uint16_t *qkv_proj, *conv_out;

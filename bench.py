@@ -504,7 +504,7 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
     t_v, t_d, t_g, t_w = timed(verify), timed(decode), timed(gemv), timed(woa)
 
     # the same calls captured once per layer in a HIP graph and replayed (the
-    # seven launches of a call are enqueued back to back without host gaps)
+    # six launches of a call are enqueued back to back without host gaps)
     def graphs_of(fn):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())

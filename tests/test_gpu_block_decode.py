@@ -265,7 +265,7 @@ def test_block_write_on_accept_equals_snapshots(B, K, H, D, hidden, rank):
 
 
 def test_block_decode_k_graph_replay_matches_eager():
-    """The block verify (seven stream-ordered launches, no allocation, no
+    """The block verify (six stream-ordered launches, no allocation, no
     memset, no synchronisation) captured once in a HIP graph and replayed
     several times, with eager work and synchronisation between replays: every
     replay equals the eager call bit for bit (output, states, snapshots)."""

@@ -739,6 +739,8 @@ int kda_block_fold_accepted(const kda_block_decode_buffers *b, float *const *sta
     if (!b || !state || !conv_state || !n_accept || !b->qkv_proj || !b->conv_out || !b->gate ||
         !b->beta)
         return fail(KDA_ERR_NULL, "kda_block_fold_accepted: null pointer argument");
+    if (!aligned16(b->qkv_proj) || !aligned16(b->conv_out) || !aligned16(b->gate))
+        return fail(KDA_ERR_SHAPE, "kda_block_fold_accepted: misaligned buffer");
     const int64_t cd = 3LL * heads * head_dim;
     int rc;
     if ((rc = hip_status(kda::launch_kda_fold(b->conv_out, cd, b->gate, b->beta, state, n_accept,

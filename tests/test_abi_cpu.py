@@ -340,3 +340,10 @@ def test_grid_limits_are_shape_errors(lib):
     assert lib.conv_silu_l2(A, 96, B, None, None, 70000, 1, 2, 16, 4, 1e-6, C, 96,
                             None, None, None, None) == E_SHAPE
     assert lib.dense_gemv_bf16_batchm(A, 256, B, 65535 * 64 + 1, 48, 256, C, 48, None) == E_SHAPE
+
+
+def test_block_fold_alignment(lib):
+    b = _decode_bufs()
+    b.conv_out += 2
+    assert lib.kda_block_fold_accepted(ctypes.byref(b), 60 << 36, 61 << 36, 64 << 36, 3, 4, 2, 16,
+                                       None) == E_SHAPE

@@ -11,16 +11,26 @@ with HIP events between the kernels.
 
 Also reported on the same JSON line (measured after the timed steps):
   decode    B=256 sequences x 64 steps, state [256,32,128,128] fp32: state
-            read+write bytes / median step time (the metric's second half);
-  decode_k  B=64, K=4 with 3 snapshots per sequence (conv decode-K + kda_decode_k);
+            read+write bytes / median step time (the metric's second half),
+            with the counted HBM traffic of a step;
+  decode_k  B=64, K=4 with 3 snapshots per sequence (conv decode-K +
+            kda_decode_k), and the write-on-accept pair kda_verify_k +
+            kda_fold_accepted on the same rows;
   stages    conv_silu_l2 / kda_gate / gated_rmsnorm at T=8192 (block shapes);
   block     the full KDA block (kda_block_prefill) at T=8192, hidden 4096:
             tokens/s, each stage kernel alone, and the projections' share;
+  prefill_varlen  the 4096 tokens as 8 x 512 and 64 x 64 prompts in one
+            kda_prefill_varlen call;
+  block_decode  the block for one sequence: K=4 verify vs one token, the
+            write-on-accept pair, HIP-graph replays, and the projection
+            kernel's weight-read rate;
   roofline  for the dominant prefill kernel, from HIP events on the stream
-            the kernels run on;
+            the kernels run on, with its counted HBM traffic;
   cpu_baseline  the fp64 oracle on the same prefill workload, on host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       (--prefill-only, --decode-only, --block-only, --block-decode-only and
+       --calibrate-copy serve profiler runs)
 """
 import argparse
 import json

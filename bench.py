@@ -362,15 +362,14 @@ def bench_block(kda, dev, reps=10):
     stages = {
         "conv_silu_l2": lambda: kda.conv_silu_l2(buf["qkv_proj"], wd["conv"], buf["conv_out"],
                                                  n_seq=1, rows=Tb, heads=H, head_dim=D,
-                                                 conv_state=ctab, q32=buf["q32"], k32=buf["k32"],
-                                                 v32=buf["v32"]),
+                                                 conv_state=ctab),
         "kda_gate": lambda: kda.kda_gate(buf["g_raw"], wd["a_log"], wd["dt_bias"], buf["gate"],
                                          T=Tb, heads=H, head_dim=D, b_raw=buf["b_raw"],
                                          beta=buf["beta"]),
-        "kda_prefill": lambda: kda.kda_prefill(buf["q32"], buf["k32"], buf["v32"], buf["gate"],
-                                               buf["beta"], st, buf["core"], buf["prefill_ws"],
-                                               T=Tb, T_pad=Tb, heads=H, head_dim=D, chunk=C,
-                                               scale=D ** -0.5),
+        "kda_prefill": lambda: kda.kda_prefill_bf16(buf["conv_out"], buf["gate"], buf["beta"],
+                                                    st, buf["core"], buf["prefill_ws"], T=Tb,
+                                                    T_pad=Tb, heads=H, head_dim=D, chunk=C,
+                                                    scale=D ** -0.5),
         "gated_rmsnorm": lambda: kda.gated_rmsnorm(buf["core"].view(Tb, qkv), buf["out_gate"],
                                                    wd["o_norm"], buf["o_norm_out"], T=Tb, heads=H,
                                                    head_dim=D),

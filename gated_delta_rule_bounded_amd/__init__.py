@@ -24,7 +24,7 @@ __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_prepare",
            "kda_block_prefill", "block_buffers", "BLOCK_WEIGHT_NAMES",
            "dense_gemv_bf16_batchm", "kda_prefill_varlen", "varlen_chunks",
            "kda_verify_k", "kda_fold_accepted", "kda_prefill_split",
-           "kda_block_verify_k", "kda_block_fold_accepted", "kda_block_decode", "kda_block_decode_k",
+           "kda_block_verify_k", "kda_block_fold_accepted", "kda_prefill_bf16", "kda_block_decode", "kda_block_decode_k",
            "block_decode_buffers",
            "ptr_table", "KdaError",
            "last_error", "library_path"]
@@ -178,16 +178,20 @@ BLOCK_WEIGHT_NAMES = ("q_proj", "k_proj", "v_proj", "conv", "f_a", "f_b", "dt_bi
                       "b_proj", "g_a", "g_b", "o_norm", "o_proj")
 
 
-def block_buffers(T_pad, *, heads, head_dim, rank, chunk, device, gemm_ws_bytes=32 << 20):
+def block_buffers(T_pad, *, heads, head_dim, rank, chunk, device, gemm_ws_bytes=32 << 20,
+                  f32_copies=False):
     """Allocate the stage buffers of kda_block_prefill as torch tensors (a
-    dict keyed by the fields of struct kda_block_buffers)."""
+    dict keyed by the fields of struct kda_block_buffers); the optional fp32
+    copies q32/k32/v32 only with ``f32_copies``."""
     qkv = heads * head_dim
     bf, f = torch.bfloat16, torch.float32
     e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
     return dict(
         qkv_proj=e((T_pad, 3 * qkv), bf), conv_out=e((T_pad, 3 * qkv), bf),
-        q32=e((T_pad, heads, head_dim), f), k32=e((T_pad, heads, head_dim), f),
-        v32=e((T_pad, heads, head_dim), f), fa=e((T_pad, rank), bf), g_raw=e((T_pad, qkv), bf),
+        q32=e((T_pad, heads, head_dim), f) if f32_copies else None,
+        k32=e((T_pad, heads, head_dim), f) if f32_copies else None,
+        v32=e((T_pad, heads, head_dim), f) if f32_copies else None,
+        fa=e((T_pad, rank), bf), g_raw=e((T_pad, qkv), bf),
         b_raw=e((T_pad, heads), bf), gate=e((T_pad, heads, head_dim), f),
         beta=e((T_pad, heads), f), core=e((T_pad, heads, head_dim), f), ga=e((T_pad, rank), bf),
         out_gate=e((T_pad, qkv), bf), o_norm_out=e((T_pad, qkv), bf),
@@ -370,3 +374,14 @@ def kda_block_fold_accepted(buffers, state, conv_state, n_accept, *, B, K, heads
         ctypes.byref(bufs), _ptr(state, torch.int64, "state"),
         _ptr(conv_state, torch.int64, "conv_state"), _ptr(n_accept, torch.int32, "n_accept"), B,
         K, heads, head_dim, _stream()))
+
+
+def kda_prefill_bf16(qkv, gate, beta, state, core, workspace, *, T, T_pad, heads, head_dim, chunk,
+                     scale):
+    """kda_prefill reading q | k | v from bf16 rows (``qkv`` [T_pad, >= 3*H*D])."""
+    f = torch.float32
+    _check(_lib.lib.kda_prefill_bf16(
+        _ptr(qkv, torch.bfloat16, "qkv"), _rowstride(qkv, "qkv"), _ptr(gate, f, "gate"),
+        _ptr(beta, f, "beta"), _ptr(state, f, "state"), _ptr(core, f, "core"), T, T_pad, heads,
+        head_dim, chunk, float(scale), _ptr(workspace, None, "workspace"), workspace.numel(),
+        _stream()))

@@ -15,7 +15,8 @@ SYMBOLS = ("kda_last_error", "conv_silu_l2", "kda_gate", "kda_prefill_workspace_
            "kda_prefill_forward", "kda_decode", "kda_decode_k", "gated_rmsnorm",
            "kda_block_prefill", "dense_gemv_bf16_batchm", "kda_block_decode_k",
            "kda_block_decode", "kda_prefill_varlen", "kda_verify_k", "kda_fold_accepted",
-           "kda_prefill_split", "kda_block_verify_k", "kda_block_fold_accepted")
+           "kda_prefill_split", "kda_block_verify_k", "kda_block_fold_accepted",
+           "kda_prefill_bf16")
 
 
 class BlockWeights(ctypes.Structure):
@@ -81,6 +82,9 @@ def _load():
     lib.kda_block_prefill.restype = ctypes.c_int
     lib.kda_block_prefill.argtypes = [P, ctypes.POINTER(BlockWeights), P, P,
                                       ctypes.POINTER(BlockBuffers), P] + [i32] * 7 + [f32] * 3 + [P]
+    lib.kda_prefill_bf16.restype = ctypes.c_int
+    lib.kda_prefill_bf16.argtypes = [P, i64, P, P, P, P, i32, i32, i32, i32, i32, f32, P,
+                                     ctypes.c_size_t, P]
     lib.kda_prefill_split.restype = ctypes.c_int
     lib.kda_prefill_split.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32,
                                       P, ctypes.c_size_t, P]

@@ -179,6 +179,42 @@ int kda_prefill(const float *q, const float *k, const float *v, const float *gat
                       "kda_prefill launch");
 }
 
+int kda_prefill_bf16(const uint16_t *qkv, int64_t ldqkv, const float *gate, const float *beta,
+                     float *state, float *core, int32_t T, int32_t T_pad, int32_t heads,
+                     int32_t head_dim, int32_t chunk, float scale, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream)
+{
+    if (!head_dim_ok(head_dim) || !(chunk == 16 || chunk == 64))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill_bf16: head_dim=%d chunk=%d", head_dim,
+                    chunk);
+    if (T < 0 || heads <= 0 || T_pad < T || T_pad % chunk)
+        return fail(KDA_ERR_SHAPE, "kda_prefill_bf16: T=%d T_pad=%d heads=%d chunk=%d", T, T_pad,
+                    heads, chunk);
+    if (T == 0) return ok();
+    if (!qkv || !gate || !beta || !state || !core || !workspace)
+        return fail(KDA_ERR_NULL, "kda_prefill_bf16: null pointer argument");
+    const int64_t qw = (int64_t)heads * head_dim;
+    if (ldqkv < 3 * qw || ldqkv % 4)
+        return fail(KDA_ERR_SHAPE, "kda_prefill_bf16: ldqkv=%lld", (long long)ldqkv);
+    const size_t need = kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "kda_prefill_bf16: workspace %zu bytes < %zu needed",
+                    workspace_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(qkv) & 7u) || !aligned16(gate) || !aligned16(state) ||
+        !aligned16(core) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(KDA_ERR_SHAPE, "kda_prefill_bf16: misaligned pointer");
+    const size_t rows_b = (size_t)T_pad * qw * 4, st_b = (size_t)heads * head_dim * head_dim * 4;
+    const size_t qkv_b = (size_t)((T_pad - 1) * ldqkv + 3 * qw) * 2;
+    if (overlap(core, rows_b, qkv, qkv_b) || overlap(core, rows_b, gate, rows_b) ||
+        overlap(core, rows_b, beta, (size_t)T_pad * heads * 4) || overlap(core, rows_b, state, st_b) ||
+        overlap(state, st_b, qkv, qkv_b) || overlap(state, st_b, gate, rows_b) ||
+        overlap(workspace, need, core, rows_b) || overlap(workspace, need, state, st_b))
+        return fail(KDA_ERR_ALIAS, "kda_prefill_bf16: core, state or workspace overlaps");
+    return hip_status(kda::launch_kda_prefill_bf16(qkv, ldqkv, gate, beta, state, core, T, heads,
+                                                   head_dim, chunk, scale, workspace, stream),
+                      "kda_prefill_bf16 launch");
+}
+
 int kda_prefill_split(const float *q, const float *k, const float *v, const float *gate,
                       const float *beta, float *state, float *core, float *cap_state,
                       int32_t T, int32_t cap, int32_t T_pad, int32_t heads, int32_t head_dim,
@@ -439,13 +475,18 @@ int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float 
         return fail(KDA_ERR_NULL, "kda_block_prefill: null pointer argument");
     const void *wp[] = {w->q_proj, w->k_proj, w->v_proj, w->conv, w->f_a, w->f_b, w->dt_bias,
                         w->a_log, w->b_proj, w->g_a, w->g_b, w->o_norm, w->o_proj};
-    const void *bp[] = {b->qkv_proj, b->conv_out, b->q32, b->k32, b->v32, b->fa, b->g_raw,
-                        b->b_raw, b->gate, b->beta, b->core, b->ga, b->out_gate,
-                        b->o_norm_out, b->prefill_ws};
+    const void *bp[] = {b->qkv_proj, b->conv_out, b->fa, b->g_raw, b->b_raw, b->gate, b->beta,
+                        b->core, b->ga, b->out_gate, b->o_norm_out, b->prefill_ws};
     for (const void *p : wp)
         if (!p) return fail(KDA_ERR_NULL, "kda_block_prefill: a weight pointer is NULL");
     for (const void *p : bp)
         if (!p) return fail(KDA_ERR_NULL, "kda_block_prefill: a buffer pointer is NULL");
+    // the fp32 copies of q, k, v are optional outputs: all three or none
+    const bool copies = b->q32 || b->k32 || b->v32;
+    if (copies && !(b->q32 && b->k32 && b->v32))
+        return fail(KDA_ERR_NULL, "kda_block_prefill: q32, k32, v32 must all be given or all NULL");
+    if (copies && (!aligned16(b->q32) || !aligned16(b->k32) || !aligned16(b->v32)))
+        return fail(KDA_ERR_SHAPE, "kda_block_prefill: misaligned fp32 copy");
     if (!b->gemm_ws && b->gemm_ws_bytes)
         return fail(KDA_ERR_NULL, "kda_block_prefill: gemm_ws is NULL with gemm_ws_bytes > 0");
     const size_t need = kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
@@ -541,9 +582,11 @@ int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float 
                                               T, heads, head_dim, b->gate, b->beta, stream),
                          "kda_block_prefill: kda_gate launch")))
         return rc;
-    if ((rc = hip_status(kda::launch_kda_prefill(b->q32, b->k32, b->v32, b->gate, b->beta, state,
-                                                 b->core, T, heads, head_dim, chunk, scale,
-                                                 b->prefill_ws, stream),
+    // the core reads q | k | v straight from the bf16 conv output (the fp32
+    // copies, when asked for, are its exact widening)
+    if ((rc = hip_status(kda::launch_kda_prefill_bf16(b->conv_out, cd, b->gate, b->beta, state,
+                                                      b->core, T, heads, head_dim, chunk, scale,
+                                                      b->prefill_ws, stream),
                          "kda_block_prefill: kda_prefill launch")))
         return rc;
     if ((rc = gemm("g_a", hidden, hidden_size, w->g_a, b->ga, rank, rank, hidden_size)) ||

@@ -65,6 +65,14 @@ hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
                               float *core, int T, int heads, int head_dim, int chunk,
                               float scale, void *workspace, hipStream_t stream);
 
+// kda_prefill reading q | k | v directly from bf16 rows [T_pad, ldqkv] (the
+// conv output; q at column 0, k at heads*head_dim, v at 2*heads*head_dim):
+// bitwise the result of kda_prefill on their exact fp32 widening.
+hipError_t launch_kda_prefill_bf16(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                                   const float *beta, float *state, float *core, int T,
+                                   int heads, int head_dim, int chunk, float scale,
+                                   void *workspace, hipStream_t stream);
+
 // Several sequences back to back (rows [cu[s], cu[s+1]) of sequence s), one
 // state pointer each; one prepare and one walk for all of them.  total_chunks
 // = sum over sequences of ceil(len / chunk) operand blocks in the workspace;

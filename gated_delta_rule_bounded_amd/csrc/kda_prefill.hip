@@ -135,23 +135,57 @@ __device__ __forceinline__ float4 exp2_4(const float4 &a) {
 }
 __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 
-// Load this lane's A-layout slice of chunk row (channels 16*t8 + 4*lg .. +3
-// for every tile t8) of k, q and the gate.  The loads are unconditional: a
-// chunk never extends past T_pad rows, so every row it touches is in bounds;
-// rows past T are replaced afterwards by select_rows.  Keeping the loads free
-// of branches and arithmetic lets them stay in flight across other work.
-template <int D>
-__device__ __forceinline__ void load_rows(const float *__restrict__ q, const float *__restrict__ k,
-                                          const float *__restrict__ gate, int64_t roff, int lg,
-                                          float4 (&K)[D / 16], float4 (&Q)[D / 16],
-                                          float4 (&G)[D / 16])
+// Where the prepare kernels read q, k and v.  BF = false: fp32 arrays
+// [rows, H, D] (the core entry points; ld = H * D).  BF = true: the bf16 conv
+// output rows [rows, ld] holding q | k | v sections (the block prefill), read
+// directly: the widening to fp32 is exact, so either source gives the same
+// bits.  gate and beta are always fp32 [rows, H, D] / [rows, H].
+template <bool BF>
+struct QkvSrc {
+    const void *q, *k, *v;
+    int64_t ld;   // elements per row
+    __device__ __forceinline__ float4 load4(const void *base, int64_t row, int64_t col) const {
+        if constexpr (BF) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(
+                static_cast<const uint16_t *>(base) + row * ld + col);
+            return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+        } else {
+            return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + row * ld + col);
+        }
+    }
+    __device__ __forceinline__ float load1(const void *base, int64_t row, int64_t col) const {
+        if constexpr (BF)
+            return bf16_to_f32(static_cast<const uint16_t *>(base)[row * ld + col]);
+        else
+            return static_cast<const float *>(base)[row * ld + col];
+    }
+    __device__ __forceinline__ void advance(int64_t rows) {   // move every section down
+        const int64_t e = rows * ld * (BF ? 2 : 4);
+        q = static_cast<const char *>(q) + e;
+        k = static_cast<const char *>(k) + e;
+        v = static_cast<const char *>(v) + e;
+    }
+};
+
+// This lane's A-layout slice of chunk row tg (channels 16*t8 + 4*lg .. +3 of
+// head h, every tile t8) of k, q and the gate, from either source.  The loads
+// are unconditional: a chunk never extends past the rows that exist, and rows
+// past T are replaced afterwards by select_rows.  Keeping the loads free of
+// branches and arithmetic lets them stay in flight across other work.
+template <int D, bool BF>
+__device__ __forceinline__ void load_rows_src(const QkvSrc<BF> &src, const float *__restrict__ gate,
+                                              int64_t tg, int h, int H, int lg,
+                                              float4 (&K)[D / 16], float4 (&Q)[D / 16],
+                                              float4 (&G)[D / 16])
 {
+    const int64_t goff = (tg * H + h) * D;
 #pragma unroll
     for (int t8 = 0; t8 < D / 16; ++t8) {
         const int d0 = 16 * t8 + 4 * lg;
-        K[t8] = *reinterpret_cast<const float4 *>(k + roff + d0);
-        Q[t8] = *reinterpret_cast<const float4 *>(q + roff + d0);
-        G[t8] = *reinterpret_cast<const float4 *>(gate + roff + d0);
+        K[t8] = src.load4(src.k, tg, (int64_t)h * D + d0);
+        Q[t8] = src.load4(src.q, tg, (int64_t)h * D + d0);
+        G[t8] = *reinterpret_cast<const float4 *>(gate + goff + d0);
     }
 }
 
@@ -360,10 +394,9 @@ __device__ __forceinline__ void invert_unit_lower(const float (*__restrict__ s_M
 // kda_chunk_prep: one workgroup per (chunk n, head h), all chunks in parallel;
 // fp32 fragments and fp32 MFMA, for the shapes without a split form.
 // ---------------------------------------------------------------------------
-template <int D, int C>
+template <int D, int C, bool BF>
 __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
-    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
+    QkvSrc<BF> src, const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
     float *__restrict__ ws, const Varlen vl)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
@@ -376,7 +409,8 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
         if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
         nblk -= vl.seg_lo;
         const int64_t r0 = sp.row0 * H;
-        q += r0 * D, k += r0 * D, v += r0 * D, gate += r0 * D, beta += r0;
+        src.advance(sp.row0);
+        gate += r0 * D, beta += r0;
         T = sp.T;
         tmax = vl.rows - 1 - sp.row0;
     }
@@ -386,7 +420,6 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     const int rl = 16 * w + lr;
     const int64_t tg = min((int64_t)n * C + rl, tmax);   // rows past T are replaced
     const bool valid = (int64_t)n * C + rl < T;
-    const int64_t roff = (tg * H + h) * D;
     float *__restrict__ blk = ws + (nblk * H + h) * B::kSize;
 
     __shared__ __align__(16) float s_tot[NW * D];
@@ -399,7 +432,7 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     // e^{G_C} and Kd = K e^{G_C - G} are formed right after the scan, K e^G
     // goes to LDS right after the A/P products, v is loaded only for U'.
     float4 K[DT], Q[DT], G[DT], Kd[DT];
-    load_rows<D>(q, k, gate, roff, lg, K, Q, G);
+    load_rows_src<D, BF>(src, gate, tg, h, H, lg, K, Q, G);
     const float braw = beta[tg * H + h];
     select_rows<D>(valid, K, Q, G);
     if (lg == 0) s_beta[rl] = valid ? braw : 0.f;
@@ -479,21 +512,24 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
         if (!diag_ok) {
             // sum_d x_r[d] k_s[d] e^{G_r[d] - G_s[d]} for one (r, s) of this
             // block, with x = k (A) or q (P); rows past T contribute zero
-            auto pair = [&](int r, int sc, const float *__restrict__ x) {
+            auto pair = [&](int r, int sc, const void *x) {
                 float acc = 0.f;
                 const int64_t tr = (int64_t)n * C + r, ts = (int64_t)n * C + sc;
                 if (sc <= r && tr < T && ts < T) {
-                    const float *xr = x + (tr * H + h) * D, *ks = k + (ts * H + h) * D;
+                    const int64_t c0 = (int64_t)h * D;
                     for (int d = 0; d < D; ++d)
-                        acc = __builtin_fmaf(xr[d], ks[d] * exp2_fast(s_kc[r][d] - s_kc[sc][d]), acc);
+                        acc = __builtin_fmaf(src.load1(x, tr, c0 + d),
+                                             src.load1(src.k, ts, c0 + d) *
+                                                 exp2_fast(s_kc[r][d] - s_kc[sc][d]),
+                                             acc);
                 }
                 return acc;
             };
             float da[4], dp[4];
 #pragma unroll
             for (int vv = 0; vv < 4; ++vv) {
-                da[vv] = pair(16 * w + 4 * lg + vv, 16 * w + lr, k);   // A tile layout
-                dp[vv] = pair(16 * w + lr, 16 * w + 4 * lg + vv, q);   // P^T tile layout
+                da[vv] = pair(16 * w + 4 * lg + vv, 16 * w + lr, src.k);   // A tile layout
+                dp[vv] = pair(16 * w + lr, 16 * w + 4 * lg + vv, src.q);   // P^T tile layout
             }
 #pragma unroll
             for (int bj = 0; bj < NW; ++bj)
@@ -577,7 +613,7 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
         if (pass == 0) {   // next right operand: V
 #pragma unroll
             for (int t8 = 0; t8 < DT; ++t8) {
-                const float4 vv = *reinterpret_cast<const float4 *>(v + roff + 16 * t8 + 4 * lg);
+                const float4 vv = src.load4(src.v, tg, (int64_t)h * D + 16 * t8 + 4 * lg);
                 *reinterpret_cast<float4 *>(&s_kc[rl][16 * t8 + 4 * lg]) = valid ? vv : zero4();
             }
         } else {           // then Kd, to be transposed into its fragments
@@ -628,10 +664,9 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
 // ---------------------------------------------------------------------------
 constexpr float kBlockSpanLog2 = 96.0f;
 
-template <int D, int C>
+template <int D, int C, bool BF>
 __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep_split_kernel(
-    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
+    QkvSrc<BF> src, const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
     float *__restrict__ ws, const Varlen vl)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
@@ -646,7 +681,8 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
         if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
         nblk -= vl.seg_lo;
         const int64_t r0 = sp.row0 * H;
-        q += r0 * D, k += r0 * D, v += r0 * D, gate += r0 * D, beta += r0;
+        src.advance(sp.row0);
+        gate += r0 * D, beta += r0;
         T = sp.T;
         tmax = vl.rows - 1 - sp.row0;
     }
@@ -655,7 +691,6 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     const int rl = 16 * w + lr;
     const int64_t tg = min((int64_t)n * C + rl, tmax);   // rows past T are replaced
     const bool valid = (int64_t)n * C + rl < T;
-    const int64_t roff = (tg * H + h) * D;
     float *__restrict__ blk = ws + (nblk * H + h) * B::kSize;
 
     __shared__ __align__(16) float s_tot[NW * D];
@@ -673,7 +708,7 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     __shared__ __align__(16) float s_tab[2 * NW + NW * (NW - 1) / 2 + 1][D];
 
     float4 K[DT], Q[DT], G[DT];
-    load_rows<D>(q, k, gate, roff, lg, K, Q, G);
+    load_rows_src<D, BF>(src, gate, tg, h, H, lg, K, Q, G);
     const float braw = beta[tg * H + h];
     if ((int64_t)(n + 1) * C <= T) {   // a whole chunk (uniform): no row to replace
 #pragma unroll
@@ -850,13 +885,16 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     } else {
         // sum_d x_r[d] k_s[d] e^{G_r[d] - G_s[d]} for one (r, s) of the chunk,
         // x = k (A) or q (P); rows past T contribute zero
-        auto pair = [&](int r, int sc, const float *__restrict__ x) {
+        auto pair = [&](int r, int sc, const void *x) {
             float acc = 0.f;
             const int64_t tr = (int64_t)n * C + r, ts = (int64_t)n * C + sc;
             if (sc <= r && tr < T && ts < T) {
-                const float *xr = x + (tr * H + h) * D, *ks = k + (ts * H + h) * D;
+                const int64_t c0 = (int64_t)h * D;
                 for (int d = 0; d < D; ++d)
-                    acc = __builtin_fmaf(xr[d], ks[d] * exp2_fast(s_x[r][d] - s_x[sc][d]), acc);
+                    acc = __builtin_fmaf(src.load1(x, tr, c0 + d),
+                                         src.load1(src.k, ts, c0 + d) *
+                                             exp2_fast(s_x[r][d] - s_x[sc][d]),
+                                         acc);
             }
             return acc;
         };
@@ -865,8 +903,8 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
             if (bj > w) continue;
 #pragma unroll
             for (int vv = 0; vv < 4; ++vv) {
-                Aacc[bj][vv] = pair(16 * w + 4 * lg + vv, 16 * bj + lr, k);
-                Pacc[bj][vv] = pair(16 * w + lr, 16 * bj + 4 * lg + vv, q);
+                Aacc[bj][vv] = pair(16 * w + 4 * lg + vv, 16 * bj + lr, src.k);
+                Pacc[bj][vv] = pair(16 * w + lr, 16 * bj + 4 * lg + vv, src.q);
             }
         }
     }
@@ -895,7 +933,7 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     // V now, for the U' pass (its latency hidden behind the inversion and W)
     float4 Vr[DT];
 #pragma unroll
-    for (int t8 = 0; t8 < DT; ++t8) Vr[t8] = *reinterpret_cast<const float4 *>(v + roff + 16 * t8 + 4 * lg);
+    for (int t8 = 0; t8 < DT; ++t8) Vr[t8] = src.load4(src.v, tg, (int64_t)h * D + 16 * t8 + 4 * lg);
 #pragma unroll
     for (int t8 = 0; t8 < DT; ++t8) put_T(t8, Kg[t8]);   // (K e^G)^T, right operand of W
 
@@ -1463,21 +1501,40 @@ int prefill_segment_chunks(int T, int heads, int head_dim, int chunk)
     return (NC + nseg - 1) / nseg;
 }
 
+template <int D, int C, bool BF>
+static hipError_t prepare_src(const QkvSrc<BF> &src, const float *gate, const float *beta, int T,
+                              int H, void *workspace, const Varlen &vl, int B, hipStream_t stream)
+{
+    const dim3 grid = vl.cu ? dim3(vl.max_chunks, H, B) : dim3((T + C - 1) / C, H);
+    if constexpr (Blk<D, C>::kSplit)
+        hipLaunchKernelGGL((kda_chunk_prep_split_kernel<D, C, BF>), grid,
+                           dim3(PrefCfg<D, C>::kThreads), 0, stream, src, gate, beta, T, H,
+                           static_cast<float *>(workspace), vl);
+    else
+        hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C, BF>), grid,
+                           dim3(PrefCfg<D, C>::kThreads), 0, stream, src, gate, beta, T, H,
+                           static_cast<float *>(workspace), vl);
+    return hipGetLastError();
+}
+
 template <int D, int C>
 static hipError_t prepare_t(const float *q, const float *k, const float *v, const float *gate,
                             const float *beta, int T, int H, void *workspace, const Varlen &vl,
                             int B, hipStream_t stream)
 {
-    const dim3 grid = vl.cu ? dim3(vl.max_chunks, H, B) : dim3((T + C - 1) / C, H);
-    if constexpr (Blk<D, C>::kSplit)
-        hipLaunchKernelGGL((kda_chunk_prep_split_kernel<D, C>), grid,
-                           dim3(PrefCfg<D, C>::kThreads), 0, stream, q, k, v, gate, beta, T, H,
-                           static_cast<float *>(workspace), vl);
-    else
-        hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C>), grid,
-                           dim3(PrefCfg<D, C>::kThreads), 0, stream, q, k, v, gate, beta, T, H,
-                           static_cast<float *>(workspace), vl);
-    return hipGetLastError();
+    const QkvSrc<false> src{q, k, v, (int64_t)H * D};
+    return prepare_src<D, C, false>(src, gate, beta, T, H, workspace, vl, B, stream);
+}
+
+// q | k | v read from bf16 rows (row stride ldqkv elements)
+template <int D, int C>
+static hipError_t prepare_bf16_t(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                                 const float *beta, int T, int H, void *workspace,
+                                 hipStream_t stream)
+{
+    const int64_t qw = (int64_t)H * D;
+    const QkvSrc<true> src{qkv, qkv + qw, qkv + 2 * qw, ldqkv};
+    return prepare_src<D, C, true>(src, gate, beta, T, H, workspace, Varlen{}, 1, stream);
 }
 
 template <int D, int C>
@@ -1539,6 +1596,29 @@ hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
         hipError_t e = launch_kda_prefill_prepare(q + r0 * HD, k + r0 * HD, v + r0 * HD,
                                                   gate + r0 * HD, beta + r0 * heads, Ts, heads,
                                                   head_dim, chunk, workspace, stream);
+        if (e != hipSuccess) return e;
+        e = launch_kda_prefill_forward(state, core + r0 * HD, Ts, heads, head_dim, chunk, scale,
+                                       workspace, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_kda_prefill_bf16(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                                   const float *beta, float *state, float *core, int T,
+                                   int heads, int head_dim, int chunk, float scale,
+                                   void *workspace, hipStream_t stream)
+{
+    // the segments of launch_kda_prefill, reading q | k | v from bf16 rows
+    const int NC = (T + chunk - 1) / chunk;
+    const int seg = prefill_segment_chunks(T, heads, head_dim, chunk);
+    const int64_t HD = (int64_t)heads * head_dim;
+    for (int c0 = 0; c0 < NC; c0 += seg) {
+        const int64_t r0 = (int64_t)c0 * chunk;
+        const int Ts = (int)std::min<int64_t>((int64_t)T - r0, (int64_t)seg * chunk);
+        hipError_t e = KDA_PREFILL_DISPATCH(prepare_bf16_t, qkv + r0 * ldqkv, ldqkv,
+                                            gate + r0 * HD, beta + r0 * heads, Ts, heads,
+                                            workspace, stream);
         if (e != hipSuccess) return e;
         e = launch_kda_prefill_forward(state, core + r0 * HD, Ts, heads, head_dim, chunk, scale,
                                        workspace, stream);

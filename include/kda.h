@@ -171,6 +171,24 @@ int kda_prefill_forward(float *state, float *core, int32_t T, int32_t T_pad,
                         size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kda_prefill_bf16 — kda_prefill reading q, k and v straight from the bf16
+ * conv output rows.  "Glm5NextKdaWorkspace" page: conv_out holds q | k | v
+ * in bf16 and the prefill's q_f32 copies are its exact widening, so reading
+ * conv_out directly gives bitwise the result of kda_prefill on those copies
+ * without writing or reading them.
+ *   qkv    bf16 [T_pad, ldqkv] rows: q at column 0, k at heads*head_dim, v at
+ *          2*heads*head_dim (ldqkv >= 3*heads*head_dim, ldqkv % 4 == 0,
+ *          8-byte aligned); rows >= T may hold anything.
+ *   gate, beta, state, core, workspace and every other argument: as
+ *   kda_prefill.
+ * ------------------------------------------------------------------------ */
+int kda_prefill_bf16(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                     const float *beta, float *state, float *core, int32_t T,
+                     int32_t T_pad, int32_t heads, int32_t head_dim, int32_t chunk,
+                     float scale, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * kda_prefill_split — one prefill pass split at row cap, with the state at
  * the split captured.  "Glm5NextLayer" page, supports_replay_tail_split: the
  * rows from cap on get exactly the bits a prefill starting at cap gives them
@@ -319,10 +337,11 @@ int gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate,
  *
  *   qkv_proj   = [h q_proj^T | h k_proj^T | h v_proj^T]     bf16 projections
  *   conv_out   = conv_silu_l2(qkv_proj) from *conv_state[0] (updated), plus
- *                its fp32 widening q32/k32/v32
+ *                its fp32 widening q32/k32/v32 when those buffers are given
  *   fa = h f_a^T, g_raw = fa f_b^T, b_raw = h b_proj^T      bf16 projections
  *   gate, beta = kda_gate(g_raw, b_raw, a_log, dt_bias)
- *   core       = kda_prefill(q32, k32, v32, gate, beta) from state (updated)
+ *   core       = kda_prefill_bf16(conv_out, gate, beta) from state (updated),
+ *                bitwise kda_prefill on the fp32 widening of conv_out
  *   ga = h g_a^T, out_gate = ga g_b^T                       bf16 projections
  *   o_norm_out = gated_rmsnorm(core, out_gate, o_norm)
  *   out        = o_norm_out o_proj^T                        bf16 [T, hidden]
@@ -340,8 +359,9 @@ int gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate,
  *   b_proj [heads, hidden]; o_norm [head_dim]; o_proj [hidden, heads*head_dim];
  *   a_log fp32 [heads]; dt_bias fp32 [heads*head_dim].
  * Buffers (device, caller-owned, rows beyond T left as they are):
- *   qkv_proj, conv_out bf16 [T_pad, 3*heads*head_dim]; q32, k32, v32, core,
- *   gate fp32 [T_pad, heads*head_dim]; beta fp32 [T_pad, heads];
+ *   qkv_proj, conv_out bf16 [T_pad, 3*heads*head_dim]; core, gate fp32
+ *   [T_pad, heads*head_dim]; q32, k32, v32 fp32 [T_pad, heads*head_dim] or
+ *   all three NULL (optional copies); beta fp32 [T_pad, heads];
  *   fa, ga bf16 [T_pad, rank]; g_raw, out_gate, o_norm_out bf16
  *   [T_pad, heads*head_dim]; b_raw bf16 [T_pad, heads];
  *   prefill_ws of at least kda_prefill_workspace_bytes(T_pad, ...) bytes.

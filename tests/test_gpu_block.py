@@ -26,7 +26,8 @@ STAGES = ("qkv_proj", "conv_out", "fa", "g_raw", "b_raw", "gate", "beta", "core"
           "out_gate", "o_norm_out")
 
 
-def run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=False):
+def run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=False,
+            f32_copies=False):
     dev = torch.device("cuda")
     wd = {n: t.to(dev).contiguous() for n, t in w.items()}
     if packed:   # q, k, v weights back to back: the block runs them as one GEMM
@@ -36,7 +37,8 @@ def run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=Fals
     xg = x[:T].to(dev).contiguous()
     st = torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).to(dev)
     cs = conv0.to(dev).contiguous()
-    buf = kda.block_buffers(T_pad, heads=H, head_dim=D, rank=rank, chunk=C, device=dev)
+    buf = kda.block_buffers(T_pad, heads=H, head_dim=D, rank=rank, chunk=C, device=dev,
+                            f32_copies=f32_copies)
     out = torch.empty(T, hidden, dtype=torch.bfloat16, device=dev)
     say("block", T, T_pad, hidden, H, D, rank, C)
     kda.kda_block_prefill(xg, wd, st, kda.ptr_table([cs]), buf, out, T=T, T_pad=T_pad,
@@ -47,6 +49,10 @@ def run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=Fals
     res["final_out"] = out.float().cpu().numpy()
     res["state"] = st.cpu().numpy()
     res["conv_state"] = cs.float().cpu().numpy()
+    if f32_copies:   # the optional fp32 copies are the exact widening of conv_out
+        co = buf["conv_out"][:T].float()
+        for i, n in enumerate(("q32", "k32", "v32")):
+            assert torch.equal(buf[n][:T].reshape(T, -1), co[:, i * H * D:(i + 1) * H * D]), n
     return res
 
 
@@ -73,7 +79,8 @@ def test_block_small_against_oracle(orc, T, T_pad, H, D, hidden, rank, C, packed
     S0 = workloads.state(H, D, 0.05, 2004)
     conv0 = workloads.conv_raw(1, H, D, 4, 3004)["state"][0]
     scale = D ** -0.5
-    got = run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=packed)
+    got = run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=packed,
+                  f32_copies=packed)
     ref = run_oracle(orc, x, w, T, H, D, S0, conv0, scale)
     compare(got, ref, T, H, D, STAGES + ("final_out",))
     assert relerr(got["state"], ref["state"]) < TOL

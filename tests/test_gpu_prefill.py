@@ -281,3 +281,39 @@ def test_prefill_split_captures_state_at_cap(T, cap, T_pad, C, D):
     if cap > 0:
         _, ref_cap = oracle_core(case, scale, T=cap)
         assert relerr(got_cap, ref_cap) < TOL
+
+
+@pytest.mark.parametrize("T,T_pad,C,D,gate_scale", [(57, 64, 16, 16, 1.0), (100, 128, 64, 16, 1.0),
+                                                    (77, 80, 16, 128, 1.0), (200, 256, 64, 128, 1.0),
+                                                    (130, 192, 64, 128, 40.0), (70, 80, 16, 128, 40.0),
+                                                    (4059, 4096, 64, 128, 1.0)])
+def test_prefill_bf16_rows_equal_fp32_widening_bitwise(T, T_pad, C, D, gate_scale):
+    """kda_prefill_bf16 reads q | k | v from bf16 rows (the conv output); on
+    the exact fp32 widening of the same rows kda_prefill gives the same bits.
+    Rows past T hold NaN in both; the row stride has 8 spare columns; a steep
+    gate sends chunks down the exact pairwise path, which reads the rows too."""
+    import gated_delta_rule_bounded_amd as kda
+    H = 32 if T > 1000 else 3
+    scale = D ** -0.5
+    case = core_case(T, H, D, 7300 + T, 0.05, qkv_bf16=True, gate_scale=gate_scale)
+    qw = H * D
+    rows = np.full((T_pad, 3 * qw + 8), np.nan, np.float32)
+    for i, n in enumerate(("q", "k", "v")):
+        rows[:T, i * qw:(i + 1) * qw] = case[n].reshape(T, qw)
+    qkv16 = torch.from_numpy(rows).to(torch.bfloat16).cuda()      # exact: values are bf16
+    assert torch.equal(qkv16.float().cpu()[:T, :3 * qw], torch.from_numpy(rows[:T, :3 * qw]))
+    g = cuda(pad_rows(case["gate"], T_pad, np.nan))
+    b = cuda(pad_rows(case["beta"], T_pad, np.nan))
+    st = cuda(case["S0"]).contiguous()
+    core = torch.full((T_pad, H, D), 7.0, device="cuda")
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(T_pad, H, D, C), dtype=torch.uint8,
+                     device="cuda")
+    say("prefill_bf16", T, T_pad, C, D, gate_scale)
+    kda.kda_prefill_bf16(qkv16, g, b, st, core, ws, T=T, T_pad=T_pad, heads=H, head_dim=D,
+                         chunk=C, scale=scale)
+    torch.cuda.synchronize()
+    ref_core, ref_S = gpu_prefill(case, T, T_pad, C, scale, fill=np.nan)
+    got = core.cpu().numpy()
+    np.testing.assert_array_equal(got[:T], ref_core[:T])
+    np.testing.assert_array_equal(st.cpu().numpy(), ref_S)
+    assert np.all(got[T:] == 7.0)

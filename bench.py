@@ -19,6 +19,8 @@ Also reported on the same JSON line (measured after the timed steps):
   stages    conv_silu_l2 / kda_gate / gated_rmsnorm at T=8192 (block shapes);
   block     the full KDA block (kda_block_prefill) at T=8192, hidden 4096:
             tokens/s, each stage kernel alone, and the projections' share;
+  prefill_bf16_rows  the same prefill with q|k|v as bf16 rows
+            (kda_prefill_bf16), checked bitwise against the fp32-input run;
   prefill_varlen  the 4096 tokens as 8 x 512 and 64 x 64 prompts in one
             kda_prefill_varlen call;
   block_decode  the block for one sequence: K=4 verify vs one token, the
@@ -153,6 +155,42 @@ def prefill_step_phases(kda, P, evs=None):
         kda.kda_prefill_forward(P["state"], core, P["ws"], scale=D ** -0.5, **kw)
         if evs is not None:
             evs[i][2].record()
+
+
+def bench_prefill_bf16(kda, dev, P, reps=200):
+    """The same prefill workload with q | k | v held as one bf16 [T, 3*H*D]
+    row buffer (the conv output's form; the workload's values are bf16, so
+    the fp32 arrays are their exact widening), run by kda_prefill_bf16.
+    Checked bitwise against kda_prefill from the same state first."""
+    qw = H * D
+    qkv16 = torch.cat([P[n].reshape(T, qw) for n in ("q", "k", "v")], 1).to(torch.bfloat16)
+    assert torch.equal(qkv16[:, :qw].float(), P["q"].reshape(T, qw))
+    S0 = torch.from_numpy(workloads.state(H, D, 0.05, workloads.SEED_STATE + 1)).to(dev)
+    st_a, st_b = S0.clone(), S0.clone()
+    core_a, core_b = torch.empty_like(P["core"]), torch.empty_like(P["core"])
+    kda.kda_prefill(P["q"], P["k"], P["v"], P["gate"], P["beta"], st_a, core_a, P["ws"], T=T,
+                    T_pad=T, heads=H, head_dim=D, chunk=C, scale=D ** -0.5)
+
+    def call(st, core):
+        kda.kda_prefill_bf16(qkv16, P["gate"], P["beta"], st, core, P["ws"], T=T, T_pad=T,
+                             heads=H, head_dim=D, chunk=C, scale=D ** -0.5)
+
+    call(st_b, core_b)
+    torch.cuda.synchronize()
+    bitwise = bool(torch.equal(core_a, core_b) and torch.equal(st_a, st_b))
+    for _ in range(20):
+        call(st_b, core_b)
+    a, b = ev(), ev()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        call(st_b, core_b)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / reps
+    return dict(config=f"prefill T={T}, heads={H}, head_dim={D}, chunk={C}, q|k|v as bf16 rows "
+                       "(kda_prefill_bf16)",
+                ms=t * 1e3, tokens_per_s=T / t, bitwise_equal_to_fp32_inputs=bitwise)
 
 
 def bench_decode(kda, dev, n_steps=64, n_inputs=8):
@@ -719,6 +757,10 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    log("prefill, bf16 q|k|v rows ...")
+    out["prefill_bf16_rows"] = bench_prefill_bf16(kda, dev, P)
+    log(f"prefill bf16 rows: {out['prefill_bf16_rows']['ms']:.4f} ms, bitwise "
+        f"{out['prefill_bf16_rows']['bitwise_equal_to_fp32_inputs']}")
     if not args.prefill_only:
         log("decode ...")
         out["decode"] = bench_decode(kda, dev)

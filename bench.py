@@ -749,7 +749,8 @@ def main():
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32 (products as 3 x bf16 MFMA, f32 accumulate)",
+        "dtype": "f32",
+        "matrix_products": "each fp32 product as 3 bf16 MFMA (hi*hi + hi*lo + lo*hi), f32 accumulate",
         "data": "synthetic",
         "config": {"workload": "chunked prefill core, 1 sequence, T=4096, heads=32, head_dim=128, "
                                "chunk=64, fp32 carried state ~N(0,0.05), q/k/v bf16-widened",

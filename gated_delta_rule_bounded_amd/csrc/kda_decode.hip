@@ -8,12 +8,11 @@
 // The second form of o needs one reduction pass over S instead of two; it is
 // the same quantity.
 //
-// Layout: one workgroup per (head, sequence).  The head's D x D fp32 state is
-// contiguous (64 KiB at D = 128); thread t owns the float4 column group
-// cg = t % (D/4) of rows rg + RG*r, so every load/store instruction of the
-// workgroup covers whole contiguous rows (128-bit accesses, fully coalesced).
-// Column sums over the key axis reduce within a wave by xor-shuffles, then
-// across waves through LDS, always in the same order.  The same kernel serves
+// Layout: one workgroup per (head, column slice, sequence).  The head's D x D
+// fp32 state is contiguous (64 KiB at D = 128); thread t owns the float4
+// column group cg = t % (DC/4) of its slice in rows rg + 16*r, so every
+// load/store instruction covers whole 128-byte row pieces (128-bit accesses).
+// Column sums over the key axis take a fixed tree (see RecCfg).  The same kernel serves
 // single-token decode (K = 1) and K-token decode, which makes the K-token
 // result bit-identical to K single-token calls: each step runs the same
 // instructions on the same values, and fp32 registers hold exactly what an
@@ -30,15 +29,24 @@
 
 namespace kda {
 
-template <int D>
+// One workgroup per (head, value-column slice, sequence).  The recurrence
+// never mixes value columns (column j of S evolves with its own u_j), so a
+// head's state splits into NS slices of D/NS columns with no exchange.  The
+// key-axis sums are formed in an order fixed by D alone — 16 row groups each
+// chain their D/16 rows (rows rg, rg + 16, ...), partner groups (2p, 2p + 1)
+// are added, and the 8 pair sums are added in order p = 0..7 — so every
+// slice count gives the same bits, and the launch picks the count from the
+// batch size: few sequences get more, smaller workgroups.
+template <int D, int NS>
 struct RecCfg {
-    static constexpr int kThreads = (D >= 128) ? 512 : 64;
-    static constexpr int kCG = D / 4;              // float4 column groups per row
-    static constexpr int kRG = kThreads / kCG;     // row groups
+    static constexpr int kRG = 16;                 // row groups
+    static constexpr int kDC = D / NS;             // columns per slice
+    static constexpr int kCG = kDC / 4;            // float4 column groups per row
+    static constexpr int kThreads = kRG * kCG;
     static constexpr int kRPT = D / kRG;           // rows per thread
-    static constexpr int kWaves = kThreads / kWave;
-    static_assert(kCG <= kWave, "a row's column groups must fit in one wave");
-    static_assert(kRG * kCG == kThreads && kRPT * kRG == D, "bad tiling");
+    static constexpr int kPairs = kRG / 2;
+    static_assert(2 * kCG <= kWave && kWave % (2 * kCG) == 0, "row-group pairs must share a wave");
+    static_assert(kRPT * kRG == D && kDC * NS == D && kDC % 4 == 0, "bad tiling");
 };
 
 // State traffic is touched once per call: non-temporal 16-byte accesses
@@ -56,34 +64,33 @@ __device__ __forceinline__ float4 fma4(float a, const float4 &b, const float4 &c
                        __builtin_fmaf(a, b.z, c.z), __builtin_fmaf(a, b.w, c.w));
 }
 
-template <int D>
-__global__ __launch_bounds__(RecCfg<D>::kThreads) void kda_recurrent_kernel(
+template <int D, int NS>
+__global__ __launch_bounds__((RecCfg<D, NS>::kThreads)) void kda_recurrent_kernel(
     const uint16_t *__restrict__ qkv, int64_t ldqkv, const float *__restrict__ gate,
     const float *__restrict__ beta, float *const *__restrict__ state,
     float *const *__restrict__ snap, float *__restrict__ core, int K, int H, float scale,
     bool write_state, const int32_t *__restrict__ n_accept)
 {
-    using Cfg = RecCfg<D>;
-    constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT, NWAVE = Cfg::kWaves;
+    using Cfg = RecCfg<D, NS>;
+    constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT, NP = Cfg::kPairs;
 
-    const int h = blockIdx.x;
+    const int h = blockIdx.x / NS;
+    const int c0 = (blockIdx.x % NS) * Cfg::kDC;   // first value column of this slice
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
     const int cg = tid % CG;
     const int rg = tid / CG;
-    const int wave = tid / kWave;
-    const int lane = tid % kWave;
     const int qkvw = H * D;
 
     __shared__ __align__(16) float s_q[D], s_k[D], s_v[D], s_e[D];
-    __shared__ float4 s_red[NWAVE > 1 ? NWAVE : 1][2][CG];
-    __shared__ float s_kq[NWAVE > 1 ? NWAVE : 1];
+    __shared__ float4 s_red[NP][2][CG];
+    __shared__ float s_kq[NP];
 
     // rows walked: all K, or the accepted ones when folding (none: nothing to do)
     const int rows = n_accept ? min(max(n_accept[b], 0), K) : K;
     if (rows == 0) return;   // uniform over the workgroup
 
-    float *__restrict__ Sg = state[b] + (size_t)h * D * D;
+    float *__restrict__ Sg = state[b] + (size_t)h * D * D + c0;
     float4 S[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
@@ -114,34 +121,30 @@ __global__ __launch_bounds__(RecCfg<D>::kThreads) void kda_recurrent_kernel(
             pq = fma4(qi, S[r], pq);
             kq = __builtin_fmaf(ki, qi, kq);
         }
-        // reduce over the row groups held by this wave
-#pragma unroll
-        for (int off = CG; off < kWave; off <<= 1) {
-            pk.x += __shfl_xor(pk.x, off); pk.y += __shfl_xor(pk.y, off);
-            pk.z += __shfl_xor(pk.z, off); pk.w += __shfl_xor(pk.w, off);
-            pq.x += __shfl_xor(pq.x, off); pq.y += __shfl_xor(pq.y, off);
-            pq.z += __shfl_xor(pq.z, off); pq.w += __shfl_xor(pq.w, off);
-            kq += __shfl_xor(kq, off);
+        // add partner row groups (2p, 2p + 1: CG lanes apart in one wave),
+        // then the 8 pair sums in order through LDS
+        pk.x += __shfl_xor(pk.x, CG); pk.y += __shfl_xor(pk.y, CG);
+        pk.z += __shfl_xor(pk.z, CG); pk.w += __shfl_xor(pk.w, CG);
+        pq.x += __shfl_xor(pq.x, CG); pq.y += __shfl_xor(pq.y, CG);
+        pq.z += __shfl_xor(pq.z, CG); pq.w += __shfl_xor(pq.w, CG);
+        kq += __shfl_xor(kq, CG);
+        if ((rg & 1) == 0) {
+            s_red[rg >> 1][0][cg] = pk;
+            s_red[rg >> 1][1][cg] = pq;
+            if (cg == 0) s_kq[rg >> 1] = kq;
         }
-        if constexpr (NWAVE > 1) {
-            if (lane < CG) {
-                s_red[wave][0][lane] = pk;
-                s_red[wave][1][lane] = pq;
-                if (lane == 0) s_kq[wave] = kq;
-            }
-            __syncthreads();
-            pk = s_red[0][0][cg];
-            pq = s_red[0][1][cg];
-            kq = s_kq[0];
+        __syncthreads();
+        pk = s_red[0][0][cg];
+        pq = s_red[0][1][cg];
+        kq = s_kq[0];
 #pragma unroll
-            for (int w = 1; w < NWAVE; ++w) {
-                const float4 a = s_red[w][0][cg], c = s_red[w][1][cg];
-                pk = make_float4(pk.x + a.x, pk.y + a.y, pk.z + a.z, pk.w + a.w);
-                pq = make_float4(pq.x + c.x, pq.y + c.y, pq.z + c.z, pq.w + c.w);
-                kq += s_kq[w];
-            }
+        for (int p = 1; p < NP; ++p) {
+            const float4 a = s_red[p][0][cg], c = s_red[p][1][cg];
+            pk = make_float4(pk.x + a.x, pk.y + a.y, pk.z + a.z, pk.w + a.w);
+            pq = make_float4(pq.x + c.x, pq.y + c.y, pq.z + c.z, pq.w + c.w);
+            kq += s_kq[p];
         }
-        const float4 v4 = reinterpret_cast<const float4 *>(s_v)[cg];
+        const float4 v4 = reinterpret_cast<const float4 *>(s_v + c0)[cg];
         const float4 u = make_float4(bt * (v4.x - pk.x), bt * (v4.y - pk.y),
                                      bt * (v4.z - pk.z), bt * (v4.w - pk.w));
         if (core != nullptr && rg == 0) {
@@ -149,14 +152,14 @@ __global__ __launch_bounds__(RecCfg<D>::kThreads) void kda_recurrent_kernel(
                                          scale * __builtin_fmaf(u.y, kq, pq.y),
                                          scale * __builtin_fmaf(u.z, kq, pq.z),
                                          scale * __builtin_fmaf(u.w, kq, pq.w));
-            reinterpret_cast<float4 *>(core + (row * H + h) * D)[cg] = o;
+            reinterpret_cast<float4 *>(core + (row * H + h) * D + c0)[cg] = o;
         }
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
             S[r] = fma4(s_k[rg + RG * r], u, S[r]);
 
         if (snap != nullptr && t + 1 < K) {
-            float *__restrict__ Sn = snap[(size_t)b * (K - 1) + t] + (size_t)h * D * D;
+            float *__restrict__ Sn = snap[(size_t)b * (K - 1) + t] + (size_t)h * D * D + c0;
 #pragma unroll
             for (int r = 0; r < RPT; ++r)
                 store_stream(Sn + (size_t)(rg + RG * r) * D + 4 * cg, S[r]);
@@ -171,16 +174,38 @@ __global__ __launch_bounds__(RecCfg<D>::kThreads) void kda_recurrent_kernel(
     }
 }
 
+template <int D, int NS>
+static hipError_t recurrent_ns(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                               const float *beta, float *const *state, float *const *snap,
+                               float *core, int B, int K, int heads, float scale,
+                               bool write_state, const int32_t *n_accept, hipStream_t stream)
+{
+    hipLaunchKernelGGL((kda_recurrent_kernel<D, NS>), dim3(heads * NS, B),
+                       dim3(RecCfg<D, NS>::kThreads), 0, stream, qkv, ldqkv, gate, beta, state,
+                       snap, core, K, heads, scale, write_state, n_accept);
+    return hipGetLastError();
+}
+
+// Slices per head: one per CU's worth of (sequence, head) pairs is enough for
+// large batches; few pairs get 4 (or 2) slices each.  Every choice gives the
+// same bits.
 template <int D>
 static hipError_t recurrent_t(const uint16_t *qkv, int64_t ldqkv, const float *gate,
                               const float *beta, float *const *state, float *const *snap,
                               float *core, int B, int K, int heads, float scale, bool write_state,
                               const int32_t *n_accept, hipStream_t stream)
 {
-    hipLaunchKernelGGL(kda_recurrent_kernel<D>, dim3(heads, B), dim3(RecCfg<D>::kThreads), 0,
-                       stream, qkv, ldqkv, gate, beta, state, snap, core, K, heads, scale,
-                       write_state, n_accept);
-    return hipGetLastError();
+    const int64_t pairs = (int64_t)B * heads;
+    if constexpr (D >= 128) {
+        if (pairs <= 128)
+            return recurrent_ns<D, 4>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
+                                      write_state, n_accept, stream);
+        if (pairs <= 256)
+            return recurrent_ns<D, 2>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
+                                      write_state, n_accept, stream);
+    }
+    return recurrent_ns<D, 1>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
+                              write_state, n_accept, stream);
 }
 
 hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float *gate,

@@ -194,3 +194,40 @@ def test_write_on_accept_equals_snapshots(B, K, H, D):
         n = min(max(int(na[b]), 0), K)
         want = S0[b] if n == 0 else (sk[b] if n == K else sn[b, n - 1])
         np.testing.assert_array_equal(got[b], want, err_msg=f"seq {b} n_accept {na[b]}")
+
+
+def test_decode_k_bits_do_not_depend_on_batch_size():
+    """The recurrent kernel splits each head's state over 4, 2 or 1
+    workgroups by value columns depending on the batch size, with the key-axis
+    sums in one fixed order, so a sequence's rows, final state and snapshots
+    are the same bits whatever batch it is decoded in (B = 1, 2 and 6 run
+    column slices; 16 runs whole heads) — a verify at one batch size matches
+    plain decode at another."""
+    import gated_delta_rule_bounded_amd as kda
+    H, D, K = 32, 128, 3
+    scale = D ** -0.5
+    Bmax = 16
+    S0 = workloads.state(H, D, 0.05, 4300, B=Bmax)
+    rows = _steps(Bmax, H, D, K, 4310)
+    qkv = torch.stack([r["qkv"] for r in rows], 1)                      # [B, K, 3HD]
+    gate = np.stack([r["gate"] for r in rows], 1)
+    beta = np.stack([r["beta"] for r in rows], 1)
+    results = {}
+    for B in (1, 2, 6, 16):
+        st = cuda(S0[:B])
+        snaps = torch.empty(B * (K - 1), H, D, D, device="cuda")
+        core = torch.empty(B * K, H, D, device="cuda")
+        say("decode_k batch", B)
+        kda.kda_decode_k(cuda(qkv[:B].reshape(B * K, -1), torch.bfloat16),
+                         cuda(gate[:B].reshape(B * K, H, D)), cuda(beta[:B].reshape(B * K, H)),
+                         kda.ptr_table(st), core, B=B, K=K, heads=H, head_dim=D, scale=scale,
+                         snap=kda.ptr_table(snaps))
+        torch.cuda.synchronize()
+        results[B] = (core.view(B, K, H, D)[0].clone(), st[0].clone(), snaps.view(B, K - 1, H, D, D)[0].clone())
+    ref = results[16]
+    for B in (1, 2, 6):
+        for a, b_ in zip(results[B], ref):
+            assert torch.equal(a, b_), B
+    ref_core, ref_S, _ = _oracle_seq(rows, S0[0], 0, H, D, scale)
+    assert relerr(ref[0].cpu().numpy(), ref_core) < TOL
+    assert relerr(ref[1].cpu().numpy(), ref_S) < TOL

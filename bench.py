@@ -646,7 +646,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); the KDA core is measured per GPU and sharding is by "
               "sequence or head with no exchange inside the core.", file=sys.stderr)
         sys.exit(2)

@@ -568,6 +568,26 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
             gs.append(g)
         return gs
 
+    # a batch: 16 sequences verifying K rows each (64 projection rows)
+    Bb = 16
+    for S in sets:
+        S["stb"] = torch.from_numpy(workloads.state(H, D, 0.05, workloads.SEED_STATE + 7,
+                                                    B=Bb)).to(dev)
+        S["tabb"] = kda.ptr_table(S["stb"])
+        S["csb"] = workloads.conv_raw(1, H, D, 4, workloads.SEED_INPUT + 7, n_seq=Bb)["state"].to(dev)
+        S["ctabb"] = kda.ptr_table(S["csb"])
+        S["xb"] = workloads.to_bf16(np.random.default_rng(77).standard_normal(
+            (Bb * K, hidden))).to(dev)
+    buf_b = kda.block_decode_buffers(Bb * K, heads=H, head_dim=D, rank=rank, device=dev)
+    out_b = torch.empty(Bb * K, hidden, dtype=torch.bfloat16, device=dev)
+
+    def verify_batch(i):
+        S = sets[i % n_sets]
+        kda.kda_block_decode_k(S["xb"], S["w"], S["tabb"], S["ctabb"], buf_b, out_b, B=Bb, K=K,
+                               hidden_size=hidden, heads=H, head_dim=D, rank=rank,
+                               scale=D ** -0.5)
+
+    t_vb = timed(verify_batch)
     gv, gd = graphs_of(verify), graphs_of(decode)
     t_gv = timed(lambda i: gv[i % n_sets].replay())
     t_gd = timed(lambda i: gd[i % n_sets].replay())
@@ -579,6 +599,8 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
                        f"{n_sets} layers rotated (weights from HBM)",
                 verify_ms=t_v * 1e3, decode_ms=t_d * 1e3, write_on_accept_ms=t_w * 1e3,
                 graph_verify_ms=t_gv * 1e3, graph_decode_ms=t_gd * 1e3,
+                batch_verify=dict(sequences=Bb, rows=Bb * K, ms=t_vb * 1e3,
+                                  tokens_per_s=Bb * K / t_vb),
                 graph_speedup_vs_serial=K * t_gd / t_gv,
                 verify_tokens_per_s=K / t_v, decode_tokens_per_s=1.0 / t_d,
                 speedup_vs_serial=K * t_d / t_v, weight_bytes=w_bytes,

@@ -36,16 +36,20 @@ namespace kda {
 // chain their D/16 rows (rows rg, rg + 16, ...), partner groups (2p, 2p + 1)
 // are added, and the 8 pair sums are added in order p = 0..7 — so every
 // slice count gives the same bits, and the launch picks the count from the
-// batch size: few sequences get more, smaller workgroups.
-template <int D, int NS>
+// batch size: few sequences get more, smaller workgroups.  Likewise a thread
+// may carry one row group or a partner pair of them (RGT), which moves the
+// pair sum from a shuffle into the thread without changing it.
+template <int D, int NS, int RGT = 1>
 struct RecCfg {
     static constexpr int kRG = 16;                 // row groups
+    static constexpr int kRGT = RGT;               // row groups per thread (1 or 2)
     static constexpr int kDC = D / NS;             // columns per slice
     static constexpr int kCG = kDC / 4;            // float4 column groups per row
-    static constexpr int kThreads = kRG * kCG;
-    static constexpr int kRPT = D / kRG;           // rows per thread
+    static constexpr int kThreads = kRG / RGT * kCG;
+    static constexpr int kRPT = D / kRG;           // rows per row group
     static constexpr int kPairs = kRG / 2;
-    static_assert(2 * kCG <= kWave && kWave % (2 * kCG) == 0, "row-group pairs must share a wave");
+    static_assert(RGT == 2 || (2 * kCG <= kWave && kWave % (2 * kCG) == 0),
+                  "row-group pairs must share a wave");
     static_assert(kRPT * kRG == D && kDC * NS == D && kDC % 4 == 0, "bad tiling");
 };
 
@@ -64,14 +68,14 @@ __device__ __forceinline__ float4 fma4(float a, const float4 &b, const float4 &c
                        __builtin_fmaf(a, b.z, c.z), __builtin_fmaf(a, b.w, c.w));
 }
 
-template <int D, int NS>
-__global__ __launch_bounds__((RecCfg<D, NS>::kThreads)) void kda_recurrent_kernel(
+template <int D, int NS, int RGT>
+__global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_kernel(
     const uint16_t *__restrict__ qkv, int64_t ldqkv, const float *__restrict__ gate,
     const float *__restrict__ beta, float *const *__restrict__ state,
     float *const *__restrict__ snap, float *__restrict__ core, int K, int H, float scale,
     bool write_state, const int32_t *__restrict__ n_accept)
 {
-    using Cfg = RecCfg<D, NS>;
+    using Cfg = RecCfg<D, NS, RGT>;
     constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT, NP = Cfg::kPairs;
 
     const int h = blockIdx.x / NS;
@@ -79,8 +83,10 @@ __global__ __launch_bounds__((RecCfg<D, NS>::kThreads)) void kda_recurrent_kerne
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
     const int cg = tid % CG;
-    const int rg = tid / CG;
+    const int tr = tid / CG;                        // thread row index
     const int qkvw = H * D;
+    // row group of this thread's j-th set of rows: tr, or 2 tr + j
+    auto rgof = [&](int j) { return RGT == 1 ? tr : 2 * tr + j; };
 
     __shared__ __align__(16) float s_q[D], s_k[D], s_v[D], s_e[D];
     __shared__ float4 s_red[NP][2][CG];
@@ -91,10 +97,12 @@ __global__ __launch_bounds__((RecCfg<D, NS>::kThreads)) void kda_recurrent_kerne
     if (rows == 0) return;   // uniform over the workgroup
 
     float *__restrict__ Sg = state[b] + (size_t)h * D * D + c0;
-    float4 S[RPT];
+    float4 S[RGT][RPT];
 #pragma unroll
-    for (int r = 0; r < RPT; ++r)
-        S[r] = load_stream(Sg + (size_t)(rg + RG * r) * D + 4 * cg);
+    for (int j = 0; j < RGT; ++j)
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+            S[j][r] = load_stream(Sg + (size_t)(rgof(j) + RG * r) * D + 4 * cg);
 
     for (int t = 0; t < rows; ++t) {
         const size_t row = (size_t)b * K + t;
@@ -108,30 +116,45 @@ __global__ __launch_bounds__((RecCfg<D, NS>::kThreads)) void kda_recurrent_kerne
         const float bt = beta[row * H + h];
         __syncthreads();
 
-        // decay, then partial column sums of S'^T k and S'^T q over this
-        // thread's rows, and the matching partial of k . q
-        float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
-        float kq = 0.f;
+        // decay, then per row group the partial column sums of S'^T k and
+        // S'^T q over its rows, and the matching partial of k . q
+        float4 pkj[RGT], pqj[RGT];
+        float kqj[RGT];
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) {
-            const int i = rg + RG * r;
-            const float e = s_e[i], ki = s_k[i], qi = s_q[i];
-            S[r] = make_float4(S[r].x * e, S[r].y * e, S[r].z * e, S[r].w * e);
-            pk = fma4(ki, S[r], pk);
-            pq = fma4(qi, S[r], pq);
-            kq = __builtin_fmaf(ki, qi, kq);
+        for (int j = 0; j < RGT; ++j) {
+            pkj[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            pqj[j] = pkj[j];
+            kqj[j] = 0.f;
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const int i = rgof(j) + RG * r;
+                const float e = s_e[i], ki = s_k[i], qi = s_q[i];
+                S[j][r] = make_float4(S[j][r].x * e, S[j][r].y * e, S[j][r].z * e, S[j][r].w * e);
+                pkj[j] = fma4(ki, S[j][r], pkj[j]);
+                pqj[j] = fma4(qi, S[j][r], pqj[j]);
+                kqj[j] = __builtin_fmaf(ki, qi, kqj[j]);
+            }
         }
-        // add partner row groups (2p, 2p + 1: CG lanes apart in one wave),
-        // then the 8 pair sums in order through LDS
-        pk.x += __shfl_xor(pk.x, CG); pk.y += __shfl_xor(pk.y, CG);
-        pk.z += __shfl_xor(pk.z, CG); pk.w += __shfl_xor(pk.w, CG);
-        pq.x += __shfl_xor(pq.x, CG); pq.y += __shfl_xor(pq.y, CG);
-        pq.z += __shfl_xor(pq.z, CG); pq.w += __shfl_xor(pq.w, CG);
-        kq += __shfl_xor(kq, CG);
-        if ((rg & 1) == 0) {
-            s_red[rg >> 1][0][cg] = pk;
-            s_red[rg >> 1][1][cg] = pq;
-            if (cg == 0) s_kq[rg >> 1] = kq;
+        // add partner row groups (2p, 2p + 1): in the thread, or CG lanes
+        // apart in one wave; then the 8 pair sums in order through LDS
+        float4 pk = pkj[0], pq = pqj[0];
+        float kq = kqj[0];
+        if constexpr (RGT == 2) {
+            pk = make_float4(pk.x + pkj[1].x, pk.y + pkj[1].y, pk.z + pkj[1].z, pk.w + pkj[1].w);
+            pq = make_float4(pq.x + pqj[1].x, pq.y + pqj[1].y, pq.z + pqj[1].z, pq.w + pqj[1].w);
+            kq += kqj[1];
+        } else {
+            pk.x += __shfl_xor(pk.x, CG); pk.y += __shfl_xor(pk.y, CG);
+            pk.z += __shfl_xor(pk.z, CG); pk.w += __shfl_xor(pk.w, CG);
+            pq.x += __shfl_xor(pq.x, CG); pq.y += __shfl_xor(pq.y, CG);
+            pq.z += __shfl_xor(pq.z, CG); pq.w += __shfl_xor(pq.w, CG);
+            kq += __shfl_xor(kq, CG);
+        }
+        const int pr = RGT == 2 ? tr : tr >> 1;   // pair index
+        if (RGT == 2 || (tr & 1) == 0) {
+            s_red[pr][0][cg] = pk;
+            s_red[pr][1][cg] = pq;
+            if (cg == 0) s_kq[pr] = kq;
         }
         __syncthreads();
         pk = s_red[0][0][cg];
@@ -147,7 +170,7 @@ __global__ __launch_bounds__((RecCfg<D, NS>::kThreads)) void kda_recurrent_kerne
         const float4 v4 = reinterpret_cast<const float4 *>(s_v + c0)[cg];
         const float4 u = make_float4(bt * (v4.x - pk.x), bt * (v4.y - pk.y),
                                      bt * (v4.z - pk.z), bt * (v4.w - pk.w));
-        if (core != nullptr && rg == 0) {
+        if (core != nullptr && tr == 0) {
             const float4 o = make_float4(scale * __builtin_fmaf(u.x, kq, pq.x),
                                          scale * __builtin_fmaf(u.y, kq, pq.y),
                                          scale * __builtin_fmaf(u.z, kq, pq.z),
@@ -155,34 +178,40 @@ __global__ __launch_bounds__((RecCfg<D, NS>::kThreads)) void kda_recurrent_kerne
             reinterpret_cast<float4 *>(core + (row * H + h) * D + c0)[cg] = o;
         }
 #pragma unroll
-        for (int r = 0; r < RPT; ++r)
-            S[r] = fma4(s_k[rg + RG * r], u, S[r]);
+        for (int j = 0; j < RGT; ++j)
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                S[j][r] = fma4(s_k[rgof(j) + RG * r], u, S[j][r]);
 
         if (snap != nullptr && t + 1 < K) {
             float *__restrict__ Sn = snap[(size_t)b * (K - 1) + t] + (size_t)h * D * D + c0;
 #pragma unroll
-            for (int r = 0; r < RPT; ++r)
-                store_stream(Sn + (size_t)(rg + RG * r) * D + 4 * cg, S[r]);
+            for (int j = 0; j < RGT; ++j)
+#pragma unroll
+                for (int r = 0; r < RPT; ++r)
+                    store_stream(Sn + (size_t)(rgof(j) + RG * r) * D + 4 * cg, S[j][r]);
         }
         __syncthreads();  // LDS is rewritten by the next row
     }
 
     if (write_state) {
 #pragma unroll
-        for (int r = 0; r < RPT; ++r)
-            store_stream(Sg + (size_t)(rg + RG * r) * D + 4 * cg, S[r]);
+        for (int j = 0; j < RGT; ++j)
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                store_stream(Sg + (size_t)(rgof(j) + RG * r) * D + 4 * cg, S[j][r]);
     }
 }
 
-template <int D, int NS>
+template <int D, int NS, int RGT = 1>
 static hipError_t recurrent_ns(const uint16_t *qkv, int64_t ldqkv, const float *gate,
                                const float *beta, float *const *state, float *const *snap,
                                float *core, int B, int K, int heads, float scale,
                                bool write_state, const int32_t *n_accept, hipStream_t stream)
 {
-    hipLaunchKernelGGL((kda_recurrent_kernel<D, NS>), dim3(heads * NS, B),
-                       dim3(RecCfg<D, NS>::kThreads), 0, stream, qkv, ldqkv, gate, beta, state,
-                       snap, core, K, heads, scale, write_state, n_accept);
+    hipLaunchKernelGGL((kda_recurrent_kernel<D, NS, RGT>), dim3(heads * NS, B),
+                       dim3(RecCfg<D, NS, RGT>::kThreads), 0, stream, qkv, ldqkv, gate, beta,
+                       state, snap, core, K, heads, scale, write_state, n_accept);
     return hipGetLastError();
 }
 
@@ -204,6 +233,13 @@ static hipError_t recurrent_t(const uint16_t *qkv, int64_t ldqkv, const float *g
             return recurrent_ns<D, 2>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
                                       write_state, n_accept, stream);
     }
+    // whole heads: the write-on-accept verify (state read only) and fold run
+    // two row groups per thread (256 threads, more state in flight per CU);
+    // decode and decode_k keep one (512 threads), measured faster for them
+    if constexpr (D >= 128)
+        if (!write_state || n_accept)
+            return recurrent_ns<D, 1, 2>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads,
+                                         scale, write_state, n_accept, stream);
     return recurrent_ns<D, 1>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
                               write_state, n_accept, stream);
 }

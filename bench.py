@@ -59,7 +59,7 @@ TRAFFIC_BYTES = {"kda_chunk_prep": (68475.59 * 2.0 + 147968.05 * 1.0) * 1024,
                  "kda_chunk_fwd": (75098.76 * 2.0 + 34816.07 * 1.0) * 1024}
 # Counted HBM traffic of one decode step at 256 sequences (FETCH_SIZE x 2 +
 # WRITE_SIZE, KiB per dispatch) for the recurrent kernel as built now.
-DECODE_TRAFFIC_BYTES = (267441.1 * 2.0 + 528943.7 * 1.0) * 1024
+DECODE_TRAFFIC_BYTES = (267440.6 * 2.0 + 528931.7 * 1.0) * 1024
 # Both prefill kernels run each fp32 product as three bf16 products (hi*hi,
 # hi*lo, lo*hi, fp32 accumulation), so their matrix-unit ceiling in
 # fp32-equivalent flops is a third of the bf16 peak.

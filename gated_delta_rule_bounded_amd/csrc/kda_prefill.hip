@@ -180,12 +180,16 @@ __device__ __forceinline__ void load_rows_src(const QkvSrc<BF> &src, const float
                                               float4 (&G)[D / 16])
 {
     const int64_t goff = (tg * H + h) * D;
+    // the gate first: the in-chunk scan needs only it, so it can start while
+    // k and q are still arriving
+#pragma unroll
+    for (int t8 = 0; t8 < D / 16; ++t8)
+        G[t8] = *reinterpret_cast<const float4 *>(gate + goff + 16 * t8 + 4 * lg);
 #pragma unroll
     for (int t8 = 0; t8 < D / 16; ++t8) {
         const int d0 = 16 * t8 + 4 * lg;
         K[t8] = src.load4(src.k, tg, (int64_t)h * D + d0);
         Q[t8] = src.load4(src.q, tg, (int64_t)h * D + d0);
-        G[t8] = *reinterpret_cast<const float4 *>(gate + goff + d0);
     }
 }
 

@@ -241,8 +241,12 @@ int kda_prefill_split(const float *q, const float *k, const float *v, const floa
     if (!aligned16(cap_state))
         return fail(KDA_ERR_SHAPE, "kda_prefill_split: cap_state must be 16-byte aligned");
     if (overlap(cap_state, st_b, state, st_b) || overlap(cap_state, st_b, core, rows_b) ||
-        overlap(cap_state, st_b, workspace, workspace_bytes))
-        return fail(KDA_ERR_ALIAS, "kda_prefill_split: cap_state overlaps state, core or workspace");
+        overlap(cap_state, st_b, workspace, workspace_bytes) ||
+        overlap(cap_state, st_b, q, rows_b) || overlap(cap_state, st_b, k, rows_b) ||
+        overlap(cap_state, st_b, v, rows_b) || overlap(cap_state, st_b, gate, rows_b) ||
+        overlap(cap_state, st_b, beta, (size_t)T_pad * heads * 4))
+        return fail(KDA_ERR_ALIAS, "kda_prefill_split: cap_state overlaps an input, the state, "
+                                   "core or the workspace");
     const int64_t HD = (int64_t)heads * head_dim;
     hipError_t e = hipSuccess;
     if (cap > 0)

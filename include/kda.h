@@ -202,7 +202,7 @@ int kda_prefill_bf16(const uint16_t *qkv, int64_t ldqkv, const float *gate,
  * Arguments and errors as kda_prefill, plus: 0 <= cap <= T; T_pad at least
  * cap + round_up(T - cap, chunk) (the tail's last chunk must exist; rows
  * past T may hold anything); cap_state 16-byte aligned and disjoint from
- * state, core and workspace (KDA_ERR_ALIAS).  T == 0 is a no-op.
+ * the inputs, state, core and workspace (KDA_ERR_ALIAS).  T == 0 is a no-op.
  * ------------------------------------------------------------------------ */
 int kda_prefill_split(const float *q, const float *k, const float *v,
                       const float *gate, const float *beta, float *state, float *core,

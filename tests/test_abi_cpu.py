@@ -308,6 +308,7 @@ def test_prefill_split_validation(lib):
     assert call(cap_state=0) == E_NULL
     assert call(cap_state=Dp + 64) == E_ALIAS                  # over the state
     assert call(cap_state=E + 256) == E_ALIAS                  # over the workspace
+    assert call(cap_state=A + 4096) == E_ALIAS                 # over q
 
 
 def test_block_write_on_accept_validation(lib):

@@ -205,10 +205,13 @@ int kda_prefill_bf16(const uint16_t *qkv, int64_t ldqkv, const float *gate, cons
         return fail(KDA_ERR_SHAPE, "kda_prefill_bf16: misaligned pointer");
     const size_t rows_b = (size_t)T_pad * qw * 4, st_b = (size_t)heads * head_dim * head_dim * 4;
     const size_t qkv_b = (size_t)((T_pad - 1) * ldqkv + 3 * qw) * 2;
+    const size_t beta_b = (size_t)T_pad * heads * 4;
     if (overlap(core, rows_b, qkv, qkv_b) || overlap(core, rows_b, gate, rows_b) ||
-        overlap(core, rows_b, beta, (size_t)T_pad * heads * 4) || overlap(core, rows_b, state, st_b) ||
+        overlap(core, rows_b, beta, beta_b) || overlap(core, rows_b, state, st_b) ||
         overlap(state, st_b, qkv, qkv_b) || overlap(state, st_b, gate, rows_b) ||
-        overlap(workspace, need, core, rows_b) || overlap(workspace, need, state, st_b))
+        overlap(state, st_b, beta, beta_b) || overlap(workspace, need, core, rows_b) ||
+        overlap(workspace, need, state, st_b) || overlap(workspace, need, qkv, qkv_b) ||
+        overlap(workspace, need, gate, rows_b) || overlap(workspace, need, beta, beta_b))
         return fail(KDA_ERR_ALIAS, "kda_prefill_bf16: core, state or workspace overlaps");
     return hip_status(kda::launch_kda_prefill_bf16(qkv, ldqkv, gate, beta, state, core, T, heads,
                                                    head_dim, chunk, scale, workspace, stream),
@@ -329,9 +332,12 @@ int kda_prefill_varlen(const float *q, const float *k, const float *v, const flo
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return fail(KDA_ERR_SHAPE, "kda_prefill_varlen: misaligned pointer");
     const size_t rows_b = (size_t)rows * heads * head_dim * 4;
-    if (overlap(core, rows_b, q, rows_b) || overlap(core, rows_b, k, rows_b) ||
-        overlap(core, rows_b, v, rows_b) || overlap(core, rows_b, gate, rows_b) ||
-        overlap(core, rows_b, beta, (size_t)rows * heads * 4) ||
+    const size_t beta_b = (size_t)rows * heads * 4;
+    const void *ins[] = {q, k, v, gate};
+    for (const void *p : ins)
+        if (overlap(core, rows_b, p, rows_b) || overlap(workspace, need, p, rows_b))
+            return fail(KDA_ERR_ALIAS, "kda_prefill_varlen: core or workspace overlaps an input");
+    if (overlap(core, rows_b, beta, beta_b) || overlap(workspace, need, beta, beta_b) ||
         overlap(workspace, need, core, rows_b))
         return fail(KDA_ERR_ALIAS, "kda_prefill_varlen: core or workspace overlaps an input");
     return hip_status(kda::launch_kda_prefill_varlen(q, k, v, gate, beta, state, core, cu_seqlens,

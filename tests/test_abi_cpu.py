@@ -348,3 +348,20 @@ def test_block_fold_alignment(lib):
     b.conv_out += 2
     assert lib.kda_block_fold_accepted(ctypes.byref(b), 60 << 36, 61 << 36, 64 << 36, 3, 4, 2, 16,
                                        None) == E_SHAPE
+
+
+def test_prefill_bf16_validation(lib):
+    H, Dh, C = 2, 16, 16
+    ws = lib.kda_prefill_workspace_bytes(64, H, Dh, C)
+
+    def call(qkv=A, ld=96, gate=B, beta=C, state=Dp, core=E, wsp=F, ws_bytes=ws, T=57, T_pad=64):
+        return lib.kda_prefill_bf16(qkv, ld, gate, beta, state, core, T, T_pad, H, Dh, C, 0.25,
+                                    wsp, ws_bytes, None)
+
+    assert call(T=0) == OK
+    assert call(ld=90) == E_SHAPE and call(ld=98) == E_SHAPE       # < 3*H*D, not % 4
+    assert call(qkv=A + 4) == E_SHAPE                              # 8-byte alignment
+    assert call(ws_bytes=ws - 1) == E_WS
+    assert call(core=A + 64) == E_ALIAS                            # core over the rows
+    assert call(wsp=B) == E_ALIAS                                  # workspace over the gate
+    assert call(state=C) == E_ALIAS                                # state over beta

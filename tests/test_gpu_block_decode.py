@@ -31,7 +31,7 @@ STAGES = ("qkv_proj", "conv_out", "fa", "g_raw", "b_raw", "gate", "beta", "core"
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,Kd", [(1, 48, 96), (4, 4096, 4096), (7, 40, 4096), (70, 136, 256),
-                                    (16, 32, 4096), (3, 4096, 128)])
+                                    (16, 32, 4096), (3, 4096, 128), (5, 64, 4224)])
 def test_gemv_matches_oracle(orc, M, N, Kd):
     r = np.random.default_rng(M * 7 + N + Kd)
     x = workloads.to_bf16(r.standard_normal((M, Kd)))
@@ -69,7 +69,8 @@ def test_gemv_rows_are_order_exact():
         kda.dense_gemv_bf16_batchm(x[m:m + 1], w, y1, M=1, N=N, Kd=Kd)
         singles.append((m, y1))
     # up to 16 rows and more rows run different kernel instances (one row
-    # tile with deeper loads, four row tiles); both accumulate in one order
+    # tile with four-step load stages, four row tiles with two-step stages);
+    # both accumulate in one order
     groups = {}
     for m0, M_ in ((30, 4), (40, 3), (8, 8), (20, 16), (2, 5)):
         yg = torch.empty(M_, N, dtype=torch.bfloat16, device="cuda")
@@ -80,6 +81,27 @@ def test_gemv_rows_are_order_exact():
     for m, y1 in singles:
         assert torch.equal(y1[0], y[m]), m
     for (m0, M_), yg in groups.items():
+        assert torch.equal(yg, y[m0:m0 + M_]), (m0, M_)
+
+
+def test_gemv_rows_are_order_exact_with_ragged_steps():
+    # Kd = 4224: 33 contraction steps per wave, a whole number of load stages
+    # for neither kernel instance, so both run passes with dummy slots; the
+    # accumulation order must still be the same in both
+    M, N, Kd = 70, 2048, 4224
+    r = np.random.default_rng(123)
+    x = workloads.to_bf16(r.standard_normal((M, Kd))).cuda()
+    w = workloads.to_bf16(r.normal(0.0, 0.02, size=(N, Kd))).cuda()
+    say("gemv ragged steps", M, N, Kd)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    kda.dense_gemv_bf16_batchm(x, w, y, M=M, N=N, Kd=Kd)
+    parts = []
+    for m0, M_ in ((0, 1), (69, 1), (10, 4), (33, 16), (40, 20)):
+        yg = torch.empty(M_, N, dtype=torch.bfloat16, device="cuda")
+        kda.dense_gemv_bf16_batchm(x[m0:m0 + M_], w, yg, M=M_, N=N, Kd=Kd)
+        parts.append((m0, M_, yg))
+    torch.cuda.synchronize()
+    for m0, M_, yg in parts:
         assert torch.equal(yg, y[m0:m0 + M_]), (m0, M_)
 
 

@@ -745,6 +745,12 @@ def main():
                                TFLOPs=f_prep / t_prep / 1e12, bytes=b_prep,
                                GBps=b_prep / t_prep / 1e9),
     }
+    # each kernel against both of its ceilings: its fp32-equivalent products
+    # at the matrix peak of the three-bf16-MFMA form, and its bytes at HBM peak
+    for k, kv in kernels.items():
+        kv["matrix_peak_TFLOPs"] = MATRIX_PEAK[k][0] / 1e12
+        kv["matrix_frac"] = kv["TFLOPs"] / kv["matrix_peak_TFLOPs"]
+        kv["hbm_frac"] = kv["GBps"] / (PEAK_HBM / 1e9)
     # The dominant kernel is the slower one; its bound is the ceiling it would
     # hit first: HBM bytes at 8 TB/s or its products at the matrix peak.
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])

@@ -111,3 +111,32 @@ def test_varlen_sequence_outside_the_workspace_is_left_alone():
         one_core, one_S = gpu_prefill(cases[s], T, -(-T // C) * C, C, scale)
         np.testing.assert_array_equal(core[cu[s]:cu[s + 1]], one_core[:T])
         np.testing.assert_array_equal(states[s], one_S)
+
+
+def test_varlen_single_chunk_prompts_same_bits_in_both_forward_instances():
+    # every prompt within one chunk runs the forward instance without the
+    # load-ahead register set; adding one longer prompt to the same call
+    # switches the launch to the load-ahead instance, and the short prompts'
+    # rows and states must come out bit for bit the same
+    H, D, C = 32, 128, 64
+    lengths = [64] * 60 + [33, 1, 64, 50]
+    scale = D ** -0.5
+    cases = [core_case(T, H, D, 1700 + s, 0.05, qkv_bf16=True) for s, T in enumerate(lengths)]
+    cu_a, core_a, states_a = run_varlen(cases, H, D, C, scale)
+    long_case = core_case(200, H, D, 1799, 0.05, qkv_bf16=True)
+    cu_b, core_b, states_b = run_varlen(cases + [long_case], H, D, C, scale)
+    for s in range(len(lengths)):
+        np.testing.assert_array_equal(core_a[cu_a[s]:cu_a[s + 1]], core_b[cu_b[s]:cu_b[s + 1]],
+                                      err_msg=f"seq {s} core")
+        np.testing.assert_array_equal(states_a[s], states_b[s], err_msg=f"seq {s} state")
+    for s in (0, 37, 60, 61):
+        c = cases[s]
+        ref_core, ref_S, _ = oracle.kda_recurrence(c["q"], c["k"], c["v"], c["gate"], c["beta"],
+                                                   c["S0"], scale, threads=THREADS)
+        assert relerr(core_a[cu_a[s]:cu_a[s + 1]], ref_core) < TOL, f"seq {s} core"
+        assert relerr(states_a[s], ref_S) < TOL, f"seq {s} state"
+    c = long_case
+    ref_core, ref_S, _ = oracle.kda_recurrence(c["q"], c["k"], c["v"], c["gate"], c["beta"],
+                                               c["S0"], scale, threads=THREADS)
+    assert relerr(core_b[cu_b[-2]:cu_b[-1]], ref_core) < TOL
+    assert relerr(states_b[-1], ref_S) < TOL

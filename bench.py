@@ -31,8 +31,8 @@ Also reported on the same JSON line (measured after the timed steps):
   cpu_baseline  the fp64 oracle on the same prefill workload, on host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-       (--prefill-only, --decode-only, --block-only, --block-decode-only and
-       --calibrate-copy serve profiler runs)
+       (--prefill-only, --decode-only, --block-only, --block-decode-only,
+       --varlen-only and --calibrate-copy serve profiler runs)
 """
 import argparse
 import json
@@ -662,6 +662,8 @@ def main():
                     help="time decode and decode_k only and print their JSON objects (profiler runs)")
     ap.add_argument("--block-decode-only", action="store_true",
                     help="time the block decode / K-row verify only (profiler runs)")
+    ap.add_argument("--varlen-only", action="store_true",
+                    help="time the several-prompt prefill only (profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (scales HBM counters)")
@@ -693,6 +695,9 @@ def main():
         return
     if args.block_decode_only:
         print(json.dumps({"block_decode": bench_block_decode(kda, dev)}), flush=True)
+        return
+    if args.varlen_only:
+        print(json.dumps({"prefill_varlen": bench_prefill_varlen(kda, dev)}), flush=True)
         return
 
     if args.calibrate_copy:

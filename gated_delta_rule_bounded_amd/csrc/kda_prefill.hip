@@ -20,13 +20,18 @@ int prefill_segment_chunks(int T, int heads, int head_dim, int chunk)
     return (NC + nseg - 1) / nseg;
 }
 
+constexpr int kMaxChunksPerLaunch = 65535;   // grid y
+
 template <int D, int C, bool BF>
 static hipError_t prepare_src(const QkvSrc<BF> &src, const float *gate, const float *beta, int T,
                               int H, void *workspace, const Varlen &vl, int B, hipStream_t stream)
 {
     const dim3 grid = vl.cu ? dim3(vl.max_chunks, H, B) : dim3((T + C - 1) / C, H);
+    // the split kernel takes one sequence's chunks in y (heads fastest); the
+    // callers launch at most kMaxChunksPerLaunch chunks at a time
+    const dim3 grid_split = vl.cu ? grid : dim3(H, (T + C - 1) / C);
     if constexpr (Blk<D, C>::kSplit)
-        hipLaunchKernelGGL((kda_chunk_prep_split_kernel<D, C, BF>), grid,
+        hipLaunchKernelGGL((kda_chunk_prep_split_kernel<D, C, BF>), grid_split,
                            dim3(PrefCfg<D, C>::kThreads), 0, stream, src, gate, beta, T, H,
                            static_cast<float *>(workspace), vl);
     else
@@ -93,8 +98,22 @@ hipError_t launch_kda_prefill_prepare(const float *q, const float *k, const floa
                                       int head_dim, int chunk, void *workspace,
                                       hipStream_t stream)
 {
-    return KDA_PREFILL_DISPATCH(prepare_t, q, k, v, gate, beta, T, heads, workspace, Varlen{},
-                                1, stream);
+    // chunks are independent here: a long sequence is prepared in pieces of
+    // at most kMaxChunksPerLaunch chunks (a grid dimension's limit), each
+    // into its own blocks of the one-pass layout
+    const int NC = (T + chunk - 1) / chunk;
+    const int64_t HD = (int64_t)heads * head_dim;
+    const size_t chunk_bytes = prefill_workspace_bytes(chunk, heads, head_dim, chunk);
+    for (int c0 = 0; c0 < NC; c0 += kMaxChunksPerLaunch) {
+        const int64_t r0 = (int64_t)c0 * chunk;
+        const int Ts = (int)std::min<int64_t>((int64_t)T - r0, (int64_t)kMaxChunksPerLaunch * chunk);
+        void *ws = static_cast<char *>(workspace) + (size_t)c0 * chunk_bytes;
+        const hipError_t e = KDA_PREFILL_DISPATCH(prepare_t, q + r0 * HD, k + r0 * HD, v + r0 * HD,
+                                                  gate + r0 * HD, beta + r0 * heads, Ts, heads,
+                                                  ws, Varlen{}, 1, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_kda_prefill_forward(float *state, float *core, int T, int heads, int head_dim,

@@ -204,6 +204,47 @@ def test_prefill_phases_equal_one_call_bitwise():
     assert np.array_equal(st.cpu().numpy().view(np.int32), S_a.view(np.int32))
 
 
+
+def test_prefill_prepare_longer_than_one_grid_dimension():
+    """kda_prefill_prepare over more chunks than one grid dimension holds
+    (65,537 chunks of 64 rows, one head of 128): it prepares them in pieces,
+    and the two phases still equal kda_prefill, which walks cache-sized
+    segments, bit for bit.  Inputs are generated on the GPU (about 23 GB of
+    buffers), keys unit-norm and log-decays small, so the walk stays finite."""
+    import gated_delta_rule_bounded_amd as kda
+    H, D, C = 1, 128, 64
+    NC = 65537
+    T_pad = NC * C
+    T = T_pad - 5
+    say("prepare in pieces", T, H, D, C)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2024)
+
+    def rnd(*shape):
+        return torch.randn(*shape, device="cuda", generator=gen)
+
+    q = rnd(T_pad, H, D).mul_(D ** -0.5)
+    k = rnd(T_pad, H, D)
+    k.div_(k.norm(dim=-1, keepdim=True))
+    v = rnd(T_pad, H, D)
+    gate = torch.rand(T_pad, H, D, device="cuda", generator=gen).mul_(-0.1)
+    beta = torch.sigmoid(rnd(T_pad, H))
+    S0 = rnd(H, D, D).mul_(0.05)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(T_pad, H, D, C), dtype=torch.uint8,
+                     device="cuda")
+    kw = dict(T=T, T_pad=T_pad, heads=H, head_dim=D, chunk=C)
+    st_a = S0.clone()
+    core_a = torch.full((T_pad, H, D), 7.0, device="cuda")
+    kda.kda_prefill(q, k, v, gate, beta, st_a, core_a, ws, scale=D ** -0.5, **kw)
+    st_b = S0.clone()
+    core_b = torch.full((T_pad, H, D), 7.0, device="cuda")
+    kda.kda_prefill_prepare(q, k, v, gate, beta, ws, **kw)
+    kda.kda_prefill_forward(st_b, core_b, ws, scale=D ** -0.5, **kw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(st_a).all()
+    assert torch.equal(core_a.view(torch.int32), core_b.view(torch.int32))
+    assert torch.equal(st_a.view(torch.int32), st_b.view(torch.int32))
+
 def test_prefill_segments_equal_one_pass_bitwise():
     """kda_prefill walks segments of kda_prefill_segment_chunks chunks, each
     prepared into the start of the workspace; at H = 64 a 2200-token prefill

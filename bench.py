@@ -56,7 +56,7 @@ PEAK_HBM = 8.0e12             # MI355X HBM3E peak, B/s
 # calibration) from rocprofv3 counter runs of the kernels as they are built
 # now; a kernel is left out once it changes after its counters were taken.
 TRAFFIC_BYTES = {"kda_chunk_prep": (66891.3 * 2.0 + 147968.0 * 1.0) * 1024,
-                 "kda_chunk_fwd": (75098.07 * 2.0 + 34816.0 * 1.0) * 1024}
+                 "kda_chunk_fwd": (75098.0 * 2.0 + 34816.0 * 1.0) * 1024}
 # Counted HBM traffic of one decode step at 256 sequences (FETCH_SIZE x 2 +
 # WRITE_SIZE, KiB per dispatch) for the recurrent kernel as built now.
 DECODE_TRAFFIC_BYTES = (267440.6 * 2.0 + 528931.7 * 1.0) * 1024

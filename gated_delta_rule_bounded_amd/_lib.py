@@ -91,10 +91,10 @@ def _load():
     lib.kda_verify_k.restype = ctypes.c_int
     lib.kda_verify_k.argtypes = [P, i64, P, P, P, P, i32, i32, i32, i32, f32, P]
     lib.kda_fold_accepted.restype = ctypes.c_int
-    lib.kda_fold_accepted.argtypes = [P, i64, P, P, P, P, i32, i32, i32, i32, P]
+    lib.kda_fold_accepted.argtypes = [P, i64, P, P, P, P, i32, i32, i32, i32, P, P]
     lib.kda_prefill_varlen.restype = ctypes.c_int
     lib.kda_prefill_varlen.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
-                                       f32, P, ctypes.c_size_t, P]
+                                       f32, P, ctypes.c_size_t, P, P]
     lib.dense_gemv_bf16_batchm.restype = ctypes.c_int
     lib.dense_gemv_bf16_batchm.argtypes = [P, i64, P, i32, i32, i32, P, i64, P]
     lib.kda_block_decode_k.restype = ctypes.c_int
@@ -107,7 +107,7 @@ def _load():
         [f32] * 3 + [P]
     lib.kda_block_fold_accepted.restype = ctypes.c_int
     lib.kda_block_fold_accepted.argtypes = [ctypes.POINTER(BlockDecodeBuffers), P, P, P, i32, i32,
-                                            i32, i32, P]
+                                            i32, i32, P, P]
     lib.kda_block_decode.restype = ctypes.c_int
     lib.kda_block_decode.argtypes = [P, ctypes.POINTER(BlockWeights), P, P,
                                      ctypes.POINTER(BlockDecodeBuffers), P] + [i32] * 5 + \

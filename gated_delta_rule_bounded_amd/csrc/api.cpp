@@ -30,6 +30,7 @@ int hip_status(hipError_t e, const char *what) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool head_dim_ok(int d) { return d == 16 || d == 128; }
 
@@ -55,7 +56,8 @@ int conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w,
                  uint16_t *y, int64_t ldy, float *q32, float *k32, float *v32,
                  hipStream_t stream)
 {
-    if (n_seq < 0 || rows < 0 || heads <= 0 || n_seq > kMaxGridYZ || (rows + 15) / 16 > kMaxGridYZ)
+    if (n_seq < 0 || rows < 0 || heads <= 0 || n_seq > kMaxGridYZ ||
+        ((int64_t)rows + kda::kConvRowsPerTile - 1) / kda::kConvRowsPerTile > kMaxGridYZ)
         return fail(KDA_ERR_SHAPE, "conv_silu_l2: n_seq=%d rows=%d heads=%d", n_seq, rows, heads);
     if (!head_dim_ok(head_dim) || kc != 4)
         return fail(KDA_ERR_UNSUPPORTED, "conv_silu_l2: head_dim=%d kc=%d (need 16|128, 4)",
@@ -312,7 +314,8 @@ int kda_prefill_varlen(const float *q, const float *k, const float *v, const flo
                        const float *beta, float *const *state, float *core,
                        const int32_t *cu_seqlens, int32_t B, int32_t rows, int32_t max_chunks,
                        int32_t total_chunks, int32_t heads, int32_t head_dim, int32_t chunk,
-                       float scale, void *workspace, size_t workspace_bytes, hipStream_t stream)
+                       float scale, void *workspace, size_t workspace_bytes, int32_t *status,
+                       hipStream_t stream)
 {
     if (!head_dim_ok(head_dim) || !(chunk == 16 || chunk == 64))
         return fail(KDA_ERR_UNSUPPORTED, "kda_prefill_varlen: head_dim=%d chunk=%d", head_dim,
@@ -329,7 +332,7 @@ int kda_prefill_varlen(const float *q, const float *k, const float *v, const flo
         return fail(KDA_ERR_WORKSPACE, "kda_prefill_varlen: workspace %zu bytes < %zu needed",
                     workspace_bytes, need);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(core) ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) || (status && !aligned4(status)))
         return fail(KDA_ERR_SHAPE, "kda_prefill_varlen: misaligned pointer");
     const size_t rows_b = (size_t)rows * heads * head_dim * 4;
     const size_t beta_b = (size_t)rows * heads * 4;
@@ -342,7 +345,8 @@ int kda_prefill_varlen(const float *q, const float *k, const float *v, const flo
         return fail(KDA_ERR_ALIAS, "kda_prefill_varlen: core or workspace overlaps an input");
     return hip_status(kda::launch_kda_prefill_varlen(q, k, v, gate, beta, state, core, cu_seqlens,
                                                      B, rows, max_chunks, total_chunks, heads,
-                                                     head_dim, chunk, scale, workspace, stream),
+                                                     head_dim, chunk, scale, workspace, status,
+                                                     stream),
                       "kda_prefill_varlen launch");
 }
 
@@ -423,7 +427,7 @@ int kda_verify_k(const uint16_t *qkv, int64_t ldqkv, const float *gate, const fl
 
 int kda_fold_accepted(const uint16_t *qkv, int64_t ldqkv, const float *gate, const float *beta,
                       float *const *state, const int32_t *n_accept, int32_t B, int32_t K,
-                      int32_t heads, int32_t head_dim, hipStream_t stream)
+                      int32_t heads, int32_t head_dim, int32_t *status, hipStream_t stream)
 {
     if (B < 0 || K < 0 || heads <= 0 || B > kMaxGridYZ)
         return fail(KDA_ERR_SHAPE, "kda_fold_accepted: B=%d K=%d heads=%d", B, K, heads);
@@ -437,8 +441,10 @@ int kda_fold_accepted(const uint16_t *qkv, int64_t ldqkv, const float *gate, con
     if (ldqkv < 3LL * heads * head_dim)
         return fail(KDA_ERR_SHAPE, "kda_fold_accepted: ldqkv=%lld < 3*heads*head_dim",
                     (long long)ldqkv);
+    if (status && !aligned4(status))
+        return fail(KDA_ERR_SHAPE, "kda_fold_accepted: status must be 4-byte aligned");
     return hip_status(kda::launch_kda_fold(qkv, ldqkv, gate, beta, state, n_accept, B, K, heads,
-                                           head_dim, stream),
+                                           head_dim, status, stream),
                       "kda_fold_accepted launch");
 }
 
@@ -477,7 +483,8 @@ int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float 
         return fail(KDA_ERR_UNSUPPORTED, "kda_block_prefill: head_dim=%d chunk=%d", head_dim, chunk);
     const int64_t qkv = (int64_t)heads * head_dim, cd = 3 * qkv;
     if (T < 0 || T_pad < T || T_pad % chunk || heads <= 0 || hidden_size <= 0 || rank <= 0 ||
-        hidden_size % 8 || rank % 8 || qkv % 8 || T_pad > (1 << 24))
+        hidden_size % 8 || rank % 8 || qkv % 8 || T_pad > (1 << 24) ||
+        ((int64_t)T + kda::kConvRowsPerTile - 1) / kda::kConvRowsPerTile > kMaxGridYZ)
         return fail(KDA_ERR_SHAPE, "kda_block_prefill: T=%d T_pad=%d hidden=%d heads=%d rank=%d",
                     T, T_pad, hidden_size, heads, rank);
     if (T == 0) return ok();
@@ -782,7 +789,8 @@ int kda_block_verify_k(const uint16_t *hidden, const kda_block_weights *w, float
 
 int kda_block_fold_accepted(const kda_block_decode_buffers *b, float *const *state,
                             uint16_t *const *conv_state, const int32_t *n_accept, int32_t B,
-                            int32_t K, int32_t heads, int32_t head_dim, hipStream_t stream)
+                            int32_t K, int32_t heads, int32_t head_dim, int32_t *status,
+                            hipStream_t stream)
 {
     if (B < 0 || K < 0 || heads <= 0 || (int64_t)B * K > (1 << 24) || B > kMaxGridYZ)
         return fail(KDA_ERR_SHAPE, "kda_block_fold_accepted: B=%d K=%d heads=%d", B, K, heads);
@@ -792,12 +800,13 @@ int kda_block_fold_accepted(const kda_block_decode_buffers *b, float *const *sta
     if (!b || !state || !conv_state || !n_accept || !b->qkv_proj || !b->conv_out || !b->gate ||
         !b->beta)
         return fail(KDA_ERR_NULL, "kda_block_fold_accepted: null pointer argument");
-    if (!aligned16(b->qkv_proj) || !aligned16(b->conv_out) || !aligned16(b->gate))
+    if (!aligned16(b->qkv_proj) || !aligned16(b->conv_out) || !aligned16(b->gate) ||
+        (status && !aligned4(status)))
         return fail(KDA_ERR_SHAPE, "kda_block_fold_accepted: misaligned buffer");
     const int64_t cd = 3LL * heads * head_dim;
     int rc;
     if ((rc = hip_status(kda::launch_kda_fold(b->conv_out, cd, b->gate, b->beta, state, n_accept,
-                                              B, K, heads, head_dim, stream),
+                                              B, K, heads, head_dim, status, stream),
                          "kda_block_fold_accepted: state fold launch")) ||
         (rc = hip_status(kda::launch_conv_fold(b->qkv_proj, cd, conv_state, n_accept, B, K, heads,
                                                head_dim, stream),

@@ -26,10 +26,10 @@ namespace kda {
 
 constexpr int kConvThreads = 256;
 constexpr int kConvKC = 4;
-// 8 rows per tile (128 VGPRs, four waves per SIMD) measured fastest at
-// 8192 rows x 12288 channels: 84 us against 88 us for 4 rows, 98 us for 16
-// (160 VGPRs, three waves) and 126 us for 32 (two waves)
-constexpr int kConvRowsPerTile = 8;
+// kConvRowsPerTile (kda_launch.hpp): 8 rows per tile (128 VGPRs, four waves
+// per SIMD) measured fastest at 8192 rows x 12288 channels: 84 us against
+// 88 us for 4 rows, 98 us for 16 (160 VGPRs, three waves) and 126 us for 32
+// (two waves)
 
 template <int D>
 __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(

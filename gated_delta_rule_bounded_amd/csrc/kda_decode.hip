@@ -73,7 +73,7 @@ __global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_
     const uint16_t *__restrict__ qkv, int64_t ldqkv, const float *__restrict__ gate,
     const float *__restrict__ beta, float *const *__restrict__ state,
     float *const *__restrict__ snap, float *__restrict__ core, int K, int H, float scale,
-    bool write_state, const int32_t *__restrict__ n_accept)
+    bool write_state, const int32_t *__restrict__ n_accept, int32_t *__restrict__ status)
 {
     using Cfg = RecCfg<D, NS, RGT>;
     constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT, NP = Cfg::kPairs;
@@ -92,8 +92,13 @@ __global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_
     __shared__ float4 s_red[NP][2][CG];
     __shared__ float s_kq[NP];
 
-    // rows walked: all K, or the accepted ones when folding (none: nothing to do)
-    const int rows = n_accept ? min(max(n_accept[b], 0), K) : K;
+    // rows walked: all K, or the accepted ones when folding (none: nothing to
+    // do); a count outside [0, K] is clamped and reported (one thread per
+    // sequence)
+    const int na = n_accept ? n_accept[b] : K;
+    if (status != nullptr && (na < 0 || na > K) && blockIdx.x == 0 && tid == 0)
+        atomicOr(status, kReportAcceptClamped);
+    const int rows = min(max(na, 0), K);
     if (rows == 0) return;   // uniform over the workgroup
 
     float *__restrict__ Sg = state[b] + (size_t)h * D * D + c0;
@@ -207,11 +212,12 @@ template <int D, int NS, int RGT = 1>
 static hipError_t recurrent_ns(const uint16_t *qkv, int64_t ldqkv, const float *gate,
                                const float *beta, float *const *state, float *const *snap,
                                float *core, int B, int K, int heads, float scale,
-                               bool write_state, const int32_t *n_accept, hipStream_t stream)
+                               bool write_state, const int32_t *n_accept, int32_t *status,
+                               hipStream_t stream)
 {
     hipLaunchKernelGGL((kda_recurrent_kernel<D, NS, RGT>), dim3(heads * NS, B),
                        dim3(RecCfg<D, NS, RGT>::kThreads), 0, stream, qkv, ldqkv, gate, beta,
-                       state, snap, core, K, heads, scale, write_state, n_accept);
+                       state, snap, core, K, heads, scale, write_state, n_accept, status);
     return hipGetLastError();
 }
 
@@ -222,16 +228,16 @@ template <int D>
 static hipError_t recurrent_t(const uint16_t *qkv, int64_t ldqkv, const float *gate,
                               const float *beta, float *const *state, float *const *snap,
                               float *core, int B, int K, int heads, float scale, bool write_state,
-                              const int32_t *n_accept, hipStream_t stream)
+                              const int32_t *n_accept, int32_t *status, hipStream_t stream)
 {
     const int64_t pairs = (int64_t)B * heads;
     if constexpr (D >= 128) {
         if (pairs <= 128)
             return recurrent_ns<D, 4>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
-                                      write_state, n_accept, stream);
+                                      write_state, n_accept, status, stream);
         if (pairs <= 256)
             return recurrent_ns<D, 2>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
-                                      write_state, n_accept, stream);
+                                      write_state, n_accept, status, stream);
     }
     // whole heads: the write-on-accept verify (state read only) and fold run
     // two row groups per thread (256 threads, more state in flight per CU);
@@ -239,9 +245,9 @@ static hipError_t recurrent_t(const uint16_t *qkv, int64_t ldqkv, const float *g
     if constexpr (D >= 128)
         if (!write_state || n_accept)
             return recurrent_ns<D, 1, 2>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads,
-                                         scale, write_state, n_accept, stream);
+                                         scale, write_state, n_accept, status, stream);
     return recurrent_ns<D, 1>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
-                              write_state, n_accept, stream);
+                              write_state, n_accept, status, stream);
 }
 
 hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float *gate,
@@ -251,9 +257,9 @@ hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float 
 {
     return head_dim == 128
                ? recurrent_t<128>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
-                                  true, nullptr, stream)
+                                  true, nullptr, nullptr, stream)
                : recurrent_t<16>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
-                                 true, nullptr, stream);
+                                 true, nullptr, nullptr, stream);
 }
 
 hipError_t launch_kda_verify(const uint16_t *qkv, int64_t ldqkv, const float *gate,
@@ -262,20 +268,21 @@ hipError_t launch_kda_verify(const uint16_t *qkv, int64_t ldqkv, const float *ga
 {
     return head_dim == 128
                ? recurrent_t<128>(qkv, ldqkv, gate, beta, state, nullptr, core, B, K, heads,
-                                  scale, false, nullptr, stream)
+                                  scale, false, nullptr, nullptr, stream)
                : recurrent_t<16>(qkv, ldqkv, gate, beta, state, nullptr, core, B, K, heads,
-                                 scale, false, nullptr, stream);
+                                 scale, false, nullptr, nullptr, stream);
 }
 
 hipError_t launch_kda_fold(const uint16_t *qkv, int64_t ldqkv, const float *gate,
                            const float *beta, float *const *state, const int32_t *n_accept,
-                           int B, int K, int heads, int head_dim, hipStream_t stream)
+                           int B, int K, int heads, int head_dim, int32_t *status,
+                           hipStream_t stream)
 {
     return head_dim == 128
                ? recurrent_t<128>(qkv, ldqkv, gate, beta, state, nullptr, nullptr, B, K, heads,
-                                  1.f, true, n_accept, stream)
+                                  1.f, true, n_accept, status, stream)
                : recurrent_t<16>(qkv, ldqkv, gate, beta, state, nullptr, nullptr, B, K, heads,
-                                 1.f, true, n_accept, stream);
+                                 1.f, true, n_accept, status, stream);
 }
 
 }  // namespace kda

@@ -10,6 +10,14 @@
 
 namespace kda {
 
+// Run-time report bits (the KDA_REPORT_* values of kda.h) that kernels OR
+// into a caller's status word with a vector atomic.
+constexpr int32_t kReportSeqSkipped = 1, kReportRowsClamped = 2, kReportAcceptClamped = 4;
+
+// Rows per conv_silu_l2 workgroup tile: a launch's row tiles form grid y,
+// so a sequence holds at most 65535 tiles of this many rows.
+constexpr int kConvRowsPerTile = 8;
+
 hipError_t launch_conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w,
                                uint16_t *const *conv_state, uint16_t *const *conv_snap,
                                int n_seq, int rows, int heads, int head_dim, float eps_l2,
@@ -46,7 +54,8 @@ hipError_t launch_kda_verify(const uint16_t *qkv, int64_t ldqkv, const float *ga
                              int heads, int head_dim, float scale, hipStream_t stream);
 hipError_t launch_kda_fold(const uint16_t *qkv, int64_t ldqkv, const float *gate,
                            const float *beta, float *const *state, const int32_t *n_accept,
-                           int B, int K, int heads, int head_dim, hipStream_t stream);
+                           int B, int K, int heads, int head_dim, int32_t *status,
+                           hipStream_t stream);
 
 size_t prefill_workspace_bytes(int T_pad, int heads, int head_dim, int chunk);
 int prefill_segment_chunks(int T, int heads, int head_dim, int chunk);
@@ -82,7 +91,8 @@ hipError_t launch_kda_prefill_varlen(const float *q, const float *k, const float
                                      const float *gate, const float *beta, float *const *state,
                                      float *core, const int32_t *cu_seqlens, int B, int64_t rows,
                                      int max_chunks, int total_chunks, int heads, int head_dim,
-                                     int chunk, float scale, void *workspace, hipStream_t stream);
+                                     int chunk, float scale, void *workspace, int32_t *status,
+                                     hipStream_t stream);
 
 // Row-order-exact bf16 products y = bf16(x w^T) for a few rows (kda_gemv.hip).
 // Each segment has its own x [M][Kd] (stride ldx), w [N][Kd] (contiguous

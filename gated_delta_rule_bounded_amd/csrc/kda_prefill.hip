@@ -178,7 +178,8 @@ hipError_t launch_kda_prefill_varlen(const float *q, const float *k, const float
                                      const float *gate, const float *beta, float *const *state,
                                      float *core, const int32_t *cu_seqlens, int B, int64_t rows,
                                      int max_chunks, int total_chunks, int heads, int head_dim,
-                                     int chunk, float scale, void *workspace, hipStream_t stream)
+                                     int chunk, float scale, void *workspace, int32_t *status,
+                                     hipStream_t stream)
 {
     // Segments of global chunks sized as kda_prefill's: each is prepared into
     // the start of the workspace and walked at once (one walk per sequence,
@@ -187,7 +188,7 @@ hipError_t launch_kda_prefill_varlen(const float *q, const float *k, const float
     const int seg = prefill_segment_chunks(total_chunks * chunk, heads, head_dim, chunk);
     for (int lo = 0; lo < total_chunks; lo += seg) {
         const Varlen vl{cu_seqlens, state, rows, max_chunks, total_chunks, lo,
-                        std::min(lo + seg, total_chunks)};
+                        std::min(lo + seg, total_chunks), status};
         hipError_t e = KDA_PREFILL_DISPATCH(prepare_t, q, k, v, gate, beta, 0, heads, workspace,
                                             vl, B, stream);
         if (e != hipSuccess) return e;

@@ -74,6 +74,7 @@ struct Varlen {
     int32_t max_chunks;     // chunks of the longest sequence (prepare grid)
     int32_t total_chunks;   // chunks of all sequences
     int32_t seg_lo, seg_hi; // global chunks of this launch; block 0 of the workspace = seg_lo
+    int32_t *status;        // run-time report word (KDA_REPORT_* bits), or nullptr
 };
 
 struct SeqSpan {
@@ -111,6 +112,22 @@ __device__ __forceinline__ SeqSpan seq_span(const Varlen &vl, int s)
     r.chunk0 = acc;
     r.ok = r.nch <= vl.max_chunks && r.chunk0 + r.nch <= vl.total_chunks;
     return r;
+}
+
+// Report bits of a several-sequence call (the KDA_REPORT_* values of kda.h):
+// a sequence that is skipped because its chunks do not fit max_chunks /
+// total_chunks, and offsets that had to be clamped.  One thread per sequence
+// reports, in the first segment's prepare launch; the bits are ORed into the
+// caller's word with a vector atomic.
+__device__ __forceinline__ void varlen_report(const Varlen &vl, int s, bool ok)
+{
+    if (vl.status == nullptr || vl.seg_lo != 0 || blockIdx.x != 0 || blockIdx.y != 0 ||
+        threadIdx.x != 0)
+        return;
+    const int64_t a = vl.cu[s], b = vl.cu[s + 1];
+    const int32_t bits = (ok ? 0 : kReportSeqSkipped) |
+                         (a < 0 || b < a || b > vl.rows ? kReportRowsClamped : 0);
+    if (bits) atomicOr(vl.status, bits);
 }
 
 template <int D, int C>
@@ -411,6 +428,7 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
     if (vl.cu) {
         const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
+        varlen_report(vl, blockIdx.z, sp.ok);
         nblk = sp.chunk0 + n;
         if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
         nblk -= vl.seg_lo;
@@ -686,6 +704,7 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
     if (vl.cu) {
         const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
+        varlen_report(vl, blockIdx.z, sp.ok);
         nblk = sp.chunk0 + n;
         if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
         nblk -= vl.seg_lo;

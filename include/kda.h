@@ -50,6 +50,20 @@ typedef enum kda_status {
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char *kda_last_error(void);
 
+/* Run-time report bits.  A few calls take their sizes from device memory
+ * (cu_seqlens, n_accept), which the host cannot check before the launch.
+ * Such a call takes an optional `status` argument: a device int32 word that
+ * the kernels OR these bits into when they meet a value they had to clamp or
+ * a sequence they had to skip.  The library never clears the word (the
+ * caller zeroes it and reads it when it likes), so one word can collect the
+ * reports of many calls; NULL turns the report off.  The results of a call
+ * whose report is 0 are exactly as documented. */
+#define KDA_REPORT_SEQ_SKIPPED 1     /* a sequence's chunks exceed max_chunks or
+                                        total_chunks: it was left untouched      */
+#define KDA_REPORT_ROWS_CLAMPED 2    /* cu_seqlens decreasing, negative or past
+                                        rows: the offsets were clamped           */
+#define KDA_REPORT_ACCEPT_CLAMPED 4  /* an n_accept outside [0, K] was clamped   */
+
 /* ------------------------------------------------------------------------
  * conv_silu_l2 — short causal depthwise conv + SiLU + per-head L2 of q and k.
  * "Glm5NextKdaWorkspace" page, fields qkv_proj and conv_out (conv + SiLU with
@@ -238,13 +252,20 @@ int kda_prefill_split(const float *q, const float *k, const float *v,
  * past the workspace.  Rows are clamped to [0, rows).  B == 0 or
  * total_chunks == 0 is a no-op.  Errors as kda_prefill; B and max_chunks at
  * most 65535.
+ *   status      optional device int32 word (NULL: no report): gets
+ *               KDA_REPORT_SEQ_SKIPPED when a sequence was skipped as above
+ *               and KDA_REPORT_ROWS_CLAMPED when an offset was clamped; both
+ *               are the "default returns an error" of the page's batched
+ *               prefill turned into a report, since the lengths are only
+ *               known on the device.
  * ------------------------------------------------------------------------ */
 int kda_prefill_varlen(const float *q, const float *k, const float *v,
                        const float *gate, const float *beta, float *const *state,
                        float *core, const int32_t *cu_seqlens, int32_t B,
                        int32_t rows, int32_t max_chunks, int32_t total_chunks,
                        int32_t heads, int32_t head_dim, int32_t chunk, float scale,
-                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+                       void *workspace, size_t workspace_bytes, int32_t *status,
+                       hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * kda_decode — one token for each of B independent sequences.
@@ -301,6 +322,8 @@ int kda_decode_k(const uint16_t *qkv, int64_t ldqkv, const float *gate,
  *   [0, K].  Afterwards *state[b] is bitwise the state kda_decode_k would
  *   have left after row n_accept[b]-1 (its snapshot, or its final state for
  *   n_accept[b] == K); n_accept[b] == 0 leaves it untouched.  Writes no output.
+ *   status: optional device int32 word (NULL: no report) that gets
+ *   KDA_REPORT_ACCEPT_CLAMPED when some n_accept[b] lay outside [0, K].
  * Errors as kda_decode_k (n_accept required).  B == 0 or K == 0 is a no-op.
  * ------------------------------------------------------------------------ */
 int kda_verify_k(const uint16_t *qkv, int64_t ldqkv, const float *gate,
@@ -311,7 +334,7 @@ int kda_verify_k(const uint16_t *qkv, int64_t ldqkv, const float *gate,
 int kda_fold_accepted(const uint16_t *qkv, int64_t ldqkv, const float *gate,
                       const float *beta, float *const *state, const int32_t *n_accept,
                       int32_t B, int32_t K, int32_t heads, int32_t head_dim,
-                      hipStream_t stream);
+                      int32_t *status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * gated_rmsnorm — sigmoid-gated RMSNorm of the core output, per (token, head).
@@ -482,7 +505,8 @@ int kda_block_decode_k(const uint16_t *hidden, const kda_block_weights *w,
  *   and *conv_state[b] are bitwise the recurrent and conv snapshots
  *   kda_block_decode_k would have written after row n_accept[b]-1 (its final
  *   states for n_accept[b] == K); n_accept[b] == 0 leaves both untouched.
- *   Two launches; no output.  Errors as kda_block_decode_k.
+ *   Two launches; no output; `status` as kda_fold_accepted.  Errors as
+ *   kda_block_decode_k.
  * ------------------------------------------------------------------------ */
 int kda_block_verify_k(const uint16_t *hidden, const kda_block_weights *w,
                        float *const *state, uint16_t *const *conv_state,
@@ -493,7 +517,8 @@ int kda_block_verify_k(const uint16_t *hidden, const kda_block_weights *w,
 
 int kda_block_fold_accepted(const kda_block_decode_buffers *buf, float *const *state,
                             uint16_t *const *conv_state, const int32_t *n_accept, int32_t B,
-                            int32_t K, int32_t heads, int32_t head_dim, hipStream_t stream);
+                            int32_t K, int32_t heads, int32_t head_dim, int32_t *status,
+                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * kda_block_decode — one token for each of B sequences through the whole

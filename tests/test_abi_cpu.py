@@ -189,6 +189,10 @@ def test_block_validation(lib):
     assert call(out=w2.q_proj) == E_ALIAS                    # writing over a weight
     assert call(state=b2.core + 64) == E_ALIAS
     assert call(x=b2.qkv_proj) == E_ALIAS                    # a buffer over the input
+    # the block's conv launch takes T rows as 8-row tiles in grid y
+    w3, b3 = _block_args(lib)
+    b3.prefill_ws_bytes = lib.kda_prefill_workspace_bytes(65535 * 8 + 16, H, Dh, 16)
+    assert call(b_=b3, T=65535 * 8 + 1, T_pad=65535 * 8 + 16) == E_SHAPE
 
 
 def test_gemv_validation(lib):
@@ -258,10 +262,10 @@ def test_varlen_validation(lib):
     ws = lib.kda_prefill_workspace_bytes(10 * C, H, Dh, C)
 
     def call(q=A, core=B, cu=C, state=Dp, wsp=E, ws_bytes=ws, Bn=3, rows=100, mx=4, tot=10,
-             head_dim=Dh, chunk=C):
+             head_dim=Dh, chunk=C, status=None):
         return lib.kda_prefill_varlen(q, q + (1 << 30), q + (2 << 30), q + (3 << 30),
                                       q + (4 << 30), state, core, cu, Bn, rows, mx, tot, H,
-                                      head_dim, chunk, 0.25, wsp, ws_bytes, None)
+                                      head_dim, chunk, 0.25, wsp, ws_bytes, status, None)
 
     assert call(Bn=0) == OK and call(tot=0) == OK and call(rows=0) == OK
     assert call(head_dim=64) == E_UNSUP
@@ -274,14 +278,15 @@ def test_varlen_validation(lib):
     assert call(core=A + 64) == E_ALIAS                        # core over q
     assert call(wsp=B + 256) == E_ALIAS                        # workspace over core
     assert call(q=A + 4) == E_SHAPE                            # misaligned
+    assert call(status=F + 2) == E_SHAPE                       # report word not 4-byte aligned
 
 
 def test_write_on_accept_validation(lib):
     def verify(qkv=A, ld=3 * 32, core=B, Bn=2, K=4, head_dim=16, state=C):
         return lib.kda_verify_k(qkv, ld, Dp, E, state, core, Bn, K, 2, head_dim, 0.25, None)
 
-    def fold(qkv=A, ld=3 * 32, na=F, Bn=2, K=4, head_dim=16, state=C):
-        return lib.kda_fold_accepted(qkv, ld, Dp, E, state, na, Bn, K, 2, head_dim, None)
+    def fold(qkv=A, ld=3 * 32, na=F, Bn=2, K=4, head_dim=16, state=C, status=None):
+        return lib.kda_fold_accepted(qkv, ld, Dp, E, state, na, Bn, K, 2, head_dim, status, None)
 
     assert verify(K=0) == OK and fold(Bn=0) == OK
     assert verify(head_dim=64) == E_UNSUP and fold(head_dim=64) == E_UNSUP
@@ -289,6 +294,7 @@ def test_write_on_accept_validation(lib):
     assert verify(ld=90) == E_SHAPE and fold(ld=90) == E_SHAPE
     assert verify(state=0) == E_NULL and fold(na=0) == E_NULL
     assert verify(core=A + 64) == E_ALIAS                     # core over the qkv rows
+    assert fold(status=F + 2) == E_SHAPE                      # report word not 4-byte aligned
 
 
 def test_prefill_split_validation(lib):
@@ -322,14 +328,17 @@ def test_block_write_on_accept_validation(lib):
     assert lib.kda_block_verify_k(63 << 36, ref(w), 60 << 36, 61 << 36, ref(b), w.q_proj, 3, 4,
                                   64, 2, 16, 32, 0.25, 1e-6, 1e-5, None) == E_ALIAS
     assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 64 << 36, 0, 4, 2, 16,
-                                       None) == OK
+                                       None, None) == OK
     assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 64 << 36, 3, 4, 2, 64,
-                                       None) == E_UNSUP
-    assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 0, 3, 4, 2, 16, None) == E_NULL
-    assert lib.kda_block_fold_accepted(None, 60 << 36, 61 << 36, 64 << 36, 3, 4, 2, 16,
+                                       None, None) == E_UNSUP
+    assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 0, 3, 4, 2, 16, None,
                                        None) == E_NULL
+    assert lib.kda_block_fold_accepted(None, 60 << 36, 61 << 36, 64 << 36, 3, 4, 2, 16,
+                                       None, None) == E_NULL
     assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 64 << 36, 3, -1, 2, 16,
-                                       None) == E_SHAPE
+                                       None, None) == E_SHAPE
+    assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 64 << 36, 3, 4, 2, 16,
+                                       (65 << 36) + 1, None) == E_SHAPE
 
 
 def test_grid_limits_are_shape_errors(lib):
@@ -337,9 +346,13 @@ def test_grid_limits_are_shape_errors(lib):
     assert lib.kda_decode(A, 96, B, C, Dp, E, 70000, 2, 16, 0.25, None) == E_SHAPE
     assert lib.kda_decode_k(A, 96, B, C, Dp, 0, E, 70000, 2, 2, 16, 0.25, None) == E_SHAPE
     assert lib.kda_verify_k(A, 96, B, C, Dp, E, 70000, 2, 2, 16, 0.25, None) == E_SHAPE
-    assert lib.kda_fold_accepted(A, 96, B, C, Dp, E, 70000, 2, 2, 16, None) == E_SHAPE
+    assert lib.kda_fold_accepted(A, 96, B, C, Dp, E, 70000, 2, 2, 16, None, None) == E_SHAPE
     assert lib.conv_silu_l2(A, 96, B, None, None, 70000, 1, 2, 16, 4, 1e-6, C, 96,
                             None, None, None, None) == E_SHAPE
+    # a sequence of conv rows is at most 65535 row tiles of 8 rows (grid y)
+    assert lib.conv_silu_l2(A, 96, B, None, None, 1, 65535 * 8 + 1, 2, 16, 4, 1e-6, C, 96,
+                            None, None, None, None) == E_SHAPE
+    assert "rows=524281" in lib.kda_last_error().decode()
     assert lib.dense_gemv_bf16_batchm(A, 256, B, 65535 * 64 + 1, 48, 256, C, 48, None) == E_SHAPE
 
 
@@ -347,7 +360,7 @@ def test_block_fold_alignment(lib):
     b = _decode_bufs()
     b.conv_out += 2
     assert lib.kda_block_fold_accepted(ctypes.byref(b), 60 << 36, 61 << 36, 64 << 36, 3, 4, 2, 16,
-                                       None) == E_SHAPE
+                                       None, None) == E_SHAPE
 
 
 def test_prefill_bf16_validation(lib):

@@ -27,7 +27,10 @@ STAGES = ("qkv_proj", "conv_out", "fa", "g_raw", "b_raw", "gate", "beta", "core"
 
 
 def run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=False,
-            f32_copies=False):
+            f32_copies=False, keep=None):
+    """One kda_block_prefill call; returns every stage buffer's first T rows,
+    the output and the carried states as numpy.  ``keep``, a dict, receives
+    the device buffers for further GPU calls."""
     dev = torch.device("cuda")
     wd = {n: t.to(dev).contiguous() for n, t in w.items()}
     if packed:   # q, k, v weights back to back: the block runs them as one GEMM
@@ -45,6 +48,8 @@ def run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=Fals
                           hidden_size=hidden, heads=H, head_dim=D, rank=rank, chunk=C,
                           scale=scale)
     torch.cuda.synchronize()
+    if keep is not None:
+        keep.update(buf)
     res = {n: buf[n][:T].float().cpu().numpy() for n in STAGES}
     res["final_out"] = out.float().cpu().numpy()
     res["state"] = st.cpu().numpy()
@@ -91,17 +96,32 @@ def test_block_full_size_causal_prefix(orc):
     # the full KDA block workload: T = 8192, hidden 4096, 32 heads x 128,
     # rank-128 gates, weights ~ N(0, 0.02), zero initial state and conv state
     T, T_pad, H, D, hidden, rank, C = 8192, 8192, 32, 128, 4096, 128, 64
-    Tp = 256
+    Tp = 512
     x, w = workloads.block_raw(T, hidden, H, D, rank, 4, 1004)
     S0 = np.zeros((H, D, D), dtype=np.float32)
     conv0 = torch.zeros(4, 3 * H * D, dtype=torch.bfloat16)
     scale = D ** -0.5
-    got = run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=True)
+    buf = {}
+    got = run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=True, keep=buf)
     ref = run_oracle(orc, x, w, Tp, H, D, S0, conv0, scale)
     compare(got, ref, Tp, H, D, STAGES + ("final_out",))
     for n in STAGES + ("final_out",):
         assert np.all(np.isfinite(got[n])), n
     assert np.all(np.isfinite(got["state"]))
+    # The block runs its core on its own conv_out, gate and beta: a
+    # kda_prefill_bf16 call on those buffers from the same (zero) state gives
+    # the block's core rows and carried state after all 8192 rows, bit for bit.
+    dev = torch.device("cuda")
+    st = torch.zeros(H, D, D, device=dev)
+    core = torch.empty(T_pad, H, D, device=dev)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(T_pad, H, D, C), dtype=torch.uint8,
+                     device=dev)
+    say("block core rerun", T)
+    kda.kda_prefill_bf16(buf["conv_out"], buf["gate"], buf["beta"], st, core, ws, T=T,
+                         T_pad=T_pad, heads=H, head_dim=D, chunk=C, scale=scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(st.cpu().numpy(), got["state"])
+    np.testing.assert_array_equal(core[:T].cpu().numpy(), got["core"].reshape(T, H, D))
 
 
 def test_block_split_equals_one_call():

@@ -270,9 +270,11 @@ def test_block_write_on_accept_equals_snapshots(B, K, H, D, hidden, rank):
         np.testing.assert_array_equal(convs[b].float().cpu().numpy(), conv0[b].float().numpy())
     na = np.array([(b % (K + 3)) - 1 for b in range(B)], np.int32) if B > 1 else np.array([2], np.int32)
     say("block fold_accepted", B, K, list(na))
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
     kda.kda_block_fold_accepted(buf, st_tab, cv_tab, torch.from_numpy(na).cuda(), B=B, K=K,
-                                heads=H, head_dim=D)
+                                heads=H, head_dim=D, status=status)
     torch.cuda.synchronize()
+    assert int(status.item()) == (4 if np.any((na < 0) | (na > K)) else 0)
     for b in range(B):
         n = min(max(int(na[b]), 0), K)
         if n == 0:

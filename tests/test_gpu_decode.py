@@ -184,10 +184,22 @@ def test_write_on_accept_equals_snapshots(B, K, H, D):
     np.testing.assert_array_equal(core.view(B, K, H, D).cpu().numpy(), ck)
     np.testing.assert_array_equal(st.cpu().numpy(), S0)
     na = np.array([(b % (K + 3)) - 1 for b in range(B)], np.int32)   # -1, 0, .., K, K+1, ...
+    # the run-time report: out-of-range counts set KDA_REPORT_ACCEPT_CLAMPED
+    # (4), in-range ones leave the word as it was
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
     say("fold_accepted", B, K, H, D)
     kda.kda_fold_accepted(qkv, gate, beta, tab, torch.from_numpy(na).cuda(), B=B, K=K, heads=H,
-                          head_dim=D)
+                          head_dim=D, status=status)
     torch.cuda.synchronize()
+    assert int(status.item()) == (4 if np.any((na < 0) | (na > K)) else 0)
+    st_in = cuda(S0)
+    ok_na = torch.from_numpy(np.clip(na, 0, K)).cuda()
+    status.zero_()
+    kda.kda_fold_accepted(qkv, gate, beta, kda.ptr_table(st_in), ok_na, B=B, K=K, heads=H,
+                          head_dim=D, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    np.testing.assert_array_equal(st_in.cpu().numpy(), st.cpu().numpy())
     got = st.cpu().numpy()
     sn = snaps.view(B, K - 1, H, D, D).cpu().numpy() if K > 1 else None
     for b in range(B):

@@ -180,6 +180,10 @@ def test_prefill_full_size_h32_d128(T, T_pad, fill):
     e_core, e_S = relerr(core[:T], ref_core), relerr(S, ref_S)
     print(f"relerr core {e_core:.3e} state {e_S:.3e}")
     assert e_core < TOL and e_S < TOL
+    # and per head, for the core rows and the carried state alike
+    for h in range(H):
+        eh_c, eh_s = relerr(core[:T, h], ref_core[:, h]), relerr(S[h], ref_S[h])
+        assert eh_c < TOL and eh_s < TOL, f"head {h}: core {eh_c:.3e} state {eh_s:.3e}"
     if T_pad > T:
         assert np.all(core[T:] == 7.0)
 

@@ -16,7 +16,11 @@ TOL = 2e-3
 SENTINEL = 7.0
 
 
-def run_varlen(cases, H, D, C, scale, tail=3, tail_fill=np.nan, total_chunks=None):
+def run_varlen(cases, H, D, C, scale, tail=3, tail_fill=np.nan, total_chunks=None, report=0,
+               cu_first=0):
+    """One kda_prefill_varlen call over the cases; its run-time report word
+    must come out as ``report``.  ``cu_first`` replaces cu_seqlens[0] (a
+    negative value is clamped to row 0 and reported)."""
     lengths = [c["q"].shape[0] for c in cases]
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     rows = int(cu[-1]) + tail      # rows past the last sequence hold poison
@@ -36,11 +40,15 @@ def run_varlen(cases, H, D, C, scale, tail=3, tail_fill=np.nan, total_chunks=Non
     ws = torch.empty(max(1, kda.kda_prefill_workspace_bytes(max(tot, 1) * C, H, D, C)),
                      dtype=torch.uint8, device="cuda")
     say("varlen", lengths, H, D, C, tot)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cu_dev = cu.copy()
+    cu_dev[0] = cu_first
     kda.kda_prefill_varlen(q, k, v, g, b, kda.ptr_table(states), core,
-                           torch.from_numpy(cu).cuda(), ws, B=len(cases), rows=rows,
+                           torch.from_numpy(cu_dev).cuda(), ws, B=len(cases), rows=rows,
                            max_chunks=mx, total_chunks=tot, heads=H, head_dim=D, chunk=C,
-                           scale=scale)
+                           scale=scale, status=status)
     torch.cuda.synchronize()
+    assert int(status.item()) == report, f"report word {int(status.item())}, expected {report}"
     return cu, core.cpu().numpy(), [s.cpu().numpy() for s in states]
 
 
@@ -103,7 +111,8 @@ def test_varlen_sequence_outside_the_workspace_is_left_alone():
     scale = D ** -0.5
     cases = [core_case(T, H, D, 1600 + s, 0.05) for s, T in enumerate(lengths)]
     _, tot = kda.varlen_chunks(lengths, C)
-    cu, core, states = run_varlen(cases, H, D, C, scale, total_chunks=tot - 1)
+    # the skip is reported (KDA_REPORT_SEQ_SKIPPED)
+    cu, core, states = run_varlen(cases, H, D, C, scale, total_chunks=tot - 1, report=1)
     np.testing.assert_array_equal(states[2], cases[2]["S0"])
     assert np.all(core[cu[2]:cu[3]] == SENTINEL)
     for s in (0, 1):
@@ -140,3 +149,18 @@ def test_varlen_single_chunk_prompts_same_bits_in_both_forward_instances():
                                                c["S0"], scale, threads=THREADS)
     assert relerr(core_b[cu_b[-2]:cu_b[-1]], ref_core) < TOL
     assert relerr(states_b[-1], ref_S) < TOL
+
+
+def test_varlen_clamped_offset_is_reported():
+    # cu_seqlens[0] = -5 is clamped to row 0 (KDA_REPORT_ROWS_CLAMPED); the
+    # rows and states are those of the call with the offset given as 0
+    H, D, C = 2, 16, 16
+    lengths = [40, 17, 33]
+    scale = D ** -0.5
+    cases = [core_case(T, H, D, 1650 + s, 0.05) for s, T in enumerate(lengths)]
+    cu_a, core_a, states_a = run_varlen(cases, H, D, C, scale)
+    cases_b = [dict(c, S0=c["S0"].copy()) for c in cases]
+    cu_b, core_b, states_b = run_varlen(cases_b, H, D, C, scale, report=2, cu_first=-5)
+    np.testing.assert_array_equal(core_a, core_b)
+    for a, b in zip(states_a, states_b):
+        np.testing.assert_array_equal(a, b)

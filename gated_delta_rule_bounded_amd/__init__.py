@@ -18,7 +18,7 @@ import torch  # loads the HIP runtime that libkda then shares
 from . import _lib
 from ._lib import KdaError, last_error  # noqa: F401
 
-__all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_prepare",
+__all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_noalloc", "kda_prefill_prepare",
            "kda_prefill_forward", "kda_decode", "kda_decode_k",
            "gated_rmsnorm", "kda_prefill_workspace_bytes", "kda_prefill_segment_chunks",
            "kda_block_prefill", "block_buffers", "BLOCK_WEIGHT_NAMES",
@@ -205,6 +205,19 @@ def kda_prefill(q, k, v, gate, beta, state, core, workspace, *, T, T_pad, heads,
         _ptr(beta, f, "beta"), _ptr(state, f, "state"), _ptr(core, f, "core"),
         T, T_pad, heads, head_dim, chunk, float(scale), _ptr(workspace, None, "workspace"),
         _nbytes(workspace), _stream()))
+
+
+def kda_prefill_noalloc(q, k, v, gate, beta, state, core, *, T, T_pad, heads, head_dim, chunk,
+                        scale):
+    """kda_prefill without a workspace argument: the operand blocks go to the
+    library's own 64 MiB device array (see include/kda.h for sharing)."""
+    f = torch.float32
+    _prefill_sizes(T_pad, heads, head_dim, q=q, k=k, v=v, gate=gate, beta=beta, state=state,
+                   core=core)
+    _check(_lib.lib.kda_prefill_noalloc(
+        _ptr(q, f, "q"), _ptr(k, f, "k"), _ptr(v, f, "v"), _ptr(gate, f, "gate"),
+        _ptr(beta, f, "beta"), _ptr(state, f, "state"), _ptr(core, f, "core"),
+        T, T_pad, heads, head_dim, chunk, float(scale), _stream()))
 
 
 def kda_prefill_prepare(q, k, v, gate, beta, workspace, *, T, T_pad, heads, head_dim, chunk):

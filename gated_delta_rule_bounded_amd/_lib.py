@@ -16,7 +16,7 @@ SYMBOLS = ("kda_last_error", "conv_silu_l2", "kda_gate", "kda_prefill_workspace_
            "kda_block_prefill", "dense_gemv_bf16_batchm", "kda_block_decode_k",
            "kda_block_decode", "kda_prefill_varlen", "kda_verify_k", "kda_fold_accepted",
            "kda_prefill_split", "kda_block_verify_k", "kda_block_fold_accepted",
-           "kda_prefill_bf16")
+           "kda_prefill_bf16", "kda_prefill_noalloc")
 
 
 class BlockWeights(ctypes.Structure):
@@ -68,6 +68,8 @@ def _load():
     lib.kda_prefill.restype = ctypes.c_int
     lib.kda_prefill.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, f32, P,
                                 ctypes.c_size_t, P]
+    lib.kda_prefill_noalloc.restype = ctypes.c_int
+    lib.kda_prefill_noalloc.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, f32, P]
     lib.kda_prefill_prepare.restype = ctypes.c_int
     lib.kda_prefill_prepare.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, P,
                                         ctypes.c_size_t, P]

@@ -18,7 +18,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "kda_gemm.cpp", "conv_silu_l2.hip", "kda_gate.hip", "gated_rmsnorm.hip",
-           "kda_decode.hip", "kda_prefill.hip", "kda_prefill_short.hip", "kda_gemv.hip"]
+           "kda_decode.hip", "kda_prefill.hip", "kda_prefill_short.hip", "kda_gemv.hip",
+           "kda_noalloc.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

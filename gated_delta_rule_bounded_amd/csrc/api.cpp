@@ -126,7 +126,8 @@ static int check_prefill(const char *who, const float *q, const float *k, const 
                          const float *gate, const float *beta, const float *state,
                          const float *core, int32_t T, int32_t T_pad, int32_t heads,
                          int32_t head_dim, int32_t chunk, const void *workspace,
-                         size_t workspace_bytes, bool need_v, bool need_beta, bool need_out)
+                         size_t workspace_bytes, bool need_v, bool need_beta, bool need_out,
+                         bool own_ws = false)
 {
     if (!head_dim_ok(head_dim) || !(chunk == 16 || chunk == 64))
         return fail(KDA_ERR_UNSUPPORTED, "%s: head_dim=%d chunk=%d (need 16|128, 16|64)", who,
@@ -135,10 +136,12 @@ static int check_prefill(const char *who, const float *q, const float *k, const 
         return fail(KDA_ERR_SHAPE, "%s: T=%d T_pad=%d heads=%d chunk=%d", who, T, T_pad, heads,
                     chunk);
     if (T == 0) return 1;   // no-op
-    if (!q || !k || !gate || !workspace || (need_v && !v) || (need_beta && !beta) ||
+    if (!q || !k || !gate || (!workspace && !own_ws) || (need_v && !v) || (need_beta && !beta) ||
         (need_out && (!state || !core)))
         return fail(KDA_ERR_NULL, "%s: null pointer argument", who);
-    const size_t need = kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
+    // own_ws: the library's own scratch array (never a caller region), so
+    // there is no caller workspace to size or to check for overlap
+    const size_t need = own_ws ? 0 : kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
     if (workspace_bytes < need)
         return fail(KDA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", who,
                     workspace_bytes, need);
@@ -179,6 +182,27 @@ int kda_prefill(const float *q, const float *k, const float *v, const float *gat
     return hip_status(kda::launch_kda_prefill(q, k, v, gate, beta, state, core, T, heads,
                                               head_dim, chunk, scale, workspace, stream),
                       "kda_prefill launch");
+}
+
+int kda_prefill_noalloc(const float *q, const float *k, const float *v, const float *gate,
+                        const float *beta, float *state, float *core, int32_t T, int32_t T_pad,
+                        int32_t heads, int32_t head_dim, int32_t chunk, float scale,
+                        hipStream_t stream)
+{
+    const int rc = check_prefill("kda_prefill_noalloc", q, k, v, gate, beta, state, core, T,
+                                 T_pad, heads, head_dim, chunk, nullptr, 0, true, true, true,
+                                 true);
+    if (rc == 1) return ok();
+    if (rc) return rc;
+    const size_t per_chunk = kda::prefill_workspace_bytes(chunk, heads, head_dim, chunk);
+    if (per_chunk > kda::kNoallocScratchBytes)
+        return fail(KDA_ERR_WORKSPACE,
+                    "kda_prefill_noalloc: one chunk of %d heads needs %zu bytes of operand blocks, "
+                    "more than the %zu-byte scratch array", heads, per_chunk,
+                    kda::kNoallocScratchBytes);
+    return hip_status(kda::launch_kda_prefill_noalloc(q, k, v, gate, beta, state, core, T, heads,
+                                                      head_dim, chunk, scale, stream),
+                      "kda_prefill_noalloc launch");
 }
 
 int kda_prefill_bf16(const uint16_t *qkv, int64_t ldqkv, const float *gate, const float *beta,

@@ -74,6 +74,22 @@ hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
                               float *core, int T, int heads, int head_dim, int chunk,
                               float scale, void *workspace, hipStream_t stream);
 
+// kda_prefill with a given segment length (seg >= 1 chunks per segment; the
+// workspace holds seg chunks' operand blocks): the same bits for every seg.
+hipError_t launch_kda_prefill_segments(const float *q, const float *k, const float *v,
+                                       const float *gate, const float *beta, float *state,
+                                       float *core, int T, int heads, int head_dim, int chunk,
+                                       float scale, void *workspace, int seg, hipStream_t stream);
+
+// kda_prefill on the library-held scratch array (kda_noalloc.hip): the
+// segment length fitted to the array; returns hipErrorInvalidValue when one
+// chunk of all heads does not fit, or the error of the symbol lookup.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+hipError_t launch_kda_prefill_noalloc(const float *q, const float *k, const float *v,
+                                      const float *gate, const float *beta, float *state,
+                                      float *core, int T, int heads, int head_dim, int chunk,
+                                      float scale, hipStream_t stream);
+
 // kda_prefill reading q | k | v directly from bf16 rows [T_pad, ldqkv] (the
 // conv output; q at column 0, k at heads*head_dim, v at 2*heads*head_dim):
 // bitwise the result of kda_prefill on their exact fp32 widening.

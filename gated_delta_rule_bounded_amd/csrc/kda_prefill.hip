@@ -129,13 +129,22 @@ hipError_t launch_kda_prefill(const float *q, const float *k, const float *v,
                               float *core, int T, int heads, int head_dim, int chunk,
                               float scale, void *workspace, hipStream_t stream)
 {
+    return launch_kda_prefill_segments(q, k, v, gate, beta, state, core, T, heads, head_dim,
+                                       chunk, scale, workspace,
+                                       prefill_segment_chunks(T, heads, head_dim, chunk), stream);
+}
+
+hipError_t launch_kda_prefill_segments(const float *q, const float *k, const float *v,
+                                       const float *gate, const float *beta, float *state,
+                                       float *core, int T, int heads, int head_dim, int chunk,
+                                       float scale, void *workspace, int seg, hipStream_t stream)
+{
     // Segments of `seg` chunks, each prepared into the start of the workspace
     // and walked at once: a segment's operand blocks (at most the cache
     // budget) are still in the last-level cache when the walk reads them.
     // Chunk boundaries and the carried state are those of one long pass, so
     // the result is bitwise the same.
     const int NC = (T + chunk - 1) / chunk;
-    const int seg = prefill_segment_chunks(T, heads, head_dim, chunk);
     const int64_t HD = (int64_t)heads * head_dim;
     for (int c0 = 0; c0 < NC; c0 += seg) {
         const int64_t r0 = (int64_t)c0 * chunk;

@@ -159,6 +159,31 @@ int kda_prefill(const float *q, const float *k, const float *v,
                 size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kda_prefill_noalloc — kda_prefill for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments as kda_prefill without the workspace;
+ * the result is bitwise that of kda_prefill.
+ *   The operand blocks go to a library-held device array of
+ *   KDA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, which each GPU the library
+ *   runs on holds until the process ends; the call itself allocates nothing
+ *   (no hipMalloc, no hipFree, no allocating library routine) and walks the
+ *   sequence in segments of as many chunks as the array holds.
+ *   Every call on one GPU shares that GPU's array: calls whose work overlaps
+ *   in time (different streams, or host threads with no ordering between
+ *   them) race on it and give undefined results; order them (one stream, or
+ *   events).  The array keeps the last call's contents; nothing in it needs
+ *   to start at zero.
+ *   Errors as kda_prefill; KDA_ERR_WORKSPACE when one chunk of all heads,
+ *   heads * (4*chunk*head_dim + chunk*chunk + head_dim) * 4 bytes, exceeds
+ *   the array; KDA_ERR_HIP when the array's address cannot be looked up.
+ * ------------------------------------------------------------------------ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int kda_prefill_noalloc(const float *q, const float *k, const float *v,
+                        const float *gate, const float *beta, float *state, float *core,
+                        int32_t T, int32_t T_pad, int32_t heads, int32_t head_dim,
+                        int32_t chunk, float scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * kda_prefill_prepare / kda_prefill_forward — the two phases of kda_prefill,
  * callable separately ("Glm5NextLayer" page, split-prefill section: a batched
  * linear-attention prefill runs its phases as separate steps).  Calling

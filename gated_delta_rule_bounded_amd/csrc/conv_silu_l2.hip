@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
         if (r >= 0)
             win[j] = *reinterpret_cast<const uint4 *>(x + (row0 + r) * ldx + c0);
         else if (st != nullptr)
-            win[j] = *reinterpret_cast<const uint4 *>(st + (int64_t)(KC + r) * conv_dim + c0);
+            win[j] = gload16(st + (int64_t)(KC + r) * conv_dim + c0);
         else
             win[j] = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
                 uint16_t *dst = conv_snap[row0 - seq + t];   // seq*(rows-1) + t
 #pragma unroll
                 for (int j = 0; j < KC; ++j)
-                    *reinterpret_cast<uint4 *>(dst + (int64_t)j * conv_dim + c0) = win[j];
+                    gstore16(dst + (int64_t)j * conv_dim + c0, win[j]);
             }
         }
     }
@@ -141,14 +141,13 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
         uint16_t *dst = conv_state[seq];
         if (ntiles == 1) {
 #pragma unroll
-            for (int j = 0; j < KC; ++j)
-                *reinterpret_cast<uint4 *>(dst + (int64_t)j * conv_dim + c0) = win[j];
+            for (int j = 0; j < KC; ++j) gstore16(dst + (int64_t)j * conv_dim + c0, win[j]);
         } else {
             // rows >= kConvRowsPerTile >= KC: the window is the last KC rows of x
 #pragma unroll
             for (int j = 0; j < KC; ++j)
-                *reinterpret_cast<uint4 *>(dst + (int64_t)j * conv_dim + c0) =
-                    *reinterpret_cast<const uint4 *>(x + (row0 + rows - KC + j) * ldx + c0);
+                gstore16(dst + (int64_t)j * conv_dim + c0,
+                         *reinterpret_cast<const uint4 *>(x + (row0 + rows - KC + j) * ldx + c0));
         }
     }
 }
@@ -173,14 +172,29 @@ __global__ __launch_bounds__(kConvThreads) void conv_fold_kernel(
     uint16_t *__restrict__ st = conv_state[b];
     uint4 old[KC];
 #pragma unroll
-    for (int j = 0; j < KC; ++j) old[j] = *reinterpret_cast<const uint4 *>(st + (int64_t)j * conv_dim + c0);
+    for (int j = 0; j < KC; ++j) old[j] = gload16(st + (int64_t)j * conv_dim + c0);
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
         const int idx = n + j;   // position in [old window; accepted rows]
-        const uint4 v = idx < KC ? old[idx]
-                                 : *reinterpret_cast<const uint4 *>(
-                                       x + ((int64_t)b * K + idx - KC) * ldx + c0);
-        *reinterpret_cast<uint4 *>(st + (int64_t)j * conv_dim + c0) = v;
+        // the accepted row idx - KC (a row of this sequence whatever idx is:
+        // clamped, and used only when idx >= KC), and old[idx] picked by
+        // selects over the unrolled window, word by word (an indexed register
+        // array, or a select between the two addresses, would go through
+        // scratch memory)
+        const uint4 xr = *reinterpret_cast<const uint4 *>(
+            x + ((int64_t)b * K + max(idx - KC, 0)) * ldx + c0);
+        uint32_t o[4] = {old[KC - 1].x, old[KC - 1].y, old[KC - 1].z, old[KC - 1].w};
+#pragma unroll
+        for (int i = KC - 2; i >= 0; --i) {
+            o[0] = idx == i ? old[i].x : o[0];
+            o[1] = idx == i ? old[i].y : o[1];
+            o[2] = idx == i ? old[i].z : o[2];
+            o[3] = idx == i ? old[i].w : o[3];
+        }
+        const bool own = idx < KC;
+        gstore16(st + (int64_t)j * conv_dim + c0,
+                 make_uint4(own ? o[0] : xr.x, own ? o[1] : xr.y, own ? o[2] : xr.z,
+                            own ? o[3] : xr.w));
     }
 }
 

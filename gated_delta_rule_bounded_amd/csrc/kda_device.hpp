@@ -41,6 +41,21 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// 16-byte accesses through addresses read from device pointer tables (states,
+// snapshots, conv windows).  The compiler cannot infer that such an address
+// is global memory and would use flat instructions, which the wave's LDS
+// wait counter also tracks, so an LDS wait would also wait for them; these
+// go through global-address-space pointers (the tables hold device-memory
+// addresses by contract).
+typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) uintx4 guintx4;
+__device__ __forceinline__ uint4 gload16(const void *p) {
+    return __builtin_bit_cast(uint4, *(const guintx4 *)(p));
+}
+__device__ __forceinline__ void gstore16(void *p, const uint4 &v) {
+    *(guintx4 *)(p) = __builtin_bit_cast(uintx4, v);
+}
+
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

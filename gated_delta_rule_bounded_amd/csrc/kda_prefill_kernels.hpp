@@ -179,7 +179,7 @@ struct QkvSrc {
         else
             return static_cast<const float *>(base)[row * ld + col];
     }
-    __device__ __forceinline__ void advance(int64_t rows) {   // move every section down
+    __host__ __device__ __forceinline__ void advance(int64_t rows) {   // move every section down
         const int64_t e = rows * ld * (BF ? 2 : 4);
         q = static_cast<const char *>(q) + e;
         k = static_cast<const char *>(k) + e;
@@ -688,52 +688,52 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
 // ---------------------------------------------------------------------------
 constexpr float kBlockSpanLog2 = 96.0f;
 
+// LDS of one prepare unit (one chunk of one head) in the split form.
+template <int D, int C>
+struct __align__(16) PrepSplitLds {
+    static constexpr int NW = C / 16;
+    // s_xbuf, fp32: first Kd^T, then the column operand K e^{R_{w-1} - G} as
+    // rows (or, on the pairwise path, the cumulative log-decay rows), then
+    // the right operands of the W and U' passes transposed: (K e^G)^T, V^T.
+    // A transposed operand is read as two 16-byte pieces per lane.
+    static constexpr int kXRow = C * (D + kPadK), kXCol = D * (C + kPadC);
+    float s_tot[NW * D];
+    float s_beta[C];
+    float s_xbuf[kXRow > kXCol ? kXRow : kXCol];
+    float s_M[C][C + kPadC];
+    float s_T[C][C + kPadC];
+    float s_tab[2 * NW + NW * (NW - 1) / 2 + 1][D];
+    int s_bad[NW];
+};
+
+// One prepare unit: chunk n of head h into its operand block `blk`, by the
+// C/16 waves whose unit-local thread indices are tid = 0 .. 64*C/16 - 1.
+// Rows past T are replaced (tmax: the last row that exists).  Every thread
+// of the workgroup passes the same barriers whatever its unit does, so a
+// workgroup may run several units side by side.
 template <int D, int C, bool BF>
-__global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep_split_kernel(
-    QkvSrc<BF> src, const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
-    float *__restrict__ ws, const Varlen vl)
+__device__ __forceinline__ void prep_split_unit(const QkvSrc<BF> &src, const float *__restrict__ gate,
+                                                const float *__restrict__ beta, int T, int H,
+                                                float *__restrict__ blk, int n, int h,
+                                                int64_t tmax, int tid, PrepSplitLds<D, C> &L)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
     constexpr int KD = DT / 2, KC = NW / 2;   // 32-deep blocks over D and over C
     using B = Blk<D, C>;
     static_assert(B::kSplit, "split operand blocks need D, C multiples of 32");
-    // one sequence: heads fastest in the grid (a round of resident workgroups
-    // reads whole token rows and writes adjacent operand blocks); several
-    // sequences: chunks in x, heads in y, sequences in z
-    const int n = vl.cu ? (int)blockIdx.x : (int)blockIdx.y, h = vl.cu ? (int)blockIdx.y : (int)blockIdx.x;
-    int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
-    if (vl.cu) {
-        const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
-        varlen_report(vl, blockIdx.z, sp.ok);
-        nblk = sp.chunk0 + n;
-        if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
-        nblk -= vl.seg_lo;
-        const int64_t r0 = sp.row0 * H;
-        src.advance(sp.row0);
-        gate += r0 * D, beta += r0;
-        T = sp.T;
-        tmax = vl.rows - 1 - sp.row0;
-    }
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int rl = 16 * w + lr;
     const int64_t tg = min((int64_t)n * C + rl, tmax);   // rows past T are replaced
     const bool valid = (int64_t)n * C + rl < T;
-    float *__restrict__ blk = ws + (nblk * H + h) * B::kSize;
 
-    __shared__ __align__(16) float s_tot[NW * D];
-    __shared__ __align__(16) float s_beta[C];
-    // s_xbuf, fp32: first Kd^T, then the column operand K e^{R_{w-1} - G} as
-    // rows (or, on the pairwise path, the cumulative log-decay rows), then
-    // the right operands of the W and U' passes transposed: (K e^G)^T, V^T.
-    // A transposed operand is read as two 16-byte pieces per lane.
-    constexpr int kXRow = C * (D + kPadK), kXCol = D * (C + kPadC);
-    __shared__ __align__(16) float s_xbuf[kXRow > kXCol ? kXRow : kXCol];
-    auto s_x = reinterpret_cast<float (*)[D + kPadK]>(s_xbuf);    // rows [C][D]
-    auto s_xT = reinterpret_cast<float (*)[C + kPadC]>(s_xbuf);   // transposed [D][C]
-    __shared__ __align__(16) float s_M[C][C + kPadC];
-    __shared__ __align__(16) float s_T[C][C + kPadC];
-    __shared__ __align__(16) float s_tab[2 * NW + NW * (NW - 1) / 2 + 1][D];
+    float *__restrict__ s_tot = L.s_tot;
+    float *__restrict__ s_beta = L.s_beta;
+    auto s_x = reinterpret_cast<float (*)[D + kPadK]>(L.s_xbuf);    // rows [C][D]
+    auto s_xT = reinterpret_cast<float (*)[C + kPadC]>(L.s_xbuf);   // transposed [D][C]
+    auto &s_M = L.s_M;
+    auto &s_T = L.s_T;
+    auto &s_tab = L.s_tab;
 
     float4 K[DT], Q[DT], G[DT];
     load_rows_src<D, BF>(src, gate, tg, h, H, lg, K, Q, G);
@@ -760,8 +760,8 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
         // a thread takes one channel d and every kParts-th row (kParts threads
         // share a channel when the workgroup has more threads than channels)
         constexpr int NT = NW * kWave, kParts = NT >= D ? NT / D : 1;
-        const int part = NT >= D ? (int)threadIdx.x / D : 0;
-        for (int d = NT >= D ? (int)threadIdx.x % D : (int)threadIdx.x; d < D; d += NT >= D ? D : NT) {
+        const int part = NT >= D ? tid / D : 0;
+        for (int d = NT >= D ? tid % D : tid; d < D; d += NT >= D ? D : NT) {
             float R[NW + 1];   // R[b + 1] = R_b
             R[0] = 0.f;
 #pragma unroll
@@ -797,7 +797,14 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
         bad |= fminf(fminf(g.x, g.y), fminf(g.z, g.w)) < -kBlockSpanLog2 ||
                fmaxf(fmaxf(g.x, g.y), fmaxf(g.z, g.w)) > 0.f;
     }
-    const bool wide = __syncthreads_or(bad);
+    // the unit's waves OR their flags through LDS (a workgroup may hold
+    // several units; each decides for its own chunk)
+    bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (lane == 0) L.s_bad[w] = bad ? 1 : 0;
+    __syncthreads();
+    bool wide = false;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) wide |= L.s_bad[ww] != 0;
     auto tab4 = [&](int row, int c) { return *reinterpret_cast<const float4 *>(&s_tab[row][c]); };
 
     // Row operands B = K e^{G - R_{w-1}}, Qb = Q e^{G - R_{w-1}} (split), the
@@ -1036,6 +1043,35 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     }
 }
 
+
+template <int D, int C, bool BF>
+__global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep_split_kernel(
+    QkvSrc<BF> src, const float *__restrict__ gate, const float *__restrict__ beta, int T, int H,
+    float *__restrict__ ws, const Varlen vl)
+{
+    using B = Blk<D, C>;
+    // one sequence: heads fastest in the grid (a round of resident workgroups
+    // reads whole token rows and writes adjacent operand blocks); several
+    // sequences: chunks in x, heads in y, sequences in z
+    const int n = vl.cu ? (int)blockIdx.x : (int)blockIdx.y, h = vl.cu ? (int)blockIdx.y : (int)blockIdx.x;
+    int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
+    if (vl.cu) {
+        const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
+        varlen_report(vl, blockIdx.z, sp.ok);
+        nblk = sp.chunk0 + n;
+        if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
+        nblk -= vl.seg_lo;
+        const int64_t r0 = sp.row0 * H;
+        src.advance(sp.row0);
+        gate += r0 * D, beta += r0;
+        T = sp.T;
+        tmax = vl.rows - 1 - sp.row0;
+    }
+    __shared__ PrepSplitLds<D, C> L;
+    prep_split_unit<D, C, BF>(src, gate, beta, T, H, ws + (nblk * H + h) * B::kSize, n, h, tmax,
+                              (int)threadIdx.x, L);
+}
+
 // ---------------------------------------------------------------------------
 // kda_chunk_fwd: per (head h, value slice j0..j0+15), serial over chunks.
 // Wave w owns chunk rows 16w..16w+15; the state slice S[:, j0..j0+15] lives
@@ -1080,7 +1116,9 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
     __shared__ float s_S[D][16 + kPad16];
 
     // S slice in MFMA output layout: Sr[t8][i] = S[16*t8 + 4*lg + i][j0 + lr]
-    float *__restrict__ Sg = state + (int64_t)h * D * D;
+    // (through a global-space pointer, as in walk_split)
+    typedef __attribute__((address_space(1))) float gfloat;
+    gfloat *__restrict__ Sg = (gfloat *)(state + (int64_t)h * D * D);
     floatx4 Sr[DT];
 #pragma unroll
     for (int t8 = 0; t8 < DT; ++t8)
@@ -1287,36 +1325,34 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
 // one operand register set, so two workgroups fit per CU where the
 // loading-ahead instance fits one.  Same products in the same order, so the
 // same bits.
-template <int D, int C, bool PF = true>
-__global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu(PF ? 2 : 4))) void kda_chunk_fwd_split_kernel(
-    const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
-    int NC, int H, float scale, const Varlen vl)
+// LDS of a walk over NJ 16-column tiles: the exchanged right operands.
+template <int D, int C, int NJ>
+struct __align__(16) WalkLds {
+    uint4 s_Sb[NJ][D / 32][2][kWave];   // S slice, right operand (hi, lo), per column tile
+    uint4 s_Ub[NJ][C / 32][2][kWave];   // U, right operand (hi, lo), per column tile
+};
+
+// The walk of head h over value columns 16*jt0 .. 16*(jt0 + NJ) - 1 by the
+// 2*C/16 waves whose workgroup-local thread indices are tid.  Each wave runs
+// its role for all NJ column tiles, so the left operands it loads (W, Kd,
+// Qg, P: the same for every column of the head) serve NJ tiles; per tile the
+// products, their order and every addition are those of NJ = 1, so any NJ
+// gives the same bits.
+template <int D, int C, bool PF, int NJ>
+__device__ __forceinline__ void walk_split(const float *__restrict__ ws, float *__restrict__ state,
+                                           float *__restrict__ core, int T, int NC, int H,
+                                           float scale, int h, int jt0, int tid,
+                                           WalkLds<D, C, NJ> &L)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
     constexpr int KD = DT / 2, KC = NW / 2;   // 32-deep blocks over D and over C
     constexpr int OWN = (DT + NW - 1) / NW;
     using B = Blk<D, C>;
     static_assert(B::kSplit, "split operand blocks need D, C multiples of 32");
-    const int h = blockIdx.x % H, jt = blockIdx.x / H, j0 = 16 * jt;
-    if (vl.cu) {   // sequence blockIdx.y: its state, and its chunks inside this segment
-        const SeqSpan sp = seq_span<C>(vl, blockIdx.y);
-        const int64_t g0 = max(sp.chunk0, (int64_t)vl.seg_lo);
-        const int64_t g1 = min(sp.chunk0 + sp.nch, (int64_t)vl.seg_hi);
-        if (!sp.ok || g0 >= g1) return;   // uniform over the workgroup
-        const int c0 = (int)(g0 - sp.chunk0);   // first chunk of the sequence walked here
-        state = vl.states[blockIdx.y];
-        core += (sp.row0 + (int64_t)c0 * C) * H * D;
-        ws += (g0 - vl.seg_lo) * H * B::kSize;
-        NC = (int)(g1 - g0);
-        T = min(sp.T - c0 * C, NC * C);
-    }
-    const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool chain = r < NW;            // waves 0..NW-1 carry the state
     const int w = chain ? r : r - NW;     // 16-row block of the chunk (and state tiles w + NW o)
-    const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-
-    __shared__ __align__(16) uint4 s_Sb[KD][2][kWave];   // S slice, right operand (hi, lo)
-    __shared__ __align__(16) uint4 s_Ub[KC][2][kWave];   // U, right operand (hi, lo)
+    const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
 
     // publish an owned tile (or a U tile) as a right operand: 8 bytes of hi
     // and of lo in half `half` of this lane's 16-byte slots
@@ -1338,21 +1374,28 @@ __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu
 
     if (chain) {
         // ---- state chain: U = U' - W S, S' = Ec * S + Kd^T U
-        float *__restrict__ Sg = state + (int64_t)h * D * D;
+        // (a global-space pointer: with several sequences the state address
+        // comes from a pointer table, and flat accesses would be waited for
+        // with the LDS counter)
+        typedef __attribute__((address_space(1))) float gfloat;
+        gfloat *__restrict__ Sg = (gfloat *)(state + (int64_t)h * D * D);
         auto own_tile = [&](int o) { return min(w + NW * o, DT - 1); };
-        // Sown[o][i] = S[16*t + 4*lg + i][j0 + lr], t = own_tile(o)
-        float4 Sown[OWN];
+        // Sown[j][o][i] = S[16*t + 4*lg + i][16*(jt0 + j) + lr], t = own_tile(o)
+        float4 Sown[NJ][OWN];
 #pragma unroll
-        for (int o = 0; o < OWN; ++o) {
-            float e[4];
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) e[i] = Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + j0 + lr];
-            Sown[o] = make_float4(e[0], e[1], e[2], e[3]);
-        }
+            for (int o = 0; o < OWN; ++o) {
+                float e[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    e[i] = Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + 16 * (jt0 + j) + lr];
+                Sown[j][o] = make_float4(e[0], e[1], e[2], e[3]);
+            }
         struct Ops {
             bf16x8 Wh[KD], Wl[KD], Kh[OWN][KC], Kl[OWN][KC];
             float4 Ec[OWN];
-            float4 Up;     // U'[16w + 4lg + i][j0 + lr], i = 0..3
+            float4 Up[NJ];     // U'[16w + 4lg + i][16 (jt0 + j) + lr], i = 0..3
         };
         auto load_Kd = [&](Ops &R, const float *b) {
 #pragma unroll
@@ -1365,75 +1408,101 @@ __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu
         };
         Ops X;
         [[maybe_unused]] Ops Y;
-        X.Up = *reinterpret_cast<const float4 *>(block(0) + B::kU + B::frag(jt, w, NW) + 4 * lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            X.Up[j] = *reinterpret_cast<const float4 *>(block(0) + B::kU + B::frag(jt0 + j, w, NW) + 4 * lane);
 #pragma unroll
         for (int kb = 0; kb < KD; ++kb) ldp(block(0) + B::kW + B::pfrag(w, kb, KD), X.Wh[kb], X.Wl[kb]);
         load_Kd(X, block(0));
 #pragma unroll
-        for (int o = 0; o < OWN; ++o) {
-            const int t8 = own_tile(o);
-            if (DT % NW == 0 || w + NW * o < DT) put(s_Sb[t8 / 2], t8 % 2, Sown[o]);
-        }
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int o = 0; o < OWN; ++o) {
+                const int t8 = own_tile(o);
+                if (DT % NW == 0 || w + NW * o < DT) put(L.s_Sb[j][t8 / 2], t8 % 2, Sown[j][o]);
+            }
         __syncthreads();   // B0: S operand visible
         __builtin_amdgcn_sched_barrier(0);
 
         auto chunk = [&](int n, Ops &cur, Ops &nxt) {
             [[maybe_unused]] const float *bn = block(min(n + 1, NC - 1));   // the last chunk reloads itself
-            bf16x8 sh[KD], sl[KD];
+            bf16x8 sh[NJ][KD], sl[NJ][KD];
 #pragma unroll
-            for (int kb = 0; kb < KD; ++kb) get(s_Sb[kb], sh[kb], sl[kb]);
-            floatx4 Wa[2], Wb[2];
-            Wa[0] = floatx4{-cur.Up.x, -cur.Up.y, -cur.Up.z, -cur.Up.w};
-            Wa[1] = Wb[0] = Wb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int kb = 0; kb < KD; ++kb) get(L.s_Sb[j][kb], sh[j][kb], sl[j][kb]);
+            floatx4 Wa[NJ][2], Wb[NJ][2];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                Wa[j][0] = floatx4{-cur.Up[j].x, -cur.Up[j].y, -cur.Up[j].z, -cur.Up[j].w};
+                Wa[j][1] = Wb[j][0] = Wb[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (PF)
-                nxt.Up = *reinterpret_cast<const float4 *>(bn + B::kU + B::frag(jt, w, NW) + 4 * lane);
+            if constexpr (PF) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    nxt.Up[j] = *reinterpret_cast<const float4 *>(bn + B::kU + B::frag(jt0 + j, w, NW) + 4 * lane);
+            }
 #pragma unroll
             for (int kb = 0; kb < KD; ++kb) {
                 if constexpr (PF) ldp(bn + B::kW + B::pfrag(w, kb, KD), nxt.Wh[kb], nxt.Wl[kb]);
-                Wa[kb & 1] = mfma_bf16(cur.Wh[kb], sh[kb], Wa[kb & 1]);
-                Wb[kb & 1] = mfma_bf16(cur.Wh[kb], sl[kb], Wb[kb & 1]);
-                Wb[kb & 1] = mfma_bf16(cur.Wl[kb], sh[kb], Wb[kb & 1]);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    Wa[j][kb & 1] = mfma_bf16(cur.Wh[kb], sh[j][kb], Wa[j][kb & 1]);
+                    Wb[j][kb & 1] = mfma_bf16(cur.Wh[kb], sl[j][kb], Wb[j][kb & 1]);
+                    Wb[j][kb & 1] = mfma_bf16(cur.Wl[kb], sh[j][kb], Wb[j][kb & 1]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            float4 u;
-            u.x = -((Wa[0][0] + Wa[1][0]) + (Wb[0][0] + Wb[1][0]));
-            u.y = -((Wa[0][1] + Wa[1][1]) + (Wb[0][1] + Wb[1][1]));
-            u.z = -((Wa[0][2] + Wa[1][2]) + (Wb[0][2] + Wb[1][2]));
-            u.w = -((Wa[0][3] + Wa[1][3]) + (Wb[0][3] + Wb[1][3]));
-            put(s_Ub[w / 2], w % 2, u);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                float4 u;
+                u.x = -((Wa[j][0][0] + Wa[j][1][0]) + (Wb[j][0][0] + Wb[j][1][0]));
+                u.y = -((Wa[j][0][1] + Wa[j][1][1]) + (Wb[j][0][1] + Wb[j][1][1]));
+                u.z = -((Wa[j][0][2] + Wa[j][1][2]) + (Wb[j][0][2] + Wb[j][1][2]));
+                u.w = -((Wa[j][0][3] + Wa[j][1][3]) + (Wb[j][0][3] + Wb[j][1][3]));
+                put(L.s_Ub[j][w / 2], w % 2, u);
+            }
             __syncthreads();   // B1: U operand visible; every read of the S operand done
             __builtin_amdgcn_sched_barrier(0);
 
-            bf16x8 uh[KC], ul[KC];
+            bf16x8 uh[NJ][KC], ul[NJ][KC];
 #pragma unroll
-            for (int kb = 0; kb < KC; ++kb) get(s_Ub[kb], uh[kb], ul[kb]);
-            floatx4 Aa[OWN], Ab[OWN];
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int o = 0; o < OWN; ++o) {
-                Aa[o] = floatx4{Sown[o].x * cur.Ec[o].x, Sown[o].y * cur.Ec[o].y,
-                                Sown[o].z * cur.Ec[o].z, Sown[o].w * cur.Ec[o].w};
-                Ab[o] = floatx4{0.f, 0.f, 0.f, 0.f};
-            }
+                for (int kb = 0; kb < KC; ++kb) get(L.s_Ub[j][kb], uh[j][kb], ul[j][kb]);
+            floatx4 Aa[NJ][OWN], Ab[NJ][OWN];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int o = 0; o < OWN; ++o) {
+                    Aa[j][o] = floatx4{Sown[j][o].x * cur.Ec[o].x, Sown[j][o].y * cur.Ec[o].y,
+                                       Sown[j][o].z * cur.Ec[o].z, Sown[j][o].w * cur.Ec[o].w};
+                    Ab[j][o] = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kb = 0; kb < KC; ++kb) {
 #pragma unroll
-                for (int o = 0; o < OWN; ++o) {
-                    Aa[o] = mfma_bf16(cur.Kh[o][kb], uh[kb], Aa[o]);
-                    Ab[o] = mfma_bf16(cur.Kh[o][kb], ul[kb], Ab[o]);
-                    Ab[o] = mfma_bf16(cur.Kl[o][kb], uh[kb], Ab[o]);
-                }
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int o = 0; o < OWN; ++o) {
+                        Aa[j][o] = mfma_bf16(cur.Kh[o][kb], uh[j][kb], Aa[j][o]);
+                        Ab[j][o] = mfma_bf16(cur.Kh[o][kb], ul[j][kb], Ab[j][o]);
+                        Ab[j][o] = mfma_bf16(cur.Kl[o][kb], uh[j][kb], Ab[j][o]);
+                    }
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (PF) load_Kd(nxt, bn);
 #pragma unroll
-            for (int o = 0; o < OWN; ++o) {
-                Sown[o] = make_float4(Aa[o][0] + Ab[o][0], Aa[o][1] + Ab[o][1], Aa[o][2] + Ab[o][2],
-                                      Aa[o][3] + Ab[o][3]);
-                const int t8 = own_tile(o);
-                if (DT % NW == 0 || w + NW * o < DT) put(s_Sb[t8 / 2], t8 % 2, Sown[o]);
-            }
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int o = 0; o < OWN; ++o) {
+                    Sown[j][o] = make_float4(Aa[j][o][0] + Ab[j][o][0], Aa[j][o][1] + Ab[j][o][1],
+                                             Aa[j][o][2] + Ab[j][o][2], Aa[j][o][3] + Ab[j][o][3]);
+                    const int t8 = own_tile(o);
+                    if (DT % NW == 0 || w + NW * o < DT) put(L.s_Sb[j][t8 / 2], t8 % 2, Sown[j][o]);
+                }
             __syncthreads();   // B2: S operand visible; every read of the U operand done
             __builtin_amdgcn_sched_barrier(0);
         };
@@ -1448,11 +1517,14 @@ __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu
             chunk(0, X, X);   // NC == 1
         }
 #pragma unroll
-        for (int o = 0; o < OWN; ++o) {
-            const float e[4] = {Sown[o].x, Sown[o].y, Sown[o].z, Sown[o].w};
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + j0 + lr] = e[i];
-        }
+            for (int o = 0; o < OWN; ++o) {
+                const float e[4] = {Sown[j][o].x, Sown[j][o].y, Sown[j][o].z, Sown[j][o].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Sg[(int64_t)(16 * own_tile(o) + 4 * lg + i) * D + 16 * (jt0 + j) + lr] = e[i];
+            }
     } else {
         // ---- outputs: O = scale (Qg S + P U)
         struct Ops {
@@ -1470,44 +1542,63 @@ __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu
         auto chunk = [&](int n, Ops &cur, Ops &nxt, auto last) {
             constexpr bool LAST = decltype(last)::value;
             [[maybe_unused]] const float *bn = block(min(n + 1, NC - 1));
-            bf16x8 sh[KD], sl[KD];
+            bf16x8 sh[NJ][KD], sl[NJ][KD];
 #pragma unroll
-            for (int kb = 0; kb < KD; ++kb) get(s_Sb[kb], sh[kb], sl[kb]);
-            floatx4 Qa[2], Qb[2];
-            Qa[0] = Qa[1] = Qb[0] = Qb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int kb = 0; kb < KD; ++kb) get(L.s_Sb[j][kb], sh[j][kb], sl[j][kb]);
+            floatx4 Qa[NJ][2], Qb[NJ][2];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) Qa[j][0] = Qa[j][1] = Qb[j][0] = Qb[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kb = 0; kb < KD; ++kb) {
                 if constexpr (PF) ldp(bn + B::kQ + B::pfrag(w, kb, KD), nxt.Qh[kb], nxt.Ql[kb]);
-                Qa[kb & 1] = mfma_bf16(cur.Qh[kb], sh[kb], Qa[kb & 1]);
-                Qb[kb & 1] = mfma_bf16(cur.Qh[kb], sl[kb], Qb[kb & 1]);
-                Qb[kb & 1] = mfma_bf16(cur.Ql[kb], sh[kb], Qb[kb & 1]);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    Qa[j][kb & 1] = mfma_bf16(cur.Qh[kb], sh[j][kb], Qa[j][kb & 1]);
+                    Qb[j][kb & 1] = mfma_bf16(cur.Qh[kb], sl[j][kb], Qb[j][kb & 1]);
+                    Qb[j][kb & 1] = mfma_bf16(cur.Ql[kb], sh[j][kb], Qb[j][kb & 1]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            floatx4 Oa = {(Qa[0][0] + Qa[1][0]) + (Qb[0][0] + Qb[1][0]),
-                          (Qa[0][1] + Qa[1][1]) + (Qb[0][1] + Qb[1][1]),
-                          (Qa[0][2] + Qa[1][2]) + (Qb[0][2] + Qb[1][2]),
-                          (Qa[0][3] + Qa[1][3]) + (Qb[0][3] + Qb[1][3])};
+            floatx4 Oa[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                Oa[j] = floatx4{(Qa[j][0][0] + Qa[j][1][0]) + (Qb[j][0][0] + Qb[j][1][0]),
+                                (Qa[j][0][1] + Qa[j][1][1]) + (Qb[j][0][1] + Qb[j][1][1]),
+                                (Qa[j][0][2] + Qa[j][1][2]) + (Qb[j][0][2] + Qb[j][1][2]),
+                                (Qa[j][0][3] + Qa[j][1][3]) + (Qb[j][0][3] + Qb[j][1][3])};
             __syncthreads();   // B1
             __builtin_amdgcn_sched_barrier(0);
 
-            bf16x8 uh[KC], ul[KC];
+            bf16x8 uh[NJ][KC], ul[NJ][KC];
 #pragma unroll
-            for (int kb = 0; kb < KC; ++kb) get(s_Ub[kb], uh[kb], ul[kb]);
-            floatx4 Ob = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int kb = 0; kb < KC; ++kb) get(L.s_Ub[j][kb], uh[j][kb], ul[j][kb]);
+            floatx4 Ob[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) Ob[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KC; ++kb) {
                 if constexpr (PF) ldp(bn + B::kP + B::pfrag(w, kb, KC), nxt.Ph[kb], nxt.Pl[kb]);
-                Oa = mfma_bf16(cur.Ph[kb], uh[kb], Oa);
-                Ob = mfma_bf16(cur.Ph[kb], ul[kb], Ob);
-                Ob = mfma_bf16(cur.Pl[kb], uh[kb], Ob);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    Oa[j] = mfma_bf16(cur.Ph[kb], uh[j][kb], Oa[j]);
+                    Ob[j] = mfma_bf16(cur.Ph[kb], ul[j][kb], Ob[j]);
+                    Ob[j] = mfma_bf16(cur.Pl[kb], uh[j][kb], Ob[j]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + i;
-                if (!LAST || tr < T) core[(tr * H + h) * D + j0 + lr] = scale * (Oa[i] + Ob[i]);
-            }
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + i;
+                    if (!LAST || tr < T)
+                        core[(tr * H + h) * D + 16 * (jt0 + j) + lr] = scale * (Oa[j][i] + Ob[j][i]);
+                }
 
             __syncthreads();   // B2
             __builtin_amdgcn_sched_barrier(0);
@@ -1530,7 +1621,28 @@ __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu
     }
 }
 
-
+template <int D, int C, bool PF = true>
+__global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu(PF ? 2 : 4))) void kda_chunk_fwd_split_kernel(
+    const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
+    int NC, int H, float scale, const Varlen vl)
+{
+    using B = Blk<D, C>;
+    const int h = blockIdx.x % H, jt = blockIdx.x / H;
+    if (vl.cu) {   // sequence blockIdx.y: its state, and its chunks inside this segment
+        const SeqSpan sp = seq_span<C>(vl, blockIdx.y);
+        const int64_t g0 = max(sp.chunk0, (int64_t)vl.seg_lo);
+        const int64_t g1 = min(sp.chunk0 + sp.nch, (int64_t)vl.seg_hi);
+        if (!sp.ok || g0 >= g1) return;   // uniform over the workgroup
+        const int c0 = (int)(g0 - sp.chunk0);   // first chunk of the sequence walked here
+        state = vl.states[blockIdx.y];
+        core += (sp.row0 + (int64_t)c0 * C) * H * D;
+        ws += (g0 - vl.seg_lo) * H * B::kSize;
+        NC = (int)(g1 - g0);
+        T = min(sp.T - c0 * C, NC * C);
+    }
+    __shared__ WalkLds<D, C, 1> L;
+    walk_split<D, C, PF, 1>(ws, state, core, T, NC, H, scale, h, jt, (int)threadIdx.x, L);
+}
 
 // The forward pass over walks of one chunk each (kda_chunk_fwd_split_kernel
 // without its load-ahead register set), launched from its own translation

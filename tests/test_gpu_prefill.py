@@ -249,20 +249,27 @@ def test_prefill_prepare_longer_than_one_grid_dimension():
     assert torch.equal(core_a.view(torch.int32), core_b.view(torch.int32))
     assert torch.equal(st_a.view(torch.int32), st_b.view(torch.int32))
 
-def test_prefill_segments_equal_one_pass_bitwise():
+@pytest.mark.parametrize("T,T_pad,H", [(2200, 2240, 64), (2200, 2240, 3), (513, 576, 32),
+                                       (512, 512, 32), (65, 128, 5), (1, 64, 32),
+                                       (4059, 4160, 32)])
+def test_prefill_segments_equal_one_pass_bitwise(T, T_pad, H):
     """kda_prefill walks segments of kda_prefill_segment_chunks chunks, each
     prepared into the start of the workspace; at H = 64 a 2200-token prefill
     takes three segments (the last one ragged).  Core and state must equal one
-    prepare + forward over all rows, bit for bit."""
+    prepare + forward over all rows, bit for bit, at that size and at one-
+    segment sizes; rows past T untouched; and the bf16-row form on the same
+    values gives the same bits."""
     import gated_delta_rule_bounded_amd as kda
-    T, T_pad, H, D, C = 2200, 2240, 64, 128, 64
+    D, C = 128, 64
     seg = kda.kda_prefill_segment_chunks(T, H, D, C)
-    assert 1 < seg < -(-T // C), "need more than one segment"
-    g = torch.Generator(device="cuda").manual_seed(1707)
+    if H == 64:
+        assert 1 < seg < -(-T // C), "need more than one segment"
+    g = torch.Generator(device="cuda").manual_seed(1707 + T + H)
     rnd = lambda *shape: torch.randn(*shape, device="cuda", generator=g)
-    q = torch.nn.functional.normalize(rnd(T_pad, H, D), dim=-1)
-    k = torch.nn.functional.normalize(rnd(T_pad, H, D), dim=-1)
-    v = rnd(T_pad, H, D) * 0.5
+    bf = lambda x: x.to(torch.bfloat16).float()   # noqa: E731  (values a bf16 row holds)
+    q = bf(torch.nn.functional.normalize(rnd(T_pad, H, D), dim=-1))
+    k = bf(torch.nn.functional.normalize(rnd(T_pad, H, D), dim=-1))
+    v = bf(rnd(T_pad, H, D) * 0.5)
     gate = -torch.rand(T_pad, H, D, device="cuda", generator=g) * 0.3
     beta = torch.rand(T_pad, H, device="cuda", generator=g)
     S0 = rnd(H, D, D) * 0.05
@@ -278,6 +285,12 @@ def test_prefill_segments_equal_one_pass_bitwise():
     assert torch.equal(core_a.view(torch.int32), core_b.view(torch.int32))
     assert torch.equal(st_a.view(torch.int32), st_b.view(torch.int32))
     assert bool((core_a[T:] == 7.0).all())
+    qkv = torch.cat([x.reshape(T_pad, H * D) for x in (q, k, v)], 1).to(torch.bfloat16)
+    st_c, core_c = S0.clone(), torch.full((T_pad, H, D), 7.0, device="cuda")
+    kda.kda_prefill_bf16(qkv, gate, beta, st_c, core_c, ws, scale=D ** -0.5, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(core_c.view(torch.int32), core_b.view(torch.int32))
+    assert torch.equal(st_c.view(torch.int32), st_b.view(torch.int32))
 
 
 @pytest.mark.parametrize("T,cap,T_pad,C,D", [(200, 37, 256, 64, 128), (200, 1, 320, 64, 128),

@@ -85,17 +85,29 @@ __device__ __forceinline__ Visit visit_of(int wave, int nsteps, int tile)
     return vs;
 }
 
-// Operands of SIF contraction steps (st0, st0 + 1, ...) for RT row tiles.
-// Every load is issued unconditionally, so the compiler can count the loads
-// in flight exactly and wait for one stage while the next is still coming:
-// slots past the wave's last step re-read its first one (their products are
-// skipped).  x
-// is read through a buffer resource bounded by the rows that exist: lanes of
-// rows past M carry an offset beyond the bound, which the hardware answers
+// Operands of SIF contraction steps (the wave's visited steps v0 .. v0 +
+// SIF - 1) for RT row tiles.  Every load is issued unconditionally, so the
+// compiler can count the loads in flight exactly and wait for one stage while
+// the next is still coming: slots past the wave's last step re-read its first
+// one (their products are skipped).
+//
+// Weights.  The MFMA's B operand wants, in lane (r, kg), 16 bytes of weight
+// row r at a 64-byte step: loaded that way, each instruction would touch 16
+// rows in 64-byte pieces, which the vector-memory path serves at about a
+// quarter of its rate for contiguous spans.  So a stage's weights are loaded
+// per row instead: a row's SIF steps are SIF * 64 consecutive bytes (unless
+// the visit wraps around inside the stage), and lane l of load i takes
+// 16-byte chunk l % (4 SIF) of row i * (16 / SIF) + l / (4 SIF), so one
+// instruction covers 16 / SIF rows with contiguous spans.  The chunks go
+// through the wave's own LDS rows into the operand layout; the values and
+// their order of use are exactly those of per-step loads.
+//
+// x is read through a buffer resource bounded by the rows that exist: lanes
+// of rows past M carry an offset beyond the bound, which the hardware answers
 // with zeros and no memory traffic.
 template <int RT, int SIF>
 struct Stage {
-    uint4 w[SIF];
+    uintx4 w[SIF];
     uint4 x[SIF][RT];
 };
 
@@ -105,28 +117,51 @@ __device__ __forceinline__ uint4 load_x(__amdgpu_buffer_rsrc_t r, uint32_t off) 
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// LDS rows of a wave's staged weights: 16 rows of 4 SIF chunks, padded by one
+// chunk against bank conflicts on the operand reads.
+template <int SIF>
+using WRows = uintx4[16][4 * SIF + 1];
+
 template <int RT, int SIF>
-__device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *wrow,
-                                           __amdgpu_buffer_rsrc_t xr,
-                                           const uint32_t (&xoff)[RT], const Visit &vs, int v0)
+__device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *__restrict__ w,
+                                           const int64_t (&wrow)[SIF], int lane,
+                                           __amdgpu_buffer_rsrc_t xr, const uint32_t (&xoff)[RT],
+                                           const Visit &vs, int v0)
 {
+    constexpr int CPR = 4 * SIF;   // 16-byte chunks per row in a stage
+    const int c = lane % CPR;
+    const int vj = v0 + c / 4;     // visited step of this lane's chunk
+    const int stc = vj < vs.cnt ? vs.step(vj) : vs.beg;   // past the end: a valid dummy
+#pragma unroll
+    for (int i = 0; i < SIF; ++i)
+        S.w[i] = *reinterpret_cast<const uintx4 *>(w + wrow[i] + 32 * stc + 8 * (c % 4));
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
-        const int st = v0 + j < vs.cnt ? vs.step(v0 + j) : vs.beg;   // past the end: a valid dummy
-        S.w[j] = *reinterpret_cast<const uint4 *>(wrow + 32 * st);
+        const int st = v0 + j < vs.cnt ? vs.step(v0 + j) : vs.beg;
 #pragma unroll
         for (int t = 0; t < RT; ++t) S.x[j][t] = load_x(xr, xoff[t] + 64u * st);
     }
 }
 
+// the staged weights into the wave's LDS rows (after the stage before them
+// has been read from there: the wave's own LDS accesses complete in order)
 template <int RT, int SIF>
-__device__ __forceinline__ void mma_stage(const Stage<RT, SIF> &S, floatx4 (&acc)[RT],
-                                          const Visit &vs, int v0)
+__device__ __forceinline__ void put_stage(const Stage<RT, SIF> &S, WRows<SIF> &L, int lane)
+{
+    constexpr int CPR = 4 * SIF, RPI = 16 / SIF;
+#pragma unroll
+    for (int i = 0; i < SIF; ++i) L[i * RPI + lane / CPR][lane % CPR] = S.w[i];
+}
+
+template <int RT, int SIF>
+__device__ __forceinline__ void mma_stage(const Stage<RT, SIF> &S, const WRows<SIF> &L,
+                                          floatx4 (&acc)[RT], const Visit &vs, int v0, int r,
+                                          int kg)
 {
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
         if (v0 + j >= vs.cnt) break;
-        const bf16x8 b = __builtin_bit_cast(bf16x8, S.w[j]);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, L[r][4 * j + kg]);
 #pragma unroll
         for (int t = 0; t < RT; ++t)
             acc[t] = mfma_bf16(__builtin_bit_cast(bf16x8, S.x[j][t]), b, acc[t]);
@@ -141,6 +176,7 @@ template <int RT, int SIF>
 __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
 {
     __shared__ float part[kWaves][RT][16][17];
+    __shared__ WRows<SIF> s_w[kWaves];
 
     // segment of this column tile (uniform scalar search over a handful)
     int s = 0;
@@ -155,9 +191,14 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
     const int r = lane & 15, kg = lane >> 4;
     const int nsteps = g.Kd >> 5;
 
-    // this lane's weight row (columns past N read row 0 and are never stored)
-    const int n = n0 + r;
-    const uint16_t *wrow = g.w + (int64_t)(n < g.N ? n : 0) * g.Kd + 8 * kg;
+    // the weight rows this lane loads (element offsets; columns past N read
+    // row 0 and are never stored)
+    int64_t wrow[SIF];
+#pragma unroll
+    for (int i = 0; i < SIF; ++i) {
+        const int n = n0 + i * (16 / SIF) + lane / (4 * SIF);
+        wrow[i] = (int64_t)(n < g.N ? n : 0) * g.Kd;
+    }
     // this lane's x rows, one per 16-row tile: byte offsets from the first
     // row of the workgroup, or out of range for rows past M
     const int rows = min(a.M - m0, RT * 16);
@@ -177,14 +218,19 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
 
     const Visit vs = visit_of(wave, nsteps, n0 / kColTile);
     if (vs.cnt > 0) {
+        WRows<SIF> &L = s_w[wave];
         Stage<RT, SIF> A, B;
-        load_stage(A, wrow, xr, xoff, vs, 0);
+        load_stage(A, g.w, wrow, lane, xr, xoff, vs, 0);
+        load_stage(B, g.w, wrow, lane, xr, xoff, vs, SIF);
+        put_stage(A, L, lane);
 #pragma unroll 1
         for (int v = 0; v < vs.cnt; v += 2 * SIF) {
-            load_stage(B, wrow, xr, xoff, vs, v + SIF);
-            mma_stage(A, acc, vs, v);
-            load_stage(A, wrow, xr, xoff, vs, v + 2 * SIF);
-            mma_stage(B, acc, vs, v + SIF);
+            mma_stage(A, L, acc, vs, v, r, kg);
+            load_stage(A, g.w, wrow, lane, xr, xoff, vs, v + 2 * SIF);
+            put_stage(B, L, lane);
+            mma_stage(B, L, acc, vs, v + SIF, r, kg);
+            load_stage(B, g.w, wrow, lane, xr, xoff, vs, v + 3 * SIF);
+            put_stage(A, L, lane);
         }
     }
 

@@ -1424,82 +1424,79 @@ __device__ __forceinline__ void walk_split(const float *__restrict__ ws, float *
         __syncthreads();   // B0: S operand visible
         __builtin_amdgcn_sched_barrier(0);
 
+        // Each phase takes the column tiles one after another (their products
+        // never mix), so only one tile's right operands are live at a time;
+        // the loads of the next chunk's operands go with the first tile.
         auto chunk = [&](int n, Ops &cur, Ops &nxt) {
             [[maybe_unused]] const float *bn = block(min(n + 1, NC - 1));   // the last chunk reloads itself
-            bf16x8 sh[NJ][KD], sl[NJ][KD];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int kb = 0; kb < KD; ++kb) get(L.s_Sb[j][kb], sh[j][kb], sl[j][kb]);
-            floatx4 Wa[NJ][2], Wb[NJ][2];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                Wa[j][0] = floatx4{-cur.Up[j].x, -cur.Up[j].y, -cur.Up[j].z, -cur.Up[j].w};
-                Wa[j][1] = Wb[j][0] = Wb[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-            }
-            __builtin_amdgcn_sched_barrier(0);
             if constexpr (PF) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
                     nxt.Up[j] = *reinterpret_cast<const float4 *>(bn + B::kU + B::frag(jt0 + j, w, NW) + 4 * lane);
             }
 #pragma unroll
-            for (int kb = 0; kb < KD; ++kb) {
-                if constexpr (PF) ldp(bn + B::kW + B::pfrag(w, kb, KD), nxt.Wh[kb], nxt.Wl[kb]);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    Wa[j][kb & 1] = mfma_bf16(cur.Wh[kb], sh[j][kb], Wa[j][kb & 1]);
-                    Wb[j][kb & 1] = mfma_bf16(cur.Wh[kb], sl[j][kb], Wb[j][kb & 1]);
-                    Wb[j][kb & 1] = mfma_bf16(cur.Wl[kb], sh[j][kb], Wb[j][kb & 1]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
             for (int j = 0; j < NJ; ++j) {
+                bf16x8 sh[KD], sl[KD];
+#pragma unroll
+                for (int kb = 0; kb < KD; ++kb) get(L.s_Sb[j][kb], sh[kb], sl[kb]);
+                floatx4 Wa[2], Wb[2];
+                Wa[0] = floatx4{-cur.Up[j].x, -cur.Up[j].y, -cur.Up[j].z, -cur.Up[j].w};
+                Wa[1] = Wb[0] = Wb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kb = 0; kb < KD; ++kb) {
+                    if constexpr (PF) {
+                        if (j == 0) ldp(bn + B::kW + B::pfrag(w, kb, KD), nxt.Wh[kb], nxt.Wl[kb]);
+                    }
+                    Wa[kb & 1] = mfma_bf16(cur.Wh[kb], sh[kb], Wa[kb & 1]);
+                    Wb[kb & 1] = mfma_bf16(cur.Wh[kb], sl[kb], Wb[kb & 1]);
+                    Wb[kb & 1] = mfma_bf16(cur.Wl[kb], sh[kb], Wb[kb & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 float4 u;
-                u.x = -((Wa[j][0][0] + Wa[j][1][0]) + (Wb[j][0][0] + Wb[j][1][0]));
-                u.y = -((Wa[j][0][1] + Wa[j][1][1]) + (Wb[j][0][1] + Wb[j][1][1]));
-                u.z = -((Wa[j][0][2] + Wa[j][1][2]) + (Wb[j][0][2] + Wb[j][1][2]));
-                u.w = -((Wa[j][0][3] + Wa[j][1][3]) + (Wb[j][0][3] + Wb[j][1][3]));
+                u.x = -((Wa[0][0] + Wa[1][0]) + (Wb[0][0] + Wb[1][0]));
+                u.y = -((Wa[0][1] + Wa[1][1]) + (Wb[0][1] + Wb[1][1]));
+                u.z = -((Wa[0][2] + Wa[1][2]) + (Wb[0][2] + Wb[1][2]));
+                u.w = -((Wa[0][3] + Wa[1][3]) + (Wb[0][3] + Wb[1][3]));
                 put(L.s_Ub[j][w / 2], w % 2, u);
             }
             __syncthreads();   // B1: U operand visible; every read of the S operand done
             __builtin_amdgcn_sched_barrier(0);
 
-            bf16x8 uh[NJ][KC], ul[NJ][KC];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < NJ; ++j) {
+                bf16x8 uh[KC], ul[KC];
 #pragma unroll
-                for (int kb = 0; kb < KC; ++kb) get(L.s_Ub[j][kb], uh[j][kb], ul[j][kb]);
-            floatx4 Aa[NJ][OWN], Ab[NJ][OWN];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
+                for (int kb = 0; kb < KC; ++kb) get(L.s_Ub[j][kb], uh[kb], ul[kb]);
+                floatx4 Aa[OWN], Ab[OWN];
 #pragma unroll
                 for (int o = 0; o < OWN; ++o) {
-                    Aa[j][o] = floatx4{Sown[j][o].x * cur.Ec[o].x, Sown[j][o].y * cur.Ec[o].y,
-                                       Sown[j][o].z * cur.Ec[o].z, Sown[j][o].w * cur.Ec[o].w};
-                    Ab[j][o] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    Aa[o] = floatx4{Sown[j][o].x * cur.Ec[o].x, Sown[j][o].y * cur.Ec[o].y,
+                                    Sown[j][o].z * cur.Ec[o].z, Sown[j][o].w * cur.Ec[o].w};
+                    Ab[o] = floatx4{0.f, 0.f, 0.f, 0.f};
                 }
-            __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb < KC; ++kb) {
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
+                for (int kb = 0; kb < KC; ++kb) {
 #pragma unroll
                     for (int o = 0; o < OWN; ++o) {
-                        Aa[j][o] = mfma_bf16(cur.Kh[o][kb], uh[j][kb], Aa[j][o]);
-                        Ab[j][o] = mfma_bf16(cur.Kh[o][kb], ul[j][kb], Ab[j][o]);
-                        Ab[j][o] = mfma_bf16(cur.Kl[o][kb], uh[j][kb], Ab[j][o]);
+                        Aa[o] = mfma_bf16(cur.Kh[o][kb], uh[kb], Aa[o]);
+                        Ab[o] = mfma_bf16(cur.Kh[o][kb], ul[kb], Ab[o]);
+                        Ab[o] = mfma_bf16(cur.Kl[o][kb], uh[kb], Ab[o]);
                     }
-                __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int o = 0; o < OWN; ++o) {
+                    Sown[j][o] = make_float4(Aa[o][0] + Ab[o][0], Aa[o][1] + Ab[o][1],
+                                             Aa[o][2] + Ab[o][2], Aa[o][3] + Ab[o][3]);
+                }
             }
             if constexpr (PF) load_Kd(nxt, bn);
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int o = 0; o < OWN; ++o) {
-                    Sown[j][o] = make_float4(Aa[j][o][0] + Ab[j][o][0], Aa[j][o][1] + Ab[j][o][1],
-                                             Aa[j][o][2] + Ab[j][o][2], Aa[j][o][3] + Ab[j][o][3]);
                     const int t8 = own_tile(o);
                     if (DT % NW == 0 || w + NW * o < DT) put(L.s_Sb[j][t8 / 2], t8 % 2, Sown[j][o]);
                 }
@@ -1542,63 +1539,56 @@ __device__ __forceinline__ void walk_split(const float *__restrict__ ws, float *
         auto chunk = [&](int n, Ops &cur, Ops &nxt, auto last) {
             constexpr bool LAST = decltype(last)::value;
             [[maybe_unused]] const float *bn = block(min(n + 1, NC - 1));
-            bf16x8 sh[NJ][KD], sl[NJ][KD];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int kb = 0; kb < KD; ++kb) get(L.s_Sb[j][kb], sh[j][kb], sl[j][kb]);
-            floatx4 Qa[NJ][2], Qb[NJ][2];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) Qa[j][0] = Qa[j][1] = Qb[j][0] = Qb[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kb = 0; kb < KD; ++kb) {
-                if constexpr (PF) ldp(bn + B::kQ + B::pfrag(w, kb, KD), nxt.Qh[kb], nxt.Ql[kb]);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    Qa[j][kb & 1] = mfma_bf16(cur.Qh[kb], sh[j][kb], Qa[j][kb & 1]);
-                    Qb[j][kb & 1] = mfma_bf16(cur.Qh[kb], sl[j][kb], Qb[j][kb & 1]);
-                    Qb[j][kb & 1] = mfma_bf16(cur.Ql[kb], sh[j][kb], Qb[j][kb & 1]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
             floatx4 Oa[NJ];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                Oa[j] = floatx4{(Qa[j][0][0] + Qa[j][1][0]) + (Qb[j][0][0] + Qb[j][1][0]),
-                                (Qa[j][0][1] + Qa[j][1][1]) + (Qb[j][0][1] + Qb[j][1][1]),
-                                (Qa[j][0][2] + Qa[j][1][2]) + (Qb[j][0][2] + Qb[j][1][2]),
-                                (Qa[j][0][3] + Qa[j][1][3]) + (Qb[j][0][3] + Qb[j][1][3])};
+            for (int j = 0; j < NJ; ++j) {
+                bf16x8 sh[KD], sl[KD];
+#pragma unroll
+                for (int kb = 0; kb < KD; ++kb) get(L.s_Sb[j][kb], sh[kb], sl[kb]);
+                floatx4 Qa[2], Qb[2];
+                Qa[0] = Qa[1] = Qb[0] = Qb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kb = 0; kb < KD; ++kb) {
+                    if constexpr (PF) {
+                        if (j == 0) ldp(bn + B::kQ + B::pfrag(w, kb, KD), nxt.Qh[kb], nxt.Ql[kb]);
+                    }
+                    Qa[kb & 1] = mfma_bf16(cur.Qh[kb], sh[kb], Qa[kb & 1]);
+                    Qb[kb & 1] = mfma_bf16(cur.Qh[kb], sl[kb], Qb[kb & 1]);
+                    Qb[kb & 1] = mfma_bf16(cur.Ql[kb], sh[kb], Qb[kb & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                Oa[j] = floatx4{(Qa[0][0] + Qa[1][0]) + (Qb[0][0] + Qb[1][0]),
+                                (Qa[0][1] + Qa[1][1]) + (Qb[0][1] + Qb[1][1]),
+                                (Qa[0][2] + Qa[1][2]) + (Qb[0][2] + Qb[1][2]),
+                                (Qa[0][3] + Qa[1][3]) + (Qb[0][3] + Qb[1][3])};
+            }
             __syncthreads();   // B1
             __builtin_amdgcn_sched_barrier(0);
 
-            bf16x8 uh[NJ][KC], ul[NJ][KC];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < NJ; ++j) {
+                bf16x8 uh[KC], ul[KC];
 #pragma unroll
-                for (int kb = 0; kb < KC; ++kb) get(L.s_Ub[j][kb], uh[j][kb], ul[j][kb]);
-            floatx4 Ob[NJ];
+                for (int kb = 0; kb < KC; ++kb) get(L.s_Ub[j][kb], uh[kb], ul[kb]);
+                floatx4 Ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) Ob[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KC; ++kb) {
-                if constexpr (PF) ldp(bn + B::kP + B::pfrag(w, kb, KC), nxt.Ph[kb], nxt.Pl[kb]);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    Oa[j] = mfma_bf16(cur.Ph[kb], uh[j][kb], Oa[j]);
-                    Ob[j] = mfma_bf16(cur.Ph[kb], ul[j][kb], Ob[j]);
-                    Ob[j] = mfma_bf16(cur.Pl[kb], uh[j][kb], Ob[j]);
+                for (int kb = 0; kb < KC; ++kb) {
+                    if constexpr (PF) {
+                        if (j == 0) ldp(bn + B::kP + B::pfrag(w, kb, KC), nxt.Ph[kb], nxt.Pl[kb]);
+                    }
+                    Oa[j] = mfma_bf16(cur.Ph[kb], uh[kb], Oa[j]);
+                    Ob = mfma_bf16(cur.Ph[kb], ul[kb], Ob);
+                    Ob = mfma_bf16(cur.Pl[kb], uh[kb], Ob);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int64_t tr = (int64_t)n * C + 16 * w + 4 * lg + i;
                     if (!LAST || tr < T)
-                        core[(tr * H + h) * D + 16 * (jt0 + j) + lr] = scale * (Oa[j][i] + Ob[j][i]);
+                        core[(tr * H + h) * D + 16 * (jt0 + j) + lr] = scale * (Oa[j][i] + Ob[i]);
                 }
+            }
 
             __syncthreads();   // B2
             __builtin_amdgcn_sched_barrier(0);
@@ -1621,13 +1611,13 @@ __device__ __forceinline__ void walk_split(const float *__restrict__ ws, float *
     }
 }
 
-template <int D, int C, bool PF = true>
-__global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu(PF ? 2 : 4))) void kda_chunk_fwd_split_kernel(
+template <int D, int C, bool PF = true, int NJ = 1>
+__global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu(PF || NJ > 1 ? 2 : 4))) void kda_chunk_fwd_split_kernel(
     const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
     int NC, int H, float scale, const Varlen vl)
 {
     using B = Blk<D, C>;
-    const int h = blockIdx.x % H, jt = blockIdx.x / H;
+    const int h = blockIdx.x % H, jt = NJ * (blockIdx.x / H);
     if (vl.cu) {   // sequence blockIdx.y: its state, and its chunks inside this segment
         const SeqSpan sp = seq_span<C>(vl, blockIdx.y);
         const int64_t g0 = max(sp.chunk0, (int64_t)vl.seg_lo);
@@ -1640,8 +1630,8 @@ __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu
         NC = (int)(g1 - g0);
         T = min(sp.T - c0 * C, NC * C);
     }
-    __shared__ WalkLds<D, C, 1> L;
-    walk_split<D, C, PF, 1>(ws, state, core, T, NC, H, scale, h, jt, (int)threadIdx.x, L);
+    __shared__ WalkLds<D, C, NJ> L;
+    walk_split<D, C, PF, NJ>(ws, state, core, T, NC, H, scale, h, jt, (int)threadIdx.x, L);
 }
 
 // The forward pass over walks of one chunk each (kda_chunk_fwd_split_kernel

@@ -164,3 +164,28 @@ def test_varlen_clamped_offset_is_reported():
     np.testing.assert_array_equal(core_a, core_b)
     for a, b in zip(states_a, states_b):
         np.testing.assert_array_equal(a, b)
+
+
+def test_varlen_many_one_chunk_prompts_whole_head_walks():
+    # 130 prompts of at most one chunk at 2 heads x 128: 260 (prompt, head)
+    # pairs, so the walk takes whole heads per workgroup; every prompt's rows
+    # and state are bitwise those of kda_prefill on it alone (16-column
+    # walks), and a sample matches the oracle
+    H, D, C = 2, 128, 64
+    rng = np.random.default_rng(1800)
+    lengths = [int(x) for x in rng.integers(1, 65, size=130)]
+    scale = D ** -0.5
+    cases = [core_case(T, H, D, 1800 + s, 0.05) for s, T in enumerate(lengths)]
+    cu, core, states = run_varlen(cases, H, D, C, scale)
+    for s in range(0, len(lengths), 7):
+        c, T = cases[s], lengths[s]
+        one_core, one_S = gpu_prefill(c, T, C, C, scale, fill=0.0)
+        np.testing.assert_array_equal(core[cu[s]:cu[s + 1]], one_core[:T], err_msg=f"seq {s}")
+        np.testing.assert_array_equal(states[s], one_S, err_msg=f"seq {s} state")
+    for s in (0, 64, 129):
+        c = cases[s]
+        ref_core, ref_S, _ = oracle.kda_recurrence(c["q"], c["k"], c["v"], c["gate"], c["beta"],
+                                                   c["S0"], scale)
+        assert relerr(core[cu[s]:cu[s + 1]], ref_core) < TOL
+        assert relerr(states[s], ref_S) < TOL
+    assert np.all(core[cu[-1]:] == SENTINEL)

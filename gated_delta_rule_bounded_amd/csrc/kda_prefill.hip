@@ -198,6 +198,13 @@ hipError_t launch_kda_prefill_varlen(const float *q, const float *k, const float
     for (int lo = 0; lo < total_chunks; lo += seg) {
         const Varlen vl{cu_seqlens, state, rows, max_chunks, total_chunks, lo,
                         std::min(lo + seg, total_chunks), status};
+        if (max_chunks <= 1 && head_dim == 128 && chunk == 64) {
+            // every sequence one chunk: prepare and walk in one kernel
+            const hipError_t e = prefill_one_chunk<128, 64>(q, k, v, gate, beta, core, heads,
+                                                            scale, workspace, vl, B, stream);
+            if (e != hipSuccess) return e;
+            continue;
+        }
         hipError_t e = KDA_PREFILL_DISPATCH(prepare_t, q, k, v, gate, beta, 0, heads, workspace,
                                             vl, B, stream);
         if (e != hipSuccess) return e;

@@ -117,13 +117,11 @@ __device__ __forceinline__ SeqSpan seq_span(const Varlen &vl, int s)
 // Report bits of a several-sequence call (the KDA_REPORT_* values of kda.h):
 // a sequence that is skipped because its chunks do not fit max_chunks /
 // total_chunks, and offsets that had to be clamped.  One thread per sequence
-// reports, in the first segment's prepare launch; the bits are ORed into the
-// caller's word with a vector atomic.
-__device__ __forceinline__ void varlen_report(const Varlen &vl, int s, bool ok)
+// reports (its leader workgroup), in the first segment's launch; the bits are
+// ORed into the caller's word with a vector atomic.
+__device__ __forceinline__ void varlen_report(const Varlen &vl, int s, bool ok, bool leader)
 {
-    if (vl.status == nullptr || vl.seg_lo != 0 || blockIdx.x != 0 || blockIdx.y != 0 ||
-        threadIdx.x != 0)
-        return;
+    if (vl.status == nullptr || vl.seg_lo != 0 || !leader || threadIdx.x != 0) return;
     const int64_t a = vl.cu[s], b = vl.cu[s + 1];
     const int32_t bits = (ok ? 0 : kReportSeqSkipped) |
                          (a < 0 || b < a || b > vl.rows ? kReportRowsClamped : 0);
@@ -428,7 +426,7 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
     int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
     if (vl.cu) {
         const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
-        varlen_report(vl, blockIdx.z, sp.ok);
+        varlen_report(vl, blockIdx.z, sp.ok, blockIdx.x == 0 && blockIdx.y == 0);
         nblk = sp.chunk0 + n;
         if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
         nblk -= vl.seg_lo;
@@ -1057,7 +1055,7 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
     if (vl.cu) {
         const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
-        varlen_report(vl, blockIdx.z, sp.ok);
+        varlen_report(vl, blockIdx.z, sp.ok, blockIdx.x == 0 && blockIdx.y == 0);
         nblk = sp.chunk0 + n;
         if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
         nblk -= vl.seg_lo;
@@ -1611,6 +1609,174 @@ __device__ __forceinline__ void walk_split(const float *__restrict__ ws, float *
     }
 }
 
+// A walk of one chunk over the whole head by the C/16 waves whose
+// workgroup-local thread indices are tid: wave w takes chunk rows
+// 16w .. 16w + 15 (U, O) and the state tiles w + (C/16) o (S'), for every
+// value-column tile in turn.  All of its left operands (W, Qg, P of its
+// rows, Kd of its state tiles) are loaded in one burst at the start; the
+// whole state is published to LDS at once as right operands (a one-chunk
+// walk reads the incoming state only), and U of one column tile at a time,
+// double-buffered, so a column tile costs one barrier.  Per tile every
+// product, its accumulator and every addition are those of walk_split, so
+// the core rows and the new state are the same bits.
+//   blk:   the chunk's operand block;   state: the head's D x D state
+//   core:  the chunk's first row;       T: rows of the chunk that exist
+template <int D, int C>
+struct __align__(16) Walk1Lds {
+    uint4 s_Sb[D / 16][D / 32][2][kWave];   // the state as right operand, per column tile
+    uint4 s_Ub[2][C / 32][2][kWave];         // U as right operand, two column tiles in turn
+};
+
+template <int D, int C>
+__device__ __forceinline__ void walk1_split(const float *__restrict__ blk, float *__restrict__ state,
+                                            float *__restrict__ core, int T, int H, float scale,
+                                            int h, int tid, Walk1Lds<D, C> &L)
+{
+    constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
+    constexpr int KD = DT / 2, KC = NW / 2, OWN = DT / NW;
+    using B = Blk<D, C>;
+    static_assert(B::kSplit && DT % NW == 0, "split operand blocks, whole state tiles per wave");
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    typedef __attribute__((address_space(1))) float gfloat;
+    typedef __attribute__((address_space(1))) char gchar;
+    // the state pointer is the same for the whole workgroup (scalar registers)
+    const uint64_t sp = reinterpret_cast<uint64_t>(state);
+    gfloat *__restrict__ Sg = reinterpret_cast<gfloat *>(
+        ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(sp >> 32)) << 32) |
+        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sp));
+    // S[16 t8 + 4 lg + i][16 j + lr], as a 32-bit byte offset from that base
+    auto at = [&](int t8, int i, int j) -> gfloat & {
+        const uint32_t off = (uint32_t)(((16 * t8 + 4 * lg + i) * D + 16 * j + lr) * 4);
+        return *reinterpret_cast<gfloat *>(reinterpret_cast<gchar *>(Sg) + off);
+    };
+    auto ldS = [&](int t8, int j) { return make_float4(at(t8, 0, j), at(t8, 1, j), at(t8, 2, j), at(t8, 3, j)); };
+    auto own_tile = [&](int o) { return w + NW * o; };
+    auto put = [&](uint4 (&dst)[2][kWave], int half, const float4 &x) {
+        uint2 hi, lo;
+        split4(x, hi, lo);
+        reinterpret_cast<uint2 *>(&dst[0][lane])[half] = hi;
+        reinterpret_cast<uint2 *>(&dst[1][lane])[half] = lo;
+    };
+    auto get = [&](const uint4 (&src)[2][kWave], bf16x8 &hi, bf16x8 &lo) {
+        hi = __builtin_bit_cast(bf16x8, src[0][lane]);
+        lo = __builtin_bit_cast(bf16x8, src[1][lane]);
+    };
+    auto ldp = [&](const float *p, bf16x8 &hi, bf16x8 &lo) {
+        hi = *reinterpret_cast<const bf16x8 *>(p + 4 * lane);
+        lo = *reinterpret_cast<const bf16x8 *>(p + 256 + 4 * lane);
+    };
+    auto ldU = [&](int j) { return *reinterpret_cast<const float4 *>(blk + B::kU + B::frag(j, w, NW) + 4 * lane); };
+
+    // every load of the prologue in flight at once: the incoming state of
+    // this wave's tiles first, then its left operands
+    float4 S0[DT][OWN];
+#pragma unroll
+    for (int j = 0; j < DT; ++j)
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) S0[j][o] = ldS(own_tile(o), j);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 Wh[KD], Wl[KD], Qh[KD], Ql[KD], Ph[KC], Pl[KC], Kh[OWN][KC], Kl[OWN][KC];
+    float4 Ec[OWN];
+#pragma unroll
+    for (int kb = 0; kb < KD; ++kb) {
+        ldp(blk + B::kW + B::pfrag(w, kb, KD), Wh[kb], Wl[kb]);
+        ldp(blk + B::kQ + B::pfrag(w, kb, KD), Qh[kb], Ql[kb]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < KC; ++kb) ldp(blk + B::kP + B::pfrag(w, kb, KC), Ph[kb], Pl[kb]);
+#pragma unroll
+    for (int o = 0; o < OWN; ++o) {
+#pragma unroll
+        for (int kb = 0; kb < KC; ++kb) ldp(blk + B::kKd + B::pfrag(own_tile(o), kb, KC), Kh[o][kb], Kl[o][kb]);
+        Ec[o] = *reinterpret_cast<const float4 *>(blk + B::kEc + 16 * own_tile(o) + 4 * lg);
+    }
+    float4 upN = ldU(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // the incoming state of this wave's tiles, every column tile, as right operands
+#pragma unroll
+    for (int j = 0; j < DT; ++j)
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) put(L.s_Sb[j][own_tile(o) / 2], own_tile(o) % 2, S0[j][o]);
+    __syncthreads();
+    // the tiles' state is read again below, one column tile ahead: the empty
+    // asm makes the pointer opaque, so those reads are not replaced by
+    // values held in registers from the reads above
+    asm volatile("" : "+s"(Sg) : : "memory");
+    float4 sN[OWN];
+#pragma unroll
+    for (int o = 0; o < OWN; ++o) sN[o] = ldS(own_tile(o), 0);
+
+#pragma unroll
+    for (int j = 0; j < DT; ++j) {
+        const float4 up = upN;
+        float4 so[OWN];
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) so[o] = sN[o];
+        if (j + 1 < DT) {
+            upN = ldU(j + 1);
+#pragma unroll
+            for (int o = 0; o < OWN; ++o) sN[o] = ldS(own_tile(o), j + 1);
+        }
+        // U = U' - W S and QS = Qg S for rows 16w.., column tile j
+        bf16x8 sh[KD], sl[KD];
+#pragma unroll
+        for (int kb = 0; kb < KD; ++kb) get(L.s_Sb[j][kb], sh[kb], sl[kb]);
+        floatx4 Wa[2], Wb[2], Qa[2], Qb[2];
+        Wa[0] = floatx4{-up.x, -up.y, -up.z, -up.w};
+        Wa[1] = Wb[0] = Wb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        Qa[0] = Qa[1] = Qb[0] = Qb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KD; ++kb) {
+            Wa[kb & 1] = mfma_bf16(Wh[kb], sh[kb], Wa[kb & 1]);
+            Wb[kb & 1] = mfma_bf16(Wh[kb], sl[kb], Wb[kb & 1]);
+            Wb[kb & 1] = mfma_bf16(Wl[kb], sh[kb], Wb[kb & 1]);
+            Qa[kb & 1] = mfma_bf16(Qh[kb], sh[kb], Qa[kb & 1]);
+            Qb[kb & 1] = mfma_bf16(Qh[kb], sl[kb], Qb[kb & 1]);
+            Qb[kb & 1] = mfma_bf16(Ql[kb], sh[kb], Qb[kb & 1]);
+        }
+        float u[4];
+        floatx4 Oa;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u[i] = -((Wa[0][i] + Wa[1][i]) + (Wb[0][i] + Wb[1][i]));
+            Oa[i] = (Qa[0][i] + Qa[1][i]) + (Qb[0][i] + Qb[1][i]);
+        }
+        put(L.s_Ub[j & 1][w / 2], w % 2, make_float4(u[0], u[1], u[2], u[3]));
+        __syncthreads();   // U of tile j visible; every read of U of tile j - 2 done
+        bf16x8 uh[KC], ul[KC];
+#pragma unroll
+        for (int kb = 0; kb < KC; ++kb) get(L.s_Ub[j & 1][kb], uh[kb], ul[kb]);
+        // O = scale (QS + P U)
+        floatx4 Ob = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KC; ++kb) {
+            Oa = mfma_bf16(Ph[kb], uh[kb], Oa);
+            Ob = mfma_bf16(Ph[kb], ul[kb], Ob);
+            Ob = mfma_bf16(Pl[kb], uh[kb], Ob);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * lg + i;
+            if (r < T) core[((int64_t)r * H + h) * D + 16 * j + lr] = scale * (Oa[i] + Ob[i]);
+        }
+        // S' = Ec * S + Kd^T U for this wave's state tiles
+#pragma unroll
+        for (int o = 0; o < OWN; ++o) {
+            floatx4 Aa = {so[o].x * Ec[o].x, so[o].y * Ec[o].y, so[o].z * Ec[o].z, so[o].w * Ec[o].w};
+            floatx4 Ab = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KC; ++kb) {
+                Aa = mfma_bf16(Kh[o][kb], uh[kb], Aa);
+                Ab = mfma_bf16(Kh[o][kb], ul[kb], Ab);
+                Ab = mfma_bf16(Kl[o][kb], uh[kb], Ab);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) at(own_tile(o), i, j) = Aa[i] + Ab[i];
+        }
+    }
+}
+
 template <int D, int C, bool PF = true, int NJ = 1>
 __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu(PF || NJ > 1 ? 2 : 4))) void kda_chunk_fwd_split_kernel(
     const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
@@ -1635,10 +1801,17 @@ __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu
 }
 
 // The forward pass over walks of one chunk each (kda_chunk_fwd_split_kernel
-// without its load-ahead register set), launched from its own translation
-// unit so that the kernels here keep their place in this file's module.
+// without its load-ahead register set, or whole-head walk1_split workgroups),
+// launched from its own translation unit so that the kernels here keep their
+// place in this file's module.
 template <int D, int C>
 hipError_t fwd_split_one_chunk(dim3 grid, const float *ws, float *state, float *core, int T,
                                int NC, int H, float scale, const Varlen &vl, hipStream_t stream);
+// Prepare and walk of a several-sequence launch whose sequences are all at
+// most one chunk, in one kernel.
+template <int D, int C>
+hipError_t prefill_one_chunk(const float *q, const float *k, const float *v, const float *gate,
+                             const float *beta, float *core, int H, float scale, void *workspace,
+                             const Varlen &vl, int B, hipStream_t stream);
 
 }  // namespace kda

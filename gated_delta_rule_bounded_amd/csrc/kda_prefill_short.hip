@@ -1,28 +1,87 @@
-// The one-chunk forward instance of the chunked prefill (every walk of the
-// launch is a single chunk: all sequences at most C rows), in a translation
-// unit of its own.  The same products in the same order as the load-ahead
-// instance, so the same bits.
+// The chunked prefill of launches in which every walk is a single chunk (all
+// sequences at most C rows), in a translation unit of its own so that the
+// kernels of kda_prefill.hip keep their place in that file's module.
 //
-// Such a walk is a short latency chain (state in, one chunk, state out).
-// With many (sequence, head) pairs in the launch, what it costs is the head's
-// operand block being pulled into every workgroup that walks part of the
-// head, so a workgroup then takes all D / 16 column tiles of its head (the
-// whole state; the block is read once per head and sequence instead of once
-// per 16 columns), one workgroup per CU.  Fewer pairs than CUs keep the
-// 16-column workgroups, which spread the few heads over more CUs.
+// Such a walk is a short chain (state in, one chunk, state out) with nothing
+// to hand on between chunks, so a workgroup takes a whole head (walk1_split):
+// the head's operand block is read once, not once per 16 value columns.
+//   fwd_split_one_chunk  the forward pass alone, over operand blocks that a
+//                        prepare launch wrote;
+//   prefill_one_chunk    prepare and walk of each (sequence, head) in one
+//                        workgroup: the operand block is written and read
+//                        back by the same workgroup right away, instead of
+//                        being written by one launch and fetched again by the
+//                        next.
+// Both run the products of the two-launch path in the same order, so every
+// core row and state is the same bits.
 #include "kda_prefill_kernels.hpp"
 
 namespace kda {
+
+// Where a (head, sequence) workgroup's single chunk is: false when the
+// sequence has no chunk in this launch's segment (or is skipped).
+template <int C>
+__device__ __forceinline__ bool one_chunk_span(const Varlen &vl, int s, SeqSpan &sp)
+{
+    sp = seq_span<C>(vl, s);
+    return sp.ok && sp.nch == 1 && sp.chunk0 >= vl.seg_lo && sp.chunk0 < vl.seg_hi;
+}
+
+template <int D, int C>
+__global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_walk1_kernel(
+    const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
+    int H, float scale, const Varlen vl)
+{
+    using B = Blk<D, C>;
+    const int h = blockIdx.x;
+    if (vl.cu) {
+        SeqSpan sp;
+        if (!one_chunk_span<C>(vl, blockIdx.y, sp)) return;   // uniform over the workgroup
+        state = vl.states[blockIdx.y];
+        core += sp.row0 * H * D;
+        ws += (sp.chunk0 - vl.seg_lo) * H * B::kSize;
+        T = sp.T;
+    }
+    __shared__ Walk1Lds<D, C> L;
+    walk1_split<D, C>(ws + (int64_t)h * B::kSize, state + (int64_t)h * D * D, core, T, H, scale, h,
+                      (int)threadIdx.x, L);
+}
+
+template <int D, int C>
+__global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_fused1_kernel(
+    QkvSrc<false> src, const float *__restrict__ gate, const float *__restrict__ beta, int H,
+    float *__restrict__ ws, float *__restrict__ core, float scale, const Varlen vl)
+{
+    using B = Blk<D, C>;
+    const int h = blockIdx.x, s = blockIdx.y;
+    SeqSpan sp;
+    const bool here = one_chunk_span<C>(vl, s, sp);
+    varlen_report(vl, s, sp.ok, h == 0);
+    if (!here) return;   // uniform over the workgroup
+    src.advance(sp.row0);
+    float *blk = ws + ((sp.chunk0 - vl.seg_lo) * H + h) * B::kSize;
+    __shared__ union {
+        PrepSplitLds<D, C> prep;
+        Walk1Lds<D, C> walk;
+    } L;
+    prep_split_unit<D, C, false>(src, gate + sp.row0 * H * D, beta + sp.row0 * H, sp.T, H, blk, 0,
+                                 h, vl.rows - 1 - sp.row0, (int)threadIdx.x, L.prep);
+    // the block's global stores visible to every wave of the workgroup, and
+    // every wave done with the prepare's LDS
+    __syncthreads();
+    walk1_split<D, C>(blk, vl.states[s] + (int64_t)h * D * D, core + sp.row0 * H * D, sp.T, H,
+                      scale, h, (int)threadIdx.x, L.walk);
+}
 
 template <int D, int C>
 hipError_t fwd_split_one_chunk(dim3 grid, const float *ws, float *state, float *core, int T,
                                int NC, int H, float scale, const Varlen &vl, hipStream_t stream)
 {
-    constexpr int NJ = D / 16;
+    // Few (sequence, head) pairs keep the 16-column workgroups, which spread
+    // the heads over more CUs; many take a whole head per workgroup.
     if ((int64_t)H * grid.y >= 256)
-        hipLaunchKernelGGL((kda_chunk_fwd_split_kernel<D, C, false, NJ>), dim3(H, grid.y),
-                           dim3(2 * PrefCfg<D, C>::kThreads), 0, stream, ws, state, core, T, NC,
-                           H, scale, vl);
+        hipLaunchKernelGGL((kda_chunk_walk1_kernel<D, C>), dim3(H, grid.y), dim3(PrefCfg<D, C>::kThreads),
+                           0, stream, ws, state, core, T, H, scale, vl);
     else
         hipLaunchKernelGGL((kda_chunk_fwd_split_kernel<D, C, false>), grid,
                            dim3(2 * PrefCfg<D, C>::kThreads), 0, stream, ws, state, core, T, NC,
@@ -30,7 +89,22 @@ hipError_t fwd_split_one_chunk(dim3 grid, const float *ws, float *state, float *
     return hipGetLastError();
 }
 
+template <int D, int C>
+hipError_t prefill_one_chunk(const float *q, const float *k, const float *v, const float *gate,
+                             const float *beta, float *core, int H, float scale, void *workspace,
+                             const Varlen &vl, int B, hipStream_t stream)
+{
+    const QkvSrc<false> src{q, k, v, (int64_t)H * D};
+    hipLaunchKernelGGL((kda_chunk_fused1_kernel<D, C>), dim3(H, B), dim3(PrefCfg<D, C>::kThreads),
+                       0, stream, src, gate, beta, H, static_cast<float *>(workspace), core, scale,
+                       vl);
+    return hipGetLastError();
+}
+
 template hipError_t fwd_split_one_chunk<128, 64>(dim3, const float *, float *, float *, int, int,
                                                  int, float, const Varlen &, hipStream_t);
+template hipError_t prefill_one_chunk<128, 64>(const float *, const float *, const float *,
+                                               const float *, const float *, float *, int, float,
+                                               void *, const Varlen &, int, hipStream_t);
 
 }  // namespace kda

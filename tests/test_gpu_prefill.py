@@ -188,6 +188,31 @@ def test_prefill_full_size_h32_d128(T, T_pad, fill):
         assert np.all(core[T:] == 7.0)
 
 
+@pytest.mark.parametrize("T", [50, 64])
+def test_prefill_one_chunk_whole_head_walks_bitwise(T):
+    """A one-chunk prefill over 256 heads (the walk takes a whole head per
+    workgroup) equals the same heads run 32 at a time (16-column walks), bit
+    for bit, and the oracle."""
+    H, D, C, G = 256, 128, 64, 32
+    case = core_case(T, H, D, 1707, 0.05, qkv_bf16=True)
+    say("one-chunk whole-head walks", T, H)
+    core, S = gpu_prefill(case, T, 64, C, D ** -0.5)
+    for h0 in range(0, H, G):
+        sub = {n: np.ascontiguousarray(a[:, h0:h0 + G]) for n, a in case.items() if n != "S0"}
+        sub["S0"] = np.ascontiguousarray(case["S0"][h0:h0 + G])
+        core_g, S_g = gpu_prefill(sub, T, 64, C, D ** -0.5)
+        assert np.array_equal(core[:, h0:h0 + G].view(np.int32), core_g.view(np.int32)), h0
+        assert np.array_equal(S[h0:h0 + G].view(np.int32), S_g.view(np.int32)), h0
+    heads = [0, 97, 255]
+    sub = {n: np.ascontiguousarray(a[:, heads]) for n, a in case.items() if n != "S0"}
+    sub["S0"] = np.ascontiguousarray(case["S0"][heads])
+    ref_core, ref_S = oracle_core(sub, D ** -0.5)
+    for i, h in enumerate(heads):
+        assert relerr(core[:T, h], ref_core[:, i]) < TOL
+        assert relerr(S[h], ref_S[i]) < TOL
+    assert np.all(core[T:] == 7.0)
+
+
 def test_prefill_phases_equal_one_call_bitwise():
     """kda_prefill_prepare then kda_prefill_forward == kda_prefill, bit for bit."""
     import gated_delta_rule_bounded_amd as kda

@@ -106,9 +106,20 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, bf16x2));
 }
+// x - hi is exact in fp32; it is formed on the bf16 dot-product unit as
+// (-1, 0) . (hi_a, hi_b) + a (products of bf16 values are exact), one
+// instruction per value instead of a widening and a subtraction.  The pair
+// (-1, 0) (bits 0x0000bf80) goes through a scalar register: as an immediate
+// the compiler encodes it as the inline constant -1.0, which the hardware
+// expands to the bits 0xbf800000, i.e. the pair (0, -1) (checked on gfx950).
 __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
-    hi = pk_bf16(a, b);
-    lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+    const bf16x2 h = __builtin_convertvector(floatx2{a, b}, bf16x2);
+    hi = __builtin_bit_cast(uint32_t, h);
+    uint32_t m1_lo = 0x0000bf80u;   // (-1, 0)
+    asm("" : "+s"(m1_lo));
+    const float la = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m1_lo), a, false);
+    const float lb = __builtin_amdgcn_fdot2_f32_bf16(h, bf16x2{(__bf16)0.0f, (__bf16)-1.0f}, b, false);
+    lo = pk_bf16(la, lb);
 }
 // four values -> 8 bytes hi, 8 bytes lo
 __device__ __forceinline__ void split4(const float4 &x, uint2 &hi, uint2 &lo) {

@@ -1613,17 +1613,19 @@ __device__ __forceinline__ void walk_split(const float *__restrict__ ws, float *
 // workgroup-local thread indices are tid: wave w takes chunk rows
 // 16w .. 16w + 15 (U, O) and the state tiles w + (C/16) o (S'), for every
 // value-column tile in turn.  All of its left operands (W, Qg, P of its
-// rows, Kd of its state tiles) are loaded in one burst at the start; the
-// whole state is published to LDS at once as right operands (a one-chunk
-// walk reads the incoming state only), and U of one column tile at a time,
-// double-buffered, so a column tile costs one barrier.  Per tile every
+// rows, Kd of its state tiles, U' of its rows) are loaded at the start; the
+// whole incoming state is published to LDS at once, fp32, in the pair order
+// of the right operands (a one-chunk walk reads the incoming state only:
+// each wave splits what it reads, and the state update reads its tiles
+// there too), and U of one column tile at a time, double-buffered, so a
+// column tile costs one barrier and no global load.  Per tile every
 // product, its accumulator and every addition are those of walk_split, so
 // the core rows and the new state are the same bits.
 //   blk:   the chunk's operand block;   state: the head's D x D state
 //   core:  the chunk's first row;       T: rows of the chunk that exist
 template <int D, int C>
 struct __align__(16) Walk1Lds {
-    uint4 s_Sb[D / 16][D / 32][2][kWave];   // the state as right operand, per column tile
+    float4 s_Sf[D / 16][D / 32][2][kWave];  // the state (fp32) in right-operand pair order, per column tile
     uint4 s_Ub[2][C / 32][2][kWave];         // U as right operand, two column tiles in turn
 };
 
@@ -1691,37 +1693,24 @@ __device__ __forceinline__ void walk1_split(const float *__restrict__ blk, float
         for (int kb = 0; kb < KC; ++kb) ldp(blk + B::kKd + B::pfrag(own_tile(o), kb, KC), Kh[o][kb], Kl[o][kb]);
         Ec[o] = *reinterpret_cast<const float4 *>(blk + B::kEc + 16 * own_tile(o) + 4 * lg);
     }
-    float4 upN = ldU(0);
     __builtin_amdgcn_sched_barrier(0);
-    // the incoming state of this wave's tiles, every column tile, as right operands
+    // the incoming state of this wave's tiles, every column tile
 #pragma unroll
     for (int j = 0; j < DT; ++j)
 #pragma unroll
-        for (int o = 0; o < OWN; ++o) put(L.s_Sb[j][own_tile(o) / 2], own_tile(o) % 2, S0[j][o]);
-    __syncthreads();
-    // the tiles' state is read again below, one column tile ahead: the empty
-    // asm makes the pointer opaque, so those reads are not replaced by
-    // values held in registers from the reads above
-    asm volatile("" : "+s"(Sg) : : "memory");
-    float4 sN[OWN];
+        for (int o = 0; o < OWN; ++o) L.s_Sf[j][own_tile(o) / 2][own_tile(o) % 2][lane] = S0[j][o];
+    float4 Up[DT];
 #pragma unroll
-    for (int o = 0; o < OWN; ++o) sN[o] = ldS(own_tile(o), 0);
+    for (int j = 0; j < DT; ++j) Up[j] = ldU(j);
+    __syncthreads();
 
 #pragma unroll
     for (int j = 0; j < DT; ++j) {
-        const float4 up = upN;
-        float4 so[OWN];
-#pragma unroll
-        for (int o = 0; o < OWN; ++o) so[o] = sN[o];
-        if (j + 1 < DT) {
-            upN = ldU(j + 1);
-#pragma unroll
-            for (int o = 0; o < OWN; ++o) sN[o] = ldS(own_tile(o), j + 1);
-        }
+        const float4 up = Up[j];
         // U = U' - W S and QS = Qg S for rows 16w.., column tile j
         bf16x8 sh[KD], sl[KD];
 #pragma unroll
-        for (int kb = 0; kb < KD; ++kb) get(L.s_Sb[j][kb], sh[kb], sl[kb]);
+        for (int kb = 0; kb < KD; ++kb) split8(L.s_Sf[j][kb][0][lane], L.s_Sf[j][kb][1][lane], sh[kb], sl[kb]);
         floatx4 Wa[2], Wb[2], Qa[2], Qb[2];
         Wa[0] = floatx4{-up.x, -up.y, -up.z, -up.w};
         Wa[1] = Wb[0] = Wb[1] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1763,7 +1752,8 @@ __device__ __forceinline__ void walk1_split(const float *__restrict__ blk, float
         // S' = Ec * S + Kd^T U for this wave's state tiles
 #pragma unroll
         for (int o = 0; o < OWN; ++o) {
-            floatx4 Aa = {so[o].x * Ec[o].x, so[o].y * Ec[o].y, so[o].z * Ec[o].z, so[o].w * Ec[o].w};
+            const float4 so = L.s_Sf[j][own_tile(o) / 2][own_tile(o) % 2][lane];
+            floatx4 Aa = {so.x * Ec[o].x, so.y * Ec[o].y, so.z * Ec[o].z, so.w * Ec[o].w};
             floatx4 Ab = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KC; ++kb) {

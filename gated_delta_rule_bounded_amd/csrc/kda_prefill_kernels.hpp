@@ -708,8 +708,11 @@ struct __align__(16) PrepSplitLds {
 // C/16 waves whose unit-local thread indices are tid = 0 .. 64*C/16 - 1.
 // Rows past T are replaced (tmax: the last row that exists).  Every thread
 // of the workgroup passes the same barriers whatever its unit does, so a
-// workgroup may run several units side by side.
-template <int D, int C, bool BF>
+// workgroup may run several units side by side.  W_LDS: W goes to the
+// unit's own LDS instead of the block (at the start of L.s_M, running on
+// into L.s_T, in the block's pair-fragment layout: C*D floats), for a walk
+// by the same workgroup right after.
+template <int D, int C, bool BF, bool W_LDS = false>
 __device__ __forceinline__ void prep_split_unit(const QkvSrc<BF> &src, const float *__restrict__ gate,
                                                 const float *__restrict__ beta, int T, int H,
                                                 float *__restrict__ blk, int n, int h,
@@ -993,6 +996,10 @@ __device__ __forceinline__ void prep_split_unit(const QkvSrc<BF> &src, const flo
     for (int bi = 0; bi < NW; ++bi)
 #pragma unroll
         for (int kb2 = 0; kb2 <= bi / 2; ++kb2) tb_operand(bi, kb2, tbh[bi][kb2], tbl[bi][kb2]);
+    if constexpr (W_LDS) {
+        static_assert(C * D <= 2 * C * (C + kPadC), "W fits in s_M and s_T");
+        __syncthreads();   // every read of s_T done before W overwrites it
+    }
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -1023,7 +1030,10 @@ __device__ __forceinline__ void prep_split_unit(const QkvSrc<BF> &src, const flo
                     }
                 }
                 if (pass == 0) {
-                    store_pair(blk + B::kW + B::pfrag(bi, g, KD), lane, f4(acc[0]), f4(acc[1]));
+                    if constexpr (W_LDS)
+                        store_pair(&L.s_M[0][0] + B::pfrag(bi, g, KD), lane, f4(acc[0]), f4(acc[1]));
+                    else
+                        store_pair(blk + B::kW + B::pfrag(bi, g, KD), lane, f4(acc[0]), f4(acc[1]));
                 } else {
 #pragma unroll
                     for (int u = 0; u < 2; ++u)
@@ -1623,16 +1633,20 @@ __device__ __forceinline__ void walk_split(const float *__restrict__ ws, float *
 // the core rows and the new state are the same bits.
 //   blk:   the chunk's operand block;   state: the head's D x D state
 //   core:  the chunk's first row;       T: rows of the chunk that exist
+//   W_LDS: W is read from wl, LDS in the block's layout that the
+//          workgroup's own prepare left there (and that the state then
+//          overwrites), instead of from the block
 template <int D, int C>
 struct __align__(16) Walk1Lds {
     float4 s_Sf[D / 16][D / 32][2][kWave];  // the state (fp32) in right-operand pair order, per column tile
     uint4 s_Ub[2][C / 32][2][kWave];         // U as right operand, two column tiles in turn
 };
 
-template <int D, int C>
+template <int D, int C, bool W_LDS = false>
 __device__ __forceinline__ void walk1_split(const float *__restrict__ blk, float *__restrict__ state,
                                             float *__restrict__ core, int T, int H, float scale,
-                                            int h, int tid, Walk1Lds<D, C> &L)
+                                            int h, int tid, Walk1Lds<D, C> &L,
+                                            const float *wl = nullptr)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
     constexpr int KD = DT / 2, KC = NW / 2, OWN = DT / NW;
@@ -1682,7 +1696,7 @@ __device__ __forceinline__ void walk1_split(const float *__restrict__ blk, float
     float4 Ec[OWN];
 #pragma unroll
     for (int kb = 0; kb < KD; ++kb) {
-        ldp(blk + B::kW + B::pfrag(w, kb, KD), Wh[kb], Wl[kb]);
+        ldp((W_LDS ? wl : blk + B::kW) + B::pfrag(w, kb, KD), Wh[kb], Wl[kb]);
         ldp(blk + B::kQ + B::pfrag(w, kb, KD), Qh[kb], Ql[kb]);
     }
 #pragma unroll
@@ -1694,6 +1708,7 @@ __device__ __forceinline__ void walk1_split(const float *__restrict__ blk, float
         Ec[o] = *reinterpret_cast<const float4 *>(blk + B::kEc + 16 * own_tile(o) + 4 * lg);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (W_LDS) __syncthreads();   // every wave has W before the state overwrites it
     // the incoming state of this wave's tiles, every column tile
 #pragma unroll
     for (int j = 0; j < DT; ++j)

@@ -708,10 +708,11 @@ struct __align__(16) PrepSplitLds {
 // C/16 waves whose unit-local thread indices are tid = 0 .. 64*C/16 - 1.
 // Rows past T are replaced (tmax: the last row that exists).  Every thread
 // of the workgroup passes the same barriers whatever its unit does, so a
-// workgroup may run several units side by side.  W_LDS: W goes to the
-// unit's own LDS instead of the block (at the start of L.s_M, running on
-// into L.s_T, in the block's pair-fragment layout: C*D floats), for a walk
-// by the same workgroup right after.
+// workgroup may run several units side by side.  W_LDS: W and U' go to the
+// unit's own LDS instead of the block, in the block's layouts (C*D floats
+// each: W from the start of L.s_M running on into L.s_T, U' from the start
+// of L.s_xbuf), for a walk by the same workgroup right after; they are
+// there once the unit's caller has passed a barrier.
 template <int D, int C, bool BF, bool W_LDS = false>
 __device__ __forceinline__ void prep_split_unit(const QkvSrc<BF> &src, const float *__restrict__ gate,
                                                 const float *__restrict__ beta, int T, int H,
@@ -996,8 +997,10 @@ __device__ __forceinline__ void prep_split_unit(const QkvSrc<BF> &src, const flo
     for (int bi = 0; bi < NW; ++bi)
 #pragma unroll
         for (int kb2 = 0; kb2 <= bi / 2; ++kb2) tb_operand(bi, kb2, tbh[bi][kb2], tbl[bi][kb2]);
+    [[maybe_unused]] float4 up_keep[W_LDS ? NW : 1][2];
     if constexpr (W_LDS) {
-        static_assert(C * D <= 2 * C * (C + kPadC), "W fits in s_M and s_T");
+        static_assert(C * D <= 2 * C * (C + kPadC) && C * D <= PrepSplitLds<D, C>::kXRow &&
+                          KD == NW, "W and U' fit in LDS; one channel-tile pair per wave");
         __syncthreads();   // every read of s_T done before W overwrites it
     }
 #pragma unroll
@@ -1036,8 +1039,12 @@ __device__ __forceinline__ void prep_split_unit(const QkvSrc<BF> &src, const flo
                         store_pair(blk + B::kW + B::pfrag(bi, g, KD), lane, f4(acc[0]), f4(acc[1]));
                 } else {
 #pragma unroll
-                    for (int u = 0; u < 2; ++u)
-                        *reinterpret_cast<float4 *>(blk + B::kU + B::frag(2 * g + u, bi, NW) + 4 * lane) = f4(acc[u]);
+                    for (int u = 0; u < 2; ++u) {
+                        if constexpr (W_LDS)
+                            up_keep[bi][u] = f4(acc[u]);
+                        else
+                            *reinterpret_cast<float4 *>(blk + B::kU + B::frag(2 * g + u, bi, NW) + 4 * lane) = f4(acc[u]);
+                    }
                 }
             }
         }
@@ -1048,6 +1055,14 @@ __device__ __forceinline__ void prep_split_unit(const QkvSrc<BF> &src, const flo
                 put_T(t8, valid ? Vr[t8] : zero4());
             __syncthreads();
         }
+    }
+    if constexpr (W_LDS) {
+        __syncthreads();   // every read of V^T in s_xbuf done before U' overwrites it
+#pragma unroll
+        for (int bi = 0; bi < NW; ++bi)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                *reinterpret_cast<float4 *>(L.s_xbuf + B::frag(2 * w + u, bi, NW) + 4 * lane) = up_keep[bi][u];
     }
 }
 
@@ -1633,9 +1648,9 @@ __device__ __forceinline__ void walk_split(const float *__restrict__ ws, float *
 // the core rows and the new state are the same bits.
 //   blk:   the chunk's operand block;   state: the head's D x D state
 //   core:  the chunk's first row;       T: rows of the chunk that exist
-//   W_LDS: W is read from wl, LDS in the block's layout that the
-//          workgroup's own prepare left there (and that the state then
-//          overwrites), instead of from the block
+//   W_LDS: W and U' are read from wl and ul, LDS in the block's layouts
+//          that the workgroup's own prepare left there (and that the state
+//          then overwrites), instead of from the block
 template <int D, int C>
 struct __align__(16) Walk1Lds {
     float4 s_Sf[D / 16][D / 32][2][kWave];  // the state (fp32) in right-operand pair order, per column tile
@@ -1646,7 +1661,7 @@ template <int D, int C, bool W_LDS = false>
 __device__ __forceinline__ void walk1_split(const float *__restrict__ blk, float *__restrict__ state,
                                             float *__restrict__ core, int T, int H, float scale,
                                             int h, int tid, Walk1Lds<D, C> &L,
-                                            const float *wl = nullptr)
+                                            const float *wl = nullptr, const float *ul = nullptr)
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
     constexpr int KD = DT / 2, KC = NW / 2, OWN = DT / NW;
@@ -1682,7 +1697,9 @@ __device__ __forceinline__ void walk1_split(const float *__restrict__ blk, float
         hi = *reinterpret_cast<const bf16x8 *>(p + 4 * lane);
         lo = *reinterpret_cast<const bf16x8 *>(p + 256 + 4 * lane);
     };
-    auto ldU = [&](int j) { return *reinterpret_cast<const float4 *>(blk + B::kU + B::frag(j, w, NW) + 4 * lane); };
+    auto ldU = [&](int j) {
+        return *reinterpret_cast<const float4 *>((W_LDS ? ul : blk + B::kU) + B::frag(j, w, NW) + 4 * lane);
+    };
 
     // every load of the prologue in flight at once: the incoming state of
     // this wave's tiles first, then its left operands
@@ -1707,16 +1724,22 @@ __device__ __forceinline__ void walk1_split(const float *__restrict__ blk, float
         for (int kb = 0; kb < KC; ++kb) ldp(blk + B::kKd + B::pfrag(own_tile(o), kb, KC), Kh[o][kb], Kl[o][kb]);
         Ec[o] = *reinterpret_cast<const float4 *>(blk + B::kEc + 16 * own_tile(o) + 4 * lg);
     }
+    float4 Up[DT];
+    if constexpr (W_LDS) {
+#pragma unroll
+        for (int j = 0; j < DT; ++j) Up[j] = ldU(j);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (W_LDS) __syncthreads();   // every wave has W before the state overwrites it
+    if constexpr (W_LDS) __syncthreads();   // every wave has W and U' before the state overwrites them
     // the incoming state of this wave's tiles, every column tile
 #pragma unroll
     for (int j = 0; j < DT; ++j)
 #pragma unroll
         for (int o = 0; o < OWN; ++o) L.s_Sf[j][own_tile(o) / 2][own_tile(o) % 2][lane] = S0[j][o];
-    float4 Up[DT];
+    if constexpr (!W_LDS) {
 #pragma unroll
-    for (int j = 0; j < DT; ++j) Up[j] = ldU(j);
+        for (int j = 0; j < DT; ++j) Up[j] = ldU(j);
+    }
     __syncthreads();
 
 #pragma unroll

@@ -64,15 +64,15 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
         PrepSplitLds<D, C> prep;
         Walk1Lds<D, C> walk;
     } L;
-    // W stays in the prepare's LDS; the rest of the block goes through the
-    // workspace (written, then read back by this workgroup)
+    // W and U' stay in the prepare's LDS; the rest of the block goes through
+    // the workspace (written, then read back by this workgroup)
     prep_split_unit<D, C, false, true>(src, gate + sp.row0 * H * D, beta + sp.row0 * H, sp.T, H,
                                        blk, 0, h, vl.rows - 1 - sp.row0, (int)threadIdx.x, L.prep);
-    // the block's global stores and W in LDS visible to every wave of the
-    // workgroup
+    // the block's global stores and W and U' in LDS visible to every wave of
+    // the workgroup
     __syncthreads();
     walk1_split<D, C, true>(blk, vl.states[s] + (int64_t)h * D * D, core + sp.row0 * H * D, sp.T, H,
-                            scale, h, (int)threadIdx.x, L.walk, &L.prep.s_M[0][0]);
+                            scale, h, (int)threadIdx.x, L.walk, &L.prep.s_M[0][0], L.prep.s_xbuf);
 }
 
 template <int D, int C>

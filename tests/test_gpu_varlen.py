@@ -17,10 +17,11 @@ SENTINEL = 7.0
 
 
 def run_varlen(cases, H, D, C, scale, tail=3, tail_fill=np.nan, total_chunks=None, report=0,
-               cu_first=0):
+               cu_first=0, max_chunks=None):
     """One kda_prefill_varlen call over the cases; its run-time report word
     must come out as ``report``.  ``cu_first`` replaces cu_seqlens[0] (a
-    negative value is clamped to row 0 and reported)."""
+    negative value is clamped to row 0 and reported); ``max_chunks`` and
+    ``total_chunks`` replace the counts the lengths give."""
     lengths = [c["q"].shape[0] for c in cases]
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     rows = int(cu[-1]) + tail      # rows past the last sequence hold poison
@@ -37,6 +38,7 @@ def run_varlen(cases, H, D, C, scale, tail=3, tail_fill=np.nan, total_chunks=Non
     core = torch.full((rows, H, D), SENTINEL, dtype=torch.float32, device="cuda")
     mx, tot = kda.varlen_chunks(lengths, C)
     tot = tot if total_chunks is None else total_chunks
+    mx = mx if max_chunks is None else max_chunks
     ws = torch.empty(max(1, kda.kda_prefill_workspace_bytes(max(tot, 1) * C, H, D, C)),
                      dtype=torch.uint8, device="cuda")
     say("varlen", lengths, H, D, C, tot)
@@ -189,3 +191,30 @@ def test_varlen_many_one_chunk_prompts_whole_head_walks():
         assert relerr(core[cu[s]:cu[s + 1]], ref_core) < TOL
         assert relerr(states[s], ref_S) < TOL
     assert np.all(core[cu[-1]:] == SENTINEL)
+
+
+@pytest.mark.parametrize("skip", ["longer_than_max_chunks", "outside_total_chunks"])
+def test_varlen_one_chunk_kernel_skips_and_reports(skip):
+    # max_chunks = 1 at 128 x 64 runs prepare and walk in one kernel; a prompt
+    # longer than one chunk (max_chunks = 1 stated anyway) or one whose chunk
+    # lies past total_chunks is skipped whole and reported, the others stay
+    # bitwise those of kda_prefill alone
+    H, D, C = 4, 128, 64
+    lengths = [64, 30, 100, 1, 64] if skip == "longer_than_max_chunks" else [64, 30, 17, 1, 64]
+    scale = D ** -0.5
+    cases = [core_case(T, H, D, 1900 + s, 0.05, qkv_bf16=True) for s, T in enumerate(lengths)]
+    if skip == "longer_than_max_chunks":
+        cu, core, states = run_varlen(cases, H, D, C, scale, max_chunks=1, report=1)
+        skipped = [2]
+    else:
+        cu, core, states = run_varlen(cases, H, D, C, scale, total_chunks=len(lengths) - 1,
+                                      report=1)
+        skipped = [4]
+    for s, T in enumerate(lengths):
+        if s in skipped:
+            np.testing.assert_array_equal(states[s], cases[s]["S0"])
+            assert np.all(core[cu[s]:cu[s + 1]] == SENTINEL)
+            continue
+        one_core, one_S = gpu_prefill(cases[s], T, C, C, scale)
+        np.testing.assert_array_equal(core[cu[s]:cu[s + 1]], one_core[:T], err_msg=f"seq {s}")
+        np.testing.assert_array_equal(states[s], one_S, err_msg=f"seq {s} state")

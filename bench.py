@@ -55,11 +55,11 @@ PEAK_HBM = 8.0e12             # MI355X HBM3E peak, B/s
 # HBM bytes per launch (FETCH_SIZE and WRITE_SIZE scaled by the copy
 # calibration) from rocprofv3 counter runs of the kernels as they are built
 # now; a kernel is left out once it changes after its counters were taken.
-TRAFFIC_BYTES = {"kda_chunk_prep": (66891.3 * 2.0 + 147968.0 * 1.0) * 1024,
-                 "kda_chunk_fwd": (75098.0 * 2.0 + 34816.0 * 1.0) * 1024}
+TRAFFIC_BYTES = {"kda_chunk_prep": (66845.3 * 2.0 + 147968.0 * 1.0) * 1024,
+                 "kda_chunk_fwd": (75096.5 * 2.0 + 34816.0 * 1.0) * 1024}
 # Counted HBM traffic of one decode step at 256 sequences (FETCH_SIZE x 2 +
 # WRITE_SIZE, KiB per dispatch) for the recurrent kernel as built now.
-DECODE_TRAFFIC_BYTES = (267440.6 * 2.0 + 528931.7 * 1.0) * 1024
+DECODE_TRAFFIC_BYTES = (267441.6 * 2.0 + 528933.7 * 1.0) * 1024
 # Both prefill kernels run each fp32 product as three bf16 products (hi*hi,
 # hi*lo, lo*hi, fp32 accumulation), so their matrix-unit ceiling in
 # fp32-equivalent flops is a third of the bf16 peak.

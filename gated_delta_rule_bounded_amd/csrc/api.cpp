@@ -760,27 +760,60 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
         {b->ga, w->g_b, b->out_gate, rk, qkv, qk, rk},
     };
     const kda::GemvSeg back[] = {{b->o_norm_out, w->o_proj, out, qkv, hs, hs, qk}};
+    // conv + SiLU + L2, the recurrence and the gated RMSNorm: for one row of
+    // few sequences in one kernel per (head, sequence), which saves two
+    // launches (the same bits as the three kernels); otherwise as three
+    // launches, where the recurrence can split a head's columns over several
+    // workgroups (the fused conv reads the head's whole conv window, so its
+    // workgroup must be the only one that rewrites it).  A verify writes
+    // neither state nor snapshots.
+    const bool fuse_mixer = K == 1 && (int64_t)B * heads <= 128;
+    kda::MixerArgs mixer{};
+    mixer.x = b->qkv_proj;
+    mixer.ldx = cd;
+    mixer.conv_w = w->conv;
+    mixer.conv_state = conv_state;
+    mixer.conv_snap = K > 1 && !verify ? conv_snap : nullptr;
+    mixer.y = b->conv_out;
+    mixer.ldy = cd;
+    mixer.gate = b->gate;
+    mixer.beta = b->beta;
+    mixer.state = state;
+    mixer.snap = K > 1 && !verify ? snap : nullptr;
+    mixer.core = b->core;
+    mixer.out_gate = b->out_gate;
+    mixer.norm_w = w->o_norm;
+    mixer.out = b->o_norm_out;
+    mixer.K = K;
+    mixer.H = heads;
+    mixer.scale = scale;
+    mixer.eps_l2 = eps_l2;
+    mixer.eps_rms = eps_rms;
+    mixer.write_state = !verify;
     int rc;
     if ((rc = hip_status(kda::launch_gemv_bf16_batchm(front, 6, Mi, stream),
                          "kda_block_decode_k: front projections launch")) ||
         (rc = hip_status(kda::launch_gemv_bf16_batchm(mid, 2, Mi, stream),
                          "kda_block_decode_k: low-rank projections launch")) ||
-        (rc = hip_status(kda::launch_conv_silu_l2(b->qkv_proj, cd, w->conv, conv_state,
-                                                  K > 1 && !verify ? conv_snap : nullptr, B, K,
-                                                  heads, head_dim, eps_l2, b->conv_out, cd,
-                                                  nullptr, nullptr, nullptr, stream, !verify),
-                         "kda_block_decode_k: conv_silu_l2 launch")) ||
-        (rc = hip_status(verify ? kda::launch_kda_verify(b->conv_out, cd, b->gate, b->beta,
-                                                         state, b->core, B, K, heads, head_dim,
-                                                         scale, stream)
-                                : kda::launch_kda_recurrent(b->conv_out, cd, b->gate, b->beta,
-                                                            state, K > 1 ? snap : nullptr,
-                                                            b->core, B, K, heads, head_dim,
-                                                            scale, stream),
+        (rc = hip_status(
+             fuse_mixer ? kda::launch_kda_mixer(mixer, B, head_dim, stream)
+                        : kda::launch_conv_silu_l2(b->qkv_proj, cd, w->conv, conv_state,
+                                                   mixer.conv_snap, B, K, heads, head_dim, eps_l2,
+                                                   b->conv_out, cd, nullptr, nullptr, nullptr,
+                                                   stream, !verify),
+             "kda_block_decode_k: conv launch")) ||
+        (rc = hip_status(fuse_mixer ? hipSuccess
+                         : verify ? kda::launch_kda_verify(b->conv_out, cd, b->gate, b->beta,
+                                                           state, b->core, B, K, heads, head_dim,
+                                                           scale, stream)
+                                  : kda::launch_kda_recurrent(b->conv_out, cd, b->gate, b->beta,
+                                                              state, mixer.snap, b->core, B, K,
+                                                              heads, head_dim, scale, stream),
                          "kda_block_decode_k: recurrent launch")) ||
-        (rc = hip_status(kda::launch_gated_rmsnorm(b->core, qkv, b->out_gate, qkv, w->o_norm, Mi,
-                                                   heads, head_dim, eps_rms, b->o_norm_out, qkv,
-                                                   stream),
+        (rc = hip_status(fuse_mixer ? hipSuccess
+                                    : kda::launch_gated_rmsnorm(b->core, qkv, b->out_gate, qkv,
+                                                                w->o_norm, Mi, heads, head_dim,
+                                                                eps_rms, b->o_norm_out, qkv, stream),
                          "kda_block_decode_k: gated_rmsnorm launch")) ||
         (rc = hip_status(kda::launch_gemv_bf16_batchm(back, 1, Mi, stream),
                          "kda_block_decode_k: o_proj launch")))

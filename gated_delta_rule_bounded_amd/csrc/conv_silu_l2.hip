@@ -21,11 +21,11 @@
 // reading it, so no other workgroup can observe a half-updated state.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
+#include "kda_rows.hpp"
 
 namespace kda {
 
 constexpr int kConvThreads = 256;
-constexpr int kConvKC = 4;
 // kConvRowsPerTile (kda_launch.hpp): 8 rows per tile (128 VGPRs, four waves
 // per SIMD) measured fastest at 8192 rows x 12288 channels: 84 us against
 // 88 us for 4 rows, 98 us for 16 (160 VGPRs, three waves) and 126 us for 32
@@ -54,16 +54,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
 
     // taps for the 8 channels: w[c][0..KC-1]
     float wt[8][KC];
-    {
-        const uint4 *wp = reinterpret_cast<const uint4 *>(w + (int64_t)c0 * KC);
-        float f[8];
-#pragma unroll
-        for (int p = 0; p < KC * 8 / 8; ++p) {
-            unpack8(wp[p], f);   // channels 2p, 2p+1, each KC taps
-#pragma unroll
-            for (int e = 0; e < 8; ++e) wt[(p * 8 + e) / KC][(p * 8 + e) % KC] = f[e];
-        }
-    }
+    conv_taps(w, c0, wt);
 
     // window: win[j] holds input row (t - KC + 1 + j) once row t is loaded
     uint4 win[KC];
@@ -96,27 +87,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
         for (int j = 0; j + 1 < KC; ++j) win[j] = win[j + 1];
         win[KC - 1] = rowv[i];
 
-        float xv[KC][8];
-#pragma unroll
-        for (int j = 0; j < KC; ++j) unpack8(win[j], xv[j]);
-        float s[8];
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float pre = wt[e][0] * xv[0][e];
-#pragma unroll
-            for (int j = 1; j < KC; ++j) pre = __builtin_fmaf(wt[e][j], xv[j][e], pre);
-            s[e] = pre * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-pre * kLog2e));
-            ss = __builtin_fmaf(s[e], s[e], ss);
-        }
-#pragma unroll
-        for (int off = 1; off < LANES_PER_HEAD; off <<= 1) ss += __shfl_xor(ss, off);
-        if (section < 2) {
-            const float inv = __builtin_amdgcn_rsqf(ss + eps_l2);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[e] *= inv;
-        }
-        const uint4 packed = pack8(s);
+        const uint4 packed = conv_row<LANES_PER_HEAD>(win, wt, section < 2, eps_l2);
         if (active) {
             *reinterpret_cast<uint4 *>(y + (row0 + t) * ldy + c0) = packed;
             if (q32 != nullptr) {

@@ -7,6 +7,7 @@
 // adjacent lanes and reduce the sum of squares by xor-shuffles.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
+#include "kda_rows.hpp"
 
 namespace kda {
 
@@ -21,7 +22,6 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
     int64_t ldo, const uint16_t *__restrict__ w, int T, int H, float eps,
     uint16_t *__restrict__ out, int64_t ldy)
 {
-    constexpr int LANES_PER_HEAD = D / 8;
     const int t = blockIdx.x;
     const int cg = blockIdx.y * kNormThreads + threadIdx.x;
     const bool active = cg < H * D / 8;
@@ -30,19 +30,9 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
     const float4 a = *reinterpret_cast<const float4 *>(core + (int64_t)t * ldc + c0);
     const float4 b = *reinterpret_cast<const float4 *>(core + (int64_t)t * ldc + c0 + 4);
     const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(xv[e], xv[e], ss);
-#pragma unroll
-    for (int off = 1; off < LANES_PER_HEAD; off <<= 1) ss += __shfl_xor(ss, off);
-    const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
-    float g[8], wv[8], o[8];
-    unpack8(*reinterpret_cast<const uint4 *>(out_gate + (int64_t)t * ldo + c0), g);
-    unpack8(*reinterpret_cast<const uint4 *>(w + d0), wv);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        o[e] = xv[e] * r * wv[e] * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-g[e] * kLog2e));
-    if (active) *reinterpret_cast<uint4 *>(out + (int64_t)t * ldy + c0) = pack8(o);
+    const uint4 o = gated_norm8<D>(xv, *reinterpret_cast<const uint4 *>(out_gate + (int64_t)t * ldo + c0),
+                                   *reinterpret_cast<const uint4 *>(w + d0), eps);
+    if (active) *reinterpret_cast<uint4 *>(out + (int64_t)t * ldy + c0) = o;
 }
 
 hipError_t launch_gated_rmsnorm(const float *core, int64_t ldc, const uint16_t *out_gate,

@@ -26,6 +26,7 @@
 // bitwise the snapshot a K-row decode would have written after that row.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
+#include "kda_rows.hpp"
 
 namespace kda {
 
@@ -68,6 +69,103 @@ __device__ __forceinline__ float4 fma4(float a, const float4 &b, const float4 &c
                        __builtin_fmaf(a, b.z, c.z), __builtin_fmaf(a, b.w, c.w));
 }
 
+// The workgroup's LDS: one row's q, k, v and decay factors e = exp(g), and the
+// key-axis partial sums.
+template <int D, int NS, int RGT>
+struct __align__(16) RecLds {
+    float s_q[D], s_k[D], s_v[D], s_e[D];
+    float4 s_red[RecCfg<D, NS, RGT>::kPairs][2][RecCfg<D, NS, RGT>::kCG];
+    float s_kq[RecCfg<D, NS, RGT>::kPairs];
+};
+
+// One row of the recurrence over this workgroup's slice (value columns c0 ..
+// c0 + D/NS - 1), with the row's q, k, v and e in L: decays S, forms
+// u = beta (v - S'^T k) and o = scale (S'^T q + u (k . q)), and adds k u^T to
+// S.  Thread row 0 owns whole columns and stores o: to core_row (the row's
+// first value column of this slice) and o_lds (the same columns), each when
+// given.  Passes one barrier (the key-axis sums go through LDS); the caller
+// passes another before L is rewritten.
+template <int D, int NS, int RGT>
+__device__ __forceinline__ void rec_row(float4 (&S)[RGT][D / 16], RecLds<D, NS, RGT> &L, float bt,
+                                        float scale, int c0, int tid, float *core_row,
+                                        float *o_lds)
+{
+    using Cfg = RecCfg<D, NS, RGT>;
+    constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT, NP = Cfg::kPairs;
+    const int cg = tid % CG;
+    const int tr = tid / CG;                        // thread row index
+    // row group of this thread's j-th set of rows: tr, or 2 tr + j
+    auto rgof = [&](int j) { return RGT == 1 ? tr : 2 * tr + j; };
+
+    // decay, then per row group the partial column sums of S'^T k and
+    // S'^T q over its rows, and the matching partial of k . q
+    float4 pkj[RGT], pqj[RGT];
+    float kqj[RGT];
+#pragma unroll
+    for (int j = 0; j < RGT; ++j) {
+        pkj[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        pqj[j] = pkj[j];
+        kqj[j] = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int i = rgof(j) + RG * r;
+            const float e = L.s_e[i], ki = L.s_k[i], qi = L.s_q[i];
+            S[j][r] = make_float4(S[j][r].x * e, S[j][r].y * e, S[j][r].z * e, S[j][r].w * e);
+            pkj[j] = fma4(ki, S[j][r], pkj[j]);
+            pqj[j] = fma4(qi, S[j][r], pqj[j]);
+            kqj[j] = __builtin_fmaf(ki, qi, kqj[j]);
+        }
+    }
+    // add partner row groups (2p, 2p + 1): in the thread, or CG lanes
+    // apart in one wave; then the 8 pair sums in order through LDS
+    float4 pk = pkj[0], pq = pqj[0];
+    float kq = kqj[0];
+    if constexpr (RGT == 2) {
+        pk = make_float4(pk.x + pkj[1].x, pk.y + pkj[1].y, pk.z + pkj[1].z, pk.w + pkj[1].w);
+        pq = make_float4(pq.x + pqj[1].x, pq.y + pqj[1].y, pq.z + pqj[1].z, pq.w + pqj[1].w);
+        kq += kqj[1];
+    } else {
+        pk.x += __shfl_xor(pk.x, CG); pk.y += __shfl_xor(pk.y, CG);
+        pk.z += __shfl_xor(pk.z, CG); pk.w += __shfl_xor(pk.w, CG);
+        pq.x += __shfl_xor(pq.x, CG); pq.y += __shfl_xor(pq.y, CG);
+        pq.z += __shfl_xor(pq.z, CG); pq.w += __shfl_xor(pq.w, CG);
+        kq += __shfl_xor(kq, CG);
+    }
+    const int pr = RGT == 2 ? tr : tr >> 1;   // pair index
+    if (RGT == 2 || (tr & 1) == 0) {
+        L.s_red[pr][0][cg] = pk;
+        L.s_red[pr][1][cg] = pq;
+        if (cg == 0) L.s_kq[pr] = kq;
+    }
+    __syncthreads();
+    pk = L.s_red[0][0][cg];
+    pq = L.s_red[0][1][cg];
+    kq = L.s_kq[0];
+#pragma unroll
+    for (int p = 1; p < NP; ++p) {
+        const float4 a = L.s_red[p][0][cg], c = L.s_red[p][1][cg];
+        pk = make_float4(pk.x + a.x, pk.y + a.y, pk.z + a.z, pk.w + a.w);
+        pq = make_float4(pq.x + c.x, pq.y + c.y, pq.z + c.z, pq.w + c.w);
+        kq += L.s_kq[p];
+    }
+    const float4 v4 = reinterpret_cast<const float4 *>(L.s_v + c0)[cg];
+    const float4 u = make_float4(bt * (v4.x - pk.x), bt * (v4.y - pk.y),
+                                 bt * (v4.z - pk.z), bt * (v4.w - pk.w));
+    if ((core_row != nullptr || o_lds != nullptr) && tr == 0) {
+        const float4 o = make_float4(scale * __builtin_fmaf(u.x, kq, pq.x),
+                                     scale * __builtin_fmaf(u.y, kq, pq.y),
+                                     scale * __builtin_fmaf(u.z, kq, pq.z),
+                                     scale * __builtin_fmaf(u.w, kq, pq.w));
+        if (core_row != nullptr) reinterpret_cast<float4 *>(core_row)[cg] = o;
+        if (o_lds != nullptr) reinterpret_cast<float4 *>(o_lds)[cg] = o;
+    }
+#pragma unroll
+    for (int j = 0; j < RGT; ++j)
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+            S[j][r] = fma4(L.s_k[rgof(j) + RG * r], u, S[j][r]);
+}
+
 template <int D, int NS, int RGT>
 __global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_kernel(
     const uint16_t *__restrict__ qkv, int64_t ldqkv, const float *__restrict__ gate,
@@ -76,7 +174,7 @@ __global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_
     bool write_state, const int32_t *__restrict__ n_accept, int32_t *__restrict__ status)
 {
     using Cfg = RecCfg<D, NS, RGT>;
-    constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT, NP = Cfg::kPairs;
+    constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT;
 
     const int h = blockIdx.x / NS;
     const int c0 = (blockIdx.x % NS) * Cfg::kDC;   // first value column of this slice
@@ -88,9 +186,7 @@ __global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_
     // row group of this thread's j-th set of rows: tr, or 2 tr + j
     auto rgof = [&](int j) { return RGT == 1 ? tr : 2 * tr + j; };
 
-    __shared__ __align__(16) float s_q[D], s_k[D], s_v[D], s_e[D];
-    __shared__ float4 s_red[NP][2][CG];
-    __shared__ float s_kq[NP];
+    __shared__ RecLds<D, NS, RGT> L;
 
     // rows walked: all K, or the accepted ones when folding (none: nothing to
     // do); a count outside [0, K] is clamped and reported (one thread per
@@ -113,80 +209,16 @@ __global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_
         const size_t row = (size_t)b * K + t;
         const uint16_t *__restrict__ qrow = qkv + row * ldqkv + (size_t)h * D;
         for (int i = tid; i < D; i += Cfg::kThreads) {
-            s_q[i] = bf16_to_f32(qrow[i]);
-            s_k[i] = bf16_to_f32(qrow[qkvw + i]);
-            s_v[i] = bf16_to_f32(qrow[2 * qkvw + i]);
-            s_e[i] = exp2_fast(gate[(row * H + h) * D + i] * kLog2e);
+            L.s_q[i] = bf16_to_f32(qrow[i]);
+            L.s_k[i] = bf16_to_f32(qrow[qkvw + i]);
+            L.s_v[i] = bf16_to_f32(qrow[2 * qkvw + i]);
+            L.s_e[i] = exp2_fast(gate[(row * H + h) * D + i] * kLog2e);
         }
         const float bt = beta[row * H + h];
         __syncthreads();
 
-        // decay, then per row group the partial column sums of S'^T k and
-        // S'^T q over its rows, and the matching partial of k . q
-        float4 pkj[RGT], pqj[RGT];
-        float kqj[RGT];
-#pragma unroll
-        for (int j = 0; j < RGT; ++j) {
-            pkj[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            pqj[j] = pkj[j];
-            kqj[j] = 0.f;
-#pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-                const int i = rgof(j) + RG * r;
-                const float e = s_e[i], ki = s_k[i], qi = s_q[i];
-                S[j][r] = make_float4(S[j][r].x * e, S[j][r].y * e, S[j][r].z * e, S[j][r].w * e);
-                pkj[j] = fma4(ki, S[j][r], pkj[j]);
-                pqj[j] = fma4(qi, S[j][r], pqj[j]);
-                kqj[j] = __builtin_fmaf(ki, qi, kqj[j]);
-            }
-        }
-        // add partner row groups (2p, 2p + 1): in the thread, or CG lanes
-        // apart in one wave; then the 8 pair sums in order through LDS
-        float4 pk = pkj[0], pq = pqj[0];
-        float kq = kqj[0];
-        if constexpr (RGT == 2) {
-            pk = make_float4(pk.x + pkj[1].x, pk.y + pkj[1].y, pk.z + pkj[1].z, pk.w + pkj[1].w);
-            pq = make_float4(pq.x + pqj[1].x, pq.y + pqj[1].y, pq.z + pqj[1].z, pq.w + pqj[1].w);
-            kq += kqj[1];
-        } else {
-            pk.x += __shfl_xor(pk.x, CG); pk.y += __shfl_xor(pk.y, CG);
-            pk.z += __shfl_xor(pk.z, CG); pk.w += __shfl_xor(pk.w, CG);
-            pq.x += __shfl_xor(pq.x, CG); pq.y += __shfl_xor(pq.y, CG);
-            pq.z += __shfl_xor(pq.z, CG); pq.w += __shfl_xor(pq.w, CG);
-            kq += __shfl_xor(kq, CG);
-        }
-        const int pr = RGT == 2 ? tr : tr >> 1;   // pair index
-        if (RGT == 2 || (tr & 1) == 0) {
-            s_red[pr][0][cg] = pk;
-            s_red[pr][1][cg] = pq;
-            if (cg == 0) s_kq[pr] = kq;
-        }
-        __syncthreads();
-        pk = s_red[0][0][cg];
-        pq = s_red[0][1][cg];
-        kq = s_kq[0];
-#pragma unroll
-        for (int p = 1; p < NP; ++p) {
-            const float4 a = s_red[p][0][cg], c = s_red[p][1][cg];
-            pk = make_float4(pk.x + a.x, pk.y + a.y, pk.z + a.z, pk.w + a.w);
-            pq = make_float4(pq.x + c.x, pq.y + c.y, pq.z + c.z, pq.w + c.w);
-            kq += s_kq[p];
-        }
-        const float4 v4 = reinterpret_cast<const float4 *>(s_v + c0)[cg];
-        const float4 u = make_float4(bt * (v4.x - pk.x), bt * (v4.y - pk.y),
-                                     bt * (v4.z - pk.z), bt * (v4.w - pk.w));
-        if (core != nullptr && tr == 0) {
-            const float4 o = make_float4(scale * __builtin_fmaf(u.x, kq, pq.x),
-                                         scale * __builtin_fmaf(u.y, kq, pq.y),
-                                         scale * __builtin_fmaf(u.z, kq, pq.z),
-                                         scale * __builtin_fmaf(u.w, kq, pq.w));
-            reinterpret_cast<float4 *>(core + (row * H + h) * D + c0)[cg] = o;
-        }
-#pragma unroll
-        for (int j = 0; j < RGT; ++j)
-#pragma unroll
-            for (int r = 0; r < RPT; ++r)
-                S[j][r] = fma4(s_k[rgof(j) + RG * r], u, S[j][r]);
+        rec_row<D, NS, RGT>(S, L, bt, scale, c0, tid,
+                            core != nullptr ? core + (row * H + h) * D + c0 : nullptr, nullptr);
 
         if (snap != nullptr && t + 1 < K) {
             float *__restrict__ Sn = snap[(size_t)b * (K - 1) + t] + (size_t)h * D * D + c0;
@@ -206,6 +238,111 @@ __global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_
             for (int r = 0; r < RPT; ++r)
                 store_stream(Sg + (size_t)(rgof(j) + RG * r) * D + 4 * cg, S[j][r]);
     }
+}
+
+// The block decode's per-head stages for every row, one workgroup per (head
+// h, sequence b) over the whole head (see launch_kda_mixer).  Lanes
+// 0 .. 3D/8 - 1 are the conv lanes: lane i of section i / (D/8) (q, k, v)
+// owns 8 channels of head h and slides their window of pre-conv rows, as a
+// conv_silu_l2 thread does (the head's D/8 lanes of a section adjacent and
+// aligned, so the L2 sum takes the same shuffle tree).  Lanes 0 .. D/8 - 1
+// then normalise the row's output as a gated_rmsnorm thread does.
+template <int D>
+__global__ __launch_bounds__((RecCfg<D, 1, 1>::kThreads)) void kda_mixer_kernel(const MixerArgs a)
+{
+    using Cfg = RecCfg<D, 1, 1>;
+    constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT;
+    constexpr int SL = D / 8;   // lanes per section of a head
+    const int h = blockIdx.x, b = blockIdx.y, K = a.K, H = a.H;
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, tr = tid / CG;
+    const int64_t qkvw = (int64_t)H * D, cd = 3 * qkvw;
+
+    __shared__ RecLds<D, 1, 1> L;
+    __shared__ __align__(16) float s_o[D];
+
+    // conv lane: section and channel of its 8 channels
+    const bool conv_lane = tid < 3 * SL;
+    const int section = conv_lane ? tid / SL : 0, li = tid % SL;
+    const int64_t c = section * qkvw + (int64_t)h * D + 8 * li;
+    float wt[8][kConvKC];
+    uint4 win[kConvKC];
+    if (conv_lane) {
+        conv_taps(a.conv_w, c, wt);
+        const uint16_t *st = a.conv_state[b];
+#pragma unroll
+        for (int j = 1; j < kConvKC; ++j) win[j] = gload16(st + (int64_t)j * cd + c);
+        win[0] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    float *__restrict__ Sg = a.state[b] + (size_t)h * D * D;
+    float4 S[1][RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) S[0][r] = load_stream(Sg + (size_t)(tr + RG * r) * D + 4 * cg);
+
+    for (int t = 0; t < K; ++t) {
+        const int64_t row = (int64_t)b * K + t;
+        if (conv_lane) {
+#pragma unroll
+            for (int j = 0; j + 1 < kConvKC; ++j) win[j] = win[j + 1];
+            win[kConvKC - 1] = *reinterpret_cast<const uint4 *>(a.x + row * a.ldx + c);
+            const uint4 packed = conv_row<SL>(win, wt, section < 2, a.eps_l2);
+            *reinterpret_cast<uint4 *>(a.y + row * a.ldy + c) = packed;
+            if (a.conv_snap != nullptr && t + 1 < K) {
+                uint16_t *dst = a.conv_snap[(int64_t)b * (K - 1) + t];
+#pragma unroll
+                for (int j = 0; j < kConvKC; ++j) gstore16(dst + (int64_t)j * cd + c, win[j]);
+            }
+            float f[8];
+            unpack8(packed, f);
+            float *dst = section == 0 ? L.s_q : section == 1 ? L.s_k : L.s_v;
+            reinterpret_cast<float4 *>(dst + 8 * li)[0] = make_float4(f[0], f[1], f[2], f[3]);
+            reinterpret_cast<float4 *>(dst + 8 * li)[1] = make_float4(f[4], f[5], f[6], f[7]);
+        }
+        for (int i = tid; i < D; i += Cfg::kThreads)
+            L.s_e[i] = exp2_fast(a.gate[(row * H + h) * D + i] * kLog2e);
+        const float bt = a.beta[row * H + h];
+        __syncthreads();
+
+        rec_row<D, 1, 1>(S, L, bt, a.scale, 0, tid, a.core + (row * H + h) * D, s_o);
+        if (a.snap != nullptr && t + 1 < K) {
+            float *__restrict__ Sn = a.snap[(size_t)b * (K - 1) + t] + (size_t)h * D * D;
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                store_stream(Sn + (size_t)(tr + RG * r) * D + 4 * cg, S[0][r]);
+        }
+        __syncthreads();   // the row's output complete; LDS is rewritten by the next row
+        if (tid < SL) {
+            const float4 lo = reinterpret_cast<const float4 *>(s_o)[2 * tid];
+            const float4 hi = reinterpret_cast<const float4 *>(s_o)[2 * tid + 1];
+            const float xv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const int64_t o0 = row * qkvw + (int64_t)h * D + 8 * tid;
+            *reinterpret_cast<uint4 *>(a.out + o0) = gated_norm8<D>(
+                xv, *reinterpret_cast<const uint4 *>(a.out_gate + o0),
+                *reinterpret_cast<const uint4 *>(a.norm_w + 8 * tid), a.eps_rms);
+        }
+    }
+
+    if (a.write_state) {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) store_stream(Sg + (size_t)(tr + RG * r) * D + 4 * cg, S[0][r]);
+        if (conv_lane) {
+            uint16_t *dst = a.conv_state[b];
+#pragma unroll
+            for (int j = 0; j < kConvKC; ++j) gstore16(dst + (int64_t)j * cd + c, win[j]);
+        }
+    }
+}
+
+hipError_t launch_kda_mixer(const MixerArgs &a, int B, int head_dim, hipStream_t stream)
+{
+    if (head_dim == 128)
+        hipLaunchKernelGGL(kda_mixer_kernel<128>, dim3(a.H, B), dim3(RecCfg<128, 1, 1>::kThreads),
+                           0, stream, a);
+    else
+        hipLaunchKernelGGL(kda_mixer_kernel<16>, dim3(a.H, B), dim3(RecCfg<16, 1, 1>::kThreads),
+                           0, stream, a);
+    return hipGetLastError();
 }
 
 template <int D, int NS, int RGT = 1>

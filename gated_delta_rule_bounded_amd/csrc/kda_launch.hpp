@@ -57,6 +57,34 @@ hipError_t launch_kda_fold(const uint16_t *qkv, int64_t ldqkv, const float *gate
                            int B, int K, int heads, int head_dim, int32_t *status,
                            hipStream_t stream);
 
+// The block decode's per-head stages in one kernel: for each of the K rows
+// of every sequence, conv + SiLU + L2 of the head's q | k | v channels, the
+// recurrence over the whole head, and the gated RMSNorm of its output — the
+// per-row code of conv_silu_l2, kda_recurrent and gated_rmsnorm, so every
+// buffer gets the bits those three launches would write.  write_state false
+// (a verify): neither state is written and no snapshots are taken.
+struct MixerArgs {
+    const uint16_t *x;              // pre-conv rows [B*K, ldx] (q | k | v)
+    int64_t ldx;
+    const uint16_t *conv_w;         // [3*H*D, 4]
+    uint16_t *const *conv_state;    // per sequence [4, 3*H*D]
+    uint16_t *const *conv_snap;     // per (sequence, row < K-1), or nullptr
+    uint16_t *y;                    // conv_out rows [B*K, ldy]
+    int64_t ldy;
+    const float *gate;              // [B*K, H, D]
+    const float *beta;              // [B*K, H]
+    float *const *state;            // per sequence [H, D, D]
+    float *const *snap;             // per (sequence, row < K-1), or nullptr
+    float *core;                    // [B*K, H*D]
+    const uint16_t *out_gate;       // [B*K, H*D]
+    const uint16_t *norm_w;         // [D]
+    uint16_t *out;                  // o_norm_out [B*K, H*D]
+    int K, H;
+    float scale, eps_l2, eps_rms;
+    bool write_state;
+};
+hipError_t launch_kda_mixer(const MixerArgs &a, int B, int head_dim, hipStream_t stream);
+
 size_t prefill_workspace_bytes(int T_pad, int heads, int head_dim, int chunk);
 int prefill_segment_chunks(int T, int heads, int head_dim, int chunk);
 

@@ -220,6 +220,55 @@ def test_block_decode_k_bitwise_equals_serial_decodes(B, K, H, D, hidden, rank):
         np.testing.assert_array_equal(got[n], ser[n], err_msg=n)
 
 
+@pytest.mark.parametrize("B,K,H,D,hidden,rank", [
+    (3, 4, 2, 16, 128, 32),
+    (2, 5, 4, 128, 256, 32),
+    (2, 1, 4, 128, 256, 32),
+])
+def test_block_decode_k_stages_equal_standalone_kernels(B, K, H, D, hidden, rank):
+    """The block decode runs conv + SiLU + L2, the recurrence and the gated
+    RMSNorm of each (head, sequence) in one kernel; its buffers and states
+    must be the bits of conv_silu_l2, kda_decode_k and gated_rmsnorm run one
+    after the other on the block's own projection outputs."""
+    x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1251 + K)
+    scale = D ** -0.5
+    dev = torch.device("cuda")
+    wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+
+    def fresh():
+        st = [torch.from_numpy(np.ascontiguousarray(S0[b])).to(dev) for b in range(B)]
+        cv = [conv0[b].to(dev).contiguous() for b in range(B)]
+        sn = [torch.full((H, D, D), 5.0, device=dev) for _ in range(B * (K - 1))]
+        cs = [torch.zeros(4, 3 * H * D, dtype=torch.bfloat16, device=dev)
+              for _ in range(B * (K - 1))]
+        return st, cv, sn, cs
+
+    tab = lambda ts: kda.ptr_table(ts) if ts else None  # noqa: E731
+    states, convs, snaps, csnaps = fresh()
+    buf = kda.block_decode_buffers(B * K, heads=H, head_dim=D, rank=rank, device=dev)
+    out = torch.empty(B * K, hidden, dtype=torch.bfloat16, device=dev)
+    say("block decode_k vs stage kernels", B, K, H, D)
+    kda.kda_block_decode_k(x.to(dev).contiguous(), wd, kda.ptr_table(states),
+                           kda.ptr_table(convs), buf, out, B=B, K=K, hidden_size=hidden,
+                           heads=H, head_dim=D, rank=rank, scale=scale, snap=tab(snaps),
+                           conv_snap=tab(csnaps))
+    states2, convs2, snaps2, csnaps2 = fresh()
+    y = torch.empty_like(buf["conv_out"])
+    kda.conv_silu_l2(buf["qkv_proj"], wd["conv"], y, n_seq=B, rows=K, heads=H, head_dim=D,
+                     conv_state=kda.ptr_table(convs2), conv_snap=tab(csnaps2))
+    core = torch.empty_like(buf["core"])
+    kda.kda_decode_k(y, buf["gate"], buf["beta"], kda.ptr_table(states2), core, B=B, K=K,
+                     heads=H, head_dim=D, scale=scale, snap=tab(snaps2))
+    onorm = torch.empty_like(buf["o_norm_out"])
+    kda.gated_rmsnorm(core, buf["out_gate"], wd["o_norm"], onorm, T=B * K, heads=H, head_dim=D)
+    torch.cuda.synchronize()
+    assert torch.equal(y, buf["conv_out"])
+    assert torch.equal(core, buf["core"])
+    assert torch.equal(onorm, buf["o_norm_out"])
+    for a, b in zip(states + convs + snaps + csnaps, states2 + convs2 + snaps2 + csnaps2):
+        assert torch.equal(a, b)
+
+
 def test_block_decode_k_full_size(orc):
     # the layer at full size (hidden 4096, 32 heads x 128, rank 128, weights
     # ~ N(0, 0.02)): one sequence verifying K = 4 draft tokens, against the

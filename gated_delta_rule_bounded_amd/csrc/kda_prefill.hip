@@ -194,17 +194,19 @@ hipError_t launch_kda_prefill_varlen(const float *q, const float *k, const float
     // the start of the workspace and walked at once (one walk per sequence,
     // head and value slice that has chunks in it), so the forward pass reads
     // operand blocks the prepare pass has just left in the last-level cache.
+    if (max_chunks <= 1 && head_dim == 128 && chunk == 64) {
+        // every sequence one chunk: prepare and walk in one kernel, which
+        // reads each operand block back at once, so one launch over all
+        // chunks (no cache-sized segments; each block at its own place)
+        const Varlen vl{cu_seqlens, state, rows, max_chunks, total_chunks, 0, total_chunks,
+                        status};
+        return prefill_one_chunk<128, 64>(q, k, v, gate, beta, core, heads, scale, workspace, vl,
+                                          B, stream);
+    }
     const int seg = prefill_segment_chunks(total_chunks * chunk, heads, head_dim, chunk);
     for (int lo = 0; lo < total_chunks; lo += seg) {
         const Varlen vl{cu_seqlens, state, rows, max_chunks, total_chunks, lo,
                         std::min(lo + seg, total_chunks), status};
-        if (max_chunks <= 1 && head_dim == 128 && chunk == 64) {
-            // every sequence one chunk: prepare and walk in one kernel
-            const hipError_t e = prefill_one_chunk<128, 64>(q, k, v, gate, beta, core, heads,
-                                                            scale, workspace, vl, B, stream);
-            if (e != hipSuccess) return e;
-            continue;
-        }
         hipError_t e = KDA_PREFILL_DISPATCH(prepare_t, q, k, v, gate, beta, 0, heads, workspace,
                                             vl, B, stream);
         if (e != hipSuccess) return e;

@@ -218,3 +218,31 @@ def test_varlen_one_chunk_kernel_skips_and_reports(skip):
         one_core, one_S = gpu_prefill(cases[s], T, C, C, scale)
         np.testing.assert_array_equal(core[cu[s]:cu[s + 1]], one_core[:T], err_msg=f"seq {s}")
         np.testing.assert_array_equal(states[s], one_S, err_msg=f"seq {s} state")
+
+
+def test_varlen_thousands_of_one_chunk_prompts():
+    # 3000 prompts of at most one chunk (one launch of the fused kernel, no
+    # segments): a sample bitwise equal to kda_prefill alone, and the oracle
+    H, D, C = 2, 128, 64
+    rng = np.random.default_rng(1950)
+    lengths = [int(x) for x in rng.integers(0, 65, size=3000)]
+    scale = D ** -0.5
+    cases = [core_case(T, H, D, 20000 + s, 0.05) for s, T in enumerate(lengths)]
+    cu, core, states = run_varlen(cases, H, D, C, scale)
+    for s in list(range(0, len(lengths), 257)) + [len(lengths) - 1]:
+        c, T = cases[s], lengths[s]
+        if T == 0:
+            np.testing.assert_array_equal(states[s], c["S0"])
+            continue
+        one_core, one_S = gpu_prefill(c, T, C, C, scale, fill=0.0)
+        np.testing.assert_array_equal(core[cu[s]:cu[s + 1]], one_core[:T], err_msg=f"seq {s}")
+        np.testing.assert_array_equal(states[s], one_S, err_msg=f"seq {s} state")
+    for s in (1, 1500, 2999):
+        c = cases[s]
+        if lengths[s] == 0:
+            continue
+        ref_core, ref_S, _ = oracle.kda_recurrence(c["q"], c["k"], c["v"], c["gate"], c["beta"],
+                                                   c["S0"], scale)
+        assert relerr(core[cu[s]:cu[s + 1]], ref_core) < TOL
+        assert relerr(states[s], ref_S) < TOL
+    assert np.all(core[cu[-1]:] == SENTINEL)

@@ -27,9 +27,9 @@ static hipError_t prepare_src(const QkvSrc<BF> &src, const float *gate, const fl
                               int H, void *workspace, const Varlen &vl, int B, hipStream_t stream)
 {
     const dim3 grid = vl.cu ? dim3(vl.max_chunks, H, B) : dim3((T + C - 1) / C, H);
-    // the split kernel takes one sequence's chunks in y (heads fastest); the
-    // callers launch at most kMaxChunksPerLaunch chunks at a time
-    const dim3 grid_split = vl.cu ? grid : dim3(H, (T + C - 1) / C);
+    // the split kernel takes the chunks in y (heads fastest); the callers
+    // launch at most kMaxChunksPerLaunch chunks at a time
+    const dim3 grid_split = vl.cu ? dim3(H, vl.max_chunks, B) : dim3(H, (T + C - 1) / C);
     if constexpr (Blk<D, C>::kSplit)
         hipLaunchKernelGGL((kda_chunk_prep_split_kernel<D, C, BF>), grid_split,
                            dim3(PrefCfg<D, C>::kThreads), 0, stream, src, gate, beta, T, H,

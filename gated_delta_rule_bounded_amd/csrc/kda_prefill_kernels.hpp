@@ -1073,10 +1073,10 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     float *__restrict__ ws, const Varlen vl)
 {
     using B = Blk<D, C>;
-    // one sequence: heads fastest in the grid (a round of resident workgroups
-    // reads whole token rows and writes adjacent operand blocks); several
-    // sequences: chunks in x, heads in y, sequences in z
-    const int n = vl.cu ? (int)blockIdx.x : (int)blockIdx.y, h = vl.cu ? (int)blockIdx.y : (int)blockIdx.x;
+    // heads fastest in the grid (a round of resident workgroups reads whole
+    // token rows and writes adjacent operand blocks): heads in x, chunks in
+    // y, and for several sequences the sequence in z
+    const int n = (int)blockIdx.y, h = (int)blockIdx.x;
     int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
     if (vl.cu) {
         const SeqSpan sp = seq_span<C>(vl, blockIdx.z);

@@ -72,10 +72,44 @@ static hipError_t forward_t(float *state, float *core, int T, int H, float scale
     const bool one = vl.cu ? vl.max_chunks <= 1 : NC <= 1;
     if constexpr (Blk<D, C>::kSplit) {
         if (!one) {
-            hipLaunchKernelGGL((kda_chunk_fwd_split_kernel<D, C, true>), grid,
-                               dim3(2 * PrefCfg<D, C>::kThreads), 0, stream,
-                               static_cast<const float *>(workspace), state, core, T, NC, H, scale,
-                               vl);
+            // Several sequences: a workgroup may take NJ column tiles of its
+            // head (the head's operand block read once for all of them; the
+            // same bits for any NJ).  Per chunk a workgroup's time is set by
+            // the block it reads, so fewer, wider workgroups finish a
+            // segment's walks in fewer rounds, as long as they still cover
+            // the CUs: the widest NJ of 1, 2, 4 that launches at least 256
+            // workgroups for the sequences a segment holds (estimated from the
+            // mean chunks per sequence).  Measured at 4096 tokens, 32 heads:
+            // 8 x 512 tokens 231 -> 188 us, 16 x 256 257 -> 202 us, 4 x 1024
+            // 216 -> 189 us (NJ = 2), 2 x 2048 best at NJ = 1.
+            int nj = 1;
+            if (vl.cu) {
+                const int64_t seg = vl.seg_hi - vl.seg_lo;
+                const int64_t seqs = std::max<int64_t>(
+                    1, std::min<int64_t>(B, (int64_t)B * seg / std::max(1, vl.total_chunks)));
+                const int64_t tiles = seqs * H * PrefCfg<D, C>::kDT;
+                for (int c = 4; c > 1 && nj == 1; c /= 2)
+                    if (PrefCfg<D, C>::kDT % c == 0 && tiles / c >= 256) nj = c;
+            }
+            const dim3 g(H * PrefCfg<D, C>::kDT / nj, grid.y);
+            const dim3 blk(2 * PrefCfg<D, C>::kThreads);
+            const float *ws = static_cast<const float *>(workspace);
+            if constexpr (PrefCfg<D, C>::kDT % 4 == 0) {
+                if (nj == 4) {
+                    hipLaunchKernelGGL((kda_chunk_fwd_split_kernel<D, C, true, 4>), g, blk, 0, stream,
+                                       ws, state, core, T, NC, H, scale, vl);
+                    return hipGetLastError();
+                }
+            }
+            if constexpr (PrefCfg<D, C>::kDT % 2 == 0) {
+                if (nj == 2) {
+                    hipLaunchKernelGGL((kda_chunk_fwd_split_kernel<D, C, true, 2>), g, blk, 0, stream,
+                                       ws, state, core, T, NC, H, scale, vl);
+                    return hipGetLastError();
+                }
+            }
+            hipLaunchKernelGGL((kda_chunk_fwd_split_kernel<D, C, true>), g, blk, 0, stream, ws,
+                               state, core, T, NC, H, scale, vl);
             return hipGetLastError();
         }
         return fwd_split_one_chunk<D, C>(grid, static_cast<const float *>(workspace), state, core,

@@ -246,3 +246,24 @@ def test_varlen_thousands_of_one_chunk_prompts():
         assert relerr(core[cu[s]:cu[s + 1]], ref_core) < TOL
         assert relerr(states[s], ref_S) < TOL
     assert np.all(core[cu[-1]:] == SENTINEL)
+
+
+@pytest.mark.parametrize("nseq,L", [(4, 1024), (16, 256)])
+def test_varlen_wide_walk_workgroups_bitwise(nseq, L):
+    # many (prompt, head) pairs per segment: the walk takes 2 or 4 value-
+    # column tiles per workgroup; every prompt's rows and state are still
+    # bitwise those of kda_prefill alone (one 16-column tile per workgroup)
+    H, D, C = 32, 128, 64
+    scale = D ** -0.5
+    lengths = [L] * nseq
+    cases = [core_case(L, H, D, 2100 + s, 0.05, qkv_bf16=True) for s in range(nseq)]
+    cu, core, states = run_varlen(cases, H, D, C, scale)
+    for s in sorted({0, nseq // 2, nseq - 1}):
+        one_core, one_S = gpu_prefill(cases[s], L, L, C, scale)
+        np.testing.assert_array_equal(core[cu[s]:cu[s + 1]], one_core[:L], err_msg=f"seq {s}")
+        np.testing.assert_array_equal(states[s], one_S, err_msg=f"seq {s} state")
+    c = cases[nseq - 1]
+    ref_core, ref_S, _ = oracle.kda_recurrence(c["q"], c["k"], c["v"], c["gate"], c["beta"],
+                                               c["S0"], scale, threads=THREADS)
+    assert relerr(core[cu[-2]:cu[-1]], ref_core) < TOL
+    assert relerr(states[-1], ref_S) < TOL

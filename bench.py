@@ -488,7 +488,7 @@ def bench_prefill_varlen(kda, dev, reps=50):
         tab = kda.ptr_table(st)
         cu = torch.arange(0, T + 1, L, dtype=torch.int32, device=dev)
         mx, tot = kda.varlen_chunks([L] * n_seq, C)
-        ws = torch.empty(kda.kda_prefill_workspace_bytes(tot * C, H, D, C), dtype=torch.uint8,
+        ws = torch.empty(kda.kda_prefill_varlen_workspace_bytes(n_seq, tot, H, D, C), dtype=torch.uint8,
                          device=dev)
         core = torch.empty(T, H, D, device=dev)
 

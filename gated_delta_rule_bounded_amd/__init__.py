@@ -21,6 +21,7 @@ from ._lib import KdaError, last_error  # noqa: F401
 __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_noalloc", "kda_prefill_prepare",
            "kda_prefill_forward", "kda_decode", "kda_decode_k",
            "gated_rmsnorm", "kda_prefill_workspace_bytes", "kda_prefill_segment_chunks",
+           "kda_prefill_varlen_workspace_bytes",
            "kda_block_prefill", "block_buffers", "BLOCK_WEIGHT_NAMES",
            "dense_gemv_bf16_batchm", "kda_prefill_varlen", "varlen_chunks",
            "kda_verify_k", "kda_fold_accepted", "kda_prefill_split",
@@ -169,6 +170,13 @@ def kda_gate(g_raw, a_log, dt_bias, gate, *, T, heads, head_dim, b_raw=None, bet
 
 def kda_prefill_workspace_bytes(T_pad, heads, head_dim, chunk):
     return int(_lib.lib.kda_prefill_workspace_bytes(T_pad, heads, head_dim, chunk))
+
+
+def kda_prefill_varlen_workspace_bytes(B, total_chunks, heads, head_dim, chunk):
+    """Workspace of kda_prefill_varlen: the operand blocks of all chunks and
+    the call's sequence tables."""
+    return int(_lib.lib.kda_prefill_varlen_workspace_bytes(B, total_chunks, heads, head_dim,
+                                                           chunk))
 
 
 def kda_prefill_segment_chunks(T, heads, head_dim, chunk):

@@ -16,7 +16,7 @@ SYMBOLS = ("kda_last_error", "conv_silu_l2", "kda_gate", "kda_prefill_workspace_
            "kda_block_prefill", "dense_gemv_bf16_batchm", "kda_block_decode_k",
            "kda_block_decode", "kda_prefill_varlen", "kda_verify_k", "kda_fold_accepted",
            "kda_prefill_split", "kda_block_verify_k", "kda_block_fold_accepted",
-           "kda_prefill_bf16", "kda_prefill_noalloc")
+           "kda_prefill_bf16", "kda_prefill_noalloc", "kda_prefill_varlen_workspace_bytes")
 
 
 class BlockWeights(ctypes.Structure):
@@ -65,6 +65,8 @@ def _load():
     lib.kda_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.kda_prefill_segment_chunks.restype = ctypes.c_int32
     lib.kda_prefill_segment_chunks.argtypes = [i32, i32, i32, i32]
+    lib.kda_prefill_varlen_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_prefill_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.kda_prefill.restype = ctypes.c_int
     lib.kda_prefill.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, f32, P,
                                 ctypes.c_size_t, P]

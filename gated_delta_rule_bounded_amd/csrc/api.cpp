@@ -114,6 +114,15 @@ size_t kda_prefill_workspace_bytes(int32_t T_pad, int32_t heads, int32_t head_di
     return kda::prefill_workspace_bytes(T_pad, heads, head_dim, chunk);
 }
 
+size_t kda_prefill_varlen_workspace_bytes(int32_t B, int32_t total_chunks, int32_t heads,
+                                          int32_t head_dim, int32_t chunk)
+{
+    if (B < 0 || B > 65535 || total_chunks < 0 || heads <= 0 || !(chunk == 16 || chunk == 64) ||
+        (int64_t)total_chunks * chunk > (int64_t)1 << 30)
+        return 0;
+    return kda::prefill_varlen_workspace_bytes(B, total_chunks, heads, head_dim, chunk);
+}
+
 int32_t kda_prefill_segment_chunks(int32_t T, int32_t heads, int32_t head_dim, int32_t chunk)
 {
     if (T < 0 || heads <= 0 || !head_dim_ok(head_dim) || !(chunk == 16 || chunk == 64)) return 0;
@@ -351,8 +360,10 @@ int kda_prefill_varlen(const float *q, const float *k, const float *v, const flo
     if (B == 0 || rows == 0 || total_chunks == 0 || max_chunks == 0) return ok();
     if (!q || !k || !v || !gate || !beta || !state || !core || !cu_seqlens || !workspace)
         return fail(KDA_ERR_NULL, "kda_prefill_varlen: null pointer argument");
-    const size_t need = kda::prefill_workspace_bytes(total_chunks * chunk, heads, head_dim, chunk);
-    if ((int64_t)total_chunks * chunk > (int64_t)1 << 30 || workspace_bytes < need)
+    if ((int64_t)total_chunks * chunk > (int64_t)1 << 30)
+        return fail(KDA_ERR_SHAPE, "kda_prefill_varlen: total_chunks=%d too large", total_chunks);
+    const size_t need = kda::prefill_varlen_workspace_bytes(B, total_chunks, heads, head_dim, chunk);
+    if (workspace_bytes < need)
         return fail(KDA_ERR_WORKSPACE, "kda_prefill_varlen: workspace %zu bytes < %zu needed",
                     workspace_bytes, need);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(core) ||

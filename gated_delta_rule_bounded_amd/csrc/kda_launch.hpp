@@ -130,7 +130,9 @@ hipError_t launch_kda_prefill_bf16(const uint16_t *qkv, int64_t ldqkv, const flo
 // state pointer each; one prepare and one walk for all of them.  total_chunks
 // = sum over sequences of ceil(len / chunk) operand blocks in the workspace;
 // max_chunks = the longest sequence's chunk count.  Sequences that would not
-// fit either are left untouched.
+// fit either are left untouched.  The workspace holds the operand blocks and
+// then the call's sequence tables: prefill_varlen_workspace_bytes.
+size_t prefill_varlen_workspace_bytes(int B, int total_chunks, int heads, int head_dim, int chunk);
 hipError_t launch_kda_prefill_varlen(const float *q, const float *k, const float *v,
                                      const float *gate, const float *beta, float *const *state,
                                      float *core, const int32_t *cu_seqlens, int B, int64_t rows,

@@ -11,6 +11,112 @@ size_t prefill_workspace_bytes(int T_pad, int heads, int head_dim, int chunk)
     return (size_t)(T_pad / chunk) * heads * blk * sizeof(float);
 }
 
+// The plan tables of a several-sequence call (layout above), and its report
+// bits (the KDA_REPORT_* values of kda.h): a sequence skipped because its
+// chunks do not fit max_chunks / total_chunks, and offsets that had to be
+// clamped, ORed into the caller's word with a vector atomic.  One workgroup of
+// kPlanThreads walks the sequences in blocks of kPlanThreads, carrying the
+// chunk and rank counts from block to block.
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void kda_varlen_plan_kernel(
+    const int32_t *__restrict__ cu, int B, int64_t rows, int C, int max_chunks,
+    int total_chunks, int32_t *__restrict__ plan, int32_t *status)
+{
+    constexpr int NWV = kPlanThreads / kWave;
+    int32_t *seq_of = plan, *chunk0 = plan + total_chunks, *rank = chunk0 + B;
+    int32_t *by_rank = rank + B + 1;
+    __shared__ int32_t s_c0[kPlanThreads];   // this block's chunk offsets (clamped)
+    __shared__ int64_t s_wc[NWV];
+    __shared__ int32_t s_wr[NWV];
+    __shared__ int32_t s_bits;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (tid == 0) s_bits = 0;
+    const int64_t cap = (int64_t)total_chunks + 1;
+    int64_t base_c = 0;   // chunks of the sequences before this block
+    int32_t base_r = 0;   // walked sequences before this block
+    int32_t bits = 0;
+    for (int s0 = 0; s0 < B; s0 += kPlanThreads) {
+        const int s = s0 + tid, n = min(kPlanThreads, B - s0);
+        int64_t nch = 0;
+        if (s < B) {
+            int64_t lo, hi;
+            seq_rows(cu, rows, s, lo, hi);
+            nch = (hi - lo + C - 1) / C;
+            const int64_t a = cu[s], b = cu[s + 1];
+            if (a < 0 || b < a || b > rows) bits |= kReportRowsClamped;
+        }
+        // exclusive prefix of the chunk counts over the block
+        int64_t inc = nch;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int64_t t = __shfl_up(inc, o);
+            if (lane >= o) inc += t;
+        }
+        if (lane == kWave - 1) s_wc[wv] = inc;
+        __syncthreads();
+        int64_t before = 0, total = 0;
+        for (int i = 0; i < NWV; ++i) {
+            before += i < wv ? s_wc[i] : 0;
+            total += s_wc[i];
+        }
+        const int64_t c0 = base_c + before + inc - nch;
+        const bool ok = nch <= max_chunks && c0 + nch <= total_chunks;
+        const int32_t walk = s < B && ok && nch > 0;
+        if (s < B && !ok) bits |= kReportSeqSkipped;
+        // exclusive prefix of the walked flags
+        int32_t rinc = walk;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int32_t t = __shfl_up(rinc, o);
+            if (lane >= o) rinc += t;
+        }
+        if (lane == kWave - 1) s_wr[wv] = rinc;
+        s_c0[tid] = (int32_t)min(c0, cap);
+        __syncthreads();
+        int32_t rbefore = 0, rtotal = 0;
+        for (int i = 0; i < NWV; ++i) {
+            rbefore += i < wv ? s_wr[i] : 0;
+            rtotal += s_wr[i];
+        }
+        const int32_t r = base_r + rbefore + rinc - walk;
+        if (s < B) {
+            chunk0[s] = s_c0[tid];
+            rank[s] = r;
+            if (walk) by_rank[r] = s;
+        }
+        // the owner of every global chunk of this block: the last sequence
+        // whose first chunk is at or before it (a sequence without chunks
+        // shares its first chunk only with sequences after it)
+        const int64_t g_end = min(base_c + total, (int64_t)total_chunks);
+        for (int64_t g = base_c + tid; g < g_end; g += kPlanThreads) {
+            int lo = 0, hi = n;   // s_c0[lo] <= g < s_c0[hi] (s_c0[n] taken as the end)
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_c0[mid] <= g) lo = mid; else hi = mid;
+            }
+            seq_of[g] = s0 + lo;
+        }
+        base_c += total;
+        base_r += rtotal;
+        __syncthreads();   // s_c0, s_wc, s_wr reused by the next block
+    }
+    for (int64_t g = min(base_c, (int64_t)total_chunks) + tid; g < total_chunks; g += kPlanThreads)
+        seq_of[g] = -1;
+    if (tid == 0) rank[B] = base_r;
+    if (status) {
+        if (bits) atomicOr(&s_bits, bits);
+        __syncthreads();
+        if (tid == 0 && s_bits) atomicOr(status, s_bits);
+    }
+}
+
+size_t prefill_varlen_workspace_bytes(int B, int total_chunks, int heads, int head_dim, int chunk)
+{
+    const size_t plan = (varlen_plan_ints(B, total_chunks) * sizeof(int32_t) + 255) & ~size_t(255);
+    return prefill_workspace_bytes(total_chunks * chunk, heads, head_dim, chunk) + plan;
+}
+
 int prefill_segment_chunks(int T, int heads, int head_dim, int chunk)
 {
     constexpr size_t kCacheBudget = size_t(160) << 20;   // of MI355X's 256 MiB last-level cache
@@ -24,12 +130,13 @@ constexpr int kMaxChunksPerLaunch = 65535;   // grid y
 
 template <int D, int C, bool BF>
 static hipError_t prepare_src(const QkvSrc<BF> &src, const float *gate, const float *beta, int T,
-                              int H, void *workspace, const Varlen &vl, int B, hipStream_t stream)
+                              int H, void *workspace, const Varlen &vl, hipStream_t stream)
 {
-    const dim3 grid = vl.cu ? dim3(vl.max_chunks, H, B) : dim3((T + C - 1) / C, H);
-    // the split kernel takes the chunks in y (heads fastest); the callers
-    // launch at most kMaxChunksPerLaunch chunks at a time
-    const dim3 grid_split = vl.cu ? dim3(H, vl.max_chunks, B) : dim3(H, (T + C - 1) / C);
+    // one workgroup per (chunk, head); for several sequences the chunks are
+    // those of the segment.  The split kernel takes the chunks in y (heads
+    // fastest); the callers launch at most kMaxChunksPerLaunch chunks at a time
+    const int nc = vl.cu ? vl.seg_hi - vl.seg_lo : (T + C - 1) / C;
+    const dim3 grid(nc, H), grid_split(H, nc);
     if constexpr (Blk<D, C>::kSplit)
         hipLaunchKernelGGL((kda_chunk_prep_split_kernel<D, C, BF>), grid_split,
                            dim3(PrefCfg<D, C>::kThreads), 0, stream, src, gate, beta, T, H,
@@ -44,10 +151,10 @@ static hipError_t prepare_src(const QkvSrc<BF> &src, const float *gate, const fl
 template <int D, int C>
 static hipError_t prepare_t(const float *q, const float *k, const float *v, const float *gate,
                             const float *beta, int T, int H, void *workspace, const Varlen &vl,
-                            int B, hipStream_t stream)
+                            hipStream_t stream)
 {
     const QkvSrc<false> src{q, k, v, (int64_t)H * D};
-    return prepare_src<D, C, false>(src, gate, beta, T, H, workspace, vl, B, stream);
+    return prepare_src<D, C, false>(src, gate, beta, T, H, workspace, vl, stream);
 }
 
 // q | k | v read from bf16 rows (row stride ldqkv elements)
@@ -58,7 +165,7 @@ static hipError_t prepare_bf16_t(const uint16_t *qkv, int64_t ldqkv, const float
 {
     const int64_t qw = (int64_t)H * D;
     const QkvSrc<true> src{qkv, qkv + qw, qkv + 2 * qw, ldqkv};
-    return prepare_src<D, C, true>(src, gate, beta, T, H, workspace, Varlen{}, 1, stream);
+    return prepare_src<D, C, true>(src, gate, beta, T, H, workspace, Varlen{}, stream);
 }
 
 template <int D, int C>
@@ -66,7 +173,9 @@ static hipError_t forward_t(float *state, float *core, int T, int H, float scale
                             const void *workspace, const Varlen &vl, int B, hipStream_t stream)
 {
     const int NC = (T + C - 1) / C;
-    const dim3 grid(H * PrefCfg<D, C>::kDT, vl.cu ? B : 1);
+    // several sequences: one row of workgroups per sequence of the segment
+    // (at most one per chunk)
+    const dim3 grid(H * PrefCfg<D, C>::kDT, vl.cu ? std::min(B, vl.seg_hi - vl.seg_lo) : 1);
     // every walk one chunk (sequences longer than max_chunks are skipped by
     // the kernels): the instance without the load-ahead register set
     const bool one = vl.cu ? vl.max_chunks <= 1 : NC <= 1;
@@ -144,7 +253,7 @@ hipError_t launch_kda_prefill_prepare(const float *q, const float *k, const floa
         void *ws = static_cast<char *>(workspace) + (size_t)c0 * chunk_bytes;
         const hipError_t e = KDA_PREFILL_DISPATCH(prepare_t, q + r0 * HD, k + r0 * HD, v + r0 * HD,
                                                   gate + r0 * HD, beta + r0 * heads, Ts, heads,
-                                                  ws, Varlen{}, 1, stream);
+                                                  ws, Varlen{}, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -224,25 +333,38 @@ hipError_t launch_kda_prefill_varlen(const float *q, const float *k, const float
                                      int chunk, float scale, void *workspace, int32_t *status,
                                      hipStream_t stream)
 {
-    // Segments of global chunks sized as kda_prefill's: each is prepared into
-    // the start of the workspace and walked at once (one walk per sequence,
-    // head and value slice that has chunks in it), so the forward pass reads
-    // operand blocks the prepare pass has just left in the last-level cache.
+    // More than a wave of sequences: the sequence tables after the operand
+    // blocks, written first (the plan kernel reports).  Then segments of
+    // global chunks sized as kda_prefill's, each prepared into the start of
+    // the workspace and walked at once (one walk per sequence, head and value
+    // slice that has chunks in it), so the forward pass reads operand blocks
+    // the prepare pass has just left in the last-level cache.
+    int32_t *plan = nullptr;
+    if (B > kWave) {
+        plan = reinterpret_cast<int32_t *>(
+            static_cast<char *>(workspace) +
+            prefill_workspace_bytes(total_chunks * chunk, heads, head_dim, chunk));
+        hipLaunchKernelGGL(kda_varlen_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream,
+                           cu_seqlens, B, rows, chunk, max_chunks, total_chunks, plan, status);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+        status = nullptr;
+    }
     if (max_chunks <= 1 && head_dim == 128 && chunk == 64) {
         // every sequence one chunk: prepare and walk in one kernel, which
         // reads each operand block back at once, so one launch over all
         // chunks (no cache-sized segments; each block at its own place)
-        const Varlen vl{cu_seqlens, state, rows, max_chunks, total_chunks, 0, total_chunks,
-                        status};
+        const Varlen vl{cu_seqlens, state, rows, B, max_chunks, total_chunks, 0, total_chunks,
+                        plan, status};
         return prefill_one_chunk<128, 64>(q, k, v, gate, beta, core, heads, scale, workspace, vl,
-                                          B, stream);
+                                          stream);
     }
-    const int seg = prefill_segment_chunks(total_chunks * chunk, heads, head_dim, chunk);
+    const int seg = std::min(prefill_segment_chunks(total_chunks * chunk, heads, head_dim, chunk),
+                             kMaxChunksPerLaunch);
     for (int lo = 0; lo < total_chunks; lo += seg) {
-        const Varlen vl{cu_seqlens, state, rows, max_chunks, total_chunks, lo,
-                        std::min(lo + seg, total_chunks), status};
+        const Varlen vl{cu_seqlens, state, rows, B, max_chunks, total_chunks, lo,
+                        std::min(lo + seg, total_chunks), plan, status};
         hipError_t e = KDA_PREFILL_DISPATCH(prepare_t, q, k, v, gate, beta, 0, heads, workspace,
-                                            vl, B, stream);
+                                            vl, stream);
         if (e != hipSuccess) return e;
         e = KDA_PREFILL_DISPATCH(forward_t, nullptr, core, 0, heads, scale, workspace, vl, B,
                                  stream);

@@ -66,66 +66,163 @@ constexpr float kSpanLimit = 86.0f; // log2 units: largest diagonal-block decay 
 // segment boundary continues in the next launch from the state the previous
 // one stored, on the same chunk grid, so the result does not depend on the
 // segmentation.  cu == nullptr: one sequence, the plain arguments apply.
+//
+// The lengths live in device memory.  Every launch of a call sizes its grid
+// by the segment alone (a prepare workgroup per chunk of the segment, a walk
+// workgroup per sequence in it), and each workgroup finds its sequence:
+//   at most kWave sequences: from cu directly, one lane per sequence (a load
+//     and a prefix sum across the wave);
+//   more: in tables that a small plan kernel (one workgroup, once per call)
+//     builds from cu, with a few reads, whatever the number of sequences.
+// Plan layout, int32:
+//   seq_of[total_chunks]  sequence owning global chunk g (-1: no sequence)
+//   chunk0[B]             first global chunk of sequence s (chunks of the
+//                         sequences before it; total_chunks + 1 when past it)
+//   rank[B + 1]           walked sequences before s (rank[B]: all of them)
+//   by_rank[B]            the r-th walked sequence
+// A sequence is walked when it has chunks and they fit: nch <= max_chunks
+// and chunk0 + nch <= total_chunks; one that does not fit is skipped.
 // ---------------------------------------------------------------------------
 struct Varlen {
     const int32_t *cu;      // [B + 1] row offsets, or nullptr
     float *const *states;   // [B] state pointers (forward)
     int64_t rows;           // rows held by the row arrays
-    int32_t max_chunks;     // chunks of the longest sequence (prepare grid)
+    int32_t B;              // sequences
+    int32_t max_chunks;     // chunks of the longest sequence
     int32_t total_chunks;   // chunks of all sequences
     int32_t seg_lo, seg_hi; // global chunks of this launch; block 0 of the workspace = seg_lo
-    int32_t *status;        // run-time report word (KDA_REPORT_* bits), or nullptr
+    const int32_t *plan;    // the plan kernel's tables (B > kWave), else nullptr
+    int32_t *status;        // report word (B <= kWave; the plan kernel reports otherwise)
 };
+
+inline size_t varlen_plan_ints(int B, int total_chunks)
+{
+    return (size_t)total_chunks + 3 * (size_t)B + 1;
+}
 
 struct SeqSpan {
     int64_t row0, chunk0;
     int T, nch;
-    bool ok;   // inside the workspace and the prepare grid
+    bool ok;   // walked: inside the workspace and max_chunks
 };
 
 // Rows of sequence i, clamped to [0, rows): the same clamp for every i, so
 // chunk offsets and chunk counts agree between all workgroups.
-__device__ __forceinline__ void seq_rows(const Varlen &vl, int i, int64_t &lo, int64_t &hi)
+__device__ __forceinline__ void seq_rows(const int32_t *cu, int64_t rows, int i, int64_t &lo,
+                                         int64_t &hi)
 {
-    lo = min(max((int64_t)vl.cu[i], (int64_t)0), vl.rows);
-    hi = min(max((int64_t)vl.cu[i + 1], lo), vl.rows);
+    lo = min(max((int64_t)cu[i], (int64_t)0), rows);
+    hi = min(max((int64_t)cu[i + 1], lo), rows);
 }
 
 template <int C>
-__device__ __forceinline__ SeqSpan seq_span(const Varlen &vl, int s)
+__device__ __forceinline__ SeqSpan seq_span(const Varlen &vl, int s, int64_t chunk0)
 {
     SeqSpan r;
     int64_t hi;
-    seq_rows(vl, s, r.row0, hi);
+    seq_rows(vl.cu, vl.rows, s, r.row0, hi);
     r.T = (int)(hi - r.row0);
     r.nch = (r.T + C - 1) / C;
-    // chunk offset: chunks of sequences 0..s-1, summed across the wave
-    const int lane = threadIdx.x & 63;
-    int64_t acc = 0;
-    for (int i = lane; i < s; i += kWave) {
-        int64_t lo_i, hi_i;
-        seq_rows(vl, i, lo_i, hi_i);
-        acc += (hi_i - lo_i + C - 1) / C;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    r.chunk0 = acc;
+    r.chunk0 = chunk0;
     r.ok = r.nch <= vl.max_chunks && r.chunk0 + r.nch <= vl.total_chunks;
     return r;
 }
 
-// Report bits of a several-sequence call (the KDA_REPORT_* values of kda.h):
-// a sequence that is skipped because its chunks do not fit max_chunks /
-// total_chunks, and offsets that had to be clamped.  One thread per sequence
-// reports (its leader workgroup), in the first segment's launch; the bits are
-// ORed into the caller's word with a vector atomic.
-__device__ __forceinline__ void varlen_report(const Varlen &vl, int s, bool ok, bool leader)
+// At most kWave sequences: lane i's view of sequence i (chunk offset, chunk
+// count, walked), the same on every wave of every workgroup.
+struct WaveSeq {
+    int64_t c0;
+    int nch;
+    bool walk;
+};
+
+template <int C>
+__device__ __forceinline__ WaveSeq wave_seq(const Varlen &vl)
 {
-    if (vl.status == nullptr || vl.seg_lo != 0 || !leader || threadIdx.x != 0) return;
-    const int64_t a = vl.cu[s], b = vl.cu[s + 1];
-    const int32_t bits = (ok ? 0 : kReportSeqSkipped) |
-                         (a < 0 || b < a || b > vl.rows ? kReportRowsClamped : 0);
-    if (bits) atomicOr(vl.status, bits);
+    const int lane = threadIdx.x & 63;
+    int64_t nch = 0;
+    if (lane < vl.B) {
+        int64_t lo, hi;
+        seq_rows(vl.cu, vl.rows, lane, lo, hi);
+        nch = (hi - lo + C - 1) / C;
+    }
+    int64_t inc = nch;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int64_t t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    WaveSeq w;
+    w.c0 = inc - nch;
+    w.nch = (int)nch;
+    w.walk = nch > 0 && nch <= vl.max_chunks && w.c0 + nch <= vl.total_chunks;
+    return w;
+}
+
+// Report bits (the KDA_REPORT_* values of kda.h) of a call of at most kWave
+// sequences, from one workgroup of its first launch: a sequence skipped
+// because its chunks do not fit max_chunks / total_chunks, and offsets that
+// had to be clamped, ORed into the caller's word with a vector atomic.
+__device__ __forceinline__ void wave_report(const Varlen &vl, const WaveSeq &w, bool leader)
+{
+    if (vl.status == nullptr || vl.seg_lo != 0 || !leader || threadIdx.x >= kWave) return;
+    const int lane = threadIdx.x;
+    bool skipped = false, clamped = false;
+    if (lane < vl.B) {
+        const int64_t a = vl.cu[lane], b = vl.cu[lane + 1];
+        skipped = !(w.nch <= vl.max_chunks && w.c0 + w.nch <= vl.total_chunks);
+        clamped = a < 0 || b < a || b > vl.rows;
+    }
+    const int32_t bits = (__ballot(skipped) ? kReportSeqSkipped : 0) |
+                         (__ballot(clamped) ? kReportRowsClamped : 0);
+    if (lane == 0 && bits) atomicOr(vl.status, bits);
+}
+
+// The sequence of the prepare workgroup for global chunk g: false when no
+// walked sequence owns the chunk.  leader: this workgroup reports for a call
+// of at most kWave sequences.
+template <int C>
+__device__ __forceinline__ bool chunk_span(const Varlen &vl, int64_t g, SeqSpan &sp, bool leader)
+{
+    if (vl.plan == nullptr) {
+        const WaveSeq w = wave_seq<C>(vl);
+        wave_report(vl, w, leader);
+        const uint64_t m = __ballot(w.nch > 0 && w.c0 <= g && g < w.c0 + w.nch);
+        if (m == 0) return false;
+        const int s = __builtin_ctzll(m);
+        sp = seq_span<C>(vl, s, __shfl(w.c0, s));
+        return sp.ok;
+    }
+    const int s = vl.plan[g];
+    if (s < 0) return false;
+    sp = seq_span<C>(vl, s, vl.plan[vl.total_chunks + s]);
+    return sp.ok;
+}
+
+// The y-th walked sequence with chunks in [seg_lo, seg_hi): false past the
+// last one.  s is its index.
+template <int C>
+__device__ __forceinline__ bool walker_span(const Varlen &vl, int y, int &s, SeqSpan &sp)
+{
+    if (vl.plan == nullptr) {
+        const WaveSeq w = wave_seq<C>(vl);
+        const uint64_t m = __ballot(w.walk && w.c0 < vl.seg_hi && w.c0 + w.nch > vl.seg_lo);
+        if (y >= __popcll(m)) return false;
+        const int lane = threadIdx.x & 63;
+        const bool mine = ((m >> lane) & 1) && __popcll(m & ((uint64_t(1) << lane) - 1)) == y;
+        s = __builtin_ctzll(__ballot(mine));
+        sp = seq_span<C>(vl, s, __shfl(w.c0, s));
+        return sp.ok;
+    }
+    const int32_t *rank = vl.plan + vl.total_chunks + vl.B;
+    const int32_t *by_rank = rank + vl.B + 1;
+    const int s_lo = vl.plan[vl.seg_lo], s_hi = vl.plan[vl.seg_hi - 1];
+    if (s_lo < 0) return false;   // the segment is past the last sequence
+    const int r = rank[s_lo] + y;
+    if (r >= (s_hi < 0 ? rank[vl.B] : rank[s_hi + 1])) return false;
+    s = by_rank[r];
+    sp = seq_span<C>(vl, s, vl.plan[vl.total_chunks + s]);
+    return sp.ok;
 }
 
 template <int D, int C>
@@ -422,14 +519,15 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_prep_kernel(
 {
     constexpr int NW = PrefCfg<D, C>::kNW, DT = PrefCfg<D, C>::kDT;
     using B = Blk<D, C>;
-    const int n = blockIdx.x, h = blockIdx.y;
+    // several sequences: x is the chunk of the segment
+    int n = blockIdx.x;
+    const int h = blockIdx.y;
     int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
     if (vl.cu) {
-        const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
-        varlen_report(vl, blockIdx.z, sp.ok, blockIdx.x == 0 && blockIdx.y == 0);
-        nblk = sp.chunk0 + n;
-        if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
-        nblk -= vl.seg_lo;
+        SeqSpan sp;
+        if (!chunk_span<C>(vl, vl.seg_lo + nblk, sp, blockIdx.x == 0 && blockIdx.y == 0))
+            return;   // uniform over the workgroup
+        n = (int)(vl.seg_lo + nblk - sp.chunk0);
         const int64_t r0 = sp.row0 * H;
         src.advance(sp.row0);
         gate += r0 * D, beta += r0;
@@ -1075,15 +1173,15 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     using B = Blk<D, C>;
     // heads fastest in the grid (a round of resident workgroups reads whole
     // token rows and writes adjacent operand blocks): heads in x, chunks in
-    // y, and for several sequences the sequence in z
-    const int n = (int)blockIdx.y, h = (int)blockIdx.x;
+    // y (for several sequences, the chunks of the segment)
+    int n = (int)blockIdx.y;
+    const int h = (int)blockIdx.x;
     int64_t nblk = n, tmax = (int64_t)1 << 62;   // operand block index; last row that exists
     if (vl.cu) {
-        const SeqSpan sp = seq_span<C>(vl, blockIdx.z);
-        varlen_report(vl, blockIdx.z, sp.ok, blockIdx.x == 0 && blockIdx.y == 0);
-        nblk = sp.chunk0 + n;
-        if (!sp.ok || n >= sp.nch || nblk < vl.seg_lo || nblk >= vl.seg_hi) return;   // uniform
-        nblk -= vl.seg_lo;
+        SeqSpan sp;
+        if (!chunk_span<C>(vl, vl.seg_lo + nblk, sp, blockIdx.x == 0 && blockIdx.y == 0))
+            return;   // uniform over the workgroup
+        n = (int)(vl.seg_lo + nblk - sp.chunk0);
         const int64_t r0 = sp.row0 * H;
         src.advance(sp.row0);
         gate += r0 * D, beta += r0;
@@ -1120,13 +1218,15 @@ __global__ __launch_bounds__(C / 16 * 64) void kda_chunk_fwd_kernel(
     // all value slices of one head share an XCD (workgroups are dealt to the
     // 8 XCDs round-robin), so they share that XCD's L2 copy of the operands
     const int h = blockIdx.x % H, jt = blockIdx.x / H, j0 = 16 * jt;
-    if (vl.cu) {   // sequence blockIdx.y: its state, and its chunks inside this segment
-        const SeqSpan sp = seq_span<C>(vl, blockIdx.y);
+    if (vl.cu) {   // the blockIdx.y-th sequence of the segment: its state and chunks here
+        int s;
+        SeqSpan sp;
+        if (!walker_span<C>(vl, blockIdx.y, s, sp)) return;   // uniform over the workgroup
         const int64_t g0 = max(sp.chunk0, (int64_t)vl.seg_lo);
         const int64_t g1 = min(sp.chunk0 + sp.nch, (int64_t)vl.seg_hi);
-        if (!sp.ok || g0 >= g1) return;   // uniform over the workgroup
+        if (g0 >= g1) return;
         const int c0 = (int)(g0 - sp.chunk0);   // first chunk of the sequence walked here
-        state = vl.states[blockIdx.y];
+        state = vl.states[s];
         core += (sp.row0 + (int64_t)c0 * C) * H * D;
         ws += (g0 - vl.seg_lo) * H * B::kSize;
         NC = (int)(g1 - g0);
@@ -1812,13 +1912,15 @@ __global__ __launch_bounds__(2 * C / 16 * 64) __attribute__((amdgpu_waves_per_eu
 {
     using B = Blk<D, C>;
     const int h = blockIdx.x % H, jt = NJ * (blockIdx.x / H);
-    if (vl.cu) {   // sequence blockIdx.y: its state, and its chunks inside this segment
-        const SeqSpan sp = seq_span<C>(vl, blockIdx.y);
+    if (vl.cu) {   // the blockIdx.y-th sequence of the segment: its state and chunks here
+        int s;
+        SeqSpan sp;
+        if (!walker_span<C>(vl, blockIdx.y, s, sp)) return;   // uniform over the workgroup
         const int64_t g0 = max(sp.chunk0, (int64_t)vl.seg_lo);
         const int64_t g1 = min(sp.chunk0 + sp.nch, (int64_t)vl.seg_hi);
-        if (!sp.ok || g0 >= g1) return;   // uniform over the workgroup
+        if (g0 >= g1) return;
         const int c0 = (int)(g0 - sp.chunk0);   // first chunk of the sequence walked here
-        state = vl.states[blockIdx.y];
+        state = vl.states[s];
         core += (sp.row0 + (int64_t)c0 * C) * H * D;
         ws += (g0 - vl.seg_lo) * H * B::kSize;
         NC = (int)(g1 - g0);
@@ -1840,6 +1942,6 @@ hipError_t fwd_split_one_chunk(dim3 grid, const float *ws, float *state, float *
 template <int D, int C>
 hipError_t prefill_one_chunk(const float *q, const float *k, const float *v, const float *gate,
                              const float *beta, float *core, int H, float scale, void *workspace,
-                             const Varlen &vl, int B, hipStream_t stream);
+                             const Varlen &vl, hipStream_t stream);
 
 }  // namespace kda

@@ -18,15 +18,6 @@
 
 namespace kda {
 
-// Where a (head, sequence) workgroup's single chunk is: false when the
-// sequence has no chunk in this launch's segment (or is skipped).
-template <int C>
-__device__ __forceinline__ bool one_chunk_span(const Varlen &vl, int s, SeqSpan &sp)
-{
-    sp = seq_span<C>(vl, s);
-    return sp.ok && sp.nch == 1 && sp.chunk0 >= vl.seg_lo && sp.chunk0 < vl.seg_hi;
-}
-
 template <int D, int C>
 __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_walk1_kernel(
     const float *__restrict__ ws, float *__restrict__ state, float *__restrict__ core, int T,
@@ -34,10 +25,12 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
 {
     using B = Blk<D, C>;
     const int h = blockIdx.x;
-    if (vl.cu) {
+    if (vl.cu) {   // the blockIdx.y-th sequence of the segment, one chunk long
+        int s;
         SeqSpan sp;
-        if (!one_chunk_span<C>(vl, blockIdx.y, sp)) return;   // uniform over the workgroup
-        state = vl.states[blockIdx.y];
+        if (!walker_span<C>(vl, blockIdx.y, s, sp) || sp.nch != 1 || sp.chunk0 < vl.seg_lo)
+            return;   // uniform over the workgroup
+        state = vl.states[s];
         core += sp.row0 * H * D;
         ws += (sp.chunk0 - vl.seg_lo) * H * B::kSize;
         T = sp.T;
@@ -53,11 +46,15 @@ __global__ __launch_bounds__(C / 16 * 64) __attribute__((amdgpu_waves_per_eu(2))
     float *__restrict__ ws, float *__restrict__ core, float scale, const Varlen vl)
 {
     using B = Blk<D, C>;
-    const int h = blockIdx.x, s = blockIdx.y;
+    // one workgroup per (head, walked sequence): every walked sequence is one
+    // chunk, prepared and walked here
+    const int h = blockIdx.x;
+    if (vl.plan == nullptr && blockIdx.x == 0 && blockIdx.y == 0)
+        wave_report(vl, wave_seq<C>(vl), true);
+    int s;
     SeqSpan sp;
-    const bool here = one_chunk_span<C>(vl, s, sp);
-    varlen_report(vl, s, sp.ok, h == 0);
-    if (!here) return;   // uniform over the workgroup
+    if (!walker_span<C>(vl, blockIdx.y, s, sp) || sp.nch != 1 || sp.chunk0 < vl.seg_lo)
+        return;   // uniform over the workgroup
     src.advance(sp.row0);
     float *blk = ws + ((sp.chunk0 - vl.seg_lo) * H + h) * B::kSize;
     __shared__ union {
@@ -94,10 +91,11 @@ hipError_t fwd_split_one_chunk(dim3 grid, const float *ws, float *state, float *
 template <int D, int C>
 hipError_t prefill_one_chunk(const float *q, const float *k, const float *v, const float *gate,
                              const float *beta, float *core, int H, float scale, void *workspace,
-                             const Varlen &vl, int B, hipStream_t stream)
+                             const Varlen &vl, hipStream_t stream)
 {
     const QkvSrc<false> src{q, k, v, (int64_t)H * D};
-    hipLaunchKernelGGL((kda_chunk_fused1_kernel<D, C>), dim3(H, B), dim3(PrefCfg<D, C>::kThreads),
+    hipLaunchKernelGGL((kda_chunk_fused1_kernel<D, C>), dim3(H, std::min(vl.B, vl.seg_hi - vl.seg_lo)),
+                       dim3(PrefCfg<D, C>::kThreads),
                        0, stream, src, gate, beta, H, static_cast<float *>(workspace), core, scale,
                        vl);
     return hipGetLastError();
@@ -107,6 +105,6 @@ template hipError_t fwd_split_one_chunk<128, 64>(dim3, const float *, float *, f
                                                  int, float, const Varlen &, hipStream_t);
 template hipError_t prefill_one_chunk<128, 64>(const float *, const float *, const float *,
                                                const float *, const float *, float *, int, float,
-                                               void *, const Varlen &, int, hipStream_t);
+                                               void *, const Varlen &, hipStream_t);
 
 }  // namespace kda

@@ -152,6 +152,18 @@ size_t kda_prefill_workspace_bytes(int32_t T_pad, int32_t heads,
 int32_t kda_prefill_segment_chunks(int32_t T, int32_t heads, int32_t head_dim,
                                    int32_t chunk);
 
+/* Workspace bytes of kda_prefill_varlen over B sequences of total_chunks
+ * chunks: the operand blocks of kda_prefill_workspace_bytes(total_chunks *
+ * chunk, ...) followed by the call's sequence tables, (total_chunks + 3B + 1)
+ * int32 rounded up to 256 bytes, which a one-workgroup kernel fills from
+ * cu_seqlens at the start of the call so that every later launch of the call
+ * is sized by its segment and finds a workgroup's sequence in a few table
+ * reads.  0 on invalid arguments (B outside [0, 65535], total_chunks < 0,
+ * total_chunks * chunk above 2^30, heads <= 0, chunk not 16 or 64). */
+size_t kda_prefill_varlen_workspace_bytes(int32_t B, int32_t total_chunks,
+                                          int32_t heads, int32_t head_dim,
+                                          int32_t chunk);
+
 int kda_prefill(const float *q, const float *k, const float *v,
                 const float *gate, const float *beta, float *state, float *core,
                 int32_t T, int32_t T_pad, int32_t heads, int32_t head_dim,
@@ -266,7 +278,7 @@ int kda_prefill_split(const float *q, const float *k, const float *v,
  *   cu_seqlens  device int32 [B+1], non-decreasing, cu_seqlens[B] <= rows.
  *   max_chunks  max over s of ceil(len_s / chunk);
  *   total_chunks sum over s of ceil(len_s / chunk);
- *   workspace   at least kda_prefill_workspace_bytes(total_chunks * chunk,
+ *   workspace   at least kda_prefill_varlen_workspace_bytes(B, total_chunks,
  *               heads, head_dim, chunk) bytes, 256-byte aligned.
  * Each sequence's core rows and final state are bitwise those of a
  * kda_prefill call on that sequence alone (the chunk arithmetic is the same;

@@ -259,7 +259,7 @@ def test_block_decode_validation(lib):
 
 def test_varlen_validation(lib):
     H, Dh, C = 2, 16, 16
-    ws = lib.kda_prefill_workspace_bytes(10 * C, H, Dh, C)
+    ws = lib.kda_prefill_varlen_workspace_bytes(3, 10, H, Dh, C)
 
     def call(q=A, core=B, cu=C, state=Dp, wsp=E, ws_bytes=ws, Bn=3, rows=100, mx=4, tot=10,
              head_dim=Dh, chunk=C, status=None):
@@ -279,6 +279,18 @@ def test_varlen_validation(lib):
     assert call(wsp=B + 256) == E_ALIAS                        # workspace over core
     assert call(q=A + 4) == E_SHAPE                            # misaligned
     assert call(status=F + 2) == E_SHAPE                       # report word not 4-byte aligned
+
+
+def test_varlen_workspace_bytes(lib):
+    # the operand blocks of every chunk, then (total_chunks + 3B + 1) int32 of
+    # sequence tables rounded up to 256 bytes
+    blocks = lib.kda_prefill_workspace_bytes(10 * 64, 32, 128, 64)
+    assert lib.kda_prefill_varlen_workspace_bytes(3, 10, 32, 128, 64) == blocks + 256
+    assert lib.kda_prefill_varlen_workspace_bytes(1000, 10, 32, 128, 64) == blocks + 12288
+    assert lib.kda_prefill_varlen_workspace_bytes(1000, 0, 32, 128, 64) == 12032
+    for bad in ((-1, 10, 32, 128, 64), (65536, 10, 32, 128, 64), (3, -1, 32, 128, 64),
+                (3, 10, 32, 128, 32), (3, 10, 0, 128, 64), (3, (1 << 24) + 1, 32, 128, 64)):
+        assert lib.kda_prefill_varlen_workspace_bytes(*bad) == 0, bad
 
 
 def test_write_on_accept_validation(lib):

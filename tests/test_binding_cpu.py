@@ -117,7 +117,7 @@ def test_stage_sizes():
 
 def test_varlen_sizes():
     rows, B = 40, 3
-    ws = z(kda.kda_prefill_workspace_bytes(4 * C, H, D, C), dtype=torch.uint8)
+    ws = z(kda.kda_prefill_varlen_workspace_bytes(B, 4, H, D, C), dtype=torch.uint8)
 
     def call(**kw):
         a = dict(q=z(rows, H, D), k=z(rows, H, D), v=z(rows, H, D), gate=z(rows, H, D),

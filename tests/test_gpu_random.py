@@ -60,7 +60,7 @@ def test_varlen_random_prompts(i):
     states = [cuda(c["S0"]).contiguous() for c in cases]
     core = torch.full((rows, H, D), 7.0, device="cuda")
     mx, tot = kda.varlen_chunks(lengths, C)
-    ws = torch.empty(max(1, kda.kda_prefill_workspace_bytes(max(tot, 1) * C, H, D, C)),
+    ws = torch.empty(max(1, kda.kda_prefill_varlen_workspace_bytes(len(cases), tot, H, D, C)),
                      dtype=torch.uint8, device="cuda")
     say("random varlen", i, D, C, H, lengths)
     kda.kda_prefill_varlen(q, k, v, g, b, kda.ptr_table(states), core, torch.from_numpy(cu).cuda(),

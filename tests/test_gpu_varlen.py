@@ -39,7 +39,7 @@ def run_varlen(cases, H, D, C, scale, tail=3, tail_fill=np.nan, total_chunks=Non
     mx, tot = kda.varlen_chunks(lengths, C)
     tot = tot if total_chunks is None else total_chunks
     mx = mx if max_chunks is None else max_chunks
-    ws = torch.empty(max(1, kda.kda_prefill_workspace_bytes(max(tot, 1) * C, H, D, C)),
+    ws = torch.empty(max(1, kda.kda_prefill_varlen_workspace_bytes(len(cases), tot, H, D, C)),
                      dtype=torch.uint8, device="cuda")
     say("varlen", lengths, H, D, C, tot)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -105,23 +105,38 @@ def test_varlen_full_size_many_prompts():
     assert np.all(core[cu[-1]:] == SENTINEL)
 
 
-def test_varlen_sequence_outside_the_workspace_is_left_alone():
+# Calls of more than a wave (64) of sequences find them through the tables of
+# a plan kernel, smaller ones from cu directly: ``lead`` empty prompts ahead
+# of the cases take a test through the tables.
+LEADS = [0, 100]
+
+
+def _with_lead(lead, H, D, lengths, seed):
+    cases = [core_case(0, H, D, seed - 1 - i, 0.05) for i in range(lead)]
+    return cases + [core_case(T, H, D, seed + s, 0.05) for s, T in enumerate(lengths)]
+
+
+@pytest.mark.parametrize("lead", LEADS)
+def test_varlen_sequence_outside_the_workspace_is_left_alone(lead):
     # total_chunks one short: the last sequence's blocks would not fit, so it
     # is skipped whole (state and core rows untouched); the others are exact
     H, D, C = 2, 128, 64
     lengths = [100, 64, 70]
     scale = D ** -0.5
-    cases = [core_case(T, H, D, 1600 + s, 0.05) for s, T in enumerate(lengths)]
+    cases = _with_lead(lead, H, D, lengths, 1600)
     _, tot = kda.varlen_chunks(lengths, C)
     # the skip is reported (KDA_REPORT_SEQ_SKIPPED)
     cu, core, states = run_varlen(cases, H, D, C, scale, total_chunks=tot - 1, report=1)
-    np.testing.assert_array_equal(states[2], cases[2]["S0"])
-    assert np.all(core[cu[2]:cu[3]] == SENTINEL)
-    for s in (0, 1):
-        T = lengths[s]
+    o = lead
+    np.testing.assert_array_equal(states[o + 2], cases[o + 2]["S0"])
+    assert np.all(core[cu[o + 2]:cu[o + 3]] == SENTINEL)
+    for s in (o, o + 1):
+        T = lengths[s - o]
         one_core, one_S = gpu_prefill(cases[s], T, -(-T // C) * C, C, scale)
         np.testing.assert_array_equal(core[cu[s]:cu[s + 1]], one_core[:T])
         np.testing.assert_array_equal(states[s], one_S)
+    for s in range(lead):
+        np.testing.assert_array_equal(states[s], cases[s]["S0"])
 
 
 def test_varlen_single_chunk_prompts_same_bits_in_both_forward_instances():
@@ -153,13 +168,14 @@ def test_varlen_single_chunk_prompts_same_bits_in_both_forward_instances():
     assert relerr(states_b[-1], ref_S) < TOL
 
 
-def test_varlen_clamped_offset_is_reported():
+@pytest.mark.parametrize("lead", LEADS)
+def test_varlen_clamped_offset_is_reported(lead):
     # cu_seqlens[0] = -5 is clamped to row 0 (KDA_REPORT_ROWS_CLAMPED); the
     # rows and states are those of the call with the offset given as 0
     H, D, C = 2, 16, 16
     lengths = [40, 17, 33]
     scale = D ** -0.5
-    cases = [core_case(T, H, D, 1650 + s, 0.05) for s, T in enumerate(lengths)]
+    cases = _with_lead(lead, H, D, lengths, 1650)
     cu_a, core_a, states_a = run_varlen(cases, H, D, C, scale)
     cases_b = [dict(c, S0=c["S0"].copy()) for c in cases]
     cu_b, core_b, states_b = run_varlen(cases_b, H, D, C, scale, report=2, cu_first=-5)
@@ -193,25 +209,26 @@ def test_varlen_many_one_chunk_prompts_whole_head_walks():
     assert np.all(core[cu[-1]:] == SENTINEL)
 
 
+@pytest.mark.parametrize("lead", LEADS)
 @pytest.mark.parametrize("skip", ["longer_than_max_chunks", "outside_total_chunks"])
-def test_varlen_one_chunk_kernel_skips_and_reports(skip):
+def test_varlen_one_chunk_kernel_skips_and_reports(skip, lead):
     # max_chunks = 1 at 128 x 64 runs prepare and walk in one kernel; a prompt
     # longer than one chunk (max_chunks = 1 stated anyway) or one whose chunk
     # lies past total_chunks is skipped whole and reported, the others stay
     # bitwise those of kda_prefill alone
     H, D, C = 4, 128, 64
     lengths = [64, 30, 100, 1, 64] if skip == "longer_than_max_chunks" else [64, 30, 17, 1, 64]
+    lengths = [0] * lead + lengths
     scale = D ** -0.5
     cases = [core_case(T, H, D, 1900 + s, 0.05, qkv_bf16=True) for s, T in enumerate(lengths)]
     if skip == "longer_than_max_chunks":
         cu, core, states = run_varlen(cases, H, D, C, scale, max_chunks=1, report=1)
-        skipped = [2]
+        skipped = [lead + 2]
     else:
-        cu, core, states = run_varlen(cases, H, D, C, scale, total_chunks=len(lengths) - 1,
-                                      report=1)
-        skipped = [4]
+        cu, core, states = run_varlen(cases, H, D, C, scale, total_chunks=5 - 1, report=1)
+        skipped = [lead + 4]
     for s, T in enumerate(lengths):
-        if s in skipped:
+        if s in skipped or T == 0:
             np.testing.assert_array_equal(states[s], cases[s]["S0"])
             assert np.all(core[cu[s]:cu[s + 1]] == SENTINEL)
             continue
@@ -267,3 +284,41 @@ def test_varlen_wide_walk_workgroups_bitwise(nseq, L):
                                                c["S0"], scale, threads=THREADS)
     assert relerr(core[cu[-2]:cu[-1]], ref_core) < TOL
     assert relerr(states[-1], ref_S) < TOL
+
+
+def test_varlen_many_multi_chunk_prompts_over_many_segments():
+    # 1200 prompts of 0..400 tokens and one of 3000 (several chunks each,
+    # empty ones between them) over 16 cache-sized segments, so that many
+    # prompts straddle a segment boundary and the call's sequence tables span
+    # two blocks of the plan kernel: every prompt that straddles a boundary,
+    # and a sample of the rest, bitwise equal to kda_prefill alone
+    H, D, C = 4, 128, 64
+    rng = np.random.default_rng(1951)
+    lengths = [int(x) for x in rng.integers(0, 401, size=1200)]
+    lengths[700] = 3000
+    scale = D ** -0.5
+    cases = [core_case(T, H, D, 30000 + s, 0.05) for s, T in enumerate(lengths)]
+    cu, core, states = run_varlen(cases, H, D, C, scale)
+    nch = [-(-T // C) for T in lengths]
+    c0 = np.concatenate([[0], np.cumsum(nch)])
+    seg = kda.kda_prefill_segment_chunks(int(c0[-1]) * C, H, D, C)
+    assert int(c0[-1]) > 15 * seg
+    straddle = [s for s in range(len(lengths))
+                if nch[s] > 1 and (c0[s] // seg) != ((c0[s + 1] - 1) // seg)]
+    assert len(straddle) >= 10
+    for s in sorted(set(straddle) | set(range(0, len(lengths), 97)) | {700, len(lengths) - 1}):
+        c, T = cases[s], lengths[s]
+        if T == 0:
+            np.testing.assert_array_equal(states[s], c["S0"])
+            assert np.all(core[cu[s]:cu[s + 1]] == SENTINEL)
+            continue
+        one_core, one_S = gpu_prefill(c, T, nch[s] * C, C, scale, fill=0.0)
+        np.testing.assert_array_equal(core[cu[s]:cu[s + 1]], one_core[:T], err_msg=f"seq {s}")
+        np.testing.assert_array_equal(states[s], one_S, err_msg=f"seq {s} state")
+    for s in (straddle[0], 700):
+        c = cases[s]
+        ref_core, ref_S, _ = oracle.kda_recurrence(c["q"], c["k"], c["v"], c["gate"], c["beta"],
+                                                   c["S0"], scale, threads=THREADS)
+        assert relerr(core[cu[s]:cu[s + 1]], ref_core) < TOL
+        assert relerr(states[s], ref_S) < TOL
+    assert np.all(core[cu[-1]:] == SENTINEL)

@@ -473,27 +473,32 @@ def bench_block(kda, dev, reps=10):
 def bench_prefill_varlen(kda, dev, reps=50):
     """The prefill workload's 4096 tokens (32 heads x 128, chunk 64, fp32
     states ~ N(0, 0.05)) as many prompts in one kda_prefill_varlen call:
-    8 x 512 and 64 x 64 tokens, each prompt from its own state."""
+    8 x 512 and 64 x 64 tokens, each prompt from its own state; and 16 times
+    the workload's tokens (its rows repeated) as 256 prompts of 256."""
     out = {}
-    for n_seq in (8, 64):
-        L = T // n_seq
-        raw = workloads.core_raw(T, H, D, workloads.SEED_INPUT + 6, qkv_bf16=True)
-        a_log, dt = torch.from_numpy(raw["a_log"]).to(dev), torch.from_numpy(raw["dt_bias"]).to(dev)
-        gate = torch.empty(T, H, D, device=dev)
-        beta = torch.empty(T, H, device=dev)
-        kda.kda_gate(workloads.to_bf16(raw["g_raw"]).to(dev), a_log, dt, gate, T=T, heads=H,
-                     head_dim=D, b_raw=workloads.to_bf16(raw["b_raw"]).to(dev), beta=beta)
-        q, k, v = (torch.from_numpy(raw[n]).to(dev) for n in ("q", "k", "v"))
-        st = torch.from_numpy(workloads.state(H, D, 0.05, workloads.SEED_STATE + 6, B=n_seq)).to(dev)
+    raw = workloads.core_raw(T, H, D, workloads.SEED_INPUT + 6, qkv_bf16=True)
+    a_log, dt = torch.from_numpy(raw["a_log"]).to(dev), torch.from_numpy(raw["dt_bias"]).to(dev)
+    gate1 = torch.empty(T, H, D, device=dev)
+    beta1 = torch.empty(T, H, device=dev)
+    kda.kda_gate(workloads.to_bf16(raw["g_raw"]).to(dev), a_log, dt, gate1, T=T, heads=H,
+                 head_dim=D, b_raw=workloads.to_bf16(raw["b_raw"]).to(dev), beta=beta1)
+    q1, k1, v1 = (torch.from_numpy(raw[n]).to(dev) for n in ("q", "k", "v"))
+    for n_seq, rep_rows in ((8, 1), (64, 1), (256, 16)):
+        rows = T * rep_rows
+        L = rows // n_seq
+        q, k, v, gate = (x.repeat(rep_rows, 1, 1) for x in (q1, k1, v1, gate1))
+        beta = beta1.repeat(rep_rows, 1)
+        gen = torch.Generator(device=dev).manual_seed(workloads.SEED_STATE + 6)
+        st = torch.randn(n_seq, H, D, D, device=dev, generator=gen) * 0.05
         tab = kda.ptr_table(st)
-        cu = torch.arange(0, T + 1, L, dtype=torch.int32, device=dev)
+        cu = torch.arange(0, rows + 1, L, dtype=torch.int32, device=dev)
         mx, tot = kda.varlen_chunks([L] * n_seq, C)
         ws = torch.empty(kda.kda_prefill_varlen_workspace_bytes(n_seq, tot, H, D, C), dtype=torch.uint8,
                          device=dev)
-        core = torch.empty(T, H, D, device=dev)
+        core = torch.empty(rows, H, D, device=dev)
 
         def call():
-            kda.kda_prefill_varlen(q, k, v, gate, beta, tab, core, cu, ws, B=n_seq, rows=T,
+            kda.kda_prefill_varlen(q, k, v, gate, beta, tab, core, cu, ws, B=n_seq, rows=rows,
                                    max_chunks=mx, total_chunks=tot, heads=H, head_dim=D,
                                    chunk=C, scale=D ** -0.5)
 
@@ -507,9 +512,11 @@ def bench_prefill_varlen(kda, dev, reps=50):
             b.record()
         torch.cuda.synchronize()
         t = float(np.median([a.elapsed_time(b) for a, b in es])) * 1e-3
-        out[f"{n_seq}x{L}"] = dict(ms=t * 1e3, tokens_per_s=T / t)
-    out["config"] = (f"{T} tokens as equal prompts, heads={H}, head_dim={D}, chunk={C}, "
-                     "one kda_prefill_varlen call, per-prompt fp32 states")
+        out[f"{n_seq}x{L}"] = dict(ms=t * 1e3, tokens_per_s=rows / t)
+        del q, k, v, gate, beta, st, ws, core
+    out["config"] = (f"{T} tokens as equal prompts (and {16 * T} as 256 x 256), heads={H}, "
+                     f"head_dim={D}, chunk={C}, one kda_prefill_varlen call, per-prompt fp32 "
+                     "states ~ N(0, 0.05)")
     return out
 
 

@@ -322,3 +322,57 @@ def test_varlen_many_multi_chunk_prompts_over_many_segments():
         assert relerr(core[cu[s]:cu[s + 1]], ref_core) < TOL
         assert relerr(states[s], ref_S) < TOL
     assert np.all(core[cu[-1]:] == SENTINEL)
+
+
+def test_varlen_most_sequences_the_call_takes():
+    # 65535 prompts (the most one call takes) of 0..3 tokens at 2 heads x 16,
+    # chunk 16: the plan kernel walks 64 blocks of prompts, and each of the
+    # four cache-sized segments launches ~12k chunks' prepare workgroups and
+    # as many walks.  Empty prompts keep their state; a sample of the rest is
+    # bitwise kda_prefill alone, and two match the oracle
+    H, D, C, B = 2, 16, 16, 65535
+    rng = np.random.default_rng(1952)
+    lengths = rng.integers(0, 4, size=B)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    rows = int(cu[-1])
+
+    def unit(x):
+        return (x / np.linalg.norm(x, axis=-1, keepdims=True)).astype(np.float32)
+    q = unit(rng.standard_normal((rows, H, D)))
+    k = unit(rng.standard_normal((rows, H, D)))
+    v = rng.standard_normal((rows, H, D)).astype(np.float32)
+    g = (-np.exp(rng.uniform(-1, 0.5, (1, H, 1))) *
+         np.log1p(np.exp(rng.standard_normal((rows, H, D))))).astype(np.float32)
+    b = (1 / (1 + np.exp(-rng.standard_normal((rows, H))))).astype(np.float32)
+    S0 = (rng.standard_normal((B, H, D, D)) * 0.05).astype(np.float32)
+    states = cuda(S0)
+    core = torch.full((rows, H, D), SENTINEL, dtype=torch.float32, device="cuda")
+    mx, tot = kda.varlen_chunks([int(x) for x in lengths], C)
+    ws = torch.empty(kda.kda_prefill_varlen_workspace_bytes(B, tot, H, D, C), dtype=torch.uint8,
+                     device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("varlen 65535 prompts", H, D, C, tot)
+    kda.kda_prefill_varlen(cuda(q), cuda(k), cuda(v), cuda(g), cuda(b), kda.ptr_table(states),
+                           core, torch.from_numpy(cu).cuda(), ws, B=B, rows=rows, max_chunks=mx,
+                           total_chunks=tot, heads=H, head_dim=D, chunk=C, scale=D ** -0.5,
+                           status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    got_S, got_core = states.cpu().numpy(), core.cpu().numpy()
+    empty = lengths == 0
+    np.testing.assert_array_equal(got_S[empty], S0[empty])
+    for s in sorted(set(range(0, B, 1311)) | {B - 1}):
+        T = int(lengths[s])
+        if T == 0:
+            continue
+        sl = slice(cu[s], cu[s + 1])
+        case = dict(q=q[sl], k=k[sl], v=v[sl], gate=g[sl], beta=b[sl], S0=S0[s])
+        one_core, one_S = gpu_prefill(case, T, C, C, D ** -0.5)
+        np.testing.assert_array_equal(got_core[sl], one_core[:T], err_msg=f"seq {s}")
+        np.testing.assert_array_equal(got_S[s], one_S, err_msg=f"seq {s} state")
+    for s in [i for i in (7, 32768, B - 2) if lengths[i] > 0]:
+        sl = slice(cu[s], cu[s + 1])
+        ref_core, ref_S, _ = oracle.kda_recurrence(q[sl], k[sl], v[sl], g[sl], b[sl], S0[s],
+                                                   D ** -0.5)
+        assert relerr(got_core[sl], ref_core) < TOL
+        assert relerr(got_S[s], ref_S) < TOL

@@ -31,7 +31,7 @@ constexpr int kConvThreads = 256;
 // 88 us for 4 rows, 98 us for 16 (160 VGPRs, three waves) and 126 us for 32
 // (two waves)
 
-template <int D>
+template <int D, int RPT>
 __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, const uint16_t *__restrict__ w,
     uint16_t *const *__restrict__ conv_state, uint16_t *const *__restrict__ conv_snap,
@@ -47,8 +47,8 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
     const int c0 = active ? grp * 8 : 0;
     const int tile = blockIdx.y;
     const int seq = blockIdx.z;
-    const int t0 = tile * kConvRowsPerTile;
-    const int t1 = min(rows, t0 + kConvRowsPerTile);
+    const int t0 = tile * RPT;
+    const int t1 = min(rows, t0 + RPT);
     const int64_t row0 = (int64_t)seq * rows;   // first row of this sequence
     const uint16_t *__restrict__ st = conv_state ? conv_state[seq] : nullptr;
 
@@ -75,12 +75,12 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
 
     // the tile's rows are all loaded up front (many 16-byte loads in flight
     // per wave), then computed in order
-    uint4 rowv[kConvRowsPerTile];
+    uint4 rowv[RPT];
 #pragma unroll
-    for (int i = 0; i < kConvRowsPerTile; ++i)
+    for (int i = 0; i < RPT; ++i)
         if (t0 + i < t1) rowv[i] = *reinterpret_cast<const uint4 *>(x + (row0 + t0 + i) * ldx + c0);
 #pragma unroll
-    for (int i = 0; i < kConvRowsPerTile; ++i) {
+    for (int i = 0; i < RPT; ++i) {
         const int t = t0 + i;
         if (t >= t1) break;
 #pragma unroll
@@ -107,7 +107,9 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_l2_kernel(
         }
     }
 
-    // new conv state = the window after the sequence's last row
+    // new conv state = the window after the sequence's last row (launched
+    // with write_state only when RPT >= KC, so that tile 0 is the only one
+    // that reads the old state)
     if (write_state && tile == 0 && st != nullptr && active) {
         uint16_t *dst = conv_state[seq];
         if (ntiles == 1) {
@@ -187,17 +189,26 @@ hipError_t launch_conv_silu_l2(const uint16_t *x, int64_t ldx, const uint16_t *w
                                hipStream_t stream, bool write_state)
 {
     const int conv_dim = 3 * heads * head_dim;
-    const int ntiles = (rows + kConvRowsPerTile - 1) / kConvRowsPerTile;
+    // A few rows that leave the conv state alone (a verify): one row per
+    // tile, so the rows run side by side instead of one after another in
+    // each thread (each tile reads its own window; the per-row arithmetic is
+    // the same, so are the bits).  Otherwise tiles of kConvRowsPerTile rows.
+    const bool by_row = !write_state && rows <= kConvRowsPerTile;
+    const int rpt = by_row ? 1 : kConvRowsPerTile;
+    const int ntiles = (rows + rpt - 1) / rpt;
     const dim3 grid((conv_dim / 8 + kConvThreads - 1) / kConvThreads, ntiles, n_seq);
+#define KDA_CONV_LAUNCH(DH, RPT)                                                              \
+    hipLaunchKernelGGL((conv_silu_l2_kernel<DH, RPT>), grid, dim3(kConvThreads), 0, stream, x, \
+                       ldx, w, conv_state, conv_snap, rows, heads, ntiles, eps_l2, y, ldy, q32, \
+                       k32, v32, write_state)
     if (head_dim == 128) {
-        hipLaunchKernelGGL(conv_silu_l2_kernel<128>, grid, dim3(kConvThreads), 0, stream, x, ldx,
-                           w, conv_state, conv_snap, rows, heads, ntiles, eps_l2, y, ldy, q32,
-                           k32, v32, write_state);
+        if (by_row) KDA_CONV_LAUNCH(128, 1);
+        else KDA_CONV_LAUNCH(128, kConvRowsPerTile);
     } else {
-        hipLaunchKernelGGL(conv_silu_l2_kernel<16>, grid, dim3(kConvThreads), 0, stream, x, ldx,
-                           w, conv_state, conv_snap, rows, heads, ntiles, eps_l2, y, ldy, q32,
-                           k32, v32, write_state);
+        if (by_row) KDA_CONV_LAUNCH(16, 1);
+        else KDA_CONV_LAUNCH(16, kConvRowsPerTile);
     }
+#undef KDA_CONV_LAUNCH
     return hipGetLastError();
 }
 

@@ -55,8 +55,8 @@ PEAK_HBM = 8.0e12             # MI355X HBM3E peak, B/s
 # HBM bytes per launch (FETCH_SIZE and WRITE_SIZE scaled by the copy
 # calibration) from rocprofv3 counter runs of the kernels as they are built
 # now; a kernel is left out once it changes after its counters were taken.
-TRAFFIC_BYTES = {"kda_chunk_prep": (66884.9 * 2.0 + 147968.0 * 1.0) * 1024,
-                 "kda_chunk_fwd": (75099.5 * 2.0 + 34816.0 * 1.0) * 1024}
+TRAFFIC_BYTES = {"kda_chunk_prep": (66872.2 * 2.0 + 143872.0 * 1.0) * 1024,
+                 "kda_chunk_fwd": (73053.5 * 2.0 + 34816.0 * 1.0) * 1024}
 # Counted HBM traffic of one decode step at 256 sequences (FETCH_SIZE x 2 +
 # WRITE_SIZE, KiB per dispatch) for the recurrent kernel as built now.
 DECODE_TRAFFIC_BYTES = (267441.6 * 2.0 + 528933.7 * 1.0) * 1024
@@ -122,8 +122,11 @@ def prep_flops_per_token_head(D, C):
 
 
 def block_floats(D, C):
-    # per (chunk, head) operand block: W, U', Qg, KdT, P, Ec
-    return 4 * C * D + C * C + D
+    # per (chunk, head) operand block as moved: W, U', Qg, KdT, Ec and the
+    # 16 x 32 pair fragments of P that reach the diagonal (a fragment wholly
+    # above it, 32 kb > 16 w + 15, is neither written nor read)
+    p_frags = sum(w // 2 + 1 for w in range(C // 16))
+    return 4 * C * D + p_frags * 16 * 32 + D
 
 
 def fwd_impl_bytes(T, H, D, C):

@@ -1045,7 +1045,8 @@ __device__ __forceinline__ void prep_split_unit(const QkvSrc<BF> &src, const flo
     }
 
     // M = diag(b) A, strictly lower, to LDS; P as pair fragments (blocks above
-    // the diagonal as zeros)
+    // the diagonal as zeros; a 32-column fragment wholly above the diagonal,
+    // 32 kb > 16 w + 15, is neither stored nor read)
     float4 pv[NW];
 #pragma unroll
     for (int bj = 0; bj < NW; ++bj) {
@@ -1062,7 +1063,8 @@ __device__ __forceinline__ void prep_split_unit(const QkvSrc<BF> &src, const flo
             }
             pv[bj] = make_float4(pe[0], pe[1], pe[2], pe[3]);
         }
-        if (bj % 2 == 1) store_pair(blk + B::kP + B::pfrag(w, bj / 2, KC), lane, pv[bj - 1], pv[bj]);
+        if (bj % 2 == 1 && bj - 1 <= w)
+            store_pair(blk + B::kP + B::pfrag(w, bj / 2, KC), lane, pv[bj - 1], pv[bj]);
     }
     __syncthreads();   // s_M complete; s_x free
     // V now, for the U' pass (its latency hidden behind the inversion and W)
@@ -1655,7 +1657,9 @@ __device__ __forceinline__ void walk_split(const float *__restrict__ ws, float *
 #pragma unroll
         for (int kb = 0; kb < KD; ++kb) ldp(block(0) + B::kQ + B::pfrag(w, kb, KD), X.Qh[kb], X.Ql[kb]);
 #pragma unroll
-        for (int kb = 0; kb < KC; ++kb) ldp(block(0) + B::kP + B::pfrag(w, kb, KC), X.Ph[kb], X.Pl[kb]);
+        for (int kb = 0; kb < KC; ++kb)
+            if (2 * kb <= w)   // fragments wholly above the diagonal are zero (not stored)
+                ldp(block(0) + B::kP + B::pfrag(w, kb, KC), X.Ph[kb], X.Pl[kb]);
         __syncthreads();   // B0
         __builtin_amdgcn_sched_barrier(0);
 
@@ -1697,12 +1701,14 @@ __device__ __forceinline__ void walk_split(const float *__restrict__ ws, float *
                 floatx4 Ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < KC; ++kb) {
-                    if constexpr (PF) {
-                        if (j == 0) ldp(bn + B::kP + B::pfrag(w, kb, KC), nxt.Ph[kb], nxt.Pl[kb]);
+                    if (2 * kb <= w) {
+                        if constexpr (PF) {
+                            if (j == 0) ldp(bn + B::kP + B::pfrag(w, kb, KC), nxt.Ph[kb], nxt.Pl[kb]);
+                        }
+                        Oa[j] = mfma_bf16(cur.Ph[kb], uh[kb], Oa[j]);
+                        Ob = mfma_bf16(cur.Ph[kb], ul[kb], Ob);
+                        Ob = mfma_bf16(cur.Pl[kb], uh[kb], Ob);
                     }
-                    Oa[j] = mfma_bf16(cur.Ph[kb], uh[kb], Oa[j]);
-                    Ob = mfma_bf16(cur.Ph[kb], ul[kb], Ob);
-                    Ob = mfma_bf16(cur.Pl[kb], uh[kb], Ob);
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
@@ -1817,7 +1823,9 @@ __device__ __forceinline__ void walk1_split(const float *__restrict__ blk, float
         ldp(blk + B::kQ + B::pfrag(w, kb, KD), Qh[kb], Ql[kb]);
     }
 #pragma unroll
-    for (int kb = 0; kb < KC; ++kb) ldp(blk + B::kP + B::pfrag(w, kb, KC), Ph[kb], Pl[kb]);
+    for (int kb = 0; kb < KC; ++kb)
+        if (2 * kb <= w)   // fragments wholly above the diagonal are zero (not stored)
+            ldp(blk + B::kP + B::pfrag(w, kb, KC), Ph[kb], Pl[kb]);
 #pragma unroll
     for (int o = 0; o < OWN; ++o) {
 #pragma unroll
@@ -1878,9 +1886,11 @@ __device__ __forceinline__ void walk1_split(const float *__restrict__ blk, float
         floatx4 Ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KC; ++kb) {
-            Oa = mfma_bf16(Ph[kb], uh[kb], Oa);
-            Ob = mfma_bf16(Ph[kb], ul[kb], Ob);
-            Ob = mfma_bf16(Pl[kb], uh[kb], Ob);
+            if (2 * kb <= w) {
+                Oa = mfma_bf16(Ph[kb], uh[kb], Oa);
+                Ob = mfma_bf16(Ph[kb], ul[kb], Ob);
+                Ob = mfma_bf16(Pl[kb], uh[kb], Ob);
+            }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -341,6 +341,33 @@ def bench_decode_k(kda, dev, n_calls=32, n_sets=4):
     torch.cuda.synchronize()
     t_ver = float(np.median([a.elapsed_time(b) for a, b, _ in evw])) * 1e-3
     t_fold = float(np.median([b.elapsed_time(c) for _, b, c in evw])) * 1e-3
+
+    # the table form: the verify also writes each row's u, the fold applies
+    # the K-1 accepted rows in one pass from them
+    wy = torch.empty(B, H, K, D, device=dev)
+    wy_tab = kda.ptr_table(wy)
+
+    def woa_wy(i, e=None):
+        st, tab, _, _ = sets[i % n_sets]
+        if e:
+            e[0].record()
+        kda.kda_verify_wy_k(y, gate, beta, tab, wy_tab, core, B=B, K=K, heads=H, head_dim=D,
+                            scale=D ** -0.5)
+        if e:
+            e[1].record()
+        kda.kda_fold_wy(y, gate, tab, wy_tab, na, B=B, K=K, heads=H, head_dim=D)
+        if e:
+            e[2].record()
+
+    for i in range(n_sets):
+        woa_wy(i)
+    evt = [(ev(), ev(), ev()) for _ in range(n_calls)]
+    torch.cuda.synchronize()
+    for i in range(n_calls):
+        woa_wy(i, evt[i])
+    torch.cuda.synchronize()
+    t_ver_wy = float(np.median([a.elapsed_time(b) for a, b, _ in evt])) * 1e-3
+    t_fold_wy = float(np.median([b.elapsed_time(c) for _, b, c in evt])) * 1e-3
     st1 = B * H * D * D * 4
     ver_b = st1 + B * K * (cd * 2 + H * D * 4 + H * 4 + H * D * 4)
     fold_b = 2 * st1 + B * (K - 1) * (2 * H * D * 2 + H * D * 4 + H * 4)
@@ -357,7 +384,10 @@ def bench_decode_k(kda, dev, n_calls=32, n_sets=4):
                                      fold_GBps=fold_b / t_fold / 1e9,
                                      state_bytes=3 * st1, decode_k_state_bytes=state_b,
                                      speedup_vs_snapshots=t_dk / (t_ver + t_fold),
-                                     n_accept=K - 1))
+                                     n_accept=K - 1,
+                                     table_form=dict(verify_ms=t_ver_wy * 1e3,
+                                                     fold_ms=t_fold_wy * 1e3,
+                                                     fold_GBps=(2 * st1 + B * (K - 1) * (H * D * 2 + H * D * 4 + H * D * 4)) / t_fold_wy / 1e9)))
 
 
 def bench_stages(kda, dev, reps=10):

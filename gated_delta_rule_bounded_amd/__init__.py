@@ -24,7 +24,8 @@ __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_noalloc", "kd
            "kda_prefill_varlen_workspace_bytes",
            "kda_block_prefill", "block_buffers", "BLOCK_WEIGHT_NAMES",
            "dense_gemv_bf16_batchm", "kda_prefill_varlen", "varlen_chunks",
-           "kda_verify_k", "kda_fold_accepted", "kda_prefill_split",
+           "kda_verify_k", "kda_fold_accepted", "kda_verify_wy_k", "kda_fold_wy",
+           "kda_prefill_split",
            "kda_block_verify_k", "kda_block_fold_accepted", "kda_prefill_bf16", "kda_block_decode", "kda_block_decode_k",
            "block_decode_buffers",
            "ptr_table", "KdaError",
@@ -536,6 +537,36 @@ def kda_fold_accepted(qkv, gate, beta, state, n_accept, *, B, K, heads, head_dim
     _check(_lib.lib.kda_fold_accepted(
         _ptr(qkv, torch.bfloat16, "qkv"), _rowstride(qkv, "qkv"), _ptr(gate, f, "gate"),
         _ptr(beta, f, "beta"), _ptr(state, torch.int64, "state"),
+        _ptr(n_accept, torch.int32, "n_accept"), B, K, heads, head_dim, st, _stream()))
+
+
+def kda_verify_wy_k(qkv, gate, beta, state, wy, core, *, B, K, heads, head_dim, scale):
+    """kda_verify_k that also writes each row's u to the WY tables ``wy`` (a
+    pointer table of B entries, each fp32 [heads, K, head_dim])."""
+    f = torch.float32
+    _decode_sizes(qkv, gate, beta, state, core, B, K, heads, head_dim)
+    _table(wy, "wy", B)
+    _check(_lib.lib.kda_verify_wy_k(
+        _ptr(qkv, torch.bfloat16, "qkv"), _rowstride(qkv, "qkv"), _ptr(gate, f, "gate"),
+        _ptr(beta, f, "beta"), _ptr(state, torch.int64, "state"), _ptr(wy, torch.int64, "wy"),
+        _ptr(core, f, "core"), B, K, heads, head_dim, float(scale), _stream()))
+
+
+def kda_fold_wy(qkv, gate, state, wy, n_accept, *, B, K, heads, head_dim, status=None):
+    """Fold the first n_accept[b] verified rows into each state in one pass
+    from the WY tables kda_verify_wy_k wrote (equal to kda_fold_accepted up
+    to rounding).  ``status`` as kda_fold_accepted."""
+    f = torch.float32
+    n, qw = B * K, heads * head_dim
+    _rows(qkv, "qkv", torch.bfloat16, n, 3 * qw)
+    _dense(gate, "gate", f, n * qw)
+    _table(state, "state", B)
+    _table(wy, "wy", B)
+    _dense(n_accept, "n_accept", torch.int32, B)
+    st = _status(status)
+    _check(_lib.lib.kda_fold_wy(
+        _ptr(qkv, torch.bfloat16, "qkv"), _rowstride(qkv, "qkv"), _ptr(gate, f, "gate"),
+        _ptr(state, torch.int64, "state"), _ptr(wy, torch.int64, "wy"),
         _ptr(n_accept, torch.int32, "n_accept"), B, K, heads, head_dim, st, _stream()))
 
 

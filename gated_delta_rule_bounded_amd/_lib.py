@@ -16,7 +16,8 @@ SYMBOLS = ("kda_last_error", "conv_silu_l2", "kda_gate", "kda_prefill_workspace_
            "kda_block_prefill", "dense_gemv_bf16_batchm", "kda_block_decode_k",
            "kda_block_decode", "kda_prefill_varlen", "kda_verify_k", "kda_fold_accepted",
            "kda_prefill_split", "kda_block_verify_k", "kda_block_fold_accepted",
-           "kda_prefill_bf16", "kda_prefill_noalloc", "kda_prefill_varlen_workspace_bytes")
+           "kda_prefill_bf16", "kda_prefill_noalloc", "kda_prefill_varlen_workspace_bytes",
+           "kda_verify_wy_k", "kda_fold_wy")
 
 
 class BlockWeights(ctypes.Structure):
@@ -96,6 +97,10 @@ def _load():
     lib.kda_verify_k.argtypes = [P, i64, P, P, P, P, i32, i32, i32, i32, f32, P]
     lib.kda_fold_accepted.restype = ctypes.c_int
     lib.kda_fold_accepted.argtypes = [P, i64, P, P, P, P, i32, i32, i32, i32, P, P]
+    lib.kda_verify_wy_k.restype = ctypes.c_int
+    lib.kda_verify_wy_k.argtypes = [P, i64, P, P, P, P, P, i32, i32, i32, i32, f32, P]
+    lib.kda_fold_wy.restype = ctypes.c_int
+    lib.kda_fold_wy.argtypes = [P, i64, P, P, P, P, i32, i32, i32, i32, P, P]
     lib.kda_prefill_varlen.restype = ctypes.c_int
     lib.kda_prefill_varlen.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
                                        f32, P, ctypes.c_size_t, P, P]

@@ -460,6 +460,52 @@ int kda_verify_k(const uint16_t *qkv, int64_t ldqkv, const float *gate, const fl
                       "kda_verify_k launch");
 }
 
+int kda_verify_wy_k(const uint16_t *qkv, int64_t ldqkv, const float *gate, const float *beta,
+                    float *const *state, float *const *wy, float *core, int32_t B, int32_t K,
+                    int32_t heads, int32_t head_dim, float scale, hipStream_t stream)
+{
+    if (B < 0 || K < 0 || heads <= 0 || B > kMaxGridYZ)
+        return fail(KDA_ERR_SHAPE, "kda_verify_wy_k: B=%d K=%d heads=%d", B, K, heads);
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_verify_wy_k: head_dim=%d", head_dim);
+    if (B == 0 || K == 0) return ok();
+    if ((int64_t)B * K > (int64_t)1 << 30)
+        return fail(KDA_ERR_SHAPE, "kda_verify_wy_k: B*K too large");
+    if (!wy) return fail(KDA_ERR_NULL, "kda_verify_wy_k: null pointer argument");
+    if (int rc = check_decode("kda_verify_wy_k", qkv, ldqkv, gate, beta, state, core, B * K,
+                              heads, head_dim))
+        return rc;
+    if ((const void *)wy == (const void *)state)
+        return fail(KDA_ERR_ALIAS, "kda_verify_wy_k: table of u rows is the state table");
+    return hip_status(kda::launch_kda_verify_wy(qkv, ldqkv, gate, beta, state, wy, core, B, K,
+                                                heads, head_dim, scale, stream),
+                      "kda_verify_wy_k launch");
+}
+
+int kda_fold_wy(const uint16_t *qkv, int64_t ldqkv, const float *gate, float *const *state,
+                float *const *wy, const int32_t *n_accept, int32_t B, int32_t K, int32_t heads,
+                int32_t head_dim, int32_t *status, hipStream_t stream)
+{
+    if (B < 0 || K < 0 || heads <= 0 || B > kMaxGridYZ)
+        return fail(KDA_ERR_SHAPE, "kda_fold_wy: B=%d K=%d heads=%d", B, K, heads);
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_fold_wy: head_dim=%d", head_dim);
+    if (B == 0 || K == 0) return ok();
+    if ((int64_t)B * K > (int64_t)1 << 30)
+        return fail(KDA_ERR_SHAPE, "kda_fold_wy: B*K too large");
+    if (!qkv || !gate || !state || !wy || !n_accept)
+        return fail(KDA_ERR_NULL, "kda_fold_wy: null pointer argument");
+    if (ldqkv < 3LL * heads * head_dim)
+        return fail(KDA_ERR_SHAPE, "kda_fold_wy: ldqkv=%lld < 3*heads*head_dim", (long long)ldqkv);
+    if (status && !aligned4(status))
+        return fail(KDA_ERR_SHAPE, "kda_fold_wy: status must be 4-byte aligned");
+    if ((const void *)wy == (const void *)state)
+        return fail(KDA_ERR_ALIAS, "kda_fold_wy: table of u rows is the state table");
+    return hip_status(kda::launch_kda_fold_wy(qkv, ldqkv, gate, state, wy, n_accept, B, K, heads,
+                                              head_dim, status, stream),
+                      "kda_fold_wy launch");
+}
+
 int kda_fold_accepted(const uint16_t *qkv, int64_t ldqkv, const float *gate, const float *beta,
                       float *const *state, const int32_t *n_accept, int32_t B, int32_t K,
                       int32_t heads, int32_t head_dim, int32_t *status, hipStream_t stream)

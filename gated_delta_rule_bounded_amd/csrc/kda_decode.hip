@@ -24,6 +24,8 @@
 // (write_state false), and a fold run applies the first n_accept[b] rows to
 // the state and writes no output.  The state a fold leaves is therefore
 // bitwise the snapshot a K-row decode would have written after that row.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 #include "kda_rows.hpp"
@@ -83,12 +85,13 @@ struct __align__(16) RecLds {
 // u = beta (v - S'^T k) and o = scale (S'^T q + u (k . q)), and adds k u^T to
 // S.  Thread row 0 owns whole columns and stores o: to core_row (the row's
 // first value column of this slice) and o_lds (the same columns), each when
-// given.  Passes one barrier (the key-axis sums go through LDS); the caller
-// passes another before L is rewritten.
+// given; and u to u_row (same columns) when given.  Passes one barrier (the
+// key-axis sums go through LDS); the caller passes another before L is
+// rewritten.
 template <int D, int NS, int RGT>
 __device__ __forceinline__ void rec_row(float4 (&S)[RGT][D / 16], RecLds<D, NS, RGT> &L, float bt,
                                         float scale, int c0, int tid, float *core_row,
-                                        float *o_lds)
+                                        float *o_lds, float *u_row = nullptr)
 {
     using Cfg = RecCfg<D, NS, RGT>;
     constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT, NP = Cfg::kPairs;
@@ -159,6 +162,7 @@ __device__ __forceinline__ void rec_row(float4 (&S)[RGT][D / 16], RecLds<D, NS, 
         if (core_row != nullptr) reinterpret_cast<float4 *>(core_row)[cg] = o;
         if (o_lds != nullptr) reinterpret_cast<float4 *>(o_lds)[cg] = o;
     }
+    if (u_row != nullptr && tr == 0) reinterpret_cast<float4 *>(u_row)[cg] = u;
 #pragma unroll
     for (int j = 0; j < RGT; ++j)
 #pragma unroll
@@ -171,7 +175,8 @@ __global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_
     const uint16_t *__restrict__ qkv, int64_t ldqkv, const float *__restrict__ gate,
     const float *__restrict__ beta, float *const *__restrict__ state,
     float *const *__restrict__ snap, float *__restrict__ core, int K, int H, float scale,
-    bool write_state, const int32_t *__restrict__ n_accept, int32_t *__restrict__ status)
+    bool write_state, const int32_t *__restrict__ n_accept, int32_t *__restrict__ status,
+    float *const *__restrict__ wy)
 {
     using Cfg = RecCfg<D, NS, RGT>;
     constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT;
@@ -218,7 +223,8 @@ __global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_
         __syncthreads();
 
         rec_row<D, NS, RGT>(S, L, bt, scale, c0, tid,
-                            core != nullptr ? core + (row * H + h) * D + c0 : nullptr, nullptr);
+                            core != nullptr ? core + (row * H + h) * D + c0 : nullptr, nullptr,
+                            wy != nullptr ? wy[b] + ((size_t)h * K + t) * D + c0 : nullptr);
 
         if (snap != nullptr && t + 1 < K) {
             float *__restrict__ Sn = snap[(size_t)b * (K - 1) + t] + (size_t)h * D * D + c0;
@@ -350,11 +356,11 @@ static hipError_t recurrent_ns(const uint16_t *qkv, int64_t ldqkv, const float *
                                const float *beta, float *const *state, float *const *snap,
                                float *core, int B, int K, int heads, float scale,
                                bool write_state, const int32_t *n_accept, int32_t *status,
-                               hipStream_t stream)
+                               hipStream_t stream, float *const *wy = nullptr)
 {
     hipLaunchKernelGGL((kda_recurrent_kernel<D, NS, RGT>), dim3(heads * NS, B),
                        dim3(RecCfg<D, NS, RGT>::kThreads), 0, stream, qkv, ldqkv, gate, beta,
-                       state, snap, core, K, heads, scale, write_state, n_accept, status);
+                       state, snap, core, K, heads, scale, write_state, n_accept, status, wy);
     return hipGetLastError();
 }
 
@@ -365,16 +371,17 @@ template <int D>
 static hipError_t recurrent_t(const uint16_t *qkv, int64_t ldqkv, const float *gate,
                               const float *beta, float *const *state, float *const *snap,
                               float *core, int B, int K, int heads, float scale, bool write_state,
-                              const int32_t *n_accept, int32_t *status, hipStream_t stream)
+                              const int32_t *n_accept, int32_t *status, hipStream_t stream,
+                              float *const *wy = nullptr)
 {
     const int64_t pairs = (int64_t)B * heads;
     if constexpr (D >= 128) {
         if (pairs <= 128)
             return recurrent_ns<D, 4>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
-                                      write_state, n_accept, status, stream);
+                                      write_state, n_accept, status, stream, wy);
         if (pairs <= 256)
             return recurrent_ns<D, 2>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
-                                      write_state, n_accept, status, stream);
+                                      write_state, n_accept, status, stream, wy);
     }
     // whole heads: the write-on-accept verify (state read only) and fold run
     // two row groups per thread (256 threads, more state in flight per CU);
@@ -382,9 +389,9 @@ static hipError_t recurrent_t(const uint16_t *qkv, int64_t ldqkv, const float *g
     if constexpr (D >= 128)
         if (!write_state || n_accept)
             return recurrent_ns<D, 1, 2>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads,
-                                         scale, write_state, n_accept, status, stream);
+                                         scale, write_state, n_accept, status, stream, wy);
     return recurrent_ns<D, 1>(qkv, ldqkv, gate, beta, state, snap, core, B, K, heads, scale,
-                              write_state, n_accept, status, stream);
+                              write_state, n_accept, status, stream, wy);
 }
 
 hipError_t launch_kda_recurrent(const uint16_t *qkv, int64_t ldqkv, const float *gate,
@@ -408,6 +415,130 @@ hipError_t launch_kda_verify(const uint16_t *qkv, int64_t ldqkv, const float *ga
                                   scale, false, nullptr, nullptr, stream)
                : recurrent_t<16>(qkv, ldqkv, gate, beta, state, nullptr, core, B, K, heads,
                                  scale, false, nullptr, nullptr, stream);
+}
+
+hipError_t launch_kda_verify_wy(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                                const float *beta, float *const *state, float *const *wy,
+                                float *core, int B, int K, int heads, int head_dim, float scale,
+                                hipStream_t stream)
+{
+    return head_dim == 128
+               ? recurrent_t<128>(qkv, ldqkv, gate, beta, state, nullptr, core, B, K, heads,
+                                  scale, false, nullptr, nullptr, stream, wy)
+               : recurrent_t<16>(qkv, ldqkv, gate, beta, state, nullptr, core, B, K, heads,
+                                 scale, false, nullptr, nullptr, stream, wy);
+}
+
+// Table-form fold ("Glm5NextLayer" page, LayerWriteOnAccept: gdn_fold_accepted
+// over the verify's WY tables).  Unrolling the recurrence over the first n
+// rows of a sequence,
+//   S_n = diag(e^{g_{n-1}}) .. diag(e^{g_0}) S_0
+//         + sum_{s<n} diag(e^{g_{n-1}}) .. diag(e^{g_{s+1}}) k_s u_s^T,
+// so with the verify's u rows (the table) the accepted rows fold into the
+// state in one pass: per key channel i, with the decays summed from the last
+// row down (sigma_s = g_{s+1} + .. + g_{n-1}, sigma_{-1} the whole sum),
+//   S[i][j] = e^{sigma_{-1}[i]} S_0[i][j], then for s = n-1 .. 0:
+//   S[i][j] += (e^{sigma_s[i]} k_s[i]) u_s[j]        (one fma, in that order).
+// One workgroup per (head, value-column slice, sequence), the decode's
+// thread layout; the accepted rows go through LDS in blocks of kFoldRows.
+constexpr int kFoldRows = 16;
+
+template <int D, int NS>
+__global__ __launch_bounds__((RecCfg<D, NS, 1>::kThreads)) void kda_fold_wy_kernel(
+    const uint16_t *__restrict__ qkv, int64_t ldqkv, const float *__restrict__ gate,
+    float *const *__restrict__ state, float *const *__restrict__ wy,
+    const int32_t *__restrict__ n_accept, int K, int H, int32_t *__restrict__ status)
+{
+    using Cfg = RecCfg<D, NS, 1>;
+    constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT, NT = Cfg::kThreads;
+    static_assert(NT >= D, "one thread per key channel for the decay sums");
+    const int h = blockIdx.x / NS;
+    const int c0 = (blockIdx.x % NS) * Cfg::kDC;
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x, cg = tid % CG, tr = tid / CG;
+    const int na = n_accept[b];
+    if (status != nullptr && (na < 0 || na > K) && blockIdx.x == 0 && tid == 0)
+        atomicOr(status, kReportAcceptClamped);
+    const int n = min(max(na, 0), K);
+    if (n == 0) return;   // uniform over the workgroup
+
+    __shared__ float s_a[kFoldRows][D];          // e^{sigma_s} k_s, per key channel
+    __shared__ float s_e[D];                     // e^{sigma_{-1}}
+    __shared__ float4 s_u[kFoldRows][CG];        // u_s, this slice's columns
+    const int64_t qkvw = (int64_t)H * D;
+    const float *__restrict__ u_tab = wy[b] + (size_t)h * K * D + c0;
+
+    if (tid < D) {   // the whole decay sum, from the last accepted row down
+        float sg = 0.f;
+        for (int s = n - 1; s >= 0; --s) sg += gate[(((size_t)b * K + s) * H + h) * D + tid];
+        s_e[tid] = exp2_fast(sg * kLog2e);
+    }
+    float *__restrict__ Sg = state[b] + (size_t)h * D * D + c0;
+    float4 S[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) S[r] = load_stream(Sg + (size_t)(tr + RG * r) * D + 4 * cg);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const float e = s_e[tr + RG * r];
+        S[r] = make_float4(S[r].x * e, S[r].y * e, S[r].z * e, S[r].w * e);
+    }
+
+    float sig = 0.f;   // sigma_s of the row being tabulated (channel tid)
+    for (int s1 = n; s1 > 0; s1 -= kFoldRows) {
+        const int s0 = max(0, s1 - kFoldRows);
+        __syncthreads();   // the previous block's table reads are done
+        if (tid < D) {
+            for (int s = s1 - 1; s >= s0; --s) {
+                const size_t row = (size_t)b * K + s;
+                const float k = bf16_to_f32(qkv[row * ldqkv + qkvw + (int64_t)h * D + tid]);
+                s_a[s - s0][tid] = exp2_fast(sig * kLog2e) * k;
+                sig += gate[(row * H + h) * D + tid];
+            }
+        }
+        for (int idx = tid; idx < (s1 - s0) * CG; idx += NT) {
+            const int s = s0 + idx / CG, c = idx % CG;
+            s_u[s - s0][c] = reinterpret_cast<const float4 *>(u_tab + (size_t)s * D)[c];
+        }
+        __syncthreads();
+        for (int s = s1 - 1; s >= s0; --s) {
+            const float4 u = s_u[s - s0][cg];
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) S[r] = fma4(s_a[s - s0][tr + RG * r], u, S[r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) store_stream(Sg + (size_t)(tr + RG * r) * D + 4 * cg, S[r]);
+}
+
+template <int D>
+static hipError_t fold_wy_t(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                            float *const *state, float *const *wy, const int32_t *n_accept, int B,
+                            int K, int heads, int32_t *status, hipStream_t stream)
+{
+    const int64_t pairs = (int64_t)B * heads;
+    auto go = [&](auto ns) {
+        constexpr int NS = decltype(ns)::value;
+        hipLaunchKernelGGL((kda_fold_wy_kernel<D, NS>), dim3(heads * NS, B),
+                           dim3(RecCfg<D, NS, 1>::kThreads), 0, stream, qkv, ldqkv, gate, state,
+                           wy, n_accept, K, heads, status);
+        return hipGetLastError();
+    };
+    if constexpr (D >= 128) {
+        if (pairs <= 128) return go(std::integral_constant<int, 4>{});
+        if (pairs <= 256) return go(std::integral_constant<int, 2>{});
+    }
+    return go(std::integral_constant<int, 1>{});
+}
+
+hipError_t launch_kda_fold_wy(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                              float *const *state, float *const *wy, const int32_t *n_accept,
+                              int B, int K, int heads, int head_dim, int32_t *status,
+                              hipStream_t stream)
+{
+    return head_dim == 128
+               ? fold_wy_t<128>(qkv, ldqkv, gate, state, wy, n_accept, B, K, heads, status, stream)
+               : fold_wy_t<16>(qkv, ldqkv, gate, state, wy, n_accept, B, K, heads, status, stream);
 }
 
 hipError_t launch_kda_fold(const uint16_t *qkv, int64_t ldqkv, const float *gate,

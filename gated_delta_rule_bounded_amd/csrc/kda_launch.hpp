@@ -56,6 +56,17 @@ hipError_t launch_kda_fold(const uint16_t *qkv, int64_t ldqkv, const float *gate
                            const float *beta, float *const *state, const int32_t *n_accept,
                            int B, int K, int heads, int head_dim, int32_t *status,
                            hipStream_t stream);
+// Table form: the verify also writes each row's u (the value the row adds to
+// the state with its key) to wy[b] fp32 [heads, K, head_dim]; the fold then
+// applies the first n_accept[b] rows in one closed-form pass from those rows.
+hipError_t launch_kda_verify_wy(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                                const float *beta, float *const *state, float *const *wy,
+                                float *core, int B, int K, int heads, int head_dim, float scale,
+                                hipStream_t stream);
+hipError_t launch_kda_fold_wy(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                              float *const *state, float *const *wy, const int32_t *n_accept,
+                              int B, int K, int heads, int head_dim, int32_t *status,
+                              hipStream_t stream);
 
 // The block decode's per-head stages in one kernel: for each of the K rows
 // of every sequence, conv + SiLU + L2 of the head's q | k | v channels, the

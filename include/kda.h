@@ -374,6 +374,44 @@ int kda_fold_accepted(const uint16_t *qkv, int64_t ldqkv, const float *gate,
                       int32_t *status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kda_verify_wy_k / kda_fold_wy — table form of write-on-accept.
+ * "Glm5NextLayer" page, LayerWriteOnAccept: gdn_verify_run_batched takes the
+ * layer's staged WY tables (wy_tables), and gdn_fold_accepted folds the
+ * accepted rows through the layer's WY pointer table (h_table) and the
+ * accepted counts (na_tab).
+ * The pages do not spell the tables out; here a sequence's table holds, per
+ * head and row, the row's delta-rule value u_t = beta_t (v_t - S'^T k_t)
+ * (S' the decayed state before row t: the U rows of the rows' WY form), so
+ * the fold is one pass of the unrolled recurrence instead of a row-by-row
+ * walk:
+ *   S_n = diag(e^{g_0 + .. + g_{n-1}}) S_0
+ *         + sum_{s<n} diag(e^{g_{s+1} + .. + g_{n-1}}) k_s u_s^T.
+ * kda_verify_wy_k: kda_verify_k (core rows bitwise those of kda_decode_k,
+ *   states unchanged) that also writes the u rows: wy is a device array [B]
+ *   of pointers to fp32 [heads, K, head_dim] (16-byte aligned), row t of
+ *   head h at wy[b] + (h*K + t)*head_dim.  wy must not be the state table
+ *   (KDA_ERR_ALIAS).
+ * kda_fold_wy: qkv and gate hold the rows the verify read (k and the decay
+ *   are read again; v, q and beta are not); wy the verify's tables, n_accept
+ *   device int32 [B], each clamped to [0, K] and reported as in
+ *   kda_fold_accepted.  Afterwards *state[b] is the state after row
+ *   n_accept[b]-1 — equal to kda_decode_k's snapshot up to rounding (the
+ *   decays are summed from the last accepted row down, each channel's
+ *   e^{sum} S_0 first, then one fma per accepted row from the last down),
+ *   not bitwise like kda_fold_accepted.
+ * Errors as kda_verify_k / kda_fold_accepted.  B == 0 or K == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+int kda_verify_wy_k(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                    const float *beta, float *const *state, float *const *wy,
+                    float *core, int32_t B, int32_t K, int32_t heads,
+                    int32_t head_dim, float scale, hipStream_t stream);
+
+int kda_fold_wy(const uint16_t *qkv, int64_t ldqkv, const float *gate,
+                float *const *state, float *const *wy, const int32_t *n_accept,
+                int32_t B, int32_t K, int32_t heads, int32_t head_dim,
+                int32_t *status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * gated_rmsnorm — sigmoid-gated RMSNorm of the core output, per (token, head).
  * "Glm5NextKdaWorkspace" page, fields core, out_gate and o_norm_out;
  * "Glm5NextKdaWeights" page, field o_norm ([head_dim] bf16).

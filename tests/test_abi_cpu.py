@@ -309,6 +309,25 @@ def test_write_on_accept_validation(lib):
     assert fold(status=F + 2) == E_SHAPE                      # report word not 4-byte aligned
 
 
+def test_write_on_accept_table_validation(lib):
+    def verify(qkv=A, ld=3 * 32, core=B, Bn=2, K=4, head_dim=16, state=C, wy=Dp):
+        return lib.kda_verify_wy_k(qkv, ld, Dp + 4096, E, state, wy, core, Bn, K, 2, head_dim,
+                                   0.25, None)
+
+    def fold(qkv=A, ld=3 * 32, na=F, Bn=2, K=4, head_dim=16, state=C, wy=Dp, status=None):
+        return lib.kda_fold_wy(qkv, ld, Dp + 4096, state, wy, na, Bn, K, 2, head_dim, status,
+                               None)
+
+    assert verify(K=0) == OK and fold(Bn=0) == OK
+    assert verify(head_dim=64) == E_UNSUP and fold(head_dim=64) == E_UNSUP
+    assert verify(K=-1) == E_SHAPE and fold(K=-1) == E_SHAPE
+    assert verify(ld=90) == E_SHAPE and fold(ld=90) == E_SHAPE
+    assert verify(wy=0) == E_NULL and fold(wy=0) == E_NULL and fold(na=0) == E_NULL
+    assert verify(wy=C) == E_ALIAS and fold(wy=C) == E_ALIAS   # u-row table is the state table
+    assert verify(core=A + 64) == E_ALIAS                        # core over the qkv rows
+    assert fold(status=F + 2) == E_SHAPE                         # report word not 4-byte aligned
+
+
 def test_prefill_split_validation(lib):
     H, Dh, C = 2, 16, 16
     ws = lib.kda_prefill_workspace_bytes(128, H, Dh, C)

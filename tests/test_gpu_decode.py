@@ -208,6 +208,59 @@ def test_write_on_accept_equals_snapshots(B, K, H, D):
         np.testing.assert_array_equal(got[b], want, err_msg=f"seq {b} n_accept {na[b]}")
 
 
+@pytest.mark.parametrize("B,K,H,D", [(6, 4, 2, 16), (6, 4, 4, 128), (64, 4, 32, 128),
+                                     (24, 20, 2, 128), (300, 3, 1, 128)])
+def test_write_on_accept_table_form(B, K, H, D):
+    """Table form of write-on-accept ("Glm5NextLayer" page, the WY tables of
+    gdn_verify_run_batched / gdn_fold_accepted): the verify's rows are bitwise
+    those of decode_k and leave the states alone; folding n_accept rows from
+    the verify's u rows in one pass gives decode_k's snapshot after that row
+    up to rounding, and the oracle's state after that row.  n_accept runs
+    over 0..K and two out-of-range values, which clamp and are reported;
+    0 leaves the state bitwise as it was.  K = 20 takes the fold's row
+    blocks (16 rows) twice; 300 x 1 heads the whole-head launch."""
+    import gated_delta_rule_bounded_amd as kda
+    scale = D ** -0.5
+    seed = 4300 + B + K
+    rows, S0, ck, sk, snaps = _decode_k_vs_serial(B, K, H, D, seed)
+    qkv = cuda(torch.stack([r["qkv"] for r in rows], 1).reshape(B * K, -1), torch.bfloat16)
+    gate = cuda(np.stack([r["gate"] for r in rows], 1).reshape(B * K, H, D))
+    beta = cuda(np.stack([r["beta"] for r in rows], 1).reshape(B * K, H))
+    st = cuda(S0)
+    tab = kda.ptr_table(st)
+    wy = torch.full((B, H, K, D), float("nan"), device="cuda")
+    core = torch.empty(B * K, H, D, device="cuda")
+    say("verify_wy_k", B, K, H, D)
+    kda.kda_verify_wy_k(qkv, gate, beta, tab, kda.ptr_table(wy), core, B=B, K=K, heads=H,
+                        head_dim=D, scale=scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(core.view(B, K, H, D).cpu().numpy(), ck)
+    np.testing.assert_array_equal(st.cpu().numpy(), S0)
+    assert torch.isfinite(wy).all()
+    na = np.array([(b % (K + 3)) - 1 for b in range(B)], np.int32)   # -1, 0, .., K, K+1, ...
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("fold_wy", B, K, H, D)
+    kda.kda_fold_wy(qkv, gate, tab, kda.ptr_table(wy), torch.from_numpy(na).cuda(), B=B, K=K,
+                    heads=H, head_dim=D, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == (4 if np.any((na < 0) | (na > K)) else 0)
+    got = st.cpu().numpy()
+    sn = snaps.view(B, K - 1, H, D, D).cpu().numpy() if K > 1 else None
+    checked = 0
+    for b in range(B):
+        n = min(max(int(na[b]), 0), K)
+        if n == 0:
+            np.testing.assert_array_equal(got[b], S0[b], err_msg=f"seq {b} untouched")
+            continue
+        want = sk[b] if n == K else sn[b, n - 1]
+        # the closed form against decode_k's row-by-row state: rounding only
+        assert relerr(got[b], want) < 1e-5, f"seq {b} n_accept {na[b]}"
+        if checked < 4:   # and against the oracle's state after row n - 1
+            checked += 1
+            _, ref_S, _ = _oracle_seq(rows[:n], S0[b], b, H, D, scale)
+            assert relerr(got[b], ref_S) < TOL, f"seq {b} n_accept {na[b]} vs oracle"
+
+
 def test_decode_k_bits_do_not_depend_on_batch_size():
     """The recurrent kernel splits each head's state over 4, 2 or 1
     workgroups by value columns depending on the batch size, with the key-axis

@@ -619,7 +619,19 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in es])) * 1e-3
 
+    wy = torch.empty(1, H, K, D, device=dev)
+    wy_tab = kda.ptr_table(wy)
+
+    def woa_wy(i):   # the same in table form: the fold from the verify's u rows
+        S = sets[i % n_sets]
+        kda.kda_block_verify_wy_k(S["x"], S["w"], S["tab"], S["ctab"], wy_tab, buf_k, out, B=1,
+                                  K=K, hidden_size=hidden, heads=H, head_dim=D, rank=rank,
+                                  scale=D ** -0.5)
+        kda.kda_block_fold_wy(buf_k, S["tab"], S["ctab"], wy_tab, na, B=1, K=K, heads=H,
+                              head_dim=D)
+
     t_v, t_d, t_g, t_w = timed(verify), timed(decode), timed(gemv), timed(woa)
+    t_wt = timed(woa_wy)
 
     # the same calls captured once per layer in a HIP graph and replayed (the
     # six launches of a call are enqueued back to back without host gaps)
@@ -669,6 +681,7 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
                        f"heads={H}, head_dim={D}, rank={rank}, bf16 weights ~N(0,0.02), "
                        f"{n_sets} layers rotated (weights from HBM)",
                 verify_ms=t_v * 1e3, decode_ms=t_d * 1e3, write_on_accept_ms=t_w * 1e3,
+                write_on_accept_table_ms=t_wt * 1e3,
                 graph_verify_ms=t_gv * 1e3, graph_decode_ms=t_gd * 1e3,
                 batch_verify=dict(sequences=Bb, rows=Bb * K, ms=t_vb * 1e3,
                                   tokens_per_s=Bb * K / t_vb),

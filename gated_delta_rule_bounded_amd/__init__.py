@@ -26,7 +26,8 @@ __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_noalloc", "kd
            "dense_gemv_bf16_batchm", "kda_prefill_varlen", "varlen_chunks",
            "kda_verify_k", "kda_fold_accepted", "kda_verify_wy_k", "kda_fold_wy",
            "kda_prefill_split",
-           "kda_block_verify_k", "kda_block_fold_accepted", "kda_prefill_bf16", "kda_block_decode", "kda_block_decode_k",
+           "kda_block_verify_k", "kda_block_fold_accepted", "kda_block_verify_wy_k",
+           "kda_block_fold_wy", "kda_prefill_bf16", "kda_block_decode", "kda_block_decode_k",
            "block_decode_buffers",
            "ptr_table", "KdaError",
            "last_error", "library_path"]
@@ -613,6 +614,41 @@ def kda_block_fold_accepted(buffers, state, conv_state, n_accept, *, B, K, heads
         ctypes.byref(bufs), _ptr(state, torch.int64, "state"),
         _ptr(conv_state, torch.int64, "conv_state"), _ptr(n_accept, torch.int32, "n_accept"), B,
         K, heads, head_dim, st, _stream()))
+
+
+def kda_block_verify_wy_k(hidden, weights, state, conv_state, wy, buffers, out, *, B, K,
+                          hidden_size, heads, head_dim, rank, scale, eps_l2=1e-6, eps_rms=1e-5):
+    """kda_block_verify_k that also writes the recurrent rows' u values to the
+    WY tables ``wy`` (a pointer table of B entries, each fp32 [heads, K,
+    head_dim])."""
+    bf = torch.bfloat16
+    _check_weights(weights, hidden_size, heads, head_dim, rank)
+    mk = _decode_buffers(buffers, B * K, heads, head_dim, rank)
+    _block_decode_sizes(hidden, state, conv_state, out, B, K, hidden_size)
+    _table(wy, "wy", B)
+    wts, bufs = _block_weights(weights), mk()
+    _check(_lib.lib.kda_block_verify_wy_k(
+        _ptr(hidden, bf, "hidden"), ctypes.byref(wts), _ptr(state, torch.int64, "state"),
+        _ptr(conv_state, torch.int64, "conv_state"), _ptr(wy, torch.int64, "wy"),
+        ctypes.byref(bufs), _ptr(out, bf, "out"), B, K, hidden_size, heads, head_dim, rank,
+        float(scale), float(eps_l2), float(eps_rms), _stream()))
+
+
+def kda_block_fold_wy(buffers, state, conv_state, wy, n_accept, *, B, K, heads, head_dim,
+                      status=None):
+    """Fold the first n_accept[b] verified rows into each recurrent state in
+    one pass from the verify's WY tables, and into each conv state as
+    kda_block_fold_accepted does; ``status`` as kda_fold_accepted."""
+    mk = _decode_buffers(buffers, B * K, heads, head_dim)
+    _table(state, "state", B)
+    _table(conv_state, "conv_state", B)
+    _table(wy, "wy", B)
+    _dense(n_accept, "n_accept", torch.int32, B)
+    st, bufs = _status(status), mk()
+    _check(_lib.lib.kda_block_fold_wy(
+        ctypes.byref(bufs), _ptr(state, torch.int64, "state"),
+        _ptr(conv_state, torch.int64, "conv_state"), _ptr(wy, torch.int64, "wy"),
+        _ptr(n_accept, torch.int32, "n_accept"), B, K, heads, head_dim, st, _stream()))
 
 
 def kda_prefill_bf16(qkv, gate, beta, state, core, workspace, *, T, T_pad, heads, head_dim, chunk,

@@ -17,7 +17,7 @@ SYMBOLS = ("kda_last_error", "conv_silu_l2", "kda_gate", "kda_prefill_workspace_
            "kda_block_decode", "kda_prefill_varlen", "kda_verify_k", "kda_fold_accepted",
            "kda_prefill_split", "kda_block_verify_k", "kda_block_fold_accepted",
            "kda_prefill_bf16", "kda_prefill_noalloc", "kda_prefill_varlen_workspace_bytes",
-           "kda_verify_wy_k", "kda_fold_wy")
+           "kda_verify_wy_k", "kda_fold_wy", "kda_block_verify_wy_k", "kda_block_fold_wy")
 
 
 class BlockWeights(ctypes.Structure):
@@ -117,6 +117,13 @@ def _load():
     lib.kda_block_fold_accepted.restype = ctypes.c_int
     lib.kda_block_fold_accepted.argtypes = [ctypes.POINTER(BlockDecodeBuffers), P, P, P, i32, i32,
                                             i32, i32, P, P]
+    lib.kda_block_verify_wy_k.restype = ctypes.c_int
+    lib.kda_block_verify_wy_k.argtypes = [P, ctypes.POINTER(BlockWeights), P, P, P,
+                                          ctypes.POINTER(BlockDecodeBuffers), P] + [i32] * 6 + \
+        [f32] * 3 + [P]
+    lib.kda_block_fold_wy.restype = ctypes.c_int
+    lib.kda_block_fold_wy.argtypes = [ctypes.POINTER(BlockDecodeBuffers), P, P, P, P, i32, i32,
+                                      i32, i32, P, P]
     lib.kda_block_decode.restype = ctypes.c_int
     lib.kda_block_decode.argtypes = [P, ctypes.POINTER(BlockWeights), P, P,
                                      ctypes.POINTER(BlockDecodeBuffers), P] + [i32] * 5 + \

@@ -730,7 +730,8 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
                             uint16_t *const *conv_snap, const kda_block_decode_buffers *b,
                             uint16_t *out, int32_t B, int32_t K, int32_t hidden_size,
                             int32_t heads, int32_t head_dim, int32_t rank, float scale,
-                            float eps_l2, float eps_rms, bool verify, hipStream_t stream)
+                            float eps_l2, float eps_rms, bool verify, hipStream_t stream,
+                            float *const *wy = nullptr)
 {
     if (!head_dim_ok(head_dim))
         return fail(KDA_ERR_UNSUPPORTED, "kda_block_decode_k: head_dim=%d", head_dim);
@@ -824,7 +825,7 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
     // workgroups (the fused conv reads the head's whole conv window, so its
     // workgroup must be the only one that rewrites it).  A verify writes
     // neither state nor snapshots.
-    const bool fuse_mixer = K == 1 && (int64_t)B * heads <= 128;
+    const bool fuse_mixer = K == 1 && (int64_t)B * heads <= 128 && wy == nullptr;
     kda::MixerArgs mixer{};
     mixer.x = b->qkv_proj;
     mixer.ldx = cd;
@@ -860,9 +861,13 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
                                                    stream, !verify),
              "kda_block_decode_k: conv launch")) ||
         (rc = hip_status(fuse_mixer ? hipSuccess
-                         : verify ? kda::launch_kda_verify(b->conv_out, cd, b->gate, b->beta,
-                                                           state, b->core, B, K, heads, head_dim,
-                                                           scale, stream)
+                         : verify ? (wy ? kda::launch_kda_verify_wy(b->conv_out, cd, b->gate,
+                                                                    b->beta, state, wy, b->core, B,
+                                                                    K, heads, head_dim, scale,
+                                                                    stream)
+                                        : kda::launch_kda_verify(b->conv_out, cd, b->gate, b->beta,
+                                                                 state, b->core, B, K, heads,
+                                                                 head_dim, scale, stream))
                                   : kda::launch_kda_recurrent(b->conv_out, cd, b->gate, b->beta,
                                                               state, mixer.snap, b->core, B, K,
                                                               heads, head_dim, scale, stream),
@@ -899,6 +904,51 @@ int kda_block_verify_k(const uint16_t *hidden, const kda_block_weights *w, float
     return block_decode_run(hidden, w, state, conv_state, nullptr, nullptr, b, out, B, K,
                             hidden_size, heads, head_dim, rank, scale, eps_l2, eps_rms, true,
                             stream);
+}
+
+int kda_block_verify_wy_k(const uint16_t *hidden, const kda_block_weights *w, float *const *state,
+                          uint16_t *const *conv_state, float *const *wy,
+                          const kda_block_decode_buffers *b, uint16_t *out, int32_t B, int32_t K,
+                          int32_t hidden_size, int32_t heads, int32_t head_dim, int32_t rank,
+                          float scale, float eps_l2, float eps_rms, hipStream_t stream)
+{
+    if (B > 0 && K > 0 && !wy)
+        return fail(KDA_ERR_NULL, "kda_block_verify_wy_k: null pointer argument");
+    if (wy && ((const void *)wy == (const void *)state || (const void *)wy == (const void *)conv_state))
+        return fail(KDA_ERR_ALIAS, "kda_block_verify_wy_k: table of u rows is a state table");
+    return block_decode_run(hidden, w, state, conv_state, nullptr, nullptr, b, out, B, K,
+                            hidden_size, heads, head_dim, rank, scale, eps_l2, eps_rms, true,
+                            stream, wy);
+}
+
+int kda_block_fold_wy(const kda_block_decode_buffers *b, float *const *state,
+                      uint16_t *const *conv_state, float *const *wy, const int32_t *n_accept,
+                      int32_t B, int32_t K, int32_t heads, int32_t head_dim, int32_t *status,
+                      hipStream_t stream)
+{
+    if (B < 0 || K < 0 || heads <= 0 || (int64_t)B * K > (1 << 24) || B > kMaxGridYZ)
+        return fail(KDA_ERR_SHAPE, "kda_block_fold_wy: B=%d K=%d heads=%d", B, K, heads);
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_block_fold_wy: head_dim=%d", head_dim);
+    if (B == 0 || K == 0) return ok();
+    if (!b || !state || !conv_state || !wy || !n_accept || !b->qkv_proj || !b->conv_out ||
+        !b->gate)
+        return fail(KDA_ERR_NULL, "kda_block_fold_wy: null pointer argument");
+    if (!aligned16(b->qkv_proj) || !aligned16(b->conv_out) || !aligned16(b->gate) ||
+        (status && !aligned4(status)))
+        return fail(KDA_ERR_SHAPE, "kda_block_fold_wy: misaligned buffer");
+    if ((const void *)wy == (const void *)state || (const void *)wy == (const void *)conv_state)
+        return fail(KDA_ERR_ALIAS, "kda_block_fold_wy: table of u rows is a state table");
+    const int64_t cd = 3LL * heads * head_dim;
+    int rc;
+    if ((rc = hip_status(kda::launch_kda_fold_wy(b->conv_out, cd, b->gate, state, wy, n_accept, B,
+                                                 K, heads, head_dim, status, stream),
+                         "kda_block_fold_wy: state fold launch")) ||
+        (rc = hip_status(kda::launch_conv_fold(b->qkv_proj, cd, conv_state, n_accept, B, K, heads,
+                                               head_dim, stream),
+                         "kda_block_fold_wy: conv fold launch")))
+        return rc;
+    return ok();
 }
 
 int kda_block_fold_accepted(const kda_block_decode_buffers *b, float *const *state,

@@ -596,6 +596,33 @@ int kda_block_fold_accepted(const kda_block_decode_buffers *buf, float *const *s
                             hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kda_block_verify_wy_k / kda_block_fold_wy — the block's write-on-accept
+ * in table form ("Glm5NextLayer" page, LayerWriteOnAccept: the verify with
+ * the layer's WY tables, gdn_fold_accepted through the WY pointer table and
+ * the accepted counts; the tables as in kda_verify_wy_k).
+ * kda_block_verify_wy_k: kda_block_verify_k that also writes the recurrent
+ *   rows' u values to wy (a device array [B] of pointers to fp32 [heads, K,
+ *   head_dim], 16-byte aligned); out and every stage buffer bitwise those of
+ *   kda_block_verify_k; wy must not be a state table (KDA_ERR_ALIAS).
+ * kda_block_fold_wy: buf the verify's stage buffers, wy its tables; the
+ *   recurrent state as kda_fold_wy (equal to kda_block_decode_k's snapshot
+ *   up to rounding), the conv state bitwise as kda_block_fold_accepted.
+ *   Two launches; no output; `status` as kda_fold_accepted.
+ * Errors as kda_block_verify_k / kda_block_fold_accepted.
+ * ------------------------------------------------------------------------ */
+int kda_block_verify_wy_k(const uint16_t *hidden, const kda_block_weights *w,
+                          float *const *state, uint16_t *const *conv_state,
+                          float *const *wy, const kda_block_decode_buffers *buf,
+                          uint16_t *out, int32_t B, int32_t K, int32_t hidden_size,
+                          int32_t heads, int32_t head_dim, int32_t rank, float scale,
+                          float eps_l2, float eps_rms, hipStream_t stream);
+
+int kda_block_fold_wy(const kda_block_decode_buffers *buf, float *const *state,
+                      uint16_t *const *conv_state, float *const *wy,
+                      const int32_t *n_accept, int32_t B, int32_t K, int32_t heads,
+                      int32_t head_dim, int32_t *status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * kda_block_decode — one token for each of B sequences through the whole
  * block ("Glm5NextKdaLayer" page, decode: single-token decode carrying both
  * states, result in out, states updated in place).  Exactly

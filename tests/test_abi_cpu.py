@@ -370,6 +370,27 @@ def test_block_write_on_accept_validation(lib):
                                        None, None) == E_SHAPE
     assert lib.kda_block_fold_accepted(ref(b), 60 << 36, 61 << 36, 64 << 36, 3, 4, 2, 16,
                                        (65 << 36) + 1, None) == E_SHAPE
+    # the table form: the same checks, plus the table of u rows
+    wy = 66 << 36
+    assert lib.kda_block_verify_wy_k(63 << 36, ref(w), 60 << 36, 61 << 36, wy, ref(b), 62 << 36,
+                                     3, 0, 64, 2, 16, 32, 0.25, 1e-6, 1e-5, None) == OK
+    assert lib.kda_block_verify_wy_k(63 << 36, ref(w), 60 << 36, 61 << 36, 0, ref(b), 62 << 36,
+                                     3, 4, 64, 2, 16, 32, 0.25, 1e-6, 1e-5, None) == E_NULL
+    assert lib.kda_block_verify_wy_k(63 << 36, ref(w), 60 << 36, 61 << 36, 60 << 36, ref(b),
+                                     62 << 36, 3, 4, 64, 2, 16, 32, 0.25, 1e-6, 1e-5,
+                                     None) == E_ALIAS
+    assert lib.kda_block_verify_wy_k(63 << 36, ref(w), 60 << 36, 61 << 36, wy, ref(b), 62 << 36,
+                                     3, 4, 64, 2, 64, 32, 0.25, 1e-6, 1e-5, None) == E_UNSUP
+    assert lib.kda_block_fold_wy(ref(b), 60 << 36, 61 << 36, wy, 64 << 36, 0, 4, 2, 16,
+                                 None, None) == OK
+    assert lib.kda_block_fold_wy(ref(b), 60 << 36, 61 << 36, 0, 64 << 36, 3, 4, 2, 16,
+                                 None, None) == E_NULL
+    assert lib.kda_block_fold_wy(ref(b), 60 << 36, 61 << 36, 61 << 36, 64 << 36, 3, 4, 2, 16,
+                                 None, None) == E_ALIAS
+    assert lib.kda_block_fold_wy(ref(b), 60 << 36, 61 << 36, wy, 64 << 36, 3, 4, 2, 64,
+                                 None, None) == E_UNSUP
+    assert lib.kda_block_fold_wy(ref(b), 60 << 36, 61 << 36, wy, 64 << 36, 3, 4, 2, 16,
+                                 (65 << 36) + 1, None) == E_SHAPE
 
 
 def test_grid_limits_are_shape_errors(lib):

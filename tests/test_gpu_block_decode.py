@@ -337,6 +337,65 @@ def test_block_write_on_accept_equals_snapshots(B, K, H, D, hidden, rank):
                                       err_msg=f"seq {b} conv state")
 
 
+@pytest.mark.parametrize("B,K,H,D,hidden,rank", [
+    (7, 4, 2, 16, 128, 32),
+    (6, 4, 2, 128, 256, 32),
+    (1, 4, 32, 128, 4096, 128),
+    (2, 1, 2, 128, 256, 32),
+])
+def test_block_write_on_accept_table_form(B, K, H, D, hidden, rank):
+    """The block's write-on-accept in table form ("Glm5NextLayer" page, the
+    verify's WY tables and the fold through them): the verify's stage
+    buffers and output are bitwise those of kda_block_decode_k and no state
+    is written; folding n_accept rows from the u rows leaves the recurrent
+    state equal to decode_k's snapshot after that row up to rounding and the
+    conv state bitwise equal to it; 0 rows leave both untouched.  K = 1 takes
+    the unfused stage kernels (the one-token fused kernel writes no table)."""
+    x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1801 + B, w_std=0.05 if hidden < 4096 else 0.02)
+    scale = D ** -0.5
+    ref = _gpu_decode_k(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)
+    dev = torch.device("cuda")
+    wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+    states = [torch.from_numpy(np.ascontiguousarray(S0[b])).to(dev) for b in range(B)]
+    convs = [conv0[b].to(dev).contiguous() for b in range(B)]
+    st_tab, cv_tab = kda.ptr_table(states), kda.ptr_table(convs)
+    wy = torch.full((B, H, K, D), float("nan"), device=dev)
+    wy_tab = kda.ptr_table(wy)
+    buf = kda.block_decode_buffers(B * K, heads=H, head_dim=D, rank=rank, device=dev)
+    out = torch.empty(B * K, hidden, dtype=torch.bfloat16, device=dev)
+    say("block verify_wy_k", B, K, hidden, H, D, rank)
+    kda.kda_block_verify_wy_k(x.to(dev).contiguous(), wd, st_tab, cv_tab, wy_tab, buf, out, B=B,
+                              K=K, hidden_size=hidden, heads=H, head_dim=D, rank=rank,
+                              scale=scale)
+    torch.cuda.synchronize()
+    for n in STAGES:
+        np.testing.assert_array_equal(buf[n].float().cpu().numpy(), ref[n], err_msg=n)
+    np.testing.assert_array_equal(out.float().cpu().numpy(), ref["final_out"])
+    assert torch.isfinite(wy).all()
+    for b in range(B):
+        np.testing.assert_array_equal(states[b].cpu().numpy(), S0[b])
+        np.testing.assert_array_equal(convs[b].float().cpu().numpy(), conv0[b].float().numpy())
+    na = (np.array([(b % (K + 3)) - 1 for b in range(B)], np.int32) if B > 2
+          else np.array([min(2, K), 0][:B], np.int32))
+    say("block fold_wy", B, K, list(na))
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    kda.kda_block_fold_wy(buf, st_tab, cv_tab, wy_tab, torch.from_numpy(na).cuda(), B=B, K=K,
+                          heads=H, head_dim=D, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == (4 if np.any((na < 0) | (na > K)) else 0)
+    for b in range(B):
+        n = min(max(int(na[b]), 0), K)
+        got_s, got_c = states[b].cpu().numpy(), convs[b].float().cpu().numpy()
+        if n == 0:
+            np.testing.assert_array_equal(got_s, S0[b])
+            np.testing.assert_array_equal(got_c, conv0[b].float().numpy())
+            continue
+        want_s, want_c = ((ref["state"][b], ref["conv_state"][b]) if n == K else
+                          (ref["state_snaps"][b, n - 1], ref["conv_snaps"][b, n - 1]))
+        assert relerr(got_s, want_s) < 1e-5, f"seq {b} n_accept {na[b]} state"
+        np.testing.assert_array_equal(got_c, want_c, err_msg=f"seq {b} conv state")
+
+
 def test_block_decode_k_graph_replay_matches_eager():
     """The block verify (six stream-ordered launches, no allocation, no
     memset, no synchronisation) captured once in a HIP graph and replayed

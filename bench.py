@@ -437,7 +437,7 @@ def bench_stages(kda, dev, reps=10):
     return res
 
 
-def bench_block(kda, dev, reps=10):
+def bench_block(kda, dev, reps=10, pack_low_rank=True):
     """The full KDA block at T = 8192 (hidden 4096, 32 heads x 128, rank-128
     gates, weights ~ N(0, 0.02)): one kda_block_prefill call per repetition,
     from a zero state.  The projections' share is the block time less the
@@ -448,9 +448,13 @@ def bench_block(kda, dev, reps=10):
     x = x.to(dev)
     wd = {n: t.to(dev).contiguous() for n, t in w.items()}
     # q, k, v projection weights packed back to back, as a serving engine
-    # stores them (the block then runs them as one GEMM)
+    # stores them (the block then runs them as one GEMM), and likewise f_a,
+    # g_a and b_proj
     wqkv = torch.cat([wd["q_proj"], wd["k_proj"], wd["v_proj"]]).contiguous()
     wd["q_proj"], wd["k_proj"], wd["v_proj"] = wqkv[:qkv], wqkv[qkv:2 * qkv], wqkv[2 * qkv:]
+    if pack_low_rank:
+        wlr = torch.cat([wd["f_a"], wd["g_a"], wd["b_proj"]]).contiguous()
+        wd["f_a"], wd["g_a"], wd["b_proj"] = wlr[:rank], wlr[rank:2 * rank], wlr[2 * rank:]
     st = torch.zeros(H, D, D, device=dev)
     cs = torch.zeros(1, 4, 3 * qkv, dtype=torch.bfloat16, device=dev)
     ctab = kda.ptr_table(cs)

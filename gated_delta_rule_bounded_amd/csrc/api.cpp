@@ -672,9 +672,35 @@ int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float 
                                                   b->q32, b->k32, b->v32, stream),
                          "kda_block_prefill: conv_silu_l2 launch")))
         return rc;
-    if ((rc = gemm("f_a", hidden, hidden_size, w->f_a, b->fa, rank, rank, hidden_size)) ||
-        (rc = gemm("f_b", b->fa, rank, w->f_b, b->g_raw, qkv, (int)qkv, rank)) ||
-        (rc = gemm("b_proj", hidden, hidden_size, w->b_proj, b->b_raw, heads, heads, hidden_size)))
+    // f_a, g_a and b_proj read the same hidden rows: weights that lie back to
+    // back ([f_a; g_a; b_proj], one [2*rank + heads, hidden] matrix) run as
+    // one GEMM into the start of the GEMM workspace, when it has room for the
+    // [T, 2*rank + heads] result beside 4 MiB for the library, and the three
+    // column ranges are copied out (the hidden rows are read once, not three
+    // times)
+    const size_t lr_w = (size_t)rank * hidden_size;
+    const int n_lr = 2 * rank + heads;
+    const size_t lr_bytes = ((size_t)T * n_lr * 2 + 255) & ~size_t(255);
+    const bool lr_packed = w->g_a == w->f_a + lr_w && w->b_proj == w->g_a + lr_w &&
+                           heads % 8 == 0 && b->gemm_ws_bytes >= lr_bytes + (size_t(4) << 20);
+    if (lr_packed) {
+        uint16_t *tmp = static_cast<uint16_t *>(b->gemm_ws);
+        if (kda::gemm_bf16_xwT(hidden, hidden_size, w->f_a, hidden_size, tmp, n_lr, T, n_lr,
+                               hidden_size, static_cast<char *>(b->gemm_ws) + lr_bytes,
+                               b->gemm_ws_bytes - lr_bytes, stream, &what))
+            return fail(KDA_ERR_HIP, "kda_block_prefill: f_a|g_a|b_proj projection: hipBLASLt %s",
+                        what);
+        uint16_t *const ys[3] = {b->fa, b->ga, b->b_raw};
+        const int cs[3] = {0, rank, 2 * rank}, ns[3] = {rank, rank, heads};
+        if ((rc = hip_status(kda::launch_split_cols(tmp, n_lr, T, 3, ys, cs, ns, stream),
+                             "kda_block_prefill: fa|ga|b_raw split launch")))
+            return rc;
+    } else if ((rc = gemm("f_a", hidden, hidden_size, w->f_a, b->fa, rank, rank, hidden_size)) ||
+               (rc = gemm("b_proj", hidden, hidden_size, w->b_proj, b->b_raw, heads, heads,
+                          hidden_size))) {
+        return rc;
+    }
+    if ((rc = gemm("f_b", b->fa, rank, w->f_b, b->g_raw, qkv, (int)qkv, rank)))
         return rc;
     if ((rc = hip_status(kda::launch_kda_gate(b->g_raw, qkv, b->b_raw, heads, w->a_log, w->dt_bias,
                                               T, heads, head_dim, b->gate, b->beta, stream),
@@ -687,7 +713,8 @@ int kda_block_prefill(const uint16_t *hidden, const kda_block_weights *w, float 
                                                       b->prefill_ws, stream),
                          "kda_block_prefill: kda_prefill launch")))
         return rc;
-    if ((rc = gemm("g_a", hidden, hidden_size, w->g_a, b->ga, rank, rank, hidden_size)) ||
+    if ((!lr_packed && (rc = gemm("g_a", hidden, hidden_size, w->g_a, b->ga, rank, rank,
+                                  hidden_size))) ||
         (rc = gemm("g_b", b->ga, rank, w->g_b, b->out_gate, qkv, (int)qkv, rank)))
         return rc;
     if ((rc = hip_status(kda::launch_gated_rmsnorm(b->core, qkv, b->out_gate, qkv, w->o_norm, T,

@@ -131,4 +131,47 @@ int gemm_bf16_xwT(const uint16_t *x, int64_t ldx, const uint16_t *w, int64_t ldw
     return 0;
 }
 
+// Column ranges of a row-major bf16 matrix x [rows][ldx] copied to their own
+// buffers: y_r[t][0 .. n_r) = x[t][c_r .. c_r + n_r), for up to three ranges
+// (n_r multiples of 8), 16 bytes per thread.
+struct ColSplit {
+    uint16_t *y[3];
+    int32_t c[3], n[3];
+    int32_t chunks;   // 16-byte pieces per row over all ranges
+};
+
+__global__ __launch_bounds__(256) void split_cols_kernel(const uint16_t *__restrict__ x,
+                                                         int64_t ldx, int64_t rows,
+                                                         const ColSplit s)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * s.chunks) return;
+    const int64_t t = i / s.chunks;
+    int p = (int)(i % s.chunks) * 8;   // element offset within the ranges
+    int r = 0;
+    while (p >= s.n[r]) p -= s.n[r++];
+    *reinterpret_cast<uint4 *>(s.y[r] + t * s.n[r] + p) =
+        *reinterpret_cast<const uint4 *>(x + t * ldx + s.c[r] + p);
+}
+
+hipError_t launch_split_cols(const uint16_t *x, int64_t ldx, int64_t rows, int nr,
+                             uint16_t *const *y, const int *c, const int *n, hipStream_t stream)
+{
+    ColSplit s{};
+    int chunks = 0;
+    for (int r = 0; r < nr; ++r) {
+        s.y[r] = y[r];
+        s.c[r] = c[r];
+        s.n[r] = n[r];
+        chunks += n[r] / 8;
+    }
+    s.chunks = chunks;
+    const int64_t total = rows * chunks;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(split_cols_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       x, ldx, rows, s);
+    return hipGetLastError();
+}
+
 }  // namespace kda
+

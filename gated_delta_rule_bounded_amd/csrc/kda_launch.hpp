@@ -179,6 +179,11 @@ hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStre
 // y[rows][n_out] (row stride ldy) = bf16(x[rows][n_in] (stride ldx) w^T), w in
 // torch Linear layout [n_out][n_in] (stride ldw), fp32 accumulation, on the
 // vendor GEMM (kda_gemm.cpp).  Returns 0, or 1 with *what naming the failure.
+// y_r[t][0 .. n[r]) = x[t][c[r] .. c[r] + n[r]) for nr <= 3 column ranges of a bf16
+// matrix (n[r] multiples of 8; x, y 16-byte aligned, ldx a multiple of 8).
+hipError_t launch_split_cols(const uint16_t *x, int64_t ldx, int64_t rows, int nr,
+                             uint16_t *const *y, const int *c, const int *n, hipStream_t stream);
+
 int gemm_bf16_xwT(const uint16_t *x, int64_t ldx, const uint16_t *w, int64_t ldw, uint16_t *y,
                   int64_t ldy, int rows, int n_out, int n_in, void *ws, size_t ws_bytes,
                   hipStream_t stream, const char **what);

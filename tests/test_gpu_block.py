@@ -33,10 +33,12 @@ def run_gpu(x, w, T, T_pad, hidden, H, D, rank, C, S0, conv0, scale, packed=Fals
     the device buffers for further GPU calls."""
     dev = torch.device("cuda")
     wd = {n: t.to(dev).contiguous() for n, t in w.items()}
-    if packed:   # q, k, v weights back to back: the block runs them as one GEMM
+    if packed:   # weights back to back: the block runs q|k|v and f_a|g_a|b_proj as one GEMM each
         qkv = H * D
         wqkv = torch.cat([wd["q_proj"], wd["k_proj"], wd["v_proj"]]).contiguous()
         wd["q_proj"], wd["k_proj"], wd["v_proj"] = wqkv[:qkv], wqkv[qkv:2 * qkv], wqkv[2 * qkv:]
+        wlr = torch.cat([wd["f_a"], wd["g_a"], wd["b_proj"]]).contiguous()
+        wd["f_a"], wd["g_a"], wd["b_proj"] = wlr[:rank], wlr[rank:2 * rank], wlr[2 * rank:]
     xg = x[:T].to(dev).contiguous()
     st = torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).to(dev)
     cs = conv0.to(dev).contiguous()
@@ -78,6 +80,7 @@ def compare(got, ref, T, H, D, names):
     (50, 64, 2, 16, 64, 16, 16, False),
     (200, 256, 2, 128, 256, 32, 64, False),
     (200, 256, 2, 128, 256, 32, 64, True),
+    (200, 256, 8, 16, 128, 32, 64, True),   # 8 heads: f_a | g_a | b_proj as one GEMM
 ])
 def test_block_small_against_oracle(orc, T, T_pad, H, D, hidden, rank, C, packed):
     x, w = workloads.block_raw(T, hidden, H, D, rank, 4, 1004, w_std=0.05)

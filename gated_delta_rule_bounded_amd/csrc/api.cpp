@@ -845,14 +845,14 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
         {b->ga, w->g_b, b->out_gate, rk, qkv, qk, rk},
     };
     const kda::GemvSeg back[] = {{b->o_norm_out, w->o_proj, out, qkv, hs, hs, qk}};
-    // conv + SiLU + L2, the recurrence and the gated RMSNorm: for one row of
-    // few sequences in one kernel per (head, sequence), which saves two
-    // launches (the same bits as the three kernels); otherwise as three
-    // launches, where the recurrence can split a head's columns over several
-    // workgroups (the fused conv reads the head's whole conv window, so its
-    // workgroup must be the only one that rewrites it).  A verify writes
-    // neither state nor snapshots.
-    const bool fuse_mixer = K == 1 && (int64_t)B * heads <= 128 && wy == nullptr;
+    // The rank-R gate products, conv + SiLU + L2, the recurrence and the
+    // gated RMSNorm: for up to 16 rows of few sequences at rank <= 128 in
+    // two launches (a workgroup per value-column slice of each (head,
+    // sequence), then one per (head, sequence) for the norm and the conv
+    // window), the same bits as the four launches otherwise taken.  A verify
+    // writes neither state nor snapshots.
+    const bool fuse_mixer = K <= kda::kMixerMaxRows && rank <= kda::kMixerMaxRank &&
+                            (int64_t)B * heads <= 128;
     kda::MixerArgs mixer{};
     mixer.x = b->qkv_proj;
     mixer.ldx = cd;
@@ -861,16 +861,25 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
     mixer.conv_snap = K > 1 && !verify ? conv_snap : nullptr;
     mixer.y = b->conv_out;
     mixer.ldy = cd;
+    mixer.fa = b->fa;
+    mixer.ga = b->ga;
+    mixer.f_b = w->f_b;
+    mixer.g_b = w->g_b;
+    mixer.a_log = w->a_log;
+    mixer.dt_bias = w->dt_bias;
+    mixer.g_raw = b->g_raw;
     mixer.gate = b->gate;
     mixer.beta = b->beta;
     mixer.state = state;
     mixer.snap = K > 1 && !verify ? snap : nullptr;
+    mixer.wy = wy;
     mixer.core = b->core;
     mixer.out_gate = b->out_gate;
     mixer.norm_w = w->o_norm;
     mixer.out = b->o_norm_out;
     mixer.K = K;
     mixer.H = heads;
+    mixer.R = rank;
     mixer.scale = scale;
     mixer.eps_l2 = eps_l2;
     mixer.eps_rms = eps_rms;
@@ -878,7 +887,7 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
     int rc;
     if ((rc = hip_status(kda::launch_gemv_bf16_batchm(front, 6, Mi, stream),
                          "kda_block_decode_k: front projections launch")) ||
-        (rc = hip_status(kda::launch_gemv_bf16_batchm(mid, 2, Mi, stream),
+        (rc = hip_status(fuse_mixer ? hipSuccess : kda::launch_gemv_bf16_batchm(mid, 2, Mi, stream),
                          "kda_block_decode_k: low-rank projections launch")) ||
         (rc = hip_status(
              fuse_mixer ? kda::launch_kda_mixer(mixer, B, head_dim, stream)

@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "kda_device.hpp"
+#include "kda_gemv.hpp"
 #include "kda_launch.hpp"
 #include "kda_rows.hpp"
 
@@ -71,27 +72,35 @@ __device__ __forceinline__ float4 fma4(float a, const float4 &b, const float4 &c
                        __builtin_fmaf(a, b.z, c.z), __builtin_fmaf(a, b.w, c.w));
 }
 
+// The key-axis partial sums of one row (exchanged through LDS).
+template <int D, int NS, int RGT>
+struct __align__(16) RecRed {
+    float4 s_red[RecCfg<D, NS, RGT>::kPairs][2][RecCfg<D, NS, RGT>::kCG];
+    float s_kq[RecCfg<D, NS, RGT>::kPairs];
+};
+
 // The workgroup's LDS: one row's q, k, v and decay factors e = exp(g), and the
 // key-axis partial sums.
 template <int D, int NS, int RGT>
 struct __align__(16) RecLds {
     float s_q[D], s_k[D], s_v[D], s_e[D];
-    float4 s_red[RecCfg<D, NS, RGT>::kPairs][2][RecCfg<D, NS, RGT>::kCG];
-    float s_kq[RecCfg<D, NS, RGT>::kPairs];
+    RecRed<D, NS, RGT> red;
 };
 
 // One row of the recurrence over this workgroup's slice (value columns c0 ..
-// c0 + D/NS - 1), with the row's q, k, v and e in L: decays S, forms
-// u = beta (v - S'^T k) and o = scale (S'^T q + u (k . q)), and adds k u^T to
-// S.  Thread row 0 owns whole columns and stores o: to core_row (the row's
-// first value column of this slice) and o_lds (the same columns), each when
-// given; and u to u_row (same columns) when given.  Passes one barrier (the
-// key-axis sums go through LDS); the caller passes another before L is
-// rewritten.
+// c0 + D/NS - 1), with the row's q, k, v and e (D values each, in LDS):
+// decays S, forms u = beta (v - S'^T k) and o = scale (S'^T q + u (k . q)),
+// and adds k u^T to S.  Thread row 0 owns whole columns and stores o: to
+// core_row (the row's first value column of this slice) and o_lds (the same
+// columns), each when given; and u to u_row (same columns) when given.
+// Passes one barrier (the key-axis sums go through R); the caller passes
+// another before R or the row's operands are rewritten.
 template <int D, int NS, int RGT>
-__device__ __forceinline__ void rec_row(float4 (&S)[RGT][D / 16], RecLds<D, NS, RGT> &L, float bt,
-                                        float scale, int c0, int tid, float *core_row,
-                                        float *o_lds, float *u_row = nullptr)
+__device__ __forceinline__ void rec_row(float4 (&S)[RGT][D / 16], const float *s_q,
+                                        const float *s_k, const float *s_v, const float *s_e,
+                                        RecRed<D, NS, RGT> &R, float bt, float scale, int c0,
+                                        int tid, float *core_row, float *o_lds,
+                                        float *u_row = nullptr)
 {
     using Cfg = RecCfg<D, NS, RGT>;
     constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT, NP = Cfg::kPairs;
@@ -112,7 +121,7 @@ __device__ __forceinline__ void rec_row(float4 (&S)[RGT][D / 16], RecLds<D, NS, 
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
             const int i = rgof(j) + RG * r;
-            const float e = L.s_e[i], ki = L.s_k[i], qi = L.s_q[i];
+            const float e = s_e[i], ki = s_k[i], qi = s_q[i];
             S[j][r] = make_float4(S[j][r].x * e, S[j][r].y * e, S[j][r].z * e, S[j][r].w * e);
             pkj[j] = fma4(ki, S[j][r], pkj[j]);
             pqj[j] = fma4(qi, S[j][r], pqj[j]);
@@ -136,22 +145,22 @@ __device__ __forceinline__ void rec_row(float4 (&S)[RGT][D / 16], RecLds<D, NS, 
     }
     const int pr = RGT == 2 ? tr : tr >> 1;   // pair index
     if (RGT == 2 || (tr & 1) == 0) {
-        L.s_red[pr][0][cg] = pk;
-        L.s_red[pr][1][cg] = pq;
-        if (cg == 0) L.s_kq[pr] = kq;
+        R.s_red[pr][0][cg] = pk;
+        R.s_red[pr][1][cg] = pq;
+        if (cg == 0) R.s_kq[pr] = kq;
     }
     __syncthreads();
-    pk = L.s_red[0][0][cg];
-    pq = L.s_red[0][1][cg];
-    kq = L.s_kq[0];
+    pk = R.s_red[0][0][cg];
+    pq = R.s_red[0][1][cg];
+    kq = R.s_kq[0];
 #pragma unroll
     for (int p = 1; p < NP; ++p) {
-        const float4 a = L.s_red[p][0][cg], c = L.s_red[p][1][cg];
+        const float4 a = R.s_red[p][0][cg], c = R.s_red[p][1][cg];
         pk = make_float4(pk.x + a.x, pk.y + a.y, pk.z + a.z, pk.w + a.w);
         pq = make_float4(pq.x + c.x, pq.y + c.y, pq.z + c.z, pq.w + c.w);
-        kq += L.s_kq[p];
+        kq += R.s_kq[p];
     }
-    const float4 v4 = reinterpret_cast<const float4 *>(L.s_v + c0)[cg];
+    const float4 v4 = reinterpret_cast<const float4 *>(s_v + c0)[cg];
     const float4 u = make_float4(bt * (v4.x - pk.x), bt * (v4.y - pk.y),
                                  bt * (v4.z - pk.z), bt * (v4.w - pk.w));
     if ((core_row != nullptr || o_lds != nullptr) && tr == 0) {
@@ -167,7 +176,7 @@ __device__ __forceinline__ void rec_row(float4 (&S)[RGT][D / 16], RecLds<D, NS, 
     for (int j = 0; j < RGT; ++j)
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
-            S[j][r] = fma4(L.s_k[rgof(j) + RG * r], u, S[j][r]);
+            S[j][r] = fma4(s_k[rgof(j) + RG * r], u, S[j][r]);
 }
 
 template <int D, int NS, int RGT>
@@ -222,7 +231,7 @@ __global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_
         const float bt = beta[row * H + h];
         __syncthreads();
 
-        rec_row<D, NS, RGT>(S, L, bt, scale, c0, tid,
+        rec_row<D, NS, RGT>(S, L.s_q, L.s_k, L.s_v, L.s_e, L.red, bt, scale, c0, tid,
                             core != nullptr ? core + (row * H + h) * D + c0 : nullptr, nullptr,
                             wy != nullptr ? wy[b] + ((size_t)h * K + t) * D + c0 : nullptr);
 
@@ -246,108 +255,361 @@ __global__ __launch_bounds__((RecCfg<D, NS, RGT>::kThreads)) void kda_recurrent_
     }
 }
 
-// The block decode's per-head stages for every row, one workgroup per (head
-// h, sequence b) over the whole head (see launch_kda_mixer).  Lanes
-// 0 .. 3D/8 - 1 are the conv lanes: lane i of section i / (D/8) (q, k, v)
-// owns 8 channels of head h and slides their window of pre-conv rows, as a
-// conv_silu_l2 thread does (the head's D/8 lanes of a section adjacent and
-// aligned, so the L2 sum takes the same shuffle tree).  Lanes 0 .. D/8 - 1
-// then normalise the row's output as a gated_rmsnorm thread does.
-template <int D>
-__global__ __launch_bounds__((RecCfg<D, 1, 1>::kThreads)) void kda_mixer_kernel(const MixerArgs a)
+// Entry b of a device table of device pointers, read on the vector-memory
+// path (a buffer load) instead of the scalar one, and kept in vector
+// registers: the read then counts among the wave's vector loads, so the
+// loads issued after it that need no table overlap its latency, and only the
+// loads through the pointer wait for it.
+template <typename T>
+__device__ __forceinline__ T *table_entry(T *const *table, int b)
 {
-    using Cfg = RecCfg<D, 1, 1>;
-    constexpr int CG = Cfg::kCG, RG = Cfg::kRG, RPT = Cfg::kRPT;
-    constexpr int SL = D / 8;   // lanes per section of a head
-    const int h = blockIdx.x, b = blockIdx.y, K = a.K, H = a.H;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T **>(table), (short)0, (b + 1) * (int)sizeof(T *), 0x00020000);
+    const uint2 p = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  r, (unsigned)b * sizeof(T *), 0, 0));
+    return reinterpret_cast<T *>((uint64_t)p.x | ((uint64_t)p.y << 32));
+}
+
+// load_stream through a pointer known to address device memory (a global
+// access rather than a flat one, which the LDS wait counter would also track)
+typedef __attribute__((address_space(1))) floatx4 gfloatx4;
+__device__ __forceinline__ float4 gload_stream(const float *p) {
+    const floatx4 v = __builtin_nontemporal_load((const gfloatx4 *)p);
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void gstore_stream(float *p, const float4 &v) {
+    __builtin_nontemporal_store(floatx4{v.x, v.y, v.z, v.w}, (gfloatx4 *)p);
+}
+
+// The block decode's per-head stages in two launches (see launch_kda_mixer):
+// the mixer, one workgroup per (head h, value-column slice, sequence b), and
+// the tail, one workgroup per (head, sequence).
+//
+// Mixer.  The recurrence of a head splits into NS slices of its value
+// columns with no exchange (as in kda_recurrent_kernel); everything else a
+// slice needs of the head is recomputed in its workgroup: the conv rows of q
+// and k (all D channels: the recurrence reads all key channels, and their L2
+// norm spans the head) and the head's whole log-decay gate.  Every global
+// operand is loaded first — the pointer-table entries of the sequence, then
+// what needs no table (gate weights, conv taps and pre-conv rows), the
+// carried conv rows, the small operands staged in LDS, and last the state
+// slice, which only the recurrence waits for — and then:
+//   1. conv + SiLU + L2 of all K rows at once, a thread per (row, 8
+//      channels): first the q and k sections (the head's D/8 threads of a
+//      section adjacent and aligned, so the L2 sum takes conv_silu_l2's
+//      shuffle tree), then the slice's v channels; rows to LDS;
+//   2. the head's column tiles of the f_b product (the log-decay gate of
+//      every row, kept in LDS as exp(gate)) and the slice's tiles of the g_b
+//      product, formed as dense_gemv_bf16_batchm forms them (kda_gemv.hpp;
+//      with R <= 128 each contraction quarter is one step: quarter q takes
+//      step q), the A operand from LDS;
+//   3. the recurrence row by row (one barrier a row: the key-axis sums of
+//      consecutive rows use two buffers).
+// Buffers the slices share (conv_out, conv snapshots, g_raw and gate) are
+// written by slice 0; the conv state, which every slice reads, is left to the
+// tail.
+//
+// Tail.  The gated RMSNorm of every row (the head's D/8 threads of a row
+// adjacent and aligned, gated_rmsnorm's shuffle tree) and, when the states
+// are written, the conv window moved past the K rows.
+//
+// Each stage runs the per-row code of its own kernel on the same values, so
+// every buffer gets the bits the separate launches write.
+template <int D, int NS>
+struct MixerCfg {
+    using Rec = RecCfg<D, NS, 1>;
+    static constexpr int kThreads = Rec::kThreads;
+    static constexpr int kWaves = kThreads / kWave;
+    static constexpr int kDC = Rec::kDC;                  // value columns of a slice
+    static constexpr int kSL = D / 8;                     // threads per section of a row
+    static constexpr int kVL = kDC / 8;                   // threads for the slice's v channels
+    static constexpr int kFT = D / kGemvColTile;          // f_b tiles (the whole head)
+    static constexpr int kGT = kDC / kGemvColTile;        // g_b tiles (the slice)
+    static constexpr int kTiles = (kFT + kGT) / kWaves;   // per wave
+    static constexpr int kItems = 1;                      // conv items per thread loaded up front
+    static_assert(kThreads % kWave == 0 && kWave % kSL == 0, "sections must not straddle waves");
+    static_assert(kDC % kGemvColTile == 0 && (kFT + kGT) % kWaves == 0, "whole tiles per wave");
+};
+
+template <int D, int NS>
+__global__ __launch_bounds__((MixerCfg<D, NS>::kThreads)) void kda_mixer_kernel(const MixerArgs a)
+{
+    using Cfg = MixerCfg<D, NS>;
+    using Rec = typename Cfg::Rec;
+    constexpr int NT = Cfg::kThreads, NW = Cfg::kWaves, DC = Cfg::kDC, SL = Cfg::kSL;
+    constexpr int VL = Cfg::kVL, FT = Cfg::kFT, TW = Cfg::kTiles, NI = Cfg::kItems;
+    constexpr int CG = Rec::kCG, RG = Rec::kRG, RPT = Rec::kRPT;
+    const int h = blockIdx.x / NS, slice = blockIdx.x % NS, c0 = slice * DC;
+    const int b = blockIdx.y, K = a.K, H = a.H, R = a.R;
     const int tid = threadIdx.x;
     const int cg = tid % CG, tr = tid / CG;
-    const int64_t qkvw = (int64_t)H * D, cd = 3 * qkvw;
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int lr = lane & 15, kg = lane >> 4;
+    const int64_t qkvw = (int64_t)H * D, cd = 3 * qkvw, row0 = (int64_t)b * K;
+    const int nsteps = R >> 5;      // 1 .. 4
+    const bool lead = slice == 0;   // writes what the slices share
 
-    __shared__ RecLds<D, 1, 1> L;
-    __shared__ __align__(16) float s_o[D];
+    __shared__ __align__(16) float s_x[kMixerMaxRows][3][D];    // conv output rows: q, k, v
+    __shared__ __align__(16) float s_e[kMixerMaxRows][D];       // exp(gate)
+    __shared__ __align__(16) uint16_t s_lr[2][kMixerMaxRows * kMixerMaxRank];   // fa, ga [K][R]
+    __shared__ float s_beta[kMixerMaxRows];
+    __shared__ __align__(16) float s_dtb[D];
+    __shared__ float s_rate;
+    __shared__ float s_g[kMixerMaxRows][D + DC];                 // gate products, fp32
+    __shared__ RecRed<D, NS, 1> s_red[2];
 
-    // conv lane: section and channel of its 8 channels
-    const bool conv_lane = tid < 3 * SL;
-    const int section = conv_lane ? tid / SL : 0, li = tid % SL;
-    const int64_t c = section * qkvw + (int64_t)h * D + 8 * li;
-    float wt[8][kConvKC];
-    uint4 win[kConvKC];
-    if (conv_lane) {
-        conv_taps(a.conv_w, c, wt);
-        const uint16_t *st = a.conv_state[b];
+    // --- loads ---
+    float *const Sb = table_entry(a.state, b);
+    const uint16_t *const cst = table_entry(a.conv_state, b);
+
+    // gate weights: the wave's tile j is f_b tile wave + NW j of the head, or
+    // (past FT) a g_b tile of the slice; this lane's row of it, step q
+    auto tile_n0 = [&](int j) {
+        const int t = wave + NW * j;
+        return t < FT ? h * D + kGemvColTile * t : h * D + c0 + kGemvColTile * (t - FT);
+    };
+    uintx4 wb[TW][kGemvQuarters];
 #pragma unroll
-        for (int j = 1; j < kConvKC; ++j) win[j] = gload16(st + (int64_t)j * cd + c);
-        win[0] = make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < TW; ++j) {
+        const bool isf = wave + NW * j < FT;
+        const uint16_t *w = (isf ? a.f_b : a.g_b) + (int64_t)(tile_n0(j) + lr) * R + 8 * kg;
+#pragma unroll
+        for (int q = 0; q < kGemvQuarters; ++q)
+            wb[j][q] = *reinterpret_cast<const uintx4 *>(w + 32 * min(q, nsteps - 1));
     }
 
-    float *__restrict__ Sg = a.state[b] + (size_t)h * D * D;
+    // conv items: i < 2 K SL are (row, q or k, 8 channels), then (row, 8 of
+    // the slice's v channels)
+    const int nqk = 2 * K * SL, nitems = nqk + K * VL;
+    auto item = [&](int i, int &t, int &section, int &ch) {
+        if (i < nqk) {
+            t = i / (2 * SL);
+            section = (i / SL) % 2;
+            ch = 8 * (i % SL);
+        } else {
+            t = (i - nqk) / VL;
+            section = 2;
+            ch = c0 + 8 * ((i - nqk) % VL);
+        }
+    };
+    // window of row t: entries t .. t + 3 of [carried rows 1 .. 3; rows 0 .. K-1]
+    auto load_item = [&](int i, uint4 (&taps)[kConvKC], uint4 (&win)[kConvKC], bool carried) {
+        int t, section, ch;
+        item(i, t, section, ch);
+        const int64_t c = section * qkvw + (int64_t)h * D + ch;
+        if (!carried) conv_taps_load(a.conv_w, c, taps);
+#pragma unroll
+        for (int jj = 0; jj < kConvKC; ++jj) {
+            const int e = t + jj;
+            if (carried && e < kConvKC - 1) win[jj] = gload16(cst + (int64_t)(e + 1) * cd + c);
+            if (!carried && e >= kConvKC - 1)
+                win[jj] = *reinterpret_cast<const uint4 *>(a.x + (row0 + e - (kConvKC - 1)) * a.ldx + c);
+        }
+    };
+    uint4 taps[NI][kConvKC], win[NI][kConvKC];
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+        if (tid + NT * u < nitems) load_item(tid + NT * u, taps[u], win[u], false);
+
+    // the carried conv rows (through the table)
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+        if (tid + NT * u < nitems) load_item(tid + NT * u, taps[u], win[u], true);
+    // fa and ga rows, beta, dt_bias and a_log of the head to LDS (their wait
+    // is the one the conv below needs anyway)
+    const int nlr = 2 * K * (R / 8);   // 16-byte pieces
+    for (int i = tid; i < nlr; i += NT) {
+        const int which = i / (K * (R / 8)), e = i % (K * (R / 8));
+        *reinterpret_cast<uint4 *>(&s_lr[which][8 * e]) =
+            *reinterpret_cast<const uint4 *>((which == 0 ? a.fa : a.ga) + row0 * R + 8 * e);
+    }
+    if (tid < D / 4)
+        reinterpret_cast<float4 *>(s_dtb)[tid] =
+            *reinterpret_cast<const float4 *>(a.dt_bias + (int64_t)h * D + 4 * tid);
+    else if (tid < D / 4 + K)
+        s_beta[tid - D / 4] = a.beta[(row0 + tid - D / 4) * H + h];
+    else if (tid == D / 4 + K)
+        s_rate = decay_rate(a.a_log[h]);
+    // the state slice last: not needed before the recurrence, so the waits
+    // above do not cover it
+    float *__restrict__ Sg = Sb + (size_t)h * D * D + c0;
     float4 S[1][RPT];
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) S[0][r] = load_stream(Sg + (size_t)(tr + RG * r) * D + 4 * cg);
+    for (int r = 0; r < RPT; ++r) S[0][r] = gload_stream(Sg + (size_t)(tr + RG * r) * D + 4 * cg);
 
-    for (int t = 0; t < K; ++t) {
-        const int64_t row = (int64_t)b * K + t;
-        if (conv_lane) {
-#pragma unroll
-            for (int j = 0; j + 1 < kConvKC; ++j) win[j] = win[j + 1];
-            win[kConvKC - 1] = *reinterpret_cast<const uint4 *>(a.x + row * a.ldx + c);
-            const uint4 packed = conv_row<SL>(win, wt, section < 2, a.eps_l2);
-            *reinterpret_cast<uint4 *>(a.y + row * a.ldy + c) = packed;
+    // --- 1. conv of every row ---
+    auto conv_item = [&](int i, const uint4 (&tp)[kConvKC], const uint4 (&wn)[kConvKC]) {
+        int t, section, ch;
+        item(i, t, section, ch);
+        const int64_t c = section * qkvw + (int64_t)h * D + ch;
+        float wt[8][kConvKC];
+        conv_taps_unpack(tp, wt);
+        const uint4 packed = conv_row<SL>(wn, wt, section < 2, a.eps_l2);
+        if (lead || section == 2) {
+            *reinterpret_cast<uint4 *>(a.y + (row0 + t) * a.ldy + c) = packed;
             if (a.conv_snap != nullptr && t + 1 < K) {
                 uint16_t *dst = a.conv_snap[(int64_t)b * (K - 1) + t];
 #pragma unroll
-                for (int j = 0; j < kConvKC; ++j) gstore16(dst + (int64_t)j * cd + c, win[j]);
+                for (int jj = 0; jj < kConvKC; ++jj) gstore16(dst + (int64_t)jj * cd + c, wn[jj]);
             }
-            float f[8];
-            unpack8(packed, f);
-            float *dst = section == 0 ? L.s_q : section == 1 ? L.s_k : L.s_v;
-            reinterpret_cast<float4 *>(dst + 8 * li)[0] = make_float4(f[0], f[1], f[2], f[3]);
-            reinterpret_cast<float4 *>(dst + 8 * li)[1] = make_float4(f[4], f[5], f[6], f[7]);
         }
-        for (int i = tid; i < D; i += Cfg::kThreads)
-            L.s_e[i] = exp2_fast(a.gate[(row * H + h) * D + i] * kLog2e);
-        const float bt = a.beta[row * H + h];
-        __syncthreads();
+        float f[8];
+        unpack8(packed, f);
+        float *dst = &s_x[t][section][ch];
+        reinterpret_cast<float4 *>(dst)[0] = make_float4(f[0], f[1], f[2], f[3]);
+        reinterpret_cast<float4 *>(dst)[1] = make_float4(f[4], f[5], f[6], f[7]);
+    };
+    // whole q / k sections per pass (nqk and NT are multiples of SL)
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+        if (tid + NT * u < nitems) conv_item(tid + NT * u, taps[u], win[u]);
+    for (int i0 = NI * NT; i0 < nitems; i0 += NT) {   // more than NI items per thread
+        const int i = i0 + tid;
+        if (i >= nitems) break;
+        load_item(i, taps[0], win[0], false);
+        load_item(i, taps[0], win[0], true);
+        conv_item(i, taps[0], win[0]);
+    }
+    __syncthreads();
 
-        rec_row<D, 1, 1>(S, L, bt, a.scale, 0, tid, a.core + (row * H + h) * D, s_o);
+    // --- 2. the gate tiles (independent products; rows past K of the A
+    // operand are whatever LDS holds: a row only meets its own output row),
+    // then each (row, column) of them by one thread through LDS: f_b with
+    // the log-decay gate from its bf16 value (as the f_b product's epilogue
+    // forms it), g_b (out_gate) ---
+    {
+        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+        uintx4 xa[2][kGemvQuarters];
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+#pragma unroll
+            for (int q = 0; q < kGemvQuarters; ++q)
+                xa[w][q] = *reinterpret_cast<const uintx4 *>(
+                    &s_lr[w][lr * R + 32 * min(q, nsteps - 1) + 8 * kg]);
+        floatx4 tot[TW];
+        auto product = [&](int j, int q) {
+            return mfma_bf16(__builtin_bit_cast(bf16x8, xa[wave + NW * j < FT ? 0 : 1][q]),
+                             __builtin_bit_cast(bf16x8, wb[j][q]), zero);
+        };
+        if (nsteps == kGemvQuarters) {   // R = 128: a step in every quarter
+#pragma unroll
+            for (int j = 0; j < TW; ++j) {
+                floatx4 p[kGemvQuarters];
+#pragma unroll
+                for (int q = 0; q < kGemvQuarters; ++q) p[q] = product(j, q);
+                tot[j] = ((p[0] + p[1]) + p[2]) + p[3];
+            }
+        } else {                         // the quarters past the last step add zeros
+#pragma unroll
+            for (int j = 0; j < TW; ++j) {
+                tot[j] = product(j, 0);
+#pragma unroll
+                for (int q = 1; q < kGemvQuarters; ++q)
+                    tot[j] = tot[j] + (q < nsteps ? product(j, q) : zero);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < TW; ++j) {
+            // rows 4 kg + i, column lr of the tile (column of the head: f_b
+            // tiles first, then the slice's g_b tiles)
+            const int col = kGemvColTile * (wave + NW * j) + lr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * kg + i < K) s_g[4 * kg + i][col] = tot[j][i];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < K * (D + DC); i += NT) {
+        const int ml = i / (D + DC), col = i % (D + DC);
+        const bool isf = col < D;
+        const int n = h * D + (isf ? col : c0 + col - D);
+        const int64_t o = (row0 + ml) * qkvw + n;
+        const uint32_t u = f32_to_bf16(s_g[ml][col]);
+        if (isf) {
+            const float gv = log_decay(bf16_to_f32(u), s_dtb[col], s_rate);
+            if (lead) {
+                a.g_raw[o] = (uint16_t)u;
+                a.gate[o] = gv;
+            }
+            s_e[ml][col] = exp2_fast(gv * kLog2e);
+        } else {
+            a.out_gate[o] = (uint16_t)u;
+        }
+    }
+    __syncthreads();
+
+    // --- 3. the recurrence ---
+    for (int t = 0; t < K; ++t) {
+        const int64_t row = row0 + t;
+        rec_row<D, NS, 1>(S, s_x[t][0], s_x[t][1], s_x[t][2], s_e[t], s_red[t & 1], s_beta[t],
+                          a.scale, c0, tid, a.core + (row * H + h) * D + c0, nullptr,
+                          a.wy != nullptr ? a.wy[b] + ((size_t)h * K + t) * D + c0 : nullptr);
         if (a.snap != nullptr && t + 1 < K) {
-            float *__restrict__ Sn = a.snap[(size_t)b * (K - 1) + t] + (size_t)h * D * D;
+            float *__restrict__ Sn = a.snap[(size_t)b * (K - 1) + t] + (size_t)h * D * D + c0;
 #pragma unroll
             for (int r = 0; r < RPT; ++r)
-                store_stream(Sn + (size_t)(tr + RG * r) * D + 4 * cg, S[0][r]);
-        }
-        __syncthreads();   // the row's output complete; LDS is rewritten by the next row
-        if (tid < SL) {
-            const float4 lo = reinterpret_cast<const float4 *>(s_o)[2 * tid];
-            const float4 hi = reinterpret_cast<const float4 *>(s_o)[2 * tid + 1];
-            const float xv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            const int64_t o0 = row * qkvw + (int64_t)h * D + 8 * tid;
-            *reinterpret_cast<uint4 *>(a.out + o0) = gated_norm8<D>(
-                xv, *reinterpret_cast<const uint4 *>(a.out_gate + o0),
-                *reinterpret_cast<const uint4 *>(a.norm_w + 8 * tid), a.eps_rms);
+                gstore_stream(Sn + (size_t)(tr + RG * r) * D + 4 * cg, S[0][r]);
         }
     }
 
     if (a.write_state) {
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) store_stream(Sg + (size_t)(tr + RG * r) * D + 4 * cg, S[0][r]);
-        if (conv_lane) {
-            uint16_t *dst = a.conv_state[b];
+        for (int r = 0; r < RPT; ++r) gstore_stream(Sg + (size_t)(tr + RG * r) * D + 4 * cg, S[0][r]);
+    }
+}
+
+constexpr int kTailThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kTailThreads) void kda_mixer_tail_kernel(const MixerArgs a)
+{
+    constexpr int SL = D / 8;
+    const int h = blockIdx.x, b = blockIdx.y, K = a.K, H = a.H;
+    const int64_t qkvw = (int64_t)H * D, cd = 3 * qkvw, row0 = (int64_t)b * K;
+    // gated RMSNorm of every row (whole rows per pass: kTailThreads % SL == 0)
+    const uint4 nw = *reinterpret_cast<const uint4 *>(a.norm_w + 8 * (threadIdx.x % SL));
+    for (int i = threadIdx.x; i < K * SL; i += kTailThreads) {
+        const int t = i / SL, l = i % SL;
+        const int64_t o0 = (row0 + t) * qkvw + (int64_t)h * D + 8 * l;
+        const float4 lo = *reinterpret_cast<const float4 *>(a.core + o0);
+        const float4 hi = *reinterpret_cast<const float4 *>(a.core + o0 + 4);
+        const float xv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        *reinterpret_cast<uint4 *>(a.out + o0) = gated_norm8<D>(
+            xv, *reinterpret_cast<const uint4 *>(a.out_gate + o0), nw, a.eps_rms);
+    }
+    // the conv window after the K rows: entries K-1 .. K+2 of [carried rows
+    // 1 .. 3; rows 0 .. K-1], read whole before any is written
+    if (a.write_state) {
+        uint16_t *__restrict__ st = a.conv_state[b];
+        for (int i = threadIdx.x; i < 3 * SL; i += kTailThreads) {
+            const int64_t c = (i / SL) * qkvw + (int64_t)h * D + 8 * (i % SL);
+            uint4 win[kConvKC];
 #pragma unroll
-            for (int j = 0; j < kConvKC; ++j) gstore16(dst + (int64_t)j * cd + c, win[j]);
+            for (int jj = 0; jj < kConvKC; ++jj) {
+                const int e = K - 1 + jj;
+                win[jj] = e < kConvKC - 1 ? gload16(st + (int64_t)(e + 1) * cd + c)
+                                          : *reinterpret_cast<const uint4 *>(
+                                                a.x + (row0 + e - (kConvKC - 1)) * a.ldx + c);
+            }
+#pragma unroll
+            for (int jj = 0; jj < kConvKC; ++jj) gstore16(st + (int64_t)jj * cd + c, win[jj]);
         }
     }
 }
 
 hipError_t launch_kda_mixer(const MixerArgs &a, int B, int head_dim, hipStream_t stream)
 {
-    if (head_dim == 128)
-        hipLaunchKernelGGL(kda_mixer_kernel<128>, dim3(a.H, B), dim3(RecCfg<128, 1, 1>::kThreads),
-                           0, stream, a);
-    else
-        hipLaunchKernelGGL(kda_mixer_kernel<16>, dim3(a.H, B), dim3(RecCfg<16, 1, 1>::kThreads),
-                           0, stream, a);
+    if (head_dim == 128) {
+        hipLaunchKernelGGL((kda_mixer_kernel<128, 2>), dim3(a.H * 2, B),
+                           dim3(MixerCfg<128, 2>::kThreads), 0, stream, a);
+        hipLaunchKernelGGL(kda_mixer_tail_kernel<128>, dim3(a.H, B), dim3(kTailThreads), 0,
+                           stream, a);
+    } else {
+        hipLaunchKernelGGL((kda_mixer_kernel<16, 1>), dim3(a.H, B),
+                           dim3(MixerCfg<16, 1>::kThreads), 0, stream, a);
+        hipLaunchKernelGGL(kda_mixer_tail_kernel<16>, dim3(a.H, B), dim3(kTailThreads), 0,
+                           stream, a);
+    }
     return hipGetLastError();
 }
 

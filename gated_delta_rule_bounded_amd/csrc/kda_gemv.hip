@@ -22,13 +22,14 @@
 // segments (the front projections of a KDA block all read the same hidden
 // rows).
 #include "kda_device.hpp"
+#include "kda_gemv.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 namespace {
 
-constexpr int kColTile = 16;  // output columns per workgroup
-constexpr int kWaves = 4;
+constexpr int kColTile = kGemvColTile;   // output columns per workgroup
+constexpr int kWaves = kGemvQuarters;    // one wave per contraction quarter
 
 struct Seg {
     const uint16_t *x;
@@ -59,31 +60,6 @@ struct Args {
     int32_t nseg;
     int32_t M;
 };
-
-// Visit order of a wave's contraction steps.  Wave w owns the contiguous
-// steps [beg, beg + cnt) and visits them starting at beg + rho, wrapping
-// around, rho = 12 x (column tile) mod cnt: the workgroups in flight read
-// different parts of their weight rows rather than all the same offset.  The
-// order depends on the column tile and the wave alone (not on M, and not on
-// how many steps a kernel instance loads at once), so every instance
-// accumulates an element in the same order.
-struct Visit {
-    int beg, cnt, rho;
-    __device__ __forceinline__ int step(int v) const {   // v-th visited step, v < 2 cnt
-        const int q = rho + v;
-        return beg + (q >= cnt ? q - cnt : q);
-    }
-};
-
-__device__ __forceinline__ Visit visit_of(int wave, int nsteps, int tile)
-{
-    const int per = (nsteps + kWaves - 1) / kWaves;
-    Visit vs;
-    vs.beg = min(wave * per, nsteps);
-    vs.cnt = min(vs.beg + per, nsteps) - vs.beg;
-    vs.rho = vs.cnt > 0 ? (12 * tile) % vs.cnt : 0;
-    return vs;
-}
 
 // Operands of SIF contraction steps (the wave's visited steps v0 .. v0 +
 // SIF - 1) for RT row tiles.  Every load is issued unconditionally, so the
@@ -126,7 +102,7 @@ template <int RT, int SIF>
 __device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *__restrict__ w,
                                            const int64_t (&wrow)[SIF], int lane,
                                            __amdgpu_buffer_rsrc_t xr, const uint32_t (&xoff)[RT],
-                                           const Visit &vs, int v0)
+                                           const GemvVisit &vs, int v0)
 {
     constexpr int CPR = 4 * SIF;   // 16-byte chunks per row in a stage
     const int c = lane % CPR;
@@ -155,7 +131,7 @@ __device__ __forceinline__ void put_stage(const Stage<RT, SIF> &S, WRows<SIF> &L
 
 template <int RT, int SIF>
 __device__ __forceinline__ void mma_stage(const Stage<RT, SIF> &S, const WRows<SIF> &L,
-                                          floatx4 (&acc)[RT], const Visit &vs, int v0, int r,
+                                          floatx4 (&acc)[RT], const GemvVisit &vs, int v0, int r,
                                           int kg)
 {
 #pragma unroll
@@ -216,7 +192,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const Visit vs = visit_of(wave, nsteps, n0 / kColTile);
+    const GemvVisit vs = gemv_visit(wave, nsteps, n0 / kColTile);
     if (vs.cnt > 0) {
         WRows<SIF> &L = s_w[wave];
         Stage<RT, SIF> A, B;

@@ -68,12 +68,18 @@ hipError_t launch_kda_fold_wy(const uint16_t *qkv, int64_t ldqkv, const float *g
                               int B, int K, int heads, int head_dim, int32_t *status,
                               hipStream_t stream);
 
-// The block decode's per-head stages in one kernel: for each of the K rows
-// of every sequence, conv + SiLU + L2 of the head's q | k | v channels, the
-// recurrence over the whole head, and the gated RMSNorm of its output — the
-// per-row code of conv_silu_l2, kda_recurrent and gated_rmsnorm, so every
-// buffer gets the bits those three launches would write.  write_state false
-// (a verify): neither state is written and no snapshots are taken.
+// The block decode's per-head stages in two launches: for each sequence,
+// the head's columns of the two rank-R products (f_b from fa with the
+// log-decay gate in its epilogue, g_b from ga), then for each of its K rows
+// conv + SiLU + L2 of the head's q | k | v channels and the recurrence (one
+// workgroup per value-column slice of the head), then the gated RMSNorm of
+// every output row and the conv window moved past the rows — the
+// accumulation order of dense_gemv_bf16_batchm and the per-row code of
+// conv_silu_l2, kda_recurrent and gated_rmsnorm, so every buffer gets the
+// bits those launches would write.  write_state false (a verify): neither
+// state is written and no snapshots are taken.
+constexpr int kMixerMaxRows = 16;    // K of a fused call (its gates are held in LDS)
+constexpr int kMixerMaxRank = 128;   // R of a fused call (one contraction step per quarter)
 struct MixerArgs {
     const uint16_t *x;              // pre-conv rows [B*K, ldx] (q | k | v)
     int64_t ldx;
@@ -82,15 +88,20 @@ struct MixerArgs {
     uint16_t *const *conv_snap;     // per (sequence, row < K-1), or nullptr
     uint16_t *y;                    // conv_out rows [B*K, ldy]
     int64_t ldy;
-    const float *gate;              // [B*K, H, D]
+    const uint16_t *fa, *ga;        // low-rank inputs [B*K, R]
+    const uint16_t *f_b, *g_b;      // [H*D, R]
+    const float *a_log, *dt_bias;   // [H], [H*D]
+    uint16_t *g_raw;                // [B*K, H*D] (f_b product, bf16)
+    float *gate;                    // [B*K, H, D] (log-decay gate of g_raw)
     const float *beta;              // [B*K, H]
     float *const *state;            // per sequence [H, D, D]
     float *const *snap;             // per (sequence, row < K-1), or nullptr
+    float *const *wy;               // per sequence [H, K, D] rows u, or nullptr
     float *core;                    // [B*K, H*D]
-    const uint16_t *out_gate;       // [B*K, H*D]
+    uint16_t *out_gate;             // [B*K, H*D] (g_b product, bf16)
     const uint16_t *norm_w;         // [D]
     uint16_t *out;                  // o_norm_out [B*K, H*D]
-    int K, H;
+    int K, H, R;
     float scale, eps_l2, eps_rms;
     bool write_state;
 };

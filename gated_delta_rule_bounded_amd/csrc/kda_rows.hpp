@@ -9,18 +9,31 @@ namespace kda {
 
 constexpr int kConvKC = 4;   // conv taps (the "Glm5NextKdaWeights" page, conv: [conv_dim, 4])
 
-// The taps of channels c0 .. c0 + 7: wt[e][j] = w[c0 + e][j].
-__device__ __forceinline__ void conv_taps(const uint16_t *__restrict__ w, int64_t c0,
-                                          float (&wt)[8][kConvKC])
+// The taps of channels c0 .. c0 + 7: wt[e][j] = w[c0 + e][j], as loaded
+// (four 16-byte pieces) and unpacked.
+__device__ __forceinline__ void conv_taps_load(const uint16_t *__restrict__ w, int64_t c0,
+                                               uint4 (&raw)[kConvKC])
 {
     const uint4 *wp = reinterpret_cast<const uint4 *>(w + c0 * kConvKC);
+#pragma unroll
+    for (int p = 0; p < kConvKC; ++p) raw[p] = wp[p];
+}
+__device__ __forceinline__ void conv_taps_unpack(const uint4 (&raw)[kConvKC], float (&wt)[8][kConvKC])
+{
     float f[8];
 #pragma unroll
     for (int p = 0; p < kConvKC; ++p) {
-        unpack8(wp[p], f);   // channels 2p, 2p+1, each kConvKC taps
+        unpack8(raw[p], f);   // channels 2p, 2p+1, each kConvKC taps
 #pragma unroll
         for (int e = 0; e < 8; ++e) wt[(p * 8 + e) / kConvKC][(p * 8 + e) % kConvKC] = f[e];
     }
+}
+__device__ __forceinline__ void conv_taps(const uint16_t *__restrict__ w, int64_t c0,
+                                          float (&wt)[8][kConvKC])
+{
+    uint4 raw[kConvKC];
+    conv_taps_load(w, c0, raw);
+    conv_taps_unpack(raw, wt);
 }
 
 // One row of conv + SiLU + (q and k sections) L2 for this lane's 8

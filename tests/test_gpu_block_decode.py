@@ -210,6 +210,7 @@ def test_block_decode_k_small_against_oracle(orc, B, K, H, D, hidden, rank):
     (3, 4, 2, 16, 128, 32),
     (2, 5, 2, 128, 256, 32),
     (5, 4, 2, 128, 256, 32),     # 20 verify rows against 5-row steps: two kernel instances
+    (1, 17, 2, 16, 128, 32),     # the four-launch path against fused single rows
 ])
 def test_block_decode_k_bitwise_equals_serial_decodes(B, K, H, D, hidden, rank):
     x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1201 + K)
@@ -224,12 +225,18 @@ def test_block_decode_k_bitwise_equals_serial_decodes(B, K, H, D, hidden, rank):
     (3, 4, 2, 16, 128, 32),
     (2, 5, 4, 128, 256, 32),
     (2, 1, 4, 128, 256, 32),
+    (1, 3, 2, 128, 256, 96),     # rank 96: three contraction steps, one quarter empty
+    (1, 4, 2, 128, 256, 224),    # rank 224: uneven quarters, the four-launch path
+    (2, 16, 2, 16, 128, 64),     # the most rows the fused kernel takes
+    (1, 17, 2, 16, 128, 32),     # one more: the four-launch path
+    (65, 2, 2, 16, 128, 32),     # 130 (sequence, head) pairs: the four-launch path
 ])
 def test_block_decode_k_stages_equal_standalone_kernels(B, K, H, D, hidden, rank):
-    """The block decode runs conv + SiLU + L2, the recurrence and the gated
-    RMSNorm of each (head, sequence) in one kernel; its buffers and states
-    must be the bits of conv_silu_l2, kda_decode_k and gated_rmsnorm run one
-    after the other on the block's own projection outputs."""
+    """The block decode runs the rank-R gate products, conv + SiLU + L2, the
+    recurrence and the gated RMSNorm of each (head, sequence) in one kernel;
+    its buffers and states must be the bits of dense_gemv_bf16_batchm,
+    kda_gate, conv_silu_l2, kda_decode_k and gated_rmsnorm run one after the
+    other on the block's own projection outputs."""
     x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1251 + K)
     scale = D ** -0.5
     dev = torch.device("cuda")
@@ -253,6 +260,15 @@ def test_block_decode_k_stages_equal_standalone_kernels(B, K, H, D, hidden, rank
                            heads=H, head_dim=D, rank=rank, scale=scale, snap=tab(snaps),
                            conv_snap=tab(csnaps))
     states2, convs2, snaps2, csnaps2 = fresh()
+    M, qkv = B * K, H * D
+    g_raw = torch.empty_like(buf["g_raw"])
+    kda.dense_gemv_bf16_batchm(buf["fa"], wd["f_b"], g_raw, M=M, N=qkv, Kd=rank)
+    out_gate = torch.empty_like(buf["out_gate"])
+    kda.dense_gemv_bf16_batchm(buf["ga"], wd["g_b"], out_gate, M=M, N=qkv, Kd=rank)
+    gate = torch.empty_like(buf["gate"])
+    beta = torch.empty_like(buf["beta"])
+    kda.kda_gate(g_raw, wd["a_log"], wd["dt_bias"], gate, T=M, heads=H, head_dim=D,
+                 b_raw=buf["b_raw"], beta=beta)
     y = torch.empty_like(buf["conv_out"])
     kda.conv_silu_l2(buf["qkv_proj"], wd["conv"], y, n_seq=B, rows=K, heads=H, head_dim=D,
                      conv_state=kda.ptr_table(convs2), conv_snap=tab(csnaps2))
@@ -262,6 +278,10 @@ def test_block_decode_k_stages_equal_standalone_kernels(B, K, H, D, hidden, rank
     onorm = torch.empty_like(buf["o_norm_out"])
     kda.gated_rmsnorm(core, buf["out_gate"], wd["o_norm"], onorm, T=B * K, heads=H, head_dim=D)
     torch.cuda.synchronize()
+    assert torch.equal(g_raw, buf["g_raw"])
+    assert torch.equal(out_gate, buf["out_gate"])
+    assert torch.equal(gate, buf["gate"])
+    assert torch.equal(beta, buf["beta"])
     assert torch.equal(y, buf["conv_out"])
     assert torch.equal(core, buf["core"])
     assert torch.equal(onorm, buf["o_norm_out"])
@@ -342,6 +362,7 @@ def test_block_write_on_accept_equals_snapshots(B, K, H, D, hidden, rank):
     (6, 4, 2, 128, 256, 32),
     (1, 4, 32, 128, 4096, 128),
     (2, 1, 2, 128, 256, 32),
+    (65, 2, 2, 16, 128, 32),     # 130 (sequence, head) pairs: the four-launch path
 ])
 def test_block_write_on_accept_table_form(B, K, H, D, hidden, rank):
     """The block's write-on-accept in table form ("Glm5NextLayer" page, the
@@ -349,8 +370,7 @@ def test_block_write_on_accept_table_form(B, K, H, D, hidden, rank):
     buffers and output are bitwise those of kda_block_decode_k and no state
     is written; folding n_accept rows from the u rows leaves the recurrent
     state equal to decode_k's snapshot after that row up to rounding and the
-    conv state bitwise equal to it; 0 rows leave both untouched.  K = 1 takes
-    the unfused stage kernels (the one-token fused kernel writes no table)."""
+    conv state bitwise equal to it; 0 rows leave both untouched."""
     x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1801 + B, w_std=0.05 if hidden < 4096 else 0.02)
     scale = D ** -0.5
     ref = _gpu_decode_k(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)

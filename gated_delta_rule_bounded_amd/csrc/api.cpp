@@ -846,11 +846,11 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
     };
     const kda::GemvSeg back[] = {{b->o_norm_out, w->o_proj, out, qkv, hs, hs, qk}};
     // The rank-R gate products, conv + SiLU + L2, the recurrence and the
-    // gated RMSNorm: for up to 16 rows of few sequences at rank <= 128 in
-    // two launches (a workgroup per value-column slice of each (head,
-    // sequence), then one per (head, sequence) for the norm and the conv
-    // window), the same bits as the four launches otherwise taken.  A verify
-    // writes neither state nor snapshots.
+    // gated RMSNorm: for up to 16 rows of few sequences at rank <= 128 in one
+    // kernel per (head, sequence), the same bits as the four launches
+    // otherwise taken (where the recurrence can split a head's columns over
+    // several workgroups; the fused kernel owns its head's whole conv window
+    // and norm).  A verify writes neither state nor snapshots.
     const bool fuse_mixer = K <= kda::kMixerMaxRows && rank <= kda::kMixerMaxRank &&
                             (int64_t)B * heads <= 128;
     kda::MixerArgs mixer{};

@@ -281,259 +281,246 @@ __device__ __forceinline__ void gstore_stream(float *p, const float4 &v) {
     __builtin_nontemporal_store(floatx4{v.x, v.y, v.z, v.w}, (gfloatx4 *)p);
 }
 
-// The block decode's per-head stages in two launches (see launch_kda_mixer):
-// the mixer, one workgroup per (head h, value-column slice, sequence b), and
-// the tail, one workgroup per (head, sequence).
-//
-// Mixer.  The recurrence of a head splits into NS slices of its value
-// columns with no exchange (as in kda_recurrent_kernel); everything else a
-// slice needs of the head is recomputed in its workgroup: the conv rows of q
-// and k (all D channels: the recurrence reads all key channels, and their L2
-// norm spans the head) and the head's whole log-decay gate.  Every global
-// operand is loaded first — the pointer-table entries of the sequence, then
-// what needs no table (gate weights, conv taps and pre-conv rows), the
-// carried conv rows, the small operands staged in LDS, and last the state
-// slice, which only the recurrence waits for — and then:
-//   1. conv + SiLU + L2 of all K rows at once, a thread per (row, 8
-//      channels): first the q and k sections (the head's D/8 threads of a
-//      section adjacent and aligned, so the L2 sum takes conv_silu_l2's
-//      shuffle tree), then the slice's v channels; rows to LDS;
-//   2. the head's column tiles of the f_b product (the log-decay gate of
-//      every row, kept in LDS as exp(gate)) and the slice's tiles of the g_b
-//      product, formed as dense_gemv_bf16_batchm forms them (kda_gemv.hpp;
-//      with R <= 128 each contraction quarter is one step: quarter q takes
-//      step q), the A operand from LDS;
+// The block decode's per-head stages, one workgroup per (head h, sequence b)
+// over the whole head (see launch_kda_mixer).  Every global operand is
+// loaded first — the pointer-table entries of the sequence (state, conv
+// window, u rows, snapshots), then what needs no table (gate weights, conv
+// taps and pre-conv rows, fa and ga rows, the gate constants, beta), then the
+// carried conv rows and last the state, which only the recurrence waits for.
+// Every load is issued whatever the thread's item (indices clamped to ones
+// that exist, unused values dropped), so that the compiler can count the
+// loads in flight exactly and wait for each group alone: a load issued
+// under a branch makes it wait for everything issued before.  Then:
+//   1. conv + SiLU + L2 of all K rows at once, a thread per (row, section q,
+//      k or v, 8 channels), the head's D/8 threads of a section adjacent and
+//      aligned so the L2 sum takes conv_silu_l2's shuffle tree; rows to LDS;
+//   2. wave w forms column tile w of the head in the f_b product and in the
+//      g_b product as dense_gemv_bf16_batchm forms them (kda_gemv.hpp; with
+//      R <= 128 each contraction quarter is one step: quarter q takes step
+//      q), the A operand (fa or ga rows) from LDS; then a thread per (row,
+//      column) rounds them: g_raw with the log-decay gate of its bf16 value
+//      (as the f_b product's epilogue forms it, kept in LDS as exp(gate)),
+//      out_gate;
 //   3. the recurrence row by row (one barrier a row: the key-axis sums of
-//      consecutive rows use two buffers).
-// Buffers the slices share (conv_out, conv snapshots, g_raw and gate) are
-// written by slice 0; the conv state, which every slice reads, is left to the
-// tail.
-//
-// Tail.  The gated RMSNorm of every row (the head's D/8 threads of a row
-// adjacent and aligned, gated_rmsnorm's shuffle tree) and, when the states
-// are written, the conv window moved past the K rows.
-//
+//      consecutive rows use two buffers), outputs kept in LDS;
+//   4. the gated RMSNorm of all K rows at once (the head's D/8 threads of a
+//      row adjacent and aligned, gated_rmsnorm's shuffle tree), and, when
+//      the states are written, the conv window moved past the K rows.
 // Each stage runs the per-row code of its own kernel on the same values, so
-// every buffer gets the bits the separate launches write.
-template <int D, int NS>
+// every buffer gets the bits those launches write.
+template <int D>
 struct MixerCfg {
-    using Rec = RecCfg<D, NS, 1>;
+    using Rec = RecCfg<D, 1, 1>;
     static constexpr int kThreads = Rec::kThreads;
     static constexpr int kWaves = kThreads / kWave;
-    static constexpr int kDC = Rec::kDC;                  // value columns of a slice
-    static constexpr int kSL = D / 8;                     // threads per section of a row
-    static constexpr int kVL = kDC / 8;                   // threads for the slice's v channels
-    static constexpr int kFT = D / kGemvColTile;          // f_b tiles (the whole head)
-    static constexpr int kGT = kDC / kGemvColTile;        // g_b tiles (the slice)
-    static constexpr int kTiles = (kFT + kGT) / kWaves;   // per wave
-    static constexpr int kItems = 1;                      // conv items per thread loaded up front
+    static constexpr int kSL = D / 8;                  // threads per section of a row
+    static constexpr int kCL = 3 * kSL;                // conv threads per row
+    static constexpr int kTiles = D / kGemvColTile;    // column tiles per product
+    static constexpr int kLR = kMixerMaxRank + 8;      // LDS row stride of fa, ga (elements)
     static_assert(kThreads % kWave == 0 && kWave % kSL == 0, "sections must not straddle waves");
-    static_assert(kDC % kGemvColTile == 0 && (kFT + kGT) % kWaves == 0, "whole tiles per wave");
+    static_assert(kTiles == kWaves, "one column tile of each product per wave");
 };
 
-template <int D, int NS>
-__global__ __launch_bounds__((MixerCfg<D, NS>::kThreads)) void kda_mixer_kernel(const MixerArgs a)
+template <int D>
+__global__ __launch_bounds__((MixerCfg<D>::kThreads)) void kda_mixer_kernel(const MixerArgs a)
 {
-    using Cfg = MixerCfg<D, NS>;
+    using Cfg = MixerCfg<D>;
     using Rec = typename Cfg::Rec;
-    constexpr int NT = Cfg::kThreads, NW = Cfg::kWaves, DC = Cfg::kDC, SL = Cfg::kSL;
-    constexpr int VL = Cfg::kVL, FT = Cfg::kFT, TW = Cfg::kTiles, NI = Cfg::kItems;
+    constexpr int NT = Cfg::kThreads, SL = Cfg::kSL, CL = Cfg::kCL, LR = Cfg::kLR;
     constexpr int CG = Rec::kCG, RG = Rec::kRG, RPT = Rec::kRPT;
-    const int h = blockIdx.x / NS, slice = blockIdx.x % NS, c0 = slice * DC;
-    const int b = blockIdx.y, K = a.K, H = a.H, R = a.R;
+    const int h = blockIdx.x, b = blockIdx.y, K = a.K, H = a.H, R = a.R;
     const int tid = threadIdx.x;
     const int cg = tid % CG, tr = tid / CG;
     const int wave = tid / kWave, lane = tid % kWave;
     const int lr = lane & 15, kg = lane >> 4;
     const int64_t qkvw = (int64_t)H * D, cd = 3 * qkvw, row0 = (int64_t)b * K;
-    const int nsteps = R >> 5;      // 1 .. 4
-    const bool lead = slice == 0;   // writes what the slices share
+    const int nsteps = R >> 5;   // 1 .. 4
 
-    __shared__ __align__(16) float s_x[kMixerMaxRows][3][D];    // conv output rows: q, k, v
-    __shared__ __align__(16) float s_e[kMixerMaxRows][D];       // exp(gate)
-    __shared__ __align__(16) uint16_t s_lr[2][kMixerMaxRows * kMixerMaxRank];   // fa, ga [K][R]
-    __shared__ float s_beta[kMixerMaxRows];
+    __shared__ __align__(16) float s_x[kMixerMaxRows][3][D];   // conv output rows: q, k, v
+    __shared__ __align__(16) float s_e[kMixerMaxRows][D];      // exp(gate)
+    __shared__ __align__(16) float s_o[kMixerMaxRows][D];      // recurrence outputs
+    __shared__ __align__(16) uint16_t s_og[kMixerMaxRows][D];  // out_gate
+    __shared__ __align__(16) uint16_t s_lr[2][kMixerMaxRows * LR];   // fa, ga rows
+    __shared__ float s_g[kMixerMaxRows][2 * D];                 // gate products, fp32
     __shared__ __align__(16) float s_dtb[D];
-    __shared__ float s_rate;
-    __shared__ float s_g[kMixerMaxRows][D + DC];                 // gate products, fp32
-    __shared__ RecRed<D, NS, 1> s_red[2];
+    __shared__ float s_beta[kMixerMaxRows], s_rate;
+    __shared__ float *s_snp[kMixerMaxRows];       // state snapshot after each row but the last
+    __shared__ uint16_t *s_csnp[kMixerMaxRows];   // conv snapshot after each row but the last
+    __shared__ RecRed<D, 1, 1> s_red[2];
 
-    // --- loads ---
+    // --- loads: the pointer-table entries (snapshots of row min(tid, K-2),
+    // staged in LDS for every thread) ---
     float *const Sb = table_entry(a.state, b);
     const uint16_t *const cst = table_entry(a.conv_state, b);
+    float *const wyb = a.wy != nullptr ? table_entry(a.wy, b) : nullptr;
+    const int snap0 = b * (K - 1) + min(tid, max(K - 2, 0));
+    float *const snp = a.snap != nullptr && K > 1 ? table_entry(a.snap, snap0) : nullptr;
+    uint16_t *const csnp = a.conv_snap != nullptr && K > 1 ? table_entry(a.conv_snap, snap0) : nullptr;
 
-    // gate weights: the wave's tile j is f_b tile wave + NW j of the head, or
-    // (past FT) a g_b tile of the slice; this lane's row of it, step q
-    auto tile_n0 = [&](int j) {
-        const int t = wave + NW * j;
-        return t < FT ? h * D + kGemvColTile * t : h * D + c0 + kGemvColTile * (t - FT);
-    };
-    uintx4 wb[TW][kGemvQuarters];
+    // gate weights: column tile `wave` of each product, this lane's row, step
+    // q, in the MFMA operand's layout
+    uintx4 wf[kGemvQuarters], wg[kGemvQuarters];
+    {
+        const int64_t n = (int64_t)h * D + kGemvColTile * wave + lr;
 #pragma unroll
-    for (int j = 0; j < TW; ++j) {
-        const bool isf = wave + NW * j < FT;
-        const uint16_t *w = (isf ? a.f_b : a.g_b) + (int64_t)(tile_n0(j) + lr) * R + 8 * kg;
-#pragma unroll
-        for (int q = 0; q < kGemvQuarters; ++q)
-            wb[j][q] = *reinterpret_cast<const uintx4 *>(w + 32 * min(q, nsteps - 1));
+        for (int q = 0; q < kGemvQuarters; ++q) {
+            const int64_t o = n * R + 32 * min(q, nsteps - 1) + 8 * kg;
+            wf[q] = *reinterpret_cast<const uintx4 *>(a.f_b + o);
+            wg[q] = *reinterpret_cast<const uintx4 *>(a.g_b + o);
+        }
     }
 
-    // conv items: i < 2 K SL are (row, q or k, 8 channels), then (row, 8 of
-    // the slice's v channels)
-    const int nqk = 2 * K * SL, nitems = nqk + K * VL;
-    auto item = [&](int i, int &t, int &section, int &ch) {
-        if (i < nqk) {
-            t = i / (2 * SL);
-            section = (i / SL) % 2;
-            ch = 8 * (i % SL);
-        } else {
-            t = (i - nqk) / VL;
-            section = 2;
-            ch = c0 + 8 * ((i - nqk) % VL);
-        }
+    // conv items: i = (row t, section, 8 channels), row-major; the window of
+    // row t is entries t .. t + 3 of [carried rows 1 .. 3; rows 0 .. K-1]
+    const int nitems = K * CL;
+    auto item = [&](int i, int &t, int &section, int64_t &c) {
+        t = i / CL;
+        section = (i % CL) / SL;
+        c = section * qkvw + (int64_t)h * D + 8 * (i % SL);
     };
-    // window of row t: entries t .. t + 3 of [carried rows 1 .. 3; rows 0 .. K-1]
-    auto load_item = [&](int i, uint4 (&taps)[kConvKC], uint4 (&win)[kConvKC], bool carried) {
-        int t, section, ch;
-        item(i, t, section, ch);
-        const int64_t c = section * qkvw + (int64_t)h * D + ch;
-        if (!carried) conv_taps_load(a.conv_w, c, taps);
+    auto load_x = [&](int i, uint4 (&taps)[kConvKC], uint4 (&xw)[kConvKC]) {
+        int t, section;
+        int64_t c;
+        item(i, t, section, c);
+        conv_taps_load(a.conv_w, c, taps);
 #pragma unroll
         for (int jj = 0; jj < kConvKC; ++jj) {
-            const int e = t + jj;
-            if (carried && e < kConvKC - 1) win[jj] = gload16(cst + (int64_t)(e + 1) * cd + c);
-            if (!carried && e >= kConvKC - 1)
-                win[jj] = *reinterpret_cast<const uint4 *>(a.x + (row0 + e - (kConvKC - 1)) * a.ldx + c);
+            const int e = max(t + jj, kConvKC - 1);
+            xw[jj] = *reinterpret_cast<const uint4 *>(a.x + (row0 + e - (kConvKC - 1)) * a.ldx + c);
         }
     };
-    uint4 taps[NI][kConvKC], win[NI][kConvKC];
+    auto load_carried = [&](int i, uint4 (&cw)[kConvKC - 1]) {
+        int t, section;
+        int64_t c;
+        item(i, t, section, c);
 #pragma unroll
-    for (int u = 0; u < NI; ++u)
-        if (tid + NT * u < nitems) load_item(tid + NT * u, taps[u], win[u], false);
+        for (int jj = 0; jj + 1 < kConvKC; ++jj)
+            cw[jj] = gload16(cst + (int64_t)(min(t + jj, kConvKC - 2) + 1) * cd + c);
+    };
+    const int i0 = min(tid, nitems - 1);
+    uint4 taps[kConvKC], xw[kConvKC], cw[kConvKC - 1];
+    load_x(i0, taps, xw);
 
-    // the carried conv rows (through the table)
-#pragma unroll
-    for (int u = 0; u < NI; ++u)
-        if (tid + NT * u < nitems) load_item(tid + NT * u, taps[u], win[u], true);
-    // fa and ga rows, beta, dt_bias and a_log of the head to LDS (their wait
-    // is the one the conv below needs anyway)
-    const int nlr = 2 * K * (R / 8);   // 16-byte pieces
-    for (int i = tid; i < nlr; i += NT) {
+    // fa and ga rows (one 16-byte piece a thread when that covers them), the
+    // gate constants, beta
+    constexpr int kLrAll = 2 * kMixerMaxRows * kMixerMaxRank / 8;   // pieces at most
+    const int nlr = 2 * K * (R / 8);
+    auto lr_piece = [&](int i) {
         const int which = i / (K * (R / 8)), e = i % (K * (R / 8));
-        *reinterpret_cast<uint4 *>(&s_lr[which][8 * e]) =
-            *reinterpret_cast<const uint4 *>((which == 0 ? a.fa : a.ga) + row0 * R + 8 * e);
-    }
-    if (tid < D / 4)
-        reinterpret_cast<float4 *>(s_dtb)[tid] =
-            *reinterpret_cast<const float4 *>(a.dt_bias + (int64_t)h * D + 4 * tid);
-    else if (tid < D / 4 + K)
-        s_beta[tid - D / 4] = a.beta[(row0 + tid - D / 4) * H + h];
-    else if (tid == D / 4 + K)
-        s_rate = decay_rate(a.a_log[h]);
-    // the state slice last: not needed before the recurrence, so the waits
-    // above do not cover it
-    float *__restrict__ Sg = Sb + (size_t)h * D * D + c0;
+        return (which == 0 ? a.fa : a.ga) + row0 * R + 8 * e;
+    };
+    auto lr_store = [&](int i, const uint4 &v) {
+        const int which = i / (K * (R / 8)), e = i % (K * (R / 8));
+        *reinterpret_cast<uint4 *>(&s_lr[which][(e / (R / 8)) * LR + 8 * (e % (R / 8))]) = v;
+    };
+    uint4 lrv = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (kLrAll <= NT) lrv = *reinterpret_cast<const uint4 *>(lr_piece(min(tid, nlr - 1)));
+    const float4 dtv = *reinterpret_cast<const float4 *>(a.dt_bias + (int64_t)h * D + 4 * (tid % (D / 4)));
+    const float btv = a.beta[(row0 + min(tid, K - 1)) * H + h];
+    const float alog = a.a_log[h];
+    const uint4 nw = *reinterpret_cast<const uint4 *>(a.norm_w + 8 * (tid % SL));
+
+    // through the tables: the carried conv rows, then the state
+    load_carried(i0, cw);
+    float *__restrict__ Sg = Sb + (size_t)h * D * D;
     float4 S[1][RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S[0][r] = gload_stream(Sg + (size_t)(tr + RG * r) * D + 4 * cg);
 
-    // --- 1. conv of every row ---
-    auto conv_item = [&](int i, const uint4 (&tp)[kConvKC], const uint4 (&wn)[kConvKC]) {
-        int t, section, ch;
-        item(i, t, section, ch);
-        const int64_t c = section * qkvw + (int64_t)h * D + ch;
-        float wt[8][kConvKC];
-        conv_taps_unpack(tp, wt);
-        const uint4 packed = conv_row<SL>(wn, wt, section < 2, a.eps_l2);
-        if (lead || section == 2) {
-            *reinterpret_cast<uint4 *>(a.y + (row0 + t) * a.ldy + c) = packed;
-            if (a.conv_snap != nullptr && t + 1 < K) {
-                uint16_t *dst = a.conv_snap[(int64_t)b * (K - 1) + t];
-#pragma unroll
-                for (int jj = 0; jj < kConvKC; ++jj) gstore16(dst + (int64_t)jj * cd + c, wn[jj]);
-            }
-        }
-        float f[8];
-        unpack8(packed, f);
-        float *dst = &s_x[t][section][ch];
-        reinterpret_cast<float4 *>(dst)[0] = make_float4(f[0], f[1], f[2], f[3]);
-        reinterpret_cast<float4 *>(dst)[1] = make_float4(f[4], f[5], f[6], f[7]);
-    };
-    // whole q / k sections per pass (nqk and NT are multiples of SL)
-#pragma unroll
-    for (int u = 0; u < NI; ++u)
-        if (tid + NT * u < nitems) conv_item(tid + NT * u, taps[u], win[u]);
-    for (int i0 = NI * NT; i0 < nitems; i0 += NT) {   // more than NI items per thread
-        const int i = i0 + tid;
-        if (i >= nitems) break;
-        load_item(i, taps[0], win[0], false);
-        load_item(i, taps[0], win[0], true);
-        conv_item(i, taps[0], win[0]);
+    // small operands to LDS
+    if constexpr (kLrAll <= NT) {
+        if (tid < nlr) lr_store(tid, lrv);
+    } else {
+        for (int i = tid; i < nlr; i += NT) lr_store(i, *reinterpret_cast<const uint4 *>(lr_piece(i)));
+    }
+    if (tid < D / 4) reinterpret_cast<float4 *>(s_dtb)[tid] = dtv;
+    if (tid < K) s_beta[tid] = btv;
+    if (tid == 0) s_rate = decay_rate(alog);
+    if (tid + 1 < K) {
+        s_snp[tid] = snp;
+        s_csnp[tid] = csnp;
     }
     __syncthreads();
 
-    // --- 2. the gate tiles (independent products; rows past K of the A
-    // operand are whatever LDS holds: a row only meets its own output row),
-    // then each (row, column) of them by one thread through LDS: f_b with
-    // the log-decay gate from its bf16 value (as the f_b product's epilogue
-    // forms it), g_b (out_gate) ---
+    // --- 1. conv of every row (whole sections per pass: NT % SL == 0) ---
+    auto conv_item = [&](int i, const uint4 (&tp)[kConvKC], const uint4 (&xr)[kConvKC],
+                         const uint4 (&cr)[kConvKC - 1]) {
+        int t, section;
+        int64_t c;
+        item(i, t, section, c);
+        uint4 win[kConvKC];
+#pragma unroll
+        for (int jj = 0; jj < kConvKC; ++jj)
+            win[jj] = jj + 1 < kConvKC && t + jj < kConvKC - 1 ? cr[min(jj, kConvKC - 2)] : xr[jj];
+        float wt[8][kConvKC];
+        conv_taps_unpack(tp, wt);
+        const uint4 packed = conv_row<SL>(win, wt, section < 2, a.eps_l2);
+        *reinterpret_cast<uint4 *>(a.y + (row0 + t) * a.ldy + c) = packed;
+        if (a.conv_snap != nullptr && t + 1 < K) {
+            uint16_t *dst = s_csnp[t];
+#pragma unroll
+            for (int jj = 0; jj < kConvKC; ++jj) gstore16(dst + (int64_t)jj * cd + c, win[jj]);
+        }
+        float f[8];
+        unpack8(packed, f);
+        float *dst = &s_x[t][section][8 * (i % SL)];
+        reinterpret_cast<float4 *>(dst)[0] = make_float4(f[0], f[1], f[2], f[3]);
+        reinterpret_cast<float4 *>(dst)[1] = make_float4(f[4], f[5], f[6], f[7]);
+    };
+    if (tid < nitems) conv_item(tid, taps, xw, cw);
+    for (int i = NT + tid; i < nitems; i += NT) {   // more items than threads
+        load_x(i, taps, xw);
+        load_carried(i, cw);
+        conv_item(i, taps, xw, cw);
+    }
+
+    // --- 2. the gate products (rows past K of the A operand are left zero:
+    // a row only meets its own output row), quarters added in order ---
     {
         const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-        uintx4 xa[2][kGemvQuarters];
+        uintx4 xf[kGemvQuarters] = {}, xg[kGemvQuarters] = {};
+        if (lr < K) {
 #pragma unroll
-        for (int w = 0; w < 2; ++w)
-#pragma unroll
-            for (int q = 0; q < kGemvQuarters; ++q)
-                xa[w][q] = *reinterpret_cast<const uintx4 *>(
-                    &s_lr[w][lr * R + 32 * min(q, nsteps - 1) + 8 * kg]);
-        floatx4 tot[TW];
-        auto product = [&](int j, int q) {
-            return mfma_bf16(__builtin_bit_cast(bf16x8, xa[wave + NW * j < FT ? 0 : 1][q]),
-                             __builtin_bit_cast(bf16x8, wb[j][q]), zero);
-        };
-        if (nsteps == kGemvQuarters) {   // R = 128: a step in every quarter
-#pragma unroll
-            for (int j = 0; j < TW; ++j) {
-                floatx4 p[kGemvQuarters];
-#pragma unroll
-                for (int q = 0; q < kGemvQuarters; ++q) p[q] = product(j, q);
-                tot[j] = ((p[0] + p[1]) + p[2]) + p[3];
-            }
-        } else {                         // the quarters past the last step add zeros
-#pragma unroll
-            for (int j = 0; j < TW; ++j) {
-                tot[j] = product(j, 0);
-#pragma unroll
-                for (int q = 1; q < kGemvQuarters; ++q)
-                    tot[j] = tot[j] + (q < nsteps ? product(j, q) : zero);
+            for (int q = 0; q < kGemvQuarters; ++q) {
+                const int o = lr * LR + 32 * min(q, nsteps - 1) + 8 * kg;
+                xf[q] = *reinterpret_cast<const uintx4 *>(&s_lr[0][o]);
+                xg[q] = *reinterpret_cast<const uintx4 *>(&s_lr[1][o]);
             }
         }
+        floatx4 pf[kGemvQuarters], pg[kGemvQuarters];
 #pragma unroll
-        for (int j = 0; j < TW; ++j) {
-            // rows 4 kg + i, column lr of the tile (column of the head: f_b
-            // tiles first, then the slice's g_b tiles)
-            const int col = kGemvColTile * (wave + NW * j) + lr;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * kg + i < K) s_g[4 * kg + i][col] = tot[j][i];
+        for (int q = 0; q < kGemvQuarters; ++q) {
+            pf[q] = mfma_bf16(__builtin_bit_cast(bf16x8, xf[q]), __builtin_bit_cast(bf16x8, wf[q]), zero);
+            pg[q] = mfma_bf16(__builtin_bit_cast(bf16x8, xg[q]), __builtin_bit_cast(bf16x8, wg[q]), zero);
         }
+        floatx4 tf = pf[0], tg = pg[0];   // quarters past the last step add zeros
+#pragma unroll
+        for (int q = 1; q < kGemvQuarters; ++q) {
+            tf = tf + (q < nsteps ? pf[q] : zero);
+            tg = tg + (q < nsteps ? pg[q] : zero);
+        }
+        // rows 4 kg + i, column lr of the tile
+        const int col = kGemvColTile * wave + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * kg + i < K) {
+                s_g[4 * kg + i][col] = tf[i];
+                s_g[4 * kg + i][D + col] = tg[i];
+            }
     }
     __syncthreads();
-    for (int i = tid; i < K * (D + DC); i += NT) {
-        const int ml = i / (D + DC), col = i % (D + DC);
-        const bool isf = col < D;
-        const int n = h * D + (isf ? col : c0 + col - D);
-        const int64_t o = (row0 + ml) * qkvw + n;
+    for (int i = tid; i < 2 * K * D; i += NT) {
+        const int ml = i / (2 * D), col = i % (2 * D);
         const uint32_t u = f32_to_bf16(s_g[ml][col]);
-        if (isf) {
+        if (col < D) {
+            const int64_t o = (row0 + ml) * qkvw + (int64_t)h * D + col;
             const float gv = log_decay(bf16_to_f32(u), s_dtb[col], s_rate);
-            if (lead) {
-                a.g_raw[o] = (uint16_t)u;
-                a.gate[o] = gv;
-            }
+            a.g_raw[o] = (uint16_t)u;
+            a.gate[o] = gv;
             s_e[ml][col] = exp2_fast(gv * kLog2e);
         } else {
-            a.out_gate[o] = (uint16_t)u;
+            a.out_gate[(row0 + ml) * qkvw + (int64_t)h * D + col - D] = (uint16_t)u;
+            s_og[ml][col - D] = (uint16_t)u;
         }
     }
     __syncthreads();
@@ -541,47 +528,38 @@ __global__ __launch_bounds__((MixerCfg<D, NS>::kThreads)) void kda_mixer_kernel(
     // --- 3. the recurrence ---
     for (int t = 0; t < K; ++t) {
         const int64_t row = row0 + t;
-        rec_row<D, NS, 1>(S, s_x[t][0], s_x[t][1], s_x[t][2], s_e[t], s_red[t & 1], s_beta[t],
-                          a.scale, c0, tid, a.core + (row * H + h) * D + c0, nullptr,
-                          a.wy != nullptr ? a.wy[b] + ((size_t)h * K + t) * D + c0 : nullptr);
+        rec_row<D, 1, 1>(S, s_x[t][0], s_x[t][1], s_x[t][2], s_e[t], s_red[t & 1], s_beta[t],
+                         a.scale, 0, tid, a.core + (row * H + h) * D, s_o[t],
+                         wyb != nullptr ? wyb + ((size_t)h * K + t) * D : nullptr);
         if (a.snap != nullptr && t + 1 < K) {
-            float *__restrict__ Sn = a.snap[(size_t)b * (K - 1) + t] + (size_t)h * D * D + c0;
+            float *__restrict__ Sn = s_snp[t] + (size_t)h * D * D;
 #pragma unroll
             for (int r = 0; r < RPT; ++r)
                 gstore_stream(Sn + (size_t)(tr + RG * r) * D + 4 * cg, S[0][r]);
         }
     }
-
     if (a.write_state) {
 #pragma unroll
         for (int r = 0; r < RPT; ++r) gstore_stream(Sg + (size_t)(tr + RG * r) * D + 4 * cg, S[0][r]);
     }
-}
+    __syncthreads();   // every output row in LDS
 
-constexpr int kTailThreads = 256;
-
-template <int D>
-__global__ __launch_bounds__(kTailThreads) void kda_mixer_tail_kernel(const MixerArgs a)
-{
-    constexpr int SL = D / 8;
-    const int h = blockIdx.x, b = blockIdx.y, K = a.K, H = a.H;
-    const int64_t qkvw = (int64_t)H * D, cd = 3 * qkvw, row0 = (int64_t)b * K;
-    // gated RMSNorm of every row (whole rows per pass: kTailThreads % SL == 0)
-    const uint4 nw = *reinterpret_cast<const uint4 *>(a.norm_w + 8 * (threadIdx.x % SL));
-    for (int i = threadIdx.x; i < K * SL; i += kTailThreads) {
+    // --- 4. the gated RMSNorm of every row (whole rows per pass) ---
+    for (int i = tid; i < K * SL; i += NT) {
         const int t = i / SL, l = i % SL;
-        const int64_t o0 = (row0 + t) * qkvw + (int64_t)h * D + 8 * l;
-        const float4 lo = *reinterpret_cast<const float4 *>(a.core + o0);
-        const float4 hi = *reinterpret_cast<const float4 *>(a.core + o0 + 4);
+        const float4 lo = reinterpret_cast<const float4 *>(s_o[t])[2 * l];
+        const float4 hi = reinterpret_cast<const float4 *>(s_o[t])[2 * l + 1];
         const float xv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        const int64_t o0 = (row0 + t) * qkvw + (int64_t)h * D + 8 * l;
         *reinterpret_cast<uint4 *>(a.out + o0) = gated_norm8<D>(
-            xv, *reinterpret_cast<const uint4 *>(a.out_gate + o0), nw, a.eps_rms);
+            xv, *reinterpret_cast<const uint4 *>(&s_og[t][8 * l]), nw, a.eps_rms);
     }
     // the conv window after the K rows: entries K-1 .. K+2 of [carried rows
-    // 1 .. 3; rows 0 .. K-1], read whole before any is written
+    // 1 .. 3; rows 0 .. K-1], each thread's 8 channels read whole before any
+    // is written (every read of the old window above is behind a barrier)
     if (a.write_state) {
-        uint16_t *__restrict__ st = a.conv_state[b];
-        for (int i = threadIdx.x; i < 3 * SL; i += kTailThreads) {
+        uint16_t *st = const_cast<uint16_t *>(cst);
+        for (int i = tid; i < CL; i += NT) {
             const int64_t c = (i / SL) * qkvw + (int64_t)h * D + 8 * (i % SL);
             uint4 win[kConvKC];
 #pragma unroll
@@ -599,17 +577,12 @@ __global__ __launch_bounds__(kTailThreads) void kda_mixer_tail_kernel(const Mixe
 
 hipError_t launch_kda_mixer(const MixerArgs &a, int B, int head_dim, hipStream_t stream)
 {
-    if (head_dim == 128) {
-        hipLaunchKernelGGL((kda_mixer_kernel<128, 2>), dim3(a.H * 2, B),
-                           dim3(MixerCfg<128, 2>::kThreads), 0, stream, a);
-        hipLaunchKernelGGL(kda_mixer_tail_kernel<128>, dim3(a.H, B), dim3(kTailThreads), 0,
+    if (head_dim == 128)
+        hipLaunchKernelGGL(kda_mixer_kernel<128>, dim3(a.H, B), dim3(MixerCfg<128>::kThreads), 0,
                            stream, a);
-    } else {
-        hipLaunchKernelGGL((kda_mixer_kernel<16, 1>), dim3(a.H, B),
-                           dim3(MixerCfg<16, 1>::kThreads), 0, stream, a);
-        hipLaunchKernelGGL(kda_mixer_tail_kernel<16>, dim3(a.H, B), dim3(kTailThreads), 0,
+    else
+        hipLaunchKernelGGL(kda_mixer_kernel<16>, dim3(a.H, B), dim3(MixerCfg<16>::kThreads), 0,
                            stream, a);
-    }
     return hipGetLastError();
 }
 

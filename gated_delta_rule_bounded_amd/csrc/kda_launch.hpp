@@ -68,16 +68,15 @@ hipError_t launch_kda_fold_wy(const uint16_t *qkv, int64_t ldqkv, const float *g
                               int B, int K, int heads, int head_dim, int32_t *status,
                               hipStream_t stream);
 
-// The block decode's per-head stages in two launches: for each sequence,
-// the head's columns of the two rank-R products (f_b from fa with the
-// log-decay gate in its epilogue, g_b from ga), then for each of its K rows
-// conv + SiLU + L2 of the head's q | k | v channels and the recurrence (one
-// workgroup per value-column slice of the head), then the gated RMSNorm of
-// every output row and the conv window moved past the rows — the
-// accumulation order of dense_gemv_bf16_batchm and the per-row code of
-// conv_silu_l2, kda_recurrent and gated_rmsnorm, so every buffer gets the
-// bits those launches would write.  write_state false (a verify): neither
-// state is written and no snapshots are taken.
+// The block decode's per-head stages in one kernel, one workgroup per
+// (head, sequence): the head's columns of the two rank-R products (f_b from fa
+// with the log-decay gate in its epilogue, g_b from ga), then for each of the
+// K rows conv + SiLU + L2 of the head's q | k | v channels, the recurrence,
+// and the gated RMSNorm of its output — the accumulation order of
+// dense_gemv_bf16_batchm and the per-row code of conv_silu_l2, kda_recurrent
+// and gated_rmsnorm, so every buffer gets the bits those launches would
+// write.  write_state false (a verify): neither state is written and no
+// snapshots are taken.
 constexpr int kMixerMaxRows = 16;    // K of a fused call (its gates are held in LDS)
 constexpr int kMixerMaxRank = 128;   // R of a fused call (one contraction step per quarter)
 struct MixerArgs {

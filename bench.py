@@ -638,7 +638,7 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
     t_wt = timed(woa_wy)
 
     # the same calls captured once per layer in a HIP graph and replayed (the
-    # six launches of a call are enqueued back to back without host gaps)
+    # launches of a call are enqueued back to back without host gaps)
     def graphs_of(fn):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())

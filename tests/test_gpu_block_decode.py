@@ -417,8 +417,8 @@ def test_block_write_on_accept_table_form(B, K, H, D, hidden, rank):
 
 
 def test_block_decode_k_graph_replay_matches_eager():
-    """The block verify (six stream-ordered launches, no allocation, no
-    memset, no synchronisation) captured once in a HIP graph and replayed
+    """The block verify (stream-ordered launches, no allocation, no memset,
+    no synchronisation) captured once in a HIP graph and replayed
     several times, with eager work and synchronisation between replays: every
     replay equals the eager call bit for bit (output, states, snapshots)."""
     B, K, H, D, hidden, rank = 2, 4, 2, 128, 256, 32

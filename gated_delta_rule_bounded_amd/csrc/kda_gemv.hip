@@ -98,7 +98,7 @@ __device__ __forceinline__ uint4 load_x(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 template <int SIF>
 using WRows = uintx4[16][4 * SIF + 1];
 
-template <int RT, int SIF>
+template <int RT, int SIF, bool NT>
 __device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *__restrict__ w,
                                            const int64_t (&wrow)[SIF], int lane,
                                            __amdgpu_buffer_rsrc_t xr, const uint32_t (&xoff)[RT],
@@ -110,7 +110,10 @@ __device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *__
     const int stc = vj < vs.cnt ? vs.step(vj) : vs.beg;   // past the end: a valid dummy
 #pragma unroll
     for (int i = 0; i < SIF; ++i)
-        S.w[i] = *reinterpret_cast<const uintx4 *>(w + wrow[i] + 32 * stc + 8 * (c % 4));
+    {
+        const uintx4 *p = reinterpret_cast<const uintx4 *>(w + wrow[i] + 32 * stc + 8 * (c % 4));
+        S.w[i] = NT ? __builtin_nontemporal_load(p) : *p;
+    }
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
         const int st = v0 + j < vs.cnt ? vs.step(v0 + j) : vs.beg;
@@ -145,10 +148,10 @@ __device__ __forceinline__ void mma_stage(const Stage<RT, SIF> &S, const WRows<S
 }
 
 // RT 16-row tiles per workgroup (grid.y covers the rest of M); SIF steps per
-// load stage, two stages in flight.  Neither changes any element's order of
-// accumulation, only how many rows a workgroup carries and how far its loads
-// run ahead.
-template <int RT, int SIF>
+// load stage, two stages in flight; NT marks the weight loads non-temporal
+// (streaming).  None of these changes any element's order of accumulation,
+// only how many rows a workgroup carries and how its loads run.
+template <int RT, int SIF, bool NT>
 __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
 {
     __shared__ float part[kWaves][RT][16][17];
@@ -196,16 +199,16 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
     if (vs.cnt > 0) {
         WRows<SIF> &L = s_w[wave];
         Stage<RT, SIF> A, B;
-        load_stage(A, g.w, wrow, lane, xr, xoff, vs, 0);
-        load_stage(B, g.w, wrow, lane, xr, xoff, vs, SIF);
+        load_stage<RT, SIF, NT>(A, g.w, wrow, lane, xr, xoff, vs, 0);
+        load_stage<RT, SIF, NT>(B, g.w, wrow, lane, xr, xoff, vs, SIF);
         put_stage(A, L, lane);
 #pragma unroll 1
         for (int v = 0; v < vs.cnt; v += 2 * SIF) {
             mma_stage(A, L, acc, vs, v, r, kg);
-            load_stage(A, g.w, wrow, lane, xr, xoff, vs, v + 2 * SIF);
+            load_stage<RT, SIF, NT>(A, g.w, wrow, lane, xr, xoff, vs, v + 2 * SIF);
             put_stage(B, L, lane);
             mma_stage(B, L, acc, vs, v + SIF, r, kg);
-            load_stage(B, g.w, wrow, lane, xr, xoff, vs, v + 3 * SIF);
+            load_stage<RT, SIF, NT>(B, g.w, wrow, lane, xr, xoff, vs, v + 3 * SIF);
             put_stage(A, L, lane);
         }
     }
@@ -253,11 +256,24 @@ hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStre
     // both depths, so no slot of the last pass is a dummy: measured on weights
     // streamed from HBM, 4 steps per stage beat 6 (which leaves dummies) by
     // about 10 %, and 8 (fewer resident workgroups) by about 6 %.
+    // Non-temporal weight loads measured 6 % faster for launches of more
+    // tiles than CUs (the q|k|v product: 20.7 against 22.1 us) and 3 % slower
+    // at one tile per CU (o_proj), so only the former take them.
+    const bool nt = tiles > 256;
     if (M <= 16) {
-        hipLaunchKernelGGL((gemv_bf16_batchm<1, 4>), dim3(tiles, 1), dim3(256), 0, stream, a);
+        if (nt)
+            hipLaunchKernelGGL((gemv_bf16_batchm<1, 4, true>), dim3(tiles, 1), dim3(256), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((gemv_bf16_batchm<1, 4, false>), dim3(tiles, 1), dim3(256), 0,
+                               stream, a);
     } else {
-        hipLaunchKernelGGL((gemv_bf16_batchm<4, 2>), dim3(tiles, (M + 63) / 64), dim3(256), 0,
-                           stream, a);
+        if (nt)
+            hipLaunchKernelGGL((gemv_bf16_batchm<4, 2, true>), dim3(tiles, (M + 63) / 64),
+                               dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemv_bf16_batchm<4, 2, false>), dim3(tiles, (M + 63) / 64),
+                               dim3(256), 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -828,15 +828,29 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
                 return fail(KDA_ERR_ALIAS, "kda_block_decode_k: regions %d and %d overlap", i, j);
 
     const int Mi = (int)M, hs = hidden_size, rk = rank, qk = (int)qkv;
-    // front: every projection of the hidden rows, one launch
+    // front: every projection of the hidden rows, one launch.  Where the
+    // output buffer can hold them (it is written only by the last launch),
+    // the f_a, g_a and b_proj products are split into kLowRankSplit chunks
+    // of the contraction, left there as chunk sums and finished by their
+    // consumer: their few column tiles then spread over the CUs next to the
+    // q|k|v tiles instead of giving some CUs a fourth whole tile.  The split
+    // depends on the shapes alone, so every path gives the same bits.
+    const int ks = kda::kLowRankSplit;
+    const bool split = hidden_size % (32 * ks) == 0 &&
+                       (int64_t)2 * ks * (2 * rank + heads) <= hidden_size;
+    float *const part = split ? reinterpret_cast<float *>(out) : nullptr;
+    const size_t lr_chunk = (size_t)ks * M * rank;   // floats of one split product
     const kda::GemvSeg front[] = {
         {hidden, w->q_proj, b->qkv_proj, hs, cd, qk, hs},
         {hidden, w->k_proj, b->qkv_proj + qkv, hs, cd, qk, hs},
         {hidden, w->v_proj, b->qkv_proj + 2 * qkv, hs, cd, qk, hs},
-        {hidden, w->f_a, b->fa, hs, rk, rk, hs},
-        {hidden, w->g_a, b->ga, hs, rk, rk, hs},
-        // b_proj with beta = sigmoid(b_raw) fused into its epilogue
-        {hidden, w->b_proj, b->b_raw, hs, heads, heads, hs, kda::kEpiBeta, b->beta},
+        {hidden, w->f_a, b->fa, hs, rk, rk, hs, kda::kEpiNone, nullptr, nullptr, nullptr, 0,
+         split ? ks : 1, part},
+        {hidden, w->g_a, b->ga, hs, rk, rk, hs, kda::kEpiNone, nullptr, nullptr, nullptr, 0,
+         split ? ks : 1, split ? part + lr_chunk : nullptr},
+        // b_proj with beta = sigmoid(b_raw) fused into its epilogue (unsplit)
+        {hidden, w->b_proj, b->b_raw, hs, heads, heads, hs, kda::kEpiBeta, b->beta, nullptr,
+         nullptr, 0, split ? ks : 1, split ? part + 2 * lr_chunk : nullptr},
     };
     const kda::GemvSeg mid[] = {
         // f_b with the log-decay gate fused into its epilogue
@@ -863,6 +877,9 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
     mixer.ldy = cd;
     mixer.fa = b->fa;
     mixer.ga = b->ga;
+    mixer.lr_part = part;
+    mixer.ks = split ? ks : 1;
+    mixer.b_raw = b->b_raw;
     mixer.f_b = w->f_b;
     mixer.g_b = w->g_b;
     mixer.a_log = w->a_log;
@@ -887,6 +904,11 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
     int rc;
     if ((rc = hip_status(kda::launch_gemv_bf16_batchm(front, 6, Mi, stream),
                          "kda_block_decode_k: front projections launch")) ||
+        (rc = hip_status(fuse_mixer || !split
+                             ? hipSuccess
+                             : kda::launch_lowrank_finish(part, ks, Mi, rk, heads, b->fa, b->ga,
+                                                          b->b_raw, b->beta, stream),
+                         "kda_block_decode_k: low-rank finish launch")) ||
         (rc = hip_status(fuse_mixer ? hipSuccess : kda::launch_gemv_bf16_batchm(mid, 2, Mi, stream),
                          "kda_block_decode_k: low-rank projections launch")) ||
         (rc = hip_status(

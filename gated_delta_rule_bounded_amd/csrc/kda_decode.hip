@@ -321,7 +321,7 @@ struct MixerCfg {
     static_assert(kTiles == kWaves, "one column tile of each product per wave");
 };
 
-template <int D>
+template <int D, int KS>
 __global__ __launch_bounds__((MixerCfg<D>::kThreads)) void kda_mixer_kernel(const MixerArgs a)
 {
     using Cfg = MixerCfg<D>;
@@ -413,10 +413,34 @@ __global__ __launch_bounds__((MixerCfg<D>::kThreads)) void kda_mixer_kernel(cons
         const int which = i / (K * (R / 8)), e = i % (K * (R / 8));
         *reinterpret_cast<uint4 *>(&s_lr[which][(e / (R / 8)) * LR + 8 * (e % (R / 8))]) = v;
     };
+    // With KS > 1 the front left f_a, g_a and b_proj as KS chunk sums each
+    // (launch_lowrank_finish's layout): this thread's piece of 8 columns and
+    // beta's b_proj column come as their chunk sums, added here in chunk
+    // order (split_sum), and fa, ga, b_raw and beta are written here.
+    const int64_t Mrows = (int64_t)gridDim.y * K;
     uint4 lrv = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (kLrAll <= NT) lrv = *reinterpret_cast<const uint4 *>(lr_piece(min(tid, nlr - 1)));
+    float4 lp[KS][2];
+    float bp[KS], btv = 0.f;
+    if constexpr (KS == 1) {
+        if constexpr (kLrAll <= NT) lrv = *reinterpret_cast<const uint4 *>(lr_piece(min(tid, nlr - 1)));
+        btv = a.beta[(row0 + min(tid, K - 1)) * H + h];
+    } else {
+        if constexpr (kLrAll <= NT) {
+            const int i = min(tid, nlr - 1);
+            const int which = i / (K * (R / 8)), e = i % (K * (R / 8));
+            const float *pw = a.lr_part + ((int64_t)which * KS * Mrows + row0 + e / (R / 8)) * R +
+                              8 * (e % (R / 8));
+#pragma unroll
+            for (int c = 0; c < KS; ++c) {
+                lp[c][0] = *reinterpret_cast<const float4 *>(pw + (int64_t)c * Mrows * R);
+                lp[c][1] = *reinterpret_cast<const float4 *>(pw + (int64_t)c * Mrows * R + 4);
+            }
+        }
+        const float *pb = a.lr_part + 2 * KS * Mrows * R + (row0 + min(tid, K - 1)) * H + h;
+#pragma unroll
+        for (int c = 0; c < KS; ++c) bp[c] = pb[(int64_t)c * Mrows * H];
+    }
     const float4 dtv = *reinterpret_cast<const float4 *>(a.dt_bias + (int64_t)h * D + 4 * (tid % (D / 4)));
-    const float btv = a.beta[(row0 + min(tid, K - 1)) * H + h];
     const float alog = a.a_log[h];
     const uint4 nw = *reinterpret_cast<const uint4 *>(a.norm_w + 8 * (tid % SL));
 
@@ -428,13 +452,57 @@ __global__ __launch_bounds__((MixerCfg<D>::kThreads)) void kda_mixer_kernel(cons
     for (int r = 0; r < RPT; ++r) S[0][r] = gload_stream(Sg + (size_t)(tr + RG * r) * D + 4 * cg);
 
     // small operands to LDS
-    if constexpr (kLrAll <= NT) {
-        if (tid < nlr) lr_store(tid, lrv);
+    if constexpr (KS == 1) {
+        if constexpr (kLrAll <= NT) {
+            if (tid < nlr) lr_store(tid, lrv);
+        } else {
+            for (int i = tid; i < nlr; i += NT) lr_store(i, *reinterpret_cast<const uint4 *>(lr_piece(i)));
+        }
+        if (tid < K) s_beta[tid] = btv;
     } else {
-        for (int i = tid; i < nlr; i += NT) lr_store(i, *reinterpret_cast<const uint4 *>(lr_piece(i)));
+        // a piece: 8 columns of row ml of fa or ga, rounded as the front's
+        // epilogue would have rounded them (sequence b's rows written by head 0)
+        auto finish_piece = [&](int i, const float (&f)[8]) {
+            const int which = i / (K * (R / 8)), e = i % (K * (R / 8));
+            const uint4 v = pack8(f);
+            lr_store(i, v);
+            if (h == 0)
+                *reinterpret_cast<uint4 *>((which == 0 ? a.fa : a.ga) + row0 * R + 8 * e) = v;
+        };
+        if constexpr (kLrAll <= NT) {
+            if (tid < nlr) {
+                float f[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    f[jj] = get4(lp[0][jj / 4], jj % 4);
+#pragma unroll
+                    for (int c = 1; c < KS; ++c) f[jj] = f[jj] + get4(lp[c][jj / 4], jj % 4);
+                }
+                finish_piece(tid, f);
+            }
+        } else {
+            for (int i = tid; i < nlr; i += NT) {
+                const int which = i / (K * (R / 8)), e = i % (K * (R / 8));
+                const float *pw = a.lr_part + (int64_t)which * KS * Mrows * R;
+                float f[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj)
+                    f[jj] = split_sum(pw, KS, Mrows, row0 + e / (R / 8), R, 8 * (e % (R / 8)) + jj);
+                finish_piece(i, f);
+            }
+        }
+        if (tid < K) {
+            float v = bp[0];
+#pragma unroll
+            for (int c = 1; c < KS; ++c) v = v + bp[c];
+            const uint32_t u = f32_to_bf16(v);
+            const float bt = sigmoid_fast(bf16_to_f32(u));
+            a.b_raw[(row0 + tid) * H + h] = (uint16_t)u;
+            a.beta[(row0 + tid) * H + h] = bt;
+            s_beta[tid] = bt;
+        }
     }
     if (tid < D / 4) reinterpret_cast<float4 *>(s_dtb)[tid] = dtv;
-    if (tid < K) s_beta[tid] = btv;
     if (tid == 0) s_rate = decay_rate(alog);
     if (tid + 1 < K) {
         s_snp[tid] = snp;
@@ -577,12 +645,22 @@ __global__ __launch_bounds__((MixerCfg<D>::kThreads)) void kda_mixer_kernel(cons
 
 hipError_t launch_kda_mixer(const MixerArgs &a, int B, int head_dim, hipStream_t stream)
 {
-    if (head_dim == 128)
-        hipLaunchKernelGGL(kda_mixer_kernel<128>, dim3(a.H, B), dim3(MixerCfg<128>::kThreads), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL(kda_mixer_kernel<16>, dim3(a.H, B), dim3(MixerCfg<16>::kThreads), 0,
-                           stream, a);
+    if (a.ks != 1 && a.ks != kLowRankSplit) return hipErrorInvalidValue;
+    if (head_dim == 128) {
+        if (a.ks == 1)
+            hipLaunchKernelGGL((kda_mixer_kernel<128, 1>), dim3(a.H, B),
+                               dim3(MixerCfg<128>::kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((kda_mixer_kernel<128, kLowRankSplit>), dim3(a.H, B),
+                               dim3(MixerCfg<128>::kThreads), 0, stream, a);
+    } else {
+        if (a.ks == 1)
+            hipLaunchKernelGGL((kda_mixer_kernel<16, 1>), dim3(a.H, B),
+                               dim3(MixerCfg<16>::kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((kda_mixer_kernel<16, kLowRankSplit>), dim3(a.H, B),
+                               dim3(MixerCfg<16>::kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -37,10 +37,12 @@ struct Seg {
     uint16_t *y;
     int64_t ldx, ldy;
     int32_t N, Kd;
-    int32_t tile0;  // first column tile of this segment in the grid
+    int32_t tile0;  // first workgroup of this segment in the grid
     int32_t epi, head_dim;
     float *act;
     const float *a_log, *dt_bias;
+    int32_t ksplit;  // contraction chunks (workgroups per column tile)
+    float *part;     // chunk sums when ksplit > 1
 };
 
 // Store one result: its bf16 rounding, and the segment's activation of it.
@@ -163,12 +165,16 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
     for (int i = 1; i < a.nseg; ++i)
         if ((int)blockIdx.x >= a.seg[i].tile0) s = i;
     const Seg g = a.seg[s];
-    const int n0 = ((int)blockIdx.x - g.tile0) * kColTile;
+    // column tile, and the contraction chunk [k0, k0 + kc) of a split segment
+    const int unit = (int)blockIdx.x - g.tile0;
+    const int chunk = unit % g.ksplit;
+    const int n0 = unit / g.ksplit * kColTile;
+    const int kc = g.Kd / g.ksplit, k0 = chunk * kc;
     const int m0 = (int)blockIdx.y * (RT * 16);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, kg = lane >> 4;
-    const int nsteps = g.Kd >> 5;
+    const int nsteps = kc >> 5;
 
     // the weight rows this lane loads (element offsets; columns past N read
     // row 0 and are never stored)
@@ -176,14 +182,15 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
 #pragma unroll
     for (int i = 0; i < SIF; ++i) {
         const int n = n0 + i * (16 / SIF) + lane / (4 * SIF);
-        wrow[i] = (int64_t)(n < g.N ? n : 0) * g.Kd;
+        wrow[i] = (int64_t)(n < g.N ? n : 0) * g.Kd + k0;
     }
-    // this lane's x rows, one per 16-row tile: byte offsets from the first
-    // row of the workgroup, or out of range for rows past M
+    // this lane's x rows, one per 16-row tile: byte offsets from the chunk's
+    // first column of the workgroup's first row, or out of range for rows
+    // past M
     const int rows = min(a.M - m0, RT * 16);
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(g.x + (int64_t)m0 * g.ldx), (short)0,
-        (int)((int64_t)rows * g.ldx * 2), 0x00020000);
+        const_cast<uint16_t *>(g.x + (int64_t)m0 * g.ldx + k0), (short)0,
+        (int)((int64_t)rows * g.ldx * 2 - (int64_t)k0 * 2), 0x00020000);
     uint32_t xoff[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
@@ -229,13 +236,50 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
             if (m < a.M) {
                 const float v = ((part[0][t][tr][tc] + part[1][t][tr][tc]) + part[2][t][tr][tc]) +
                                 part[3][t][tr][tc];
-                store_out(g, m, n0 + tc, v);
+                if (g.ksplit > 1)
+                    g.part[((int64_t)chunk * a.M + m) * g.N + n0 + tc] = v;
+                else
+                    store_out(g, m, n0 + tc, v);
             }
         }
     }
 }
 
+// The low-rank products of a block split along the contraction: each
+// (row, column) of f_a, g_a (rank columns) and b_proj (heads columns) summed
+// from its chunks, rounded to bf16, and beta = sigmoid(b_raw) formed as the
+// b_proj epilogue forms it.
+__global__ __launch_bounds__(256) void lowrank_finish_kernel(
+    const float *__restrict__ part, int ks, int M, int rank, int heads, uint16_t *__restrict__ fa,
+    uint16_t *__restrict__ ga, uint16_t *__restrict__ b_raw, float *__restrict__ beta)
+{
+    const int ncol = 2 * rank + heads;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * ncol) return;
+    const int m = (int)(i / ncol), n = (int)(i % ncol);
+    if (n < 2 * rank) {
+        const int which = n / rank, j = n % rank;
+        const uint32_t u = f32_to_bf16(split_sum(part + (int64_t)which * ks * M * rank, ks, M, m, rank, j));
+        (which == 0 ? fa : ga)[(int64_t)m * rank + j] = (uint16_t)u;
+    } else {
+        const int j = n - 2 * rank;
+        const uint32_t u = f32_to_bf16(split_sum(part + (int64_t)2 * ks * M * rank, ks, M, m, heads, j));
+        b_raw[(int64_t)m * heads + j] = (uint16_t)u;
+        beta[(int64_t)m * heads + j] = sigmoid_fast(bf16_to_f32(u));
+    }
+}
+
 }  // namespace
+
+hipError_t launch_lowrank_finish(const float *part, int ks, int M, int rank, int heads,
+                                 uint16_t *fa, uint16_t *ga, uint16_t *b_raw, float *beta,
+                                 hipStream_t stream)
+{
+    const int64_t n = (int64_t)M * (2 * rank + heads);
+    hipLaunchKernelGGL(lowrank_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, part, ks, M, rank, heads, fa, ga, b_raw, beta);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStream_t stream)
 {
@@ -246,8 +290,8 @@ hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStre
         a.seg[i] = Seg{segs[i].x,     segs[i].w,        segs[i].y,   segs[i].ldx,
                        segs[i].ldy,   segs[i].N,        segs[i].Kd,  tiles,
                        segs[i].epi,   segs[i].head_dim, segs[i].act, segs[i].a_log,
-                       segs[i].dt_bias};
-        tiles += (segs[i].N + kColTile - 1) / kColTile;
+                       segs[i].dt_bias, max(segs[i].ksplit, 1), segs[i].part};
+        tiles += (segs[i].N + kColTile - 1) / kColTile * max(segs[i].ksplit, 1);
     }
     a.nseg = nseg;
     a.M = M;

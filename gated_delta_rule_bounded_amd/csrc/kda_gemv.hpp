@@ -44,4 +44,14 @@ __device__ __forceinline__ GemvVisit gemv_visit(int quarter, int nsteps, int til
     return vs;
 }
 
+// An element of a product split along the contraction (GemvSeg::ksplit):
+// the chunk sums part[(c M + m) N + n] added in chunk order from the first.
+__device__ __forceinline__ float split_sum(const float *__restrict__ part, int ks, int64_t M,
+                                           int64_t m, int N, int n)
+{
+    float v = part[m * N + n];
+    for (int c = 1; c < ks; ++c) v = v + part[((int64_t)c * M + m) * N + n];
+    return v;
+}
+
 }  // namespace kda

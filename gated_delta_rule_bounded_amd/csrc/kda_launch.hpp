@@ -87,12 +87,15 @@ struct MixerArgs {
     uint16_t *const *conv_snap;     // per (sequence, row < K-1), or nullptr
     uint16_t *y;                    // conv_out rows [B*K, ldy]
     int64_t ldy;
-    const uint16_t *fa, *ga;        // low-rank inputs [B*K, R]
+    uint16_t *fa, *ga;              // low-rank inputs [B*K, R] (ks == 1), else written here
+    const float *lr_part;           // with ks > 1: the chunk sums of f_a, g_a, b_proj
+    int ks;                         // (launch_lowrank_finish's layout)
+    uint16_t *b_raw;                // [B*K, H], written when ks > 1
     const uint16_t *f_b, *g_b;      // [H*D, R]
     const float *a_log, *dt_bias;   // [H], [H*D]
     uint16_t *g_raw;                // [B*K, H*D] (f_b product, bf16)
     float *gate;                    // [B*K, H, D] (log-decay gate of g_raw)
-    const float *beta;              // [B*K, H]
+    float *beta;                    // [B*K, H] (read; written when ks > 1)
     float *const *state;            // per sequence [H, D, D]
     float *const *snap;             // per (sequence, row < K-1), or nullptr
     float *const *wy;               // per sequence [H, K, D] rows u, or nullptr
@@ -173,6 +176,12 @@ constexpr int kGemvMaxSegs = 6;
 // sigmoid(b_raw) — written to act[m * N + n], exactly as kda_gate forms
 // them from the same bf16 values.
 enum GemvEpi : int32_t { kEpiNone = 0, kEpiGate = 1, kEpiBeta = 2 };
+// A segment may also be split along the contraction into ksplit equal
+// chunks (Kd % (32 ksplit) == 0), each a workgroup of its own: chunk c then
+// writes its fp32 sum (the chunk's quarters added as usual) to part[(c M + m)
+// N + n] instead of y, and the element is lowrank_sum's sum of the chunks in
+// order, rounded to bf16 by whoever consumes it.  Small products then spread
+// over more workgroups next to large ones in the same launch.
 struct GemvSeg {
     const uint16_t *x;
     const uint16_t *w;
@@ -183,8 +192,17 @@ struct GemvSeg {
     float *act = nullptr;
     const float *a_log = nullptr, *dt_bias = nullptr;
     int32_t head_dim = 0;
+    int32_t ksplit = 1;
+    float *part = nullptr;
 };
 hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStream_t stream);
+// A block's f_a, g_a and b_proj products split ks ways (chunk sums in part:
+// f_a [ks][M][rank], then g_a alike, then b_proj [ks][M][heads]) finished
+// into fa, ga, b_raw and beta.
+constexpr int kLowRankSplit = 4;   // contraction chunks of a block's low-rank products
+hipError_t launch_lowrank_finish(const float *part, int ks, int M, int rank, int heads,
+                                 uint16_t *fa, uint16_t *ga, uint16_t *b_raw, float *beta,
+                                 hipStream_t stream);
 
 // y[rows][n_out] (row stride ldy) = bf16(x[rows][n_in] (stride ldx) w^T), w in
 // torch Linear layout [n_out][n_in] (stride ldw), fp32 accumulation, on the

@@ -198,6 +198,7 @@ def _check_oracle(orc, got, x, w, S0, conv0, B, K, H, D, hidden, scale):
     (3, 4, 2, 16, 128, 32),
     (2, 5, 2, 128, 256, 32),
     (4, 1, 2, 16, 64, 32),
+    (2, 5, 2, 16, 640, 32),      # f_a, g_a, b_proj split over the contraction
 ])
 def test_block_decode_k_small_against_oracle(orc, B, K, H, D, hidden, rank):
     x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1101 + K)
@@ -211,6 +212,7 @@ def test_block_decode_k_small_against_oracle(orc, B, K, H, D, hidden, rank):
     (2, 5, 2, 128, 256, 32),
     (5, 4, 2, 128, 256, 32),     # 20 verify rows against 5-row steps: two kernel instances
     (1, 17, 2, 16, 128, 32),     # the four-launch path against fused single rows
+    (1, 17, 2, 16, 640, 32),     # the same with the low-rank products split
 ])
 def test_block_decode_k_bitwise_equals_serial_decodes(B, K, H, D, hidden, rank):
     x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1201 + K)
@@ -230,6 +232,8 @@ def test_block_decode_k_bitwise_equals_serial_decodes(B, K, H, D, hidden, rank):
     (2, 16, 2, 16, 128, 64),     # the most rows the fused kernel takes
     (1, 17, 2, 16, 128, 32),     # one more: the four-launch path
     (65, 2, 2, 16, 128, 32),     # 130 (sequence, head) pairs: the four-launch path
+    (65, 2, 2, 16, 640, 32),     # the same with the low-rank products split
+    (3, 4, 2, 16, 640, 32),      # the fused kernel finishing the split products
 ])
 def test_block_decode_k_stages_equal_standalone_kernels(B, K, H, D, hidden, rank):
     """The block decode runs the rank-R gate products, conv + SiLU + L2, the

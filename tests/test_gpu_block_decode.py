@@ -231,6 +231,7 @@ def test_block_decode_k_bitwise_equals_serial_decodes(B, K, H, D, hidden, rank):
     (1, 4, 2, 128, 256, 224),    # rank 224: uneven quarters, the four-launch path
     (2, 16, 2, 16, 128, 64),     # the most rows the fused kernel takes
     (1, 17, 2, 16, 128, 32),     # one more: the four-launch path
+    (64, 2, 2, 16, 128, 32),     # 128 (sequence, head) pairs: the most the fused kernel takes
     (65, 2, 2, 16, 128, 32),     # 130 (sequence, head) pairs: the four-launch path
     (65, 2, 2, 16, 640, 32),     # the same with the low-rank products split
     (3, 4, 2, 16, 640, 32),      # the fused kernel finishing the split products
@@ -420,12 +421,16 @@ def test_block_write_on_accept_table_form(B, K, H, D, hidden, rank):
         np.testing.assert_array_equal(got_c, want_c, err_msg=f"seq {b} conv state")
 
 
-def test_block_decode_k_graph_replay_matches_eager():
+@pytest.mark.parametrize("B,K,H,D,hidden,rank", [
+    (2, 4, 2, 128, 256, 32),
+    (2, 4, 2, 16, 640, 32),      # the low-rank products split (chunk sums in the output buffer)
+    (65, 2, 2, 16, 640, 32),     # the six-launch path with the split and its finish kernel
+])
+def test_block_decode_k_graph_replay_matches_eager(B, K, H, D, hidden, rank):
     """The block verify (stream-ordered launches, no allocation, no memset,
     no synchronisation) captured once in a HIP graph and replayed
     several times, with eager work and synchronisation between replays: every
     replay equals the eager call bit for bit (output, states, snapshots)."""
-    B, K, H, D, hidden, rank = 2, 4, 2, 128, 256, 32
     x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1801)
     scale = D ** -0.5
     ref = _gpu_decode_k(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)

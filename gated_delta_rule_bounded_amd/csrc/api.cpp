@@ -860,13 +860,11 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
     };
     const kda::GemvSeg back[] = {{b->o_norm_out, w->o_proj, out, qkv, hs, hs, qk}};
     // The rank-R gate products, conv + SiLU + L2, the recurrence and the
-    // gated RMSNorm: for up to 16 rows of few sequences at rank <= 128 in one
-    // kernel per (head, sequence), the same bits as the four launches
-    // otherwise taken (where the recurrence can split a head's columns over
-    // several workgroups; the fused kernel owns its head's whole conv window
-    // and norm).  A verify writes neither state nor snapshots.
-    const bool fuse_mixer = K <= kda::kMixerMaxRows && rank <= kda::kMixerMaxRank &&
-                            (int64_t)B * heads <= 128;
+    // gated RMSNorm: for up to 16 rows at rank <= 128 in one kernel per
+    // (head, sequence) (measured faster than the four launches below at every
+    // batch from 1 to 256 sequences), the same bits as the four launches
+    // otherwise taken.  A verify writes neither state nor snapshots.
+    const bool fuse_mixer = K <= kda::kMixerMaxRows && rank <= kda::kMixerMaxRank;
     kda::MixerArgs mixer{};
     mixer.x = b->qkv_proj;
     mixer.ldx = cd;

@@ -549,9 +549,9 @@ int dense_gemv_bf16_batchm(const uint16_t *x, int64_t ldx, const uint16_t *w,
  * weights must be pairwise disjoint where one of them is written
  * (KDA_ERR_ALIAS); the per-sequence states are reached through the tables
  * and must be distinct, with snapshots disjoint from them.  B == 0 or K == 0
- * is a no-op.  Allocates nothing; three launches on `stream` when K <= 16,
- * rank <= 128 and B*heads <= 128 (the gate products, conv, recurrence and
- * norm of each (head, sequence) in one kernel), six otherwise; the same bits
+ * is a no-op.  Allocates nothing; three launches on `stream` when K <= 16
+ * and rank <= 128 (the gate products, conv, recurrence and norm of each
+ * (head, sequence) in one kernel), six or seven otherwise; the same bits
  * either way.
  * ------------------------------------------------------------------------ */
 typedef struct kda_block_decode_buffers {

@@ -231,8 +231,8 @@ def test_block_decode_k_bitwise_equals_serial_decodes(B, K, H, D, hidden, rank):
     (1, 4, 2, 128, 256, 224),    # rank 224: uneven quarters, the four-launch path
     (2, 16, 2, 16, 128, 64),     # the most rows the fused kernel takes
     (1, 17, 2, 16, 128, 32),     # one more: the four-launch path
-    (64, 2, 2, 16, 128, 32),     # 128 (sequence, head) pairs: the most the fused kernel takes
-    (65, 2, 2, 16, 128, 32),     # 130 (sequence, head) pairs: the four-launch path
+    (1, 17, 2, 16, 640, 32),     # the same with the low-rank products split
+    (65, 2, 2, 16, 128, 32),     # many sequences in the fused kernel
     (65, 2, 2, 16, 640, 32),     # the same with the low-rank products split
     (3, 4, 2, 16, 640, 32),      # the fused kernel finishing the split products
 ])
@@ -367,7 +367,7 @@ def test_block_write_on_accept_equals_snapshots(B, K, H, D, hidden, rank):
     (6, 4, 2, 128, 256, 32),
     (1, 4, 32, 128, 4096, 128),
     (2, 1, 2, 128, 256, 32),
-    (65, 2, 2, 16, 128, 32),     # 130 (sequence, head) pairs: the four-launch path
+    (2, 17, 2, 16, 128, 32),     # 17 rows: the four-launch path
 ])
 def test_block_write_on_accept_table_form(B, K, H, D, hidden, rank):
     """The block's write-on-accept in table form ("Glm5NextLayer" page, the
@@ -424,7 +424,7 @@ def test_block_write_on_accept_table_form(B, K, H, D, hidden, rank):
 @pytest.mark.parametrize("B,K,H,D,hidden,rank", [
     (2, 4, 2, 128, 256, 32),
     (2, 4, 2, 16, 640, 32),      # the low-rank products split (chunk sums in the output buffer)
-    (65, 2, 2, 16, 640, 32),     # the six-launch path with the split and its finish kernel
+    (1, 17, 2, 16, 640, 32),     # the six-launch path with the split and its finish kernel
 ])
 def test_block_decode_k_graph_replay_matches_eager(B, K, H, D, hidden, rank):
     """The block verify (stream-ordered launches, no allocation, no memset,

@@ -294,12 +294,17 @@ def test_block_decode_k_stages_equal_standalone_kernels(B, K, H, D, hidden, rank
         assert torch.equal(a, b)
 
 
-def test_block_decode_k_full_size(orc):
+@pytest.mark.parametrize("B,K", [
+    (1, 4),
+    (3, 4),      # several sequences in the fused kernel
+    (1, 17),     # the six-launch path (with the split low-rank products and their finish)
+])
+def test_block_decode_k_full_size(orc, B, K):
     # the layer at full size (hidden 4096, 32 heads x 128, rank 128, weights
-    # ~ N(0, 0.02)): one sequence verifying K = 4 draft tokens, against the
-    # oracle and bitwise against four single-token decodes
-    B, K, H, D, hidden, rank = 1, 4, 32, 128, 4096, 128
-    x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1301, w_std=0.02)
+    # ~ N(0, 0.02)): sequences verifying K draft tokens, against the oracle
+    # and bitwise against K single-token decodes
+    H, D, hidden, rank = 32, 128, 4096, 128
+    x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1301 + 7 * B + K, w_std=0.02)
     scale = D ** -0.5
     got = _gpu_decode_k(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)
     _check_oracle(orc, got, x, w, S0, conv0, B, K, H, D, hidden, scale)

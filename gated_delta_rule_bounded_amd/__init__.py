@@ -29,7 +29,7 @@ __all__ = ["conv_silu_l2", "kda_gate", "kda_prefill", "kda_prefill_noalloc", "kd
            "kda_block_verify_k", "kda_block_fold_accepted", "kda_block_verify_wy_k",
            "kda_block_fold_wy", "kda_prefill_bf16", "kda_block_decode", "kda_block_decode_k",
            "block_decode_buffers",
-           "ptr_table", "KdaError",
+           "ptr_table", "bind", "KdaError",
            "last_error", "library_path"]
 
 
@@ -106,6 +106,48 @@ def _status(t):
 def _check(rc):
     if rc != 0:
         raise KdaError(rc, _lib.last_error())
+
+
+class _Recorder:
+    """Stands in for the loaded library while :func:`bind` runs a call: each
+    C entry point the call reaches is recorded with its arguments, not run."""
+
+    def __init__(self, real):
+        self._real, self.calls = real, []
+
+    def __getattr__(self, name):
+        fn = getattr(self._real, name)
+
+        def record(*args):
+            self.calls.append((fn, args))
+            return 0
+        return record
+
+
+def bind(fn, *args, **kwargs):
+    """One of this module's launching calls (``fn``) with its arguments,
+    checked and marshalled once, returned as a function of no arguments that
+    makes the same C call(s) again: the same pointers, sizes and stream (the
+    stream current at bind time).  For loops that re-run one call on tensors
+    refilled in place, where the per-call checks would cost more host time
+    than the GPU work; the tensors must outlive the returned function.
+    Nothing is launched by ``bind`` itself.  Not for the size queries, whose
+    results it would drop; not thread-safe with other calls of this module."""
+    real = _lib.lib
+    rec = _Recorder(real)
+    _lib.lib = rec
+    try:
+        fn(*args, **kwargs)
+    finally:
+        _lib.lib = real
+    calls = tuple(rec.calls)
+    if not calls:
+        raise ValueError(f"bind: {getattr(fn, '__name__', fn)} made no library call")
+
+    def call():
+        for f, a in calls:
+            _check(f(*a))
+    return call
 
 
 def ptr_table(tensors, device=None):

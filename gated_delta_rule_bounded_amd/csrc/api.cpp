@@ -848,7 +848,8 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
          split ? ks : 1, part},
         {hidden, w->g_a, b->ga, hs, rk, rk, hs, kda::kEpiNone, nullptr, nullptr, nullptr, 0,
          split ? ks : 1, split ? part + lr_chunk : nullptr},
-        // b_proj with beta = sigmoid(b_raw) fused into its epilogue (unsplit)
+        // b_proj, beta = sigmoid(b_raw) in its epilogue when unsplit (else the
+        // consumer forms both from the chunk sums)
         {hidden, w->b_proj, b->b_raw, hs, heads, heads, hs, kda::kEpiBeta, b->beta, nullptr,
          nullptr, 0, split ? ks : 1, split ? part + 2 * lr_chunk : nullptr},
     };
@@ -899,6 +900,11 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
     mixer.eps_l2 = eps_l2;
     mixer.eps_rms = eps_rms;
     mixer.write_state = !verify;
+    // o_proj's weight, [hidden, H*D], read while the mixer runs
+    mixer.warm_w = w->o_proj;
+    mixer.warm_bytes = (int64_t)hidden_size * qkv * 2;
+    mixer.warm_tile_bytes = (int64_t)16 * qkv * 2;
+    mixer.warm_sleeps = 4;
     int rc;
     if ((rc = hip_status(kda::launch_gemv_bf16_batchm(front, 6, Mi, stream),
                          "kda_block_decode_k: front projections launch")) ||

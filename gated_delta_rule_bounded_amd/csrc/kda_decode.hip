@@ -321,9 +321,43 @@ struct MixerCfg {
     static_assert(kTiles == kWaves, "one column tile of each product per wave");
 };
 
+// A warm-up workgroup (MixerArgs::warm_w): workgroup j of nw, dispatched as
+// number base + j, reads one word of every 128-byte line of the tiles t = x
+// (mod 8), x its XCD, nw / 8 workgroups sharing each XCD's tiles.  It first
+// sleeps warm_sleeps x 2048 cycles (about the mixer's load phase), so the
+// mixer's own loads go ahead.
+template <int NT>
+__device__ __forceinline__ void mixer_warm(const MixerArgs &a, int j, int nw, int base, int tid)
+{
+    const int per = nw / 8;
+    if (j >= 8 * per) return;
+    const int x = (base + j) & 7;
+    const int64_t tb = a.warm_tile_bytes, tiles = (a.warm_bytes + tb - 1) / tb;
+    const int64_t lines_per_tile = tb / 128;
+    // this workgroup's tiles: x + 8 (j / 8) + 8 per r, r = 0, 1, ...
+    const int64_t t0 = x + 8 * (j / 8), dt = 8 * (int64_t)per;
+    const int64_t mine = t0 < tiles ? (tiles - 1 - t0) / dt + 1 : 0;
+    const int64_t total = mine * lines_per_tile;
+    const char *w = reinterpret_cast<const char *>(a.warm_w);
+    for (int i = 0; i < a.warm_sleeps; ++i) __builtin_amdgcn_s_sleep(32);
+    uint32_t acc = 0;
+#pragma unroll 4
+    for (int64_t i = tid; i < total; i += NT) {
+        const int64_t off = (t0 + dt * (i / lines_per_tile)) * tb + 128 * (i % lines_per_tile);
+        if (off < a.warm_bytes) acc ^= *reinterpret_cast<const uint32_t *>(w + off);
+    }
+    asm volatile("" ::"v"(acc));   // the words are read, their values unused
+}
+
 template <int D, int KS>
 __global__ __launch_bounds__((MixerCfg<D>::kThreads)) void kda_mixer_kernel(const MixerArgs a)
 {
+    if ((int)blockIdx.y >= a.B) {   // a warm-up workgroup
+        mixer_warm<MixerCfg<D>::kThreads>(a, (int)(blockIdx.x + gridDim.x * (blockIdx.y - a.B)),
+                                          (int)(gridDim.x * (gridDim.y - a.B)),
+                                          a.H * a.B, (int)threadIdx.x);
+        return;
+    }
     using Cfg = MixerCfg<D>;
     using Rec = typename Cfg::Rec;
     constexpr int NT = Cfg::kThreads, SL = Cfg::kSL, CL = Cfg::kCL, LR = Cfg::kLR;
@@ -417,7 +451,7 @@ __global__ __launch_bounds__((MixerCfg<D>::kThreads)) void kda_mixer_kernel(cons
     // (launch_lowrank_finish's layout): this thread's piece of 8 columns and
     // beta's b_proj column come as their chunk sums, added here in chunk
     // order (split_sum), and fa, ga, b_raw and beta are written here.
-    const int64_t Mrows = (int64_t)gridDim.y * K;
+    const int64_t Mrows = (int64_t)a.B * K;
     uint4 lrv = make_uint4(0u, 0u, 0u, 0u);
     float4 lp[KS][2];
     float bp[KS], btv = 0.f;
@@ -643,22 +677,47 @@ __global__ __launch_bounds__((MixerCfg<D>::kThreads)) void kda_mixer_kernel(cons
     }
 }
 
-hipError_t launch_kda_mixer(const MixerArgs &a, int B, int head_dim, hipStream_t stream)
+// Compute units of the current device (cached per device).
+static int device_cus()
 {
-    if (a.ks != 1 && a.ks != kLowRankSplit) return hipErrorInvalidValue;
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+hipError_t launch_kda_mixer(const MixerArgs &a0, int B, int head_dim, hipStream_t stream)
+{
+    if (a0.ks != 1 && a0.ks != kLowRankSplit) return hipErrorInvalidValue;
+    MixerArgs a = a0;
+    a.B = B;
+    // warm-up workgroups: whole rows of H on the CUs the (head, sequence)
+    // workgroups leave free (one workgroup fills a CU's LDS)
+    int rows = 0;
+    if (a.warm_w != nullptr && a.warm_bytes > 0 && a.warm_tile_bytes >= 128) {
+        const int64_t free_cus = (int64_t)device_cus() - (int64_t)a.H * B;
+        if (free_cus > 0) rows = (int)(free_cus / a.H);
+    }
+    const dim3 grid(a.H, B + rows);
     if (head_dim == 128) {
         if (a.ks == 1)
-            hipLaunchKernelGGL((kda_mixer_kernel<128, 1>), dim3(a.H, B),
-                               dim3(MixerCfg<128>::kThreads), 0, stream, a);
+            hipLaunchKernelGGL((kda_mixer_kernel<128, 1>), grid, dim3(MixerCfg<128>::kThreads), 0,
+                               stream, a);
         else
-            hipLaunchKernelGGL((kda_mixer_kernel<128, kLowRankSplit>), dim3(a.H, B),
+            hipLaunchKernelGGL((kda_mixer_kernel<128, kLowRankSplit>), grid,
                                dim3(MixerCfg<128>::kThreads), 0, stream, a);
     } else {
         if (a.ks == 1)
-            hipLaunchKernelGGL((kda_mixer_kernel<16, 1>), dim3(a.H, B),
-                               dim3(MixerCfg<16>::kThreads), 0, stream, a);
+            hipLaunchKernelGGL((kda_mixer_kernel<16, 1>), grid, dim3(MixerCfg<16>::kThreads), 0,
+                               stream, a);
         else
-            hipLaunchKernelGGL((kda_mixer_kernel<16, kLowRankSplit>), dim3(a.H, B),
+            hipLaunchKernelGGL((kda_mixer_kernel<16, kLowRankSplit>), grid,
                                dim3(MixerCfg<16>::kThreads), 0, stream, a);
     }
     return hipGetLastError();

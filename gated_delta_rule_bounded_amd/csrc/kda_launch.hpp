@@ -104,8 +104,19 @@ struct MixerArgs {
     const uint16_t *norm_w;         // [D]
     uint16_t *out;                  // o_norm_out [B*K, H*D]
     int K, H, R;
+    int B;                      // sequences (set by launch_kda_mixer)
     float scale, eps_l2, eps_rms;
     bool write_state;
+    // Optional warm-up of the weight that the next launch on the stream
+    // streams (a dense_gemv_bf16_batchm operand read in 16-row column tiles,
+    // tile t by that launch's workgroup t): the CUs the mixer leaves idle run
+    // workgroups of this launch that read one word of every 128-byte line of
+    // it, each tile from the XCD (t mod 8 in dispatch order) whose L2 the
+    // reading workgroup will use.  Only reads; no result changes.
+    const uint16_t *warm_w;
+    int64_t warm_bytes;         // the whole weight
+    int64_t warm_tile_bytes;    // one 16-row tile
+    int32_t warm_sleeps;        // delay before the reads, in units of 2048 cycles
 };
 hipError_t launch_kda_mixer(const MixerArgs &a, int B, int head_dim, hipStream_t stream);
 
@@ -179,7 +190,7 @@ enum GemvEpi : int32_t { kEpiNone = 0, kEpiGate = 1, kEpiBeta = 2 };
 // A segment may also be split along the contraction into ksplit equal
 // chunks (Kd % (32 ksplit) == 0), each a workgroup of its own: chunk c then
 // writes its fp32 sum (the chunk's quarters added as usual) to part[(c M + m)
-// N + n] instead of y, and the element is lowrank_sum's sum of the chunks in
+// N + n] instead of y, and the element is split_sum's sum of the chunks in
 // order, rounded to bf16 by whoever consumes it.  Small products then spread
 // over more workgroups next to large ones in the same launch.
 struct GemvSeg {

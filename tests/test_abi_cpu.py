@@ -430,3 +430,44 @@ def test_prefill_bf16_validation(lib):
     assert call(core=A + 64) == E_ALIAS                            # core over the rows
     assert call(wsp=B) == E_ALIAS                                  # workspace over the gate
     assert call(state=C) == E_ALIAS                                # state over beta
+
+
+def test_bind_records_then_replays(monkeypatch):
+    # kda.bind runs the wrapper once against a recorder (no library call is
+    # made), then each call of the returned function repeats the recorded C
+    # calls in order with the same arguments, and a failing status raises
+    import gated_delta_rule_bounded_amd as kda
+    made = []
+
+    class FakeLib:
+        rc = 0
+
+        def kda_first(self, *a):
+            made.append(("first",) + a)
+            return self.rc
+
+        def kda_second(self, *a):
+            made.append(("second",) + a)
+            return self.rc
+
+        def kda_last_error(self):
+            return b"fake failure"
+
+    fake = FakeLib()
+    monkeypatch.setattr(kda._lib, "lib", fake)
+
+    def two_calls(v, *, w):
+        kda._check(kda._lib.lib.kda_first(v, w))
+        kda._check(kda._lib.lib.kda_second(w))
+
+    again = kda.bind(two_calls, 7, w=3)
+    assert made == []
+    assert kda._lib.lib is fake
+    again()
+    again()
+    assert made == [("first", 7, 3), ("second", 3)] * 2
+    fake.rc = -2
+    with pytest.raises(kda.KdaError, match="fake failure"):
+        again()
+    with pytest.raises(ValueError):
+        kda.bind(lambda: None)

@@ -486,3 +486,41 @@ def test_block_decode_k_graph_replay_matches_eager(B, K, H, D, hidden, rank):
         np.testing.assert_array_equal(got_sn, ref["state_snaps"], err_msg=f"replay {rep} snaps")
         got_c = np.stack([c.float().cpu().numpy() for c in convs])
         np.testing.assert_array_equal(got_c, ref["conv_state"], err_msg=f"replay {rep} conv")
+
+
+def test_block_decode_k_bound_call_matches_direct():
+    """kda.bind: the block verify marshalled once and re-issued three times
+    (states reset in between) gives the direct call's bits every time."""
+    B, K, H, D, hidden, rank = 2, 4, 2, 128, 256, 32
+    x, w, S0, conv0 = _case(B, K, H, D, hidden, rank, 1901)
+    scale = D ** -0.5
+    ref = _gpu_decode_k(x, w, S0, conv0, B, K, H, D, hidden, rank, scale)
+    dev = torch.device("cuda")
+    wd = {n: t.to(dev).contiguous() for n, t in w.items()}
+    xg = x.to(dev).contiguous()
+    S0g = torch.from_numpy(np.ascontiguousarray(S0)).to(dev)
+    C0g = conv0.to(dev).contiguous()
+    states = [torch.empty(H, D, D, device=dev) for _ in range(B)]
+    convs = [torch.empty(4, 3 * H * D, dtype=torch.bfloat16, device=dev) for _ in range(B)]
+    snaps = [torch.empty(H, D, D, device=dev) for _ in range(B * (K - 1))]
+    csnaps = [torch.empty(4, 3 * H * D, dtype=torch.bfloat16, device=dev) for _ in range(B * (K - 1))]
+    tabs = [kda.ptr_table(t) for t in (states, convs, snaps, csnaps)]
+    buf = kda.block_decode_buffers(B * K, heads=H, head_dim=D, rank=rank, device=dev)
+    out = torch.empty(B * K, hidden, dtype=torch.bfloat16, device=dev)
+    say("bound block decode_k", B, K)
+    again = kda.bind(kda.kda_block_decode_k, xg, wd, tabs[0], tabs[1], buf, out, B=B, K=K,
+                     hidden_size=hidden, heads=H, head_dim=D, rank=rank, scale=scale,
+                     snap=tabs[2], conv_snap=tabs[3])
+    for rep in range(3):
+        for b in range(B):
+            states[b].copy_(S0g[b])
+            convs[b].copy_(C0g[b])
+        out.fill_(-1.0)
+        again()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.float().cpu().numpy(), ref["final_out"], err_msg=f"call {rep}")
+        np.testing.assert_array_equal(np.stack([s.cpu().numpy() for s in states]), ref["state"],
+                                      err_msg=f"call {rep} state")
+        np.testing.assert_array_equal(
+            np.stack([s.cpu().numpy() for s in snaps]).reshape(B, K - 1, H, D, D),
+            ref["state_snaps"], err_msg=f"call {rep} snaps")

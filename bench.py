@@ -623,6 +623,16 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in es])) * 1e-3
 
+    def back_to_back(fn):   # reps calls between two events: per call, as layers follow layers
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(reps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
     wy = torch.empty(1, H, K, D, device=dev)
     wy_tab = kda.ptr_table(wy)
 
@@ -646,6 +656,7 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
         timed(bound(woa))
     t_wt = timed(bound(woa_wy))
     t_v_py, t_d_py = timed(verify), timed(decode)
+    t_v_bb, t_d_bb = back_to_back(bound(verify)), back_to_back(bound(decode))
 
     # the same calls captured once per layer in a HIP graph and replayed (the
     # launches of a call are enqueued back to back without host gaps)
@@ -695,6 +706,8 @@ def bench_block_decode(kda, dev, reps=40, n_sets=4):
                        f"heads={H}, head_dim={D}, rank={rank}, bf16 weights ~N(0,0.02), "
                        f"{n_sets} layers rotated (weights from HBM)",
                 verify_ms=t_v * 1e3, decode_ms=t_d * 1e3,
+                back_to_back_ms=dict(verify=t_v_bb * 1e3, decode=t_d_bb * 1e3,
+                                     note=f"{reps} calls between two events, per call"),
                 python_call_ms=dict(verify=t_v_py * 1e3, decode=t_d_py * 1e3,
                                     note="the same calls through the checking wrappers, "
                                          "each call marshalled anew"),

@@ -698,11 +698,18 @@ hipError_t launch_kda_mixer(const MixerArgs &a0, int B, int head_dim, hipStream_
     MixerArgs a = a0;
     a.B = B;
     // warm-up workgroups: whole rows of H on the CUs the (head, sequence)
-    // workgroups leave free (one workgroup fills a CU's LDS)
+    // workgroups leave free (one workgroup fills a CU's LDS), when they are
+    // enough to read at most 256 KiB each within the fused kernel's time
+    // (measured with 32 heads and a 32 MiB o_proj: 1.3, 1.1, 0.4 and 0.5 us
+    // gained at 1, 2, 3 and 4 sequences; at 6, 512 KiB each, 0.9 us lost)
     int rows = 0;
     if (a.warm_w != nullptr && a.warm_bytes > 0 && a.warm_tile_bytes >= 128) {
         const int64_t free_cus = (int64_t)device_cus() - (int64_t)a.H * B;
-        if (free_cus > 0) rows = (int)(free_cus / a.H);
+        if (free_cus > 0) {
+            rows = (int)(free_cus / a.H);
+            const int64_t used = (int64_t)rows * a.H / 8 * 8;   // workgroups that read
+            if (used == 0 || a.warm_bytes > used * (256 << 10)) rows = 0;
+        }
     }
     const dim3 grid(a.H, B + rows);
     if (head_dim == 128) {

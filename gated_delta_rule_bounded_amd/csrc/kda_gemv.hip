@@ -43,6 +43,7 @@ struct Seg {
     const float *a_log, *dt_bias;
     int32_t ksplit;  // contraction chunks (workgroups per column tile)
     float *part;     // chunk sums when ksplit > 1
+    const uint16_t *xpack;   // x in operand order, or nullptr
 };
 
 // Store one result: its bf16 rounding, and the segment's activation of it.
@@ -104,7 +105,7 @@ template <int RT, int SIF, bool NT>
 __device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *__restrict__ w,
                                            const int64_t (&wrow)[SIF], int lane,
                                            __amdgpu_buffer_rsrc_t xr, const uint32_t (&xoff)[RT],
-                                           const GemvVisit &vs, int v0)
+                                           uint32_t xstep, const GemvVisit &vs, int v0)
 {
     constexpr int CPR = 4 * SIF;   // 16-byte chunks per row in a stage
     const int c = lane % CPR;
@@ -120,7 +121,7 @@ __device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *__
     for (int j = 0; j < SIF; ++j) {
         const int st = v0 + j < vs.cnt ? vs.step(v0 + j) : vs.beg;
 #pragma unroll
-        for (int t = 0; t < RT; ++t) S.x[j][t] = load_x(xr, xoff[t] + 64u * st);
+        for (int t = 0; t < RT; ++t) S.x[j][t] = load_x(xr, xoff[t] + xstep * (uint32_t)st);
     }
 }
 
@@ -187,15 +188,29 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
     // this lane's x rows, one per 16-row tile: byte offsets from the chunk's
     // first column of the workgroup's first row, or out of range for rows
     // past M
+    // (or, with x in operand order, of the step's 1 KiB operand block)
     const int rows = min(a.M - m0, RT * 16);
-    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(g.x + (int64_t)m0 * g.ldx + k0), (short)0,
-        (int)((int64_t)rows * g.ldx * 2 - (int64_t)k0 * 2), 0x00020000);
-    uint32_t xoff[RT];
+    __amdgpu_buffer_rsrc_t xr;
+    uint32_t xoff[RT], xstep;
+    if (g.xpack == nullptr) {
+        xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(g.x + (int64_t)m0 * g.ldx + k0), (short)0,
+            (int)((int64_t)rows * g.ldx * 2 - (int64_t)k0 * 2), 0x00020000);
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-        const int m = 16 * t + r;
-        xoff[t] = m < rows ? (uint32_t)(((int64_t)m * g.ldx + 8 * kg) * 2) : kOutOfRange;
+        for (int t = 0; t < RT; ++t) {
+            const int m = 16 * t + r;
+            xoff[t] = m < rows ? (uint32_t)(((int64_t)m * g.ldx + 8 * kg) * 2) : kOutOfRange;
+        }
+        xstep = 64;
+    } else {
+        const int S = g.Kd >> 5, tiles = (rows + 15) >> 4;
+        xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(g.xpack + (((int64_t)(m0 >> 4) * S + (k0 >> 5)) << 9)),
+            (short)0, (int)((((int64_t)tiles * S - (k0 >> 5)) << 10)), 0x00020000);
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+            xoff[t] = t < tiles ? (uint32_t)((((int64_t)t * S) << 10) + 16 * lane) : kOutOfRange;
+        xstep = 1024;
     }
 
     floatx4 acc[RT];
@@ -206,16 +221,16 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
     if (vs.cnt > 0) {
         WRows<SIF> &L = s_w[wave];
         Stage<RT, SIF> A, B;
-        load_stage<RT, SIF, NT>(A, g.w, wrow, lane, xr, xoff, vs, 0);
-        load_stage<RT, SIF, NT>(B, g.w, wrow, lane, xr, xoff, vs, SIF);
+        load_stage<RT, SIF, NT>(A, g.w, wrow, lane, xr, xoff, xstep, vs, 0);
+        load_stage<RT, SIF, NT>(B, g.w, wrow, lane, xr, xoff, xstep, vs, SIF);
         put_stage(A, L, lane);
 #pragma unroll 1
         for (int v = 0; v < vs.cnt; v += 2 * SIF) {
             mma_stage(A, L, acc, vs, v, r, kg);
-            load_stage<RT, SIF, NT>(A, g.w, wrow, lane, xr, xoff, vs, v + 2 * SIF);
+            load_stage<RT, SIF, NT>(A, g.w, wrow, lane, xr, xoff, xstep, vs, v + 2 * SIF);
             put_stage(B, L, lane);
             mma_stage(B, L, acc, vs, v + SIF, r, kg);
-            load_stage<RT, SIF, NT>(B, g.w, wrow, lane, xr, xoff, vs, v + 3 * SIF);
+            load_stage<RT, SIF, NT>(B, g.w, wrow, lane, xr, xoff, xstep, vs, v + 3 * SIF);
             put_stage(A, L, lane);
         }
     }
@@ -269,7 +284,36 @@ __global__ __launch_bounds__(256) void lowrank_finish_kernel(
     }
 }
 
+// One thread per 16-byte piece of the operand-order copy of x.
+__global__ __launch_bounds__(256) void gemv_pack_x_kernel(const uint16_t *__restrict__ x,
+                                                          int64_t ldx, int M, int Kd,
+                                                          uint16_t *__restrict__ xpack)
+{
+    const int S = Kd >> 5;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t n = (int64_t)((M + 15) >> 4) * S * 64;
+    if (i >= n) return;
+    const int l = (int)(i & 63);
+    const int64_t ts = i >> 6;
+    const int s = (int)(ts % S), T = (int)(ts / S);
+    const int m = 16 * T + (l & 15);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (m < M) v = *reinterpret_cast<const uint4 *>(x + (int64_t)m * ldx + 32 * s + 8 * (l >> 4));
+    *reinterpret_cast<uint4 *>(xpack + 8 * i) = v;
+}
+
 }  // namespace
+
+hipError_t launch_gemv_pack_x(const uint16_t *x, int64_t ldx, int M, int Kd, uint16_t *xpack,
+                              hipStream_t stream)
+{
+    if (M <= 0) return hipSuccess;
+    if (Kd % 32 != 0) return hipErrorInvalidValue;
+    const int64_t n = (int64_t)((M + 15) / 16) * (Kd / 32) * 64;
+    hipLaunchKernelGGL(gemv_pack_x_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, x, ldx, M, Kd, xpack);
+    return hipGetLastError();
+}
 
 hipError_t launch_lowrank_finish(const float *part, int ks, int M, int rank, int heads,
                                  uint16_t *fa, uint16_t *ga, uint16_t *b_raw, float *beta,
@@ -290,7 +334,7 @@ hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStre
         a.seg[i] = Seg{segs[i].x,     segs[i].w,        segs[i].y,   segs[i].ldx,
                        segs[i].ldy,   segs[i].N,        segs[i].Kd,  tiles,
                        segs[i].epi,   segs[i].head_dim, segs[i].act, segs[i].a_log,
-                       segs[i].dt_bias, max(segs[i].ksplit, 1), segs[i].part};
+                       segs[i].dt_bias, max(segs[i].ksplit, 1), segs[i].part, segs[i].xpack};
         tiles += (segs[i].N + kColTile - 1) / kColTile * max(segs[i].ksplit, 1);
     }
     a.nseg = nseg;

@@ -840,14 +840,7 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
                        (int64_t)2 * ks * (2 * rank + heads) <= hidden_size;
     float *const part = split ? reinterpret_cast<float *>(out) : nullptr;
     const size_t lr_chunk = (size_t)ks * M * rank;   // floats of one split product
-    // Past 16 rows each workgroup reads the hidden rows over its whole
-    // contraction, several times the bytes of its weights; they are first put
-    // in the projection kernel's operand order (one contiguous 1 KiB block per
-    // operand instead of 16 rows' 64-byte pieces) in the conv output buffer,
-    // which the front leaves untouched and a later launch overwrites.
-    uint16_t *const xp = Mi > 16 && kda::gemv_pack_x_elems(Mi, hs) <= (int64_t)M * cd
-                             ? b->conv_out : nullptr;
-    kda::GemvSeg front[] = {
+    const kda::GemvSeg front[] = {
         {hidden, w->q_proj, b->qkv_proj, hs, cd, qk, hs},
         {hidden, w->k_proj, b->qkv_proj + qkv, hs, cd, qk, hs},
         {hidden, w->v_proj, b->qkv_proj + 2 * qkv, hs, cd, qk, hs},
@@ -860,7 +853,6 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
         {hidden, w->b_proj, b->b_raw, hs, heads, heads, hs, kda::kEpiBeta, b->beta, nullptr,
          nullptr, 0, split ? ks : 1, split ? part + 2 * lr_chunk : nullptr},
     };
-    for (kda::GemvSeg &g : front) g.xpack = xp;
     const kda::GemvSeg mid[] = {
         // f_b with the log-decay gate fused into its epilogue
         {b->fa, w->f_b, b->g_raw, rk, qkv, qk, rk, kda::kEpiGate, b->gate, w->a_log, w->dt_bias,
@@ -914,9 +906,7 @@ static int block_decode_run(const uint16_t *hidden, const kda_block_weights *w,
     mixer.warm_tile_bytes = (int64_t)16 * qkv * 2;
     mixer.warm_sleeps = 4;
     int rc;
-    if ((rc = hip_status(xp ? kda::launch_gemv_pack_x(hidden, hs, Mi, hs, xp, stream) : hipSuccess,
-                         "kda_block_decode_k: operand-order copy of the hidden rows")) ||
-        (rc = hip_status(kda::launch_gemv_bf16_batchm(front, 6, Mi, stream),
+    if ((rc = hip_status(kda::launch_gemv_bf16_batchm(front, 6, Mi, stream),
                          "kda_block_decode_k: front projections launch")) ||
         (rc = hip_status(fuse_mixer || !split
                              ? hipSuccess

@@ -43,7 +43,6 @@ struct Seg {
     const float *a_log, *dt_bias;
     int32_t ksplit;  // contraction chunks (workgroups per column tile)
     float *part;     // chunk sums when ksplit > 1
-    const uint16_t *xpack;   // x in operand order, or nullptr
 };
 
 // Store one result: its bf16 rounding, and the segment's activation of it.
@@ -100,14 +99,18 @@ __device__ __forceinline__ uint4 load_x(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 // chunk against bank conflicts on the operand reads.
 template <int SIF>
 using WRows = uintx4[16][4 * SIF + 1];
+// With XL the x rows go the same way (16 RT rows: each row's stage is one
+// contiguous span, instead of 16 rows' 64-byte pieces per load).
+template <int RT, int SIF>
+using XRows = uintx4[16 * RT][4 * SIF + 1];
 
-template <int RT, int SIF, bool NT>
+template <int RT, int SIF, bool NT, bool XL>
 __device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *__restrict__ w,
                                            const int64_t (&wrow)[SIF], int lane,
                                            __amdgpu_buffer_rsrc_t xr, const uint32_t (&xoff)[RT],
-                                           uint32_t xstep, const GemvVisit &vs, int v0)
+                                           uint32_t xrows, const GemvVisit &vs, int v0)
 {
-    constexpr int CPR = 4 * SIF;   // 16-byte chunks per row in a stage
+    constexpr int CPR = 4 * SIF, RPI = 16 / SIF;   // 16-byte chunks per row, rows per load
     const int c = lane % CPR;
     const int vj = v0 + c / 4;     // visited step of this lane's chunk
     const int stc = vj < vs.cnt ? vs.step(vj) : vs.beg;   // past the end: a valid dummy
@@ -117,36 +120,55 @@ __device__ __forceinline__ void load_stage(Stage<RT, SIF> &S, const uint16_t *__
         const uintx4 *p = reinterpret_cast<const uintx4 *>(w + wrow[i] + 32 * stc + 8 * (c % 4));
         S.w[i] = NT ? __builtin_nontemporal_load(p) : *p;
     }
+    if constexpr (XL) {
+        // load i: rows i RPI + lane / CPR, this lane's chunk of their stage;
+        // xoff[0] is the byte offset of row lane / CPR (out of range past the
+        // rows), xrows the bytes of RPI rows
+        const uint32_t o = xoff[0] + 2u * (uint32_t)(32 * stc + 8 * (c % 4));
 #pragma unroll
-    for (int j = 0; j < SIF; ++j) {
-        const int st = v0 + j < vs.cnt ? vs.step(v0 + j) : vs.beg;
+        for (int i = 0; i < SIF * RT; ++i) S.x[i / RT][i % RT] = load_x(xr, o + xrows * (uint32_t)i);
+    } else {
 #pragma unroll
-        for (int t = 0; t < RT; ++t) S.x[j][t] = load_x(xr, xoff[t] + xstep * (uint32_t)st);
+        for (int j = 0; j < SIF; ++j) {
+            const int st = v0 + j < vs.cnt ? vs.step(v0 + j) : vs.beg;
+#pragma unroll
+            for (int t = 0; t < RT; ++t) S.x[j][t] = load_x(xr, xoff[t] + 64u * st);
+        }
     }
 }
 
-// the staged weights into the wave's LDS rows (after the stage before them
-// has been read from there: the wave's own LDS accesses complete in order)
-template <int RT, int SIF>
-__device__ __forceinline__ void put_stage(const Stage<RT, SIF> &S, WRows<SIF> &L, int lane)
+// the staged weights (and with XL the x rows) into the wave's LDS rows
+// (after the stage before them has been read from there: the wave's own LDS
+// accesses complete in order)
+template <int RT, int SIF, bool XL>
+__device__ __forceinline__ void put_stage(const Stage<RT, SIF> &S, WRows<SIF> &L,
+                                          XRows<RT, SIF> &X, int lane)
 {
     constexpr int CPR = 4 * SIF, RPI = 16 / SIF;
 #pragma unroll
     for (int i = 0; i < SIF; ++i) L[i * RPI + lane / CPR][lane % CPR] = S.w[i];
+    if constexpr (XL) {
+#pragma unroll
+        for (int i = 0; i < SIF * RT; ++i)
+            X[i * RPI + lane / CPR][lane % CPR] = __builtin_bit_cast(uintx4, S.x[i / RT][i % RT]);
+    }
 }
 
-template <int RT, int SIF>
+template <int RT, int SIF, bool XL>
 __device__ __forceinline__ void mma_stage(const Stage<RT, SIF> &S, const WRows<SIF> &L,
-                                          floatx4 (&acc)[RT], const GemvVisit &vs, int v0, int r,
-                                          int kg)
+                                          const XRows<RT, SIF> &X, floatx4 (&acc)[RT],
+                                          const GemvVisit &vs, int v0, int r, int kg)
 {
 #pragma unroll
     for (int j = 0; j < SIF; ++j) {
         if (v0 + j >= vs.cnt) break;
         const bf16x8 b = __builtin_bit_cast(bf16x8, L[r][4 * j + kg]);
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
-            acc[t] = mfma_bf16(__builtin_bit_cast(bf16x8, S.x[j][t]), b, acc[t]);
+        for (int t = 0; t < RT; ++t) {
+            const bf16x8 xa = XL ? __builtin_bit_cast(bf16x8, X[16 * t + r][4 * j + kg])
+                                 : __builtin_bit_cast(bf16x8, S.x[j][t]);
+            acc[t] = mfma_bf16(xa, b, acc[t]);
+        }
     }
 }
 
@@ -154,11 +176,12 @@ __device__ __forceinline__ void mma_stage(const Stage<RT, SIF> &S, const WRows<S
 // load stage, two stages in flight; NT marks the weight loads non-temporal
 // (streaming).  None of these changes any element's order of accumulation,
 // only how many rows a workgroup carries and how its loads run.
-template <int RT, int SIF, bool NT>
+template <int RT, int SIF, bool NT, bool XL>
 __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
 {
     __shared__ float part[kWaves][RT][16][17];
     __shared__ WRows<SIF> s_w[kWaves];
+    __shared__ XRows<RT, SIF> s_x[XL ? kWaves : 1];   // with XL only
 
     // segment of this column tile (uniform scalar search over a handful)
     int s = 0;
@@ -187,30 +210,23 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
     }
     // this lane's x rows, one per 16-row tile: byte offsets from the chunk's
     // first column of the workgroup's first row, or out of range for rows
-    // past M
-    // (or, with x in operand order, of the step's 1 KiB operand block)
+    // past M (with XL: xoff[0] the row lane / (4 SIF) of the contiguous row
+    // loads, xrows the bytes of 16 / SIF rows; rows past M then lie past the
+    // bound by themselves)
     const int rows = min(a.M - m0, RT * 16);
-    __amdgpu_buffer_rsrc_t xr;
-    uint32_t xoff[RT], xstep;
-    if (g.xpack == nullptr) {
-        xr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(g.x + (int64_t)m0 * g.ldx + k0), (short)0,
-            (int)((int64_t)rows * g.ldx * 2 - (int64_t)k0 * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(g.x + (int64_t)m0 * g.ldx + k0), (short)0,
+        (int)((int64_t)rows * g.ldx * 2 - (int64_t)k0 * 2), 0x00020000);
+    uint32_t xoff[RT] = {}, xrows = 0;
+    if constexpr (XL) {
+        xoff[0] = (uint32_t)((int64_t)(lane / (4 * SIF)) * g.ldx * 2);
+        xrows = (uint32_t)((int64_t)(16 / SIF) * g.ldx * 2);
+    } else {
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
             const int m = 16 * t + r;
             xoff[t] = m < rows ? (uint32_t)(((int64_t)m * g.ldx + 8 * kg) * 2) : kOutOfRange;
         }
-        xstep = 64;
-    } else {
-        const int S = g.Kd >> 5, tiles = (rows + 15) >> 4;
-        xr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(g.xpack + (((int64_t)(m0 >> 4) * S + (k0 >> 5)) << 9)),
-            (short)0, (int)((((int64_t)tiles * S - (k0 >> 5)) << 10)), 0x00020000);
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-            xoff[t] = t < tiles ? (uint32_t)((((int64_t)t * S) << 10) + 16 * lane) : kOutOfRange;
-        xstep = 1024;
     }
 
     floatx4 acc[RT];
@@ -220,18 +236,19 @@ __global__ __launch_bounds__(256) void gemv_bf16_batchm(const Args a)
     const GemvVisit vs = gemv_visit(wave, nsteps, n0 / kColTile);
     if (vs.cnt > 0) {
         WRows<SIF> &L = s_w[wave];
+        XRows<RT, SIF> &X = s_x[XL ? wave : 0];
         Stage<RT, SIF> A, B;
-        load_stage<RT, SIF, NT>(A, g.w, wrow, lane, xr, xoff, xstep, vs, 0);
-        load_stage<RT, SIF, NT>(B, g.w, wrow, lane, xr, xoff, xstep, vs, SIF);
-        put_stage(A, L, lane);
+        load_stage<RT, SIF, NT, XL>(A, g.w, wrow, lane, xr, xoff, xrows, vs, 0);
+        load_stage<RT, SIF, NT, XL>(B, g.w, wrow, lane, xr, xoff, xrows, vs, SIF);
+        put_stage<RT, SIF, XL>(A, L, X, lane);
 #pragma unroll 1
         for (int v = 0; v < vs.cnt; v += 2 * SIF) {
-            mma_stage(A, L, acc, vs, v, r, kg);
-            load_stage<RT, SIF, NT>(A, g.w, wrow, lane, xr, xoff, xstep, vs, v + 2 * SIF);
-            put_stage(B, L, lane);
-            mma_stage(B, L, acc, vs, v + SIF, r, kg);
-            load_stage<RT, SIF, NT>(B, g.w, wrow, lane, xr, xoff, xstep, vs, v + 3 * SIF);
-            put_stage(A, L, lane);
+            mma_stage<RT, SIF, XL>(A, L, X, acc, vs, v, r, kg);
+            load_stage<RT, SIF, NT, XL>(A, g.w, wrow, lane, xr, xoff, xrows, vs, v + 2 * SIF);
+            put_stage<RT, SIF, XL>(B, L, X, lane);
+            mma_stage<RT, SIF, XL>(B, L, X, acc, vs, v + SIF, r, kg);
+            load_stage<RT, SIF, NT, XL>(B, g.w, wrow, lane, xr, xoff, xrows, vs, v + 3 * SIF);
+            put_stage<RT, SIF, XL>(A, L, X, lane);
         }
     }
 
@@ -284,36 +301,7 @@ __global__ __launch_bounds__(256) void lowrank_finish_kernel(
     }
 }
 
-// One thread per 16-byte piece of the operand-order copy of x.
-__global__ __launch_bounds__(256) void gemv_pack_x_kernel(const uint16_t *__restrict__ x,
-                                                          int64_t ldx, int M, int Kd,
-                                                          uint16_t *__restrict__ xpack)
-{
-    const int S = Kd >> 5;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t n = (int64_t)((M + 15) >> 4) * S * 64;
-    if (i >= n) return;
-    const int l = (int)(i & 63);
-    const int64_t ts = i >> 6;
-    const int s = (int)(ts % S), T = (int)(ts / S);
-    const int m = 16 * T + (l & 15);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (m < M) v = *reinterpret_cast<const uint4 *>(x + (int64_t)m * ldx + 32 * s + 8 * (l >> 4));
-    *reinterpret_cast<uint4 *>(xpack + 8 * i) = v;
-}
-
 }  // namespace
-
-hipError_t launch_gemv_pack_x(const uint16_t *x, int64_t ldx, int M, int Kd, uint16_t *xpack,
-                              hipStream_t stream)
-{
-    if (M <= 0) return hipSuccess;
-    if (Kd % 32 != 0) return hipErrorInvalidValue;
-    const int64_t n = (int64_t)((M + 15) / 16) * (Kd / 32) * 64;
-    hipLaunchKernelGGL(gemv_pack_x_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                       stream, x, ldx, M, Kd, xpack);
-    return hipGetLastError();
-}
 
 hipError_t launch_lowrank_finish(const float *part, int ks, int M, int rank, int heads,
                                  uint16_t *fa, uint16_t *ga, uint16_t *b_raw, float *beta,
@@ -334,7 +322,7 @@ hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStre
         a.seg[i] = Seg{segs[i].x,     segs[i].w,        segs[i].y,   segs[i].ldx,
                        segs[i].ldy,   segs[i].N,        segs[i].Kd,  tiles,
                        segs[i].epi,   segs[i].head_dim, segs[i].act, segs[i].a_log,
-                       segs[i].dt_bias, max(segs[i].ksplit, 1), segs[i].part, segs[i].xpack};
+                       segs[i].dt_bias, max(segs[i].ksplit, 1), segs[i].part};
         tiles += (segs[i].N + kColTile - 1) / kColTile * max(segs[i].ksplit, 1);
     }
     a.nseg = nseg;
@@ -348,20 +336,25 @@ hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStre
     // tiles than CUs (the q|k|v product: 20.7 against 22.1 us) and 3 % slower
     // at one tile per CU (o_proj), so only the former take them.
     const bool nt = tiles > 256;
+    // past 16 rows the x rows (then several times the bytes of a tile's
+    // weights) are read as contiguous row spans through LDS, as the weights
+    // are: at 64 rows 64.5 -> 39.8 us for q|k|v, against 16 rows' 64-byte
+    // pieces per load
     if (M <= 16) {
         if (nt)
-            hipLaunchKernelGGL((gemv_bf16_batchm<1, 4, true>), dim3(tiles, 1), dim3(256), 0,
+            hipLaunchKernelGGL((gemv_bf16_batchm<1, 4, true, false>), dim3(tiles, 1), dim3(256), 0,
                                stream, a);
         else
-            hipLaunchKernelGGL((gemv_bf16_batchm<1, 4, false>), dim3(tiles, 1), dim3(256), 0,
-                               stream, a);
+            hipLaunchKernelGGL((gemv_bf16_batchm<1, 4, false, false>), dim3(tiles, 1), dim3(256),
+                               0, stream, a);
     } else {
+        const dim3 grid(tiles, (M + 63) / 64);
         if (nt)
-            hipLaunchKernelGGL((gemv_bf16_batchm<4, 2, true>), dim3(tiles, (M + 63) / 64),
-                               dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((gemv_bf16_batchm<4, 2, true, true>), grid, dim3(256), 0, stream,
+                               a);
         else
-            hipLaunchKernelGGL((gemv_bf16_batchm<4, 2, false>), dim3(tiles, (M + 63) / 64),
-                               dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((gemv_bf16_batchm<4, 2, false, true>), grid, dim3(256), 0, stream,
+                               a);
     }
     return hipGetLastError();
 }

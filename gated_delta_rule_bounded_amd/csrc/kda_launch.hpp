@@ -205,21 +205,8 @@ struct GemvSeg {
     int32_t head_dim = 0;
     int32_t ksplit = 1;
     float *part = nullptr;
-    // x already in operand order (launch_gemv_pack_x of x, the same M and
-    // Kd), or nullptr: x is then read row by row
-    const uint16_t *xpack = nullptr;
 };
 hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStream_t stream);
-// x [M][Kd] (row stride ldx) rearranged into the MFMA A-operand order of the
-// projection kernel: for 16-row tile T and 32-deep step s, 1 KiB = 64 lanes x
-// 8 values, lane l holding row 16 T + l % 16, columns 32 s + 8 (l / 16) ..
-// + 8, at element ((T (Kd / 32) + s) 64 + l) 8; rows past M are zeros.  The
-// projection kernel then reads each operand as one contiguous 1 KiB block
-// instead of 16 rows' 64-byte pieces.  xpack holds gemv_pack_x_elems(M, Kd)
-// bf16 values; Kd a multiple of 32.
-inline int64_t gemv_pack_x_elems(int M, int Kd) { return (int64_t)((M + 15) / 16) * 16 * Kd; }
-hipError_t launch_gemv_pack_x(const uint16_t *x, int64_t ldx, int M, int Kd, uint16_t *xpack,
-                              hipStream_t stream);
 // A block's f_a, g_a and b_proj products split ks ways (chunk sums in part:
 // f_a [ks][M][rank], then g_a alike, then b_proj [ks][M][heads]) finished
 // into fa, ga, b_raw and beta.

@@ -551,10 +551,8 @@ int dense_gemv_bf16_batchm(const uint16_t *x, int64_t ldx, const uint16_t *w,
  * and must be distinct, with snapshots disjoint from them.  B == 0 or K == 0
  * is a no-op.  Allocates nothing; three launches on `stream` when K <= 16
  * and rank <= 128 (the gate products, conv, recurrence and norm of each
- * (head, sequence) in one kernel), six or seven otherwise, and one more
- * first when B*K > 16 (the hidden rows copied into conv_out in the
- * projection kernel's operand order; conv_out is rewritten later in the
- * call); the same bits either way.
+ * (head, sequence) in one kernel), six or seven otherwise; the same bits
+ * either way.
  * ------------------------------------------------------------------------ */
 typedef struct kda_block_decode_buffers {
     uint16_t *qkv_proj, *conv_out;

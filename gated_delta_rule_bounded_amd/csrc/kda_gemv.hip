@@ -336,17 +336,32 @@ hipError_t launch_gemv_bf16_batchm(const GemvSeg *segs, int nseg, int M, hipStre
     // tiles than CUs (the q|k|v product: 20.7 against 22.1 us) and 3 % slower
     // at one tile per CU (o_proj), so only the former take them.
     const bool nt = tiles > 256;
-    // past 16 rows the x rows (then several times the bytes of a tile's
-    // weights) are read as contiguous row spans through LDS, as the weights
-    // are: at 64 rows 64.5 -> 39.8 us for q|k|v, against 16 rows' 64-byte
-    // pieces per load
-    if (M <= 16) {
+    // past 8 rows the x rows (then as many bytes as a tile's weights, or
+    // several times) are read as contiguous row spans through LDS, as the
+    // weights are, against 16 rows' 64-byte pieces per load: q|k|v at 16
+    // rows 25.4 -> 22.4 us, at 64 rows 64.5 -> 39.8 us; 17 to 32 rows take
+    // two row tiles a workgroup (at 17 rows 31.0 -> 24.6 us against four)
+    if (M <= 8) {
         if (nt)
             hipLaunchKernelGGL((gemv_bf16_batchm<1, 4, true, false>), dim3(tiles, 1), dim3(256), 0,
                                stream, a);
         else
             hipLaunchKernelGGL((gemv_bf16_batchm<1, 4, false, false>), dim3(tiles, 1), dim3(256),
                                0, stream, a);
+    } else if (M <= 16) {
+        if (nt)
+            hipLaunchKernelGGL((gemv_bf16_batchm<1, 4, true, true>), dim3(tiles, 1), dim3(256), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((gemv_bf16_batchm<1, 4, false, true>), dim3(tiles, 1), dim3(256),
+                               0, stream, a);
+    } else if (M <= 32) {
+        if (nt)
+            hipLaunchKernelGGL((gemv_bf16_batchm<2, 2, true, true>), dim3(tiles, (M + 31) / 32),
+                               dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemv_bf16_batchm<2, 2, false, true>), dim3(tiles, (M + 31) / 32),
+                               dim3(256), 0, stream, a);
     } else {
         const dim3 grid(tiles, (M + 63) / 64);
         if (nt)

@@ -31,7 +31,8 @@ STAGES = ("qkv_proj", "conv_out", "fa", "g_raw", "b_raw", "gate", "beta", "core"
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,Kd", [(1, 48, 96), (4, 4096, 4096), (7, 40, 4096), (70, 136, 256),
-                                    (16, 32, 4096), (3, 4096, 128), (5, 64, 4224)])
+                                    (16, 32, 4096), (3, 4096, 128), (5, 64, 4224), (12, 48, 4224),
+                                    (24, 96, 4096), (33, 40, 4096)])
 def test_gemv_matches_oracle(orc, M, N, Kd):
     r = np.random.default_rng(M * 7 + N + Kd)
     x = workloads.to_bf16(r.standard_normal((M, Kd)))
@@ -68,11 +69,13 @@ def test_gemv_rows_are_order_exact():
         y1 = torch.empty(1, N, dtype=torch.bfloat16, device="cuda")
         kda.dense_gemv_bf16_batchm(x[m:m + 1], w, y1, M=1, N=N, Kd=Kd)
         singles.append((m, y1))
-    # up to 16 rows and more rows run different kernel instances (one row
-    # tile with four-step load stages, four row tiles with two-step stages);
-    # both accumulate in one order
+    # the row counts run different kernel instances (one row tile with
+    # four-step load stages up to 16 rows, its x rows through LDS past 8;
+    # two row tiles up to 32 and four past that, two-step stages, x rows
+    # through LDS); all accumulate in one order
     groups = {}
-    for m0, M_ in ((30, 4), (40, 3), (8, 8), (20, 16), (2, 5)):
+    for m0, M_ in ((30, 4), (40, 3), (8, 8), (20, 16), (2, 5), (50, 12), (10, 24), (5, 32),
+                   (1, 40)):
         yg = torch.empty(M_, N, dtype=torch.bfloat16, device="cuda")
         kda.dense_gemv_bf16_batchm(x[m0:m0 + M_], w, yg, M=M_, N=N, Kd=Kd)
         groups[(m0, M_)] = yg
@@ -96,7 +99,7 @@ def test_gemv_rows_are_order_exact_with_ragged_steps():
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     kda.dense_gemv_bf16_batchm(x, w, y, M=M, N=N, Kd=Kd)
     parts = []
-    for m0, M_ in ((0, 1), (69, 1), (10, 4), (33, 16), (40, 20)):
+    for m0, M_ in ((0, 1), (69, 1), (10, 4), (33, 16), (40, 20), (3, 9), (20, 33)):
         yg = torch.empty(M_, N, dtype=torch.bfloat16, device="cuda")
         kda.dense_gemv_bf16_batchm(x[m0:m0 + M_], w, yg, M=M_, N=N, Kd=Kd)
         parts.append((m0, M_, yg))

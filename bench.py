@@ -23,12 +23,15 @@ Also reported on the same JSON line (measured after the timed steps):
             (kda_prefill_bf16), checked bitwise against the fp32-input run;
   prefill_varlen  the 4096 tokens as 8 x 512 and 64 x 64 prompts in one
             kda_prefill_varlen call;
-  block_decode  the block for one sequence: K=4 verify vs one token, the
-            write-on-accept pair, HIP-graph replays, and the projection
-            kernel's weight-read rate;
+  block_decode  the block for one sequence: K=4 verify vs one token (each
+            call marshalled once with kda.bind; per call, and per call over
+            40 calls back to back), the write-on-accept pair, HIP-graph
+            replays, 16 sequences x 4 rows, and the projection kernel's
+            weight-read rate;
   roofline  for the dominant prefill kernel, from HIP events on the stream
             the kernels run on, with its counted HBM traffic;
-  cpu_baseline  the fp64 oracle on the same prefill workload, on host cores.
+  cpu_baseline  the fp64 oracle on the same prefill workload, and on samples
+            of the decode and decode_k workloads, on host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        (--prefill-only, --decode-only, --block-only, --block-decode-only,

@@ -112,7 +112,8 @@ struct MixerArgs {
     // tile t by that launch's workgroup t): the CUs the mixer leaves idle run
     // workgroups of this launch that read one word of every 128-byte line of
     // it, each tile from the XCD (t mod 8 in dispatch order) whose L2 the
-    // reading workgroup will use.  Only reads; no result changes.
+    // reading workgroup will use (measured: the lines are then served from
+    // the last-level cache, not that L2).  Only reads; no result changes.
     const uint16_t *warm_w;
     int64_t warm_bytes;         // the whole weight
     int64_t warm_tile_bytes;    // one 16-row tile
